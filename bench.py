@@ -1,0 +1,255 @@
+"""Benchmark of the codec's hot path on one MI355X.
+
+One step = the whole path over one batch: tq_encode_kv of every key and value
+of the workload into its compressed paged cache, then one tq_decode_attend of
+every sequence's query over that cache.  Default workload: one sequence of
+32768 tokens, 8 KV heads, 64 query heads (GQA 8), head_dim 128, bf16 K/V with
+outlier-channel keys, 4-bit keys and values, 16-token pages.
+
+The C sets of inputs, caches and workspaces rotate from step to step (C * set
+bytes >= 1 GiB, four times the 256 MB Infinity Cache), so every step reads
+from HBM.  Inputs are resident on the GPU before timing starts.
+
+Printed: one JSON line (rank 0).  `value` is decode-attend GB/s of compressed
+KV read (algorithmic bytes / mean decode-kernel time); encoded vectors/s and
+the encode GB/s are reported beside it, each with its fraction of the 8 TB/s
+HBM peak.  Kernel times are HIP events on the stream the kernels run on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode-attend GB/s of compressed KV read (% HBM peak) + encoded vectors/s"
+KERNEL_SOURCES = ["kv_cache_vector_encode_amd/csrc/tq_encode.hip", "kv_cache_vector_encode_amd/csrc/tq_decode.hip",
+                  "kv_cache_vector_encode_amd/csrc/tq_device.h", "kv_cache_vector_encode_amd/csrc/tq_internal.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def bytes_per_vector(bits: int, in_bytes: int = 2, qjl: bool = False) -> tuple[int, int]:
+    """(input bytes, compressed bytes) of one 128-d vector."""
+    return 128 * in_bytes, 128 * bits // 8 + 2 + ((16 + 2) if qjl else 0)
+
+
+def cpu_baseline(w, sample_tokens: int):
+    """The oracle (float64 numpy) on a bounded sample of the same workload."""
+    from threadpoolctl import threadpool_info
+
+    from kv_cache_vector_encode_amd import workloads as W
+    from oracle import tq_oracle as O
+
+    c32, _ = O.codebook_fp32(128, w.bits_k)
+    kb, k64 = W.keys(w, 0, sample_tokens)
+    vb, v64 = W.values(w, 0, sample_tokens)
+    x = np.concatenate([k64.reshape(-1, 128), v64.reshape(-1, 128)])
+    t0 = time.perf_counter()
+    encs = [O.encode(x[i:i + 32768], w.rot_seed, c32) for i in range(0, len(x), 32768)]
+    t_enc = time.perf_counter() - t0
+    # decode over the sample: reconstruct + original-frame attention for every
+    # query head of the sample's KV heads
+    kidx = np.concatenate([e["idx"] for e in encs])[: len(k64.reshape(-1, 128))].reshape(sample_tokens, w.num_kv_heads, 128)
+    kg = np.concatenate([e["gamma16"] for e in encs])[: sample_tokens * w.num_kv_heads].reshape(sample_tokens, w.num_kv_heads)
+    vidx = np.concatenate([e["idx"] for e in encs])[sample_tokens * w.num_kv_heads:].reshape(sample_tokens, w.num_kv_heads, 128)
+    vg = np.concatenate([e["gamma16"] for e in encs])[sample_tokens * w.num_kv_heads:].reshape(sample_tokens, w.num_kv_heads)
+    _, q64 = W.queries(w)
+    G = w.num_q_heads // w.num_kv_heads
+    t0 = time.perf_counter()
+    for h in range(w.num_kv_heads):
+        khat = O.reconstruct(kidx[:, h], kg[:, h], w.rot_seed, c32)
+        vhat = O.reconstruct(vidx[:, h], vg[:, h], w.rot_seed, c32)
+        for g in range(G):
+            O.attention(q64[0, h * G + g], khat, vhat)
+    t_dec = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    _, comp = bytes_per_vector(w.bits_k)
+    return {
+        "value": round(sample_tokens * w.num_kv_heads * 2 * comp / t_dec / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{sample_tokens} tokens x {w.num_kv_heads} KV heads of the workload: float64 numpy oracle "
+                   f"encode of {len(x)} vectors ({len(x) / t_enc:.0f} vectors/s) and original-frame decode-attend "
+                   f"of {w.num_q_heads} query heads over them ({t_dec:.1f} s)"),
+        "encode_vectors_per_s": round(len(x) / t_enc, 1),
+        "seconds": round(t_enc + t_dec, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_1x32768_h8_gqa8_b4")
+    ap.add_argument("--sets", type=int, default=0, help="rotating input/cache sets (0: enough for 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    ap.add_argument("--only", choices=["encode", "decode", "both"], default="both",
+                    help="profiling aid: time only one of the two kernels")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU mode.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_vector_encode_amd import tq
+    from kv_cache_vector_encode_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = W.CONFIGS[args.workload]
+    tq.lib()
+    print(f"# workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+
+    # ---- inputs (identical copies per set; rotation only defeats the caches)
+    kb, _ = W.keys(w)
+    vb, _ = W.values(w)
+    qb, _ = W.queries(w)
+    K0 = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(dev)
+    V0 = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(dev)
+    q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).to(dev)
+    slots = torch.from_numpy(W.slot_mapping(w)).to(dev)
+    bt = torch.from_numpy(W.block_tables(w)).to(dev)
+    lens = torch.from_numpy(W.seq_lens(w)).to(dev)
+    del kb, vb
+
+    rot = tq.tq_make_rotation(w.rot_seed, 128)
+    cfg = tq.make_config(w.num_kv_heads, w.num_blocks, w.bits_k, w.bits_v, rot)
+    pool_bytes = tq.tq_cache_bytes(cfg)
+    set_bytes = 2 * K0.numel() * 2 + pool_bytes
+    nsets = args.sets or max(1, math.ceil((1 << 30) / set_bytes))
+    sets = []
+    for i in range(nsets):
+        pool = torch.zeros(pool_bytes, dtype=torch.uint8, device=dev)
+        cache = tq.tq_cache_create(cfg, pool)
+        ws = tq.new_workspace(cache, w.num_seqs, w.num_q_heads, bt.shape[1], device=dev)
+        sets.append(dict(K=K0.clone() if i else K0, V=V0.clone() if i else V0, cache=cache, ws=ws,
+                         out=torch.empty((w.num_seqs, w.num_q_heads, 128), device=dev)))
+    torch.cuda.synchronize()
+
+    nvec = 2 * w.tokens * w.num_kv_heads
+    in_b, comp_b = bytes_per_vector(w.bits_k)
+    enc_bytes = nvec * (in_b + comp_b)
+    dec_bytes = w.tokens * w.num_kv_heads * 2 * comp_b     # K and V records + norms
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        s = sets[i % nsets]
+        if args.only != "decode":
+            if ev is not None:
+                ev[0].record(stream)
+            tq.tq_encode_kv(s["K"], s["V"], slots, w.bits_k, s["cache"], stream)
+            if ev is not None:
+                ev[1].record(stream)
+        if args.only != "encode":
+            if ev is not None:
+                ev[2].record(stream)
+            tq.tq_decode_attend(q, s["cache"], bt, lens, s["out"], s["ws"], stream=stream)
+            if ev is not None:
+                ev[3].record(stream)
+
+    print(f"# {nsets} rotating sets of {set_bytes / 1e6:.1f} MB; warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    enc_ms = [e[0].elapsed_time(e[1]) for e in evs] if args.only != "decode" else [float("nan")]
+    dec_ms = [e[2].elapsed_time(e[3]) for e in evs] if args.only != "encode" else [float("nan")]
+    enc_s = float(np.mean(enc_ms)) / 1e3
+    dec_s = float(np.mean(dec_ms)) / 1e3
+    dec_gbps = dec_bytes / dec_s / 1e9
+    enc_gbps = enc_bytes / enc_s / 1e9
+    enc_vps = nvec / enc_s
+
+    kernels = {
+        "tq_encode": {"bound": "hbm", "achieved": round(enc_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                      "frac": round(enc_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": enc_bytes,
+                      "us_per_launch": round(enc_s * 1e6, 2), "median_us": round(float(np.median(enc_ms)) * 1e3, 2)},
+        "tq_decode_attend": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": dec_bytes,
+                             "us_per_launch": round(dec_s * 1e6, 2), "median_us": round(float(np.median(dec_ms)) * 1e3, 2)},
+    }
+    dom = "tq_encode" if enc_s >= dec_s else "tq_decode_attend"
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tf):
+        with open(tf) as f:
+            tj = json.load(f)
+        ent = tj.get(w.name, {}).get(dom)
+        if ent and ent.get("kernel_hash") == kernel_hash():
+            traffic = ent.get("hbm_bytes_per_launch")
+    roof = dict(kernels[dom])
+    roof["kernel"] = dom
+    roof["traffic"] = traffic
+    for k in ("bytes_per_launch", "us_per_launch", "median_us"):
+        roof.pop(k, None)
+
+    res = {
+        "metric": METRIC,
+        "value": round(dec_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "seq_len": w.seq_len,
+                   "num_kv_heads": w.num_kv_heads, "num_q_heads": w.num_q_heads, "head_dim": 128,
+                   "bits_k": w.bits_k, "bits_v": w.bits_v, "block_tokens": 16, "input": "bf16",
+                   "rotating_sets": nsets},
+        "decode_frac_hbm": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "encode_vectors_per_s": round(enc_vps, 1),
+        "encode_gbps": round(enc_gbps, 1),
+        "encode_frac_hbm": round(enc_gbps / HBM_PEAK_GBPS, 4),
+        "kernels": kernels,
+        "roofline": roof,
+        "wall_s_timed": round(t_wall, 4),
+    }
+    if args.only != "both":
+        res["only"] = args.only
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * tq.h - C ABI of libtq: rotation-preconditioned (TurboQuant-style) KV-cache
+ * compression for one AMD MI355X (gfx950).
+ *
+ * Sources of the operations (page titles as printed on the pages):
+ *   [P1] "TurboQuant: KV Cache Vector Quantization" (llm-engineer card):
+ *        three stages Split / Rotate / Codebook, online compression.
+ *   [P2] "TurboQuant: KV Cache Compression" (Bit-Axon docs): quantisation
+ *        function Q(K) = argmin over the codebook, dequantisation, attention
+ *        over the quantised cache softmax(Q K^T / sqrt(d_h)) V, planned API
+ *        TurboQuant(bits).compress / decompress.
+ *   [P3] OCTOPUS summary (aitrends.kr): Method steps 1-2 (norm/direction
+ *        split, R = H diag(s)), glossary entries "Walsh-Hadamard rotation" and
+ *        "Lloyd-Max quantization", contribution "Optional 1-bit QJL residual
+ *        for unbiased dot-product".
+ *   [P4] TurboQuant deep-dive blog (cell-devlog): Step 1 randomized Hadamard
+ *        transform (sign flip, Hadamard, 1/sqrt(d)); Step 2 compress_key
+ *        (fp16 magnitude + direction indices, 128*4+16 = 528 bits); the
+ *        TurboQuantConfig(key_bits, value_bits, hadamard_seed) example.
+ *
+ * Conventions for every entry point:
+ *   - Return value: TQ_OK (0) or a negative tq_status.  Nothing aborts and no
+ *     C++ exception crosses the ABI.  tq_last_error() gives a thread-local
+ *     text for the last failure on the calling thread.
+ *   - "device" pointers are HIP device memory on the current device, owned by
+ *     the caller; the library never frees them.  "host" pointers are ordinary
+ *     process memory.
+ *   - GPU work is enqueued on the caller's hipStream_t (passed as void*; NULL
+ *     is the default stream) and is asynchronous: the caller synchronises.
+ *     Argument checks are synchronous; kernel faults surface as HIP errors on
+ *     the stream and are reported as TQ_ERR_HIP by the next call that checks.
+ *   - Every array is densely packed in the stated row-major shape.
+ *   - Supported now: head dimension d = 128, bits in {2, 3, 4}, 16-token
+ *     blocks.  Other values return TQ_ERR_UNSUPPORTED.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_LAYOUT_VERSION 1
+#define TQ_BLOCK_TOKENS 16
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = -1,   /* null/negative/inconsistent argument        */
+  TQ_ERR_UNSUPPORTED = -2,   /* valid but not implemented (d, bits, block)  */
+  TQ_ERR_BITS_MISMATCH = -3, /* bits argument differs from the cache's      */
+  TQ_ERR_OOM = -4,           /* host allocation failed                      */
+  TQ_ERR_NO_DEVICE = -5,     /* no usable HIP device                        */
+  TQ_ERR_HIP = -6,           /* a HIP runtime call or launch failed         */
+  TQ_ERR_WORKSPACE = -7      /* workspace missing or too small              */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
+
+/* Static text for a status code ("TQ_OK", ...). */
+const char* tq_status_string(int status);
+/* Detail text of the last failure on this thread ("" if none). */
+const char* tq_last_error(void);
+/* Cache layout version implemented (TQ_LAYOUT_VERSION). */
+int tq_layout_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Seeded random rotation R = H diag(s) / sqrt(d)   ([P4] Step 1; [P3] Method
+ * step 2 and glossary "Walsh-Hadamard rotation").
+ * s_j = +1 if the top bit of the j-th SplitMix64 output for `seed` is 0, else
+ * -1 (SplitMix64: Steele, Lea & Flood 2014).  H is the Sylvester Hadamard
+ * matrix.  The object is host memory owned by the library, immutable, and
+ * freed by tq_rotation_destroy.  d must be a power of two in [2, 4096]. */
+typedef struct tq_rotation tq_rotation;
+int tq_make_rotation(uint64_t seed, int32_t d, tq_rotation** out);
+/* Copies the d signs (+1/-1) into host_out[d]. */
+int tq_rotation_signs(const tq_rotation* rot, int8_t* host_out);
+int32_t tq_rotation_dim(const tq_rotation* rot);
+void tq_rotation_destroy(tq_rotation* rot);
+
+/* ---------------------------------------------------------------------------
+ * Lloyd-Max codebook ([P3] glossary "Lloyd-Max quantization": alternating
+ * centroid / boundary updates minimising MSE for a 1-D density; [P3] key idea:
+ * per-coordinate Lloyd-Max on the rotated marginals).  The density is the
+ * coordinate marginal of a uniform unit vector in R^d,
+ * f(x) = K_d (1 - x^2)^((d-3)/2).  Outputs (host arrays):
+ *   centroids[2^bits]    fp32, ascending (code i <-> centroids[i]);
+ *   thresholds[2^bits-1] fp32 midpoints of adjacent fp32 centroids.
+ * Computed in float64 on the host, cached per (d, bits). bits in [1, 4]. */
+int tq_codebook(int32_t d, int32_t bits, float* centroids, float* thresholds);
+
+/* ---------------------------------------------------------------------------
+ * Compressed paged cache.  The pool is caller-owned device memory of
+ * tq_cache_bytes() bytes laid out (layout version 1) as
+ *   [num_blocks][num_kv_heads][block_bytes], 16 tokens per block;
+ *   block = K codes [16][d*bits_k/8] | V codes [16][d*bits_v/8] (bits_v > 0)
+ *         | gamma_K [16] fp16 | gamma_V [16] fp16 (bits_v > 0)
+ *         | (qjl) rho [16] fp16 | sign bits [16][d/8].
+ * A token's code record stores code j at bits [j*b, j*b+b) of the record read
+ * as a little-endian bit string; codes are ascending centroid ranks.  QJL sign
+ * bit j (bit j of the sign record) is 1 when (R' r)_j < 0. */
+typedef struct {
+  int32_t d;            /* head dimension (128)                                  */
+  int32_t num_kv_heads; /* >= 1                                                  */
+  int32_t bits_k;       /* 2..4                                                  */
+  int32_t bits_v;       /* 2..4, or 0 for a keys-only cache                      */
+  int32_t qjl;          /* 0/1: 1-bit QJL residual sidecar on keys               */
+  int32_t block_size;   /* must be 16                                            */
+  int64_t num_blocks;   /* >= 1                                                  */
+  const tq_rotation* rot;     /* R (shared by keys and values); not owned        */
+  const tq_rotation* rot_qjl; /* R' (independent seed) if qjl, else NULL         */
+  int32_t layout_version;     /* TQ_LAYOUT_VERSION                               */
+} tq_cache_config;
+
+typedef struct {
+  int64_t block_bytes;     /* bytes of one (block, kv head)                       */
+  int64_t k_rec_bytes, v_rec_bytes;
+  int64_t off_k, off_v, off_gamma_k, off_gamma_v, off_rho, off_sign;
+  int64_t pool_bytes;
+} tq_cache_layout;
+
+/* Pool size in bytes (>= 0) or a negative tq_status. */
+int64_t tq_cache_bytes(const tq_cache_config* cfg);
+/* Region offsets of layout version 1 for cfg (host only). */
+int tq_cache_layout_query(const tq_cache_config* cfg, tq_cache_layout* out);
+
+/* Binds a descriptor to a device pool of tq_cache_bytes(cfg) bytes.  Host only:
+ * builds the codebooks and lookup tables; allocates no device memory.  The
+ * descriptor copies the rotation signs, so the rotations may be destroyed
+ * afterwards.  Freed by tq_cache_destroy (never frees the pool). */
+typedef struct tq_cache tq_cache;
+int tq_cache_create(const tq_cache_config* cfg, void* device_pool, tq_cache** out);
+void tq_cache_destroy(tq_cache* cache);
+
+/* ---------------------------------------------------------------------------
+ * Encode ([P1] Split / Rotate / Codebook; [P3] Method steps 1, 2, 6; [P2]
+ * Q(K) = argmin; [P4] Step 2 compress_key; optional [P3] QJL residual).
+ * For every token t with slot_mapping[t] >= 0 and every KV head h:
+ *   gamma = ||x||, y = R x / gamma, code_j = #{i : y_j > thresholds[i]},
+ *   stored with fp16(gamma) (round to nearest even, saturated at 65504) at
+ *   block slot/16, row slot%16.  With qjl: r = y - c[code], rho = fp16(||r||),
+ *   sign bits of R' r.
+ *   K, V: device [num_tokens][num_kv_heads][d] of `dtype`; V may be NULL only
+ *         for a keys-only cache (and must be NULL then).
+ *   slot_mapping: device int32[num_tokens]; -1 skips the token; other values
+ *         must be < num_blocks*16 (not checked on the device).
+ *   bits: must equal cache bits_k (and bits_v when V is given), else
+ *         TQ_ERR_BITS_MISMATCH.
+ * Decisions are taken in fp32.  A vector whose fp32 squared norm underflows
+ * to 0 is stored as the zero vector (codes 2^(b-1)-1, gamma 0).  Non-finite
+ * input is outside the contract. */
+int tq_encode_kv(const void* K, const void* V, int32_t dtype, int64_t num_tokens,
+                 const int32_t* slot_mapping, int32_t bits, tq_cache* cache,
+                 void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode-attend in the rotated frame ([P2] attention under quantisation;
+ * [P4] "RHT preserves inner products, attention can be computed without
+ * restoring"; [P3] contribution: the decoder never materialises K_hat).
+ *   q:            device [num_seqs][num_q_heads][d], TQ_F32/TQ_F16/TQ_BF16.
+ *                 Query head h reads KV head h / (num_q_heads/num_kv_heads);
+ *                 num_q_heads must be a multiple of num_kv_heads with a group
+ *                 of at most 16.
+ *   block_tables: device int32[num_seqs][max_blocks_per_seq] physical blocks.
+ *   seq_lens:     device int32[num_seqs], each in [0, max_blocks_per_seq*16].
+ *   scale:        logit scale; <= 0 selects 1/sqrt(d).
+ *   out:          device f32 [num_seqs][num_q_heads][d]:
+ *                 o = R^T( sum_t softmax_t(s) gamma_v,t c[codes_v,t] ) with
+ *                 s_t = scale * gamma_k,t * <R q, c[codes_k,t]> (+ QJL term
+ *                 scale*gamma_k,t*rho_t*sqrt(pi/2)/sqrt(d)*<sign_t, R' R q>).
+ *                 A sequence of length 0 gets o = 0.
+ *   logits_out:   NULL or device f32 [num_seqs][num_q_heads][max_blocks_per_seq*16];
+ *                 receives s_t for t < seq_len (other entries untouched).
+ *   workspace:    device memory of tq_decode_workspace_bytes() bytes.  Its
+ *                 counter region must be zero before the first call (a zero
+ *                 filled buffer is fine); every call leaves it zero again.
+ *                 Calls that share a workspace must not overlap in time.
+ * Requires a cache with values (bits_v > 0). */
+int64_t tq_decode_workspace_bytes(const tq_cache* cache, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_blocks_per_seq);
+int tq_decode_attend(const void* q, int32_t q_dtype, const tq_cache* cache,
+                     const int32_t* block_tables, const int32_t* seq_lens,
+                     int32_t num_seqs, int32_t num_q_heads,
+                     int32_t max_blocks_per_seq, float scale, float* out,
+                     float* logits_out, void* workspace, int64_t workspace_bytes,
+                     void* hip_stream);
+
+/* Keys-only scores ([P2] Q K_hat^T / sqrt(d_h); [P4] attention logits):
+ * logits_out device f32 [num_seqs][num_q_heads][max_blocks_per_seq*16],
+ * s_t as in tq_decode_attend for t < seq_len.  Works on any cache. */
+int tq_decode_logits(const void* q, int32_t q_dtype, const tq_cache* cache,
+                     const int32_t* block_tables, const int32_t* seq_lens,
+                     int32_t num_seqs, int32_t num_q_heads,
+                     int32_t max_blocks_per_seq, float scale, float* logits_out,
+                     void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Reconstruct cached vectors in the original frame ([P2] K_hat = DQ(K_q);
+ * [P4] Step 2 decompress_key): x_hat = fp16 gamma * R^T c[codes].
+ *   slots: device int32[n]; which: 0 = keys, 1 = values;
+ *   out:   device f32 [n][num_kv_heads][d]. */
+int tq_reconstruct(const tq_cache* cache, const int32_t* slots, int64_t n,
+                   int32_t which, float* out, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H_ */

@@ -1,0 +1,303 @@
+// tq_decode: attention of one decode query per sequence over the compressed
+// paged cache, computed in the rotated frame, plus the keys-only logits path.
+//
+// Method: Bit-Axon "TurboQuant: KV Cache Compression", attention under
+// quantisation softmax(Q K_hat^T / sqrt(d_h)) V_hat; deep-dive blog Step 1
+// ("RHT is orthogonal, inner products and attention scores are preserved, so
+// attention can be computed right after the transform without restoring");
+// OCTOPUS summary contributions (the decoder never materialises K_hat; the
+// optional QJL residual adds a correction to q^T k_hat).
+//
+// In the rotated frame <q, k_hat_t> = gamma_t <R q, c[codes_t]>, so q is
+// rotated once, every logit is a centroid-lookup dot product, and the value
+// sum o_rot = sum_t p_t gamma_v,t c[codes_v,t] is rotated back once:
+// o = R^T o_rot = D H o_rot / sqrt(d).
+//
+// Grid: (split, kv-head slice, sequence).  A workgroup (256 threads = 16 rows
+// of 16 lanes) owns up to 8 query heads of one KV head and a contiguous range
+// of blocks of one sequence.  Lane p of a row handles coordinates 8p..8p+7.
+//   A. logits: each row takes one token at a time; per-lane partial dot
+//      products are summed over the row with DPP; scores go to LDS.
+//   B. per head: max and exp-sum over the split (one row per head).
+//   C. values: each row accumulates p_t * gamma_v * c[codes] for its tokens.
+//   D. rows are reduced (shuffles inside a wave, LDS across waves), the
+//      split's (m, l, o_rot) goes to the workspace, and the last workgroup of
+//      the (sequence, slice) to arrive merges all splits, applies R^T and
+//      writes the output (fixed merge order: deterministic results).
+
+#include "tq_device.h"
+
+namespace tq {
+
+constexpr int kMaxSplitTokens = 1024;
+
+template <int DT>
+__device__ __forceinline__ void load_q8(const DecodeArgs& a, int64_t elem, float (&x)[8]) {
+  load8<DT>(a.q, elem, x);
+}
+
+template <int BK, int BV, bool QJL, int GMAX, bool ATTEND>
+__global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a, int ns, int gs) {
+  __shared__ float s_q[GMAX][kD];
+  __shared__ float s_w[QJL ? GMAX : 1][kD];
+  __shared__ float s_ck[16];
+  __shared__ float s_cv[16];
+  __shared__ float s_p[ATTEND ? kMaxSplitTokens * GMAX : 1];
+  __shared__ float s_ml[2][GMAX];
+  __shared__ float s_red[ATTEND ? 4 : 1][GMAX][kD];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int r = tid >> 4, p = tid & 15;
+  const int split = blockIdx.x, unit = blockIdx.y, n = blockIdx.z;
+  const int h = unit / ns, slice = unit - h * ns;
+  const int g0 = slice * gs;
+  const int gcount = min(gs, a.group - g0);
+  const int seq_len = max(0, min(a.seq_lens[n], a.max_blocks * kBlock));
+  const int t0 = split * a.blocks_per_split * kBlock;
+  const int t1 = min(seq_len, t0 + a.blocks_per_split * kBlock);
+  const FwhtLane fc = fwht_lane(p);
+  const int64_t Hq = a.num_q_heads;
+
+  if (tid < 16) {
+    s_ck[tid] = a.cent_k[tid];
+    s_cv[tid] = a.cent_v[tid];
+  }
+
+  // ---- D0: rotate this slice's queries, q_rot = H D q / sqrt(d) (and R' q_rot)
+  if (r < gcount) {
+    const int64_t hq = (int64_t)h * a.group + g0 + r;
+    const int ell = perm16(p);
+    float x[8];
+    const int64_t elem = ((int64_t)n * Hq + hq) * kD + 8 * ell;
+    if (a.q_dtype == 0) load_q8<0>(a, elem, x);
+    else if (a.q_dtype == 1) load_q8<1>(a, elem, x);
+    else load_q8<2>(a, elem, x);
+    const uint32_t sb = sign_byte(a.rot, ell);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = flip(x[e], sb, e);
+    fwht_row(x, fc);
+    const float sc = fc.sig * kInvSqrtD;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] *= sc;
+      s_q[r][8 * p + e] = x[e];
+    }
+    if constexpr (QJL) {
+      const uint32_t qb = sign_byte(a.rot_qjl, p);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = flip(x[e], qb, e);
+      fwht_row(x, fc);
+      const int lo = perm16(p);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_w[r][8 * lo + e] = x[e] * sc;
+    }
+  }
+  __syncthreads();
+
+  float qreg[GMAX][8];
+  float wreg[QJL ? GMAX : 1][8];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qreg[g][e] = g < gcount ? s_q[g][8 * p + e] : 0.f;
+      if constexpr (QJL) wreg[g][e] = g < gcount ? s_w[g][8 * p + e] : 0.f;
+    }
+
+  const int32_t* btab = a.block_tables + (int64_t)n * a.max_blocks;
+  const int64_t Hkv = a.num_kv_heads;
+
+  // ---- A: logits
+  for (int tok = t0 + r; tok < t1; tok += 16) {
+    int blk = btab[tok >> 4];
+    blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
+    const int row = tok & 15;
+    const uint8_t* base = a.pool + ((int64_t)blk * Hkv + h) * a.lay.block_bytes;
+    const uint32_t cw = load_codes8<BK>(base + a.lay.off_k + (int64_t)row * a.lay.k_rec, p);
+    float c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = s_ck[(cw >> (BK * e)) & ((1u << BK) - 1)];
+    const float gk = load_half(base + a.lay.off_gk + 2 * row);
+    float qj_rho = 0.f;
+    uint32_t sbits = 0;
+    if constexpr (QJL) {
+      sbits = base[a.lay.off_sign + row * 16 + p];
+      qj_rho = load_half(base + a.lay.off_rho + 2 * row) * (kSqrtHalfPi * kInvSqrtD);
+    }
+    float mine = 0.f;
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(c[e], qreg[g][e], dot);
+      dot = row_sum(dot);
+      float sg = a.scale * gk * dot;
+      if constexpr (QJL) {
+        float qd = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qd += flip(wreg[g][e], sbits, e);
+        qd = row_sum(qd);
+        sg = __builtin_fmaf(a.scale * gk * qj_rho, qd, sg);
+      }
+      if (p == g) mine = sg;
+    }
+    if (p < gcount) {
+      if (a.logits)
+        a.logits[((int64_t)n * Hq + (int64_t)h * a.group + g0 + p) * a.logits_stride + tok] = mine;
+      if constexpr (ATTEND) s_p[(tok - t0) * GMAX + p] = mine;
+    }
+  }
+  if constexpr (!ATTEND) return;
+  __syncthreads();
+
+  // ---- B: per-head max / exp-sum over the split
+  const int ntok = max(0, t1 - t0);
+  if (r < gcount) {
+    float m = -INFINITY;
+    for (int t = p; t < ntok; t += 16) m = fmaxf(m, s_p[t * GMAX + r]);
+    m = row_max(m);
+    float l = 0.f;
+    for (int t = p; t < ntok; t += 16) {
+      const float e = __expf(s_p[t * GMAX + r] - m);
+      s_p[t * GMAX + r] = e;
+      l += e;
+    }
+    l = row_sum(l);
+    if (p == 0) {
+      s_ml[0][r] = m;
+      s_ml[1][r] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- C: values
+  float acc[GMAX][8];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+  for (int tok = t0 + r; tok < t1; tok += 16) {
+    int blk = btab[tok >> 4];
+    blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
+    const int row = tok & 15;
+    const uint8_t* base = a.pool + ((int64_t)blk * Hkv + h) * a.lay.block_bytes;
+    const uint32_t cw = load_codes8<BV>(base + a.lay.off_v + (int64_t)row * a.lay.v_rec, p);
+    const float gv = load_half(base + a.lay.off_gv + 2 * row);
+    float c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = s_cv[(cw >> (BV * e)) & ((1u << BV) - 1)];
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      const float pw = s_p[(tok - t0) * GMAX + g] * gv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[g][e] = __builtin_fmaf(pw, c[e], acc[g][e]);
+    }
+  }
+
+  // ---- D: reduce the 16 rows (4 per wave, then 4 waves)
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[g][e];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      acc[g][e] = v;
+    }
+  const int wave = tid >> 6;
+  if ((tid & 63) < 16) {
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_red[wave][g][8 * p + e] = acc[g][e];
+  }
+  __syncthreads();
+  const int64_t nsplit = a.num_splits;
+  float* part_base = a.partials + (((int64_t)n * Hkv + h) * nsplit) * a.group * 130;
+  for (int i = tid; i < gcount * kD; i += 256) {
+    const int g = i / kD, j = i - g * kD;
+    const float v = s_red[0][g][j] + s_red[1][g][j] + s_red[2][g][j] + s_red[3][g][j];
+    part_base[((int64_t)split * a.group + g0 + g) * 130 + j] = v;
+  }
+  if (tid < gcount) {
+    float* pp = part_base + ((int64_t)split * a.group + g0 + tid) * 130;
+    pp[128] = s_ml[0][tid];
+    pp[129] = s_ml[1][tid];
+  }
+
+  // ---- last workgroup of this (sequence, KV head, slice) merges the splits
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t* ctr = a.counters + ((int64_t)n * Hkv + h) * ns + slice;
+    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old == (uint32_t)(nsplit - 1)) ? 1 : 0;
+    if (s_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  if (r < gcount) {
+    const int g = g0 + r;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) {
+      const float* pp = part_base + ((int64_t)s * a.group + g) * 130;
+      if (pp[129] > 0.f) M = fmaxf(M, pp[128]);
+    }
+    float Lsum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nsplit; ++s) {
+      const float* pp = part_base + ((int64_t)s * a.group + g) * 130;
+      const float l = pp[129];
+      if (!(l > 0.f)) continue;
+      const float w = __expf(pp[128] - M);
+      Lsum = __builtin_fmaf(l, w, Lsum);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(w, pp[8 * p + e], o[e]);
+    }
+    const float invl = Lsum > 0.f ? 1.f / Lsum : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= invl;
+    // o = D H o_rot / sqrt(d): natural input leaves lane p with output lane perm16(p)
+    fwht_row(o, fc);
+    const int lo = perm16(p);
+    const uint32_t sb = sign_byte(a.rot, lo);
+    float* dst = a.out + ((int64_t)n * Hq + (int64_t)h * a.group + g) * kD + 8 * lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = flip(o[e] * fc.sig * kInvSqrtD, sb, e);
+  }
+}
+
+template <int BK, int BV, bool QJL, bool ATTEND>
+static int launch_g(const DecodeArgs& a, int ns, int gs, hipStream_t s) {
+  dim3 grid((unsigned)a.num_splits, (unsigned)(a.num_kv_heads * ns), (unsigned)a.num_seqs);
+  if (gs <= 1) hipLaunchKernelGGL((decode_kernel<BK, BV, QJL, 1, ATTEND>), grid, dim3(256), 0, s, a, ns, gs);
+  else if (gs <= 2) hipLaunchKernelGGL((decode_kernel<BK, BV, QJL, 2, ATTEND>), grid, dim3(256), 0, s, a, ns, gs);
+  else if (gs <= 4) hipLaunchKernelGGL((decode_kernel<BK, BV, QJL, 4, ATTEND>), grid, dim3(256), 0, s, a, ns, gs);
+  else hipLaunchKernelGGL((decode_kernel<BK, BV, QJL, 8, ATTEND>), grid, dim3(256), 0, s, a, ns, gs);
+  return (int)hipGetLastError();
+}
+
+template <int B, bool ATTEND>
+static int launch_b(const DecodeArgs& a, bool qjl, int ns, int gs, hipStream_t s) {
+  if (qjl) return launch_g<B, ATTEND ? B : 2, true, ATTEND>(a, ns, gs, s);
+  return launch_g<B, ATTEND ? B : 2, false, ATTEND>(a, ns, gs, s);
+}
+
+int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int attend, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int ns = (a.group + 7) / 8;
+  const int gs = (a.group + ns - 1) / ns;
+  if (attend && bits_v != bits_k) return (int)hipErrorInvalidValue;
+  switch (bits_k) {
+    case 2: return attend ? launch_b<2, true>(a, qjl, ns, gs, s) : launch_b<2, false>(a, qjl, ns, gs, s);
+    case 3: return attend ? launch_b<3, true>(a, qjl, ns, gs, s) : launch_b<3, false>(a, qjl, ns, gs, s);
+    case 4: return attend ? launch_b<4, true>(a, qjl, ns, gs, s) : launch_b<4, false>(a, qjl, ns, gs, s);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+int decode_slices(int group) { return (group + 7) / 8; }
+
+}  // namespace tq

@@ -1,0 +1,582 @@
+// Host side of libtq: status/error handling, seeded rotations, the float64
+// Lloyd-Max codebook, cache layout, argument validation and kernel launch.
+// No device memory is owned here: per-cache tables travel in kernel arguments.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <limits>
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/tq.h"
+#include "tq_internal.h"
+
+struct tq_rotation {
+  uint64_t seed;
+  int32_t d;
+  std::vector<int8_t> signs;
+};
+
+struct tq_cache {
+  tq_cache_config cfg;
+  tq_cache_layout lay;
+  void* pool;
+  tq::SignMask rot;
+  tq::SignMask rot_qjl;
+  tq::CodecTables tab_k;
+  tq::CodecTables tab_v;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int hip_fail(int err, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(static_cast<hipError_t>(err));
+  return TQ_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- signs ----
+// SplitMix64 (Steele, Lea & Flood 2014; Vigna's splitmix64.c): the j-th output
+// of the generator seeded with `seed`.
+uint64_t splitmix64_nth(uint64_t seed, uint64_t j) {
+  uint64_t z = seed + (j + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// ------------------------------------------------------------- codebook ----
+// Coordinate marginal of a uniform unit vector in R^d:
+// f(x) = K_d (1 - x^2)^((d-3)/2).  With x = sin(phi) the mass of [0, x] is
+// K_d * J_{d-2}(phi), J_n(phi) = integral_0^phi cos^n, which obeys
+// J_n = cos^{n-1} sin / n + (n-1)/n J_{n-2} (J_0 = phi, J_1 = sin phi).
+double cos_power_integral(int n, double phi) {
+  const double s = std::sin(phi), c = std::cos(phi);
+  double j = (n % 2 == 0) ? phi : s;      // J_0 or J_1
+  double cpow = (n % 2 == 0) ? c : c * c; // cos^{k-1} for the first k
+  for (int k = (n % 2 == 0) ? 2 : 3; k <= n; k += 2) {
+    j = cpow * s / k + (double)(k - 1) / k * j;
+    cpow *= c * c;
+  }
+  return j;
+}
+
+struct Marginal {
+  int d;
+  double kd;   // normaliser
+  explicit Marginal(int d_) : d(d_) {
+    kd = 1.0 / (2.0 * cos_power_integral(d - 2, M_PI / 2));
+  }
+  // mass of [-1, x]
+  double cdf(double x) const {
+    if (x <= -1.0) return 0.0;
+    if (x >= 1.0) return 1.0;
+    return 0.5 + kd * cos_power_integral(d - 2, std::asin(x));
+  }
+  // integral of x f(x) over [a, b] = K_d/(d-1) [cos^{d-1}(asin a) - cos^{d-1}(asin b)]
+  double first_moment(double a, double b) const {
+    auto cp = [&](double x) {
+      x = std::fmin(1.0, std::fmax(-1.0, x));
+      return std::pow(std::sqrt(std::fmax(0.0, 1.0 - x * x)), d - 1);
+    };
+    return kd / (d - 1) * (cp(a) - cp(b));
+  }
+};
+
+// Lloyd-Max iteration in float64: thresholds at midpoints, centroids at cell
+// conditional means, centroids symmetrised every step, until no centroid
+// moves by more than 1e-14 of the largest (or the step stops shrinking at the
+// float64 noise floor).  The start is the quantiles at (i + 1/2) / 2^bits,
+// found by bisection on the CDF; the fixed point is unique for this
+// log-concave density, so the start only changes the step count.
+void lloyd_max(int d, int bits, std::vector<double>& c) {
+  const int n = 1 << bits;
+  Marginal m(d);
+  c.resize(n);
+  for (int i = 0; i < n; ++i) {
+    const double target = (i + 0.5) / n;
+    double lo = -1.0, hi = 1.0;
+    for (int k = 0; k < 80; ++k) {
+      const double mid = 0.5 * (lo + hi);
+      (m.cdf(mid) < target ? lo : hi) = mid;
+    }
+    c[i] = 0.5 * (lo + hi);
+  }
+  std::vector<double> nc(n), edge(n + 1), cdf(n + 1);
+  double best = 1e300;
+  int stale = 0;
+  for (int it = 0; it < 1000000; ++it) {
+    edge[0] = -1.0;
+    edge[n] = 1.0;
+    for (int i = 1; i < n; ++i) edge[i] = 0.5 * (c[i - 1] + c[i]);
+    for (int i = 0; i <= n; ++i) cdf[i] = m.cdf(edge[i]);
+    for (int i = 0; i < n; ++i)
+      nc[i] = m.first_moment(edge[i], edge[i + 1]) / (cdf[i + 1] - cdf[i]);
+    double moved = 0.0, cmax = 0.0;
+    for (int i = 0; i < n / 2; ++i) {
+      const double v = 0.5 * (nc[n - 1 - i] - nc[i]);   // symmetric pair
+      moved = std::fmax(moved, std::fabs(v - c[n - 1 - i]));
+      c[n - 1 - i] = v;
+      c[i] = -v;
+      cmax = std::fmax(cmax, v);
+    }
+    if (moved < 1e-14 * cmax) return;
+    if (moved < best) {
+      best = moved;
+      stale = 0;
+    } else if (++stale > 2000) {
+      return;
+    }
+  }
+}
+
+struct Codebook {
+  std::vector<float> c;
+  std::vector<float> t;
+};
+
+const Codebook* codebook_cached(int d, int bits) {
+  static std::mutex mu;
+  static std::map<std::pair<int, int>, Codebook> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(d, bits);
+  auto it = cache.find(key);
+  if (it != cache.end()) return &it->second;
+  std::vector<double> c;
+  lloyd_max(d, bits, c);
+  Codebook cb;
+  const int n = 1 << bits;
+  cb.c.resize(n);
+  cb.t.resize(n - 1);
+  for (int i = 0; i < n; ++i) cb.c[i] = (float)c[i];
+  for (int i = 0; i < n - 1; ++i)
+    cb.t[i] = (float)(0.5 * ((double)cb.c[i] + (double)cb.c[i + 1]));
+  return &cache.emplace(key, std::move(cb)).first->second;
+}
+
+// Bucket table of the encoder's threshold search (see tq::CodecTables).
+int build_codec_tables(int d, int bits, tq::CodecTables& tab) {
+  const Codebook* cb = codebook_cached(d, bits);
+  std::memset(&tab, 0, sizeof(tab));
+  tab.bits = bits;
+  const int n = 1 << bits, nt = n - 1;
+  for (int i = 0; i < n; ++i) tab.centroid[i] = cb->c[i];
+  for (int i = 0; i < nt; ++i) tab.threshold[i] = cb->t[i];
+  double gap = 1e300;
+  for (int i = 0; i + 1 < nt; ++i) gap = std::fmin(gap, (double)cb->t[i + 1] - cb->t[i]);
+  if (nt == 1) gap = 2.0 * std::fabs((double)cb->c[1]);
+  const double w = 0.5 * gap;
+  const double lo0 = (double)cb->t[0] - 2.0 * w;
+  double best_margin = -1.0;
+  float best_s = 0.f, best_o = 0.f;
+  int best_n = 0;
+  for (int ph = 0; ph < 64; ++ph) {
+    const double lo = lo0 - w * ph / 64.0;
+    const float S = (float)(1.0 / w);
+    const float O = (float)(-lo / w);
+    const double hi = (double)cb->t[nt - 1] + 2.0 * w;
+    const int nb = (int)std::ceil(((double)hi * S + O)) + 1;
+    if (nb > tq::kLutMax) continue;
+    double margin = 1e300;
+    for (int i = 0; i < nt; ++i) {
+      const double u = (double)cb->t[i] * S + O;   // position in bucket units
+      margin = std::fmin(margin, std::fabs(u - std::nearbyint(u)) / S);
+    }
+    if (margin > best_margin) {
+      best_margin = margin;
+      best_s = S;
+      best_o = O;
+      best_n = nb;
+    }
+  }
+  if (best_margin < 1e-6) return fail(TQ_ERR_UNSUPPORTED, "no bucket grid with enough threshold margin");
+  tab.lut_n = best_n;
+  tab.lut_scale = best_s;
+  tab.lut_offset = best_o;
+  for (int k = 0; k < best_n; ++k) {
+    const double e0 = ((double)k - best_o) / best_s;        // lower edge
+    const double e1 = ((double)k + 1 - best_o) / best_s;    // upper edge
+    int base = 0;
+    float thr = std::numeric_limits<float>::infinity();
+    for (int i = 0; i < nt; ++i) {
+      const double t = cb->t[i];
+      if (t < e0) ++base;
+      else if (t < e1) thr = cb->t[i];
+    }
+    tab.lut_base[k] = base;
+    tab.lut_thr[k] = thr;
+  }
+  // the clamped end buckets must not hold thresholds
+  if (tab.lut_base[0] != 0 || tab.lut_thr[0] != std::numeric_limits<float>::infinity() ||
+      tab.lut_thr[best_n - 1] != std::numeric_limits<float>::infinity() ||
+      tab.lut_base[best_n - 1] != nt)
+    return fail(TQ_ERR_UNSUPPORTED, "bucket table end check failed");
+  return TQ_OK;
+}
+
+int layout_of(const tq_cache_config* cfg, tq_cache_layout* lay) {
+  if (!cfg || !lay) return fail(TQ_ERR_INVALID_ARG, "null argument");
+  if (cfg->layout_version != TQ_LAYOUT_VERSION)
+    return fail(TQ_ERR_UNSUPPORTED, "layout_version must be 1");
+  if (cfg->d != tq::kD) return fail(TQ_ERR_UNSUPPORTED, "only d = 128 is supported");
+  if (cfg->block_size != tq::kBlock) return fail(TQ_ERR_UNSUPPORTED, "block_size must be 16");
+  if (cfg->num_kv_heads < 1) return fail(TQ_ERR_INVALID_ARG, "num_kv_heads < 1");
+  if (cfg->num_blocks < 1) return fail(TQ_ERR_INVALID_ARG, "num_blocks < 1");
+  if (cfg->bits_k < 2 || cfg->bits_k > 4) return fail(TQ_ERR_UNSUPPORTED, "bits_k must be 2..4");
+  if (cfg->bits_v != 0 && (cfg->bits_v < 2 || cfg->bits_v > 4))
+    return fail(TQ_ERR_UNSUPPORTED, "bits_v must be 0 or 2..4");
+  if (cfg->bits_v != 0 && cfg->bits_v != cfg->bits_k)
+    return fail(TQ_ERR_UNSUPPORTED, "bits_v must be 0 or equal to bits_k");
+  if (cfg->qjl != 0 && cfg->qjl != 1) return fail(TQ_ERR_INVALID_ARG, "qjl must be 0/1");
+  const int64_t B = tq::kBlock, d = cfg->d;
+  lay->k_rec_bytes = d * cfg->bits_k / 8;
+  lay->v_rec_bytes = d * cfg->bits_v / 8;
+  lay->off_k = 0;
+  lay->off_v = B * lay->k_rec_bytes;
+  lay->off_gamma_k = lay->off_v + B * lay->v_rec_bytes;
+  lay->off_gamma_v = lay->off_gamma_k + 2 * B;
+  lay->off_rho = lay->off_gamma_v + (cfg->bits_v > 0 ? 2 * B : 0);
+  lay->off_sign = lay->off_rho + 2 * B;
+  lay->block_bytes = lay->off_rho + (cfg->qjl ? 2 * B + B * d / 8 : 0);
+  const int64_t per_block = lay->block_bytes * cfg->num_kv_heads;
+  if (cfg->num_blocks > std::numeric_limits<int64_t>::max() / per_block)
+    return fail(TQ_ERR_INVALID_ARG, "pool size overflows int64");
+  lay->pool_bytes = per_block * cfg->num_blocks;
+  return TQ_OK;
+}
+
+void to_mask(const std::vector<int8_t>& s, tq::SignMask& m) {
+  std::memset(&m, 0, sizeof(m));
+  for (int j = 0; j < tq::kD; ++j)
+    if (s[j] < 0) m.neg[j / 32] |= 1u << (j % 32);
+}
+
+int check_device() {
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    return fail(TQ_ERR_NO_DEVICE, "no HIP device");
+  }
+  return TQ_OK;
+}
+
+int blocks_per_split_for(const tq_cache* c, int32_t num_seqs, int32_t group, int32_t max_blocks) {
+  int64_t work = (int64_t)max_blocks * num_seqs * c->cfg.num_kv_heads;
+  int64_t bps = (work + 1023) / 1024;
+  const int cap = group > 8 ? 32 : 64;
+  if (bps < 4) bps = 4;
+  if (bps > cap) bps = cap;
+  if (const char* env = std::getenv("TQ_BLOCKS_PER_SPLIT")) {
+    const int v = std::atoi(env);
+    if (v >= 1 && v <= cap) bps = v;
+  }
+  return (int)bps;
+}
+
+int validate_decode(const void* q, int32_t q_dtype, const tq_cache* cache,
+                    const int32_t* block_tables, const int32_t* seq_lens,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks) {
+  if (!cache) return fail(TQ_ERR_INVALID_ARG, "null cache");
+  if (num_seqs < 0 || max_blocks < 0) return fail(TQ_ERR_INVALID_ARG, "negative size");
+  if (num_seqs > 0 && (!q || !block_tables || !seq_lens))
+    return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  if (q_dtype != TQ_F32 && q_dtype != TQ_F16 && q_dtype != TQ_BF16)
+    return fail(TQ_ERR_INVALID_ARG, "bad q dtype");
+  const int hkv = cache->cfg.num_kv_heads;
+  if (num_q_heads < hkv || num_q_heads % hkv != 0)
+    return fail(TQ_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (num_q_heads / hkv > tq::kMaxGroup)
+    return fail(TQ_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
+  return TQ_OK;
+}
+
+void fill_decode_args(tq::DecodeArgs& a, const void* q, int32_t q_dtype, const tq_cache* c,
+                      const int32_t* bt, const int32_t* sl, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t max_blocks, float scale) {
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.pool = static_cast<const uint8_t*>(c->pool);
+  a.block_tables = bt;
+  a.seq_lens = sl;
+  a.lay.block_bytes = c->lay.block_bytes;
+  a.lay.off_k = c->lay.off_k;
+  a.lay.off_v = c->lay.off_v;
+  a.lay.off_gk = c->lay.off_gamma_k;
+  a.lay.off_gv = c->lay.off_gamma_v;
+  a.lay.off_rho = c->lay.off_rho;
+  a.lay.off_sign = c->lay.off_sign;
+  a.lay.k_rec = (int32_t)c->lay.k_rec_bytes;
+  a.lay.v_rec = (int32_t)c->lay.v_rec_bytes;
+  a.num_blocks = c->cfg.num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = c->cfg.num_kv_heads;
+  a.group = num_q_heads / c->cfg.num_kv_heads;
+  a.max_blocks = max_blocks;
+  a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)c->cfg.d);
+  a.rot = c->rot;
+  a.rot_qjl = c->rot_qjl;
+  for (int i = 0; i < 16; ++i) {
+    a.cent_k[i] = i < (1 << c->cfg.bits_k) ? c->tab_k.centroid[i] : 0.f;
+    a.cent_v[i] = (c->cfg.bits_v > 0 && i < (1 << c->cfg.bits_v)) ? c->tab_v.centroid[i] : 0.f;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_status_string(int status) {
+  switch (status) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_ERR_INVALID_ARG: return "TQ_ERR_INVALID_ARG";
+    case TQ_ERR_UNSUPPORTED: return "TQ_ERR_UNSUPPORTED";
+    case TQ_ERR_BITS_MISMATCH: return "TQ_ERR_BITS_MISMATCH";
+    case TQ_ERR_OOM: return "TQ_ERR_OOM";
+    case TQ_ERR_NO_DEVICE: return "TQ_ERR_NO_DEVICE";
+    case TQ_ERR_HIP: return "TQ_ERR_HIP";
+    case TQ_ERR_WORKSPACE: return "TQ_ERR_WORKSPACE";
+    default: return "TQ_ERR_UNKNOWN";
+  }
+}
+
+const char* tq_last_error(void) { return g_last_error.c_str(); }
+
+int tq_layout_version(void) { return TQ_LAYOUT_VERSION; }
+
+int tq_make_rotation(uint64_t seed, int32_t d, tq_rotation** out) {
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "null out");
+  *out = nullptr;
+  if (d < 2 || d > 4096 || (d & (d - 1))) return fail(TQ_ERR_INVALID_ARG, "d must be a power of two in [2, 4096]");
+  tq_rotation* r = new (std::nothrow) tq_rotation;
+  if (!r) return fail(TQ_ERR_OOM, "out of host memory");
+  r->seed = seed;
+  r->d = d;
+  try {
+    r->signs.resize(d);
+  } catch (...) {
+    delete r;
+    return fail(TQ_ERR_OOM, "out of host memory");
+  }
+  for (int j = 0; j < d; ++j) r->signs[j] = (splitmix64_nth(seed, j) >> 63) ? -1 : 1;
+  *out = r;
+  return TQ_OK;
+}
+
+int tq_rotation_signs(const tq_rotation* rot, int8_t* host_out) {
+  if (!rot || !host_out) return fail(TQ_ERR_INVALID_ARG, "null argument");
+  std::memcpy(host_out, rot->signs.data(), rot->d);
+  return TQ_OK;
+}
+
+int32_t tq_rotation_dim(const tq_rotation* rot) { return rot ? rot->d : 0; }
+
+void tq_rotation_destroy(tq_rotation* rot) { delete rot; }
+
+int tq_codebook(int32_t d, int32_t bits, float* centroids, float* thresholds) {
+  if (!centroids || !thresholds) return fail(TQ_ERR_INVALID_ARG, "null output");
+  if (d < 4 || d > 65536) return fail(TQ_ERR_INVALID_ARG, "d out of range [4, 65536]");
+  if (bits < 1 || bits > 4) return fail(TQ_ERR_UNSUPPORTED, "bits must be 1..4");
+  const Codebook* cb = codebook_cached(d, bits);
+  std::memcpy(centroids, cb->c.data(), sizeof(float) * cb->c.size());
+  std::memcpy(thresholds, cb->t.data(), sizeof(float) * cb->t.size());
+  return TQ_OK;
+}
+
+int64_t tq_cache_bytes(const tq_cache_config* cfg) {
+  tq_cache_layout lay;
+  const int s = layout_of(cfg, &lay);
+  return s != TQ_OK ? s : lay.pool_bytes;
+}
+
+int tq_cache_layout_query(const tq_cache_config* cfg, tq_cache_layout* out) {
+  return layout_of(cfg, out);
+}
+
+int tq_cache_create(const tq_cache_config* cfg, void* device_pool, tq_cache** out) {
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "null out");
+  *out = nullptr;
+  tq_cache_layout lay;
+  int s = layout_of(cfg, &lay);
+  if (s != TQ_OK) return s;
+  if (!device_pool) return fail(TQ_ERR_INVALID_ARG, "null device pool");
+  if (reinterpret_cast<uintptr_t>(device_pool) % 16 != 0)
+    return fail(TQ_ERR_INVALID_ARG, "device pool must be 16-byte aligned");
+  if (!cfg->rot || cfg->rot->d != cfg->d) return fail(TQ_ERR_INVALID_ARG, "rotation missing or of wrong dimension");
+  if (cfg->qjl && (!cfg->rot_qjl || cfg->rot_qjl->d != cfg->d))
+    return fail(TQ_ERR_INVALID_ARG, "qjl needs rot_qjl of dimension d");
+  tq_cache* c = new (std::nothrow) tq_cache;
+  if (!c) return fail(TQ_ERR_OOM, "out of host memory");
+  std::memset(c, 0, sizeof(*c));
+  c->cfg = *cfg;
+  c->cfg.rot = nullptr;       // signs are copied; the rotations may be freed
+  c->cfg.rot_qjl = nullptr;
+  c->lay = lay;
+  c->pool = device_pool;
+  to_mask(cfg->rot->signs, c->rot);
+  if (cfg->qjl) to_mask(cfg->rot_qjl->signs, c->rot_qjl);
+  if ((s = build_codec_tables(cfg->d, cfg->bits_k, c->tab_k)) != TQ_OK ||
+      (cfg->bits_v > 0 && (s = build_codec_tables(cfg->d, cfg->bits_v, c->tab_v)) != TQ_OK)) {
+    delete c;
+    return s;
+  }
+  *out = c;
+  return TQ_OK;
+}
+
+void tq_cache_destroy(tq_cache* cache) { delete cache; }
+
+int tq_encode_kv(const void* K, const void* V, int32_t dtype, int64_t num_tokens,
+                 const int32_t* slot_mapping, int32_t bits, tq_cache* cache, void* hip_stream) {
+  if (!cache) return fail(TQ_ERR_INVALID_ARG, "null cache");
+  if (num_tokens < 0) return fail(TQ_ERR_INVALID_ARG, "num_tokens < 0");
+  if (dtype != TQ_F32 && dtype != TQ_F16 && dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad dtype");
+  const tq_cache_config& cfg = cache->cfg;
+  if (cfg.bits_v == 0 && V) return fail(TQ_ERR_INVALID_ARG, "V given for a keys-only cache");
+  if (cfg.bits_v > 0 && !V) return fail(TQ_ERR_INVALID_ARG, "V missing for a cache with values");
+  if (bits != cfg.bits_k || (V && bits != cfg.bits_v))
+    return fail(TQ_ERR_BITS_MISMATCH, "bits differs from the cache's bit width");
+  if (num_tokens == 0) return TQ_OK;
+  if (!K || !slot_mapping) return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  const int64_t nvec = num_tokens * cfg.num_kv_heads;
+  if (nvec / cfg.num_kv_heads != num_tokens || nvec >= ((int64_t)1 << 31))
+    return fail(TQ_ERR_INVALID_ARG, "too many vectors");
+  int s = check_device();
+  if (s != TQ_OK) return s;
+  tq::EncodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.slot_mapping = slot_mapping;
+  a.pool = static_cast<uint8_t*>(cache->pool);
+  a.num_vectors = nvec;
+  a.num_slots = cfg.num_blocks * tq::kBlock;
+  a.block_bytes = cache->lay.block_bytes;
+  a.rho_off = cache->lay.off_rho;
+  a.sign_off = cache->lay.off_sign;
+  a.num_heads = cfg.num_kv_heads;
+  a.div_heads = tq::make_fast_div((uint32_t)cfg.num_kv_heads);
+  a.rot = cache->rot;
+  a.rot_qjl = cache->rot_qjl;
+  a.tab = cache->tab_k;
+  a.stream[0] = {K, cache->lay.off_k, cache->lay.off_gamma_k, (int32_t)cache->lay.k_rec_bytes, cfg.qjl};
+  a.stream[1] = {V, cache->lay.off_v, cache->lay.off_gamma_v, (int32_t)cache->lay.v_rec_bytes, 0};
+  const int streams = V ? 2 : 1;
+  int err = tq::launch_encode(a, streams, dtype, hip_stream);
+  if (err != 0) return hip_fail(err, "encode launch");
+  return TQ_OK;
+}
+
+int64_t tq_decode_workspace_bytes(const tq_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_blocks_per_seq) {
+  if (!cache || num_seqs < 0 || max_blocks_per_seq < 0 || num_q_heads < cache->cfg.num_kv_heads ||
+      num_q_heads % cache->cfg.num_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARG, "bad workspace query");
+  const int group = num_q_heads / cache->cfg.num_kv_heads;
+  const int bps = blocks_per_split_for(cache, num_seqs, group, max_blocks_per_seq);
+  const int64_t splits = std::max<int64_t>(1, (max_blocks_per_seq + bps - 1) / bps);
+  const int64_t nsh = (int64_t)num_seqs * cache->cfg.num_kv_heads;
+  const int64_t counters = ((nsh * tq::decode_slices(group) * 4 + 255) / 256) * 256;
+  return counters + nsh * splits * group * 130 * 4;
+}
+
+int tq_decode_attend(const void* q, int32_t q_dtype, const tq_cache* cache,
+                     const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t max_blocks_per_seq, float scale, float* out,
+                     float* logits_out, void* workspace, int64_t workspace_bytes, void* hip_stream) {
+  int s = validate_decode(q, q_dtype, cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                          max_blocks_per_seq);
+  if (s != TQ_OK) return s;
+  if (cache->cfg.bits_v == 0) return fail(TQ_ERR_INVALID_ARG, "decode_attend needs a cache with values");
+  if (num_seqs == 0) return TQ_OK;
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "null out");
+  const int64_t need = tq_decode_workspace_bytes(cache, num_seqs, num_q_heads, max_blocks_per_seq);
+  if (!workspace || workspace_bytes < need) return fail(TQ_ERR_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(TQ_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  if ((s = check_device()) != TQ_OK) return s;
+  tq::DecodeArgs a;
+  fill_decode_args(a, q, q_dtype, cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                   max_blocks_per_seq, scale);
+  a.out = out;
+  a.logits = logits_out;
+  a.logits_stride = (int64_t)max_blocks_per_seq * tq::kBlock;
+  a.blocks_per_split = blocks_per_split_for(cache, num_seqs, a.group, max_blocks_per_seq);
+  a.num_splits = std::max(1, (max_blocks_per_seq + a.blocks_per_split - 1) / a.blocks_per_split);
+  const int64_t nsh = (int64_t)num_seqs * cache->cfg.num_kv_heads;
+  const int64_t counters = ((nsh * tq::decode_slices(a.group) * 4 + 255) / 256) * 256;
+  a.counters = static_cast<uint32_t*>(workspace);
+  a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counters);
+  int err = tq::launch_decode(a, cache->cfg.bits_k, cache->cfg.bits_v, cache->cfg.qjl, 1, hip_stream);
+  if (err != 0) return hip_fail(err, "decode launch");
+  return TQ_OK;
+}
+
+int tq_decode_logits(const void* q, int32_t q_dtype, const tq_cache* cache,
+                     const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t max_blocks_per_seq, float scale,
+                     float* logits_out, void* hip_stream) {
+  int s = validate_decode(q, q_dtype, cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                          max_blocks_per_seq);
+  if (s != TQ_OK) return s;
+  if (num_seqs == 0 || max_blocks_per_seq == 0) return TQ_OK;
+  if (!logits_out) return fail(TQ_ERR_INVALID_ARG, "null logits_out");
+  if ((s = check_device()) != TQ_OK) return s;
+  tq::DecodeArgs a;
+  fill_decode_args(a, q, q_dtype, cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                   max_blocks_per_seq, scale);
+  a.logits = logits_out;
+  a.logits_stride = (int64_t)max_blocks_per_seq * tq::kBlock;
+  a.blocks_per_split = blocks_per_split_for(cache, num_seqs, a.group, max_blocks_per_seq);
+  a.num_splits = std::max(1, (max_blocks_per_seq + a.blocks_per_split - 1) / a.blocks_per_split);
+  int err = tq::launch_decode(a, cache->cfg.bits_k, 0, cache->cfg.qjl, 0, hip_stream);
+  if (err != 0) return hip_fail(err, "logits launch");
+  return TQ_OK;
+}
+
+int tq_reconstruct(const tq_cache* cache, const int32_t* slots, int64_t n, int32_t which,
+                   float* out, void* hip_stream) {
+  if (!cache) return fail(TQ_ERR_INVALID_ARG, "null cache");
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n < 0");
+  if (which != 0 && which != 1) return fail(TQ_ERR_INVALID_ARG, "which must be 0 (K) or 1 (V)");
+  if (which == 1 && cache->cfg.bits_v == 0) return fail(TQ_ERR_INVALID_ARG, "cache has no values");
+  if (n == 0) return TQ_OK;
+  if (!slots || !out) return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  if (n * cache->cfg.num_kv_heads >= ((int64_t)1 << 31)) return fail(TQ_ERR_INVALID_ARG, "too many vectors");
+  int s = check_device();
+  if (s != TQ_OK) return s;
+  tq::ReconArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.pool = static_cast<const uint8_t*>(cache->pool);
+  a.slots = slots;
+  a.out = out;
+  a.n_vectors = n * cache->cfg.num_kv_heads;
+  a.num_slots = cache->cfg.num_blocks * tq::kBlock;
+  a.block_bytes = cache->lay.block_bytes;
+  a.num_heads = cache->cfg.num_kv_heads;
+  a.div_heads = tq::make_fast_div((uint32_t)cache->cfg.num_kv_heads);
+  a.rot = cache->rot;
+  const tq::CodecTables& tab = which ? cache->tab_v : cache->tab_k;
+  a.bits = tab.bits;
+  for (int i = 0; i < 16; ++i) a.centroid[i] = tab.centroid[i];
+  a.rec_off = which ? cache->lay.off_v : cache->lay.off_k;
+  a.norm_off = which ? cache->lay.off_gamma_v : cache->lay.off_gamma_k;
+  a.rec_bytes = (int32_t)(which ? cache->lay.v_rec_bytes : cache->lay.k_rec_bytes);
+  int err = tq::launch_reconstruct(a, hip_stream);
+  if (err != 0) return hip_fail(err, "reconstruct launch");
+  return TQ_OK;
+}
+
+}  // extern "C"

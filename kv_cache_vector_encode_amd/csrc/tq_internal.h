@@ -1,0 +1,123 @@
+// Internal structures shared by the host code (tq_host.cpp) and the HIP
+// kernels.  Everything a kernel needs about a cache travels by value in its
+// kernel-argument struct (a few hundred bytes): codebooks, the bucket lookup
+// table of the threshold search, and the rotation signs as bit masks.
+#pragma once
+
+#include <stdint.h>
+
+namespace tq {
+
+constexpr int kD = 128;          // head dimension supported by the kernels
+constexpr int kBlock = 16;       // tokens per cache block
+constexpr int kLutMax = 96;      // buckets of the threshold-search table
+constexpr int kMaxGroup = 16;    // query heads per KV head
+
+// Codebook of one bit width, plus the bucket table used by the encoder's
+// threshold search: for y in bucket k = clamp(floor(y*lut_scale+lut_offset)),
+// code = lut_base[k] + (y > lut_thr[k]).  The host builds the grid so that a
+// bucket holds at most one threshold and every threshold sits at least 1e-6
+// away from a bucket edge; a y that rounds into a neighbouring bucket then
+// still gets the exact threshold count.
+struct CodecTables {
+  int32_t bits;
+  int32_t lut_n;
+  float lut_scale;
+  float lut_offset;
+  float centroid[16];           // ascending, fp32
+  float threshold[15];          // fp32 midpoints
+  float lut_thr[kLutMax];       // +inf when the bucket holds no threshold
+  int32_t lut_base[kLutMax];
+};
+
+// Rotation signs as a bit mask: bit j of neg[j/32] set <=> s_j = -1.
+struct SignMask {
+  uint32_t neg[kD / 32];
+};
+
+// Exact division by a runtime constant for numerators below 2^31.
+struct FastDiv {
+  uint32_t mul;
+  uint32_t shift;
+};
+
+inline FastDiv make_fast_div(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const unsigned __int128 num = (unsigned __int128)1 << (31 + l);
+  const uint64_t m = (uint64_t)((num + d - 1) / d);
+  return FastDiv{(uint32_t)m, 31 + l};
+}
+
+struct Layout {
+  int64_t block_bytes;
+  int64_t off_k, off_v, off_gk, off_gv, off_rho, off_sign;
+  int32_t k_rec, v_rec;
+};
+
+// ---------------------------------------------------------------- encode --
+struct EncodeStream {
+  const void* src;        // [tokens][heads][128]
+  int64_t rec_off;        // code region offset inside (block, head)
+  int64_t norm_off;       // fp16 norm region offset
+  int32_t rec_bytes;
+  int32_t qjl;            // 1: also write the QJL sidecar (keys only)
+};
+
+struct EncodeArgs {
+  EncodeStream stream[2];   // gridDim.y streams (K, then V)
+  const int32_t* slot_mapping;
+  uint8_t* pool;
+  int64_t num_vectors;      // tokens * heads
+  int64_t num_slots;        // num_blocks * 16; larger slots are skipped
+  int64_t block_bytes;
+  int64_t rho_off, sign_off;
+  int32_t num_heads;
+  FastDiv div_heads;
+  SignMask rot, rot_qjl;
+  CodecTables tab;
+};
+
+// ---------------------------------------------------------------- decode --
+struct DecodeArgs {
+  const void* q;            // [seqs][q_heads][128]
+  const uint8_t* pool;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* out;               // [seqs][q_heads][128] (attend)
+  float* logits;            // [seqs][q_heads][logits_stride] or null
+  float* partials;          // [seqs][kv_heads][splits][group][130]
+  uint32_t* counters;       // [seqs][kv_heads]
+  int64_t logits_stride;
+  Layout lay;
+  int64_t num_blocks;       // block-table entries outside [0, num_blocks) read as block 0
+  int32_t q_dtype;
+  int32_t num_seqs, num_q_heads, num_kv_heads, group;
+  int32_t max_blocks, blocks_per_split, num_splits;
+  float scale;
+  SignMask rot, rot_qjl;
+  float cent_k[16];
+  float cent_v[16];
+};
+
+// ----------------------------------------------------------- reconstruct --
+struct ReconArgs {
+  const uint8_t* pool;
+  const int32_t* slots;
+  float* out;               // [n][heads][128]
+  int64_t n_vectors;        // n * heads
+  int64_t num_slots;        // slots outside [0, num_slots) give zero vectors
+  int64_t rec_off, norm_off, block_bytes;
+  int32_t rec_bytes, bits, num_heads;
+  FastDiv div_heads;
+  SignMask rot;
+  float centroid[16];
+};
+
+// Launchers implemented in the .hip files; return a hipError_t value.
+int launch_encode(const EncodeArgs& a, int num_streams, int in_dtype, void* stream);
+int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int attend, void* stream);
+int decode_slices(int group);
+int launch_reconstruct(const ReconArgs& a, void* stream);
+
+}  // namespace tq

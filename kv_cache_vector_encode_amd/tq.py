@@ -1,0 +1,263 @@
+"""ctypes binding of libtq (include/tq.h): the same entry points, argument
+marshalling only.
+
+Device buffers are torch tensors on a ROCm device (torch supplies memory and
+streams; every step of the codec runs in libtq's HIP kernels).  Status codes
+other than TQ_OK raise ``TQError``.  The library is loaded from this package
+directory; if it is missing the import fails loudly (there is no fallback).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "tq.h")
+
+TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_BITS_MISMATCH = 0, -1, -2, -3
+TQ_ERR_OOM, TQ_ERR_NO_DEVICE, TQ_ERR_HIP, TQ_ERR_WORKSPACE = -4, -5, -6, -7
+TQ_F32, TQ_F16, TQ_BF16 = 0, 1, 2
+LAYOUT_VERSION = 1
+BLOCK = 16
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {status_string(status)} ({status}): {detail}")
+        self.status = status
+
+
+class CacheConfig(ctypes.Structure):
+    _fields_ = [
+        ("d", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("bits_k", ctypes.c_int32), ("bits_v", ctypes.c_int32),
+        ("qjl", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+        ("rot", ctypes.c_void_p), ("rot_qjl", ctypes.c_void_p),
+        ("layout_version", ctypes.c_int32),
+    ]
+
+
+class CacheLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "block_bytes", "k_rec_bytes", "v_rec_bytes", "off_k", "off_v", "off_gamma_k",
+        "off_gamma_v", "off_rho", "off_sign", "pool_bytes")]
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libtq.so not built ({LIB_PATH}); run python -m kv_cache_vector_encode_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "tq_last_error": (ctypes.c_char_p, []),
+            "tq_layout_version": (ctypes.c_int, []),
+            "tq_make_rotation": (ctypes.c_int, [ctypes.c_uint64, ctypes.c_int32, ctypes.POINTER(_P)]),
+            "tq_rotation_signs": (ctypes.c_int, [_P, _P]),
+            "tq_rotation_dim": (ctypes.c_int32, [_P]),
+            "tq_rotation_destroy": (None, [_P]),
+            "tq_codebook": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, _P]),
+            "tq_cache_bytes": (ctypes.c_int64, [ctypes.POINTER(CacheConfig)]),
+            "tq_cache_layout_query": (ctypes.c_int, [ctypes.POINTER(CacheConfig), ctypes.POINTER(CacheLayout)]),
+            "tq_cache_create": (ctypes.c_int, [ctypes.POINTER(CacheConfig), _P, ctypes.POINTER(_P)]),
+            "tq_cache_destroy": (None, [_P]),
+            "tq_encode_kv": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int64, _P, ctypes.c_int32, _P, _P]),
+            "tq_decode_workspace_bytes": (ctypes.c_int64, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
+            "tq_decode_attend": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_float, _P, _P, _P, ctypes.c_int64, _P]),
+            "tq_decode_logits": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_float, _P, _P]),
+            "tq_reconstruct": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/tq.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib().tq_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != TQ_OK:
+        raise TQError(status, where, lib().tq_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    m = {torch.float32: TQ_F32, torch.float16: TQ_F16, torch.bfloat16: TQ_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+# ----------------------------------------------------------------- rotation --
+
+class Rotation:
+    """Owns a tq_rotation* (freed on garbage collection)."""
+
+    def __init__(self, handle: int, seed: int, d: int):
+        self.handle, self.seed, self.d = handle, seed, d
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.tq_rotation_destroy(self.handle)
+            self.handle = None
+
+
+def tq_make_rotation(seed: int, d: int) -> Rotation:
+    h = _P()
+    _check(lib().tq_make_rotation(ctypes.c_uint64(seed & (2 ** 64 - 1)), d, ctypes.byref(h)), "tq_make_rotation")
+    return Rotation(h.value, seed, d)
+
+
+def tq_rotation_signs(rot: Rotation) -> np.ndarray:
+    out = np.empty(rot.d, dtype=np.int8)
+    _check(lib().tq_rotation_signs(rot.handle, out.ctypes.data), "tq_rotation_signs")
+    return out
+
+
+def tq_codebook(d: int, bits: int):
+    c = np.empty(1 << bits, dtype=np.float32)
+    t = np.empty((1 << bits) - 1, dtype=np.float32)
+    _check(lib().tq_codebook(d, bits, c.ctypes.data, t.ctypes.data), "tq_codebook")
+    return c, t
+
+
+# -------------------------------------------------------------------- cache --
+
+def make_config(num_kv_heads: int, num_blocks: int, bits_k: int, bits_v: int, rot: Rotation,
+                qjl: bool = False, rot_qjl: Rotation | None = None, d: int = 128) -> CacheConfig:
+    return CacheConfig(d, num_kv_heads, bits_k, bits_v, int(qjl), BLOCK, num_blocks,
+                       rot.handle if rot else None, rot_qjl.handle if rot_qjl else None,
+                       LAYOUT_VERSION)
+
+
+def tq_cache_bytes(cfg: CacheConfig) -> int:
+    n = lib().tq_cache_bytes(ctypes.byref(cfg))
+    if n < 0:
+        _check(int(n), "tq_cache_bytes")
+    return int(n)
+
+
+def tq_cache_layout_query(cfg: CacheConfig) -> CacheLayout:
+    lay = CacheLayout()
+    _check(lib().tq_cache_layout_query(ctypes.byref(cfg), ctypes.byref(lay)), "tq_cache_layout_query")
+    return lay
+
+
+class Cache:
+    """Owns a tq_cache* descriptor bound to a caller pool (kept alive here)."""
+
+    def __init__(self, handle: int, cfg: CacheConfig, pool, rots):
+        self.handle, self.cfg, self.pool, self._rots = handle, cfg, pool, rots
+        self.layout = tq_cache_layout_query(cfg)
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.tq_cache_destroy(self.handle)
+            self.handle = None
+
+
+def tq_cache_create(cfg: CacheConfig, pool) -> Cache:
+    h = _P()
+    _check(lib().tq_cache_create(ctypes.byref(cfg), _ptr(pool), ctypes.byref(h)), "tq_cache_create")
+    return Cache(h.value, cfg, pool, None)
+
+
+# ------------------------------------------------------------------- encode --
+
+def tq_encode_kv(K, V, slot_mapping, bits: int, cache: Cache, stream=None):
+    """K, V: device tensors [tokens][kv_heads][128] (V None for keys-only)."""
+    _check(lib().tq_encode_kv(_ptr(K), _ptr(V), _dtype_code(K), K.shape[0], _ptr(slot_mapping), bits,
+                              cache.handle, _stream(stream)), "tq_encode_kv")
+
+
+# ------------------------------------------------------------------- decode --
+
+def tq_decode_workspace_bytes(cache: Cache, num_seqs: int, num_q_heads: int, max_blocks_per_seq: int) -> int:
+    n = lib().tq_decode_workspace_bytes(cache.handle, num_seqs, num_q_heads, max_blocks_per_seq)
+    if n < 0:
+        _check(int(n), "tq_decode_workspace_bytes")
+    return int(n)
+
+
+def tq_decode_attend(q, cache: Cache, block_tables, seq_lens, out, workspace, logits_out=None,
+                     scale: float = 0.0, stream=None):
+    """q [seqs][q_heads][128]; block_tables int32 [seqs][max_blocks]; out f32
+    [seqs][q_heads][128]; workspace: uint8 tensor (zero before first use)."""
+    ns, hq, _ = q.shape
+    _check(lib().tq_decode_attend(_ptr(q), _dtype_code(q), cache.handle, _ptr(block_tables), _ptr(seq_lens),
+                                  ns, hq, block_tables.shape[1], scale, _ptr(out), _ptr(logits_out),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)), "tq_decode_attend")
+
+
+def tq_decode_logits(q, cache: Cache, block_tables, seq_lens, logits_out, scale: float = 0.0, stream=None):
+    ns, hq, _ = q.shape
+    _check(lib().tq_decode_logits(_ptr(q), _dtype_code(q), cache.handle, _ptr(block_tables), _ptr(seq_lens),
+                                  ns, hq, block_tables.shape[1], scale, _ptr(logits_out), _stream(stream)),
+           "tq_decode_logits")
+
+
+def tq_reconstruct(cache: Cache, slots, which: int, out, stream=None):
+    _check(lib().tq_reconstruct(cache.handle, _ptr(slots), slots.shape[0], which, _ptr(out), _stream(stream)),
+           "tq_reconstruct")
+
+
+# ------------------------------------------------------------------ helpers --
+
+def new_cache(num_kv_heads: int, num_blocks: int, bits_k: int, bits_v: int, seed: int = 42,
+              qjl: bool = False, qjl_seed: int = 43, device="cuda"):
+    """Allocate a zeroed pool with torch and bind a descriptor to it."""
+    import torch
+    rot = tq_make_rotation(seed, 128)
+    rq = tq_make_rotation(qjl_seed, 128) if qjl else None
+    cfg = make_config(num_kv_heads, num_blocks, bits_k, bits_v, rot, qjl, rq)
+    pool = torch.zeros(tq_cache_bytes(cfg), dtype=torch.uint8, device=device)
+    c = tq_cache_create(cfg, pool)
+    c._rots = (rot, rq)
+    return c
+
+
+def new_workspace(cache: Cache, num_seqs: int, num_q_heads: int, max_blocks: int, device="cuda"):
+    import torch
+    return torch.zeros(tq_decode_workspace_bytes(cache, num_seqs, num_q_heads, max_blocks),
+                       dtype=torch.uint8, device=device)

@@ -51,7 +51,7 @@ __all__ = [
     "reconstruct", "qjl_encode", "qjl_dot_estimate", "logits",
     "attention", "bits_per_vector", "LayoutV1", "pack_codes",
     "unpack_codes", "pack_signs", "unpack_signs", "write_cache",
-    "read_cache", "SQRT_HALF_PI",
+    "read_cache", "unpack_pool", "SQRT_HALF_PI",
 ]
 
 _MASK64 = (1 << 64) - 1
@@ -454,4 +454,33 @@ def read_cache(pool, lay: LayoutV1, slot: int, head: int) -> dict:
         out["rho16"] = np.frombuffer(pool[o:o + 2], dtype=np.float16)[0]
         o = b + lay.off_sig + row * (lay.d // 8)
         out["qjl_bits"] = unpack_signs(pool[o:o + lay.d // 8], lay.d)
+    return out
+
+
+def unpack_pool(pool, lay: LayoutV1, blocks=None) -> dict:
+    """Vectorised form of ``read_cache`` for whole blocks (same spec): returns
+    arrays indexed [block, head, row, ...] for the selected physical blocks.
+    Pinned against the per-token unpacker in the oracle tests."""
+    buf = np.frombuffer(bytes(pool) if not isinstance(pool, np.ndarray) else pool.tobytes(), dtype=np.uint8)
+    arr = buf.reshape(lay.num_blocks, lay.hkv, lay.block_bytes)
+    if blocks is not None:
+        arr = arr[np.asarray(blocks)]
+    B, d = lay.BLOCK, lay.d
+
+    def codes(off, rec, bits):
+        raw = arr[:, :, off:off + B * rec].reshape(arr.shape[0], lay.hkv, B, rec)
+        bitv = np.unpackbits(raw, axis=-1, bitorder="little").reshape(arr.shape[0], lay.hkv, B, d, bits)
+        return np.sum(bitv.astype(np.int64) << np.arange(bits), axis=-1)
+
+    def halves(off):
+        return arr[:, :, off:off + 2 * B].copy().view(np.float16).reshape(arr.shape[0], lay.hkv, B)
+
+    out = {"k_idx": codes(lay.off_k, lay.k_rec, lay.bk), "k_g16": halves(lay.off_gk)}
+    if lay.bv > 0:
+        out["v_idx"] = codes(lay.off_v, lay.v_rec, lay.bv)
+        out["v_g16"] = halves(lay.off_gv)
+    if lay.qjl:
+        out["rho16"] = halves(lay.off_rho)
+        raw = arr[:, :, lay.off_sig:lay.off_sig + B * d // 8].reshape(arr.shape[0], lay.hkv, B, d // 8)
+        out["qjl_bits"] = np.unpackbits(raw, axis=-1, bitorder="little").astype(np.int64)
     return out

@@ -486,3 +486,19 @@ def test_attention_without_quantisation_is_textbook():
     o, s = O.attention(q, K, V)
     p = special.softmax(K @ q / math.sqrt(D))
     np.testing.assert_allclose(o, p @ V, atol=1e-13)
+
+
+def test_vectorised_unpacker_equals_per_token_spec():
+    rng = np.random.default_rng(21)
+    for bk, bv, qjl in ((4, 4, False), (3, 3, True), (2, 0, True)):
+        lay = O.LayoutV1(128, 2, bk, bv, qjl, 3)
+        pool = bytearray(rng.integers(0, 256, lay.pool_bytes, dtype=np.uint8).tobytes())
+        vec = O.unpack_pool(pool, lay)
+        for slot in (0, 5, 16, 47):
+            for h in range(2):
+                one = O.read_cache(pool, lay, slot, h)
+                b, r = divmod(slot, 16)
+                for k, v in one.items():
+                    np.testing.assert_array_equal(np.asarray(vec[k][b, h, r]), np.asarray(v), err_msg=k)
+        sub = O.unpack_pool(pool, lay, blocks=[2, 0])
+        np.testing.assert_array_equal(sub["k_idx"][0], vec["k_idx"][2])
