@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
-SOURCES = ["tq_host.cpp", "tq_encode.hip", "tq_decode.hip", "tq_reconstruct.hip"]
+SOURCES = ["tq_host.cpp", "tq_encode.hip", "tq_decode.hip", "tq_decode_mfma.hip", "tq_reconstruct.hip"]
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")
 
 
@@ -37,6 +37,8 @@ def _flags() -> list[str]:
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
         # packed fp32 VALU ops stay off: the kernels use scalar fp32 only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core accumulators in ordinary VGPRs (no AGPR round trips)
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", os.path.join(ROOT, "include"),
     ]
 

@@ -214,59 +214,21 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a, int ns,
   }
   __syncthreads();
   const int64_t nsplit = a.num_splits;
-  float* part_base = a.partials + (((int64_t)n * Hkv + h) * nsplit) * a.group * 130;
+  float* part_base = a.partials + (((int64_t)n * Hkv + h) * nsplit) * a.group * kPartStride;
   for (int i = tid; i < gcount * kD; i += 256) {
     const int g = i / kD, j = i - g * kD;
     const float v = s_red[0][g][j] + s_red[1][g][j] + s_red[2][g][j] + s_red[3][g][j];
-    part_base[((int64_t)split * a.group + g0 + g) * 130 + j] = v;
+    st_coherent(part_base + ((int64_t)split * a.group + g0 + g) * kPartStride + j, v);
   }
   if (tid < gcount) {
-    float* pp = part_base + ((int64_t)split * a.group + g0 + tid) * 130;
-    pp[128] = s_ml[0][tid];
-    pp[129] = s_ml[1][tid];
+    float* pp = part_base + ((int64_t)split * a.group + g0 + tid) * kPartStride;
+    st_coherent(pp + 128, s_ml[0][tid]);
+    st_coherent(pp + 129, s_ml[1][tid]);
   }
 
   // ---- last workgroup of this (sequence, KV head, slice) merges the splits
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t* ctr = a.counters + ((int64_t)n * Hkv + h) * ns + slice;
-    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (old == (uint32_t)(nsplit - 1)) ? 1 : 0;
-    if (s_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  if (r < gcount) {
-    const int g = g0 + r;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) {
-      const float* pp = part_base + ((int64_t)s * a.group + g) * 130;
-      if (pp[129] > 0.f) M = fmaxf(M, pp[128]);
-    }
-    float Lsum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsplit; ++s) {
-      const float* pp = part_base + ((int64_t)s * a.group + g) * 130;
-      const float l = pp[129];
-      if (!(l > 0.f)) continue;
-      const float w = __expf(pp[128] - M);
-      Lsum = __builtin_fmaf(l, w, Lsum);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(w, pp[8 * p + e], o[e]);
-    }
-    const float invl = Lsum > 0.f ? 1.f / Lsum : 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] *= invl;
-    // o = D H o_rot / sqrt(d): natural input leaves lane p with output lane perm16(p)
-    fwht_row(o, fc);
-    const int lo = perm16(p);
-    const uint32_t sb = sign_byte(a.rot, lo);
-    float* dst = a.out + ((int64_t)n * Hq + (int64_t)h * a.group + g) * kD + 8 * lo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dst[e] = flip(o[e] * fc.sig * kInvSqrtD, sb, e);
-  }
+  if (!arrive_last(a.counters + ((int64_t)n * Hkv + h) * ns + slice, (uint32_t)nsplit, tid, &s_last)) return;
+  merge_splits_and_write(a, part_base, h, g0, gcount, tid);
 }
 
 template <int BK, int BV, bool QJL, bool ATTEND>
@@ -290,6 +252,7 @@ int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int atte
   const int ns = (a.group + 7) / 8;
   const int gs = (a.group + ns - 1) / ns;
   if (attend && bits_v != bits_k) return (int)hipErrorInvalidValue;
+  if (attend && !qjl) return launch_decode_mfma(a, bits_k, ns, gs, stream);
   switch (bits_k) {
     case 2: return attend ? launch_b<2, true>(a, qjl, ns, gs, s) : launch_b<2, false>(a, qjl, ns, gs, s);
     case 3: return attend ? launch_b<3, true>(a, qjl, ns, gs, s) : launch_b<3, false>(a, qjl, ns, gs, s);

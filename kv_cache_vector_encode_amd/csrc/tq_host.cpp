@@ -274,18 +274,40 @@ int check_device() {
   return TQ_OK;
 }
 
-int blocks_per_split_for(const tq_cache* c, int32_t num_seqs, int32_t group, int32_t max_blocks) {
-  int64_t work = (int64_t)max_blocks * num_seqs * c->cfg.num_kv_heads;
-  int64_t bps = (work + 1023) / 1024;
-  const int cap = group > 8 ? 32 : 64;
-  if (bps < 4) bps = 4;
-  if (bps > cap) bps = cap;
+// Blocks per split of a decode launch.  The matrix-core kernel keeps no
+// per-split score buffer, so its splits are sized for about two workgroups
+// per CU (256 CUs); the vector kernel stages its split's scores in LDS and
+// caps a split at 64 blocks.  A decode-attend launch has at most kMaxSplits
+// splits per (sequence, KV head) (the merge keeps one weight per split in
+// LDS).  TQ_BLOCKS_PER_SPLIT overrides (tuning only).  Returns 0 when no valid
+// split size exists.
+int blocks_per_split_for(const tq_cache* c, int32_t num_seqs, int32_t group, int32_t max_blocks, bool mfma,
+                         bool attend) {
+  const int64_t units = (int64_t)num_seqs * c->cfg.num_kv_heads * tq::decode_slices(group);
+  const int64_t cap = mfma ? ((int64_t)1 << 30) : 64;
+  int64_t bps;
+  if (mfma) {
+    bps = ((int64_t)max_blocks * units + 511) / 512;
+    if (bps < 8) bps = 8;
+  } else {
+    bps = ((int64_t)max_blocks * units + 1023) / 1024;
+    if (bps < 4) bps = 4;
+  }
   if (const char* env = std::getenv("TQ_BLOCKS_PER_SPLIT")) {
     const int v = std::atoi(env);
-    if (v >= 1 && v <= cap) bps = v;
+    if (v >= 1) bps = v;
   }
+  if (attend) {
+    const int64_t min_bps = ((int64_t)max_blocks + tq::kMaxSplits - 1) / tq::kMaxSplits;
+    if (bps < min_bps) bps = min_bps;
+  }
+  if (mfma) bps = (bps + 1) & ~(int64_t)1;
+  if (bps > cap) bps = attend ? 0 : cap;
+  if (attend && bps > 0 && ((int64_t)max_blocks + bps - 1) / bps > tq::kMaxSplits) bps = 0;
   return (int)bps;
 }
+
+bool decode_uses_mfma(const tq_cache* c, bool attend) { return attend && !c->cfg.qjl; }
 
 int validate_decode(const void* q, int32_t q_dtype, const tq_cache* cache,
                     const int32_t* block_tables, const int32_t* seq_lens,
@@ -486,11 +508,12 @@ int64_t tq_decode_workspace_bytes(const tq_cache* cache, int32_t num_seqs, int32
       num_q_heads % cache->cfg.num_kv_heads != 0)
     return fail(TQ_ERR_INVALID_ARG, "bad workspace query");
   const int group = num_q_heads / cache->cfg.num_kv_heads;
-  const int bps = blocks_per_split_for(cache, num_seqs, group, max_blocks_per_seq);
+  const int bps = blocks_per_split_for(cache, num_seqs, group, max_blocks_per_seq, decode_uses_mfma(cache, true), true);
+  if (bps <= 0) return fail(TQ_ERR_UNSUPPORTED, "sequence too long for this cache's decode kernel");
   const int64_t splits = std::max<int64_t>(1, (max_blocks_per_seq + bps - 1) / bps);
   const int64_t nsh = (int64_t)num_seqs * cache->cfg.num_kv_heads;
   const int64_t counters = ((nsh * tq::decode_slices(group) * 4 + 255) / 256) * 256;
-  return counters + nsh * splits * group * 130 * 4;
+  return counters + nsh * splits * group * tq::kPartStride * 4;
 }
 
 int tq_decode_attend(const void* q, int32_t q_dtype, const tq_cache* cache,
@@ -513,7 +536,8 @@ int tq_decode_attend(const void* q, int32_t q_dtype, const tq_cache* cache,
   a.out = out;
   a.logits = logits_out;
   a.logits_stride = (int64_t)max_blocks_per_seq * tq::kBlock;
-  a.blocks_per_split = blocks_per_split_for(cache, num_seqs, a.group, max_blocks_per_seq);
+  a.blocks_per_split = blocks_per_split_for(cache, num_seqs, a.group, max_blocks_per_seq, decode_uses_mfma(cache, true), true);
+  if (a.blocks_per_split <= 0) return fail(TQ_ERR_UNSUPPORTED, "sequence too long for this cache's decode kernel");
   a.num_splits = std::max(1, (max_blocks_per_seq + a.blocks_per_split - 1) / a.blocks_per_split);
   const int64_t nsh = (int64_t)num_seqs * cache->cfg.num_kv_heads;
   const int64_t counters = ((nsh * tq::decode_slices(a.group) * 4 + 255) / 256) * 256;
@@ -539,7 +563,7 @@ int tq_decode_logits(const void* q, int32_t q_dtype, const tq_cache* cache,
                    max_blocks_per_seq, scale);
   a.logits = logits_out;
   a.logits_stride = (int64_t)max_blocks_per_seq * tq::kBlock;
-  a.blocks_per_split = blocks_per_split_for(cache, num_seqs, a.group, max_blocks_per_seq);
+  a.blocks_per_split = blocks_per_split_for(cache, num_seqs, a.group, max_blocks_per_seq, false, false);
   a.num_splits = std::max(1, (max_blocks_per_seq + a.blocks_per_split - 1) / a.blocks_per_split);
   int err = tq::launch_decode(a, cache->cfg.bits_k, 0, cache->cfg.qjl, 0, hip_stream);
   if (err != 0) return hip_fail(err, "logits launch");
