@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "decode-attend GB/s of compressed KV read (% HBM peak) + encoded vectors/s"
 KERNEL_SOURCES = ["kv_cache_vector_encode_amd/csrc/tq_encode.hip", "kv_cache_vector_encode_amd/csrc/tq_decode.hip",
+                  "kv_cache_vector_encode_amd/csrc/tq_decode_mfma.hip", "kv_cache_vector_encode_amd/csrc/tq_merge.hip",
                   "kv_cache_vector_encode_amd/csrc/tq_device.h", "kv_cache_vector_encode_amd/csrc/tq_internal.h"]
 
 

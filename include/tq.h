@@ -172,10 +172,11 @@ int tq_encode_kv(const void* K, const void* V, int32_t dtype, int64_t num_tokens
  *                 A sequence of length 0 gets o = 0.
  *   logits_out:   NULL or device f32 [num_seqs][num_q_heads][max_blocks_per_seq*16];
  *                 receives s_t for t < seq_len (other entries untouched).
- *   workspace:    device memory of tq_decode_workspace_bytes() bytes.  Its
- *                 counter region must be zero before the first call (a zero
- *                 filled buffer is fine); every call leaves it zero again.
- *                 Calls that share a workspace must not overlap in time.
+ *   workspace:    device memory of tq_decode_workspace_bytes() bytes, 16-byte
+ *                 aligned, no initial contents needed: it receives the
+ *                 per-split partial results (two launches on hip_stream: the
+ *                 split pass, then the merge).  Calls that share a workspace
+ *                 must not overlap in time.
  * Requires a cache with values (bits_v > 0). */
 int64_t tq_decode_workspace_bytes(const tq_cache* cache, int32_t num_seqs,
                                   int32_t num_q_heads, int32_t max_blocks_per_seq);

@@ -45,7 +45,6 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a, int ns,
   __shared__ float s_p[ATTEND ? kMaxSplitTokens * GMAX : 1];
   __shared__ float s_ml[2][GMAX];
   __shared__ float s_red[ATTEND ? 4 : 1][GMAX][kD];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int r = tid >> 4, p = tid & 15;
@@ -218,17 +217,14 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a, int ns,
   for (int i = tid; i < gcount * kD; i += 256) {
     const int g = i / kD, j = i - g * kD;
     const float v = s_red[0][g][j] + s_red[1][g][j] + s_red[2][g][j] + s_red[3][g][j];
-    st_coherent(part_base + ((int64_t)split * a.group + g0 + g) * kPartStride + j, v);
+    part_base[((int64_t)split * a.group + g0 + g) * kPartStride + j] = v;
   }
   if (tid < gcount) {
     float* pp = part_base + ((int64_t)split * a.group + g0 + tid) * kPartStride;
-    st_coherent(pp + 128, s_ml[0][tid]);
-    st_coherent(pp + 129, s_ml[1][tid]);
+    pp[128] = s_ml[0][tid];
+    pp[129] = s_ml[1][tid];
   }
 
-  // ---- last workgroup of this (sequence, KV head, slice) merges the splits
-  if (!arrive_last(a.counters + ((int64_t)n * Hkv + h) * ns + slice, (uint32_t)nsplit, tid, &s_last)) return;
-  merge_splits_and_write(a, part_base, h, g0, gcount, tid);
 }
 
 template <int BK, int BV, bool QJL, bool ATTEND>
@@ -252,13 +248,18 @@ int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int atte
   const int ns = (a.group + 7) / 8;
   const int gs = (a.group + ns - 1) / ns;
   if (attend && bits_v != bits_k) return (int)hipErrorInvalidValue;
-  if (attend && !qjl) return launch_decode_mfma(a, bits_k, ns, gs, stream);
+  if (attend && !qjl) {
+    const int e = launch_decode_mfma(a, bits_k, ns, gs, stream);
+    return e ? e : launch_merge(a, stream);
+  }
+  int e = 0;
   switch (bits_k) {
-    case 2: return attend ? launch_b<2, true>(a, qjl, ns, gs, s) : launch_b<2, false>(a, qjl, ns, gs, s);
-    case 3: return attend ? launch_b<3, true>(a, qjl, ns, gs, s) : launch_b<3, false>(a, qjl, ns, gs, s);
-    case 4: return attend ? launch_b<4, true>(a, qjl, ns, gs, s) : launch_b<4, false>(a, qjl, ns, gs, s);
+    case 2: e = attend ? launch_b<2, true>(a, qjl, ns, gs, s) : launch_b<2, false>(a, qjl, ns, gs, s); break;
+    case 3: e = attend ? launch_b<3, true>(a, qjl, ns, gs, s) : launch_b<3, false>(a, qjl, ns, gs, s); break;
+    case 4: e = attend ? launch_b<4, true>(a, qjl, ns, gs, s) : launch_b<4, false>(a, qjl, ns, gs, s); break;
     default: return (int)hipErrorInvalidValue;
   }
+  return (e == 0 && attend) ? launch_merge(a, stream) : e;
 }
 
 int decode_slices(int group) { return (group + 7) / 8; }

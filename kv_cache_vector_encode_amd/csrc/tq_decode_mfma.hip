@@ -147,7 +147,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a, in
   __shared__ float s_acc[4][16][kD];   // per wave: [column][dim]
   __shared__ float s_wm[4][8], s_wl[4][8];
   __shared__ float s_ml[2][8];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -385,18 +384,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a, in
       const float mw = s_wm[w][hd];
       if (mw != -INFINITY) o += __builtin_amdgcn_exp2f(mw - M) * (s_acc[w][hd][d] + s_acc[w][hd + 8][d]);
     }
-    st_coherent(part_base + ((int64_t)split * a.group + g0 + hd) * kPartStride + d, o);
+    part_base[((int64_t)split * a.group + g0 + hd) * kPartStride + d] = o;
   }
   if (tid < gcount) {
     float* pp = part_base + ((int64_t)split * a.group + g0 + tid) * kPartStride;
     // the merge step works in natural-log units
-    st_coherent(pp + 128, s_ml[0][tid] * (1.f / LOG2E));
-    st_coherent(pp + 129, s_ml[1][tid]);
+    pp[128] = s_ml[0][tid] * (1.f / LOG2E);
+    pp[129] = s_ml[1][tid];
   }
 
-  // ---- last workgroup of this (sequence, KV head, slice) merges the splits
-  if (!arrive_last(a.counters + ((int64_t)n * Hkv + h) * ns + slice, (uint32_t)nsplit, tid, &s_last)) return;
-  merge_splits_and_write(a, part_base, h, g0, gcount, tid);
 }
 
 int launch_decode_mfma(const DecodeArgs& a, int bits, int ns, int gs, void* stream) {

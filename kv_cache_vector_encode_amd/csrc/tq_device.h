@@ -190,127 +190,4 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
 constexpr float kInvSqrtD = 0.08838834764831845f;   // 1/sqrt(128)
 constexpr float kSqrtHalfPi = 1.2533141373155003f;  // sqrt(pi/2)
 
-// Cross-workgroup hand-off of decode partials.  Each XCD has its own L2, and
-// an agent-scope release/acquire fence writes back / invalidates the whole
-// L2; instead the partials are written and read with agent-scope relaxed
-// atomic accesses (coherent at the agent level without flushing), the
-// writer waits for its stores (workgroup-scope release = wait for this
-// wave's memory operations) and a barrier before one thread bumps the
-// split counter, and the last workgroup reads only after seeing the count.
-__device__ __forceinline__ void st_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Called by every workgroup after writing its partials; returns true in the
-// last workgroup of the (sequence, KV head, slice) to arrive (all threads).
-__device__ __forceinline__ bool arrive_last(uint32_t* ctr, uint32_t expected, int tid, int* s_flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = (old == expected - 1) ? 1 : 0;
-    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = last;
-  }
-  __syncthreads();
-  return *s_flag != 0;
-}
-
-// Final step of decode-attend, run by the last workgroup of a (sequence, KV
-// head, slice) to finish: merge the splits' (m, l, o_rot), normalise, and
-// rotate back, o = R^T o_rot = D H o_rot / sqrt(d).  part_base points at the
-// (sequence, KV head) partials [split][group][kPartStride] = (o_rot[128], m, l) with m
-// in natural-log units.  All 256 threads take part: split weights go through
-// LDS, then each thread sums one float4 column of o_rot over the splits with
-// eight loads in flight, always in split order (deterministic).  Splits are at
-// most kMaxSplits.
-__device__ __forceinline__ void merge_splits_and_write(const DecodeArgs& a, const float* part_base, int h,
-                                                       int g0, int gcount, int tid) {
-  __shared__ float s_w[kMaxSplits][8];   // split weights per head
-  __shared__ float s_M[8], s_L[8];
-  __shared__ float4 s_o[8][32];
-  const int n = blockIdx.z;
-  const int nsplit = a.num_splits;
-  // 1. running max per head (one wave per group of heads)
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int gg = wave; gg < gcount; gg += 4) {
-    float M = -INFINITY;
-    for (int s = lane; s < nsplit; s += 64) {
-      const float* pp = part_base + ((int64_t)s * a.group + g0 + gg) * kPartStride;
-      const float l = ld_coherent(pp + 129), m = ld_coherent(pp + 128);
-      if (l > 0.f) M = fmaxf(M, m);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float L = 0.f;
-    for (int s = lane; s < nsplit; s += 64) {
-      const float* pp = part_base + ((int64_t)s * a.group + g0 + gg) * kPartStride;
-      const float l = ld_coherent(pp + 129);
-      const float w = l > 0.f ? __expf(ld_coherent(pp + 128) - M) : 0.f;
-      s_w[s][gg] = w;
-      L = __builtin_fmaf(l, w, L);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
-    if (lane == 0) {
-      s_M[gg] = M;
-      s_L[gg] = L;
-    }
-  }
-  __syncthreads();
-  // 2. o_rot columns: thread -> (head, 4 dims)
-  {
-    const int gg = tid >> 5, c4 = tid & 31;
-    if (gg < gcount) {
-      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-      int s = 0;
-      for (; s + 8 <= nsplit; s += 8) {
-        float4 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float* pp = part_base + ((int64_t)(s + u) * a.group + g0 + gg) * kPartStride + 4 * c4;
-          v[u] = make_float4(ld_coherent(pp), ld_coherent(pp + 1), ld_coherent(pp + 2), ld_coherent(pp + 3));
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float w = s_w[s + u][gg];
-          o.x = __builtin_fmaf(w, v[u].x, o.x);
-          o.y = __builtin_fmaf(w, v[u].y, o.y);
-          o.z = __builtin_fmaf(w, v[u].z, o.z);
-          o.w = __builtin_fmaf(w, v[u].w, o.w);
-        }
-      }
-      for (; s < nsplit; ++s) {
-        const float* pp = part_base + ((int64_t)s * a.group + g0 + gg) * kPartStride + 4 * c4;
-        const float w = s_w[s][gg];
-        o.x = __builtin_fmaf(w, ld_coherent(pp), o.x);
-        o.y = __builtin_fmaf(w, ld_coherent(pp + 1), o.y);
-        o.z = __builtin_fmaf(w, ld_coherent(pp + 2), o.z);
-        o.w = __builtin_fmaf(w, ld_coherent(pp + 3), o.w);
-      }
-      s_o[gg][c4] = o;
-    }
-  }
-  __syncthreads();
-  // 3. normalise and rotate back: rows of 16 lanes, one head each
-  const int r = tid >> 4, p = tid & 15;
-  if (r >= gcount) return;
-  const float L = s_L[r];
-  const float invl = L > 0.f ? 1.f / L : 0.f;
-  const float4 o0 = s_o[r][2 * p], o1 = s_o[r][2 * p + 1];
-  float o[8] = {o0.x * invl, o0.y * invl, o0.z * invl, o0.w * invl,
-                o1.x * invl, o1.y * invl, o1.z * invl, o1.w * invl};
-  // natural input leaves lane p holding output lane perm16(p)
-  const FwhtLane fc = fwht_lane(p);
-  fwht_row(o, fc);
-  const int lo = perm16(p);
-  const uint32_t sb = sign_byte(a.rot, lo);
-  float* dst = a.out + ((int64_t)n * a.num_q_heads + (int64_t)h * a.group + g0 + r) * kD + 8 * lo;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) dst[e] = flip(o[e] * fc.sig * kInvSqrtD, sb, e);
-}
-
 }  // namespace tq

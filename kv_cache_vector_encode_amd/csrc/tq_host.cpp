@@ -512,8 +512,7 @@ int64_t tq_decode_workspace_bytes(const tq_cache* cache, int32_t num_seqs, int32
   if (bps <= 0) return fail(TQ_ERR_UNSUPPORTED, "sequence too long for this cache's decode kernel");
   const int64_t splits = std::max<int64_t>(1, (max_blocks_per_seq + bps - 1) / bps);
   const int64_t nsh = (int64_t)num_seqs * cache->cfg.num_kv_heads;
-  const int64_t counters = ((nsh * tq::decode_slices(group) * 4 + 255) / 256) * 256;
-  return counters + nsh * splits * group * tq::kPartStride * 4;
+  return nsh * splits * group * tq::kPartStride * 4;
 }
 
 int tq_decode_attend(const void* q, int32_t q_dtype, const tq_cache* cache,
@@ -539,10 +538,7 @@ int tq_decode_attend(const void* q, int32_t q_dtype, const tq_cache* cache,
   a.blocks_per_split = blocks_per_split_for(cache, num_seqs, a.group, max_blocks_per_seq, decode_uses_mfma(cache, true), true);
   if (a.blocks_per_split <= 0) return fail(TQ_ERR_UNSUPPORTED, "sequence too long for this cache's decode kernel");
   a.num_splits = std::max(1, (max_blocks_per_seq + a.blocks_per_split - 1) / a.blocks_per_split);
-  const int64_t nsh = (int64_t)num_seqs * cache->cfg.num_kv_heads;
-  const int64_t counters = ((nsh * tq::decode_slices(a.group) * 4 + 255) / 256) * 256;
-  a.counters = static_cast<uint32_t*>(workspace);
-  a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counters);
+  a.partials = static_cast<float*>(workspace);
   int err = tq::launch_decode(a, cache->cfg.bits_k, cache->cfg.bits_v, cache->cfg.qjl, 1, hip_stream);
   if (err != 0) return hip_fail(err, "decode launch");
   return TQ_OK;

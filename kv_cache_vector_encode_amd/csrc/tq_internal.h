@@ -13,7 +13,7 @@ constexpr int kBlock = 16;       // tokens per cache block
 constexpr int kLutMax = 96;      // buckets of the threshold-search table
 constexpr int kMaxGroup = 16;    // query heads per KV head
 constexpr int kPartStride = 132; // floats per (split, head) partial: o_rot[128], m, l, pad
-constexpr int kMaxSplits = 512;  // splits per (sequence, KV head) of a decode launch
+constexpr int kMaxSplits = 4096; // splits per (sequence, KV head) of a decode launch
 
 // Codebook of one bit width, plus the bucket table used by the encoder's
 // threshold search: for y in bucket k = clamp(floor(y*lut_scale+lut_offset)),
@@ -89,7 +89,6 @@ struct DecodeArgs {
   float* out;               // [seqs][q_heads][128] (attend)
   float* logits;            // [seqs][q_heads][logits_stride] or null
   float* partials;          // [seqs][kv_heads][splits][group][kPartStride]
-  uint32_t* counters;       // [seqs][kv_heads]
   int64_t logits_stride;
   Layout lay;
   int64_t num_blocks;       // block-table entries outside [0, num_blocks) read as block 0
@@ -121,6 +120,7 @@ int launch_encode(const EncodeArgs& a, int num_streams, int in_dtype, void* stre
 int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int attend, void* stream);
 int decode_slices(int group);
 int launch_decode_mfma(const DecodeArgs& a, int bits, int ns, int gs, void* stream);
+int launch_merge(const DecodeArgs& a, void* stream);
 int launch_reconstruct(const ReconArgs& a, void* stream);
 
 }  // namespace tq

@@ -222,7 +222,7 @@ def tq_decode_workspace_bytes(cache: Cache, num_seqs: int, num_q_heads: int, max
 def tq_decode_attend(q, cache: Cache, block_tables, seq_lens, out, workspace, logits_out=None,
                      scale: float = 0.0, stream=None):
     """q [seqs][q_heads][128]; block_tables int32 [seqs][max_blocks]; out f32
-    [seqs][q_heads][128]; workspace: uint8 tensor (zero before first use)."""
+    [seqs][q_heads][128]; workspace: uint8 tensor of tq_decode_workspace_bytes() bytes."""
     ns, hq, _ = q.shape
     _check(lib().tq_decode_attend(_ptr(q), _dtype_code(q), cache.handle, _ptr(block_tables), _ptr(seq_lens),
                                   ns, hq, block_tables.shape[1], scale, _ptr(out), _ptr(logits_out),

@@ -204,9 +204,6 @@ def _decode_case(device, bits, group, hkv, lens, qjl=False, dtype="bf16", scale=
             e = np.linalg.norm(go[n, hq] - o) / np.linalg.norm(o)
             assert e <= OUT_RTOL, (n, hq, e)
             worst_o = max(worst_o, e)
-    # workspace counters are back to zero
-    cnt = ws[: 4 * nseq * hkv * ((group + 7) // 8)].view(torch.int32).cpu()
-    assert torch.all(cnt == 0)
     _say(f"decode bits={bits} G={group} hkv={hkv} qjl={qjl}: worst logit {worst_l:.2e} worst out {worst_o:.2e}")
     return out, logits, (q, cache, bt_d, lens_d, ws)
 
