@@ -106,6 +106,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
     ap.add_argument("--only", choices=["encode", "decode", "both"], default="both",
                     help="profiling aid: time only one of the two kernels")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (steps times), to scale HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU mode.",
@@ -118,6 +120,15 @@ def main():
     from kv_cache_vector_encode_amd import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": args.steps}), flush=True)
+        return
     w = W.CONFIGS[args.workload]
     tq.lib()
     print(f"# workload {w.name}: generating inputs", file=sys.stderr, flush=True)
@@ -170,6 +181,12 @@ def main():
             if ev is not None:
                 ev[3].record(stream)
 
+    if args.only == "decode":
+        # decode-only timing still reads real codes (bank conflicts of the
+        # table lookups depend on them): encode every set once, untimed
+        for s in sets:
+            tq.tq_encode_kv(s["K"], s["V"], slots, w.bits_k, s["cache"], stream)
+        torch.cuda.synchronize()
     print(f"# {nsets} rotating sets of {set_bytes / 1e6:.1f} MB; warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)

@@ -158,7 +158,8 @@ int tq_encode_kv(const void* K, const void* V, int32_t dtype, int64_t num_tokens
  * Decode-attend in the rotated frame ([P2] attention under quantisation;
  * [P4] "RHT preserves inner products, attention can be computed without
  * restoring"; [P3] contribution: the decoder never materialises K_hat).
- *   q:            device [num_seqs][num_q_heads][d], TQ_F32/TQ_F16/TQ_BF16.
+ *   q:            device [num_seqs][num_q_heads][d], TQ_F32/TQ_F16/TQ_BF16,
+ *                 16-byte aligned.
  *                 Query head h reads KV head h / (num_q_heads/num_kv_heads);
  *                 num_q_heads must be a multiple of num_kv_heads with a group
  *                 of at most 16.

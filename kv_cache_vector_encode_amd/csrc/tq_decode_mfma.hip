@@ -1,7 +1,7 @@
 // tq_decode_mfma: decode-attend for grouped queries on the gfx950 matrix
 // cores.  Same computation as decode_kernel (tq_decode.hip): logits in the
 // rotated frame, s_t = scale * gamma_t * <R q, c[codes_t]>, softmax, value
-// sum in the rotated frame, one inverse rotation per query head at the end
+// sum in the rotated frame; the inverse rotation runs in merge_kernel
 // (Bit-Axon "TurboQuant: KV Cache Compression", attention under quantisation;
 // deep-dive blog Step 1, attention directly on the rotated data).
 //
@@ -21,14 +21,22 @@
 //
 // Work: grid (split, KV-head slice of <= 8 query heads, sequence); 4 waves
 // per workgroup, each takes pairs of 16-token blocks of the split in turn
-// and keeps its own running max / sum / accumulator.  The waves are merged
-// in LDS, the split's (m, l, o_rot) goes to the workspace, and the last
-// workgroup of the (sequence, slice) merges the splits in fixed order and
-// applies R^T (shared with decode_kernel).
+// and keeps its own running max / sum / accumulator.
+//
+// Memory: every wave streams its (block, KV head) chunks into a private ring
+// of LDS stages with global_load_lds (global memory straight to LDS, no
+// registers held while the data is in flight), several block pairs ahead,
+// and waits for a stage with an explicit vmcnt.  The loop issues no other
+// vector-memory loads, so the count is exact.  The waves are merged in LDS
+// and the split's (m, l, o_rot) goes to the workspace for merge_kernel.
 
 #include <hip/hip_bf16.h>
 
 #include "tq_device.h"
+
+#ifndef TQ_B4_REPLICATED
+#define TQ_B4_REPLICATED 0
+#endif
 
 namespace tq {
 
@@ -72,6 +80,100 @@ __device__ __forceinline__ void add_col_pairs(const f32x4& c, float (&o)[4]) {
       : "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]));
 }
 
+// Geometry of one (block, KV head) chunk of a cache with values and no QJL
+// sidecar (K codes [16][16b] | V codes [16][16b] | gamma_k [16] | gamma_v
+// [16], fp16 norms), and of its LDS stage slot.  The chunk is copied by
+// kFull 1 KiB pieces (64 lanes x 16 B) and one tail piece: a dword copy
+// (64 lanes x 4 B, lanes past the tail re-read its last dword) when the tail
+// is at most 256 B, else a 16 B copy with the lane offsets clamped to the
+// chunk.  kStages block pairs per wave leave room for three workgroups per
+// CU in LDS.
+template <int BITS>
+struct Chunk {
+  static constexpr int kBytes = 512 * BITS + 64;
+  static constexpr int kOffV = 256 * BITS, kOffGK = 512 * BITS, kOffGV = 512 * BITS + 32;
+  static constexpr int kFull = kBytes / 1024;
+  static constexpr int kRem = kBytes - 1024 * kFull;
+  static constexpr bool kTailDword = kRem <= 256;
+  static constexpr int kSlot = 1024 * kFull + (kTailDword ? 256 : 1024);
+  static constexpr int kDma = kFull + 1;     // copy instructions per chunk
+  static constexpr int kStages = BITS == 2 ? 4 : 2;
+  static constexpr int kWaveRing = kStages * 2 * kSlot;
+};
+
+// Copy one chunk from global memory (wave-uniform src) to LDS byte address
+// lds.  v16 = 16 * lane, vt = the lane's tail offset.  The LDS address of a
+// piece is m0 + instruction offset + lane * size (the offset applies to both
+// sides), so every piece lands at its offset inside the slot.  m0 is saved
+// and restored around the copies.
+template <int BITS>
+__device__ __forceinline__ void dma_chunk(uint32_t lds, const uint8_t* src, uint32_t v16, uint32_t vt, uint32_t vv) {
+  uint32_t save;
+  if constexpr (BITS == 4) {
+    // the V piece (codes of the 16 values) goes through the swizzled lane
+    // offsets vv (see v_slot)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "global_load_lds_dwordx4 %5, %3 offset:1024\n\t"
+        "global_load_lds_dword %4, %3 offset:2048\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save) : "s"(lds), "v"(v16), "s"(src), "v"(vt), "v"(vv) : "memory");
+  } else if constexpr (BITS == 3) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "global_load_lds_dwordx4 %4, %3 offset:1024\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save) : "s"(lds), "v"(v16), "s"(src), "v"(vt) : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "global_load_lds_dword %4, %3 offset:1024\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save) : "s"(lds), "v"(v16), "s"(src), "v"(vt) : "memory");
+  }
+}
+
+// One 16 B-per-lane copy: LDS lds + 16 lane <- global src + voff.
+__device__ __forceinline__ void dma_x4(uint32_t lds, const void* src, uint32_t voff) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save) : "s"(lds), "v"(voff), "s"(src) : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// wait for the oldest staged pair while `behind` younger pairs stay in flight
+template <int BITS>
+__device__ __forceinline__ void wait_pairs_behind(int behind) {
+  constexpr int P = 2 * Chunk<BITS>::kDma;
+  if (behind <= 0) wait_vm<0>();
+  else if (behind == 1) wait_vm<P>();
+  else if (behind == 2) wait_vm<2 * P>();
+  else if (behind == 3) wait_vm<3 * P>();
+  else wait_vm<4 * P>();
+}
+
+// With 4-bit codes the V region (16 records of 64 B, 64 pieces of 16 B) is
+// staged transposed by token: piece (token T, quarter d) of the record goes
+// to slot 16 (T % 4) + 4 (T / 4) + d, so the reads below (lane (m, g) takes
+// 4 B of token 4g + i at a time) hit 64 different banks.  Lane L of the copy
+// fetches the piece that belongs in slot L.
+__device__ __forceinline__ uint32_t v_slot_src(int L) {
+  const int T = 4 * ((L >> 2) & 3) + (L >> 4), d = L & 3;
+  return (uint32_t)(16 * (4 * T + d));
+}
+
 template <int BITS>
 struct BlockRegs {
   uint32_t k[BITS];     // 32 codes: dims 32g .. 32g+31 of token row m
@@ -80,54 +182,39 @@ struct BlockRegs {
   uint32_t gv[2];
 };
 
-// Per-lane byte offsets inside a (block, KV head) chunk, fixed for the whole
-// kernel: loads then take a wave-uniform base plus a 32-bit lane offset.
-struct LaneOffsets {
-  uint32_t k;      // K code chunk of row m, dims 32g..
-  uint32_t v[4];   // V codes of tokens 4g+i, dims 8m..
-  uint32_t gk, gv; // norms of tokens 4g..4g+3
-};
-
+// this lane's codes and norms of one chunk staged in LDS at st
 template <int BITS>
-__device__ __forceinline__ LaneOffsets lane_offsets(const Layout& lay, int m, int g) {
-  LaneOffsets o;
-  o.k = (uint32_t)(lay.off_k + m * lay.k_rec + g * (4 * BITS));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o.v[i] = (uint32_t)(lay.off_v + (4 * g + i) * lay.v_rec + ((BITS * 8 * m) >> 3));
-  o.gk = (uint32_t)(lay.off_gk + 8 * g);
-  o.gv = (uint32_t)(lay.off_gv + 8 * g);
-  return o;
-}
-
-template <int BITS>
-__device__ __forceinline__ void load_block(BlockRegs<BITS>& r, const uint8_t* base, const LaneOffsets& o, int m) {
+__device__ __forceinline__ void read_chunk(BlockRegs<BITS>& r, const uint8_t* st, int m, int g) {
+  using C = Chunk<BITS>;
   if constexpr (BITS == 4) {
-    const uint4 t = *reinterpret_cast<const uint4*>(base + o.k);
+    const uint4 t = *reinterpret_cast<const uint4*>(st + m * 64 + g * 16);
     r.k[0] = t.x; r.k[1] = t.y; r.k[2] = t.z; r.k[3] = t.w;
   } else if constexpr (BITS == 3) {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(base + o.k);
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(st + m * 48 + g * 12);
     r.k[0] = p[0]; r.k[1] = p[1]; r.k[2] = p[2];
   } else {
-    const uint2 t = *reinterpret_cast<const uint2*>(base + o.k);
+    const uint2 t = *reinterpret_cast<const uint2*>(st + m * 32 + g * 8);
     r.k[0] = t.x; r.k[1] = t.y;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const int off = C::kOffV + (4 * g + i) * 16 * BITS + BITS * m;
     if constexpr (BITS == 4) {
-      r.v[i] = *reinterpret_cast<const uint32_t*>(base + o.v[i]);
+      // transposed staging: token 4g + i, dims 8m.. at 256 i + 64 g + 4 m
+      r.v[i] = *reinterpret_cast<const uint32_t*>(st + C::kOffV + 256 * i + 64 * g + 4 * m);
     } else if constexpr (BITS == 2) {
-      r.v[i] = *reinterpret_cast<const uint16_t*>(base + o.v[i]);
+      r.v[i] = *reinterpret_cast<const uint16_t*>(st + off);
     } else {
-      // 24 bits at byte 3m: two aligned dwords and a funnel shift (the
-      // second can run past the record; other regions follow the codes)
-      const uint32_t al = o.v[i] & ~3u, sh = 8 * (o.v[i] & 3u);
-      const uint32_t lo = *reinterpret_cast<const uint32_t*>(base + al);
-      const uint32_t hi = *reinterpret_cast<const uint32_t*>(base + al + 4);
-      r.v[i] = (uint32_t)((((uint64_t)hi << 32) | lo) >> sh) & 0xFFFFFFu;
+      // 24 bits at byte off: two aligned dwords (the second may reach into
+      // the gamma_k region of the slot) and a byte funnel shift
+      const int al = off & ~3;
+      const uint32_t lo = *reinterpret_cast<const uint32_t*>(st + al);
+      const uint32_t hi = *reinterpret_cast<const uint32_t*>(st + al + 4);
+      r.v[i] = __builtin_amdgcn_alignbyte(hi, lo, (uint32_t)(off & 3)) & 0xFFFFFFu;
     }
   }
-  const uint2 a = *reinterpret_cast<const uint2*>(base + o.gk);
-  const uint2 b = *reinterpret_cast<const uint2*>(base + o.gv);
+  const uint2 a = *reinterpret_cast<const uint2*>(st + C::kOffGK + 8 * g);
+  const uint2 b = *reinterpret_cast<const uint2*>(st + C::kOffGV + 8 * g);
   r.gk[0] = a.x; r.gk[1] = a.y;
   r.gv[0] = b.x; r.gv[1] = b.y;
 }
@@ -135,18 +222,44 @@ __device__ __forceinline__ void load_block(BlockRegs<BITS>& r, const uint8_t* ba
 __device__ __forceinline__ float half_lo(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w & 0xFFFF))); }
 __device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w >> 16))); }
 
-template <int BITS, bool LOGITS>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a, int ns, int gs) {
-  // Dequantisation tables, indexed by a pair of codes (2*BITS bits):
-  //  keys:   (hi | lo << 16, hi | lo << 16) bf16 of the two centroids,
+// LDS of one workgroup, in one object so the tables sit at address 0 (a
+// lookup address then fits the instruction's offset field).
+template <int BITS>
+struct DecodeSmem {
+  // Dequantisation tables.  With 4-bit codes one entry per code, repeated
+  // in all 64 banks (entry e of lane l at dword 64 e + l: every lane reads
+  // its own bank, no conflicts):
+  //  keys:   bf16 hi | bf16 lo << 16 of c[e],   values: f16(c[e]).
+  // With 2 or 3 bits one entry per pair of codes (2*BITS bits):
+  //  keys:   (hi | lo << 16, hi | lo << 16) of the two centroids,
   //  values: f16(c[first]) | f16(c[second]) << 16.
-  __shared__ uint2 s_tk2[1 << (2 * BITS)];
-  __shared__ uint32_t s_tv2[1 << (2 * BITS)];
-  __shared__ float s_q[8][kD];
-  __shared__ u32x4 s_qb[8][64];        // logit B operands [step][lane]
-  __shared__ float s_acc[4][16][kD];   // per wave: [column][dim]
-  __shared__ float s_wm[4][8], s_wl[4][8];
-  __shared__ float s_ml[2][8];
+  static constexpr bool kRep = BITS == 4 && TQ_B4_REPLICATED;
+  static constexpr int kTk = kRep ? 16 * 64 : 2 << (2 * BITS);
+  static constexpr int kTv = kRep ? 16 * 64 : 1 << (2 * BITS);
+  uint32_t tk[kTk];
+  uint32_t tv[kTv];
+  u32x4 qb[8][64];                     // logit B operands [step][lane]
+  alignas(16) uint8_t qs[8 * kD * 4];  // the slice's queries as loaded
+  float cent[2][16];                   // key / value centroids
+  float wm[4][8], wl[4][8], ml[2][8];
+  alignas(16) uint8_t ring[4 * Chunk<BITS>::kWaveRing];
+};
+
+template <int BITS, bool LOGITS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(const DecodeArgs a, int ns, int gs) {
+  using C = Chunk<BITS>;
+  constexpr int NS = C::kStages;
+  __shared__ DecodeSmem<BITS> sm;
+  const uint2* const s_tk2 = reinterpret_cast<const uint2*>(sm.tk);
+  const uint32_t* const s_tv2 = sm.tv;
+  auto& s_qb = sm.qb;
+  auto& s_wm = sm.wm;
+  auto& s_wl = sm.wl;
+  auto& s_ml = sm.ml;
+  uint8_t* const s_ring = sm.ring;
+  // per-wave [column][dim] accumulator rows, padded where the ring has room
+  constexpr int kAccRow = 16 * (kD + 4) * 4 <= C::kWaveRing ? kD + 4 : kD;
+  static_assert(16 * kAccRow * 4 <= C::kWaveRing, "wave accumulator must fit in the wave's ring");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -159,113 +272,264 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a, in
   const int nblk_seq = (seq_len + kBlock - 1) / kBlock;
   const int sb0 = split * a.blocks_per_split;
   const int sb1 = min(nblk_seq, sb0 + a.blocks_per_split);
+  const int tok_end = min(seq_len, sb1 * kBlock);
   const int64_t Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const float LOG2E = 1.4426950408889634f;
 
-  for (int i = tid; i < (1 << (2 * BITS)); i += 256) {
-    constexpr uint32_t mask = (1u << BITS) - 1;
-    const float c0 = a.cent_k[i & mask], c1 = a.cent_k[i >> BITS];
-    const uint32_t h0 = bf16_bits(c0), h1 = bf16_bits(c1);
-    s_tk2[i] = make_uint2(h0 | (bf16_bits(c0 - bf16_val(h0)) << 16), h1 | (bf16_bits(c1 - bf16_val(h1)) << 16));
-    s_tv2[i] = f16_bits(a.cent_v[i & mask]) | (f16_bits(a.cent_v[i >> BITS]) << 16);
+  // ---- this wave's block pairs: wave, wave + 4, ... of the split
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int npairs = max(0, (sb1 - sb0 + 1) / 2);
+  const int my_n = npairs > wv ? (npairs - wv + 3) / 4 : 0;
+  // the block table is read through the constant address space: it does not
+  // change during the launch, so its wave-uniform reads stay scalar loads
+  // (the asm around them would otherwise force vector loads and full waits)
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  const const_i32_ptr btab = (const_i32_ptr)(a.block_tables + (int64_t)n * a.max_blocks);
+  const uint32_t nblocks = (uint32_t)min(a.num_blocks, (int64_t)INT32_MAX);
+  const uint8_t* const pool_h = a.pool + (int64_t)h * C::kBytes;
+  const int64_t blk_stride = Hkv * C::kBytes;
+  // block-table entries of this wave's k-th pair (the second block of a
+  // split's odd tail re-reads the first; its data is never used)
+  auto fetch_pair = [&](int k, int& b0, int& b1) {
+    const int lb = sb0 + 2 * (wv + 4 * k);
+    b0 = btab[lb];
+    b1 = btab[lb + 1 < sb1 ? lb + 1 : lb];
+  };
+  auto chunk_src = [&](int blk) -> const uint8_t* {
+    return pool_h + (int64_t)((uint32_t)blk < nblocks ? blk : 0) * blk_stride;   // out-of-range ids read block 0
+  };
+  const uint32_t ring_lds = (uint32_t)reinterpret_cast<uintptr_t>(s_ring) + (uint32_t)(wv * C::kWaveRing);
+  const uint32_t v16 = 16u * lane;
+  const uint32_t vt = C::kTailDword ? 4u * (uint32_t)min(lane, C::kRem / 4 - 1)
+                                    : (uint32_t)min(16 * lane, C::kRem - 16);
+  const uint32_t vv = v_slot_src(lane);
+  auto dma_pair = [&](int k, int b0, int b1) {   // k-th pair of this wave into stage k % NS
+    const uint32_t st = ring_lds + (uint32_t)((k % NS) * 2 * C::kSlot);
+    dma_chunk<BITS>(st, chunk_src(b0), v16, vt, vv);
+    dma_chunk<BITS>(st + C::kSlot, chunk_src(b1), v16, vt, vv);
+  };
+  // The kernel issues no vector-memory loads of its own: the slice's
+  // queries and the first stages are copied to LDS here, before the set-up
+  // below, whose latency they hide; centroids and signs come through scalar
+  // loads.  Wave 0 copies the queries (gcount heads of 128 elements,
+  // contiguous) first, so it can wait for them alone.
+  const int qsize = a.q_dtype == 0 ? 4 : 2;
+  if (wv == 0) {
+    const int qbytes = gcount * kD * qsize;   // a multiple of 256
+    const uint8_t* qsrc = static_cast<const uint8_t*>(a.q) + ((int64_t)n * Hq + (int64_t)h * a.group + g0) * kD * qsize;
+    const uint32_t qs_lds = (uint32_t)reinterpret_cast<uintptr_t>(sm.qs);
+    for (int j = 0; 1024 * j < qbytes; ++j)
+      dma_x4(qs_lds + 1024u * j, qsrc, (uint32_t)min(16 * lane + 1024 * j, qbytes - 16));
+  }
+  const int k_pro = min(NS, my_n);
+  for (int k = 0; k < k_pro; ++k) {
+    int b0, b1;
+    fetch_pair(k, b0, b1);
+    dma_pair(k, b0, b1);
   }
 
-  // ---- rotate this slice's queries (rows of 16 lanes, one head each)
+  constexpr bool kRep = DecodeSmem<BITS>::kRep;
+  constexpr int kLevels = 1 << BITS;
+  // centroids through LDS: one lane writes them from wave-uniform (scalar)
+  // loads of the arguments, so no per-lane argument load is needed
+  if (tid == 0) {
+#pragma unroll
+    for (int i = 0; i < kLevels; ++i) {
+      sm.cent[0][i] = a.cent_k[i];
+      sm.cent[1][i] = a.cent_v[i];
+    }
+  }
+  __syncthreads();
+  if constexpr (kRep) {
+    for (int i = tid; i < 16 * 64; i += 256) {
+      const float c = sm.cent[0][i >> 6];
+      const uint32_t hb = bf16_bits(c);
+      sm.tk[i] = hb | (bf16_bits(c - bf16_val(hb)) << 16);
+      sm.tv[i] = f16_bits(sm.cent[1][i >> 6]);
+    }
+  } else {
+    for (int i = tid; i < (1 << (2 * BITS)); i += 256) {
+      constexpr int mask = kLevels - 1;
+      const float c0 = sm.cent[0][i & mask], c1 = sm.cent[0][i >> BITS];
+      const uint32_t h0 = bf16_bits(c0), h1 = bf16_bits(c1);
+      sm.tk[2 * i] = h0 | (bf16_bits(c0 - bf16_val(h0)) << 16);
+      sm.tk[2 * i + 1] = h1 | (bf16_bits(c1 - bf16_val(h1)) << 16);
+      sm.tv[i] = f16_bits(sm.cent[1][i & mask]) | (f16_bits(sm.cent[1][i >> BITS]) << 16);
+    }
+  }
+  if (wv == 0) wait_pairs_behind<BITS>(k_pro);   // the query copy has landed
+  __syncthreads();
+
+  // ---- rotate this slice's queries (rows of 16 lanes, one head each; the
+  // logit scale and log2(e) are folded in, so logits come out in log2 units)
+  // and scatter them into the B operands of the logit product: column c ->
+  // head c%8, part c/8 (bf16 q_hi, bf16 residual); in the operand of lane
+  // (c, g) at step st, slots (2e, 2e+1) both carry dim 32g + 4st + e.
+  // Columns of heads past the slice stay zero.
   {
     const int r = tid >> 4, p = tid & 15;
-    if (r < gcount) {
-      const FwhtLane fc = fwht_lane(p);
-      const int64_t hq = (int64_t)h * a.group + g0 + r;
-      const int ell = perm16(p);
-      float x[8];
-      const int64_t elem = ((int64_t)n * Hq + hq) * kD + 8 * ell;
-      if (a.q_dtype == 0) load8<0>(a.q, elem, x);
-      else if (a.q_dtype == 1) load8<1>(a.q, elem, x);
-      else load8<2>(a.q, elem, x);
-      const uint32_t sb = sign_byte(a.rot, ell);
+    if (r < 8) {
+      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (r < gcount) {
+        const FwhtLane fc = fwht_lane(p);
+        const int ell = perm16(p);
+        const int elem = r * kD + 8 * ell;
+        if (a.q_dtype == 0) load8<0>(sm.qs, elem, x);
+        else if (a.q_dtype == 1) load8<1>(sm.qs, elem, x);
+        else load8<2>(sm.qs, elem, x);
+        // sign byte ell of the rotation: word picked among uniform loads
+        const int wsel = ell >> 2;
+        const uint32_t wd = wsel == 0 ? a.rot.neg[0] : wsel == 1 ? a.rot.neg[1] : wsel == 2 ? a.rot.neg[2] : a.rot.neg[3];
+        const uint32_t sb = (wd >> (8 * (ell & 3))) & 0xFFu;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = flip(x[e], sb, e);
-      fwht_row(x, fc);
-      const float sc = fc.sig * kInvSqrtD;
+        for (int e = 0; e < 8; ++e) x[e] = flip(x[e], sb, e);
+        fwht_row(x, fc);   // lane p now holds dims 8p .. 8p+7
+        const float sc = fc.sig * kInvSqrtD * a.scale * LOG2E;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_q[r][8 * p + e] = x[e] * sc;
-    }
-  }
-  __syncthreads();
-
-  // ---- B operands of the logit product: column m -> head m%8, part m/8;
-  // step st, slots (2e, 2e+1) both carry dim 32g + 4st + e.  Kept in LDS
-  // (each lane reads back its own 8 x 16 bytes per block) to spare VGPRs.
-  {
-    const int hd = m & 7;
-    const bool lo = m >= 8;
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      if (st % 4 != wave) continue;   // the 4 waves fill 2 steps each
-      u32x4 q4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float qv = hd < gcount ? s_q[hd][32 * g + 4 * st + e] : 0.f;
-        const uint32_t hb = bf16_bits(qv);
-        const uint32_t v = lo ? bf16_bits(qv - bf16_val(hb)) : hb;
-        q4[e] = v | (v << 16);
+        for (int e = 0; e < 8; ++e) x[e] *= sc;
       }
-      s_qb[st][lane] = q4;
+      uint32_t* qb = reinterpret_cast<uint32_t*>(s_qb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 8 * p + e, gq = d >> 5, st = (d >> 2) & 7, ee = d & 3;
+        const uint32_t hb = bf16_bits(x[e]);
+        const uint32_t lb = bf16_bits(x[e] - bf16_val(hb));
+        qb[(st * 64 + r + 16 * gq) * 4 + ee] = hb | (hb << 16);
+        qb[(st * 64 + r + 8 + 16 * gq) * 4 + ee] = lb | (lb << 16);
+      }
     }
   }
   __syncthreads();
-  const float sscale = a.scale * LOG2E;       // scores kept in log2 units
   const bool col_lo = m >= 8;
   const bool col_live = (m & 7) < gcount;
-  const uint32_t live_mask = col_live ? 0xFFFFu : 0u;
+  const uint32_t live_mask = col_live ? 0xFFFFFFFFu : 0u;
 
   f32x4 acc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float run_m = -INFINITY, run_l = 0.f;
 
-  const int32_t* btab = a.block_tables + (int64_t)n * a.max_blocks;
-  const int npairs = max(0, (sb1 - sb0 + 1) / 2);
-  // wave-uniform indices: block-table reads become scalar loads, which do not
-  // hold up the vector-memory counter the prefetched data waits on
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lane4 = 4u * lane;
+  // logit B operands stay in registers for the whole loop
+  u32x4 qreg[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) qreg[st] = s_qb[st][lane];
 
-  auto block_base = [&](int lb) -> const uint8_t* {
-    int blk = (lb < sb1) ? btab[lb] : 0;
-    blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
-    return a.pool + ((int64_t)blk * Hkv + h) * a.lay.block_bytes;
-  };
-  const LaneOffsets lo_off = lane_offsets<BITS>(a.lay, m, g);
-  auto load_pair = [&](BlockRegs<BITS>(&r)[2], int pi) {
-    load_block<BITS>(r[0], block_base(sb0 + 2 * pi), lo_off, m);
-    load_block<BITS>(r[1], block_base(sb0 + 2 * pi + 1), lo_off, m);
-  };
-  auto compute_pair = [&](const BlockRegs<BITS>(&cur)[2], int pi) {
-    // ---- logits of the two blocks
+  auto compute_pair = [&](const BlockRegs<BITS>(&cur)[2], int lb0) {
+    // ---- logits of the two blocks (log2 units): all table reads first,
+    // then the two 8-step product chains interleaved
+    uint32_t kd[2][32];   // (hi | lo) of the lane's 32 codes (dims 32g + i)
+    if constexpr (kRep) {
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // even / odd nibbles as bytes; byte b of either picks a table row
+          const uint32_t ev = cur[X].k[w] & 0x0F0F0F0Fu, od = (cur[X].k[w] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const uint32_t sel = 0x0C0C0400u | ((4u + b) << 8);   // (byte b << 8) | 4 lane
+            kd[X][8 * w + 2 * b] = *reinterpret_cast<const uint32_t*>(
+                reinterpret_cast<const uint8_t*>(sm.tk) + __builtin_amdgcn_perm(ev, lane4, sel));
+            kd[X][8 * w + 2 * b + 1] = *reinterpret_cast<const uint32_t*>(
+                reinterpret_cast<const uint8_t*>(sm.tk) + __builtin_amdgcn_perm(od, lane4, sel));
+          }
+        }
+    } else {
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint2 t = s_tk2[field<2 * BITS>(cur[X].k, i)];
+          kd[X][2 * i] = t.x;
+          kd[X][2 * i + 1] = t.y;
+        }
+    }
+    f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int X = 0; X < 2; ++X) {
+        const u32x4 av = {kd[X][4 * st], kd[X][4 * st + 1], kd[X][4 * st + 2], kd[X][4 * st + 3]};
+        c[X] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                       __builtin_bit_cast(bf16x8, qreg[st]), c[X], 0, 0, 0);
+      }
+    // ---- value operands: table reads issued before the softmax needs them
+    // (tile t = dims 8m+t; the A operand pairs tokens (4g, 4g+1),
+    // (4g+2, 4g+3) of each block)
+    u32x4 va[8];
+    if constexpr (kRep) {
+      // per token word: even / odd nibbles (dims 8m + t) as bytes, one
+      // 16-bit table read per code, two tokens per operand dword
+      const uint8_t* tvb = reinterpret_cast<const uint8_t*>(sm.tv);
+      uint32_t ve[2][4], vo[2][4];
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ve[X][i] = cur[X].v[i] & 0x0F0F0F0Fu;
+          vo[X][i] = (cur[X].v[i] >> 4) & 0x0F0F0F0Fu;
+        }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t sel = 0x0C0C0400u | ((4u + (t >> 1)) << 8);
+        uint32_t d[4];
+#pragma unroll
+        for (int X = 0; X < 2; ++X)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t wa = (t & 1) ? vo[X][2 * q] : ve[X][2 * q];
+            const uint32_t wb = (t & 1) ? vo[X][2 * q + 1] : ve[X][2 * q + 1];
+            const uint32_t lo = *reinterpret_cast<const uint16_t*>(tvb + __builtin_amdgcn_perm(wa, lane4, sel));
+            const uint32_t hi = *reinterpret_cast<const uint16_t*>(tvb + __builtin_amdgcn_perm(wb, lane4, sel));
+            d[2 * X + q] = lo | (hi << 16);
+          }
+        va[t] = (u32x4){d[0], d[1], d[2], d[3]};
+      }
+    } else {
+      uint32_t iv[4][8];   // [word pair][t]: code(first) | code(second) << BITS
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint32_t wa = cur[X].v[2 * q], wb = cur[X].v[2 * q + 1];
+          constexpr uint32_t mask = (1u << BITS) - 1;
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            iv[2 * X + q][t] = ((wa >> (BITS * t)) & mask) | (((wb >> (BITS * t)) & mask) << BITS);
+        }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) va[t] = (u32x4){s_tv2[iv[0][t]], s_tv2[iv[1][t]], s_tv2[iv[2][t]], s_tv2[iv[3][t]]};
+    }
+
     float s[2][4];
 #pragma unroll
     for (int X = 0; X < 2; ++X) {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const uint2 t0 = s_tk2[field<2 * BITS>(cur[X].k, 2 * st)];
-        const uint2 t1 = s_tk2[field<2 * BITS>(cur[X].k, 2 * st + 1)];
-        const u32x4 av = {t0.x, t0.y, t1.x, t1.y};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                    __builtin_bit_cast(bf16x8, s_qb[st][lane]), c, 0, 0, 0);
-      }
-      const int lb = sb0 + 2 * pi + X;
       float cs[4];
-      add_col_pairs(c, cs);
+      add_col_pairs(c[X], cs);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float v = cs[j];
         const float gk = (j & 1) ? half_hi(cur[X].gk[j >> 1]) : half_lo(cur[X].gk[j >> 1]);
-        const int tok = lb * kBlock + 4 * g + j;
-        v = (lb < sb1 && tok < seq_len) ? v * gk * sscale : -INFINITY;
-        s[X][j] = v;
-        if (LOGITS && !col_lo && col_live && lb < sb1 && tok < seq_len)
-          a.logits[((int64_t)n * Hq + (int64_t)h * a.group + g0 + m) * a.logits_stride + tok] = v * (1.f / LOG2E);
+        s[X][j] = cs[j] * gk;
+      }
+    }
+    if ((lb0 + 2) * kBlock > tok_end) {   // pair reaches past the split's last token
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if ((lb0 + X) * kBlock + 4 * g + j >= tok_end) s[X][j] = -INFINITY;
+    }
+    if constexpr (LOGITS) {
+      if (!col_lo && col_live) {
+        float* lrow = a.logits + ((int64_t)n * Hq + (int64_t)h * a.group + g0 + m) * a.logits_stride;
+#pragma unroll
+        for (int X = 0; X < 2; ++X)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int tok = (lb0 + X) * kBlock + 4 * g + j;
+            if (tok < tok_end) lrow[tok] = s[X][j] * (1.f / LOG2E);
+          }
       }
     }
     // ---- online softmax over the 32 tokens (per head = per column pair)
@@ -283,84 +547,68 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a, in
       for (int t = 0; t < 8; ++t) acc[t] *= alpha;
     }
     run_m = new_m;
+    const float mref = (new_m == -INFINITY) ? 0.f : new_m;   // all masked: exp2(-inf) = 0
     uint32_t pw[2][2];
-#pragma unroll
-    for (int X = 0; X < 2; ++X) {
-      uint32_t hv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p = (new_m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[X][j] - new_m);
-        run_l += p;
-        const float gv = (j & 1) ? half_hi(cur[X].gv[j >> 1]) : half_lo(cur[X].gv[j >> 1]);
-        const float pv = p * gv;
-        // columns 0..7 take f16(pv), columns 8..15 its f16 residual; no
-        // branches here (a branch would make the compiler wait for every
-        // outstanding load, including the prefetched block pair)
-        const float hi = __half2float(__float2half_rn(pv));
-        hv[j] = f16_bits(col_lo ? pv - hi : pv) & live_mask;
-      }
-      pw[X][0] = hv[0] | (hv[1] << 16);
-      pw[X][1] = hv[2] | (hv[3] << 16);
-    }
-    const u32x4 pb = {pw[0][0], pw[0][1], pw[1][0], pw[1][1]};
-    // ---- values: one product per 8-dim tile t (dims 8m+t); the A operand
-    // pairs tokens (4g, 4g+1), (4g+2, 4g+3) of each block
-    uint32_t iv[4][8];   // [word pair][t]: code(first) | code(second) << BITS
 #pragma unroll
     for (int X = 0; X < 2; ++X)
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const uint32_t wa = cur[X].v[2 * q], wb = cur[X].v[2 * q + 1];
-        if constexpr (BITS == 4) {
-          // interleave nibbles: byte k of ev = (a_{2k}, b_{2k}), of od = (a_{2k+1}, b_{2k+1})
-          const uint32_t ev = (wa & 0x0F0F0F0Fu) | ((wb & 0x0F0F0F0Fu) << 4);
-          const uint32_t od = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
+        float pv[2];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            iv[2 * X + q][2 * k] = (ev >> (8 * k)) & 0xFFu;
-            iv[2 * X + q][2 * k + 1] = (od >> (8 * k)) & 0xFFu;
-          }
-        } else {
-          constexpr uint32_t mask = (1u << BITS) - 1;
-#pragma unroll
-          for (int t = 0; t < 8; ++t)
-            iv[2 * X + q][t] = ((wa >> (BITS * t)) & mask) | (((wb >> (BITS * t)) & mask) << BITS);
+        for (int u = 0; u < 2; ++u) {
+          const float p = __builtin_amdgcn_exp2f(s[X][2 * q + u] - mref);
+          run_l += p;
+          const float gv = u ? half_hi(cur[X].gv[q]) : half_lo(cur[X].gv[q]);
+          pv[u] = p * gv;
         }
+        // columns 0..7 take f16(pv) (rounded toward zero), columns 8..15 the
+        // f16 of its residual, which is exact in f32
+        const auto hi = __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]);
+        const auto lo = __builtin_amdgcn_cvt_pkrtz(pv[0] - (float)hi[0], pv[1] - (float)hi[1]);
+        const uint32_t w = col_lo ? __builtin_bit_cast(uint32_t, lo) : __builtin_bit_cast(uint32_t, hi);
+        pw[X][q] = w & live_mask;
       }
+    const u32x4 pb = {pw[0][0], pw[0][1], pw[1][0], pw[1][1]};
+    // ---- values: one product per 8-dim tile
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const u32x4 av = {s_tv2[iv[0][t]], s_tv2[iv[1][t]], s_tv2[iv[2][t]], s_tv2[iv[3][t]]};
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av),
+    for (int t = 0; t < 8; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, va[t]),
                                                      __builtin_bit_cast(f16x8, pb), acc[t], 0, 0, 0);
-    }
   };
 
-  // Two register sets in turn (no copies, so a wait only covers the older
-  // set).  Prefetches are unconditional, past the split's end they re-read
-  // block 0 (never used): with a fixed number of loads in flight the
-  // compiler can wait for just the older set.
-  BlockRegs<BITS> ra[2], rb[2];
-  int pi = wv;
-  load_pair(ra, pi);
-  for (; pi < npairs; pi += 8) {
-    load_pair(rb, pi + 4);
-    compute_pair(ra, pi);
-    if (pi + 4 >= npairs) break;
-    load_pair(ra, pi + 8);
-    compute_pair(rb, pi + 4);
+  // ---- main loop: wait for stage k, read it, refill it with pair k + NS
+  // (its block-table entries were fetched one iteration earlier)
+  const uint8_t* ring = s_ring + wv * C::kWaveRing;
+  int nb0 = 0, nb1 = 0;
+  if (NS < my_n) fetch_pair(NS, nb0, nb1);
+  for (int k = 0; k < my_n; ++k) {
+    wait_pairs_behind<BITS>(min(NS - 1, my_n - 1 - k));
+    const uint8_t* st = ring + (k % NS) * 2 * C::kSlot;
+    BlockRegs<BITS> cur[2];
+    read_chunk<BITS>(cur[0], st, m, g);
+    read_chunk<BITS>(cur[1], st + C::kSlot, m, g);
+    if (k + NS < my_n) {
+      // the stage is overwritten only after this wave's reads of it are done
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      dma_pair(k + NS, nb0, nb1);
+      if (k + NS + 1 < my_n) fetch_pair(k + NS + 1, nb0, nb1);
+    }
+    compute_pair(cur, sb0 + 2 * (wv + 4 * k));
   }
 
-  // ---- merge the 4 waves of the workgroup
+  // ---- merge the 4 waves of the workgroup (each wave's accumulator goes
+  // into its own ring, whose copies have all been waited for)
   run_l += __shfl_xor(run_l, 16);
   run_l += __shfl_xor(run_l, 32);
   if (g == 0 && m < 8) {
     s_wm[wave][m] = run_m;
     s_wl[wave][m] = run_l;
   }
+  float* s_acc = reinterpret_cast<float*>(s_ring + wave * C::kWaveRing);   // [column][kAccRow]
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s_acc[wave][m][8 * (4 * g + j) + t] = acc[t][j];
+    for (int j = 0; j < 4; ++j) s_acc[m * kAccRow + 8 * (4 * g + j) + t] = acc[t][j];
   __syncthreads();
 
   const int64_t nsplit = a.num_splits;
@@ -382,7 +630,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a, in
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float mw = s_wm[w][hd];
-      if (mw != -INFINITY) o += __builtin_amdgcn_exp2f(mw - M) * (s_acc[w][hd][d] + s_acc[w][hd + 8][d]);
+      const float* sa = reinterpret_cast<const float*>(s_ring + w * C::kWaveRing);
+      if (mw != -INFINITY) o += __builtin_amdgcn_exp2f(mw - M) * (sa[hd * kAccRow + d] + sa[(hd + 8) * kAccRow + d]);
     }
     part_base[((int64_t)split * a.group + g0 + hd) * kPartStride + d] = o;
   }
@@ -392,11 +641,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a, in
     pp[128] = s_ml[0][tid] * (1.f / LOG2E);
     pp[129] = s_ml[1][tid];
   }
-
 }
 
 int launch_decode_mfma(const DecodeArgs& a, int bits, int ns, int gs, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // the kernel's chunk geometry is fixed at compile time: values, no sidecar
+  const int64_t expect = 512 * bits + 64;
+  if (a.lay.block_bytes != expect || a.lay.off_k != 0 || a.lay.off_v != 256 * bits ||
+      a.lay.off_gk != 512 * bits || a.lay.off_gv != 512 * bits + 32 ||
+      (reinterpret_cast<uintptr_t>(a.pool) & 15) != 0)
+    return (int)hipErrorInvalidValue;
   dim3 grid((unsigned)a.num_splits, (unsigned)(a.num_kv_heads * ns), (unsigned)a.num_seqs);
   const bool lg = a.logits != nullptr;
   switch (bits) {

@@ -275,19 +275,20 @@ int check_device() {
 }
 
 // Blocks per split of a decode launch.  The matrix-core kernel keeps no
-// per-split score buffer, so its splits are sized for about two workgroups
-// per CU (256 CUs); the vector kernel stages its split's scores in LDS and
-// caps a split at 64 blocks.  A decode-attend launch has at most kMaxSplits
-// splits per (sequence, KV head) (the merge keeps one weight per split in
-// LDS).  TQ_BLOCKS_PER_SPLIT overrides (tuning only).  Returns 0 when no valid
-// split size exists.
+// per-split score buffer, so its splits are sized for one round of three
+// workgroups per CU (256 CUs); the vector kernel stages its split's scores in
+// LDS and caps a split at 64 blocks.  A decode-attend launch has at most
+// kMaxSplits splits per (sequence, KV head), which bounds the workspace.
+// TQ_BLOCKS_PER_SPLIT overrides (tuning only).  Returns 0 when no valid split
+// size exists.
 int blocks_per_split_for(const tq_cache* c, int32_t num_seqs, int32_t group, int32_t max_blocks, bool mfma,
                          bool attend) {
   const int64_t units = (int64_t)num_seqs * c->cfg.num_kv_heads * tq::decode_slices(group);
   const int64_t cap = mfma ? ((int64_t)1 << 30) : 64;
   int64_t bps;
   if (mfma) {
-    bps = ((int64_t)max_blocks * units + 511) / 512;
+    // three 256-thread workgroups fit on a CU: aim for one such wave of them
+    bps = ((int64_t)max_blocks * units + 767) / 768;
     if (bps < 8) bps = 8;
   } else {
     bps = ((int64_t)max_blocks * units + 1023) / 1024;
@@ -318,6 +319,8 @@ int validate_decode(const void* q, int32_t q_dtype, const tq_cache* cache,
     return fail(TQ_ERR_INVALID_ARG, "null pointer");
   if (q_dtype != TQ_F32 && q_dtype != TQ_F16 && q_dtype != TQ_BF16)
     return fail(TQ_ERR_INVALID_ARG, "bad q dtype");
+  if (num_seqs > 0 && (reinterpret_cast<uintptr_t>(q) & 15) != 0)
+    return fail(TQ_ERR_INVALID_ARG, "q must be 16-byte aligned");
   const int hkv = cache->cfg.num_kv_heads;
   if (num_q_heads < hkv || num_q_heads % hkv != 0)
     return fail(TQ_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");

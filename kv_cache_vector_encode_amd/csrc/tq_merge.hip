@@ -2,7 +2,7 @@
 // (sequence, query head) and split of the sequence, the unnormalised
 // rotated-frame output o_rot (128 floats), the split's running max m
 // (natural-log units) and exp-sum l.  One workgroup per (sequence, query head)
-// merges them in split order (deterministic), normalises and rotates back:
+// merges them in a fixed order (deterministic), normalises and rotates back:
 // o = R^T o_rot / L = D H o_rot / (sqrt(d) L)  (Bit-Axon "TurboQuant: KV Cache
 // Compression", attention softmax(Q K_hat^T / sqrt(d_h)) V_hat; deep-dive
 // blog Step 1, the inverse of the orthogonal rotation is its transpose).
@@ -13,81 +13,89 @@
 namespace tq {
 
 __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
-  __shared__ float s_w[kMaxSplits];
-  __shared__ float s_red[2][8];
+  __shared__ float s_m[8], s_l[8];
   __shared__ float4 s_part[8][32];
   __shared__ float4 s_o[32];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float s_L;
+  const int tid = threadIdx.x;
   const int hq = blockIdx.x, n = blockIdx.y;
   const int h = hq / a.group, g = hq - h * a.group;
   const int nsplit = a.num_splits;
   const int64_t stride = (int64_t)a.group * kPartStride;   // between splits
   const float* base = a.partials + ((int64_t)n * a.num_kv_heads + h) * nsplit * stride + (int64_t)g * kPartStride;
 
-  // 1. running max M and total L over the splits
-  float M = -INFINITY;
-  for (int s = tid; s < nsplit; s += 256) {
-    const float* pp = base + s * stride;
-    if (pp[129] > 0.f) M = fmaxf(M, pp[128]);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) s_red[0][wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
-  float L = 0.f;
-  for (int s = tid; s < nsplit; s += 256) {
-    const float* pp = base + s * stride;
-    const float l = pp[129];
-    const float w = l > 0.f ? __expf(pp[128] - M) : 0.f;
-    s_w[s] = w;
-    L = __builtin_fmaf(l, w, L);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
-  if (lane == 0) s_red[1][wave] = L;
-  __syncthreads();
-  L = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
-
-  // 2. weighted sum of o_rot: thread -> (4 dims c4, every 8th split from sg)
+  // 1. thread (c4, sg) takes dims 4c4..4c4+3 of splits sg, sg+8, ...: up
+  // to 16 of them per round, all loads issued before any arithmetic (one
+  // memory round trip), then a local max / weights / sums in registers
   {
     const int c4 = tid & 31, sg = tid >> 5;
+    float M = -INFINITY, L = 0.f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    int s = sg;
-    for (; s + 24 < nsplit; s += 32) {
-      float4 v[4];
+    for (int s0 = sg; s0 < nsplit; s0 += 8 * 16) {
+      float ms[16], ls[16];
+      float4 v[16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(base + (s + 8 * u) * stride + 4 * c4);
+      for (int u = 0; u < 16; ++u) {
+        const int s = s0 + 8 * u;
+        if (s < nsplit) {
+          const float* pp = base + s * stride;
+          ms[u] = pp[128];
+          ls[u] = pp[129];
+          v[u] = *reinterpret_cast<const float4*>(pp + 4 * c4);
+        } else {
+          ms[u] = -INFINITY;
+          ls[u] = 0.f;
+          v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+      float Mn = M;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float w = s_w[s + 8 * u];
+      for (int u = 0; u < 16; ++u)
+        if (ls[u] > 0.f) Mn = fmaxf(Mn, ms[u]);
+      if (Mn == -INFINITY) continue;   // nothing in these splits yet
+      const float r = M == -INFINITY ? 0.f : __expf(M - Mn);
+      L *= r;
+      o.x *= r; o.y *= r; o.z *= r; o.w *= r;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float w = ls[u] > 0.f ? __expf(ms[u] - Mn) : 0.f;
+        L = __builtin_fmaf(ls[u], w, L);
         o.x = __builtin_fmaf(w, v[u].x, o.x);
         o.y = __builtin_fmaf(w, v[u].y, o.y);
         o.z = __builtin_fmaf(w, v[u].z, o.z);
         o.w = __builtin_fmaf(w, v[u].w, o.w);
       }
+      M = Mn;
     }
-    for (; s < nsplit; s += 8) {
-      const float4 v = *reinterpret_cast<const float4*>(base + s * stride + 4 * c4);
-      const float w = s_w[s];
+    s_part[sg][c4] = o;
+    if (c4 == 0) {
+      s_m[sg] = M;
+      s_l[sg] = L;
+    }
+  }
+  __syncthreads();
+  // 2. combine the 8 groups (in fixed order)
+  if (tid < 32) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) M = fmaxf(M, s_m[k]);
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float w = s_m[k] == -INFINITY ? 0.f : __expf(s_m[k] - M);
+      const float4 v = s_part[k][tid];
+      L = __builtin_fmaf(s_l[k], w, L);
       o.x = __builtin_fmaf(w, v.x, o.x);
       o.y = __builtin_fmaf(w, v.y, o.y);
       o.z = __builtin_fmaf(w, v.z, o.z);
       o.w = __builtin_fmaf(w, v.w, o.w);
     }
-    s_part[sg][c4] = o;
-  }
-  __syncthreads();
-  if (tid < 32) {
-    float4 o = s_part[0][tid];
-#pragma unroll
-    for (int k = 1; k < 8; ++k) {
-      const float4 v = s_part[k][tid];
-      o.x += v.x; o.y += v.y; o.z += v.z; o.w += v.w;
-    }
     s_o[tid] = o;
+    if (tid == 0) s_L = L;
   }
   __syncthreads();
+  const float L = s_L;
 
   // 3. normalise and rotate back in one 16-lane row
   if (tid >= 16) return;
