@@ -243,12 +243,12 @@ static int launch_b(const DecodeArgs& a, bool qjl, int ns, int gs, hipStream_t s
   return launch_g<B, ATTEND ? B : 2, false, ATTEND>(a, ns, gs, s);
 }
 
-int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int attend, void* stream) {
+int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int attend, int mfma, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int ns = (a.group + 7) / 8;
   const int gs = (a.group + ns - 1) / ns;
   if (attend && bits_v != bits_k) return (int)hipErrorInvalidValue;
-  if (attend && !qjl) {
+  if (attend && mfma && !qjl) {
     const int e = launch_decode_mfma(a, bits_k, ns, gs, stream);
     return e ? e : launch_merge(a, stream);
   }

@@ -303,12 +303,18 @@ int blocks_per_split_for(const tq_cache* c, int32_t num_seqs, int32_t group, int
     if (bps < min_bps) bps = min_bps;
   }
   if (mfma) bps = (bps + 1) & ~(int64_t)1;
-  if (bps > cap) bps = attend ? 0 : cap;
-  if (attend && bps > 0 && ((int64_t)max_blocks + bps - 1) / bps > tq::kMaxSplits) bps = 0;
+  if (bps > cap) bps = cap;
+  if (attend && ((int64_t)max_blocks + bps - 1) / bps > tq::kMaxSplits) bps = 0;
   return (int)bps;
 }
 
-bool decode_uses_mfma(const tq_cache* c, bool attend) { return attend && !c->cfg.qjl; }
+// Decode-attend without a QJL sidecar runs on the matrix cores.
+// TQ_DECODE_VALU=1 selects the vector-unit kernel instead (comparison only).
+bool decode_uses_mfma(const tq_cache* c, bool attend) {
+  if (const char* env = std::getenv("TQ_DECODE_VALU"))
+    if (std::atoi(env) == 1) return false;
+  return attend && !c->cfg.qjl;
+}
 
 int validate_decode(const void* q, int32_t q_dtype, const tq_cache* cache,
                     const int32_t* block_tables, const int32_t* seq_lens,
@@ -542,7 +548,8 @@ int tq_decode_attend(const void* q, int32_t q_dtype, const tq_cache* cache,
   if (a.blocks_per_split <= 0) return fail(TQ_ERR_UNSUPPORTED, "sequence too long for this cache's decode kernel");
   a.num_splits = std::max(1, (max_blocks_per_seq + a.blocks_per_split - 1) / a.blocks_per_split);
   a.partials = static_cast<float*>(workspace);
-  int err = tq::launch_decode(a, cache->cfg.bits_k, cache->cfg.bits_v, cache->cfg.qjl, 1, hip_stream);
+  int err = tq::launch_decode(a, cache->cfg.bits_k, cache->cfg.bits_v, cache->cfg.qjl, 1,
+                              decode_uses_mfma(cache, true) ? 1 : 0, hip_stream);
   if (err != 0) return hip_fail(err, "decode launch");
   return TQ_OK;
 }
@@ -564,7 +571,7 @@ int tq_decode_logits(const void* q, int32_t q_dtype, const tq_cache* cache,
   a.logits_stride = (int64_t)max_blocks_per_seq * tq::kBlock;
   a.blocks_per_split = blocks_per_split_for(cache, num_seqs, a.group, max_blocks_per_seq, false, false);
   a.num_splits = std::max(1, (max_blocks_per_seq + a.blocks_per_split - 1) / a.blocks_per_split);
-  int err = tq::launch_decode(a, cache->cfg.bits_k, 0, cache->cfg.qjl, 0, hip_stream);
+  int err = tq::launch_decode(a, cache->cfg.bits_k, 0, cache->cfg.qjl, 0, 0, hip_stream);
   if (err != 0) return hip_fail(err, "logits launch");
   return TQ_OK;
 }

@@ -117,7 +117,7 @@ struct ReconArgs {
 
 // Launchers implemented in the .hip files; return a hipError_t value.
 int launch_encode(const EncodeArgs& a, int num_streams, int in_dtype, void* stream);
-int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int attend, void* stream);
+int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int attend, int mfma, void* stream);
 int decode_slices(int group);
 int launch_decode_mfma(const DecodeArgs& a, int bits, int ns, int gs, void* stream);
 int launch_merge(const DecodeArgs& a, void* stream);

@@ -12,6 +12,7 @@
 
 namespace tq {
 
+template <int U>
 __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
   __shared__ float s_m[8], s_l[8];
   __shared__ float4 s_part[8][32];
@@ -24,40 +25,37 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
   const int64_t stride = (int64_t)a.group * kPartStride;   // between splits
   const float* base = a.partials + ((int64_t)n * a.num_kv_heads + h) * nsplit * stride + (int64_t)g * kPartStride;
 
-  // 1. thread (c4, sg) takes dims 4c4..4c4+3 of splits sg, sg+8, ...: up
-  // to 16 of them per round, all loads issued before any arithmetic (one
-  // memory round trip), then a local max / weights / sums in registers
+  // 1. thread (c4, sg) takes dims 4c4..4c4+3 of splits sg, sg+8, ...: U of
+  // them per round (U covers the split count when it is at most 128), all
+  // loads issued before any arithmetic (one memory round trip), then a local
+  // max / weights / sums in registers
   {
     const int c4 = tid & 31, sg = tid >> 5;
     float M = -INFINITY, L = 0.f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = sg; s0 < nsplit; s0 += 8 * 16) {
-      float ms[16], ls[16];
-      float4 v[16];
+    for (int s0 = sg; s0 < nsplit; s0 += 8 * U) {
+      float ms[U], ls[U];
+      float4 v[U];
+      // unconditional loads (indices past the end re-read the last split and
+      // are masked below): a branch per load would serialise them
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int s = s0 + 8 * u;
-        if (s < nsplit) {
-          const float* pp = base + s * stride;
-          ms[u] = pp[128];
-          ls[u] = pp[129];
-          v[u] = *reinterpret_cast<const float4*>(pp + 4 * c4);
-        } else {
-          ms[u] = -INFINITY;
-          ls[u] = 0.f;
-          v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+      for (int u = 0; u < U; ++u) {
+        const float* pp = base + min(s0 + 8 * u, nsplit - 1) * stride;
+        const float2 ml = *reinterpret_cast<const float2*>(pp + 128);
+        ms[u] = ml.x;
+        ls[u] = s0 + 8 * u < nsplit ? ml.y : 0.f;
+        v[u] = *reinterpret_cast<const float4*>(pp + 4 * c4);
       }
       float Mn = M;
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
+      for (int u = 0; u < U; ++u)
         if (ls[u] > 0.f) Mn = fmaxf(Mn, ms[u]);
       if (Mn == -INFINITY) continue;   // nothing in these splits yet
       const float r = M == -INFINITY ? 0.f : __expf(M - Mn);
       L *= r;
       o.x *= r; o.y *= r; o.z *= r; o.w *= r;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < U; ++u) {
         const float w = ls[u] > 0.f ? __expf(ms[u] - Mn) : 0.f;
         L = __builtin_fmaf(ls[u], w, L);
         o.x = __builtin_fmaf(w, v[u].x, o.x);
@@ -116,7 +114,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
 
 int launch_merge(const DecodeArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(256), 0, s, a);
+  const dim3 grid((unsigned)a.num_q_heads, (unsigned)a.num_seqs);
+  const int per = (a.num_splits + 7) / 8;   // splits per thread group
+  if (per <= 1) hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(256), 0, s, a);
+  else if (per <= 2) hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(256), 0, s, a);
+  else if (per <= 4) hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(256), 0, s, a);
+  else if (per <= 8) hipLaunchKernelGGL(merge_kernel<8>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(merge_kernel<16>, grid, dim3(256), 0, s, a);
   return (int)hipGetLastError();
 }
 

@@ -166,3 +166,18 @@ def test_no_device_is_reported_without_touching_memory():
     c = _fake_cache()
     st = tq.lib().tq_encode_kv(0x200000, 0x300000, 2, 10, 0x400000, 4, c.handle, None)
     assert st == tq.TQ_ERR_NO_DEVICE
+
+
+def test_qjl_attend_split_sizes_for_long_sequences():
+    # The QJL decode-attend kernel caps a split at 64 blocks; long sequences
+    # take more splits (up to 4096 per sequence and KV head), not an error.
+    r, rq = tq.tq_make_rotation(42, 128), tq.tq_make_rotation(43, 128)
+    cfg = tq.make_config(8, 4, 4, 4, r, qjl=True, rot_qjl=rq)
+    c = tq.tq_cache_create(cfg, 0x100000)
+    c._rots = (r, rq)
+    L = tq.lib()
+    # 4 sequences of 131072 tokens: 8192 blocks -> 128 splits of 64 blocks
+    n = L.tq_decode_workspace_bytes(c.handle, 4, 64, 8192)
+    assert n == 4 * 8 * 128 * 8 * 132 * 4
+    assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 64 * 4096) > 0
+    assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 64 * 4096 + 1) == tq.TQ_ERR_UNSUPPORTED
