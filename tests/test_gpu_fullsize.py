@@ -1,0 +1,251 @@
+"""GPU parity at the full sizes of the benchmark configurations.
+
+* decode_1x32768_h8_gqa8_b4 and prefill_16x8192_h8_gqa8_b4: one
+  tq_encode_kv of every key and value, then tq_decode_attend without
+  logits (the launch configuration bench.py times) and with logits; codes
+  and norms of sampled token windows, and outputs / logits of sampled
+  (sequence, query head) pairs, against the oracle computed one by one.
+* llama70b_4x131072_h8_gqa8_b3: the same, with the encode split into one
+  call per sequence (host memory), decode as in bench.py.
+* sweep_16h_65536_keys: keys-only caches for b = 2, 3, 4 with and without
+  the QJL residual; tq_decode_logits for one query per head; parity of codes
+  and logits on exactly 10^5 seeded (head, token) pairs, plus the logit bias
+  and MSE against the unquantised keys (reported; the QJL variant must lower
+  the MSE).
+"""
+
+import functools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_vector_encode_amd import tq
+from kv_cache_vector_encode_amd import workloads as W
+from oracle import tq_oracle as O
+
+from gpu_common import (LOGIT_RTOL, OUT_RTOL, check_codes, check_norms, cs_scale, make_cache,
+                        to_device)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _chunks(cache, w, blocks, head=None):
+    """Pool bytes of the given physical blocks (all heads, or one head) and an
+    oracle layout describing exactly that sub-pool."""
+    lay_full = O.LayoutV1(128, w.num_kv_heads, w.bits_k, w.bits_v, w.qjl, w.num_blocks)
+    view = cache.pool.view(w.num_blocks, w.num_kv_heads, lay_full.block_bytes)
+    idx = torch.from_numpy(np.asarray(blocks, dtype=np.int64)).to(cache.pool.device)
+    sub = view.index_select(0, idx)
+    if head is not None:
+        sub = sub[:, head:head + 1]
+    arr = sub.contiguous().cpu().numpy()
+    lay = O.LayoutV1(128, arr.shape[1], w.bits_k, w.bits_v, w.qjl, arr.shape[0])
+    return arr, lay
+
+
+def _encode_all(w, device, per_call_tokens=None):
+    cache = make_cache(w, device)
+    slots = W.slot_mapping(w)
+    n = w.tokens if per_call_tokens is None else per_call_tokens
+    for t0 in range(0, w.tokens, n):
+        cnt = min(n, w.tokens - t0)
+        kb, _ = W.keys(w, t0, cnt)
+        vb, _ = W.values(w, t0, cnt)
+        K, V = to_device(kb, w.in_dtype, device), to_device(vb, w.in_dtype, device)
+        del kb, vb
+        sm = torch.from_numpy(np.ascontiguousarray(slots[t0:t0 + cnt])).to(device)
+        tq.tq_encode_kv(K, V, sm, w.bits_k, cache)
+        torch.cuda.synchronize()
+        del K, V
+    return cache, slots
+
+
+def _check_encode_windows(w, cache, slots, rng, windows=4, width=256):
+    c32, t32 = O.codebook_fp32(128, w.bits_k)
+    starts = rng.choice(w.tokens // width, windows, replace=False) * width
+    worst = 0
+    for t0 in starts:
+        k64 = W.keys(w, int(t0), width)[1]
+        v64 = W.values(w, int(t0), width)[1]
+        s = slots[t0:t0 + width]
+        blocks, inv = np.unique(s // 16, return_inverse=True)
+        arr, lay = _chunks(cache, w, blocks)
+        up = O.unpack_pool(arr, lay)
+        for name, x64, ki, kg in (("K", k64, "k_idx", "k_g16"), ("V", v64, "v_idx", "v_g16")):
+            enc = O.encode(x64.reshape(-1, 128), w.rot_seed, c32)
+            gidx = up[ki][inv, :, s % 16].reshape(-1, 128)
+            g16 = up[kg][inv, :, s % 16].reshape(-1)
+            worst = max(worst, check_codes(gidx, enc["idx"], enc["y"], t32, what=f"{name} window {t0}"))
+            check_norms(g16, enc["gamma"], what=f"{name} norms window {t0}")
+    return worst
+
+
+def _check_decode_pairs(w, cache, pairs, out, logits=None):
+    c32k, _ = O.codebook_fp32(128, w.bits_k)
+    c32v, _ = O.codebook_fp32(128, w.bits_v)
+    bt = W.block_tables(w)
+    _, q64 = W.queries(w)
+    group = w.num_q_heads // w.num_kv_heads
+    R = O.rotation_matrix(w.rot_seed, 128)
+    tau = 1 / math.sqrt(128)
+    go = out.cpu().numpy().astype(np.float64)
+    gl = logits.cpu().numpy() if logits is not None else None
+    worst_o = worst_l = 0.0
+    for n, hq in pairs:
+        h = hq // group
+        L = w.seq_len
+        arr, lay = _chunks(cache, w, bt[n, :w.blocks_per_seq], head=h)
+        up = O.unpack_pool(arr, lay)
+        kidx = up["k_idx"][:, 0].reshape(-1, 128)[:L]
+        kg = up["k_g16"][:, 0].reshape(-1)[:L]
+        khat = O.reconstruct(kidx, kg, w.rot_seed, c32k)
+        vhat = O.reconstruct(up["v_idx"][:, 0].reshape(-1, 128)[:L], up["v_g16"][:, 0].reshape(-1)[:L],
+                             w.rot_seed, c32v)
+        o, s = O.attention(q64[n, hq], khat, vhat)
+        e = np.linalg.norm(go[n, hq] - o) / np.linalg.norm(o)
+        assert e <= OUT_RTOL, (n, hq, e)
+        worst_o = max(worst_o, e)
+        if gl is not None:
+            scl = cs_scale(tau, kg, np.linalg.norm(R @ q64[n, hq]), np.linalg.norm(c32k[kidx], axis=1))
+            err = np.abs(gl[n, hq, :L].astype(np.float64) - s)
+            assert np.all(err <= LOGIT_RTOL * scl), (n, hq, float((err / scl).max()))
+            worst_l = max(worst_l, float((err / scl).max()))
+    return worst_o, worst_l
+
+
+def _decode(w, cache, device, want_logits):
+    bt = torch.from_numpy(W.block_tables(w)).to(device)
+    lens = torch.from_numpy(W.seq_lens(w)).to(device)
+    qb, _ = W.queries(w)
+    q = to_device(qb, "bf16", device)
+    out = torch.full((w.num_seqs, w.num_q_heads, 128), float("nan"), device=device)
+    logits = None
+    if want_logits:
+        logits = torch.full((w.num_seqs, w.num_q_heads, bt.shape[1] * 16), float("nan"), device=device)
+    ws = tq.new_workspace(cache, w.num_seqs, w.num_q_heads, bt.shape[1], device=device)
+    tq.tq_decode_attend(q, cache, bt, lens, out, ws, logits_out=logits)
+    torch.cuda.synchronize()
+    return out, logits
+
+
+@pytest.mark.parametrize("name,npairs", [("decode_1x32768_h8_gqa8_b4", 8), ("prefill_16x8192_h8_gqa8_b4", 8)])
+def test_fullsize_encode_and_decode(device, name, npairs):
+    w = W.CONFIGS[name]
+    rng = np.random.default_rng(11)
+    _say(f"{name}: encode {2 * w.tokens * w.num_kv_heads} vectors")
+    cache, slots = _encode_all(w, device)
+    nb = _check_encode_windows(w, cache, slots, rng)
+    pairs = [(int(rng.integers(w.num_seqs)), int(hq)) for hq in rng.choice(w.num_q_heads, npairs, replace=False)]
+    out, _ = _decode(w, cache, device, want_logits=False)
+    wo, _ = _check_decode_pairs(w, cache, pairs, out)
+    out2, logits = _decode(w, cache, device, want_logits=True)
+    wo2, wl = _check_decode_pairs(w, cache, pairs, out2, logits)
+    _say(f"{name}: band mismatches {nb}; worst out {max(wo, wo2):.2e}; worst logit {wl:.2e} (bars 2e-3, 1e-4)")
+
+
+def test_fullsize_llama70b_b3(device):
+    w = W.LLAMA70B_128K
+    rng = np.random.default_rng(12)
+    _say(f"{w.name}: encode {2 * w.tokens * w.num_kv_heads} vectors, one call per sequence")
+    cache, slots = _encode_all(w, device, per_call_tokens=w.seq_len)
+    nb = _check_encode_windows(w, cache, slots, rng)
+    pairs = [(int(rng.integers(w.num_seqs)), int(rng.integers(w.num_q_heads))) for _ in range(4)]
+    out, _ = _decode(w, cache, device, want_logits=False)
+    wo, _ = _check_decode_pairs(w, cache, pairs, out)
+    out2, logits = _decode(w, cache, device, want_logits=True)
+    wo2, wl = _check_decode_pairs(w, cache, pairs[:2], out2, logits)
+    _say(f"{w.name}: band mismatches {nb}; worst out {max(wo, wo2):.2e}; worst logit {wl:.2e}")
+
+
+# ------------------------------------------------------------ sweep config --
+
+@functools.lru_cache(maxsize=1)
+def _sweep_keys():
+    w = W.SWEEP_64K
+    kb, k64 = W.keys(w)
+    return kb, k64
+
+
+def _sample_records(arr, lay, blocks, heads, rows):
+    """Oracle-unpacked records for the sampled (block, head, row) triples,
+    unpacking the pool a slice of blocks at a time."""
+    n = len(blocks)
+    out = {}
+    step = 256
+    for b0 in range(0, lay.num_blocks, step):
+        sel = np.nonzero((blocks >= b0) & (blocks < b0 + step))[0]
+        if len(sel) == 0:
+            continue
+        nb = min(step, lay.num_blocks - b0)
+        sub = arr[b0:b0 + nb]
+        up = O.unpack_pool(sub, O.LayoutV1(128, lay.hkv, lay.bk, lay.bv, lay.qjl, nb))
+        for k, v in up.items():
+            if k not in out:
+                out[k] = np.zeros((n,) + v.shape[3:], dtype=v.dtype)
+            out[k][sel] = v[blocks[sel] - b0, heads[sel], rows[sel]]
+    return out
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_sweep_logits_1e5_pairs(device, bits):
+    base = W.SWEEP_64K
+    kb, k64 = _sweep_keys()
+    K = to_device(kb, base.in_dtype, device)
+    rng = np.random.default_rng(2024 + bits)
+    NP = 100_000
+    heads = rng.integers(0, base.num_kv_heads, NP)
+    toks = rng.integers(0, base.tokens, NP)
+    qb, q64 = W.queries(base)             # one query per head (16 query heads)
+    q = to_device(qb, "bf16", device)
+    c32, t32 = O.codebook_fp32(128, bits)
+    R = O.rotation_matrix(base.rot_seed, 128)
+    tau = 1 / math.sqrt(128)
+    xs = k64[toks, heads]                 # the sampled exact keys
+    enc = O.encode(xs, base.rot_seed, c32)
+    s_exact = tau * np.einsum("nd,nd->n", xs, q64[0, heads])
+    mse = {}
+    for qjl in (False, True):
+        w = base.with_(bits_k=bits, qjl=qjl)
+        cache = make_cache(w, device)
+        slots = torch.from_numpy(W.slot_mapping(w)).to(device)
+        tq.tq_encode_kv(K, None, slots, bits, cache)
+        bt = torch.from_numpy(W.block_tables(w)).to(device)
+        lens = torch.from_numpy(W.seq_lens(w)).to(device)
+        logits = torch.full((1, w.num_q_heads, bt.shape[1] * 16), float("nan"), device=device)
+        tq.tq_decode_logits(q, cache, bt, lens, logits)
+        torch.cuda.synchronize()
+        lay = O.LayoutV1(128, w.num_kv_heads, bits, 0, qjl, w.num_blocks)
+        arr = cache.pool.cpu().numpy().reshape(w.num_blocks, w.num_kv_heads, lay.block_bytes)
+        s_map = W.slot_mapping(w)[toks]
+        rec = _sample_records(arr, lay, s_map // 16, heads, s_map % 16)
+        # codes and norms of the sampled keys
+        check_codes(rec["k_idx"], enc["idx"], enc["y"], t32, what=f"b{bits} qjl={qjl} codes")
+        check_norms(rec["k_g16"], enc["gamma"], what=f"b{bits} qjl={qjl} norms")
+        # logits: oracle from the GPU's codes, original frame
+        khat = O.reconstruct(rec["k_idx"], rec["k_g16"], base.rot_seed, c32)
+        s_or = tau * np.einsum("nd,nd->n", khat, q64[0, heads])
+        rho = None
+        if qjl:
+            qrot = q64[0, heads] @ R.T
+            est = O.qjl_dot_estimate(rec["qjl_bits"], rec["rho16"], qrot, base.qjl_seed)
+            s_or = s_or + tau * rec["k_g16"].astype(np.float64) * est
+            rho = rec["rho16"]
+        gl = logits.cpu().numpy()[0, heads, toks].astype(np.float64)
+        qn = np.linalg.norm(q64[0, heads] @ R.T, axis=1)
+        scl = cs_scale(tau, rec["k_g16"], qn, np.linalg.norm(c32[rec["k_idx"]], axis=1), rho)
+        err = np.abs(gl - s_or)
+        assert np.all(err <= LOGIT_RTOL * scl), f"b{bits} qjl={qjl}: worst {float((err / scl).max()):.3g}"
+        e = gl - s_exact
+        mse[qjl] = float(np.mean(e * e))
+        se = float(np.std(e) / math.sqrt(NP))
+        _say(f"sweep b={bits} qjl={qjl}: logit parity worst {float((err / scl).max()):.2e} of the bar; "
+             f"vs unquantised keys: bias {float(np.mean(e)):+.3e} (SE {se:.1e}), MSE {mse[qjl]:.3e}, "
+             f"normalised MSE {mse[qjl] / float(np.mean(s_exact ** 2)):.3e}")
+        del cache
+    assert mse[True] < 0.85 * mse[False], f"b{bits}: QJL did not lower the logit MSE ({mse})"
