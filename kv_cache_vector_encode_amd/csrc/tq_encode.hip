@@ -9,12 +9,22 @@
 // Step 1 (sign flip, Hadamard, 1/sqrt(d)) and Step 2 (fp16 magnitude plus
 // direction indices).
 //
-// Work mapping: one vector (d = 128) per 16-lane row, 8 coordinates per lane,
-// so a wave64 encodes 4 vectors at once and a 256-thread workgroup 16.  A
-// workgroup handles kIters such groups; all their input loads are issued
-// before any arithmetic so each lane has kIters 16-byte loads in flight.
-// A row's 16 lanes read the vector's 256 contiguous bytes (permuted among
-// the lanes, still one coalesced request) and write its code record.
+// Two kernels:
+//  * encode_mx_kernel (bf16 / f16 input, no QJL sidecar): the Hadamard
+//    product on the matrix cores, 16 vectors per wave; the norm, the bucketed
+//    threshold search and the packing stay on the vector ALUs (described at
+//    the kernel).
+//  * encode_kernel (fp32 input, or the QJL sidecar): one vector (d = 128)
+//    per 16-lane row, 8 coordinates per lane, the FWHT as in-lane butterflies
+//    plus DPP lane stages, so a wave64 encodes 4 vectors at once and a
+//    256-thread workgroup 16.  A workgroup handles kIters such groups; all
+//    their input loads are issued before any arithmetic.  A row's 16 lanes
+//    read the vector's 256 contiguous bytes (permuted among the lanes, still
+//    one coalesced request) and write its code record.
+
+#include <algorithm>
+#include <cstdlib>
+#include <type_traits>
 
 #include "tq_device.h"
 
@@ -22,21 +32,111 @@ namespace tq {
 
 constexpr int kIters = 4;
 
+// 8 input coordinates of one lane with the rotation's sign flips applied
+// through the raw bits: m[i] holds the sign masks of the i-th 32-bit word
+// (bits 15 / 31 for two 16-bit inputs, bit 31 for one fp32 input).
+template <int DT>
+__device__ __forceinline__ void load8_signed(const void* base, int64_t elem, const uint32_t (&m)[8], float (&x)[8]) {
+  if constexpr (DT == 0) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + elem);
+    const uint4 a = p[0], b = p[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(w[e] ^ m[e]);
+  } else {
+    const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+    const uint32_t w[4] = {r.x ^ m[0], r.y ^ m[1], r.z ^ m[2], r.w ^ m[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == 2) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      } else {
+        x[2 * i] = __half2float(__ushort_as_half((unsigned short)(w[i] & 0xFFFFu)));
+        x[2 * i + 1] = __half2float(__ushort_as_half((unsigned short)(w[i] >> 16)));
+      }
+    }
+  }
+}
+
+// Bucketed threshold search for one row (8 coordinates per lane): z = y_raw
+// * zs + lut_off in bucket units, bucket = nearest integer to z clamped to
+// [0, 255] by the conversion, code = base + (z > bucket threshold).
+template <int BITS>
+__device__ __forceinline__ void row_codes(const float (&x)[8], float zs, float lut_off, const uint2* s_lut,
+                                          uint32_t (&code)[8]) {
+  float z[8];
+  uint32_t key4[2] = {0u, 0u};   // four bucket indices per word
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    z[e] = __builtin_fmaf(x[e], zs, lut_off);
+    key4[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(z[e], e & 3, key4[e >> 2]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint2 ent = s_lut[(key4[e >> 2] >> (8 * (e & 3))) & 0xFFu];
+    code[e] = ent.y + (z[e] > __uint_as_float(ent.x) ? 1u : 0u);
+  }
+}
+
+// Lane L of a row holds the codes of coordinates 8L..8L+7; every lane of the
+// row takes part in the DPP exchanges.  Returns the 32-bit word this lane
+// stores (if store_lane) at byte store_off of the vector's record.
+template <int BITS>
+__device__ __forceinline__ uint32_t row_pack(const uint32_t (&code)[8], int L, bool& store_lane, int& store_off) {
+  uint32_t word = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) word |= code[e] << (BITS * e);
+  store_lane = true;
+  store_off = 4 * L;
+  if constexpr (BITS == 2) {
+    const uint32_t nb = dpp_u<kDppXor1>(word);
+    store_lane = (L & 1) == 0;
+    store_off = 2 * L;
+    return word | (nb << 16);
+  } else if constexpr (BITS == 3) {
+    const uint32_t nb = dpp_u<kDppQuadNext>(word);
+    const int q = L & 3;
+    store_lane = q < 3;
+    store_off = 12 * (L >> 2) + 4 * q;
+    return (word >> (8 * q)) | (q < 3 ? nb << (24 - 8 * q) : 0u);
+  }
+  return word;
+}
+
+// 256-entry bucket table in threshold-search units (entries past lut_n
+// repeat the last bucket, which holds no threshold).
+__device__ __forceinline__ void fill_lut(uint2* s_lut, const EncodeArgs& a, float lut_scale, float lut_off, int tid) {
+  const int k = min(tid, a.tab.lut_n - 1);
+  s_lut[tid] = make_uint2(__float_as_uint(__builtin_fmaf(a.tab.lut_thr[k], lut_scale, lut_off)),
+                          (uint32_t)a.tab.lut_base[k]);
+}
+
 template <int BITS, int DT, bool QJL>
 __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
-  __shared__ uint2 s_lut[kLutMax];
+  // Threshold search in bucket units: z = y * lut_scale + lut_offset - 1/2,
+  // bucket k = round-to-nearest(z) clamped to [0, 255] by the conversion
+  // (the floor of y * lut_scale + lut_offset away from bucket edges, which
+  // hold no threshold), code = base[k] + (z > threshold of bucket k in the
+  // same units).  Entries past the host's lut_n repeat its last bucket.
+  __shared__ uint2 s_lut[256];
   __shared__ float s_cent[16];
   const int tid = threadIdx.x;
-  if (tid < a.tab.lut_n) s_lut[tid] = make_uint2(__float_as_uint(a.tab.lut_thr[tid]), (uint32_t)a.tab.lut_base[tid]);
+  const float lut_scale = a.tab.lut_scale, lut_off = a.tab.lut_offset - 0.5f;
+  fill_lut(s_lut, a, lut_scale, lut_off, tid);
   if (tid < 16) s_cent[tid] = a.tab.centroid[tid];
 
   const EncodeStream st = a.stream[blockIdx.y];
   const int L = tid & 15;
   const int ell = perm16(L);
   const uint32_t sneg = sign_byte(a.rot, ell);       // signs of my inputs 8*ell+e
+  uint32_t smask[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (DT == 0) smask[i] = ((sneg >> i) & 1u) << 31;
+    else smask[i] = i < 4 ? (((sneg >> (2 * i)) & 1u) << 15) | (((sneg >> (2 * i + 1)) & 1u) << 31) : 0u;
+  }
   const FwhtLane fc = fwht_lane(L);
-  const float lut_scale = a.tab.lut_scale, lut_off = a.tab.lut_offset;
-  const float lut_top = (float)(a.tab.lut_n - 1);
   const int32_t H = a.num_heads;
 
   // ---- issue every load of this workgroup first
@@ -48,7 +148,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
     const int64_t v = ((int64_t)blockIdx.x * kIters + i) * 16 + (tid >> 4);
     const bool ok = v < a.num_vectors;
     const uint32_t vl = ok ? (uint32_t)v : 0u;
-    load8<DT>(st.src, (int64_t)vl * kD + 8 * ell, x[i]);
+    load8_signed<DT>(st.src, (int64_t)vl * kD + 8 * ell, smask, x[i]);
     const uint32_t t = fast_div(vl, a.div_heads);
     head[i] = vl - t * (uint32_t)H;
     const int32_t sm = ok ? a.slot_mapping[t] : -1;
@@ -60,10 +160,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
   for (int i = 0; i < kIters; ++i) {
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x[i][e] = flip(x[i][e], sneg, e);
-      ss = __builtin_fmaf(x[i][e], x[i][e], ss);
-    }
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[i][e], x[i][e], ss);
     ss = row_sum(ss);
     fwht_row(x[i], fc);                 // lane L now holds coordinates 8L..8L+7
     // 1-ulp hardware sqrt / reciprocal: their error (~1e-7 relative) is far
@@ -72,34 +169,10 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
     const float inv = ss > 0.f ? fc.sig * __builtin_amdgcn_rcpf(gamma * 11.313708498984761f) : 0.f;
 
     uint32_t code[8];
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      y[e] = x[i][e] * inv;
-      const float kf = __builtin_amdgcn_fmed3f(__builtin_fmaf(y[e], lut_scale, lut_off), 0.f, lut_top);
-      const uint2 ent = s_lut[(int)kf];
-      code[e] = ent.y + (y[e] > __uint_as_float(ent.x) ? 1u : 0u);
-    }
-
-    // ---- pack (every lane of the row takes part in the DPP exchanges)
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) word |= code[e] << (BITS * e);
-    uint32_t store_word = word;
-    bool store_lane = true;
-    int store_off = 4 * L;
-    if constexpr (BITS == 2) {
-      const uint32_t nb = dpp_u<kDppXor1>(word);
-      store_word = word | (nb << 16);
-      store_lane = (L & 1) == 0;
-      store_off = 2 * L;
-    } else if constexpr (BITS == 3) {
-      const uint32_t nb = dpp_u<kDppQuadNext>(word);
-      const int q = L & 3;
-      store_word = (word >> (8 * q)) | (q < 3 ? nb << (24 - 8 * q) : 0u);
-      store_lane = q < 3;
-      store_off = 12 * (L >> 2) + 4 * q;
-    }
+    row_codes<BITS>(x[i], inv * lut_scale, lut_off, s_lut, code);
+    bool store_lane;
+    int store_off;
+    const uint32_t store_word = row_pack<BITS>(code, L, store_lane, store_off);
 
     // ---- optional QJL sketch of the rotated-frame residual (keys)
     uint32_t sbits = 0;
@@ -111,7 +184,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
         const uint32_t qneg = sign_byte(a.rot_qjl, L);   // natural coords 8L+e
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          r[e] = y[e] - s_cent[code[e]];
+          r[e] = x[i][e] * inv - s_cent[code[e]];
           rr = __builtin_fmaf(r[e], r[e], rr);
         }
         rr = row_sum(rr);
@@ -146,12 +219,274 @@ __global__ __launch_bounds__(256) void encode_kernel(const EncodeArgs a) {
   }
 }
 
+// two-term dot product of packed 16-bit pairs with a zero accumulator (the
+// three-operand form; the builtin spends a move on the zero)
+template <int DT>
+__device__ __forceinline__ float dot2_zero(uint32_t w, uint32_t b) {
+  float r;
+  if constexpr (DT == 2)
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(w), "v"(b));
+  else
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(w), "v"(b));
+  return r;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+template <int DT>
+__device__ __forceinline__ float dot2_acc(uint32_t w, uint32_t b, float c) {
+  if constexpr (DT == 2)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, b), c, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core encode for 16-bit inputs (no QJL sidecar).
+//
+// The Hadamard part of the rotation is the dense product Y = H X' for a batch
+// of 16 vectors: X' is the 128 x 16 input with the sign flips applied as an
+// xor of sign bits (exact), H has entries +-1 (exact in 16 bits), and the
+// products accumulate in fp32.  Output coordinates form 8 tiles of 16, input
+// dims 4 steps of 32, one v_mfma_f32_16x16x32 per (tile, step).
+//
+// Row i of tile n stands for coordinate 32 (n >> 1) + 8 (i >> 2) + 4 (n & 1)
+// + (i & 3).  With that order accumulator lane (g, j) (g = lane / 16,
+// j = lane % 16) of tiles 2m and 2m + 1 holds coordinates 32 m + 8 g .. +7
+// of vector j: the eight consecutive coordinates of one packed code group,
+// so codes are searched and packed where they are produced.
+//
+// The H operand of tile n, step k at lane (g', i), element s is
+// (-1)^popcount(p & d) for coordinate p above and input dim d = 32 k + 8 g' + s:
+//   popcount(p & d) = i0 s0 + i1 s1 + i2 g'0 + i3 g'1   lane and element
+//                   + n0 s2                             odd tiles: elements 4..7
+//                   + n1 k0 + n2 k1                     same for the whole tile and step
+// so each operand is one of +-B0, +-B1, B1 being B0 with elements 4..7 negated.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+#ifndef TQ_MX_BATCHES
+#define TQ_MX_BATCHES 1
+#endif
+constexpr int kMxBatches = TQ_MX_BATCHES;   // 16-vector batches per wave
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma_h(const u32x4_t& h, const u32x4_t& x, const f32x4_t& c) {
+  if constexpr (DT == 2)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, h), __builtin_bit_cast(bf16x8_t, x), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, h), __builtin_bit_cast(f16x8_t, x), c,
+                                                  0, 0, 0);
+}
+
+// sum over the four lanes j, j + 16, j + 32, j + 48
+__device__ __forceinline__ float sum_rows(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float w = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t uw = __float_as_uint(w);
+  const auto b = __builtin_amdgcn_permlane32_swap(uw, uw, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int BITS>
+struct MxShared {
+  static constexpr int kRecStride = 16 * BITS + 16;   // padded staging record
+  uint2 lut[256];
+  u32x4_t smask[4][4];                                // [g][k]: sign-bit masks of dims 32 k + 8 g + 0..7
+  __align__(16) uint8_t rec[4][16 * kRecStride];      // per wave: 16 packed records
+};
+
+// Bucket table, sign masks (shared) and the H operands B0, B1, -B0, -B1 of
+// this lane (lane = (g', i) of the A layout).
+template <int BITS, int DT>
+__device__ __forceinline__ void mx_setup(const EncodeArgs& a, MxShared<BITS>& sh, u32x4_t (&B)[4], int tid) {
+  fill_lut(sh.lut, a, a.tab.lut_scale, a.tab.lut_offset - 0.5f, tid);
+  if (tid < 64) {
+    const int gg = tid >> 4, k = (tid >> 2) & 3, q = tid & 3;
+    const uint32_t sb = sign_byte(a.rot, 4 * k + gg);
+    sh.smask[gg][k][q] = (((sb >> (2 * q)) & 1u) << 15) | (((sb >> (2 * q + 1)) & 1u) << 31);
+  }
+  const uint32_t one = DT == 2 ? 0x3F80u : 0x3C00u;
+  const int lane = tid & 63, i = lane & 15, gp = lane >> 4;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = 2 * w + h;
+      const uint32_t neg = ((i & e) ^ ((i >> 1) & (e >> 1)) ^ ((i >> 2) & gp) ^ ((i >> 3) & (gp >> 1))) & 1u;
+      word |= (one | (neg << 15)) << (16 * h);
+    }
+    B[0][w] = word;
+    B[1][w] = w >= 2 ? word ^ 0x80008000u : word;
+    B[2][w] = B[0][w] ^ 0x80008000u;
+    B[3][w] = B[1][w] ^ 0x80008000u;
+  }
+}
+
+// One batch: this lane's share of vector j (dims 32 k + 8 g .. +7 in X[k]),
+// its slot (-1: nothing stored) and head.
+struct MxBatch {
+  u32x4_t X[4];
+  int32_t slot;
+  uint32_t head;
+};
+
+__device__ __forceinline__ void mx_load(const EncodeArgs& a, const void* src, uint32_t batch, int g, int j,
+                                        MxBatch& o) {
+  // past the last vector a lane re-reads the last one (nothing is stored)
+  const uint32_t nvec = (uint32_t)a.num_vectors;
+  const uint32_t v = 16u * batch + j;
+  const uint32_t vc = min(v, nvec - 1u);
+  const u32x4_t* p =
+      reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(src) + (uint64_t)vc * (2 * kD) + 16 * g);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o.X[k] = p[4 * k];
+  const uint32_t t = fast_div(vc, a.div_heads);
+  o.head = vc - t * (uint32_t)a.num_heads;
+  o.slot = v < nvec ? a.slot_mapping[t] : -1;
+}
+
+template <int BITS, int DT, bool OFF32>
+__device__ __forceinline__ void mx_batch(const EncodeArgs& a, const EncodeStream& st, const MxBatch& in,
+                                         const u32x4_t (&B)[4], MxShared<BITS>& sh, int wave, int g, int j) {
+  constexpr int kRecStride = MxShared<BITS>::kRecStride;
+  const float lut_scale = a.tab.lut_scale, lut_off = a.tab.lut_offset - 0.5f;
+  uint8_t* rec_w = sh.rec[wave];
+  // |x|^2 of vector j: this lane holds 32 of its 128 dims
+  float ss = dot2_zero<DT>(in.X[0][0], in.X[0][0]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int q = (k == 0 ? 1 : 0); q < 4; ++q) ss = dot2_acc<DT>(in.X[k][q], in.X[k][q], ss);
+  ss = sum_rows(ss);
+  const float gamma = __builtin_amdgcn_sqrtf(ss);
+  // 1-ulp hardware square root and reciprocal square root: ~1e-7 relative,
+  // far inside the decision band
+  const float zs = ss > 0.f ? lut_scale * kInvSqrtD * __builtin_amdgcn_rsqf(ss) : 0.f;
+  u32x4_t xs[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) xs[k] = in.X[k] ^ sh.smask[g][k];
+
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int neg = ((m & k) ^ ((m >> 1) & (k >> 1))) & 1;
+      c0 = mfma_h<DT>(B[2 * neg], xs[k], c0);
+      c1 = mfma_h<DT>(B[1 + 2 * neg], xs[k], c1);
+    }
+    const float y[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    uint32_t code[8];
+    row_codes<BITS>(y, zs, lut_off, sh.lut, code);
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) word |= code[e] << (BITS * e);
+    // codes of coordinates 32 m + 8 g .. +7 sit at record byte BITS (4 m + g)
+    uint8_t* dst = rec_w + j * kRecStride + BITS * (4 * m + g);
+    if constexpr (BITS == 4) {
+      *reinterpret_cast<uint32_t*>(dst) = word;
+    } else if constexpr (BITS == 2) {
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)word;
+    } else {
+      // 3 bytes at an odd or even address: a 16-bit and an 8-bit write
+      const bool odd = (g & 1) != 0;
+      *reinterpret_cast<uint16_t*>(dst + (odd ? 1 : 0)) = (uint16_t)(odd ? word >> 8 : word);
+      dst[odd ? 0 : 2] = (uint8_t)(odd ? word : word >> 16);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  using Off = typename std::conditional<OFF32, uint32_t, uint64_t>::type;
+  const int32_t sm = in.slot;
+  if (sm >= 0 && sm < a.num_slots) {
+    const uint32_t row = (uint32_t)sm & 15u;
+    const uint32_t blk_bytes = (uint32_t)(a.num_heads * a.block_bytes);
+    const uint32_t bb = (uint32_t)a.block_bytes;
+    Off off;
+    if constexpr (OFF32)
+      off = __umul24((uint32_t)sm >> 4, blk_bytes) + __umul24(in.head, bb);
+    else
+      off = (uint64_t)((uint32_t)sm >> 4) * blk_bytes + (uint64_t)in.head * bb;
+    if (g < BITS) {
+      const u32x4_t r = *reinterpret_cast<const u32x4_t*>(rec_w + j * kRecStride + 16 * g);
+      const Off ro = off + (uint32_t)st.rec_off + __umul24(row, (uint32_t)st.rec_bytes) + 16u * (uint32_t)g;
+      *reinterpret_cast<u32x4_t*>(a.pool + ro) = r;
+    }
+    if (g == 0) {
+      const Off no = off + (uint32_t)st.norm_off + 2u * row;
+      *reinterpret_cast<__half*>(a.pool + no) = __float2half_rn(fminf(gamma, 65504.f));
+    }
+  }
+  // the next batch rewrites this wave's staging records
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// kMxBatches batches per wave, all loads issued up front.
+template <int BITS, int DT, bool OFF32>
+__global__ __launch_bounds__(256) void encode_mx_kernel(const EncodeArgs a) {
+  __shared__ MxShared<BITS> sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, j = lane & 15;
+  u32x4_t B[4];
+  mx_setup<BITS, DT>(a, sh, B, tid);
+  const EncodeStream& st = a.stream[blockIdx.y];
+  const uint32_t b0 = (blockIdx.x * 4u + (uint32_t)wave) * kMxBatches;
+  MxBatch in[kMxBatches];
+#pragma unroll
+  for (int u = 0; u < kMxBatches; ++u) mx_load(a, st.src, b0 + u, g, j, in[u]);
+  __syncthreads();   // bucket table and sign masks
+#pragma unroll
+  for (int u = 0; u < kMxBatches; ++u) mx_batch<BITS, DT, OFF32>(a, st, in[u], B, sh, wave, g, j);
+}
+
+// TQ_ENCODE_GENERIC=1 keeps 16-bit inputs on encode_kernel (comparison only).
+static bool encode_generic_only() {
+  static const bool v = [] {
+    const char* e = std::getenv("TQ_ENCODE_GENERIC");
+    return e && std::atoi(e) == 1;
+  }();
+  return v;
+}
+
 template <int BITS, int DT>
 static int launch_bits_dt(const EncodeArgs& a, int streams, bool qjl, hipStream_t s) {
-  const int64_t groups = (a.num_vectors + 16 * kIters - 1) / (16 * kIters);
+  // 16-byte record stores need 16-byte aligned chunks and record regions
+  // (the layout's sizes are multiples of 16; the pool base is checked)
+  const bool mx = DT != 0 && !qjl && !encode_generic_only() && a.num_vectors < ((int64_t)1 << 31) &&
+                  a.block_bytes % 16 == 0 && a.stream[0].rec_off % 16 == 0 && a.stream[1].rec_off % 16 == 0 &&
+                  (reinterpret_cast<uintptr_t>(a.pool) & 15) == 0;
+  if (mx) {
+    constexpr int DT16 = DT == 0 ? 1 : DT;
+    // 32-bit cache offsets: the whole pool below 4 GiB, block index and
+    // per-block bytes below 2^24 (24-bit multiplies)
+    const int64_t blocks = a.num_slots / 16, per_block = a.num_heads * a.block_bytes;
+    const bool off32 = blocks < ((int64_t)1 << 24) && per_block < ((int64_t)1 << 24) &&
+                       blocks * per_block <= ((int64_t)1 << 32) - per_block;
+    dim3 gmx((unsigned)((a.num_vectors + 64 * kMxBatches - 1) / (64 * kMxBatches)), (unsigned)streams);
+    if (off32)
+      hipLaunchKernelGGL((encode_mx_kernel<BITS, DT16, true>), gmx, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((encode_mx_kernel<BITS, DT16, false>), gmx, dim3(256), 0, s, a);
+    return (int)hipGetLastError();
+  }
+  const int64_t groups = (a.num_vectors + 16 * kIters - 1) / (16 * kIters);   // 64 vectors each
   dim3 grid((unsigned)groups, (unsigned)streams);
-  if (qjl) hipLaunchKernelGGL((encode_kernel<BITS, DT, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((encode_kernel<BITS, DT, false>), grid, dim3(256), 0, s, a);
+  if (qjl)
+    hipLaunchKernelGGL((encode_kernel<BITS, DT, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((encode_kernel<BITS, DT, false>), grid, dim3(256), 0, s, a);
   return (int)hipGetLastError();
 }
 
