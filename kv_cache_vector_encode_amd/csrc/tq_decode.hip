@@ -199,10 +199,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a, int ns,
   for (int g = 0; g < GMAX; ++g)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float v = acc[g][e];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      acc[g][e] = v;
+      acc[g][e] = sum_rows(acc[g][e]);
     }
   const int wave = tid >> 6;
   if ((tid & 63) < 16) {

@@ -146,6 +146,15 @@ __device__ __forceinline__ void dma_x4(uint32_t lds, const void* src, uint32_t v
       : "=&s"(save) : "s"(lds), "v"(voff), "s"(src) : "memory");
 }
 
+// One dword per lane from global memory (wave-uniform base + lane offset),
+// written as asm so that the compiler neither tracks nor waits for it: the
+// caller orders it before the copies it waits for.
+__device__ __forceinline__ uint32_t load_dword_untracked(const void* base, uint32_t voff) {
+  uint32_t v;
+  asm volatile("global_load_dword %0, %1, %2" : "=v"(v) : "v"(voff), "s"(base) : "memory");
+  return v;
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight
 // (they complete in issue order).
 template <int N>
@@ -308,7 +317,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     dma_chunk<BITS>(st, chunk_src(b0), v16, vt, vv);
     dma_chunk<BITS>(st + C::kSlot, chunk_src(b1), v16, vt, vv);
   };
-  // The kernel issues no vector-memory loads of its own: the slice's
+  // Block-table entries of this wave's pairs for the loop: lane j holds
+  // those of pair j (at most 64 pairs per wave, by the split size), read
+  // here with per-lane loads issued before every copy, so each wait for a
+  // copy below also covers them.  (Scalar loads in the loop would share the
+  // LDS wait counter and, completing out of order, force a full wait on
+  // every table read.)  Lanes past the wave's pairs re-read its first entry.
+  uint32_t ids0 = 0, ids1 = 0;
+  if (my_n > 0) {
+    const int j = min(lane, my_n - 1);
+    const int lb = sb0 + 2 * (wv + 4 * j);
+    const void* row = a.block_tables + (int64_t)n * a.max_blocks;
+    ids0 = load_dword_untracked(row, 4u * (uint32_t)lb);
+    ids1 = load_dword_untracked(row, 4u * (uint32_t)(lb + 1 < sb1 ? lb + 1 : lb));
+  }
+  // The kernel issues no other vector-memory loads of its own: the slice's
   // queries and the first stages are copied to LDS here, before the set-up
   // below, whose latency they hide; centroids and signs come through scalar
   // loads.  Wave 0 copies the queries (gcount heads of 128 elements,
@@ -493,10 +516,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const uint32_t wa = cur[X].v[2 * q], wb = cur[X].v[2 * q + 1];
-          constexpr uint32_t mask = (1u << BITS) - 1;
+          if constexpr (BITS == 4) {
+            // whole-word masks: byte k of ze / zo is the pair index of dim
+            // 2k / 2k + 1 (the low nibble from wa, the high one from wb)
+            const uint32_t ze = (wa & 0x0F0F0F0Fu) | ((wb & 0x0F0F0F0Fu) << 4);
+            const uint32_t zo = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
 #pragma unroll
-          for (int t = 0; t < 8; ++t)
-            iv[2 * X + q][t] = ((wa >> (BITS * t)) & mask) | (((wb >> (BITS * t)) & mask) << BITS);
+            for (int k = 0; k < 4; ++k) {
+              iv[2 * X + q][2 * k] = (ze >> (8 * k)) & 0xFFu;
+              iv[2 * X + q][2 * k + 1] = (zo >> (8 * k)) & 0xFFu;
+            }
+          } else {
+            constexpr uint32_t mask = (1u << BITS) - 1;
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+              iv[2 * X + q][t] = ((wa >> (BITS * t)) & mask) | (((wb >> (BITS * t)) & mask) << BITS);
+          }
         }
 #pragma unroll
       for (int t = 0; t < 8; ++t) va[t] = (u32x4){s_tv2[iv[0][t]], s_tv2[iv[1][t]], s_tv2[iv[2][t]], s_tv2[iv[3][t]]};
@@ -535,8 +570,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     // ---- online softmax over the 32 tokens (per head = per column pair)
     float bm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    bm = max_rows(bm);
     const float new_m = fmaxf(run_m, bm);
     // rescale only when some head's running max moved (rare after the first
     // blocks); the accumulators stay in the matrix-core registers otherwise
@@ -579,10 +613,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
   // ---- main loop: wait for stage k, read it, refill it with pair k + NS
   // (its block-table entries were fetched one iteration earlier)
   const uint8_t* ring = s_ring + wv * C::kWaveRing;
-  int nb0 = 0, nb1 = 0;
-  if (NS < my_n) fetch_pair(NS, nb0, nb1);
   for (int k = 0; k < my_n; ++k) {
     wait_pairs_behind<BITS>(min(NS - 1, my_n - 1 - k));
+    // the block-table loads are older than the copy just waited for; this
+    // keeps their uses below that wait
+    asm volatile("" : "+v"(ids0), "+v"(ids1));
     const uint8_t* st = ring + (k % NS) * 2 * C::kSlot;
     BlockRegs<BITS> cur[2];
     read_chunk<BITS>(cur[0], st, m, g);
@@ -590,16 +625,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     if (k + NS < my_n) {
       // the stage is overwritten only after this wave's reads of it are done
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      dma_pair(k + NS, nb0, nb1);
-      if (k + NS + 1 < my_n) fetch_pair(k + NS + 1, nb0, nb1);
+      dma_pair(k + NS, (int)__builtin_amdgcn_readlane(ids0, k + NS), (int)__builtin_amdgcn_readlane(ids1, k + NS));
     }
     compute_pair(cur, sb0 + 2 * (wv + 4 * k));
   }
 
   // ---- merge the 4 waves of the workgroup (each wave's accumulator goes
   // into its own ring, whose copies have all been waited for)
-  run_l += __shfl_xor(run_l, 16);
-  run_l += __shfl_xor(run_l, 32);
+  run_l = sum_rows(run_l);
   if (g == 0 && m < 8) {
     s_wm[wave][m] = run_m;
     s_wl[wave][m] = run_l;
@@ -651,6 +684,8 @@ int launch_decode_mfma(const DecodeArgs& a, int bits, int ns, int gs, void* stre
       a.lay.off_gk != 512 * bits || a.lay.off_gv != 512 * bits + 32 ||
       (reinterpret_cast<uintptr_t>(a.pool) & 15) != 0)
     return (int)hipErrorInvalidValue;
+  // a wave keeps the block-table entries of its pairs one per lane
+  if (a.blocks_per_split < 1 || a.blocks_per_split > 2 * 4 * 64) return (int)hipErrorInvalidValue;
   dim3 grid((unsigned)a.num_splits, (unsigned)(a.num_kv_heads * ns), (unsigned)a.num_seqs);
   const bool lg = a.logits != nullptr;
   switch (bits) {

@@ -118,6 +118,27 @@ __device__ __forceinline__ float row_sum(float v) {
   v += dpp<kDppMirror>(v);
   return v;
 }
+// Sum / max over the four 16-lane rows (lanes j, j + 16, j + 32, j + 48);
+// every lane receives the result.  permlane16/32_swap exchange rows on the
+// vector ALU: with both operands v, the two results hold v of the lane and
+// of its partner 16 (32) lanes away, in some order.
+__device__ __forceinline__ float sum_rows(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float w = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t uw = __float_as_uint(w);
+  const auto b = __builtin_amdgcn_permlane32_swap(uw, uw, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float max_rows(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float w = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t uw = __float_as_uint(w);
+  const auto b = __builtin_amdgcn_permlane32_swap(uw, uw, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ float row_max(float v) {
   v = fmaxf(v, dpp<kDppXor1>(v));
   v = fmaxf(v, dpp<kDppXor2>(v));

@@ -284,16 +284,6 @@ __device__ __forceinline__ f32x4_t mfma_h(const u32x4_t& h, const u32x4_t& x, co
                                                   0, 0, 0);
 }
 
-// sum over the four lanes j, j + 16, j + 32, j + 48
-__device__ __forceinline__ float sum_rows(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float w = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const uint32_t uw = __float_as_uint(w);
-  const auto b = __builtin_amdgcn_permlane32_swap(uw, uw, false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 template <int BITS>
 struct MxShared {
   static constexpr int kRecStride = 16 * BITS + 16;   // padded staging record

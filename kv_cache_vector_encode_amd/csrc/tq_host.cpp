@@ -284,7 +284,9 @@ int check_device() {
 int blocks_per_split_for(const tq_cache* c, int32_t num_seqs, int32_t group, int32_t max_blocks, bool mfma,
                          bool attend) {
   const int64_t units = (int64_t)num_seqs * c->cfg.num_kv_heads * tq::decode_slices(group);
-  const int64_t cap = mfma ? ((int64_t)1 << 30) : 64;
+  // matrix-core kernel: at most 64 block pairs per wave (4 waves), the
+  // block-table entries a wave keeps one per lane
+  const int64_t cap = mfma ? 512 : 64;
   int64_t bps;
   if (mfma) {
     // three 256-thread workgroups fit on a CU: aim for one such wave of them
