@@ -208,6 +208,14 @@ def _decode_case(device, bits, group, hkv, lens, qjl=False, dtype="bf16", scale=
     return out, logits, (q, cache, bt_d, lens_d, ws)
 
 
+def test_decode_attend_longest_split(device, monkeypatch):
+    # 512-block splits (the matrix-core kernel's cap): waves of the first
+    # split take 64 block pairs each, so every lane of the per-lane block-
+    # table copy is used; 8200 tokens leave a one-block second split.
+    monkeypatch.setenv("TQ_BLOCKS_PER_SPLIT", "512")
+    _decode_case(device, 4, 8, 1, [8200, 300])
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_decode_attend_gqa8(device, bits):
     _decode_case(device, bits, 8, 2, [1, 17, 300, 1029])
