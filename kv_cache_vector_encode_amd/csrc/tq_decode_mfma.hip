@@ -6,18 +6,27 @@
 // deep-dive blog Step 1, attention directly on the rotated data).
 //
 // With 8 query heads per KV head every code is used by 8 dot products, so
-// both contractions are dense; they run as v_mfma_f32_16x16x32 products and
-// the vector units only dequantise codes and run the softmax.
+// both contractions are dense; they run as matrix-core products and the
+// vector units only dequantise codes and run the softmax.
 //
-//   logits  C[16 tokens x 16] = A[16 tokens x 32] * B[32 x 16], 8 steps over
-//           the 128 dims.  A slots hold (hi, lo) bf16 pairs of centroid
-//           values (c = hi + lo to 2^-17); B columns hold q_hi (heads 0..7)
-//           and q_lo (residual of q, heads 0..7); logit = col h + col h+8.
+//   logits, 4-bit keys: C[16 tokens x 16] = A[16 tokens x 64] * B[64 x 16]
+//           in 8-bit integers, 2 steps over the 128 dims for each of the two
+//           byte planes of the integer centroids (c ~ (256 hi + lo + 128.5)
+//           * 2^-s, |error| <= 2^-(s+1), s = 17 at d = 128); B columns hold
+//           the bytes of a 16-bit integer query, Qh (heads 0..7) and Ql.
+//           The planes are built from the codes with byte permutes, so the
+//           keys need no table lookups.  Exact int32 sums, combined in fp32.
+//   logits, 2-/3-bit keys: C[16 x 16] = A[16 x 32] * B[32 x 16] in bf16, 8
+//           steps over the 128 dims.  A slots hold (hi, lo) bf16 pairs of
+//           centroid values (c = hi + lo to 2^-17); B columns hold q_hi
+//           (heads 0..7) and q_lo (residual of q).  Logit = col h + col h+8.
 //   values  C[16 dims x 16] += A[16 dims x 32 tokens] * B[32 tokens x 16] in
 //           f16, one product per 8-dim tile over a pair of blocks; B columns
 //           hold p*gamma_v in f16 (heads 0..7) and its f16 residual.
-// Operand layout (16x16x32, checked on the device): lane l holds
-// A[l%16][8(l/16)+s], B[8(l/16)+s][l%16] and C[4(l/16)+r][l%16].
+// Operand layout (checked on the device): for 16x16x32 lane l holds
+// A[l%16][8(l/16)+s], B[8(l/16)+s][l%16] and C[4(l/16)+r][l%16]; the
+// 16x16x64 integer product pairs byte s of lane l's A operand with byte s of
+// lane l's B operand the same way, so only the two must agree on the dims.
 //
 // Work: grid (split, KV-head slice of <= 8 query heads, sequence); 4 waves
 // per workgroup, each takes pairs of 16-token blocks of the split in turn
@@ -34,16 +43,13 @@
 
 #include "tq_device.h"
 
-#ifndef TQ_B4_REPLICATED
-#define TQ_B4_REPLICATED 0
-#endif
-
 namespace tq {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t bf16_bits(float v) {
   return (uint32_t)__builtin_bit_cast(unsigned short, __float2bfloat16(v));
@@ -80,59 +86,105 @@ __device__ __forceinline__ void add_col_pairs(const f32x4& c, float (&o)[4]) {
       : "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]));
 }
 
+// The same column-pair add for values the vector unit produced: two wait
+// states cover a DPP read of a vector-unit result.
+__device__ __forceinline__ void add_col_pairs_v(const float (&c)[4], float (&o)[4]) {
+  asm("s_nop 1\n\t"
+      "v_add_f32_dpp %0, %4, %4 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %1, %5, %5 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %2, %6, %6 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %3, %7, %7 row_ror:8 row_mask:0xf bank_mask:0xf"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]));
+}
+
+// 4-bit key codes -> the two signed-byte planes of their integer centroids,
+// on the vector unit (no table in LDS).  A word holds 8 codes, one nibble
+// each; byte k of the "even" results belongs to the low nibble of byte k of
+// the word, byte k of the "odd" results to its high nibble.
+//  - m: 0xFF in the bytes whose code has bit 3 set (positive half).  v_perm
+//    selectors 8..11 replicate bit 7 of bytes 1, 3 of either source, so the
+//    words are shifted until each code's bit 3 sits in such a bit 7.
+//  - sel = (code ^ m) & 7: the code itself in the negative half, 15 - code
+//    (its mirror) in the positive half.
+//  - plane byte = table[sel] ^ m: the mirror's bytes, NOT-ed for positives.
+// The tables hold the eight negative-half bytes: t0 = entries 0..3, t1 = 4..7.
+struct KeyI8Tab {
+  uint32_t h0, h1, l0, l1;
+};
+__device__ __forceinline__ void key_planes_b4(uint32_t w, const KeyI8Tab& t, uint32_t& he, uint32_t& ho,
+                                              uint32_t& le, uint32_t& lo) {
+  constexpr uint32_t kSignSel = 0x090B080Au;   // bytes 0..3 <- bit 7 of src0 b1, src1 b1, src0 b3, src1 b3
+  const uint32_t me = __builtin_amdgcn_perm(w << 12, w << 4, kSignSel);
+  const uint32_t mo = __builtin_amdgcn_perm(w << 8, w, kSignSel);
+  const uint32_t se = __builtin_amdgcn_bitop3_b32(w, me, 0x07070707u, 0x28);        // (a ^ b) & c
+  const uint32_t so = __builtin_amdgcn_bitop3_b32(w >> 4, mo, 0x07070707u, 0x28);
+  he = __builtin_amdgcn_perm(t.h1, t.h0, se) ^ me;
+  le = __builtin_amdgcn_perm(t.l1, t.l0, se) ^ me;
+  ho = __builtin_amdgcn_perm(t.h1, t.h0, so) ^ mo;
+  lo = __builtin_amdgcn_perm(t.l1, t.l0, so) ^ mo;
+}
+
 // Geometry of one (block, KV head) chunk of a cache with values and no QJL
 // sidecar (K codes [16][16b] | V codes [16][16b] | gamma_k [16] | gamma_v
-// [16], fp16 norms), and of its LDS stage slot.  The chunk is copied by
-// kFull 1 KiB pieces (64 lanes x 16 B) and one tail piece: a dword copy
-// (64 lanes x 4 B, lanes past the tail re-read its last dword) when the tail
-// is at most 256 B, else a 16 B copy with the lane offsets clamped to the
-// chunk.  kStages block pairs per wave leave room for three workgroups per
-// CU in LDS.
+// [16], fp16 norms), and of its LDS stage slot.  The chunk is copied by kFull
+// 1 KiB pieces (64 lanes x 16 B) and one tail piece of kRem bytes by the
+// first kRem / 16 lanes, so a slot holds exactly one chunk.  kStages block
+// pairs per wave.
 template <int BITS>
 struct Chunk {
   static constexpr int kBytes = 512 * BITS + 64;
   static constexpr int kOffV = 256 * BITS, kOffGK = 512 * BITS, kOffGV = 512 * BITS + 32;
   static constexpr int kFull = kBytes / 1024;
   static constexpr int kRem = kBytes - 1024 * kFull;
-  static constexpr bool kTailDword = kRem <= 256;
-  static constexpr int kSlot = 1024 * kFull + (kTailDword ? 256 : 1024);
+  static constexpr int kTailLanes = kRem / 16;
+  static constexpr int kSlot = kBytes;
   static constexpr int kDma = kFull + 1;     // copy instructions per chunk
-  static constexpr int kStages = BITS == 2 ? 4 : 2;
+  static constexpr int kStages = BITS == 2 ? 4 : BITS == 3 ? 3 : 2;
   static constexpr int kWaveRing = kStages * 2 * kSlot;
+  static_assert(kRem > 0 && kRem % 16 == 0 && kTailLanes <= 64, "tail piece");
+  // exec mask of the tail copy
+  static constexpr uint32_t kTailLo = kTailLanes >= 32 ? 0xFFFFFFFFu : (1u << kTailLanes) - 1u;
+  static constexpr uint32_t kTailHi = kTailLanes > 32 ? (kTailLanes == 64 ? 0xFFFFFFFFu : (1u << (kTailLanes - 32)) - 1u) : 0u;
 };
 
 // Copy one chunk from global memory (wave-uniform src) to LDS byte address
-// lds.  v16 = 16 * lane, vt = the lane's tail offset.  The LDS address of a
-// piece is m0 + instruction offset + lane * size (the offset applies to both
-// sides), so every piece lands at its offset inside the slot.  m0 is saved
-// and restored around the copies.
+// lds.  v16 = 16 * lane.  The LDS address of a piece is m0 + instruction
+// offset + lane * 16 (the offset applies to both sides), so every piece
+// lands at its offset inside the slot.  The tail piece runs with the exec
+// mask narrowed to its lanes (inactive lanes neither read nor write); m0 and
+// exec are saved and restored inside the asm.
 template <int BITS>
-__device__ __forceinline__ void dma_chunk(uint32_t lds, const uint8_t* src, uint32_t v16, uint32_t vt, uint32_t vv) {
+__device__ __forceinline__ void dma_chunk(uint32_t lds, const uint8_t* src, uint32_t v16, uint32_t vv) {
+  using C = Chunk<BITS>;
   uint32_t save;
+  uint64_t esave;
   if constexpr (BITS == 4) {
     // the V piece (codes of the 16 values) goes through the swizzled lane
-    // offsets vv (see v_slot)
+    // offsets vv (see v_slot_src)
     asm volatile(
-        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-        "global_load_lds_dwordx4 %2, %3\n\t"
-        "global_load_lds_dwordx4 %5, %3 offset:1024\n\t"
-        "global_load_lds_dword %4, %3 offset:2048\n\t"
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %4\n\t"
+        "global_load_lds_dwordx4 %5, %4 offset:1024\n\t"
+        "s_mov_b64 %1, exec\n\ts_mov_b32 exec_lo, %6\n\ts_mov_b32 exec_hi, %7\n\ts_nop 1\n\t"
+        "global_load_lds_dwordx4 %3, %4 offset:2048\n\t"
+        "s_mov_b64 exec, %1\n\t"
         "s_mov_b32 m0, %0"
-        : "=&s"(save) : "s"(lds), "v"(v16), "s"(src), "v"(vt), "v"(vv) : "memory");
-  } else if constexpr (BITS == 3) {
-    asm volatile(
-        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-        "global_load_lds_dwordx4 %2, %3\n\t"
-        "global_load_lds_dwordx4 %4, %3 offset:1024\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(save) : "s"(lds), "v"(v16), "s"(src), "v"(vt) : "memory");
+        : "=&s"(save), "=&s"(esave)
+        : "s"(lds), "v"(v16), "s"(src), "v"(vv), "i"(C::kTailLo), "i"(C::kTailHi)
+        : "memory");
   } else {
     asm volatile(
-        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-        "global_load_lds_dwordx4 %2, %3\n\t"
-        "global_load_lds_dword %4, %3 offset:1024\n\t"
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %4\n\t"
+        "s_mov_b64 %1, exec\n\ts_mov_b32 exec_lo, %5\n\ts_mov_b32 exec_hi, %6\n\ts_nop 1\n\t"
+        "global_load_lds_dwordx4 %3, %4 offset:1024\n\t"
+        "s_mov_b64 exec, %1\n\t"
         "s_mov_b32 m0, %0"
-        : "=&s"(save) : "s"(lds), "v"(v16), "s"(src), "v"(vt) : "memory");
+        : "=&s"(save), "=&s"(esave)
+        : "s"(lds), "v"(v16), "s"(src), "i"(C::kTailLo), "i"(C::kTailHi)
+        : "memory");
+    (void)vv;
   }
 }
 
@@ -235,27 +287,31 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ush
 // lookup address then fits the instruction's offset field).
 template <int BITS>
 struct DecodeSmem {
-  // Dequantisation tables.  With 4-bit codes one entry per code, repeated
-  // in all 64 banks (entry e of lane l at dword 64 e + l: every lane reads
-  // its own bank, no conflicts):
-  //  keys:   bf16 hi | bf16 lo << 16 of c[e],   values: f16(c[e]).
-  // With 2 or 3 bits one entry per pair of codes (2*BITS bits):
-  //  keys:   (hi | lo << 16, hi | lo << 16) of the two centroids,
+  // Dequantisation tables, one entry per pair of codes (2*BITS bits):
+  //  keys:   (hi | lo << 16, hi | lo << 16) bf16 parts of the two centroids,
   //  values: f16(c[first]) | f16(c[second]) << 16.
-  static constexpr bool kRep = BITS == 4 && TQ_B4_REPLICATED;
-  static constexpr int kTk = kRep ? 16 * 64 : 2 << (2 * BITS);
-  static constexpr int kTv = kRep ? 16 * 64 : 1 << (2 * BITS);
+  // With 4-bit keys the logits take 8-bit integer operands built on the
+  // vector unit (key_planes_b4): no key table, two B-operand steps.
+  static constexpr bool kI8 = BITS == 4;
+  static constexpr int kTk = kI8 ? 4 : 2 << (2 * BITS);
+  static constexpr int kTv = 1 << (2 * BITS);
+  static constexpr int kQSteps = kI8 ? 2 : 8;
   uint32_t tk[kTk];
   uint32_t tv[kTv];
-  u32x4 qb[8][64];                     // logit B operands [step][lane]
-  alignas(16) uint8_t qs[8 * kD * 4];  // the slice's queries as loaded
+  float qcorr[8], qmult[8];            // 8-bit logits: per-head offset and scale
+  // the slice's queries as loaded, then (after a barrier) the logit B
+  // operands [step][lane] built from them
+  union {
+    alignas(16) uint8_t qs[8 * kD * 4];
+    u32x4 qb[kQSteps][64];
+  };
   float cent[2][16];                   // key / value centroids
   float wm[4][8], wl[4][8], ml[2][8];
   alignas(16) uint8_t ring[4 * Chunk<BITS>::kWaveRing];
 };
 
 template <int BITS, bool LOGITS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(const DecodeArgs a, int ns, int gs) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 3))) void decode_mfma_kernel(const DecodeArgs a, int ns, int gs) {
   using C = Chunk<BITS>;
   constexpr int NS = C::kStages;
   __shared__ DecodeSmem<BITS> sm;
@@ -309,13 +365,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
   };
   const uint32_t ring_lds = (uint32_t)reinterpret_cast<uintptr_t>(s_ring) + (uint32_t)(wv * C::kWaveRing);
   const uint32_t v16 = 16u * lane;
-  const uint32_t vt = C::kTailDword ? 4u * (uint32_t)min(lane, C::kRem / 4 - 1)
-                                    : (uint32_t)min(16 * lane, C::kRem - 16);
   const uint32_t vv = v_slot_src(lane);
   auto dma_pair = [&](int k, int b0, int b1) {   // k-th pair of this wave into stage k % NS
     const uint32_t st = ring_lds + (uint32_t)((k % NS) * 2 * C::kSlot);
-    dma_chunk<BITS>(st, chunk_src(b0), v16, vt, vv);
-    dma_chunk<BITS>(st + C::kSlot, chunk_src(b1), v16, vt, vv);
+    dma_chunk<BITS>(st, chunk_src(b0), v16, vv);
+    dma_chunk<BITS>(st + C::kSlot, chunk_src(b1), v16, vv);
   };
   // Block-table entries of this wave's pairs for the loop: lane j holds
   // those of pair j (at most 64 pairs per wave, by the split size), read
@@ -351,7 +405,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     dma_pair(k, b0, b1);
   }
 
-  constexpr bool kRep = DecodeSmem<BITS>::kRep;
+  constexpr bool kI8 = DecodeSmem<BITS>::kI8;
   constexpr int kLevels = 1 << BITS;
   // centroids through LDS: one lane writes them from wave-uniform (scalar)
   // loads of the arguments, so no per-lane argument load is needed
@@ -363,62 +417,90 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     }
   }
   __syncthreads();
-  if constexpr (kRep) {
-    for (int i = tid; i < 16 * 64; i += 256) {
-      const float c = sm.cent[0][i >> 6];
-      const uint32_t hb = bf16_bits(c);
-      sm.tk[i] = hb | (bf16_bits(c - bf16_val(hb)) << 16);
-      sm.tv[i] = f16_bits(sm.cent[1][i >> 6]);
-    }
-  } else {
-    for (int i = tid; i < (1 << (2 * BITS)); i += 256) {
-      constexpr int mask = kLevels - 1;
+  for (int i = tid; i < (1 << (2 * BITS)); i += 256) {
+    constexpr int mask = kLevels - 1;
+    if constexpr (!kI8) {
       const float c0 = sm.cent[0][i & mask], c1 = sm.cent[0][i >> BITS];
       const uint32_t h0 = bf16_bits(c0), h1 = bf16_bits(c1);
       sm.tk[2 * i] = h0 | (bf16_bits(c0 - bf16_val(h0)) << 16);
       sm.tk[2 * i + 1] = h1 | (bf16_bits(c1 - bf16_val(h1)) << 16);
-      sm.tv[i] = f16_bits(sm.cent[1][i & mask]) | (f16_bits(sm.cent[1][i >> BITS]) << 16);
     }
+    sm.tv[i] = f16_bits(sm.cent[1][i & mask]) | (f16_bits(sm.cent[1][i >> BITS]) << 16);
   }
   if (wv == 0) wait_pairs_behind<BITS>(k_pro);   // the query copy has landed
   __syncthreads();
 
   // ---- rotate this slice's queries (rows of 16 lanes, one head each; the
   // logit scale and log2(e) are folded in, so logits come out in log2 units)
-  // and scatter them into the B operands of the logit product: column c ->
-  // head c%8, part c/8 (bf16 q_hi, bf16 residual); in the operand of lane
-  // (c, g) at step st, slots (2e, 2e+1) both carry dim 32g + 4st + e.
-  // Columns of heads past the slice stay zero.
+  // and scatter them into the B operands of the logit product.  Columns of
+  // heads past the slice are zero.
   {
     const int r = tid >> 4, p = tid & 15;
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (r < 8 && r < gcount) {
+      const FwhtLane fc = fwht_lane(p);
+      const int ell = perm16(p);
+      const int elem = r * kD + 8 * ell;
+      if (a.q_dtype == 0) load8<0>(sm.qs, elem, x);
+      else if (a.q_dtype == 1) load8<1>(sm.qs, elem, x);
+      else load8<2>(sm.qs, elem, x);
+      // sign byte ell of the rotation: word picked among uniform loads
+      const int wsel = ell >> 2;
+      const uint32_t wd = wsel == 0 ? a.rot.neg[0] : wsel == 1 ? a.rot.neg[1] : wsel == 2 ? a.rot.neg[2] : a.rot.neg[3];
+      const uint32_t sb = (wd >> (8 * (ell & 3))) & 0xFFu;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = flip(x[e], sb, e);
+      fwht_row(x, fc);   // lane p now holds dims 8p .. 8p+7
+      const float sc = fc.sig * kInvSqrtD * a.scale * LOG2E;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= sc;
+    }
+    // every read of the staged queries is done before the B operands,
+    // which share their storage, are written
+    __syncthreads();
     if (r < 8) {
-      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (r < gcount) {
-        const FwhtLane fc = fwht_lane(p);
-        const int ell = perm16(p);
-        const int elem = r * kD + 8 * ell;
-        if (a.q_dtype == 0) load8<0>(sm.qs, elem, x);
-        else if (a.q_dtype == 1) load8<1>(sm.qs, elem, x);
-        else load8<2>(sm.qs, elem, x);
-        // sign byte ell of the rotation: word picked among uniform loads
-        const int wsel = ell >> 2;
-        const uint32_t wd = wsel == 0 ? a.rot.neg[0] : wsel == 1 ? a.rot.neg[1] : wsel == 2 ? a.rot.neg[2] : a.rot.neg[3];
-        const uint32_t sb = (wd >> (8 * (ell & 3))) & 0xFFu;
+      if constexpr (kI8) {
+        // 16-bit integer query Q = rint(x S), S = 32512 / max|x| over the
+        // head, split as Q = 256 Qh + Ql into signed bytes: column r takes
+        // Qh, column r + 8 takes Ql.  In the operand of lane (c, g) at step
+        // st, byte s carries dim 32g + 16st + 8(s>>3) + 2(s&3) + ((s>>2)&1),
+        // the order key_planes_b4 leaves the key codes in.  The sum of Q
+        // restores the 128.5-unit offset of the key values.
+        float mx = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = flip(x[e], sb, e);
-        fwht_row(x, fc);   // lane p now holds dims 8p .. 8p+7
-        const float sc = fc.sig * kInvSqrtD * a.scale * LOG2E;
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[e]));
+        mx = row_max(mx);
+        const float S = mx > 0.f ? 32512.f / mx : 1.f;
+        uint8_t* qb = reinterpret_cast<uint8_t*>(s_qb);
+        int qsum = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= sc;
-      }
-      uint32_t* qb = reinterpret_cast<uint32_t*>(s_qb);
+        for (int e = 0; e < 8; ++e) {
+          const int Q = (int)rintf(x[e] * S);
+          const int qh = (Q + 128) >> 8, ql = Q - 256 * qh;
+          qsum += Q;
+          const int d = 8 * p + e, gq = d >> 5, st = (d >> 4) & 1;
+          const int sl = 8 * ((d >> 3) & 1) + 4 * (d & 1) + ((d >> 1) & 3);
+          qb[(st * 64 + r + 16 * gq) * 16 + sl] = (uint8_t)qh;
+          qb[(st * 64 + r + 8 + 16 * gq) * 16 + sl] = (uint8_t)ql;
+        }
+        const float qsf = row_sum((float)qsum);
+        if (p == 0) {
+          sm.qcorr[r] = 128.5f * qsf;
+          sm.qmult[r] = a.ki8_unit / S;
+        }
+      } else {
+        // column c -> head c%8, part c/8 (bf16 q_hi, bf16 residual); in the
+        // operand of lane (c, g) at step st, slots (2e, 2e+1) both carry dim
+        // 32g + 4st + e
+        uint32_t* qb = reinterpret_cast<uint32_t*>(s_qb);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * p + e, gq = d >> 5, st = (d >> 2) & 7, ee = d & 3;
-        const uint32_t hb = bf16_bits(x[e]);
-        const uint32_t lb = bf16_bits(x[e] - bf16_val(hb));
-        qb[(st * 64 + r + 16 * gq) * 4 + ee] = hb | (hb << 16);
-        qb[(st * 64 + r + 8 + 16 * gq) * 4 + ee] = lb | (lb << 16);
+        for (int e = 0; e < 8; ++e) {
+          const int d = 8 * p + e, gq = d >> 5, st = (d >> 2) & 7, ee = d & 3;
+          const uint32_t hb = bf16_bits(x[e]);
+          const uint32_t lb = bf16_bits(x[e] - bf16_val(hb));
+          qb[(st * 64 + r + 16 * gq) * 4 + ee] = hb | (hb << 16);
+          qb[(st * 64 + r + 8 + 16 * gq) * 4 + ee] = lb | (lb << 16);
+        }
       }
     }
   }
@@ -432,33 +514,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
   for (int t = 0; t < 8; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float run_m = -INFINITY, run_l = 0.f;
 
-  const uint32_t lane4 = 4u * lane;
   // logit B operands stay in registers for the whole loop
-  u32x4 qreg[8];
+  constexpr int QS = DecodeSmem<BITS>::kQSteps;
+  u32x4 qreg[QS];
 #pragma unroll
-  for (int st = 0; st < 8; ++st) qreg[st] = s_qb[st][lane];
+  for (int st = 0; st < QS; ++st) qreg[st] = s_qb[st][lane];
+  // 8-bit logits: column m sums 65536 Qh-products + 256 Ql-products of the
+  // hi plane and 256 Qh + Ql products of the lo plane (m < 8), or the Ql
+  // parts of the same (m >= 8, weights / 256); head m%8 then adds the two
+  // columns, the offset term and the scale
+  const float ka = col_lo ? 256.f : 65536.f, kb = col_lo ? 1.f : 256.f;
+  const float kcorr = kI8 ? sm.qcorr[m & 7] : 0.f, kmult = kI8 ? sm.qmult[m & 7] : 1.f;
+  const KeyI8Tab kt = {a.ki8_hi[0], a.ki8_hi[1], a.ki8_lo[0], a.ki8_lo[1]};
 
   auto compute_pair = [&](const BlockRegs<BITS>(&cur)[2], int lb0) {
-    // ---- logits of the two blocks (log2 units): all table reads first,
-    // then the two 8-step product chains interleaved
-    uint32_t kd[2][32];   // (hi | lo) of the lane's 32 codes (dims 32g + i)
-    if constexpr (kRep) {
+    // ---- logits of the two blocks (log2 units)
+    float cs[2][4];   // sum over the column pair, before offset and scale
+    if constexpr (kI8) {
+      // signed-byte planes of the centroids built on the vector unit, two
+      // 64-dim steps per block, one product chain per (block, plane)
+      i32x4 c1[2], c2[2];
 #pragma unroll
-      for (int X = 0; X < 2; ++X)
+      for (int X = 0; X < 2; ++X) c1[X] = c2[X] = (i32x4){0, 0, 0, 0};
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // even / odd nibbles as bytes; byte b of either picks a table row
-          const uint32_t ev = cur[X].k[w] & 0x0F0F0F0Fu, od = (cur[X].k[w] >> 4) & 0x0F0F0F0Fu;
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t sel = 0x0C0C0400u | ((4u + b) << 8);   // (byte b << 8) | 4 lane
-            kd[X][8 * w + 2 * b] = *reinterpret_cast<const uint32_t*>(
-                reinterpret_cast<const uint8_t*>(sm.tk) + __builtin_amdgcn_perm(ev, lane4, sel));
-            kd[X][8 * w + 2 * b + 1] = *reinterpret_cast<const uint32_t*>(
-                reinterpret_cast<const uint8_t*>(sm.tk) + __builtin_amdgcn_perm(od, lane4, sel));
-          }
+        for (int X = 0; X < 2; ++X) {
+          uint32_t h[4], l[4];
+          key_planes_b4(cur[X].k[2 * st], kt, h[0], h[1], l[0], l[1]);
+          key_planes_b4(cur[X].k[2 * st + 1], kt, h[2], h[3], l[2], l[3]);
+          const u32x4 ah = {h[0], h[1], h[2], h[3]}, al = {l[0], l[1], l[2], l[3]};
+          c1[X] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, ah),
+                                                        __builtin_bit_cast(i32x4, qreg[st]), c1[X], 0, 0, 0);
+          c2[X] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, al),
+                                                        __builtin_bit_cast(i32x4, qreg[st]), c2[X], 0, 0, 0);
         }
+#pragma unroll
+      for (int X = 0; X < 2; ++X) {
+        float f[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[j] = fmaf((float)c2[X][j], kb, (float)c1[X][j] * ka);
+        add_col_pairs_v(f, cs[X]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cs[X][j] = (cs[X][j] + kcorr) * kmult;
+      }
     } else {
+      // all table reads first, then the two 8-step product chains interleaved
+      uint32_t kd[2][32];   // (hi | lo) of the lane's 32 codes (dims 32g + i)
 #pragma unroll
       for (int X = 0; X < 2; ++X)
 #pragma unroll
@@ -467,49 +569,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
           kd[X][2 * i] = t.x;
           kd[X][2 * i + 1] = t.y;
         }
+      f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int X = 0; X < 2; ++X) {
+          const u32x4 av = {kd[X][4 * st], kd[X][4 * st + 1], kd[X][4 * st + 2], kd[X][4 * st + 3]};
+          c[X] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                         __builtin_bit_cast(bf16x8, qreg[st]), c[X], 0, 0, 0);
+        }
+#pragma unroll
+      for (int X = 0; X < 2; ++X) add_col_pairs(c[X], cs[X]);
     }
-    f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int st = 0; st < 8; ++st)
-#pragma unroll
-      for (int X = 0; X < 2; ++X) {
-        const u32x4 av = {kd[X][4 * st], kd[X][4 * st + 1], kd[X][4 * st + 2], kd[X][4 * st + 3]};
-        c[X] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                       __builtin_bit_cast(bf16x8, qreg[st]), c[X], 0, 0, 0);
-      }
     // ---- value operands: table reads issued before the softmax needs them
     // (tile t = dims 8m+t; the A operand pairs tokens (4g, 4g+1),
     // (4g+2, 4g+3) of each block)
     u32x4 va[8];
-    if constexpr (kRep) {
-      // per token word: even / odd nibbles (dims 8m + t) as bytes, one
-      // 16-bit table read per code, two tokens per operand dword
-      const uint8_t* tvb = reinterpret_cast<const uint8_t*>(sm.tv);
-      uint32_t ve[2][4], vo[2][4];
-#pragma unroll
-      for (int X = 0; X < 2; ++X)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ve[X][i] = cur[X].v[i] & 0x0F0F0F0Fu;
-          vo[X][i] = (cur[X].v[i] >> 4) & 0x0F0F0F0Fu;
-        }
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t sel = 0x0C0C0400u | ((4u + (t >> 1)) << 8);
-        uint32_t d[4];
-#pragma unroll
-        for (int X = 0; X < 2; ++X)
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const uint32_t wa = (t & 1) ? vo[X][2 * q] : ve[X][2 * q];
-            const uint32_t wb = (t & 1) ? vo[X][2 * q + 1] : ve[X][2 * q + 1];
-            const uint32_t lo = *reinterpret_cast<const uint16_t*>(tvb + __builtin_amdgcn_perm(wa, lane4, sel));
-            const uint32_t hi = *reinterpret_cast<const uint16_t*>(tvb + __builtin_amdgcn_perm(wb, lane4, sel));
-            d[2 * X + q] = lo | (hi << 16);
-          }
-        va[t] = (u32x4){d[0], d[1], d[2], d[3]};
-      }
-    } else {
+    {
       uint32_t iv[4][8];   // [word pair][t]: code(first) | code(second) << BITS
 #pragma unroll
       for (int X = 0; X < 2; ++X)
@@ -539,15 +615,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 
     float s[2][4];
 #pragma unroll
-    for (int X = 0; X < 2; ++X) {
-      float cs[4];
-      add_col_pairs(c[X], cs);
+    for (int X = 0; X < 2; ++X)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float gk = (j & 1) ? half_hi(cur[X].gk[j >> 1]) : half_lo(cur[X].gk[j >> 1]);
-        s[X][j] = cs[j] * gk;
+        s[X][j] = cs[X][j] * gk;
       }
-    }
     if ((lb0 + 2) * kBlock > tok_end) {   // pair reaches past the split's last token
 #pragma unroll
       for (int X = 0; X < 2; ++X)
@@ -684,6 +757,8 @@ int launch_decode_mfma(const DecodeArgs& a, int bits, int ns, int gs, void* stre
       a.lay.off_gk != 512 * bits || a.lay.off_gv != 512 * bits + 32 ||
       (reinterpret_cast<uintptr_t>(a.pool) & 15) != 0)
     return (int)hipErrorInvalidValue;
+  // 4-bit keys need the integer form of the key codebook (odd-symmetric)
+  if (bits == 4 && !(a.ki8_unit > 0.f)) return (int)hipErrorInvalidValue;
   // a wave keeps the block-table entries of its pairs one per lane
   if (a.blocks_per_split < 1 || a.blocks_per_split > 2 * 4 * 64) return (int)hipErrorInvalidValue;
   dim3 grid((unsigned)a.num_splits, (unsigned)(a.num_kv_heads * ns), (unsigned)a.num_seqs);

@@ -289,12 +289,14 @@ int blocks_per_split_for(const tq_cache* c, int32_t num_seqs, int32_t group, int
   const int64_t cap = mfma ? 512 : 64;
   int64_t bps;
   if (mfma) {
-    // three 256-thread workgroups fit on a CU: aim for one such wave of them.
-    // Short splits (a few pairs per wave) pay the per-workgroup set-up and
-    // merge more than they gain from the third workgroup: there aim for two
-    // per CU, with a multiple of 8 blocks so the 4 waves get equal pairs
-    // (measured on 1 x 32768 tokens x 8 KV heads: 22 -> 32 blocks, -9%).
-    bps = ((int64_t)max_blocks * units + 767) / 768;
+    // four (4-bit codes) or three (2/3-bit) 256-thread workgroups fit on a
+    // CU: aim for one such wave of them.  Short splits (a few pairs per wave)
+    // pay the per-workgroup set-up and merge more than they gain from the
+    // extra workgroups: there aim for two per CU, with a multiple of 8 blocks
+    // so the 4 waves get equal pairs (measured on 1 x 32768 tokens x 8 KV
+    // heads: 22 -> 32 blocks, -9%).
+    const int64_t wgs = 256 * (c->cfg.bits_k == 4 ? 4 : 3);
+    bps = ((int64_t)max_blocks * units + wgs - 1) / wgs;
     if (bps <= 32) bps = (((int64_t)max_blocks * units + 511) / 512 + 7) & ~(int64_t)7;
     if (bps < 8) bps = 8;
   } else {
@@ -342,6 +344,36 @@ int validate_decode(const void* q, int32_t q_dtype, const tq_cache* cache,
   return TQ_OK;
 }
 
+// 8-bit integer form of an odd-symmetric key codebook (the matrix-core
+// logits).  With unit = 2^-s, s the largest power keeping the centroids
+// within 32000 units, centroid i of the negative half is approximated by
+// Y_i = V_i + 128.5 units, V_i = 256*hi_i + lo_i an integer with signed bytes
+// hi_i, lo_i, and |Y_i - c_i / unit| <= 1/2.  The mirror code 2^b-1-i holds
+// the bitwise NOT of both bytes, V = -V_i - 257, so its Y is exactly -Y_i.
+// The kernel adds the constant 128.5 units back through the query sum.
+// Returns false if the codebook is not exactly odd-symmetric.
+bool make_key_i8_tables(const float* c, int bits, uint32_t hi[2], uint32_t lo[2], float* unit) {
+  const int n = 1 << bits, half = n / 2;
+  double cmax = 0.0;
+  for (int i = 0; i < n; ++i) {
+    if (c[n - 1 - i] != -c[i]) return false;
+    cmax = std::max(cmax, std::fabs((double)c[i]));
+  }
+  if (!(cmax > 0.0)) return false;
+  const int s = (int)std::floor(std::log2(32000.0 / cmax));
+  hi[0] = hi[1] = lo[0] = lo[1] = 0;
+  for (int i = 0; i < half; ++i) {
+    const int64_t v = (int64_t)std::llround(std::ldexp((double)c[i], s) - 128.5);
+    const int64_t h = (v + 128) >> 8;          // floor: lo in [-128, 127]
+    const int64_t l = v - 256 * h;
+    if (h < -127 || h > 127) return false;
+    hi[i / 4] |= (uint32_t)(uint8_t)(int8_t)h << (8 * (i % 4));
+    lo[i / 4] |= (uint32_t)(uint8_t)(int8_t)l << (8 * (i % 4));
+  }
+  *unit = (float)std::ldexp(1.0, -s);
+  return true;
+}
+
 void fill_decode_args(tq::DecodeArgs& a, const void* q, int32_t q_dtype, const tq_cache* c,
                       const int32_t* bt, const int32_t* sl, int32_t num_seqs,
                       int32_t num_q_heads, int32_t max_blocks, float scale) {
@@ -373,6 +405,7 @@ void fill_decode_args(tq::DecodeArgs& a, const void* q, int32_t q_dtype, const t
     a.cent_k[i] = i < (1 << c->cfg.bits_k) ? c->tab_k.centroid[i] : 0.f;
     a.cent_v[i] = (c->cfg.bits_v > 0 && i < (1 << c->cfg.bits_v)) ? c->tab_v.centroid[i] : 0.f;
   }
+  if (!make_key_i8_tables(c->tab_k.centroid, c->cfg.bits_k, a.ki8_hi, a.ki8_lo, &a.ki8_unit)) a.ki8_unit = 0.f;
 }
 
 }  // namespace

@@ -99,6 +99,13 @@ struct DecodeArgs {
   SignMask rot, rot_qjl;
   float cent_k[16];
   float cent_v[16];
+  // Keys as 8-bit integer planes for the matrix-core logits: centroid i of
+  // the negative half (i < 2^(b-1)) is (256*hi_i + lo_i + 128.5) * ki8_unit,
+  // bytes hi_i / lo_i packed four to a word; a code of the positive half
+  // takes the bitwise NOT of both bytes of its mirror 2^b-1-i, which is the
+  // mirror's value negated because the codebook is odd-symmetric.
+  uint32_t ki8_hi[2], ki8_lo[2];
+  float ki8_unit;
 };
 
 // ----------------------------------------------------------- reconstruct --

@@ -185,20 +185,25 @@ def test_qjl_attend_split_sizes_for_long_sequences():
 
 def test_matrix_core_attend_split_sizes():
     # Splits of the matrix-core decode-attend kernel (values, no QJL): aim
-    # at 768 workgroups; when that leaves splits of at most 32 blocks, aim
+    # at one round of workgroups, 4 per CU with 4-bit codes (1024) and 3 per
+    # CU otherwise (768); when that leaves splits of at most 32 blocks, aim
     # at 512 with a multiple of 8 blocks; never more than 512 blocks (a
     # wave keeps its 64 pairs' block-table entries one per lane).
     r = tq.tq_make_rotation(42, 128)
     c = tq.tq_cache_create(tq.make_config(8, 4, 4, 4, r), 0x100000)
     c._rots = (r,)
+    c3 = tq.tq_cache_create(tq.make_config(8, 4, 3, 3, r), 0x100000)
+    c3._rots = (r,)
     L = tq.lib()
     per = 8 * 132 * 4   # 8 query heads of the group, 132 floats each
-    # 1 x 32768 tokens: 2048 blocks, 8 units -> 32 blocks -> 64 splits
+    # 1 x 32768 tokens: 2048 blocks, 8 units -> 16 blocks -> short: 32 blocks -> 64 splits
     assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 2048) == 1 * 8 * 64 * per
-    # 16 x 8192 tokens: 512 blocks, 128 units -> 86 blocks -> 6 splits
-    assert L.tq_decode_workspace_bytes(c.handle, 16, 64, 512) == 16 * 8 * 6 * per
-    # 4 x 131072 tokens: 8192 blocks, 32 units -> 342 blocks -> 24 splits
-    assert L.tq_decode_workspace_bytes(c.handle, 4, 64, 8192) == 4 * 8 * 24 * per
+    # 16 x 8192 tokens: 512 blocks, 128 units -> 64 blocks -> 8 splits
+    assert L.tq_decode_workspace_bytes(c.handle, 16, 64, 512) == 16 * 8 * 8 * per
+    # 4 x 131072 tokens: 8192 blocks, 32 units -> 256 blocks -> 32 splits
+    assert L.tq_decode_workspace_bytes(c.handle, 4, 64, 8192) == 4 * 8 * 32 * per
+    # 3-bit codes: 768 workgroups -> 342 blocks -> 24 splits
+    assert L.tq_decode_workspace_bytes(c3.handle, 4, 64, 8192) == 4 * 8 * 24 * per
     # the 512-block cap and the 4096-split limit
     assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 512 * 4096) == 1 * 8 * 4096 * per
     assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 512 * 4096 + 1) == tq.TQ_ERR_UNSUPPORTED
