@@ -68,34 +68,28 @@ __device__ __forceinline__ uint32_t field(const uint32_t (&w)[N], int i) {
   return ((w[wi] >> sh) | (w[wi + 1] << (32 - sh))) & mask;
 }
 
-// c + c of the lane 8 columns away (row_ror:8 inside each 16-lane row), for
-// the four C registers of a logit tile: adds the q_hi and q_lo columns.
-// Written out because the compiler, combining a DPP move with an add, fed
-// all four registers from the first.  The C registers come straight from the
-// matrix core, and the compiler does not pad inline asm for that hazard: the
-// s_nops give 20 wait states (an 8-pass matrix-core write needs 10 before a
-// vector read, a 16-pass one 18), which also cover the 2 a DPP read of a
-// vector-unit result needs.
-__device__ __forceinline__ void add_col_pairs(const f32x4& c, float (&o)[4]) {
-  asm("s_nop 7\n\ts_nop 7\n\ts_nop 3\n\t"
-      "v_add_f32_dpp %0, %4, %4 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
-      "v_add_f32_dpp %1, %5, %5 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
-      "v_add_f32_dpp %2, %6, %6 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
-      "v_add_f32_dpp %3, %7, %7 row_ror:8 row_mask:0xf bank_mask:0xf"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
-      : "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]));
-}
-
-// The same column-pair add for values the vector unit produced: two wait
-// states cover a DPP read of a vector-unit result.
-__device__ __forceinline__ void add_col_pairs_v(const float (&c)[4], float (&o)[4]) {
+// Exchanges with the lane 8 columns away inside each 16-lane row
+// (row_ror:8), written out so that the compiler cannot fold the DPP move
+// into the arithmetic around it (it once fed four such folded adds from the
+// first register).  The sources are vector-unit results: the leading s_nop 1
+// gives the two wait states a DPP read of such a result needs.
+//   r[j] += ror8(x[j]) * w
+__device__ __forceinline__ void fmac_ror8_4(float (&r)[4], const float (&x)[4], float w) {
   asm("s_nop 1\n\t"
-      "v_add_f32_dpp %0, %4, %4 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
-      "v_add_f32_dpp %1, %5, %5 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
-      "v_add_f32_dpp %2, %6, %6 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
-      "v_add_f32_dpp %3, %7, %7 row_ror:8 row_mask:0xf bank_mask:0xf"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
-      : "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]));
+      "v_fmac_f32_dpp %0, %4, %8 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %5, %8 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %6, %8 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %7, %8 row_ror:8 row_mask:0xf bank_mask:0xf"
+      : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3])
+      : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(w));
+}
+//   o[j] = x[j] of the lane 8 columns away
+__device__ __forceinline__ void ror8_2(const uint32_t (&x)[2], uint32_t (&o)[2]) {
+  asm("s_nop 1\n\t"
+      "v_mov_b32_dpp %0, %2 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mov_b32_dpp %1, %3 row_ror:8 row_mask:0xf bank_mask:0xf"
+      : "=&v"(o[0]), "=&v"(o[1])
+      : "v"(x[0]), "v"(x[1]));
 }
 
 // 4-bit key codes -> the two signed-byte planes of their integer centroids,
@@ -507,7 +501,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
   __syncthreads();
   const bool col_lo = m >= 8;
   const bool col_live = (m & 7) < gcount;
-  const uint32_t live_mask = col_live ? 0xFFFFFFFFu : 0u;
 
   f32x4 acc[8];
 #pragma unroll
@@ -519,17 +512,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
   u32x4 qreg[QS];
 #pragma unroll
   for (int st = 0; st < QS; ++st) qreg[st] = s_qb[st][lane];
-  // 8-bit logits: column m sums 65536 Qh-products + 256 Ql-products of the
-  // hi plane and 256 Qh + Ql products of the lo plane (m < 8), or the Ql
-  // parts of the same (m >= 8, weights / 256); head m%8 then adds the two
-  // columns, the offset term and the scale
-  const float ka = col_lo ? 256.f : 65536.f, kb = col_lo ? 1.f : 256.f;
-  const float kcorr = kI8 ? sm.qcorr[m & 7] : 0.f, kmult = kI8 ? sm.qmult[m & 7] : 1.f;
+  // After the logit products, the two 8-lane halves of every row hold the
+  // two parts of the same head's sums (column m: q_hi / Qh for m < 8, q_lo /
+  // Ql for m >= 8).  Each half keeps one block of the pair: lanes m < 8 take
+  // block 0, lanes m >= 8 block 1, and receive the other part of their block
+  // from the lane 8 columns away, so the softmax runs once per logit.
+  //  8-bit logits: v = 256 hi-plane sum + lo-plane sum of a column (exact
+  //  int32); head logit = (256 v[Qh column] + v[Ql column] + offset) * unit.
+  const int xo = col_lo ? 1 : 0;   // this lane's block of the pair
+  const float kmult = kI8 ? sm.qmult[m & 7] : 1.f;
+  const float w_own = kI8 ? (col_lo ? 1.f : 256.f) * kmult : 1.f;
+  const float w_par = kI8 ? (col_lo ? 256.f : 1.f) * kmult : 1.f;
+  const float kc = kI8 ? sm.qcorr[m & 7] * kmult : 0.f;
   const KeyI8Tab kt = {a.ki8_hi[0], a.ki8_hi[1], a.ki8_lo[0], a.ki8_lo[1]};
 
   auto compute_pair = [&](const BlockRegs<BITS>(&cur)[2], int lb0) {
     // ---- logits of the two blocks (log2 units)
-    float cs[2][4];   // sum over the column pair, before offset and scale
+    float fv[2][4];   // this lane's column of each block's product
     if constexpr (kI8) {
       // signed-byte planes of the centroids built on the vector unit, two
       // 64-dim steps per block, one product chain per (block, plane)
@@ -549,15 +548,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
           c2[X] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, al),
                                                         __builtin_bit_cast(i32x4, qreg[st]), c2[X], 0, 0, 0);
         }
+      // |hi-plane sum| <= 128 * 2^14, so 256 * it + the lo-plane sum fits in int32
 #pragma unroll
-      for (int X = 0; X < 2; ++X) {
-        float f[4];
+      for (int X = 0; X < 2; ++X)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) f[j] = fmaf((float)c2[X][j], kb, (float)c1[X][j] * ka);
-        add_col_pairs_v(f, cs[X]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) cs[X][j] = (cs[X][j] + kcorr) * kmult;
-      }
+        for (int j = 0; j < 4; ++j) fv[X][j] = (float)((c1[X][j] << 8) + c2[X][j]);
     } else {
       // all table reads first, then the two 8-step product chains interleaved
       uint32_t kd[2][32];   // (hi | lo) of the lane's 32 codes (dims 32g + i)
@@ -579,7 +574,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
                                                          __builtin_bit_cast(bf16x8, qreg[st]), c[X], 0, 0, 0);
         }
 #pragma unroll
-      for (int X = 0; X < 2; ++X) add_col_pairs(c[X], cs[X]);
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fv[X][j] = c[X][j];
+    }
+    // own block's part, plus the other part from the lane 8 columns away
+    float cs[4];
+    {
+      float send[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        cs[j] = fmaf(col_lo ? fv[1][j] : fv[0][j], w_own, kc);
+        send[j] = col_lo ? fv[0][j] : fv[1][j];
+      }
+      fmac_ror8_4(cs, send, w_par);
     }
     // ---- value operands: table reads issued before the softmax needs them
     // (tile t = dims 8m+t; the A operand pairs tokens (4g, 4g+1),
@@ -595,8 +603,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
           if constexpr (BITS == 4) {
             // whole-word masks: byte k of ze / zo is the pair index of dim
             // 2k / 2k + 1 (the low nibble from wa, the high one from wb)
-            const uint32_t ze = (wa & 0x0F0F0F0Fu) | ((wb & 0x0F0F0F0Fu) << 4);
-            const uint32_t zo = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
+            constexpr uint32_t M = 0x0F0F0F0Fu;
+            uint32_t ze = (wa & M) | ((wb << 4) & ~M);
+            uint32_t zo = ((wa >> 4) & M) | (wb & ~M);
+            // built once: each index below is one byte-select shift of these
+            asm volatile("" : "+v"(ze), "+v"(zo));
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               iv[2 * X + q][2 * k] = (ze >> (8 * k)) & 0xFFu;
@@ -613,36 +624,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
       for (int t = 0; t < 8; ++t) va[t] = (u32x4){s_tv2[iv[0][t]], s_tv2[iv[1][t]], s_tv2[iv[2][t]], s_tv2[iv[3][t]]};
     }
 
-    float s[2][4];
+    // ---- this lane's 4 logits: tokens 4g .. 4g+3 of block xo, head m % 8
+    const uint32_t gk2[2] = {col_lo ? cur[1].gk[0] : cur[0].gk[0], col_lo ? cur[1].gk[1] : cur[0].gk[1]};
+    const uint32_t gv2[2] = {col_lo ? cur[1].gv[0] : cur[0].gv[0], col_lo ? cur[1].gv[1] : cur[0].gv[1]};
+    float s[4];
 #pragma unroll
-    for (int X = 0; X < 2; ++X)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float gk = (j & 1) ? half_hi(cur[X].gk[j >> 1]) : half_lo(cur[X].gk[j >> 1]);
-        s[X][j] = cs[X][j] * gk;
-      }
+    for (int j = 0; j < 4; ++j) s[j] = cs[j] * ((j & 1) ? half_hi(gk2[j >> 1]) : half_lo(gk2[j >> 1]));
+    const int tok0 = (lb0 + xo) * kBlock + 4 * g;
     if ((lb0 + 2) * kBlock > tok_end) {   // pair reaches past the split's last token
 #pragma unroll
-      for (int X = 0; X < 2; ++X)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if ((lb0 + X) * kBlock + 4 * g + j >= tok_end) s[X][j] = -INFINITY;
+      for (int j = 0; j < 4; ++j)
+        if (tok0 + j >= tok_end) s[j] = -INFINITY;
     }
     if constexpr (LOGITS) {
-      if (!col_lo && col_live) {
-        float* lrow = a.logits + ((int64_t)n * Hq + (int64_t)h * a.group + g0 + m) * a.logits_stride;
+      if (col_live) {
+        float* lrow = a.logits + ((int64_t)n * Hq + (int64_t)h * a.group + g0 + (m & 7)) * a.logits_stride;
 #pragma unroll
-        for (int X = 0; X < 2; ++X)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int tok = (lb0 + X) * kBlock + 4 * g + j;
-            if (tok < tok_end) lrow[tok] = s[X][j] * (1.f / LOG2E);
-          }
+        for (int j = 0; j < 4; ++j)
+          if (tok0 + j < tok_end) lrow[tok0 + j] = s[j] * (1.f / LOG2E);
       }
     }
-    // ---- online softmax over the 32 tokens (per head = per column pair)
-    float bm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    // ---- online softmax over the 32 tokens (per head: both row halves)
+    float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    bm = fmaxf(bm, dpp<kDppRor8>(bm));
     bm = max_rows(bm);
     const float new_m = fmaxf(run_m, bm);
     // rescale only when some head's running max moved (rare after the first
@@ -654,28 +658,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
       for (int t = 0; t < 8; ++t) acc[t] *= alpha;
     }
     run_m = new_m;
-    const float mref = (new_m == -INFINITY) ? 0.f : new_m;   // all masked: exp2(-inf) = 0
-    uint32_t pw[2][2];
+    // all masked: exp2(-inf) = 0; heads past the slice: +inf, so p = 0
+    const float mref = !col_live ? INFINITY : (new_m == -INFINITY) ? 0.f : new_m;
+    uint32_t hi[2], lo[2];
 #pragma unroll
-    for (int X = 0; X < 2; ++X)
+    for (int q = 0; q < 2; ++q) {
+      float pv[2];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        float pv[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float p = __builtin_amdgcn_exp2f(s[X][2 * q + u] - mref);
-          run_l += p;
-          const float gv = u ? half_hi(cur[X].gv[q]) : half_lo(cur[X].gv[q]);
-          pv[u] = p * gv;
-        }
-        // columns 0..7 take f16(pv) (rounded toward zero), columns 8..15 the
-        // f16 of its residual, which is exact in f32
-        const auto hi = __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]);
-        const auto lo = __builtin_amdgcn_cvt_pkrtz(pv[0] - (float)hi[0], pv[1] - (float)hi[1]);
-        const uint32_t w = col_lo ? __builtin_bit_cast(uint32_t, lo) : __builtin_bit_cast(uint32_t, hi);
-        pw[X][q] = w & live_mask;
+      for (int u = 0; u < 2; ++u) {
+        const float p = __builtin_amdgcn_exp2f(s[2 * q + u] - mref);
+        run_l += p;
+        pv[u] = p * (u ? half_hi(gv2[q]) : half_lo(gv2[q]));
       }
-    const u32x4 pb = {pw[0][0], pw[0][1], pw[1][0], pw[1][1]};
+      // f16(pv) (rounded toward zero) and the f16 of its residual, exact in f32
+      const auto ph = __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]);
+      const auto pl = __builtin_amdgcn_cvt_pkrtz(pv[0] - (float)ph[0], pv[1] - (float)ph[1]);
+      hi[q] = __builtin_bit_cast(uint32_t, ph);
+      lo[q] = __builtin_bit_cast(uint32_t, pl);
+    }
+    // B columns 0..7 take f16(p gamma_v) of both blocks, columns 8..15 its
+    // residual: lanes m < 8 send their block-0 residuals across, lanes m >= 8
+    // their block-1 high parts
+    uint32_t snd[2] = {col_lo ? hi[0] : lo[0], col_lo ? hi[1] : lo[1]}, rcv[2];
+    ror8_2(snd, rcv);
+    const u32x4 pb = col_lo ? (u32x4){rcv[0], rcv[1], lo[0], lo[1]} : (u32x4){hi[0], hi[1], rcv[0], rcv[1]};
     // ---- values: one product per 8-dim tile
 #pragma unroll
     for (int t = 0; t < 8; ++t)
@@ -706,6 +712,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
   // ---- merge the 4 waves of the workgroup (each wave's accumulator goes
   // into its own ring, whose copies have all been waited for)
   run_l = sum_rows(run_l);
+  run_l += dpp<kDppRor8>(run_l);   // the two row halves hold the pair's two blocks
   if (g == 0 && m < 8) {
     s_wm[wave][m] = run_m;
     s_wl[wave][m] = run_l;

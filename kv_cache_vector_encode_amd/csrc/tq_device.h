@@ -19,6 +19,7 @@ constexpr int kDppXor2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 constexpr int kDppQuadNext = 0xF9;
+constexpr int kDppRor8 = 0x128;     // row_ror:8
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
