@@ -299,7 +299,15 @@ __device__ __forceinline__ void mx_setup(const EncodeArgs& a, MxShared<BITS>& sh
   fill_lut(sh.lut, a, a.tab.lut_scale, a.tab.lut_offset - 0.5f, tid);
   if (tid < 64) {
     const int gg = tid >> 4, k = (tid >> 2) & 3, q = tid & 3;
-    const uint32_t sb = sign_byte(a.rot, 4 * k + gg);
+    // sign byte 4 k + gg, picked among wave-uniform (scalar) loads of the
+    // four mask words: a per-lane load of the argument block would be one
+    // more memory round trip before the batch can start
+    // (readfirstlane keeps the compiler from turning the select into a
+    // per-lane address)
+    const uint32_t n0 = __builtin_amdgcn_readfirstlane(a.rot.neg[0]), n1 = __builtin_amdgcn_readfirstlane(a.rot.neg[1]);
+    const uint32_t n2 = __builtin_amdgcn_readfirstlane(a.rot.neg[2]), n3 = __builtin_amdgcn_readfirstlane(a.rot.neg[3]);
+    const uint32_t wd = k == 0 ? n0 : k == 1 ? n1 : k == 2 ? n2 : n3;
+    const uint32_t sb = (wd >> (8 * gg)) & 0xFFu;
     sh.smask[gg][k][q] = (((sb >> (2 * q)) & 1u) << 15) | (((sb >> (2 * q + 1)) & 1u) << 31);
   }
   const uint32_t one = DT == 2 ? 0x3F80u : 0x3C00u;
@@ -429,13 +437,15 @@ __global__ __launch_bounds__(256) void encode_mx_kernel(const EncodeArgs a) {
   __shared__ MxShared<BITS> sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
-  u32x4_t B[4];
-  mx_setup<BITS, DT>(a, sh, B, tid);
+  // the input loads go first: the set-up's per-lane reads of the argument
+  // tables (and their waits) then overlap them instead of preceding them
   const EncodeStream& st = a.stream[blockIdx.y];
   const uint32_t b0 = (blockIdx.x * 4u + (uint32_t)wave) * kMxBatches;
   MxBatch in[kMxBatches];
 #pragma unroll
   for (int u = 0; u < kMxBatches; ++u) mx_load(a, st.src, b0 + u, g, j, in[u]);
+  u32x4_t B[4];
+  mx_setup<BITS, DT>(a, sh, B, tid);
   __syncthreads();   // bucket table and sign masks
 #pragma unroll
   for (int u = 0; u < kMxBatches; ++u) mx_batch<BITS, DT, OFF32>(a, st, in[u], B, sh, wave, g, j);
