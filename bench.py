@@ -211,6 +211,24 @@ def main():
     enc_gbps = enc_bytes / enc_s / 1e9
     enc_vps = nvec / enc_s
 
+    # ---- decompression of every cached key and value to bf16 (attention over
+    # a compressed prefix): outside the step, reported beside it
+    dq_ms = []
+    if args.only == "both":
+        Ko = torch.empty((w.tokens, w.num_kv_heads, 128), dtype=torch.bfloat16, device=dev)
+        Vo = torch.empty_like(Ko)
+        for i in range(3):
+            tq.tq_decompress_kv(sets[i % nsets]["cache"], slots, Ko, Vo, stream=stream)
+        reps = max(5, args.steps // 4)
+        dq_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(reps):
+            dq_ev[i][0].record(stream)
+            tq.tq_decompress_kv(sets[(i + 3) % nsets]["cache"], slots, Ko, Vo, stream=stream)
+            dq_ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        dq_ms = [e[0].elapsed_time(e[1]) for e in dq_ev]
+        del Ko, Vo
+
     kernels = {
         "tq_encode": {"bound": "hbm", "achieved": round(enc_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                       "frac": round(enc_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": enc_bytes,
@@ -219,6 +237,14 @@ def main():
                              "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": dec_bytes,
                              "us_per_launch": round(dec_s * 1e6, 2), "median_us": round(float(np.median(dec_ms)) * 1e3, 2)},
     }
+    if dq_ms:
+        dq_s = float(np.mean(dq_ms)) / 1e3
+        dq_bytes = w.tokens * w.num_kv_heads * 2 * (comp_b + 2 * 128)   # codes + norms in, bf16 out
+        kernels["tq_decompress_kv"] = {
+            "bound": "hbm", "achieved": round(dq_bytes / dq_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(dq_bytes / dq_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": dq_bytes,
+            "us_per_launch": round(dq_s * 1e6, 2), "median_us": round(float(np.median(dq_ms)) * 1e3, 2),
+            "note": "every cached key and value to bf16; not part of the timed step"}
     dom = "tq_encode" if enc_s >= dec_s else "tq_decode_attend"
     traffic = None
     tf = os.path.join(ROOT, "profiles", "traffic.json")

@@ -205,6 +205,26 @@ int tq_decode_logits(const void* q, int32_t q_dtype, const tq_cache* cache,
 int tq_reconstruct(const tq_cache* cache, const int32_t* slots, int64_t n,
                    int32_t which, float* out, void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * Decompress cache rows to 16-bit floats, keys and values in one call, for
+ * attention over a compressed prefix ([P2] Implementation plan, the planned
+ * decompress call; [P2] Math, K_hat = DQ(K_q); [P4] Step 2 decompress_key).
+ * For row i of slots and KV head h:
+ *   K_out[i][h][:] = round(gamma16_k * R^T c_k[codes_k]),  V_out likewise,
+ * computed in fp32 and rounded to nearest even in out_dtype.
+ *   slots:     device int32[n], slot = block*16 + row; a slot < 0 or past
+ *              the pool gives zero vectors;
+ *   out_dtype: TQ_BF16 or TQ_F16;
+ *   K_out, V_out: device [n][num_kv_heads][d] of out_dtype, 16-byte aligned,
+ *              caller-owned; either may be NULL (not written); V_out must be
+ *              NULL for a keys-only cache.
+ * Asynchronous on hip_stream.  Errors: TQ_ERR_INVALID_ARG (null cache, n < 0,
+ * bad dtype, misaligned output, values asked of a keys-only cache, more than
+ * 2^31 vectors), TQ_ERR_NO_DEVICE, TQ_ERR_HIP (launch failure). */
+int tq_decompress_kv(const tq_cache* cache, const int32_t* slots, int64_t n,
+                     int32_t out_dtype, void* K_out, void* V_out,
+                     void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -616,6 +616,45 @@ int tq_decode_logits(const void* q, int32_t q_dtype, const tq_cache* cache,
   return TQ_OK;
 }
 
+int tq_decompress_kv(const tq_cache* cache, const int32_t* slots, int64_t n, int32_t out_dtype,
+                     void* K_out, void* V_out, void* hip_stream) {
+  if (!cache) return fail(TQ_ERR_INVALID_ARG, "null cache");
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n < 0");
+  if (out_dtype != TQ_BF16 && out_dtype != TQ_F16) return fail(TQ_ERR_INVALID_ARG, "out_dtype must be TQ_BF16 or TQ_F16");
+  if (V_out && cache->cfg.bits_v == 0) return fail(TQ_ERR_INVALID_ARG, "V_out given for a keys-only cache");
+  if ((reinterpret_cast<uintptr_t>(K_out) | reinterpret_cast<uintptr_t>(V_out)) % 16 != 0)
+    return fail(TQ_ERR_INVALID_ARG, "outputs must be 16-byte aligned");
+  if (n == 0 || (!K_out && !V_out)) return TQ_OK;
+  if (!slots) return fail(TQ_ERR_INVALID_ARG, "null slots");
+  if (n * cache->cfg.num_kv_heads >= ((int64_t)1 << 31)) return fail(TQ_ERR_INVALID_ARG, "too many vectors");
+  int s = check_device();
+  if (s != TQ_OK) return s;
+  tq::DecompArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.pool = static_cast<const uint8_t*>(cache->pool);
+  a.slots = slots;
+  a.n_vectors = n * cache->cfg.num_kv_heads;
+  a.num_slots = cache->cfg.num_blocks * tq::kBlock;
+  a.block_bytes = cache->lay.block_bytes;
+  a.num_heads = cache->cfg.num_kv_heads;
+  a.out_dtype = out_dtype;
+  a.div_heads = tq::make_fast_div((uint32_t)cache->cfg.num_kv_heads);
+  a.rot = cache->rot;
+  for (int k = 0; k < 2; ++k) {
+    tq::DecompStream& st = a.stream[k];
+    const tq::CodecTables& tab = k ? cache->tab_v : cache->tab_k;
+    st.out = k ? V_out : K_out;
+    st.rec_off = k ? cache->lay.off_v : cache->lay.off_k;
+    st.norm_off = k ? cache->lay.off_gamma_v : cache->lay.off_gamma_k;
+    st.rec_bytes = (int32_t)(k ? cache->lay.v_rec_bytes : cache->lay.k_rec_bytes);
+    st.bits = k ? cache->cfg.bits_v : cache->cfg.bits_k;
+    for (int i = 0; i < 16; ++i) st.centroid[i] = (st.out && i < (1 << st.bits)) ? tab.centroid[i] : 0.f;
+  }
+  int err = tq::launch_decompress(a, hip_stream);
+  if (err != 0) return hip_fail(err, "decompress launch");
+  return TQ_OK;
+}
+
 int tq_reconstruct(const tq_cache* cache, const int32_t* slots, int64_t n, int32_t which,
                    float* out, void* hip_stream) {
   if (!cache) return fail(TQ_ERR_INVALID_ARG, "null cache");

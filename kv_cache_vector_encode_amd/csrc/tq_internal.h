@@ -122,6 +122,25 @@ struct ReconArgs {
   float centroid[16];
 };
 
+// Decompression of cache rows to 16-bit floats (keys and values in one launch).
+struct DecompStream {
+  void* out;                // [n][heads][128] of out_dtype; nullptr: stream skipped
+  int64_t rec_off, norm_off;
+  int32_t rec_bytes, bits;
+  float centroid[16];
+};
+struct DecompArgs {
+  const uint8_t* pool;
+  const int32_t* slots;
+  int64_t n_vectors;        // n * heads
+  int64_t num_slots;        // slots outside [0, num_slots) give zero vectors
+  int64_t block_bytes;
+  int32_t num_heads, out_dtype;   // TQ_F16 = 1, TQ_BF16 = 2
+  FastDiv div_heads;
+  SignMask rot;
+  DecompStream stream[2];   // keys, values
+};
+
 // Launchers implemented in the .hip files; return a hipError_t value.
 int launch_encode(const EncodeArgs& a, int num_streams, int in_dtype, void* stream);
 int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int attend, int mfma, void* stream);
@@ -129,5 +148,6 @@ int decode_slices(int group);
 int launch_decode_mfma(const DecodeArgs& a, int bits, int ns, int gs, void* stream);
 int launch_merge(const DecodeArgs& a, void* stream);
 int launch_reconstruct(const ReconArgs& a, void* stream);
+int launch_decompress(const DecompArgs& a, void* stream);
 
 }  // namespace tq

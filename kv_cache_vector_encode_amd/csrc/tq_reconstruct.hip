@@ -6,6 +6,8 @@
 // One vector per 16-lane row: lane L gathers the codes of coordinates
 // 8*kPerm(L)+e so the FWHT leaves it holding output coordinates 8L..8L+7.
 
+#include <hip/hip_bf16.h>
+
 #include "tq_device.h"
 
 namespace tq {
@@ -55,6 +57,111 @@ int launch_reconstruct(const ReconArgs& a, void* stream) {
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// decompress_kernel: the same dequantisation for whole cache rows, keys and
+// values in one launch (blockIdx.y picks the stream), written as 16-bit
+// floats (round to nearest even) for attention over a compressed prefix.
+// Every output vector is one 256-byte store per 16-lane row (16 bytes per
+// lane); a workgroup takes VPR vectors per row, all loads issued first.
+// Per vector it reads d*b/8 + 2 bytes and writes 256.
+// ---------------------------------------------------------------------------
+template <int OUT>
+__device__ __forceinline__ uint32_t pack16(float lo, float hi) {
+  if constexpr (OUT == 2) {
+    return (uint32_t)__builtin_bit_cast(unsigned short, __float2bfloat16(lo)) |
+           ((uint32_t)__builtin_bit_cast(unsigned short, __float2bfloat16(hi)) << 16);
+  } else {
+    return (uint32_t)__half_as_ushort(__float2half_rn(lo)) | ((uint32_t)__half_as_ushort(__float2half_rn(hi)) << 16);
+  }
+}
+
+constexpr int kDecompVpr = 4;   // vectors per 16-lane row
+
+template <int BITS, int OUT>
+__global__ __launch_bounds__(256) void decompress_kernel(const DecompArgs a) {
+  const DecompStream& st = a.stream[blockIdx.y];
+  __shared__ float s_cent[16];
+  const int tid = threadIdx.x;
+  const int L = tid & 15;
+  const int ell = perm16(L);
+  const int64_t H = a.num_heads;
+  // ---- loads first: slots, then codes and norms of this row's vectors
+  int64_t v[kDecompVpr];
+  int32_t slot[kDecompVpr];
+#pragma unroll
+  for (int u = 0; u < kDecompVpr; ++u) {
+    v[u] = ((int64_t)blockIdx.x * kDecompVpr + u) * 16 + (tid >> 4);
+    const int64_t vc = v[u] < a.n_vectors ? v[u] : a.n_vectors - 1;
+    slot[u] = a.slots[fast_div((uint32_t)vc, a.div_heads)];
+  }
+  uint32_t cw[kDecompVpr];
+  float g[kDecompVpr];
+#pragma unroll
+  for (int u = 0; u < kDecompVpr; ++u) {
+    const int64_t vc = v[u] < a.n_vectors ? v[u] : a.n_vectors - 1;
+    const uint32_t i = fast_div((uint32_t)vc, a.div_heads);
+    const int64_t h = vc - (int64_t)i * H;
+    const bool ok = slot[u] >= 0 && slot[u] < a.num_slots;
+    const int32_t sl = ok ? slot[u] : 0;   // invalid slots read slot 0; written as zeros
+    const uint8_t* base = a.pool + ((int64_t)(sl >> 4) * H + h) * a.block_bytes;
+    const int row = sl & 15;
+    cw[u] = load_codes8<BITS>(base + st.rec_off + (int64_t)row * st.rec_bytes, ell);
+    g[u] = ok ? load_half(base + st.norm_off + 2 * row) : 0.f;
+  }
+  if (tid < 16) s_cent[tid] = st.centroid[tid];
+  __syncthreads();
+  const FwhtLane fc = fwht_lane(L);
+  const uint32_t sb = sign_byte(a.rot, L);
+#pragma unroll
+  for (int u = 0; u < kDecompVpr; ++u) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = s_cent[(cw[u] >> (BITS * e)) & ((1u << BITS) - 1)];
+    fwht_row(x, fc);   // every lane of the row takes part, also past the end
+    const float gs = g[u] * fc.sig * kInvSqrtD;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack16<OUT>(flip(x[2 * e] * gs, sb, 2 * e), flip(x[2 * e + 1] * gs, sb, 2 * e + 1));
+    if (v[u] < a.n_vectors) {
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint8_t*>(st.out) + (v[u] * kD + 8 * L) * 2);
+      *dst = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+template <int BITS>
+static void launch_decomp_bits(const DecompArgs& a, dim3 grid, hipStream_t s) {
+  if (a.out_dtype == 2) hipLaunchKernelGGL((decompress_kernel<BITS, 2>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((decompress_kernel<BITS, 1>), grid, dim3(256), 0, s, a);
+}
+
+int launch_decompress(const DecompArgs& a, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t groups = (a.n_vectors + 16 * kDecompVpr - 1) / (16 * kDecompVpr);
+  if (groups > 0x7FFFFFFF || a.n_vectors >= ((int64_t)1 << 31)) return (int)hipErrorInvalidValue;
+  // one launch per distinct bit width (keys and values share one when equal)
+  DecompArgs b = a;
+  int streams = 0;
+  for (int k = 0; k < 2; ++k)
+    if (a.stream[k].out) b.stream[streams++] = a.stream[k];
+  if (streams == 0) return 0;
+  const bool same = streams == 1 || b.stream[0].bits == b.stream[1].bits;
+  for (int part = 0; part < (same ? 1 : 2); ++part) {
+    DecompArgs c = b;
+    if (!same) c.stream[0] = b.stream[part];
+    const dim3 grid((unsigned)groups, (unsigned)(same ? streams : 1));
+    switch (c.stream[0].bits) {
+      case 2: launch_decomp_bits<2>(c, grid, s); break;
+      case 3: launch_decomp_bits<3>(c, grid, s); break;
+      case 4: launch_decomp_bits<4>(c, grid, s); break;
+      default: return (int)hipErrorInvalidValue;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  return 0;
 }
 
 }  // namespace tq

@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "tq_decode_logits": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.c_float, _P, _P]),
             "tq_reconstruct": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
+            "tq_decompress_kv": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -240,6 +241,14 @@ def tq_decode_logits(q, cache: Cache, block_tables, seq_lens, logits_out, scale:
 def tq_reconstruct(cache: Cache, slots, which: int, out, stream=None):
     _check(lib().tq_reconstruct(cache.handle, _ptr(slots), slots.shape[0], which, _ptr(out), _stream(stream)),
            "tq_reconstruct")
+
+
+def tq_decompress_kv(cache: Cache, slots, K_out, V_out=None, stream=None):
+    """K_out / V_out: device tensors [n][kv_heads][128] of bfloat16 or float16
+    (the same dtype); either may be None."""
+    ref = K_out if K_out is not None else V_out
+    _check(lib().tq_decompress_kv(cache.handle, _ptr(slots), slots.shape[0], _dtype_code(ref) if ref is not None else 2,
+                                  _ptr(K_out), _ptr(V_out), _stream(stream)), "tq_decompress_kv")
 
 
 # ------------------------------------------------------------------ helpers --

@@ -285,6 +285,81 @@ def test_reconstruct_matches_oracle(device, bits):
         assert np.all(got[-2:] == 0)
 
 
+# -------------------------------------------------------------- decompress --
+
+def _round16(x64, dt):
+    """float64 -> nearest-even bf16 / f16, as float64 (rounded through float32;
+    the rare double-rounding ties stay inside the test's tolerance)."""
+    x32 = x64.astype(np.float32)
+    if dt == "f16":
+        return x32.astype(np.float16).astype(np.float64)
+    u = x32.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _check_decompressed(got, want, g16, c32, dt):
+    # fp32 arithmetic, then one rounding to 16 bits: within half an ulp of the
+    # float64 value plus the fp32 error.  Away from zero (where the FWHT's
+    # fp32 cancellation error is negligible next to half an ulp) it is also
+    # the oracle's own round-to-nearest-even, except where the fp32 result
+    # straddles a rounding midpoint; near zero (small codebooks give exact
+    # float64 cancellations) only the bound applies.
+    half_ulp = 2.0 ** -8 if dt == "bf16" else 2.0 ** -11
+    scale = np.abs(g16.astype(np.float64))[..., None] * np.max(np.abs(c32))
+    assert np.all(np.abs(got - want) <= half_ulp * np.abs(want) + 1e-5 * scale + 2.0 ** -24)
+    big = np.abs(want) >= 1e-2 * scale
+    assert big.mean() > 0.5
+    match = np.mean(got[big] == _round16(want[big], dt))
+    assert match >= 0.998, match
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_decompress_matches_oracle(device, bits, dt):
+    """Keys and values to 16-bit floats in one call; every 5th token (a ragged
+    tail of the 64-vector workgroups), then a negative slot and one past the
+    pool (zeros)."""
+    w = W.DECODE_32K.with_(seq_len=300, num_kv_heads=2, bits_k=bits, bits_v=bits)
+    cache, _, _, slots = encode_gpu(w, device)
+    up = O.unpack_pool(pool_bytes(cache), oracle_layout(w))
+    sl = np.concatenate([slots[::5], [-1, w.num_blocks * 16 + 3]]).astype(np.int32)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    Ko = torch.full((len(sl), 2, 128), float("nan"), dtype=tdt, device=device)
+    Vo = torch.full_like(Ko, float("nan"))
+    tq.tq_decompress_kv(cache, torch.from_numpy(sl).to(device), Ko, Vo)
+    c32 = O.codebook_fp32(128, bits)[0]
+    for out, key, g in ((Ko, "k_idx", "k_g16"), (Vo, "v_idx", "v_g16")):
+        got = out.float().cpu().numpy().astype(np.float64)
+        idx, g16 = gpu_codes_at(up, sl[:-2], key, g)
+        _check_decompressed(got[:-2], O.reconstruct(idx, g16, w.rot_seed, c32), g16, c32, dt)
+        assert np.all(got[-2:] == 0)
+
+
+def test_decompress_one_stream_and_keys_only_cache(device):
+    """Keys only asked of a cache with values (values untouched), and a
+    keys-only cache."""
+    w = W.DECODE_32K.with_(seq_len=100, num_kv_heads=2, bits_k=4, bits_v=4)
+    cache, _, _, slots = encode_gpu(w, device)
+    up = O.unpack_pool(pool_bytes(cache), oracle_layout(w))
+    sl = torch.from_numpy(slots.astype(np.int32)).to(device)
+    Ko = torch.empty((len(slots), 2, 128), dtype=torch.bfloat16, device=device)
+    tq.tq_decompress_kv(cache, sl, Ko, None)
+    c32 = O.codebook_fp32(128, 4)[0]
+    idx, g16 = gpu_codes_at(up, slots, "k_idx", "k_g16")
+    _check_decompressed(Ko.float().cpu().numpy().astype(np.float64), O.reconstruct(idx, g16, w.rot_seed, c32), g16,
+                        c32, "bf16")
+    wk = W.SWEEP_64K.with_(seq_len=200, num_kv_heads=2, bits_k=3, qjl=True)
+    cache, _, _, slots = encode_gpu(wk, device)
+    up = O.unpack_pool(pool_bytes(cache), oracle_layout(wk))
+    Ko = torch.empty((len(slots), 2, 128), dtype=torch.float16, device=device)
+    tq.tq_decompress_kv(cache, torch.from_numpy(slots.astype(np.int32)).to(device), Ko)
+    c32 = O.codebook_fp32(128, 3)[0]
+    idx, g16 = gpu_codes_at(up, slots, "k_idx", "k_g16")
+    _check_decompressed(Ko.float().cpu().numpy().astype(np.float64), O.reconstruct(idx, g16, wk.rot_seed, c32), g16,
+                        c32, "f16")
+
+
 # -------------------------------------------------------- tiny end to end --
 
 def test_tiny_config_end_to_end(device):

@@ -207,3 +207,20 @@ def test_matrix_core_attend_split_sizes():
     # the 512-block cap and the 4096-split limit
     assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 512 * 4096) == 1 * 8 * 4096 * per
     assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 512 * 4096 + 1) == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_decompress_argument_checks_happen_before_the_device():
+    c = _fake_cache()
+    L = tq.lib()
+    sl, Ko, Vo = 0x200000, 0x300000, 0x400000
+    assert L.tq_decompress_kv(None, sl, 10, tq.TQ_BF16, Ko, Vo, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_decompress_kv(c.handle, sl, -1, tq.TQ_BF16, Ko, Vo, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_decompress_kv(c.handle, sl, 10, tq.TQ_F32, Ko, Vo, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_decompress_kv(c.handle, sl, 10, tq.TQ_BF16, Ko + 8, Vo, None) == tq.TQ_ERR_INVALID_ARG
+    assert "aligned" in L.tq_last_error().decode()
+    assert L.tq_decompress_kv(c.handle, None, 10, tq.TQ_F16, Ko, Vo, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_decompress_kv(c.handle, sl, 0, tq.TQ_BF16, Ko, Vo, None) == tq.TQ_OK       # nothing to do
+    assert L.tq_decompress_kv(c.handle, sl, 10, tq.TQ_BF16, None, None, None) == tq.TQ_OK  # no outputs
+    ko = _fake_cache(bits_v=0)
+    assert L.tq_decompress_kv(ko.handle, sl, 10, tq.TQ_BF16, Ko, Vo, None) == tq.TQ_ERR_INVALID_ARG
+    assert "keys-only" in L.tq_last_error().decode()
