@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "decode-attend GB/s of compressed KV read (% HBM peak) + encoded vectors/s"
-KERNEL_SOURCES = ["kv_cache_vector_encode_amd/csrc/tq_encode.hip", "kv_cache_vector_encode_amd/csrc/tq_decode.hip",
+KERNEL_SOURCES = ["kv_cache_vector_encode_amd/csrc/tq_encode.hip", "kv_cache_vector_encode_amd/csrc/tq_encode_row.h",
+                  "kv_cache_vector_encode_amd/csrc/tq_decode.hip",
                   "kv_cache_vector_encode_amd/csrc/tq_decode_mfma.hip", "kv_cache_vector_encode_amd/csrc/tq_merge.hip",
                   "kv_cache_vector_encode_amd/csrc/tq_device.h", "kv_cache_vector_encode_amd/csrc/tq_internal.h"]
 
@@ -229,6 +230,37 @@ def main():
         dq_ms = [e[0].elapsed_time(e[1]) for e in dq_ev]
         del Ko, Vo
 
+    # ---- one decode step with append (each sequence's last token arrives
+    # with the step) against the same work as two calls: encode of the new
+    # tokens, then decode-attend.  Outside the timed step, reported beside it.
+    st_ms, un_ms = [], []
+    if args.only == "both":
+        S = w.seq_len
+        Kn = K0.view(w.num_seqs, S, w.num_kv_heads, 128)[:, S - 1].contiguous()
+        Vn = V0.view(w.num_seqs, S, w.num_kv_heads, 128)[:, S - 1].contiguous()
+        new_slots = slots.view(w.num_seqs, S)[:, S - 1].contiguous()
+        reps = max(5, args.steps // 4)
+
+        def fused(i):
+            s = sets[i % nsets]
+            tq.tq_decode_step(q, Kn, Vn, s["cache"], bt, lens, s["out"], s["ws"], stream=stream)
+
+        def unfused(i):
+            s = sets[i % nsets]
+            tq.tq_encode_kv(Kn, Vn, new_slots, w.bits_k, s["cache"], stream)
+            tq.tq_decode_attend(q, s["cache"], bt, lens, s["out"], s["ws"], stream=stream)
+
+        for fn, acc in ((fused, st_ms), (unfused, un_ms)):
+            for i in range(3):
+                fn(i)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+            for i in range(reps):
+                ev[i][0].record(stream)
+                fn(i + 3)
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            acc.extend(e[0].elapsed_time(e[1]) for e in ev)
+
     kernels = {
         "tq_encode": {"bound": "hbm", "achieved": round(enc_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                       "frac": round(enc_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": enc_bytes,
@@ -245,6 +277,15 @@ def main():
             "frac": round(dq_bytes / dq_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": dq_bytes,
             "us_per_launch": round(dq_s * 1e6, 2), "median_us": round(float(np.median(dq_ms)) * 1e3, 2),
             "note": "every cached key and value to bf16; not part of the timed step"}
+    if st_ms:
+        st_s, un_s = float(np.mean(st_ms)) / 1e3, float(np.mean(un_ms)) / 1e3
+        kernels["tq_decode_step"] = {
+            "bound": "hbm", "achieved": round(dec_bytes / st_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(dec_bytes / st_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": dec_bytes,
+            "us_per_launch": round(st_s * 1e6, 2), "median_us": round(float(np.median(st_ms)) * 1e3, 2),
+            "unfused_us": round(un_s * 1e6, 2),
+            "note": "append each sequence's new token + decode-attend in one call; unfused_us = tq_encode_kv of "
+                    "the new tokens + tq_decode_attend; not part of the timed step"}
     dom = "tq_encode" if enc_s >= dec_s else "tq_decode_attend"
     traffic = None
     tf = os.path.join(ROOT, "profiles", "traffic.json")

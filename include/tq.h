@@ -188,6 +188,33 @@ int tq_decode_attend(const void* q, int32_t q_dtype, const tq_cache* cache,
                      float* logits_out, void* workspace, int64_t workspace_bytes,
                      void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * One decode step: append each sequence's new token to the compressed cache
+ * and attend over the whole sequence, new token included, in one call with
+ * one attend launch ([P1] online compression as tokens arrive, no
+ * calibration; [P2] Implementation plan, cache update then attention).
+ * Same result as tq_encode_kv of the new tokens followed by tq_decode_attend.
+ *   K_new, V_new: device [num_seqs][num_kv_heads][d], kv_dtype TQ_F32 /
+ *                 TQ_F16 / TQ_BF16, 16-byte aligned: the new token of every
+ *                 sequence;
+ *   seq_lens:     counts the new token, which sits at position seq_len - 1:
+ *                 slot block_tables[n][(seq_len-1)/16] * 16 + (seq_len-1) % 16
+ *                 (the block must be allocated; sequences of length 0 are
+ *                 skipped);
+ *   other arguments, the workspace and the outputs as tq_decode_attend.
+ * The split of the attend kernel that holds the new token's block encodes it
+ * (the vector-unit encoder's arithmetic) before streaming that block.  Needs
+ * a cache with values of the key bit width and no QJL sidecar
+ * (TQ_ERR_BITS_MISMATCH, TQ_ERR_UNSUPPORTED otherwise).  Asynchronous on
+ * hip_stream. */
+int tq_decode_step(const void* q, int32_t q_dtype, const void* K_new,
+                   const void* V_new, int32_t kv_dtype, tq_cache* cache,
+                   const int32_t* block_tables, const int32_t* seq_lens,
+                   int32_t num_seqs, int32_t num_q_heads,
+                   int32_t max_blocks_per_seq, float scale, float* out,
+                   float* logits_out, void* workspace, int64_t workspace_bytes,
+                   void* hip_stream);
+
 /* Keys-only scores ([P2] Q K_hat^T / sqrt(d_h); [P4] attention logits):
  * logits_out device f32 [num_seqs][num_q_heads][max_blocks_per_seq*16],
  * s_t as in tq_decode_attend for t < seq_len.  Works on any cache. */

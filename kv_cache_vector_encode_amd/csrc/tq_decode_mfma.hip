@@ -41,7 +41,10 @@
 
 #include <hip/hip_bf16.h>
 
+#include <type_traits>
+
 #include "tq_device.h"
+#include "tq_encode_row.h"
 
 namespace tq {
 
@@ -304,8 +307,69 @@ struct DecodeSmem {
   alignas(16) uint8_t ring[4 * Chunk<BITS>::kWaveRing];
 };
 
-template <int BITS, bool LOGITS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 3))) void decode_mfma_kernel(const DecodeArgs a, int ns, int gs) {
+// Decode step: encode the sequence's new token (keys and values of KV head
+// h) into row `row` of block `blk`, with the vector encoder's row algorithm
+// (FWHT in one 16-lane row, bucketed threshold search, packing, fp16 norm):
+// lanes 0..15 of wave 0 take the key, lanes 16..31 the value.  `lut` is 2 KB
+// of LDS not otherwise in use; every thread of the workgroup calls this.
+// The stores are performed (vmcnt 0) before the closing barrier, so the
+// workgroup's copies of the block that follow read the new rows.
+template <int BITS>
+__device__ __forceinline__ void append_token(const DecodeArgs& a, const AppendArgs& ap, int n, int h, int blk, int row,
+                                             uint2* lut, int tid) {
+  const float lut_scale = ap.tab.lut_scale, lut_off = ap.tab.lut_offset - 0.5f;
+  fill_lut(lut, ap.tab, lut_scale, lut_off, tid);
+  __syncthreads();
+  if (tid < 32) {
+    const int r = tid >> 4, L = tid & 15, ell = perm16(L);
+    // sign byte ell of the rotation, picked among wave-uniform words
+    const uint32_t n0 = __builtin_amdgcn_readfirstlane(a.rot.neg[0]), n1 = __builtin_amdgcn_readfirstlane(a.rot.neg[1]);
+    const uint32_t n2 = __builtin_amdgcn_readfirstlane(a.rot.neg[2]), n3 = __builtin_amdgcn_readfirstlane(a.rot.neg[3]);
+    const int wsel = ell >> 2;
+    const uint32_t wd = wsel == 0 ? n0 : wsel == 1 ? n1 : wsel == 2 ? n2 : n3;
+    const uint32_t sneg = (wd >> (8 * (ell & 3))) & 0xFFu;
+    uint32_t smask[8];
+    float x[8];
+    const int64_t elem = ((int64_t)n * a.num_kv_heads + h) * kD + 8 * ell;
+    const void* src = r ? ap.v_new : ap.k_new;
+    if (ap.dtype == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) smask[i] = ((sneg >> i) & 1u) << 31;
+      load8_signed<0>(src, elem, smask, x);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        smask[i] = i < 4 ? (((sneg >> (2 * i)) & 1u) << 15) | (((sneg >> (2 * i + 1)) & 1u) << 31) : 0u;
+      if (ap.dtype == 1) load8_signed<1>(src, elem, smask, x);
+      else load8_signed<2>(src, elem, smask, x);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+    ss = row_sum(ss);
+    const FwhtLane fc = fwht_lane(L);
+    fwht_row(x, fc);   // lane L now holds coordinates 8L..8L+7
+    const float gamma = __builtin_amdgcn_sqrtf(ss);
+    const float inv = ss > 0.f ? fc.sig * __builtin_amdgcn_rcpf(gamma * 11.313708498984761f) : 0.f;
+    uint32_t code[8];
+    row_codes<BITS>(x, inv * lut_scale, lut_off, lut, code);
+    bool store_lane;
+    int store_off;
+    const uint32_t word = row_pack<BITS>(code, L, store_lane, store_off);
+    uint8_t* base = const_cast<uint8_t*>(a.pool) + ((int64_t)blk * a.num_kv_heads + h) * a.lay.block_bytes;
+    uint8_t* rec = base + (r ? a.lay.off_v + (int64_t)row * a.lay.v_rec : a.lay.off_k + (int64_t)row * a.lay.k_rec);
+    if (store_lane) *reinterpret_cast<uint32_t*>(rec + store_off) = word;
+    if (L == 0)
+      *reinterpret_cast<__half*>(base + (r ? a.lay.off_gv : a.lay.off_gk) + 2 * row) =
+          __float2half_rn(fminf(gamma, 65504.f));
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+template <int BITS, bool LOGITS, bool APPEND>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 3))) void decode_mfma_kernel(
+    const DecodeArgs a, int ns, int gs, const typename std::conditional<APPEND, AppendArgs, NoAppend>::type ap) {
   using C = Chunk<BITS>;
   constexpr int NS = C::kStages;
   __shared__ DecodeSmem<BITS> sm;
@@ -392,12 +456,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
     for (int j = 0; 1024 * j < qbytes; ++j)
       dma_x4(qs_lds + 1024u * j, qsrc, (uint32_t)min(16 * lane + 1024 * j, qbytes - 16));
   }
-  const int k_pro = min(NS, my_n);
-  for (int k = 0; k < k_pro; ++k) {
-    int b0, b1;
-    fetch_pair(k, b0, b1);
-    dma_pair(k, b0, b1);
+  // decode step: the split holding the new token's block encodes it first,
+  // and copies nothing before that
+  bool owner = false;
+  int new_blk = 0, new_row = 0;
+  if constexpr (APPEND) {
+    const int t_new = seq_len - 1;
+    if (t_new >= 0 && t_new / kBlock >= sb0 && t_new / kBlock < sb1) {
+      new_blk = btab[t_new / kBlock];
+      new_row = t_new & (kBlock - 1);
+      owner = (uint32_t)new_blk < nblocks;
+    }
   }
+  const int k_pro = min(NS, my_n);
+  auto prologue_copies = [&]() {
+    for (int k = 0; k < k_pro; ++k) {
+      int b0, b1;
+      fetch_pair(k, b0, b1);
+      dma_pair(k, b0, b1);
+    }
+  };
+  if (!owner) prologue_copies();
 
   constexpr bool kI8 = DecodeSmem<BITS>::kI8;
   constexpr int kLevels = 1 << BITS;
@@ -421,7 +500,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
     }
     sm.tv[i] = f16_bits(sm.cent[1][i & mask]) | (f16_bits(sm.cent[1][i >> BITS]) << 16);
   }
-  if (wv == 0) wait_pairs_behind<BITS>(k_pro);   // the query copy has landed
+  if (wv == 0) wait_pairs_behind<BITS>(owner ? 0 : k_pro);   // the query copy has landed
   __syncthreads();
 
   // ---- rotate this slice's queries (rows of 16 lanes, one head each; the
@@ -499,6 +578,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
     }
   }
   __syncthreads();
+  if constexpr (APPEND) {
+    if (owner) {   // workgroup-uniform; no copy is in flight, so the ring is free
+      append_token<BITS>(a, ap, n, h, new_blk, new_row, reinterpret_cast<uint2*>(s_ring), tid);
+      prologue_copies();
+    }
+  }
   const bool col_lo = m >= 8;
   const bool col_live = (m & 7) < gcount;
 
@@ -756,36 +841,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
   }
 }
 
-int launch_decode_mfma(const DecodeArgs& a, int bits, int ns, int gs, void* stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
+static int check_mfma_args(const DecodeArgs& a, int bits) {
   // the kernel's chunk geometry is fixed at compile time: values, no sidecar
   const int64_t expect = 512 * bits + 64;
   if (a.lay.block_bytes != expect || a.lay.off_k != 0 || a.lay.off_v != 256 * bits ||
       a.lay.off_gk != 512 * bits || a.lay.off_gv != 512 * bits + 32 ||
       (reinterpret_cast<uintptr_t>(a.pool) & 15) != 0)
     return (int)hipErrorInvalidValue;
+  if (bits < 2 || bits > 4) return (int)hipErrorInvalidValue;
   // 4-bit keys need the integer form of the key codebook (odd-symmetric)
   if (bits == 4 && !(a.ki8_unit > 0.f)) return (int)hipErrorInvalidValue;
   // a wave keeps the block-table entries of its pairs one per lane
   if (a.blocks_per_split < 1 || a.blocks_per_split > 2 * 4 * 64) return (int)hipErrorInvalidValue;
-  dim3 grid((unsigned)a.num_splits, (unsigned)(a.num_kv_heads * ns), (unsigned)a.num_seqs);
+  return 0;
+}
+
+template <bool APPEND, typename AP>
+static void launch_mfma(const DecodeArgs& a, const AP& ap, int bits, int ns, int gs, hipStream_t s) {
+  const dim3 grid((unsigned)a.num_splits, (unsigned)(a.num_kv_heads * ns), (unsigned)a.num_seqs);
   const bool lg = a.logits != nullptr;
   switch (bits) {
     case 2:
-      if (lg) hipLaunchKernelGGL((decode_mfma_kernel<2, true>), grid, dim3(256), 0, s, a, ns, gs);
-      else hipLaunchKernelGGL((decode_mfma_kernel<2, false>), grid, dim3(256), 0, s, a, ns, gs);
+      if (lg) hipLaunchKernelGGL((decode_mfma_kernel<2, true, APPEND>), grid, dim3(256), 0, s, a, ns, gs, ap);
+      else hipLaunchKernelGGL((decode_mfma_kernel<2, false, APPEND>), grid, dim3(256), 0, s, a, ns, gs, ap);
       break;
     case 3:
-      if (lg) hipLaunchKernelGGL((decode_mfma_kernel<3, true>), grid, dim3(256), 0, s, a, ns, gs);
-      else hipLaunchKernelGGL((decode_mfma_kernel<3, false>), grid, dim3(256), 0, s, a, ns, gs);
+      if (lg) hipLaunchKernelGGL((decode_mfma_kernel<3, true, APPEND>), grid, dim3(256), 0, s, a, ns, gs, ap);
+      else hipLaunchKernelGGL((decode_mfma_kernel<3, false, APPEND>), grid, dim3(256), 0, s, a, ns, gs, ap);
       break;
-    case 4:
-      if (lg) hipLaunchKernelGGL((decode_mfma_kernel<4, true>), grid, dim3(256), 0, s, a, ns, gs);
-      else hipLaunchKernelGGL((decode_mfma_kernel<4, false>), grid, dim3(256), 0, s, a, ns, gs);
+    default:
+      if (lg) hipLaunchKernelGGL((decode_mfma_kernel<4, true, APPEND>), grid, dim3(256), 0, s, a, ns, gs, ap);
+      else hipLaunchKernelGGL((decode_mfma_kernel<4, false, APPEND>), grid, dim3(256), 0, s, a, ns, gs, ap);
       break;
-    default: return (int)hipErrorInvalidValue;
   }
+}
+
+int launch_decode_mfma(const DecodeArgs& a, int bits, int ns, int gs, void* stream) {
+  const int e = check_mfma_args(a, bits);
+  if (e) return e;
+  launch_mfma<false>(a, NoAppend{}, bits, ns, gs, static_cast<hipStream_t>(stream));
   return (int)hipGetLastError();
+}
+
+// Decode step: append each sequence's new token, attend, merge.
+int launch_decode_step(const DecodeArgs& a, const AppendArgs& ap, int bits, void* stream) {
+  const int e = check_mfma_args(a, bits);
+  if (e) return e;
+  const int ns = decode_slices(a.group);
+  const int gs = (a.group + ns - 1) / ns;
+  launch_mfma<true>(a, ap, bits, ns, gs, static_cast<hipStream_t>(stream));
+  const hipError_t le = hipGetLastError();
+  if (le != hipSuccess) return (int)le;
+  return launch_merge(a, stream);
 }
 
 }  // namespace tq

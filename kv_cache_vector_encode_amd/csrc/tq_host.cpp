@@ -594,6 +594,46 @@ int tq_decode_attend(const void* q, int32_t q_dtype, const tq_cache* cache,
   return TQ_OK;
 }
 
+int tq_decode_step(const void* q, int32_t q_dtype, const void* K_new, const void* V_new, int32_t kv_dtype,
+                   tq_cache* cache, const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                   int32_t num_q_heads, int32_t max_blocks_per_seq, float scale, float* out, float* logits_out,
+                   void* workspace, int64_t workspace_bytes, void* hip_stream) {
+  int s = validate_decode(q, q_dtype, cache, block_tables, seq_lens, num_seqs, num_q_heads, max_blocks_per_seq);
+  if (s != TQ_OK) return s;
+  const tq_cache_config& cfg = cache->cfg;
+  if (cfg.bits_v == 0) return fail(TQ_ERR_INVALID_ARG, "decode_step needs a cache with values");
+  if (cfg.bits_v != cfg.bits_k) return fail(TQ_ERR_BITS_MISMATCH, "decode_step needs keys and values of one bit width");
+  if (!decode_uses_mfma(cache, true))
+    return fail(TQ_ERR_UNSUPPORTED, "decode_step runs on the matrix-core decode (no QJL sidecar)");
+  if (kv_dtype != TQ_F32 && kv_dtype != TQ_F16 && kv_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad kv_dtype");
+  if (num_seqs == 0) return TQ_OK;
+  if (!out || !K_new || !V_new) return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  if ((reinterpret_cast<uintptr_t>(K_new) | reinterpret_cast<uintptr_t>(V_new)) % 16 != 0)
+    return fail(TQ_ERR_INVALID_ARG, "K_new and V_new must be 16-byte aligned");
+  const int64_t need = tq_decode_workspace_bytes(cache, num_seqs, num_q_heads, max_blocks_per_seq);
+  if (!workspace || workspace_bytes < need) return fail(TQ_ERR_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(TQ_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  if ((s = check_device()) != TQ_OK) return s;
+  tq::DecodeArgs a;
+  fill_decode_args(a, q, q_dtype, cache, block_tables, seq_lens, num_seqs, num_q_heads, max_blocks_per_seq, scale);
+  a.out = out;
+  a.logits = logits_out;
+  a.logits_stride = (int64_t)max_blocks_per_seq * tq::kBlock;
+  a.blocks_per_split = blocks_per_split_for(cache, num_seqs, a.group, max_blocks_per_seq, true, true);
+  if (a.blocks_per_split <= 0) return fail(TQ_ERR_UNSUPPORTED, "sequence too long for this cache's decode kernel");
+  a.num_splits = std::max(1, (max_blocks_per_seq + a.blocks_per_split - 1) / a.blocks_per_split);
+  a.partials = static_cast<float*>(workspace);
+  tq::AppendArgs ap;
+  std::memset(&ap, 0, sizeof(ap));
+  ap.k_new = K_new;
+  ap.v_new = V_new;
+  ap.dtype = kv_dtype;
+  ap.tab = cache->tab_k;
+  int err = tq::launch_decode_step(a, ap, cfg.bits_k, hip_stream);
+  if (err != 0) return hip_fail(err, "decode step launch");
+  return TQ_OK;
+}
+
 int tq_decode_logits(const void* q, int32_t q_dtype, const tq_cache* cache,
                      const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
                      int32_t num_q_heads, int32_t max_blocks_per_seq, float scale,

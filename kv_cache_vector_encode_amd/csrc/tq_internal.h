@@ -108,6 +108,17 @@ struct DecodeArgs {
   float ki8_unit;
 };
 
+// Decode step with append: each sequence's new token (position seq_len - 1,
+// its slot taken from the block table) is encoded into the cache by the
+// split that holds its block, before that split streams the block.
+struct AppendArgs {
+  const void* k_new;        // [seqs][kv_heads][128]
+  const void* v_new;
+  int32_t dtype;            // 0 fp32, 1 fp16, 2 bf16
+  CodecTables tab;          // keys and values share the bit width
+};
+struct NoAppend {};
+
 // ----------------------------------------------------------- reconstruct --
 struct ReconArgs {
   const uint8_t* pool;
@@ -147,6 +158,7 @@ int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int atte
 int decode_slices(int group);
 int launch_decode_mfma(const DecodeArgs& a, int bits, int ns, int gs, void* stream);
 int launch_merge(const DecodeArgs& a, void* stream);
+int launch_decode_step(const DecodeArgs& a, const AppendArgs& ap, int bits, void* stream);
 int launch_reconstruct(const ReconArgs& a, void* stream);
 int launch_decompress(const DecompArgs& a, void* stream);
 

@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.c_int32, ctypes.c_float, _P, _P]),
             "tq_reconstruct": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
             "tq_decompress_kv": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
+            "tq_decode_step": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P, _P, _P, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P,
+                                              ctypes.c_int64, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -241,6 +244,20 @@ def tq_decode_logits(q, cache: Cache, block_tables, seq_lens, logits_out, scale:
 def tq_reconstruct(cache: Cache, slots, which: int, out, stream=None):
     _check(lib().tq_reconstruct(cache.handle, _ptr(slots), slots.shape[0], which, _ptr(out), _stream(stream)),
            "tq_reconstruct")
+
+
+def tq_decode_step(q, K_new, V_new, cache: Cache, block_tables, seq_lens, out, workspace, logits_out=None,
+                   scale: float = 0.0, stream=None):
+    """Append every sequence's new token (K_new, V_new [seqs][kv_heads][128],
+    at position seq_len - 1) and attend over the whole sequence; arguments
+    otherwise as tq_decode_attend."""
+    ns, hq, _ = q.shape
+    if K_new.dtype != V_new.dtype:
+        raise TypeError("K_new and V_new must have one dtype")
+    _check(lib().tq_decode_step(_ptr(q), _dtype_code(q), _ptr(K_new), _ptr(V_new), _dtype_code(K_new), cache.handle,
+                                _ptr(block_tables), _ptr(seq_lens), ns, hq, block_tables.shape[1], scale, _ptr(out),
+                                _ptr(logits_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream)), "tq_decode_step")
 
 
 def tq_decompress_kv(cache: Cache, slots, K_out, V_out=None, stream=None):

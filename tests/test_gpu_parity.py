@@ -264,6 +264,84 @@ def test_decode_logits_keys_only(device, bits, qjl):
         assert np.all(err <= LOGIT_RTOL * scl), float((err / scl).max())
 
 
+# ------------------------------------------------------------- decode step --
+
+def _step_case(device, bits, group, hkv, lens, kv_dtype="bf16", seed=11):
+    """Every token but each sequence's last goes in with tq_encode_kv; the
+    last arrives with tq_decode_step (position len - 1, its slot from the
+    block table).  Held to the oracle: the new tokens' codes (band rule) and
+    fp16 norms against the oracle encode of the same inputs, then logits and
+    outputs over the whole cache as read back."""
+    nseq = len(lens)
+    w = W.DECODE_32K.with_(seed=seed, num_seqs=nseq, seq_len=max(lens), num_kv_heads=hkv,
+                           num_q_heads=hkv * group, bits_k=bits, bits_v=bits)
+    S = w.seq_len
+    new_tok = np.array([n * S + L - 1 for n, L in enumerate(lens) if L > 0], dtype=np.int64)
+    slots = W.slot_mapping(w).copy()
+    slots[new_tok] = -1                          # the new tokens are not in the cache yet
+    cache, _, _, _ = encode_gpu(w, device, slots=slots)
+    kb, k64 = W.keys(w)
+    vb, v64 = W.values(w)
+    last = np.array([n * S + max(L, 1) - 1 for n, L in enumerate(lens)])
+    Kn, Vn = to_device(kb[last], "bf16", device), to_device(vb[last], "bf16", device)
+    if kv_dtype == "f32":
+        Kn, Vn = Kn.float(), Vn.float()
+    elif kv_dtype == "f16":   # bf16 values that f16 holds exactly (N(0,1) magnitudes)
+        Kn, Vn = Kn.float().half(), Vn.float().half()
+    bt = W.block_tables(w)
+    qb, q64 = W.queries(w)
+    q = to_device(qb, "bf16", device)
+    bt_d = torch.from_numpy(bt).to(device)
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=device)
+    out = torch.full((nseq, w.num_q_heads, 128), float("nan"), device=device)
+    logits = torch.full((nseq, w.num_q_heads, bt.shape[1] * 16), float("nan"), device=device)
+    ws = tq.new_workspace(cache, nseq, w.num_q_heads, bt.shape[1], device=device)
+    tq.tq_decode_step(q, Kn, Vn, cache, bt_d, lens_d, out, ws, logits_out=logits)
+    torch.cuda.synchronize()
+    up = O.unpack_pool(pool_bytes(cache), oracle_layout(w))
+    # the new tokens' codes and norms
+    c32, t32 = O.codebook_fp32(128, bits)
+    kin = Kn.float().cpu().numpy().astype(np.float64)
+    vin = Vn.float().cpu().numpy().astype(np.float64)
+    for n, L in enumerate(lens):
+        if L == 0:
+            continue
+        b, r = bt[n, (L - 1) // 16], (L - 1) % 16
+        for x, key, g in ((kin[n], "k_idx", "k_g16"), (vin[n], "v_idx", "v_g16")):
+            enc = O.encode(x, w.rot_seed, c32)
+            check_codes(up[key][b, :, r], enc["idx"], enc["y"], t32, what="appended codes")
+            check_norms(up[g][b, :, r], enc["gamma"], what="appended norms")
+    ref = _oracle_decode(w, up, bt, lens, q64, group)
+    go, gl = out.cpu().numpy().astype(np.float64), logits.cpu().numpy().astype(np.float64)
+    for (n, hq), (s_, scl, o) in ref.items():
+        L = lens[n]
+        if L == 0:
+            assert np.all(go[n, hq] == 0)
+            continue
+        err = np.abs(gl[n, hq, :L] - s_)
+        assert np.all(err <= LOGIT_RTOL * scl), (n, hq, float((err / scl).max()))
+        e = np.linalg.norm(go[n, hq] - o) / np.linalg.norm(o)
+        assert e <= OUT_RTOL, (n, hq, e)
+    return up, bt
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_decode_step_appends_and_attends(device, bits):
+    # new token first in a block (17), mid-block (700), last in a block (1024),
+    # a one-token sequence, an empty one
+    _step_case(device, bits, 8, 2, [17, 700, 1024, 1, 0])
+
+
+@pytest.mark.parametrize("group", [1, 16])
+def test_decode_step_group_sizes(device, group):
+    # 16 query heads per KV head: two slices of 8 both append the token
+    _step_case(device, 4, group, 2, [300, 2100], kv_dtype="f32")
+
+
+def test_decode_step_f16_inputs_and_long_split_chain(device):
+    _step_case(device, 4, 8, 1, [4100, 33], kv_dtype="f16")
+
+
 # ------------------------------------------------------------- reconstruct --
 
 @pytest.mark.parametrize("bits", [2, 3, 4])

@@ -224,3 +224,25 @@ def test_decompress_argument_checks_happen_before_the_device():
     ko = _fake_cache(bits_v=0)
     assert L.tq_decompress_kv(ko.handle, sl, 10, tq.TQ_BF16, Ko, Vo, None) == tq.TQ_ERR_INVALID_ARG
     assert "keys-only" in L.tq_last_error().decode()
+
+
+def test_decode_step_argument_checks_happen_before_the_device():
+    c = _fake_cache()
+    L = tq.lib()
+    q, K, V, bt, sl, out, ws = 0x200000, 0x300000, 0x400000, 0x500000, 0x600000, 0x700000, 0x800000
+
+    def step(cache, kv_dtype=tq.TQ_BF16, Kp=K, Vp=V, ns=2, wsb=1 << 30):
+        return L.tq_decode_step(q, tq.TQ_BF16, Kp, Vp, kv_dtype, cache, bt, sl, ns, 64, 8, 0.0, out, None, ws, wsb,
+                                None)
+
+    assert step(None) == tq.TQ_ERR_INVALID_ARG
+    assert step(c.handle, kv_dtype=7) == tq.TQ_ERR_INVALID_ARG
+    assert step(c.handle, Kp=None) == tq.TQ_ERR_INVALID_ARG
+    assert step(c.handle, Vp=V + 4) == tq.TQ_ERR_INVALID_ARG
+    assert "aligned" in L.tq_last_error().decode()
+    assert step(c.handle, wsb=16) == tq.TQ_ERR_WORKSPACE
+    assert step(c.handle, ns=0) == tq.TQ_OK   # nothing to do
+    assert step(_fake_cache(bits_v=0).handle) == tq.TQ_ERR_INVALID_ARG
+    r, r2 = tq.tq_make_rotation(42, 128), tq.tq_make_rotation(43, 128)
+    qc = tq.tq_cache_create(tq.make_config(8, 4, 4, 4, r, True, r2), 0x100000)
+    assert step(qc.handle) == tq.TQ_ERR_UNSUPPORTED
