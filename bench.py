@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--workload", default="decode_1x32768_h8_gqa8_b4")
     ap.add_argument("--sets", type=int, default=0, help="rotating input/cache sets (0: enough for 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the decompress and decode-step measurements after the step (profiling aid: their "
+                         "launches would mix into the per-kernel statistics)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
     ap.add_argument("--only", choices=["encode", "decode", "both"], default="both",
                     help="profiling aid: time only one of the two kernels")
@@ -215,7 +218,7 @@ def main():
     # ---- decompression of every cached key and value to bf16 (attention over
     # a compressed prefix): outside the step, reported beside it
     dq_ms = []
-    if args.only == "both":
+    if args.only == "both" and not args.no_extras:
         Ko = torch.empty((w.tokens, w.num_kv_heads, 128), dtype=torch.bfloat16, device=dev)
         Vo = torch.empty_like(Ko)
         for i in range(3):
@@ -234,7 +237,7 @@ def main():
     # with the step) against the same work as two calls: encode of the new
     # tokens, then decode-attend.  Outside the timed step, reported beside it.
     st_ms, un_ms = [], []
-    if args.only == "both":
+    if args.only == "both" and not args.no_extras:
         S = w.seq_len
         Kn = K0.view(w.num_seqs, S, w.num_kv_heads, 128)[:, S - 1].contiguous()
         Vn = V0.view(w.num_seqs, S, w.num_kv_heads, 128)[:, S - 1].contiguous()
