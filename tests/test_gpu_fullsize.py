@@ -7,6 +7,11 @@
   (sequence, query head) pairs, against the oracle computed one by one.
 * llama70b_4x131072_h8_gqa8_b3: the same, with the encode split into one
   call per sequence (host memory), decode as in bench.py.
+* decode_1x32768_h8_gqa8_b4 as a generation step: every token but the last
+  through tq_encode_kv, the last through tq_decode_step (the launch
+  configuration bench.py times); the appended codes and norms and sampled
+  outputs against the oracle; then tq_decompress_kv of every key and value
+  to bf16, checked on sampled vectors.
 * sweep_16h_65536_keys: keys-only caches for b = 2, 3, 4 with and without
   the QJL residual; tq_decode_logits for one query per head; parity of codes
   and logits on exactly 10^5 seeded (head, token) pairs, plus the logit bias
@@ -49,9 +54,9 @@ def _chunks(cache, w, blocks, head=None):
     return arr, lay
 
 
-def _encode_all(w, device, per_call_tokens=None):
+def _encode_all(w, device, per_call_tokens=None, slots=None):
     cache = make_cache(w, device)
-    slots = W.slot_mapping(w)
+    slots = W.slot_mapping(w) if slots is None else slots
     n = w.tokens if per_call_tokens is None else per_call_tokens
     for t0 in range(0, w.tokens, n):
         cnt = min(n, w.tokens - t0)
@@ -147,6 +152,58 @@ def test_fullsize_encode_and_decode(device, name, npairs):
     out2, logits = _decode(w, cache, device, want_logits=True)
     wo2, wl = _check_decode_pairs(w, cache, pairs, out2, logits)
     _say(f"{name}: band mismatches {nb}; worst out {max(wo, wo2):.2e}; worst logit {wl:.2e} (bars 2e-3, 1e-4)")
+
+
+def test_fullsize_decode_step_and_decompress(device):
+    w = W.DECODE_32K
+    rng = np.random.default_rng(14)
+    S = w.seq_len
+    full = W.slot_mapping(w)
+    slots = full.copy()
+    slots[S - 1::S] = -1                       # each sequence's last token arrives with the step
+    _say(f"{w.name}: encode {2 * (w.tokens - w.num_seqs) * w.num_kv_heads} vectors, then one decode step")
+    cache, _ = _encode_all(w, device, slots=slots)
+    kb, k64 = W.keys(w, S - 1, 1)
+    vb, v64 = W.values(w, S - 1, 1)
+    Kn, Vn = to_device(kb, w.in_dtype, device), to_device(vb, w.in_dtype, device)
+    bt = torch.from_numpy(W.block_tables(w)).to(device)
+    lens = torch.from_numpy(W.seq_lens(w)).to(device)
+    q = to_device(W.queries(w)[0], "bf16", device)
+    out = torch.full((w.num_seqs, w.num_q_heads, 128), float("nan"), device=device)
+    ws = tq.new_workspace(cache, w.num_seqs, w.num_q_heads, bt.shape[1], device=device)
+    tq.tq_decode_step(q, Kn, Vn, cache, bt, lens, out, ws)
+    torch.cuda.synchronize()
+    # appended token: codes and norms against the oracle encode
+    c32, t32 = O.codebook_fp32(128, w.bits_k)
+    s_new = full[S - 1]
+    arr, lay = _chunks(cache, w, [s_new // 16])
+    up = O.unpack_pool(arr, lay)
+    for x64, ki, kg in ((k64, "k_idx", "k_g16"), (v64, "v_idx", "v_g16")):
+        enc = O.encode(x64.reshape(-1, 128), w.rot_seed, c32)
+        check_codes(up[ki][0, :, s_new % 16], enc["idx"], enc["y"], t32, what="appended codes")
+        check_norms(up[kg][0, :, s_new % 16], enc["gamma"], what="appended norms")
+    pairs = [(0, int(hq)) for hq in rng.choice(w.num_q_heads, 6, replace=False)]
+    wo, _ = _check_decode_pairs(w, cache, pairs, out)
+    # every key and value back to bf16; sampled vectors against the oracle
+    Ko = torch.empty((w.tokens, w.num_kv_heads, 128), dtype=torch.bfloat16, device=device)
+    Vo = torch.empty_like(Ko)
+    tq.tq_decompress_kv(cache, torch.from_numpy(full).to(device), Ko, Vo)
+    torch.cuda.synchronize()
+    toks = np.sort(rng.choice(w.tokens, 64, replace=False))
+    arr, lay = _chunks(cache, w, full[toks] // 16)
+    up = O.unpack_pool(arr, lay)
+    r = full[toks] % 16
+    worst = 0.0
+    for out16, ki, kg in ((Ko, "k_idx", "k_g16"), (Vo, "v_idx", "v_g16")):
+        got = out16[torch.from_numpy(toks).to(device)].float().cpu().numpy().astype(np.float64)
+        idx = up[ki][np.arange(len(toks)), :, r]
+        g16 = up[kg][np.arange(len(toks)), :, r]
+        want = O.reconstruct(idx, g16, w.rot_seed, c32)
+        scale = np.abs(g16.astype(np.float64))[..., None] * np.max(np.abs(c32))
+        err = np.abs(got - want) - (2.0 ** -8) * np.abs(want)
+        assert np.all(err <= 1e-5 * scale + 2.0 ** -24)
+        worst = max(worst, float(np.max(np.abs(got - want) / (scale + 1e-30))))
+    _say(f"{w.name} step: worst out {wo:.2e} (bar 2e-3); decompress worst |err|/scale {worst:.2e}")
 
 
 def test_fullsize_llama70b_b3(device):

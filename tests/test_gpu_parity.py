@@ -123,6 +123,29 @@ def test_encode_zero_vectors_skips_and_untouched_slots(device):
             assert np.all(rec == 0xAB)
 
 
+def test_encode_norm_saturates_at_fp16_max(device):
+    """A norm above 65504 is stored as the fp16 maximum; its codes are those
+    of its direction."""
+    w = W.DECODE_32K.with_(seq_len=32, num_kv_heads=2)
+    kb, k64 = W.keys(w)
+    vb, v64 = W.values(w)
+    big = W.bf16_bits(np.float32(4096.0) * W.bf16_to_f64(kb[3]).astype(np.float32))
+    kb[3] = big
+    k64[3] = W.bf16_to_f64(big)
+    slots = W.slot_mapping(w)
+    cache = make_cache(w, device)
+    tq.tq_encode_kv(to_device(kb, "bf16", device), to_device(vb, "bf16", device),
+                    torch.from_numpy(slots).to(device), w.bits_k, cache)
+    lay = oracle_layout(w)
+    up = O.unpack_pool(pool_bytes(cache), lay)
+    c32, t32 = O.codebook_fp32(128, w.bits_k)
+    enc = O.encode(k64[3], w.rot_seed, c32)
+    assert np.all(enc["gamma"] > 65504)
+    b, r = slots[3] // 16, slots[3] % 16
+    assert np.all(up["k_g16"][b, :, r] == np.float16(65504))
+    check_codes(up["k_idx"][b, :, r], enc["idx"], enc["y"], t32, what="saturated-norm codes")
+
+
 def test_encode_bits_mismatch_is_rejected(device):
     w = W.DECODE_32K.with_(seq_len=16)
     cache = make_cache(w, device)
