@@ -278,6 +278,49 @@ def reconstruct(idx, gamma16, seed: int, c32):
 
 
 # ---------------------------------------------------------------------------
+# Comparison codec: per-vector min/max uniform quantiser after the same
+# rotation ([P4] Step 3 compress_value / decompress_value: rotate the whole
+# vector, scale = (max - min) / (2^b - 1), q = round((y - min) / scale),
+# scale and zero point stored as fp16; undone by the inverse rotation).
+# ---------------------------------------------------------------------------
+
+def fp16_sat(v) -> np.ndarray:
+    """fp16 round-to-nearest-even, saturating at +-65504 (this build's reading:
+    the page's .half() would give infinities past the fp16 range)."""
+    return np.clip(np.asarray(v, dtype=np.float64), -65504.0, 65504.0).astype(np.float16)
+
+
+def minmax_encode(x, seed: int, bits: int):
+    """Min/max codes of vectors ``x`` (..., d): y = R x (no norm split);
+    lo = min_j y_j, hi = max_j y_j; scale = (hi - lo) / (2^bits - 1);
+    u_j = (y_j - lo) / scale; q_j = round half to even (torch's round) of
+    u_j, clipped to [0, 2^bits - 1].  A vector whose rotated coordinates are
+    all equal (scale = 0, e.g. zero) takes every code 0 (the page divides by
+    zero there; this build's reading).  scale16 = fp16(scale), zero16 =
+    fp16(lo).  Returns dict(codes, scale, zero, scale16, zero16, u, y)."""
+    x = np.asarray(x, dtype=np.float64)
+    R = rotation_matrix(seed, x.shape[-1])
+    y = x @ R.T
+    lo, hi = y.min(axis=-1), y.max(axis=-1)
+    scale = (hi - lo) / ((1 << bits) - 1)
+    safe = np.where(scale > 0, scale, 1.0)
+    u = np.where((scale > 0)[..., None], (y - lo[..., None]) / safe[..., None], 0.0)
+    q = np.clip(np.rint(u), 0, (1 << bits) - 1).astype(np.int64)
+    return {"codes": q, "scale": scale, "zero": lo, "scale16": fp16_sat(scale), "zero16": fp16_sat(lo),
+            "u": u, "y": y}
+
+
+def minmax_decode(codes, scale16, zero16, seed: int):
+    """x_hat = R^T (codes * scale16 + zero16), in float64 from the stored
+    fp16 scale and zero point ([P4] Step 3 decompress_value; the inverse is
+    R^T, not a second forward rotation)."""
+    codes = np.asarray(codes, dtype=np.float64)
+    R = rotation_matrix(seed, codes.shape[-1])
+    yhat = codes * np.asarray(scale16, dtype=np.float64)[..., None] + np.asarray(zero16, dtype=np.float64)[..., None]
+    return yhat @ R
+
+
+# ---------------------------------------------------------------------------
 # E6: optional 1-bit QJL residual sketch  ([P3] contribution "Optional 1-bit
 # QJL residual for unbiased dot-product": sketch the signs of the rotated-frame
 # residual through an independent R', store sigma, add a correction to q^T k).

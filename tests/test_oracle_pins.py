@@ -502,3 +502,81 @@ def test_vectorised_unpacker_equals_per_token_spec():
                     np.testing.assert_array_equal(np.asarray(vec[k][b, h, r]), np.asarray(v), err_msg=k)
         sub = O.unpack_pool(pool, lay, blocks=[2, 0])
         np.testing.assert_array_equal(sub["k_idx"][0], vec["k_idx"][2])
+
+
+# ---------------------------------------------------------------------------
+# Min/max comparison codec ([P4] Step 3 compress_value / decompress_value)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_minmax_arithmetic_progression_closed_form(bits):
+    # rotated coordinates a + (b - a) j / 127 in a shuffled order: lo = a,
+    # scale = (b - a) / (2^bits - 1), code of step j = round(j (2^bits-1)/127)
+    # (127 is prime, so no step lands on a rounding tie)
+    rng = np.random.default_rng(bits)
+    a, b = -0.7, 1.3
+    j = rng.permutation(128)
+    y = a + (b - a) * j / 127.0
+    x = y @ O.rotation_matrix(5, 128)           # R x = y
+    enc = O.minmax_encode(x, 5, bits)
+    levels = (1 << bits) - 1
+    assert np.allclose(enc["y"], y, atol=1e-13)
+    assert abs(enc["zero"] - a) < 1e-13 and abs(enc["scale"] - (b - a) / levels) < 1e-13
+    assert np.array_equal(enc["codes"], np.rint(j * levels / 127.0).astype(np.int64))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_minmax_endpoints_and_error_bound(bits):
+    rng = np.random.default_rng(10 + bits)
+    x = rng.standard_normal((500, 128)) * rng.lognormal(size=(500, 1))
+    enc = O.minmax_encode(x, 42, bits)
+    levels = (1 << bits) - 1
+    rows = np.arange(500)
+    assert np.all(enc["codes"][rows, enc["y"].argmin(-1)] == 0)
+    assert np.all(enc["codes"][rows, enc["y"].argmax(-1)] == levels)
+    # with the exact scale and zero point every coordinate is within half a step
+    yq = enc["codes"] * enc["scale"][:, None] + enc["zero"][:, None]
+    assert np.all(np.abs(yq - enc["y"]) <= enc["scale"][:, None] / 2 * (1 + 1e-12))
+    # decoding from the fp16 parameters adds at most their rounding errors
+    xh = O.minmax_decode(enc["codes"], enc["scale16"], enc["zero16"], 42)
+    yh = xh @ O.rotation_matrix(42, 128).T
+    bound = (enc["scale"] / 2 + levels * np.abs(enc["scale16"].astype(np.float64) - enc["scale"])
+             + np.abs(enc["zero16"].astype(np.float64) - enc["zero"]))
+    assert np.all(np.abs(yh - enc["y"]) <= bound[:, None] * (1 + 1e-9))
+
+
+def test_minmax_uniform_data_mse_is_step_squared_over_12():
+    # i.i.d. U(-1, 1) rotated coordinates: a uniform quantiser's error is
+    # uniform on half a step, mean square scale^2 / 12 (exact parameters)
+    rng = np.random.default_rng(21)
+    y = rng.uniform(-1, 1, size=(4000, 128))
+    x = y @ O.rotation_matrix(3, 128)
+    enc = O.minmax_encode(x, 3, 4)
+    err = enc["codes"] * enc["scale"][:, None] + enc["zero"][:, None] - enc["y"]
+    ratio = np.mean(err ** 2) / np.mean(enc["scale"] ** 2 / 12)
+    assert abs(ratio - 1) < 0.02, ratio
+
+
+def test_minmax_zero_vector():
+    enc = O.minmax_encode(np.zeros((2, 128)), 42, 3)
+    assert np.all(enc["codes"] == 0) and np.all(enc["scale16"] == 0) and np.all(enc["zero16"] == 0)
+    assert np.all(O.minmax_decode(enc["codes"], enc["scale16"], enc["zero16"], 42) == 0)
+
+
+def test_minmax_against_lloyd_max_on_gaussian_vectors():
+    # The comparison the codec is built for.  Lloyd-Max is MSE-optimal for the
+    # coordinate marginal (and spends 16 bits per vector on the norm, against
+    # 32 for scale + zero point), so at every bit width its relative error on
+    # N(0, I) vectors must be the lower one.
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((3000, 128))
+    for bits in (2, 3, 4):
+        c32, _ = O.codebook_fp32(128, bits)
+        e = O.encode(x, 42, c32)
+        xl = O.reconstruct(e["idx"], e["gamma16"], 42, c32)
+        m = O.minmax_encode(x, 42, bits)
+        xm = O.minmax_decode(m["codes"], m["scale16"], m["zero16"], 42)
+        n2 = np.sum(x * x, axis=1)
+        mse_l = np.mean(np.sum((x - xl) ** 2, axis=1) / n2)
+        mse_m = np.mean(np.sum((x - xm) ** 2, axis=1) / n2)
+        assert mse_l < mse_m, (bits, mse_l, mse_m)
