@@ -264,6 +264,37 @@ def main():
             torch.cuda.synchronize()
             acc.extend(e[0].elapsed_time(e[1]) for e in ev)
 
+    # ---- the min/max comparison codec on the same keys and values
+    mm_enc_ms, mm_dec_ms = [], []
+    if args.only == "both" and not args.no_extras:
+        mrot = tq.tq_make_rotation(w.rot_seed, 128)
+        nv = w.tokens * w.num_kv_heads
+        mcodes = [torch.empty((nv, 16 * w.bits_k), dtype=torch.uint8, device=dev) for _ in range(2)]
+        mparams = [torch.empty((nv, 2), dtype=torch.int16, device=dev) for _ in range(2)]
+        mout = torch.empty((nv, 128), dtype=torch.bfloat16, device=dev)
+        reps = max(5, args.steps // 4)
+
+        def mm_enc(i):
+            s = sets[i % nsets]
+            tq.tq_minmax_encode(s["K"].view(-1, 128), w.bits_k, mrot, mcodes[0], mparams[0], stream)
+            tq.tq_minmax_encode(s["V"].view(-1, 128), w.bits_k, mrot, mcodes[1], mparams[1], stream)
+
+        def mm_dec(i):
+            for j in range(2):
+                tq.tq_minmax_decode(mcodes[j], mparams[j], w.bits_k, mrot, mout, stream)
+
+        for fn, acc in ((mm_enc, mm_enc_ms), (mm_dec, mm_dec_ms)):
+            for i in range(3):
+                fn(i)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+            for i in range(reps):
+                ev[i][0].record(stream)
+                fn(i + 3)
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            acc.extend(e[0].elapsed_time(e[1]) for e in ev)
+        del mcodes, mparams, mout
+
     kernels = {
         "tq_encode": {"bound": "hbm", "achieved": round(enc_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                       "frac": round(enc_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": enc_bytes,
@@ -289,6 +320,21 @@ def main():
             "unfused_us": round(un_s * 1e6, 2),
             "note": "append each sequence's new token + decode-attend in one call; unfused_us = tq_encode_kv of "
                     "the new tokens + tq_decode_attend; not part of the timed step"}
+    if mm_enc_ms:
+        mb = nvec * (in_b + 128 * w.bits_k // 8 + 4)            # bf16 in, codes + fp16 scale and zero out
+        me_s = float(np.mean(mm_enc_ms)) / 1e3
+        kernels["tq_minmax_encode"] = {
+            "bound": "hbm", "achieved": round(mb / me_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(mb / me_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": mb,
+            "us_per_launch": round(me_s * 1e6, 2), "vectors_per_s": round(nvec / me_s, 1),
+            "note": "min/max comparison codec, every key and value (two launches); not part of the timed step"}
+        db = nvec * (128 * w.bits_k // 8 + 4 + 256)
+        md_s = float(np.mean(mm_dec_ms)) / 1e3
+        kernels["tq_minmax_decode"] = {
+            "bound": "hbm", "achieved": round(db / md_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(db / md_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": db,
+            "us_per_launch": round(md_s * 1e6, 2),
+            "note": "min/max comparison codec back to bf16, every key and value (two launches)"}
     dom = "tq_encode" if enc_s >= dec_s else "tq_decode_attend"
     traffic = None
     tf = os.path.join(ROOT, "profiles", "traffic.json")

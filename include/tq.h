@@ -248,6 +248,32 @@ int tq_reconstruct(const tq_cache* cache, const int32_t* slots, int64_t n,
  * Asynchronous on hip_stream.  Errors: TQ_ERR_INVALID_ARG (null cache, n < 0,
  * bad dtype, misaligned output, values asked of a keys-only cache, more than
  * 2^31 vectors), TQ_ERR_NO_DEVICE, TQ_ERR_HIP (launch failure). */
+/* ---------------------------------------------------------------------------
+ * Comparison codec: per-vector min/max uniform quantiser after the same
+ * rotation ([P4] Step 3 compress_value / decompress_value).  y = R x;
+ * lo = min_j y_j; scale = (max_j y_j - lo) / (2^bits - 1);
+ * code_j = round half to even of (y_j - lo) / scale, in [0, 2^bits - 1]
+ * (all codes 0 when scale = 0); scale and lo stored as fp16 (round to
+ * nearest even, saturating at +-65504).  Flat buffers, caller-owned:
+ *   X:      device [n][128] of dtype (TQ_F32 / TQ_F16 / TQ_BF16), 16-byte aligned;
+ *   codes:  device [n][16 * bits] bytes, code j of a vector in bits
+ *           [j*bits, (j+1)*bits) LSB first, 4-byte aligned;
+ *   params: device [n][2] fp16 words (scale, zero point), 4-byte aligned.
+ * bits in {2, 3, 4}; rot: dimension 128.  Asynchronous on hip_stream.
+ * Errors: TQ_ERR_INVALID_ARG (null pointer, bad dtype, misalignment, n < 0,
+ * n >= 2^31), TQ_ERR_UNSUPPORTED (bits, rotation dimension), TQ_ERR_NO_DEVICE,
+ * TQ_ERR_HIP. */
+int tq_minmax_encode(const void* X, int32_t dtype, int64_t n, int32_t bits,
+                     const tq_rotation* rot, void* codes, void* params,
+                     void* hip_stream);
+
+/* Decode of the same buffers: x_hat = R^T (code * scale16 + zero16), in
+ * fp32 then written as out_dtype (TQ_F32, or TQ_F16 / TQ_BF16 rounded to
+ * nearest even); out: device [n][128], 16-byte aligned. */
+int tq_minmax_decode(const void* codes, const void* params, int64_t n,
+                     int32_t bits, const tq_rotation* rot, int32_t out_dtype,
+                     void* out, void* hip_stream);
+
 int tq_decompress_kv(const tq_cache* cache, const int32_t* slots, int64_t n,
                      int32_t out_dtype, void* K_out, void* V_out,
                      void* hip_stream);

@@ -695,6 +695,60 @@ int tq_decompress_kv(const tq_cache* cache, const int32_t* slots, int64_t n, int
   return TQ_OK;
 }
 
+int tq_minmax_encode(const void* X, int32_t dtype, int64_t n, int32_t bits, const tq_rotation* rot, void* codes,
+                     void* params, void* hip_stream) {
+  if (!rot || rot->d != 128) return fail(TQ_ERR_UNSUPPORTED, "the min/max codec needs a rotation of dimension 128");
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n < 0");
+  if (bits < 2 || bits > 4) return fail(TQ_ERR_UNSUPPORTED, "bits must be 2..4");
+  if (dtype != TQ_F32 && dtype != TQ_F16 && dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad dtype");
+  if (n == 0) return TQ_OK;
+  if (!X || !codes || !params) return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  if (reinterpret_cast<uintptr_t>(X) % 16 != 0 || reinterpret_cast<uintptr_t>(codes) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(params) % 4 != 0)
+    return fail(TQ_ERR_INVALID_ARG, "X must be 16-byte aligned, codes and params 4-byte aligned");
+  if (n >= ((int64_t)1 << 31)) return fail(TQ_ERR_INVALID_ARG, "too many vectors");
+  int s = check_device();
+  if (s != TQ_OK) return s;
+  tq::MinmaxArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.src = X;
+  a.codes = static_cast<uint8_t*>(codes);
+  a.params = static_cast<uint16_t*>(params);
+  a.n = n;
+  a.in_dtype = dtype;
+  to_mask(rot->signs, a.rot);
+  int err = tq::launch_minmax_encode(a, bits, hip_stream);
+  if (err != 0) return hip_fail(err, "min/max encode launch");
+  return TQ_OK;
+}
+
+int tq_minmax_decode(const void* codes, const void* params, int64_t n, int32_t bits, const tq_rotation* rot,
+                     int32_t out_dtype, void* out, void* hip_stream) {
+  if (!rot || rot->d != 128) return fail(TQ_ERR_UNSUPPORTED, "the min/max codec needs a rotation of dimension 128");
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n < 0");
+  if (bits < 2 || bits > 4) return fail(TQ_ERR_UNSUPPORTED, "bits must be 2..4");
+  if (out_dtype != TQ_F32 && out_dtype != TQ_F16 && out_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad out_dtype");
+  if (n == 0) return TQ_OK;
+  if (!codes || !params || !out) return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  if (reinterpret_cast<uintptr_t>(out) % 16 != 0 || reinterpret_cast<uintptr_t>(codes) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(params) % 4 != 0)
+    return fail(TQ_ERR_INVALID_ARG, "out must be 16-byte aligned, codes and params 4-byte aligned");
+  if (n >= ((int64_t)1 << 31)) return fail(TQ_ERR_INVALID_ARG, "too many vectors");
+  int s = check_device();
+  if (s != TQ_OK) return s;
+  tq::MinmaxArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.codes = const_cast<uint8_t*>(static_cast<const uint8_t*>(codes));
+  a.params = const_cast<uint16_t*>(static_cast<const uint16_t*>(params));
+  a.out = out;
+  a.n = n;
+  a.out_dtype = out_dtype;
+  to_mask(rot->signs, a.rot);
+  int err = tq::launch_minmax_decode(a, bits, hip_stream);
+  if (err != 0) return hip_fail(err, "min/max decode launch");
+  return TQ_OK;
+}
+
 int tq_reconstruct(const tq_cache* cache, const int32_t* slots, int64_t n, int32_t which,
                    float* out, void* hip_stream) {
   if (!cache) return fail(TQ_ERR_INVALID_ARG, "null cache");

@@ -152,6 +152,18 @@ struct DecompArgs {
   DecompStream stream[2];   // keys, values
 };
 
+// Min/max comparison codec on flat buffers: per vector, d*b/8 bytes of codes
+// (LSB first) and two fp16 words (scale, zero point).
+struct MinmaxArgs {
+  const void* src;          // encode: [n][128] of in_dtype
+  uint8_t* codes;           // [n][16 * bits]
+  uint16_t* params;         // [n][2]: fp16 scale, fp16 zero point
+  void* out;                // decode: [n][128] of out_dtype
+  int64_t n;
+  int32_t in_dtype, out_dtype;   // 0 fp32, 1 fp16, 2 bf16
+  SignMask rot;
+};
+
 // Launchers implemented in the .hip files; return a hipError_t value.
 int launch_encode(const EncodeArgs& a, int num_streams, int in_dtype, void* stream);
 int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int attend, int mfma, void* stream);
@@ -161,5 +173,7 @@ int launch_merge(const DecodeArgs& a, void* stream);
 int launch_decode_step(const DecodeArgs& a, const AppendArgs& ap, int bits, void* stream);
 int launch_reconstruct(const ReconArgs& a, void* stream);
 int launch_decompress(const DecompArgs& a, void* stream);
+int launch_minmax_encode(const MinmaxArgs& a, int bits, void* stream);
+int launch_minmax_decode(const MinmaxArgs& a, int bits, void* stream);
 
 }  // namespace tq

@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.c_int32, ctypes.c_float, _P, _P]),
             "tq_reconstruct": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
             "tq_decompress_kv": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
+            "tq_minmax_encode": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]),
+            "tq_minmax_decode": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, ctypes.c_int32, _P, _P]),
             "tq_decode_step": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P, _P, _P, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P,
                                               ctypes.c_int64, _P]),
@@ -258,6 +260,19 @@ def tq_decode_step(q, K_new, V_new, cache: Cache, block_tables, seq_lens, out, w
                                 _ptr(block_tables), _ptr(seq_lens), ns, hq, block_tables.shape[1], scale, _ptr(out),
                                 _ptr(logits_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _stream(stream)), "tq_decode_step")
+
+
+def tq_minmax_encode(X, bits: int, rot, codes, params, stream=None):
+    """X: device [n][128] (f32/f16/bf16); codes: uint8 [n][16*bits]; params:
+    [n][2] 16-bit words (fp16 scale, fp16 zero point)."""
+    _check(lib().tq_minmax_encode(_ptr(X), _dtype_code(X), X.shape[0], bits, rot.handle, _ptr(codes),
+                                  _ptr(params), _stream(stream)), "tq_minmax_encode")
+
+
+def tq_minmax_decode(codes, params, bits: int, rot, out, stream=None):
+    """out: device [n][128] of f32/f16/bf16."""
+    _check(lib().tq_minmax_decode(_ptr(codes), _ptr(params), codes.shape[0], bits, rot.handle,
+                                  _dtype_code(out), _ptr(out), _stream(stream)), "tq_minmax_decode")
 
 
 def tq_decompress_kv(cache: Cache, slots, K_out, V_out=None, stream=None):

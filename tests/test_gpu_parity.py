@@ -461,6 +461,57 @@ def test_decompress_one_stream_and_keys_only_cache(device):
                         c32, "f16")
 
 
+# ------------------------------------------------------ min/max comparison --
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_minmax_codec_matches_oracle(device, bits, dt):
+    """Codes, fp16 parameters and decode of the min/max codec against the
+    oracle.  1000 outlier-channel keys (a ragged tail of 16-vector groups)
+    and one zero vector.  Codes: equal except where the oracle's (y - lo) /
+    scale lies within 1e-4 of a rounding tie (the decision is taken in fp32),
+    then on the adjacent code.  Parameters: equal fp16 words for all but a
+    few vectors, never more than one ulp apart (fp32 vs float64 extremes)."""
+    w = W.DECODE_32K.with_(seq_len=125, num_kv_heads=8) if dt == "bf16" else W.TINY
+    kb, k64 = W.keys(w)
+    n = 1000
+    kb = np.ascontiguousarray(kb.reshape(-1, 128)[:n])
+    x64 = k64.reshape(-1, 128)[:n].copy()
+    kb[7] = 0
+    x64[7] = 0.0
+    X = to_device(kb, dt, device)
+    rot = tq.tq_make_rotation(42, 128)
+    codes = torch.zeros((n, 16 * bits), dtype=torch.uint8, device=device)
+    params = torch.zeros((n, 2), dtype=torch.int16, device=device)
+    tq.tq_minmax_encode(X, bits, rot, codes, params)
+    torch.cuda.synchronize()
+    enc = O.minmax_encode(x64, 42, bits)
+    cb = codes.cpu().numpy()
+    got = np.stack([O.unpack_codes(cb[i].tobytes(), bits, 128) for i in range(n)])
+    bad = got != enc["codes"]
+    if bad.any():
+        u = enc["u"][bad]
+        assert np.all(np.abs(got[bad] - enc["codes"][bad]) == 1)
+        assert np.all(np.abs(u - np.floor(u) - 0.5) < 1e-4), "code mismatch away from a rounding tie"
+    assert bad.sum() <= max(3, 1e-4 * bad.size)
+    pw = params.cpu().numpy().view(np.uint16)
+    for col, ref in ((0, enc["scale16"]), (1, enc["zero16"])):
+        gb, ob = pw[:, col].astype(np.int64), ref.view(np.uint16).astype(np.int64)
+        assert np.all(np.abs(gb - ob) <= 1) and np.sum(gb != ob) <= 5, (col, int(np.sum(gb != ob)))
+    assert np.all(got[7] == 0) and pw[7, 0] == 0 and pw[7, 1] == 0
+    # decode from the GPU's own codes and parameters
+    s16, z16 = pw[:, 0].view(np.float16), pw[:, 1].view(np.float16)
+    want = O.minmax_decode(got, s16, z16, 42)
+    out = torch.full((n, 128), float("nan"), device=device)
+    tq.tq_minmax_decode(codes, params, bits, rot, out)
+    scale = np.abs(s16.astype(np.float64)) * (1 << bits) + np.abs(z16.astype(np.float64))
+    assert np.all(np.abs(out.cpu().numpy().astype(np.float64) - want) <= 1e-5 * scale[:, None] + 1e-30)
+    ob16 = torch.full((n, 128), float("nan"), dtype=torch.bfloat16, device=device)
+    tq.tq_minmax_decode(codes, params, bits, rot, ob16)
+    g16 = ob16.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(g16 - want) <= 2.0 ** -8 * np.abs(want) + 1e-5 * scale[:, None] + 2.0 ** -24)
+
+
 # -------------------------------------------------------- tiny end to end --
 
 def test_tiny_config_end_to_end(device):

@@ -246,3 +246,22 @@ def test_decode_step_argument_checks_happen_before_the_device():
     r, r2 = tq.tq_make_rotation(42, 128), tq.tq_make_rotation(43, 128)
     qc = tq.tq_cache_create(tq.make_config(8, 4, 4, 4, r, True, r2), 0x100000)
     assert step(qc.handle) == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_minmax_argument_checks_happen_before_the_device():
+    L = tq.lib()
+    r = tq.tq_make_rotation(42, 128)
+    r64 = tq.tq_make_rotation(42, 64)
+    X, cd, pr, out = 0x200000, 0x300000, 0x400000, 0x500000
+    assert L.tq_minmax_encode(X, tq.TQ_BF16, 10, 4, None, cd, pr, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_minmax_encode(X, tq.TQ_BF16, 10, 4, r64.handle, cd, pr, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_minmax_encode(X, tq.TQ_BF16, 10, 5, r.handle, cd, pr, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_minmax_encode(X, 9, 10, 4, r.handle, cd, pr, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_minmax_encode(X, tq.TQ_BF16, -1, 4, r.handle, cd, pr, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_minmax_encode(X + 8, tq.TQ_BF16, 10, 4, r.handle, cd, pr, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_minmax_encode(X, tq.TQ_BF16, 10, 4, r.handle, None, pr, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_minmax_encode(X, tq.TQ_BF16, 0, 4, r.handle, cd, pr, None) == tq.TQ_OK      # nothing to do
+    assert L.tq_minmax_decode(cd, pr, 10, 3, r.handle, 9, out, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_minmax_decode(cd, pr + 2, 10, 3, r.handle, tq.TQ_F32, out, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_minmax_decode(cd, pr, 10, 1, r.handle, tq.TQ_F32, out, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_minmax_decode(cd, pr, 0, 3, r.handle, tq.TQ_F32, out, None) == tq.TQ_OK
