@@ -7,8 +7,7 @@
 // Lloyd-Max codec (per-coordinate codebook and fp16 norm).
 //
 // One vector per 16-lane row, 8 coordinates per lane, the in-register
-// 16-lane FWHT of the encoder.  The code decision uses IEEE fp32 division,
-// as the page's arithmetic does.
+// 16-lane FWHT of the encoder.  The code decision is taken in fp32.
 
 #include <hip/hip_bf16.h>
 
@@ -63,10 +62,14 @@ __global__ __launch_bounds__(256) void minmax_encode_kernel(const MinmaxArgs a) 
   hi = row_max(hi);
   constexpr int kLevels = (1 << BITS) - 1;
   const float scale = (hi - lo) / (float)kLevels;
+  // (y - lo) / scale as a product with the hardware reciprocal (1 ulp): it
+  // differs from the page's division only within a few ulps of a rounding
+  // tie, and the row's 8 divisions were most of the kernel's vector work
+  const float inv = scale > 0.f ? __builtin_amdgcn_rcpf(scale) : 0.f;
   uint32_t code[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float u = scale > 0.f ? (x[e] - lo) / scale : 0.f;
+    const float u = (x[e] - lo) * inv;
     code[e] = (uint32_t)fminf(fmaxf(rintf(u), 0.f), (float)kLevels);
   }
   bool store_lane;

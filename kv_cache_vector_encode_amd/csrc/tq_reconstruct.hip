@@ -64,7 +64,7 @@ int launch_reconstruct(const ReconArgs& a, void* stream) {
 // values in one launch (blockIdx.y picks the stream), written as 16-bit
 // floats (round to nearest even) for attention over a compressed prefix.
 // Every output vector is one 256-byte store per 16-lane row (16 bytes per
-// lane); a workgroup takes VPR vectors per row, all loads issued first.
+// lane); a workgroup takes kDecompVpr vectors per row, all loads issued first.
 // Per vector it reads d*b/8 + 2 bytes and writes 256.
 // ---------------------------------------------------------------------------
 template <int OUT>
@@ -77,9 +77,7 @@ __device__ __forceinline__ uint32_t pack16(float lo, float hi) {
   }
 }
 
-constexpr int kDecompVpr = 4;   // vectors per 16-lane row
-
-template <int BITS, int OUT>
+template <int BITS, int OUT, int kDecompVpr>
 __global__ __launch_bounds__(256) void decompress_kernel(const DecompArgs a) {
   const DecompStream& st = a.stream[blockIdx.y];
   __shared__ float s_cent[16];
@@ -131,15 +129,25 @@ __global__ __launch_bounds__(256) void decompress_kernel(const DecompArgs a) {
   }
 }
 
+// Vectors per 16-lane row: 4 below 2^20 vectors per stream, 8 from there
+// (measured on keys and values of 2^18 vectors each: 46 us at 4 against 50
+// at 8; of 2^20 each: 180 us at 4 against 170 at 8).
+template <int BITS, int VPR>
+static void launch_decomp_vpr(const DecompArgs& a, dim3 grid, hipStream_t s) {
+  if (a.out_dtype == 2) hipLaunchKernelGGL((decompress_kernel<BITS, 2, VPR>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((decompress_kernel<BITS, 1, VPR>), grid, dim3(256), 0, s, a);
+}
+
 template <int BITS>
-static void launch_decomp_bits(const DecompArgs& a, dim3 grid, hipStream_t s) {
-  if (a.out_dtype == 2) hipLaunchKernelGGL((decompress_kernel<BITS, 2>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((decompress_kernel<BITS, 1>), grid, dim3(256), 0, s, a);
+static void launch_decomp_bits(const DecompArgs& a, dim3 grid, int vpr, hipStream_t s) {
+  if (vpr == 8) launch_decomp_vpr<BITS, 8>(a, grid, s);
+  else launch_decomp_vpr<BITS, 4>(a, grid, s);
 }
 
 int launch_decompress(const DecompArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t groups = (a.n_vectors + 16 * kDecompVpr - 1) / (16 * kDecompVpr);
+  const int vpr = a.n_vectors >= ((int64_t)1 << 20) ? 8 : 4;
+  const int64_t groups = (a.n_vectors + 16 * vpr - 1) / (16 * vpr);
   if (groups > 0x7FFFFFFF || a.n_vectors >= ((int64_t)1 << 31)) return (int)hipErrorInvalidValue;
   // one launch per distinct bit width (keys and values share one when equal)
   DecompArgs b = a;
@@ -153,9 +161,9 @@ int launch_decompress(const DecompArgs& a, void* stream) {
     if (!same) c.stream[0] = b.stream[part];
     const dim3 grid((unsigned)groups, (unsigned)(same ? streams : 1));
     switch (c.stream[0].bits) {
-      case 2: launch_decomp_bits<2>(c, grid, s); break;
-      case 3: launch_decomp_bits<3>(c, grid, s); break;
-      case 4: launch_decomp_bits<4>(c, grid, s); break;
+      case 2: launch_decomp_bits<2>(c, grid, vpr, s); break;
+      case 3: launch_decomp_bits<3>(c, grid, vpr, s); break;
+      case 4: launch_decomp_bits<4>(c, grid, vpr, s); break;
       default: return (int)hipErrorInvalidValue;
     }
     const hipError_t e = hipGetLastError();
