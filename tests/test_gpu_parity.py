@@ -540,3 +540,41 @@ def test_tiny_config_end_to_end(device):
     err = np.abs(logits.cpu().numpy()[0, 0].astype(np.float64) - s)
     assert np.all(err[ok] <= LOGIT_RTOL * scl[ok])
     _say(f"tiny e2e: {nmis} band code mismatches, worst logit {(err / scl).max():.2e}")
+
+
+def test_encode_step_and_decompress_are_deterministic(device):
+    """Repeated calls on the same inputs give identical bytes: the encode's
+    pool, the decode step's appended rows and output, and decompression
+    (fixed reduction orders, no atomics)."""
+    w = W.DECODE_32K.with_(seq_len=600, num_kv_heads=2, num_q_heads=16)
+    kb, _ = W.keys(w)
+    vb, _ = W.values(w)
+    K, V = to_device(kb, "bf16", device), to_device(vb, "bf16", device)
+    slots = torch.from_numpy(W.slot_mapping(w)).to(device)
+    pools = []
+    for _ in range(2):
+        cache = make_cache(w, device)
+        tq.tq_encode_kv(K, V, slots, w.bits_k, cache)
+        pools.append(cache)
+    torch.cuda.synchronize()
+    assert torch.equal(pools[0].pool, pools[1].pool)
+    bt = torch.from_numpy(W.block_tables(w)).to(device)
+    lens = torch.tensor([600], dtype=torch.int32, device=device)
+    q = to_device(W.queries(w)[0], "bf16", device)
+    Kn, Vn = K[599:600].contiguous(), V[599:600].contiguous()
+    outs = []
+    for cache in pools:
+        out = torch.empty((1, 16, 128), device=device)
+        ws = tq.new_workspace(cache, 1, 16, bt.shape[1], device=device)
+        tq.tq_decode_step(q, Kn, Vn, cache, bt, lens, out, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(pools[0].pool, pools[1].pool)
+    dq = []
+    for cache in pools:
+        Ko = torch.empty((600, 2, 128), dtype=torch.bfloat16, device=device)
+        Vo = torch.empty_like(Ko)
+        tq.tq_decompress_kv(cache, slots, Ko, Vo)
+        dq.append((Ko, Vo))
+    torch.cuda.synchronize()
+    assert torch.equal(dq[0][0], dq[1][0]) and torch.equal(dq[0][1], dq[1][1])
