@@ -295,6 +295,36 @@ def main():
             acc.extend(e[0].elapsed_time(e[1]) for e in ev)
         del mcodes, mparams, mout
 
+    # ---- on-box ceilings: a plain stream read (the library's measurement
+    # aid) and a device copy, each over 2 GiB
+    onbox = None
+    if args.only == "both" and not args.no_extras:
+        buf = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+        buf2 = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            tq.tq_stream_read(buf, sink, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            tq.tq_stream_read(buf, sink, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        read_gbps = 10 * buf.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
+        src = buf[: 1 << 30]
+        for _ in range(3):
+            buf2.copy_(src)
+        e0.record(stream)
+        for _ in range(10):
+            buf2.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 10 * 2 * buf2.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
+        del buf, buf2, src
+        onbox = {"read_gbps": round(read_gbps, 1), "copy_gbps": round(copy_gbps, 1),
+                 "read_kernel": "tq_stream_read, 2 GiB, non-temporal 16-byte loads",
+                 "copy_kernel": "torch copy_, 1 GiB (read + write counted)"}
+
     kernels = {
         "tq_encode": {"bound": "hbm", "achieved": round(enc_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                       "frac": round(enc_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": enc_bytes,
@@ -375,6 +405,10 @@ def main():
         "roofline": roof,
         "wall_s_timed": round(t_wall, 4),
     }
+    if onbox:
+        onbox["decode_frac_of_read"] = round(dec_gbps / onbox["read_gbps"], 4)
+        onbox["encode_frac_of_copy"] = round(enc_gbps / onbox["copy_gbps"], 4)
+        res["onbox_ceiling"] = onbox
     if args.only != "both":
         res["only"] = args.only
     if not args.no_cpu_baseline:

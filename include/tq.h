@@ -278,6 +278,15 @@ int tq_decompress_kv(const tq_cache* cache, const int32_t* slots, int64_t n,
                      int32_t out_dtype, void* K_out, void* V_out,
                      void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement aid (not part of the codec): read `bytes` of device memory at
+ * `src` as a plain stream (grid-stride 16-byte non-temporal loads) and write
+ * one folded word to `sink` (device, 4 bytes).  Timing it gives the on-box
+ * read ceiling that the read-dominated decode is compared with, beside the
+ * vendor's 8 TB/s.  src 16-byte aligned; bytes is rounded down to a multiple
+ * of 32 KiB (less than that: nothing is read).  Asynchronous on hip_stream. */
+int tq_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

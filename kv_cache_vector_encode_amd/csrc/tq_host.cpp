@@ -749,6 +749,18 @@ int tq_minmax_decode(const void* codes, const void* params, int64_t n, int32_t b
   return TQ_OK;
 }
 
+int tq_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* hip_stream) {
+  if (bytes < 0) return fail(TQ_ERR_INVALID_ARG, "bytes < 0");
+  if (bytes < 16 * 256 * 8) return TQ_OK;   // less than one thread-group's pass: nothing to time
+  if (!src || !sink) return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0) return fail(TQ_ERR_INVALID_ARG, "src must be 16-byte aligned");
+  int s = check_device();
+  if (s != TQ_OK) return s;
+  int err = tq::launch_stream_read(src, bytes, sink, hip_stream);
+  if (err != 0) return hip_fail(err, "stream read launch");
+  return TQ_OK;
+}
+
 int tq_reconstruct(const tq_cache* cache, const int32_t* slots, int64_t n, int32_t which,
                    float* out, void* hip_stream) {
   if (!cache) return fail(TQ_ERR_INVALID_ARG, "null cache");

@@ -175,5 +175,6 @@ int launch_reconstruct(const ReconArgs& a, void* stream);
 int launch_decompress(const DecompArgs& a, void* stream);
 int launch_minmax_encode(const MinmaxArgs& a, int bits, void* stream);
 int launch_minmax_decode(const MinmaxArgs& a, int bits, void* stream);
+int launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 
 }  // namespace tq

@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "tq_reconstruct": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
             "tq_decompress_kv": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
             "tq_minmax_encode": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]),
+            "tq_stream_read": (ctypes.c_int, [_P, ctypes.c_int64, _P, _P]),
             "tq_minmax_decode": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, ctypes.c_int32, _P, _P]),
             "tq_decode_step": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P, _P, _P, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P,
@@ -273,6 +274,12 @@ def tq_minmax_decode(codes, params, bits: int, rot, out, stream=None):
     """out: device [n][128] of f32/f16/bf16."""
     _check(lib().tq_minmax_decode(_ptr(codes), _ptr(params), codes.shape[0], bits, rot.handle,
                                   _dtype_code(out), _ptr(out), _stream(stream)), "tq_minmax_decode")
+
+
+def tq_stream_read(src, sink, stream=None):
+    """Measurement aid: stream-read the device tensor src (its whole storage)."""
+    _check(lib().tq_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)),
+           "tq_stream_read")
 
 
 def tq_decompress_kv(cache: Cache, slots, K_out, V_out=None, stream=None):

@@ -33,6 +33,7 @@ int launch_decompress(const DecompArgs&, void*) { unreachable("decompress"); }
 int launch_reconstruct(const ReconArgs&, void*) { unreachable("reconstruct"); }
 int launch_minmax_encode(const MinmaxArgs&, int, void*) { unreachable("minmax encode"); }
 int launch_minmax_decode(const MinmaxArgs&, int, void*) { unreachable("minmax decode"); }
+int launch_stream_read(const void*, int64_t, uint32_t*, void*) { unreachable("stream read"); }
 int decode_slices(int group) { return (group + 7) / 8; }
 }  // namespace tq
 
@@ -123,6 +124,10 @@ int main() {
   CHECK(tq_minmax_encode(p, TQ_BF16, 7, 3, r, w, w, nullptr) == TQ_ERR_NO_DEVICE);
   CHECK(tq_minmax_decode(p, p, 7, 3, r, TQ_F32, w, nullptr) == TQ_ERR_NO_DEVICE);
   CHECK(tq_minmax_encode(p, TQ_BF16, 7, 5, r, w, w, nullptr) == TQ_ERR_UNSUPPORTED);
+  uint32_t* sink = reinterpret_cast<uint32_t*>(uintptr_t(0x600000));
+  CHECK(tq_stream_read(p, int64_t(1) << 30, sink, nullptr) == TQ_ERR_NO_DEVICE);
+  CHECK(tq_stream_read(p, -1, sink, nullptr) == TQ_ERR_INVALID_ARG);
+  CHECK(tq_stream_read(p, 100, sink, nullptr) == TQ_OK);
   for (tq_cache* cache : caches) tq_cache_destroy(cache);
   tq_rotation_destroy(r);
   std::printf("host sanitize driver: ok\n");

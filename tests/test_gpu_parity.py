@@ -578,3 +578,22 @@ def test_encode_step_and_decompress_are_deterministic(device):
         dq.append((Ko, Vo))
     torch.cuda.synchronize()
     assert torch.equal(dq[0][0], dq[1][0]) and torch.equal(dq[0][1], dq[1][1])
+
+
+def test_stream_read_folds_its_loads(device):
+    """The measurement aid reads what it is given: the word it leaves is the
+    xor of the 16-byte words its last thread group's first thread loads
+    (grid 8192 x 256, eight loads 256 words apart per pass)."""
+    n16 = 1 << 25                                        # 512 MiB
+    words = torch.arange(n16 * 4, dtype=torch.int32, device=device)
+    sink = torch.zeros(4, dtype=torch.int32, device=device)
+    tq.tq_stream_read(words, sink)
+    torch.cuda.synchronize()
+    i, stride, acc = 8191 * 256 * 8, 8192 * 256 * 8, 0
+    host = words.view(-1, 4)
+    while i + 256 * 7 < n16:
+        for u in range(8):
+            w = host[i + 256 * u].cpu().numpy().astype(np.uint32)
+            acc ^= int(w[0] ^ w[1] ^ w[2] ^ w[3])
+        i += stride
+    assert int(sink[0].cpu().numpy().astype(np.uint32)) == acc
