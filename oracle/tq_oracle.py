@@ -30,7 +30,14 @@ with its reason, in the design notes of the repository):
   * fp16 round-to-nearest-even norm, saturating at 65504;
   * QJL residual taken in the rotated unit-direction frame with estimator
     constant sqrt(pi/2)/sqrt(d) and an independent sign-Hadamard R';
-  * logit scale 1/sqrt(d); query head h reads KV head h // (Hq / Hkv).
+  * logit scale 1/sqrt(d); query head h reads KV head h // (Hq / Hkv);
+  * triplet codec: the last of ceil(d/3) triplets padded with zeros; the
+    octahedral map is the equal-area one (the glossary calls it equal-area),
+    so C_xi is the uniform quantiser; rho takes Lloyd-Max for its exact
+    marginal; B_tri = 2 b_dir + b_nrm with (b_dir, b_nrm) = (b+1, b-1); the
+    3x3 joint rounding scans the nearest cell and its neighbours in xi and
+    eta and, per candidate direction, the norm code nearest the projection;
+    a zero triplet takes the direction (0, 0, 1).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against
 values the pages print, closed forms, textbook limits or brute force.
@@ -51,7 +58,12 @@ __all__ = [
     "reconstruct", "qjl_encode", "qjl_dot_estimate", "logits",
     "attention", "bits_per_vector", "LayoutV1", "pack_codes",
     "unpack_codes", "pack_signs", "unpack_signs", "write_cache",
-    "read_cache", "unpack_pool", "SQRT_HALF_PI",
+    "read_cache", "unpack_pool", "SQRT_HALF_PI", "fp16_sat",
+    "minmax_encode", "minmax_decode", "octo_bits", "octo_triplets",
+    "oct_map", "oct_unmap", "octo_dir_codebook", "rho_cdf",
+    "rho_partial_mean", "rho_lloyd_max", "octo_codebooks", "octo_encode",
+    "octo_encode_triplets", "octo_triplet_error", "octo_decode",
+    "octo_record_bytes", "octo_pack", "octo_unpack",
 ]
 
 _MASK64 = (1 << 64) - 1
@@ -527,3 +539,237 @@ def unpack_pool(pool, lay: LayoutV1, blocks=None) -> dict:
         raw = arr[:, :, lay.off_sig:lay.off_sig + B * d // 8].reshape(arr.shape[0], lay.hkv, B, d // 8)
         out["qjl_bits"] = np.unpackbits(raw, axis=-1, bitorder="little").astype(np.int64)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Triplet codec ([P3] "Octahedral triplet direction quantizer with norm
+# marginals" and the Method list, steps 1-7): the rotated unit direction is
+# cut into ceil(d/3) triplets t_i (the last padded with zeros); each triplet
+# is rho_i = ||t_i|| times a unit direction n_i; n_i goes through an
+# equal-area octahedral map to (xi, eta) in [-1, 1]^2 ([P3] glossary
+# "octahedral map"); xi and eta take b_dir-bit codebooks, rho takes a
+# b_nrm-bit codebook, with (b_dir, b_nrm) = (b + 1, b - 1) ([P3] "MSE-optimal
+# non-uniform bit allocation": B_tri = 2 b_dir + b_nrm); a 3x3 joint rounding
+# picks the final codes; the state is (gamma, I_dir, I_nrm).
+# ---------------------------------------------------------------------------
+
+def octo_bits(b: int) -> tuple[int, int]:
+    """(b_dir, b_nrm) = (b + 1, b - 1) for a budget of b bits per coordinate."""
+    if b < 2:
+        raise ValueError("the triplet codec needs b >= 2 (b_nrm = b - 1 >= 1)")
+    return b + 1, b - 1
+
+
+def octo_triplets(d: int) -> int:
+    """n_tri = ceil(d / 3)."""
+    return -(-d // 3)
+
+
+def oct_map(n):
+    """Equal-area octahedral map of unit vectors n (..., 3) to (xi, eta).
+
+    Upper hemisphere (z >= 0): L1 radius r = sqrt(1 - z) (the cap z' >= z has
+    area 2 pi (1 - z), the diamond |xi| + |eta| <= r has area 2 r^2, ratio pi
+    everywhere); along the diamond edge the azimuth phi = atan2(|y|, |x|) in
+    [0, pi/2] moves linearly: |eta| = r * phi / (pi/2), |xi| = r - |eta|,
+    signs of x and y.  Lower hemisphere: the same point reflected across the
+    diamond edge, (|xi|, |eta|) -> (1 - |eta|, 1 - |xi|), which preserves area.
+    """
+    n = np.asarray(n, dtype=np.float64)
+    x, y, z = n[..., 0], n[..., 1], n[..., 2]
+    r = np.sqrt(np.maximum(1.0 - np.abs(z), 0.0))
+    phi = np.arctan2(np.abs(y), np.abs(x))
+    ae = r * phi / (np.pi / 2.0)
+    ax = r - ae
+    lower = z < 0
+    ax, ae = np.where(lower, 1.0 - ae, ax), np.where(lower, 1.0 - ax, ae)
+    sx = np.where(x < 0, -1.0, 1.0)
+    sy = np.where(y < 0, -1.0, 1.0)
+    return sx * ax, sy * ae
+
+
+def oct_unmap(xi, eta):
+    """Inverse of oct_map: (xi, eta) in [-1, 1]^2 to unit vectors (..., 3)."""
+    xi = np.asarray(xi, dtype=np.float64)
+    eta = np.asarray(eta, dtype=np.float64)
+    ax, ae = np.abs(xi), np.abs(eta)
+    lower = ax + ae > 1.0
+    ax, ae = np.where(lower, 1.0 - ae, ax), np.where(lower, 1.0 - ax, ae)
+    r = ax + ae
+    z = 1.0 - r * r
+    phi = np.where(r > 0, (np.pi / 2.0) * ae / np.where(r > 0, r, 1.0), 0.0)
+    s = r * np.sqrt(np.maximum(2.0 - r * r, 0.0))          # sqrt(1 - z^2)
+    x = np.where(xi < 0, -1.0, 1.0) * s * np.cos(phi)
+    y = np.where(eta < 0, -1.0, 1.0) * s * np.sin(phi)
+    return np.stack([x, y, np.where(lower, -z, z)], axis=-1)
+
+
+def octo_dir_codebook(b_dir: int) -> np.ndarray:
+    """Codebook C_xi of xi and eta.  For a uniformly random unit vector in
+    R^d every triplet direction is uniform on S^2 (the triplet's law is
+    invariant under rotations of R^3), so through an equal-area map xi and eta
+    are uniform on [-1, 1]; the Lloyd-Max quantiser of the uniform density is
+    the uniform one: c_j = -1 + (2j + 1) / 2^b_dir."""
+    n = 1 << b_dir
+    return -1.0 + (2.0 * np.arange(n) + 1.0) / n
+
+
+def rho_cdf(r, d: int):
+    """P(rho <= r) for the norm of one triplet of a uniformly random unit
+    vector in R^d: rho^2 ~ Beta(3/2, (d - 3)/2)."""
+    r = np.clip(np.asarray(r, dtype=np.float64), 0.0, 1.0)
+    return special.betainc(1.5, (d - 3) / 2.0, r * r)
+
+
+def rho_partial_mean(a, b, d: int):
+    """Integral of r f_rho(r) over [a, b] = E[X^(1/2); a^2 <= X <= b^2] for
+    X ~ Beta(3/2, beta): B(2, beta) / B(3/2, beta) * (I_{b^2}(2, beta) -
+    I_{a^2}(2, beta)), beta = (d - 3)/2."""
+    a = np.clip(np.asarray(a, dtype=np.float64), 0.0, 1.0)
+    b = np.clip(np.asarray(b, dtype=np.float64), 0.0, 1.0)
+    be = (d - 3) / 2.0
+    ratio = math.exp(special.betaln(2.0, be) - special.betaln(1.5, be))
+    return ratio * (special.betainc(2.0, be, b * b) - special.betainc(2.0, be, a * a))
+
+
+def rho_lloyd_max(d: int, bits: int, tol: float = 1e-14, max_iter: int = 200000):
+    """Float64 Lloyd-Max quantiser of rho with 2^bits levels: thresholds at
+    midpoints, centroids at cell conditional means, from quantile start."""
+    n = 1 << bits
+    q = (np.arange(n) + 0.5) / n
+    c = np.sqrt(special.betaincinv(1.5, (d - 3) / 2.0, q))
+    for _ in range(max_iter):
+        t = 0.5 * (c[:-1] + c[1:])
+        lo = np.concatenate(([0.0], t))
+        hi = np.concatenate((t, [1.0]))
+        new = rho_partial_mean(lo, hi, d) / (rho_cdf(hi, d) - rho_cdf(lo, d))
+        moved = np.max(np.abs(new - c))
+        c = new
+        if moved < tol * np.max(c):
+            break
+    else:
+        raise RuntimeError("Lloyd-Max did not converge")
+    return c, 0.5 * (c[:-1] + c[1:])
+
+
+def octo_codebooks(d: int, b: int):
+    """Tables as stored (fp32 values held in float64):
+    dirs[a, c] = fp32(oct_unmap(C_xi[a], C_xi[c])), shape (2^b_dir, 2^b_dir, 3);
+    crho = fp32(Lloyd-Max centroids of rho)."""
+    b_dir, b_nrm = octo_bits(b)
+    cx = octo_dir_codebook(b_dir)
+    dirs = oct_unmap(cx[:, None], cx[None, :]).astype(np.float32).astype(np.float64)
+    c, _ = rho_lloyd_max(d, b_nrm)
+    return dirs, c.astype(np.float32).astype(np.float64)
+
+
+def _rotated_triplets(x, seed: int):
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    gamma = np.sqrt(np.sum(x * x, axis=-1))
+    safe = np.where(gamma > 0, gamma, 1.0)
+    u = np.where((gamma > 0)[..., None], x / safe[..., None], 0.0)
+    y = u @ rotation_matrix(seed, d).T
+    nt = octo_triplets(d)
+    pad = np.zeros(y.shape[:-1] + (3 * nt - d,))
+    return gamma, np.concatenate([y, pad], axis=-1).reshape(y.shape[:-1] + (nt, 3))
+
+
+def octo_encode(x, seed: int, b: int, dirs, crho):
+    """Triplet codes of vectors x (..., d).
+
+    gamma = ||x||, u = x / gamma (0 when gamma = 0), y = R u cut into
+    triplets t_i; rho_i = ||t_i||, n_i = t_i / rho_i (n_i = (0, 0, 1) when
+    rho_i = 0); (xi, eta) = oct_map(n_i); the nearest codes j_xi, j_eta on the
+    uniform grid (cell floor((v + 1) 2^(b_dir - 1)), clamped).  Joint rounding:
+    for every (a, c) with a in {j_xi - 1, j_xi, j_xi + 1} and c in
+    {j_eta - 1, j_eta, j_eta + 1} inside the grid (a-major, ascending), with
+    n_hat = dirs[a, c] and p = t_i . n_hat, the norm code k minimising
+    (p - crho_k)^2 (first on ties) and the error ||t_i - crho_k n_hat||^2; the
+    first candidate of least error wins.
+    Returns dict(a, c, k: int64 (..., n_tri), gamma, gamma16, err, t)."""
+    gamma, t = _rotated_triplets(x, seed)
+    out = octo_encode_triplets(t, b, dirs, crho)
+    out.update(gamma=gamma, gamma16=fp16_norm(gamma), t=t)
+    return out
+
+
+def octo_encode_triplets(t, b: int, dirs, crho):
+    """The per-triplet stage of octo_encode on triplets t (..., 3): returns
+    dict(a, c, k, err)."""
+    b_dir, _ = octo_bits(b)
+    nd = 1 << b_dir
+    t = np.asarray(t, dtype=np.float64)
+    rho = np.sqrt(np.sum(t * t, axis=-1))
+    n = np.where((rho > 0)[..., None], t / np.where(rho > 0, rho, 1.0)[..., None], np.array([0.0, 0.0, 1.0]))
+    xi, eta = oct_map(n)
+    jx = np.clip(np.floor((xi + 1.0) * (nd / 2)).astype(np.int64), 0, nd - 1)
+    je = np.clip(np.floor((eta + 1.0) * (nd / 2)).astype(np.int64), 0, nd - 1)
+    best = np.full(rho.shape, np.inf)
+    A = np.zeros(rho.shape, np.int64)
+    C = np.zeros(rho.shape, np.int64)
+    K = np.zeros(rho.shape, np.int64)
+    crho = np.asarray(crho, dtype=np.float64)
+    for da in (-1, 0, 1):
+        for dc in (-1, 0, 1):
+            a, c = jx + da, je + dc
+            ok = (a >= 0) & (a < nd) & (c >= 0) & (c < nd)
+            nh = dirs[np.clip(a, 0, nd - 1), np.clip(c, 0, nd - 1)]
+            p = np.sum(t * nh, axis=-1)
+            k = np.argmin((p[..., None] - crho) ** 2, axis=-1)
+            err = np.sum((t - crho[k][..., None] * nh) ** 2, axis=-1)
+            take = ok & (err < best)
+            best = np.where(take, err, best)
+            A, C, K = np.where(take, a, A), np.where(take, c, C), np.where(take, k, K)
+    return {"a": A, "c": C, "k": K, "err": best}
+
+
+def octo_triplet_error(t, a, c, k, dirs, crho):
+    """||t - crho[k] dirs[a, c]||^2 for given codes (the quantity the joint
+    rounding minimises)."""
+    nh = dirs[a, c]
+    return np.sum((np.asarray(t) - np.asarray(crho)[k][..., None] * nh) ** 2, axis=-1)
+
+
+def octo_decode(a, c, k, gamma16, seed: int, d: int, dirs, crho):
+    """x_hat = gamma16 * R^T y_hat, y_hat the first d entries of the
+    concatenated crho[k_i] * dirs[a_i, c_i] ([P3] Method step 7: each triplet
+    rebuilt from its norm and direction codes)."""
+    yh = np.asarray(crho)[k][..., None] * dirs[a, c]
+    yh = yh.reshape(yh.shape[:-2] + (-1,))[..., :d]
+    return np.asarray(gamma16, dtype=np.float64)[..., None] * (yh @ rotation_matrix(seed, d))
+
+
+def octo_record_bytes(d: int, b: int) -> int:
+    """Bytes of one vector's code record: n_tri fields of B_tri = 2 b_dir +
+    b_nrm bits, triplet i at bit i * B_tri, fields xi | eta << b_dir |
+    rho << 2 b_dir, LSB first; rounded up to whole 32-bit words (this build's
+    layout; the page fixes none)."""
+    b_dir, b_nrm = octo_bits(b)
+    bits = octo_triplets(d) * (2 * b_dir + b_nrm)
+    return 4 * (-(-bits // 32))
+
+
+def octo_pack(a, c, k, b: int, d: int) -> np.ndarray:
+    """Records (..., octo_record_bytes) of uint8 from codes (..., n_tri)."""
+    b_dir, b_nrm = octo_bits(b)
+    bt = 2 * b_dir + b_nrm
+    a, c, k = (np.asarray(v, dtype=np.int64) for v in (a, c, k))
+    field = a | (c << b_dir) | (k << (2 * b_dir))
+    nt = field.shape[-1]
+    bits = ((field[..., :, None] >> np.arange(bt)) & 1).reshape(field.shape[:-1] + (nt * bt,))
+    nb = octo_record_bytes(d, b)
+    full = np.zeros(field.shape[:-1] + (8 * nb,), np.int64)
+    full[..., :nt * bt] = bits
+    return (full.reshape(field.shape[:-1] + (nb, 8)) << np.arange(8)).sum(axis=-1).astype(np.uint8)
+
+
+def octo_unpack(rec, b: int, d: int):
+    """Codes (a, c, k), each (..., n_tri), from records."""
+    b_dir, b_nrm = octo_bits(b)
+    bt = 2 * b_dir + b_nrm
+    nt = octo_triplets(d)
+    rec = np.asarray(rec, dtype=np.uint8)
+    bits = ((rec[..., :, None].astype(np.int64) >> np.arange(8)) & 1).reshape(rec.shape[:-1] + (-1,))
+    f = (bits[..., :nt * bt].reshape(rec.shape[:-1] + (nt, bt)) << np.arange(bt)).sum(axis=-1)
+    return f & ((1 << b_dir) - 1), (f >> b_dir) & ((1 << b_dir) - 1), f >> (2 * b_dir)

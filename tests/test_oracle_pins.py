@@ -580,3 +580,162 @@ def test_minmax_against_lloyd_max_on_gaussian_vectors():
         mse_l = np.mean(np.sum((x - xl) ** 2, axis=1) / n2)
         mse_m = np.mean(np.sum((x - xm) ** 2, axis=1) / n2)
         assert mse_l < mse_m, (bits, mse_l, mse_m)
+
+
+# --------------------------------------------------------- triplet codec ----
+
+def _unit_sphere(n, rng):
+    g = rng.standard_normal((n, 3))
+    return g / np.linalg.norm(g, axis=1, keepdims=True)
+
+
+def test_oct_map_fixed_points_and_round_trip():
+    pts = np.array([[0, 0, 1], [1, 0, 0], [0, 1, 0], [-1, 0, 0], [0, -1, 0]], float)
+    xi, eta = O.oct_map(pts)
+    np.testing.assert_allclose(np.stack([xi, eta], 1), [[0, 0], [1, 0], [0, 1], [-1, 0], [0, -1]], atol=1e-15)
+    xi, eta = O.oct_map(np.array([[0.0, 0.0, -1.0]]))
+    assert abs(xi[0]) == 1.0 and abs(eta[0]) == 1.0          # south pole: a corner
+    # the diagonal direction of the first octant's equator lands mid-edge
+    xi, eta = O.oct_map(np.array([[1.0, 1.0, 0.0]]) / math.sqrt(2))
+    np.testing.assert_allclose([xi[0], eta[0]], [0.5, 0.5], atol=1e-15)
+    n = _unit_sphere(5000, np.random.default_rng(3))
+    xi, eta = O.oct_map(n)
+    assert np.all(np.abs(xi) <= 1) and np.all(np.abs(eta) <= 1)
+    np.testing.assert_allclose(O.oct_unmap(xi, eta), n, atol=1e-12)
+    np.testing.assert_allclose(np.linalg.norm(O.oct_unmap(*np.random.default_rng(4).uniform(-1, 1, (2, 999))),
+                                              axis=1), 1.0, atol=1e-14)
+
+
+def test_oct_unmap_is_equal_area():
+    # the sphere (area 4 pi) over the square (area 4): the area element of the
+    # inverse map is pi everywhere, measured by central differences
+    rng = np.random.default_rng(5)
+    p = rng.uniform(-0.98, 0.98, (400, 2))
+    s = np.abs(p).sum(1)
+    keep = (np.abs(s - 1) > 0.01) & (np.abs(p[:, 0]) > 0.01) & (np.abs(p[:, 1]) > 0.01)
+    p = p[keep]
+    h = 1e-6
+    dx = (O.oct_unmap(p[:, 0] + h, p[:, 1]) - O.oct_unmap(p[:, 0] - h, p[:, 1])) / (2 * h)
+    dy = (O.oct_unmap(p[:, 0], p[:, 1] + h) - O.oct_unmap(p[:, 0], p[:, 1] - h)) / (2 * h)
+    np.testing.assert_allclose(np.linalg.norm(np.cross(dx, dy), axis=1), math.pi, rtol=1e-6)
+
+
+def test_uniform_directions_map_to_uniform_square_so_the_uniform_codebook_is_lloyd_max():
+    # triplets of uniform unit vectors in R^128 have isotropic directions, and
+    # through the map xi and eta come out uniform on [-1, 1]
+    rng = np.random.default_rng(6)
+    g = rng.standard_normal((4000, D))
+    t = (g / np.linalg.norm(g, axis=1, keepdims=True))[:, :126].reshape(-1, 3)
+    xi, eta = O.oct_map(t / np.linalg.norm(t, axis=1, keepdims=True))
+    from scipy import stats
+    for v in (xi, eta):
+        assert stats.kstest(v, "uniform", args=(-1, 2)).pvalue > 1e-3
+    # uniform density: every centroid is the mean of its cell
+    for bd in (3, 4, 5):
+        c = O.octo_dir_codebook(bd)
+        edges = np.concatenate(([-1.0], 0.5 * (c[:-1] + c[1:]), [1.0]))
+        np.testing.assert_allclose(c, 0.5 * (edges[:-1] + edges[1:]), atol=1e-15)
+        assert np.all(np.diff(edges) > 0) and len(c) == 1 << bd
+
+
+def test_rho_codebook_is_lloyd_max_by_quadrature_and_monte_carlo():
+    from scipy import stats
+    be = (D - 3) / 2.0
+    dens = lambda r: 2 * r * stats.beta.pdf(r * r, 1.5, be)
+    m2, _ = integrate.quad(lambda r: r * r * dens(r), 0, 1)
+    assert abs(m2 - 3.0 / D) < 1e-10                        # E[rho^2] = 3/d
+    for bits in (1, 2, 3):
+        c, t = O.rho_lloyd_max(D, bits)
+        edges = np.concatenate(([0.0], t, [1.0]))
+        for i in range(len(c)):
+            num, _ = integrate.quad(lambda r: r * dens(r), edges[i], edges[i + 1], epsabs=1e-14)
+            den, _ = integrate.quad(dens, edges[i], edges[i + 1], epsabs=1e-14)
+            assert abs(num / den - c[i]) < 1e-9
+    rng = np.random.default_rng(8)
+    g = rng.standard_normal((20000, D))
+    rho = np.linalg.norm((g / np.linalg.norm(g, axis=1, keepdims=True))[:, :3], axis=1)
+    c, _ = O.rho_lloyd_max(D, 3)
+    cells = np.searchsorted(0.5 * (c[:-1] + c[1:]), rho)
+    for i in range(8):
+        sel = rho[cells == i]
+        assert abs(sel.mean() - c[i]) < 5 * sel.std() / math.sqrt(len(sel)) + 1e-4
+
+
+def test_triplet_joint_rounding_reaches_brute_force_and_beats_independent_rounding():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((60, D))
+    for b in (2, 3):
+        dirs, crho = O.octo_codebooks(D, b)
+        e = O.octo_encode(x, 7, b, dirs, crho)
+        t = e["t"]
+        best = np.full(t.shape[:2], np.inf)
+        for a in range(dirs.shape[0]):
+            for c in range(dirs.shape[1]):
+                for k in range(len(crho)):
+                    best = np.minimum(best, np.sum((t - crho[k] * dirs[a, c]) ** 2, axis=-1))
+        assert np.all(e["err"] >= best - 1e-15)
+        assert np.mean(e["err"] <= best + 1e-15) > 0.99
+        np.testing.assert_allclose(O.octo_triplet_error(t, e["a"], e["c"], e["k"], dirs, crho), e["err"], atol=1e-15)
+        # independent rounding: nearest xi, eta, rho separately
+        rho = np.linalg.norm(t, axis=-1)
+        xi, eta = O.oct_map(t / rho[..., None])
+        nd = dirs.shape[0]
+        ja = np.clip(np.floor((xi + 1) * nd / 2).astype(int), 0, nd - 1)
+        jc = np.clip(np.floor((eta + 1) * nd / 2).astype(int), 0, nd - 1)
+        jk = np.argmin((rho[..., None] - crho) ** 2, axis=-1)
+        ind = O.octo_triplet_error(t, ja, jc, jk, dirs, crho)
+        assert np.all(e["err"] <= ind + 1e-15) and np.mean(e["err"] < ind - 1e-12) > 0.05
+
+
+def test_triplet_codes_are_a_fixed_point_of_the_triplet_stage():
+    # a triplet built from codes (a, c, k) encodes back to (a, c, k) with no
+    # error: pins the a-major table index (xi first), the norm scaling and
+    # the candidate window around the nearest cell
+    rng = np.random.default_rng(10)
+    for b in (2, 3, 4):
+        dirs, crho = O.octo_codebooks(D, b)
+        nd = dirs.shape[0]
+        a, c, k = rng.integers(0, nd, 500), rng.integers(0, nd, 500), rng.integers(0, len(crho), 500)
+        e = O.octo_encode_triplets(crho[k][:, None] * dirs[a, c], b, dirs, crho)
+        np.testing.assert_array_equal(e["a"], a)
+        np.testing.assert_array_equal(e["c"], c)
+        np.testing.assert_array_equal(e["k"], k)
+        assert np.all(e["err"] < 1e-12)
+
+
+def test_triplet_codec_matches_the_pages_synthetic_results():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((8000, D))
+    u = x / np.linalg.norm(x, axis=1, keepdims=True)
+    mse_page = {int(r.split()[0]): float(r.split()[1]) for r in _golden_lines("octopus_synthetic_mse.txt")}
+    cos_page = {int(r.split()[0]): float(r.split()[1]) for r in _golden_lines("octopus_synthetic_cos.txt")}
+    lm = {b: D * O.codebook_distortion(D, b) for b in (2, 3, 4)}
+    for b in (2, 3, 4):
+        dirs, crho = O.octo_codebooks(D, b)
+        e = O.octo_encode(x, 7, b, dirs, crho)
+        xh = O.octo_decode(e["a"], e["c"], e["k"], e["gamma"], 7, D, dirs, crho) / e["gamma"][:, None]
+        mse = np.mean(np.sum((xh - u) ** 2, 1))
+        cos = np.mean(np.sum(xh * u, 1) / np.linalg.norm(xh, axis=1))
+        assert abs(mse - mse_page[b]) < 0.12 * mse_page[b], (b, mse)
+        assert abs(cos - cos_page[b]) < 0.005, (b, cos)
+        assert mse < lm[b]                               # below the per-coordinate codec
+
+
+def test_triplet_records_place_fields_lsb_first():
+    b = 2                       # fields of 3 + 3 + 1 = 7 bits
+    nt = O.octo_triplets(D)
+    a = np.zeros(nt, int); c = np.zeros(nt, int); k = np.zeros(nt, int)
+    a[0], c[0], k[0] = 5, 3, 1          # 101 | 011 << 3 | 1 << 6 = 0b1011101
+    a[1], k[1] = 7, 1                   # bits 7..13: 0b1000111
+    rec = O.octo_pack(a, c, k, b, D)
+    assert rec.shape == (O.octo_record_bytes(D, b),) == (40,)
+    assert rec[0] == 0b11011101 and rec[1] == 0b00100011
+    assert np.all(rec[2:] == 0)
+    assert [O.octo_record_bytes(D, b) for b in (2, 3, 4)] == [40, 56, 72]
+    rng = np.random.default_rng(13)
+    for b in (2, 3, 4):
+        bd, bn = O.octo_bits(b)
+        codes = [rng.integers(0, 1 << w, (4, nt)) for w in (bd, bd, bn)]
+        back = O.octo_unpack(O.octo_pack(*codes, b, D), b, D)
+        for u, v in zip(codes, back):
+            np.testing.assert_array_equal(u, v)
