@@ -279,6 +279,66 @@ int tq_decompress_kv(const tq_cache* cache, const int32_t* slots, int64_t n,
                      void* hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * Octahedral triplet codec ([P3] "Octahedral triplet direction quantizer
+ * with norm marginals", "MSE-optimal non-uniform bit allocation", Method
+ * steps 1-7), d = 128, budget bits b in {2, 3, 4}.  gamma = ||x||; the
+ * rotated direction y = R x / gamma is cut into 43 triplets t_i (the last is
+ * (y126, y127, 0)); rho_i = ||t_i||, n_i = t_i / rho_i ((0, 0, 1) when
+ * rho_i = 0); (xi, eta) = the equal-area octahedral map of n_i.  xi and eta
+ * take (b+1)-bit codes on the uniform grid c_j = -1 + (2j+1)/2^(b+1) (the
+ * Lloyd-Max quantiser of their uniform marginal); rho takes a (b-1)-bit
+ * Lloyd-Max code for its marginal (rho^2 ~ Beta(3/2, 125/2)).  Joint
+ * rounding: among the nearest grid cell and its in-grid neighbours in xi and
+ * eta (xi-major, ascending), with n_hat the table direction and the norm code
+ * nearest to t_i . n_hat, the first of least ||t_i - rho_hat n_hat||^2 wins.
+ *
+ * Record of one vector (tq_octo_record_bytes: 40 / 56 / 72 bytes): 43 fields
+ * of 2(b+1) + (b-1) bits, field i at bit 7i / 10i / 13i, LSB first, holding
+ * xi code | eta code << (b+1) | rho code << 2(b+1); unused bits zero.  gamma
+ * is stored beside it as fp16 (round to nearest even, saturating at 65504). */
+
+/* Bytes of one record; negative status for unsupported d or bits. */
+int64_t tq_octo_record_bytes(int32_t d, int32_t bits);
+
+/* Bytes of the device direction table of bit budget `bits`:
+ * 16 * 4^(bits+1) (4 / 16 / 64 KiB). */
+int64_t tq_octo_table_bytes(int32_t bits);
+
+/* Host copies of the tables (computed in float64, rounded to fp32, cached):
+ *   dirs:          [4^(bits+1)][4], entry a * 2^(bits+1) + c = the unit
+ *                  direction of grid point (c_a, c_c): x, y, z, 0; may be NULL;
+ *   rho_centroids: [2^(bits-1)] ascending; may be NULL. */
+int tq_octo_codebook(int32_t d, int32_t bits, float* dirs, float* rho_centroids);
+
+/* Fill a caller-owned device buffer of tq_octo_table_bytes(bits) bytes
+ * (16-byte aligned) with the direction table; asynchronous on hip_stream.
+ * The buffer is what the encode and logits calls of the same bits read. */
+int tq_octo_tables(int32_t bits, void* dev_tables, void* hip_stream);
+
+/* Encode n vectors.  X: device [n][128] of dtype (TQ_F32 / TQ_F16 /
+ * TQ_BF16), 16-byte aligned; codes: device [n][record bytes], 8-byte aligned;
+ * gamma: device [n] fp16; dev_tables: filled by tq_octo_tables(bits).  All
+ * caller-owned.  Asynchronous on hip_stream.  Errors: TQ_ERR_INVALID_ARG
+ * (null pointer, dtype, alignment, n < 0, n >= 2^31), TQ_ERR_UNSUPPORTED
+ * (bits, rotation dimension), TQ_ERR_NO_DEVICE, TQ_ERR_HIP. */
+int tq_octo_encode(const void* X, int32_t dtype, int64_t n, int32_t bits,
+                   const tq_rotation* rot, const void* dev_tables, void* codes,
+                   void* gamma, void* hip_stream);
+
+/* Logits straight from the records, no reconstructed key written ([P3]
+ * Method step 7: the dot product from each triplet's norm and direction):
+ *   out[h][g][j] = scale * gamma_hj * sum_i rho_hat_hji ((R q_hg)_i . n_hat_hji)
+ * which equals scale * q_hg . x_hat_hj.  q: device fp32 [heads][group][128],
+ * 16-byte aligned; codes: [heads][n][record bytes]; gamma: [heads][n] fp16;
+ * out: fp32 [heads][group][n]; group in 1..16, heads in 1..65535,
+ * heads * n < 2^31.  Errors as tq_octo_encode (group > 16 is
+ * TQ_ERR_UNSUPPORTED; a non-finite scale is TQ_ERR_INVALID_ARG). */
+int tq_octo_logits(const float* q, const void* codes, const void* gamma,
+                   int32_t heads, int32_t group, int64_t n, int32_t bits,
+                   const tq_rotation* rot, const void* dev_tables, float scale,
+                   float* out, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
  * Measurement aid (not part of the codec): read `bytes` of device memory at
  * `src` as a plain stream (grid-stride 16-byte non-temporal loads) and write
  * one folded word to `sink` (device, 4 bytes).  Timing it gives the on-box

@@ -167,6 +167,135 @@ const Codebook* codebook_cached(int d, int bits) {
   return &cache.emplace(key, std::move(cb)).first->second;
 }
 
+// --------------------------------------------------------- triplet codec --
+// Norm of one triplet of a uniform unit vector in R^d: rho^2 ~ Beta(3/2,
+// (d-3)/2), density proportional to r^2 (1 - r^2)^((d-5)/2).  With
+// r = sin(phi) the mass of [0, r] is proportional to
+// integral_0^phi sin^2 cos^(d-4) = J_{d-4}(phi) - J_{d-2}(phi), and the first
+// moment to integral_0^phi sin^3 cos^(d-4)
+//   = (1 - cos^(d-3) phi)/(d-3) - (1 - cos^(d-1) phi)/(d-1).
+struct RhoMarginal {
+  int d;
+  double norm;
+  explicit RhoMarginal(int d_) : d(d_) {
+    norm = 1.0 / (cos_power_integral(d - 4, M_PI / 2) - cos_power_integral(d - 2, M_PI / 2));
+  }
+  double cdf(double r) const {
+    if (r <= 0.0) return 0.0;
+    if (r >= 1.0) return 1.0;
+    const double phi = std::asin(r);
+    return norm * (cos_power_integral(d - 4, phi) - cos_power_integral(d - 2, phi));
+  }
+  double first_moment(double a, double b) const {
+    auto m = [&](double r) {
+      r = std::fmin(1.0, std::fmax(0.0, r));
+      const double c = std::sqrt(std::fmax(0.0, 1.0 - r * r));
+      return (1.0 - std::pow(c, d - 3)) / (d - 3) - (1.0 - std::pow(c, d - 1)) / (d - 1);
+    };
+    return norm * (m(b) - m(a));
+  }
+};
+
+// Lloyd-Max for rho on [0, 1]: the same iteration as lloyd_max without the
+// symmetry (this density is log-concave too, so the fixed point is unique).
+void rho_lloyd_max(int d, int bits, std::vector<double>& c) {
+  const int n = 1 << bits;
+  RhoMarginal m(d);
+  c.resize(n);
+  for (int i = 0; i < n; ++i) {
+    const double target = (i + 0.5) / n;
+    double lo = 0.0, hi = 1.0;
+    for (int k = 0; k < 80; ++k) {
+      const double mid = 0.5 * (lo + hi);
+      (m.cdf(mid) < target ? lo : hi) = mid;
+    }
+    c[i] = 0.5 * (lo + hi);
+  }
+  std::vector<double> edge(n + 1), cdf(n + 1);
+  double best = 1e300;
+  int stale = 0;
+  for (int it = 0; it < 1000000; ++it) {
+    edge[0] = 0.0;
+    edge[n] = 1.0;
+    for (int i = 1; i < n; ++i) edge[i] = 0.5 * (c[i - 1] + c[i]);
+    for (int i = 0; i <= n; ++i) cdf[i] = m.cdf(edge[i]);
+    double moved = 0.0, cmax = 0.0;
+    for (int i = 0; i < n; ++i) {
+      const double v = m.first_moment(edge[i], edge[i + 1]) / (cdf[i + 1] - cdf[i]);
+      moved = std::fmax(moved, std::fabs(v - c[i]));
+      c[i] = v;
+      cmax = std::fmax(cmax, v);
+    }
+    if (moved < 1e-14 * cmax) return;
+    if (moved < best) {
+      best = moved;
+      stale = 0;
+    } else if (++stale > 2000) {
+      return;
+    }
+  }
+}
+
+// Inverse of the equal-area octahedral map, (xi, eta) in [-1, 1]^2 to a unit
+// vector: past the diamond |xi| + |eta| = 1 the point is reflected back
+// ((|xi|, |eta|) -> (1 - |eta|, 1 - |xi|)) and lands in the lower hemisphere;
+// the L1 radius r gives z = 1 - r^2, the position along the diamond edge the
+// azimuth phi = (pi/2) |eta| / r, and sqrt(1 - z^2) = r sqrt(2 - r^2).
+void oct_unmap(double xi, double eta, double out[3]) {
+  double ax = std::fabs(xi), ae = std::fabs(eta);
+  const bool lower = ax + ae > 1.0;
+  if (lower) {
+    const double t = ax;
+    ax = 1.0 - ae;
+    ae = 1.0 - t;
+  }
+  const double r = ax + ae;
+  const double z = 1.0 - r * r;
+  const double phi = r > 0.0 ? (M_PI / 2) * ae / r : 0.0;
+  const double s = r * std::sqrt(std::fmax(2.0 - r * r, 0.0));
+  out[0] = (xi < 0 ? -1.0 : 1.0) * s * std::cos(phi);
+  out[1] = (eta < 0 ? -1.0 : 1.0) * s * std::sin(phi);
+  out[2] = lower ? -z : z;
+}
+
+// Tables of the triplet codec with budget b: directions of the (b+1)-bit
+// uniform grid c_j = -1 + (2j + 1) / 2^(b+1) in xi and eta (entry a * nd + c
+// is the direction of (c_a, c_c), x y z 0 as fp32), and the (b-1)-bit
+// Lloyd-Max norm codebook with fp32 midpoint thresholds.
+struct OctoTables {
+  std::vector<float> dirs;   // [nd * nd][4]
+  std::vector<float> crho;   // [2^(b-1)]
+  std::vector<float> trho;   // [2^(b-1) - 1]
+};
+
+const OctoTables* octo_tables_cached(int d, int b) {
+  static std::mutex mu;
+  static std::map<std::pair<int, int>, OctoTables> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(d, b);
+  auto it = cache.find(key);
+  if (it != cache.end()) return &it->second;
+  OctoTables t;
+  const int nd = 1 << (b + 1);
+  t.dirs.resize((size_t)nd * nd * 4);
+  for (int a = 0; a < nd; ++a)
+    for (int c = 0; c < nd; ++c) {
+      double v[3];
+      oct_unmap(-1.0 + (2.0 * a + 1.0) / nd, -1.0 + (2.0 * c + 1.0) / nd, v);
+      float* e = &t.dirs[((size_t)a * nd + c) * 4];
+      e[0] = (float)v[0];
+      e[1] = (float)v[1];
+      e[2] = (float)v[2];
+      e[3] = 0.f;
+    }
+  std::vector<double> c;
+  rho_lloyd_max(d, b - 1, c);
+  for (double v : c) t.crho.push_back((float)v);
+  for (size_t i = 0; i + 1 < t.crho.size(); ++i)
+    t.trho.push_back((float)(0.5 * ((double)t.crho[i] + (double)t.crho[i + 1])));
+  return &cache.emplace(key, std::move(t)).first->second;
+}
+
 // Bucket table of the encoder's threshold search (see tq::CodecTables).
 int build_codec_tables(int d, int bits, tq::CodecTables& tab) {
   const Codebook* cb = codebook_cached(d, bits);
@@ -758,6 +887,113 @@ int tq_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* hip_str
   if (s != TQ_OK) return s;
   int err = tq::launch_stream_read(src, bytes, sink, hip_stream);
   if (err != 0) return hip_fail(err, "stream read launch");
+  return TQ_OK;
+}
+
+int64_t tq_octo_record_bytes(int32_t d, int32_t bits) {
+  if (d != tq::kD) return fail(TQ_ERR_UNSUPPORTED, "the triplet codec supports d = 128");
+  if (bits < 2 || bits > 4) return fail(TQ_ERR_UNSUPPORTED, "bits must be 2..4");
+  const int64_t field = 2 * (bits + 1) + (bits - 1);
+  return 4 * ((tq::kOctoTri * field + 31) / 32);
+}
+
+int64_t tq_octo_table_bytes(int32_t bits) {
+  if (bits < 2 || bits > 4) return fail(TQ_ERR_UNSUPPORTED, "bits must be 2..4");
+  return (int64_t)16 << (2 * (bits + 1));
+}
+
+int tq_octo_codebook(int32_t d, int32_t bits, float* dirs, float* rho_centroids) {
+  if (d != tq::kD) return fail(TQ_ERR_UNSUPPORTED, "the triplet codec supports d = 128");
+  if (bits < 2 || bits > 4) return fail(TQ_ERR_UNSUPPORTED, "bits must be 2..4");
+  const OctoTables* t = octo_tables_cached(d, bits);
+  if (dirs) std::memcpy(dirs, t->dirs.data(), sizeof(float) * t->dirs.size());
+  if (rho_centroids) std::memcpy(rho_centroids, t->crho.data(), sizeof(float) * t->crho.size());
+  return TQ_OK;
+}
+
+int tq_octo_tables(int32_t bits, void* dev_tables, void* hip_stream) {
+  if (bits < 2 || bits > 4) return fail(TQ_ERR_UNSUPPORTED, "bits must be 2..4");
+  if (!dev_tables) return fail(TQ_ERR_INVALID_ARG, "null table buffer");
+  if (reinterpret_cast<uintptr_t>(dev_tables) % 16 != 0) return fail(TQ_ERR_INVALID_ARG, "table buffer must be 16-byte aligned");
+  int s = check_device();
+  if (s != TQ_OK) return s;
+  const OctoTables* t = octo_tables_cached(tq::kD, bits);   // cached for the process: a valid copy source
+  hipError_t e = hipMemcpyAsync(dev_tables, t->dirs.data(), sizeof(float) * t->dirs.size(), hipMemcpyHostToDevice,
+                                static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail((int)e, "table copy");
+  return TQ_OK;
+}
+
+namespace {
+int octo_args(int32_t bits, const tq_rotation* rot, const void* dev_tables, tq::OctoArgs& a) {
+  if (!rot || rot->d != tq::kD) return fail(TQ_ERR_UNSUPPORTED, "the triplet codec needs a rotation of dimension 128");
+  if (bits < 2 || bits > 4) return fail(TQ_ERR_UNSUPPORTED, "bits must be 2..4");
+  if (!dev_tables || reinterpret_cast<uintptr_t>(dev_tables) % 16 != 0)
+    return fail(TQ_ERR_INVALID_ARG, "tables must be a 16-byte aligned device buffer filled by tq_octo_tables");
+  std::memset(&a, 0, sizeof(a));
+  const OctoTables* t = octo_tables_cached(tq::kD, bits);
+  a.dirs = static_cast<const float*>(dev_tables);
+  for (int i = 0; i < 8; ++i) {
+    a.crho[i] = i < (int)t->crho.size() ? t->crho[i] : 0.f;
+    a.trho[i] = i < (int)t->trho.size() ? t->trho[i] : std::numeric_limits<float>::infinity();
+  }
+  to_mask(rot->signs, a.rot);
+  return TQ_OK;
+}
+}  // namespace
+
+int tq_octo_encode(const void* X, int32_t dtype, int64_t n, int32_t bits, const tq_rotation* rot,
+                   const void* dev_tables, void* codes, void* gamma, void* hip_stream) {
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n < 0");
+  if (dtype != TQ_F32 && dtype != TQ_F16 && dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad dtype");
+  tq::OctoArgs a;
+  int s = octo_args(bits, rot, dev_tables, a);
+  if (s != TQ_OK) return s;
+  if (n == 0) return TQ_OK;
+  if (!X || !codes || !gamma) return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  if (reinterpret_cast<uintptr_t>(X) % 16 != 0 || reinterpret_cast<uintptr_t>(codes) % 8 != 0 ||
+      reinterpret_cast<uintptr_t>(gamma) % 2 != 0)
+    return fail(TQ_ERR_INVALID_ARG, "X must be 16-byte aligned, codes 8-byte, gamma 2-byte");
+  if (n >= ((int64_t)1 << 31)) return fail(TQ_ERR_INVALID_ARG, "too many vectors");
+  if ((s = check_device()) != TQ_OK) return s;
+  a.src = X;
+  a.codes = static_cast<uint8_t*>(codes);
+  a.gamma = static_cast<uint16_t*>(gamma);
+  a.n = n;
+  a.dtype = dtype;
+  a.heads = 1;
+  int err = tq::launch_octo_encode(a, bits, hip_stream);
+  if (err != 0) return hip_fail(err, "triplet encode launch");
+  return TQ_OK;
+}
+
+int tq_octo_logits(const float* q, const void* codes, const void* gamma, int32_t heads, int32_t group, int64_t n,
+                   int32_t bits, const tq_rotation* rot, const void* dev_tables, float scale, float* out,
+                   void* hip_stream) {
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n < 0");
+  if (heads < 1 || heads > 65535) return fail(TQ_ERR_INVALID_ARG, "heads must be 1..65535");
+  if (group < 1 || group > tq::kOctoMaxGroup) return fail(TQ_ERR_UNSUPPORTED, "group must be 1..16");
+  if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, "scale must be finite");
+  tq::OctoArgs a;
+  int s = octo_args(bits, rot, dev_tables, a);
+  if (s != TQ_OK) return s;
+  if (n == 0) return TQ_OK;
+  if (!q || !codes || !gamma || !out) return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(codes) % 8 != 0 ||
+      reinterpret_cast<uintptr_t>(gamma) % 2 != 0 || reinterpret_cast<uintptr_t>(out) % 4 != 0)
+    return fail(TQ_ERR_INVALID_ARG, "q must be 16-byte aligned, codes 8-byte, gamma 2-byte, out 4-byte");
+  if (n * heads >= ((int64_t)1 << 31)) return fail(TQ_ERR_INVALID_ARG, "too many keys");
+  if ((s = check_device()) != TQ_OK) return s;
+  a.q = q;
+  a.codes = const_cast<uint8_t*>(static_cast<const uint8_t*>(codes));
+  a.gamma = const_cast<uint16_t*>(static_cast<const uint16_t*>(gamma));
+  a.out = out;
+  a.n = n;
+  a.heads = heads;
+  a.group = group;
+  a.scale = scale;
+  int err = tq::launch_octo_logits(a, bits, hip_stream);
+  if (err != 0) return hip_fail(err, "triplet logits launch");
   return TQ_OK;
 }
 

@@ -164,6 +164,27 @@ struct MinmaxArgs {
   SignMask rot;
 };
 
+// Triplet codec on flat buffers.  Per vector: kOctoTri fields of
+// 2 (b+1) + (b-1) bits (xi code | eta code << (b+1) | norm code << 2(b+1)),
+// triplet i at bit i * field_bits, LSB first, in a record of whole 32-bit
+// words; the norm gamma as fp16 beside it.
+constexpr int kOctoTri = 43;        // ceil(128 / 3); the last triplet is (y126, y127, 0)
+constexpr int kOctoMaxGroup = 16;   // queries per head of a logits launch
+struct OctoArgs {
+  const void* src;          // encode: [n][128] of dtype
+  const float* dirs;        // [nd * nd][4] unit directions (x, y, z, 0), nd = 2^(b+1)
+  uint8_t* codes;           // [heads][n][rec_bytes]
+  uint16_t* gamma;          // [heads][n] fp16
+  const float* q;           // logits: [heads][group][128] fp32
+  float* out;               // logits: [heads][group][n]
+  int64_t n;
+  int32_t dtype, heads, group;
+  float scale;
+  SignMask rot;
+  float crho[8];            // norm centroids (2^(b-1) used)
+  float trho[8];            // thresholds, +inf past the last
+};
+
 // Launchers implemented in the .hip files; return a hipError_t value.
 int launch_encode(const EncodeArgs& a, int num_streams, int in_dtype, void* stream);
 int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int attend, int mfma, void* stream);
@@ -176,5 +197,7 @@ int launch_decompress(const DecompArgs& a, void* stream);
 int launch_minmax_encode(const MinmaxArgs& a, int bits, void* stream);
 int launch_minmax_decode(const MinmaxArgs& a, int bits, void* stream);
 int launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+int launch_octo_encode(const OctoArgs& a, int bits, void* stream);
+int launch_octo_logits(const OctoArgs& a, int bits, void* stream);
 
 }  // namespace tq

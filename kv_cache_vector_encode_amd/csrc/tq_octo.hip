@@ -1,0 +1,274 @@
+// tq_octo: the octahedral triplet codec of the OCTOPUS summary (sections
+// "Octahedral triplet direction quantizer with norm marginals", "MSE-optimal
+// non-uniform bit allocation" and the Method list): the rotated unit
+// direction y = R k / ||k|| is cut into 43 triplets (the last is
+// (y126, y127, 0)); each triplet t = rho n keeps its norm rho and the
+// direction n mapped by the equal-area octahedral map to (xi, eta) in
+// [-1, 1]^2.  xi and eta take (b+1)-bit uniform codes, rho a (b-1)-bit
+// Lloyd-Max code, and a 3x3 joint rounding over the nearest direction cell
+// and its neighbours picks the codes with the least ||t - rho_hat n_hat||^2.
+//
+// Encode: one vector per 16-lane row (the in-register FWHT of the encoder),
+// the rotated coordinates staged in LDS, then each lane takes triplets
+// L, L+16, L+32 of its row; the direction table sits in LDS.
+// Logits: one key per thread; its record is unpacked field by field, each
+// triplet's direction read from the LDS table and scaled by its norm code,
+// and dotted with the group's rotated queries (LDS broadcast).  No K_hat is
+// written anywhere.
+
+#include <hip/hip_bf16.h>
+
+#include "tq_device.h"
+#include "tq_encode_row.h"
+
+namespace tq {
+
+template <int B>
+struct Octo {
+  static constexpr int kBd = B + 1;                  // bits of xi and of eta
+  static constexpr int kBn = B - 1;                  // bits of rho
+  static constexpr int kNd = 1 << kBd;               // grid cells per axis
+  static constexpr int kNr = 1 << kBn;               // norm codes
+  static constexpr int kField = 2 * kBd + kBn;       // bits per triplet
+  static constexpr int kWords = (kOctoTri * kField + 31) / 32;
+  static constexpr int kRec = 4 * kWords;            // bytes per record
+};
+
+constexpr int kOctoRowPad = 132;   // LDS floats per row: 128 coordinates, zero pad
+
+__device__ __forceinline__ int octo_cell(float v, int nd) {
+  const int j = (int)floorf((v + 1.f) * (float)(nd / 2));
+  return min(max(j, 0), nd - 1);
+}
+
+// Equal-area octahedral map of a unit vector: L1 radius sqrt(1 - |z|), the
+// azimuth atan2(|y|, |x|) spread linearly along the diamond edge, the lower
+// hemisphere reflected across the edge.
+__device__ __forceinline__ void oct_map(float nx, float ny, float nz, float& xi, float& eta) {
+  const float r = sqrtf(fmaxf(1.f - fabsf(nz), 0.f));
+  const float phi = atan2f(fabsf(ny), fabsf(nx));
+  float ae = r * phi * 0.636619772367581343f;   // 2 / pi
+  float ax = r - ae;
+  if (nz < 0.f) {
+    const float t = ax;
+    ax = 1.f - ae;
+    ae = 1.f - t;
+  }
+  xi = nx < 0.f ? -ax : ax;
+  eta = ny < 0.f ? -ae : ae;
+}
+
+template <int B, int DT>
+__global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
+  using C = Octo<B>;
+  __shared__ float4 s_dir[C::kNd * C::kNd];
+  __shared__ float s_y[16][kOctoRowPad];
+  __shared__ uint32_t s_rec[16][C::kWords];
+  const int tid = threadIdx.x, row = tid >> 4;
+  const int L = tid & 15, ell = perm16(L);
+  for (int i = tid; i < C::kNd * C::kNd; i += 256) s_dir[i] = reinterpret_cast<const float4*>(a.dirs)[i];
+  const uint32_t sneg = sign_byte(a.rot, ell);
+  uint32_t smask[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (DT == 0) smask[i] = ((sneg >> i) & 1u) << 31;
+    else smask[i] = i < 4 ? (((sneg >> (2 * i)) & 1u) << 15) | (((sneg >> (2 * i + 1)) & 1u) << 31) : 0u;
+  }
+  const FwhtLane fc = fwht_lane(L);
+  const int64_t groups = (a.n + 15) / 16;
+  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+    const int64_t v = grp * 16 + row;
+    const int64_t vc = v < a.n ? v : a.n - 1;
+    float x[8];
+    load8_signed<DT>(a.src, vc * kD + 8 * ell, smask, x);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+    const float gamma = sqrtf(row_sum(ss));
+    fwht_row(x, fc);   // lane L: coordinates 8L..8L+7 of H s.x, times fc.sig
+    const float g = gamma > 0.f ? fc.sig * kInvSqrtD / gamma : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_y[row][8 * L + e] = x[e] * g;
+    if (L < kOctoRowPad - kD) s_y[row][kD + L] = 0.f;
+    for (int w = L; w < C::kWords; w += 16) s_rec[row][w] = 0u;
+    __syncthreads();
+    for (int i = L; i < kOctoTri; i += 16) {
+      const float tx = s_y[row][3 * i], ty = s_y[row][3 * i + 1], tz = s_y[row][3 * i + 2];
+      const float rho = sqrtf(tx * tx + ty * ty + tz * tz);
+      float nx = 0.f, ny = 0.f, nz = 1.f;
+      if (rho > 0.f) {
+        nx = tx / rho;
+        ny = ty / rho;
+        nz = tz / rho;
+      }
+      float xi, eta;
+      oct_map(nx, ny, nz, xi, eta);
+      const int jx = octo_cell(xi, C::kNd), je = octo_cell(eta, C::kNd);
+      float best = INFINITY;
+      uint32_t field = 0;
+#pragma unroll
+      for (int da = -1; da <= 1; ++da) {
+        const int ca = jx + da;
+        if (ca < 0 || ca >= C::kNd) continue;
+#pragma unroll
+        for (int dc = -1; dc <= 1; ++dc) {
+          const int cc = je + dc;
+          if (cc < 0 || cc >= C::kNd) continue;
+          const float4 d = s_dir[ca * C::kNd + cc];
+          const float p = tx * d.x + ty * d.y + tz * d.z;
+          float cr = a.crho[0];
+          uint32_t k = 0;
+#pragma unroll
+          for (int j = 0; j + 1 < C::kNr; ++j) {
+            const bool up = p > a.trho[j];
+            cr = up ? a.crho[j + 1] : cr;
+            k += up ? 1u : 0u;
+          }
+          const float ex = tx - cr * d.x, ey = ty - cr * d.y, ez = tz - cr * d.z;
+          const float err = ex * ex + ey * ey + ez * ez;
+          if (err < best) {
+            best = err;
+            field = (uint32_t)ca | ((uint32_t)cc << C::kBd) | (k << (2 * C::kBd));
+          }
+        }
+      }
+      const int bit = i * C::kField, w = bit >> 5, sh = bit & 31;
+      atomicOr(&s_rec[row][w], field << sh);
+      if (sh + C::kField > 32) atomicOr(&s_rec[row][w + 1], field >> (32 - sh));
+    }
+    __syncthreads();
+    if (v < a.n) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + v * C::kRec);
+      for (int w = L; w < C::kWords; w += 16) dst[w] = s_rec[row][w];
+      if (L == 0) a.gamma[v] = __half_as_ushort(__float2half_rn(fminf(gamma, 65504.f)));
+    }
+    __syncthreads();   // s_y and s_rec are rewritten by the next group
+  }
+}
+
+// Logits of a head's group of queries against n keys: out = scale * gamma *
+// sum_i rho_hat_i (R q)_i . n_hat_i.  Block (x = tile of 256 keys, y = head).
+// The tile's records are staged in LDS (word stride kWords + 1, odd, so the
+// threads' reads of one field fall in distinct banks); each thread then walks
+// its key's 43 fields in order.
+template <int B, int G>
+__global__ __launch_bounds__(256) void octo_logits_kernel(const OctoArgs a) {
+  using C = Octo<B>;
+  constexpr int kStride = C::kWords + 1;
+  __shared__ float4 s_dir[C::kNd * C::kNd];
+  __shared__ float4 s_q[G][kOctoTri + 1];
+  __shared__ uint32_t s_rec[256 * kStride];
+  __shared__ float s_rho[8];
+  const int tid = threadIdx.x;
+  const int head = blockIdx.y;
+  const int64_t key0 = (int64_t)blockIdx.x * 256;
+  const int nk = (int)(a.n - key0 < 256 ? a.n - key0 : 256);
+  for (int i = tid; i < C::kNd * C::kNd; i += 256) s_dir[i] = reinterpret_cast<const float4*>(a.dirs)[i];
+  if (tid < 8) s_rho[tid] = a.crho[tid];
+  {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.codes + ((int64_t)head * a.n + key0) * C::kRec);
+    for (int i = tid; i < nk * C::kWords; i += 256) {
+      const int k = i / C::kWords, w = i - k * C::kWords;
+      s_rec[k * kStride + w] = src[i];
+    }
+  }
+  // rotate the group's queries: one per 16-lane row, scaled by the logit scale
+  float* qf = reinterpret_cast<float*>(&s_q[0][0]);
+  for (int i = tid; i < G * (kOctoTri + 1) * 4; i += 256) qf[i] = 0.f;
+  __syncthreads();
+  {
+    const int row = tid >> 4, L = tid & 15, ell = perm16(L);
+    const int rq = row < a.group ? row : 0;
+    const uint32_t sneg = sign_byte(a.rot, ell);
+    uint32_t smask[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) smask[i] = ((sneg >> i) & 1u) << 31;
+    float x[8];
+    load8_signed<0>(a.q, ((int64_t)head * a.group + rq) * kD + 8 * ell, smask, x);
+    const FwhtLane fc = fwht_lane(L);
+    fwht_row(x, fc);
+    const float g = fc.sig * kInvSqrtD * a.scale;
+    if (row < a.group && row < G) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 8 * L + e;
+        qf[(row * (kOctoTri + 1) + j / 3) * 4 + j % 3] = x[e] * g;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid >= nk) return;
+  const int64_t key = key0 + tid;
+  const float gamma = __half2float(__ushort_as_half(a.gamma[(int64_t)head * a.n + key]));
+  const uint32_t* rec = s_rec + tid * kStride;
+  float acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = 0.f;
+#pragma unroll 2
+  for (int i = 0; i < kOctoTri; ++i) {
+    const int bit = i * C::kField, wi = bit >> 5, sh = bit & 31;
+    const uint32_t lo = rec[wi], hi = rec[wi + 1];   // word kWords is the pad: read, never used
+    const uint32_t f = (uint32_t)((((uint64_t)hi << 32) | lo) >> sh) & ((1u << C::kField) - 1u);
+    const uint32_t ca = f & (C::kNd - 1), cc = (f >> C::kBd) & (C::kNd - 1), k = f >> (2 * C::kBd);
+    const float4 d = s_dir[ca * C::kNd + cc];
+    const float r = s_rho[k];
+    const float kx = r * d.x, ky = r * d.y, kz = r * d.z;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float4 qv = s_q[g][i];
+      acc[g] = __builtin_fmaf(qv.x, kx, __builtin_fmaf(qv.y, ky, __builtin_fmaf(qv.z, kz, acc[g])));
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    if (g < a.group) a.out[((int64_t)head * a.group + g) * a.n + key] = acc[g] * gamma;
+}
+
+template <int B>
+static void octo_enc(const OctoArgs& a, dim3 grid, hipStream_t s) {
+  if (a.dtype == 0) hipLaunchKernelGGL((octo_encode_kernel<B, 0>), grid, dim3(256), 0, s, a);
+  else if (a.dtype == 1) hipLaunchKernelGGL((octo_encode_kernel<B, 1>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((octo_encode_kernel<B, 2>), grid, dim3(256), 0, s, a);
+}
+
+int launch_octo_encode(const OctoArgs& a, int bits, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t groups = (a.n + 15) / 16;
+  if (a.n <= 0) return (int)hipErrorInvalidValue;
+  // the direction table is loaded once per workgroup: at most 8 workgroups
+  // per CU, each looping over groups of 16 vectors
+  const dim3 grid((unsigned)(groups < 2048 ? groups : 2048));
+  switch (bits) {
+    case 2: octo_enc<2>(a, grid, s); break;
+    case 3: octo_enc<3>(a, grid, s); break;
+    case 4: octo_enc<4>(a, grid, s); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+template <int B>
+static void octo_log(const OctoArgs& a, dim3 grid, hipStream_t s) {
+  if (a.group <= 1) hipLaunchKernelGGL((octo_logits_kernel<B, 1>), grid, dim3(256), 0, s, a);
+  else if (a.group <= 4) hipLaunchKernelGGL((octo_logits_kernel<B, 4>), grid, dim3(256), 0, s, a);
+  else if (a.group <= 8) hipLaunchKernelGGL((octo_logits_kernel<B, 8>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((octo_logits_kernel<B, 16>), grid, dim3(256), 0, s, a);
+}
+
+int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t tiles = (a.n + 255) / 256;
+  if (a.n <= 0 || a.heads < 1 || a.heads > 65535 || a.group < 1 || a.group > kOctoMaxGroup ||
+      tiles > 0x7FFFFFFF)
+    return (int)hipErrorInvalidValue;
+  const dim3 grid((unsigned)tiles, (unsigned)a.heads);
+  switch (bits) {
+    case 2: octo_log<2>(a, grid, s); break;
+    case 3: octo_log<3>(a, grid, s); break;
+    case 4: octo_log<4>(a, grid, s); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace tq

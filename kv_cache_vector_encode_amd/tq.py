@@ -10,6 +10,7 @@ directory; if it is missing the import fails loudly (there is no fallback).
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import re
 
@@ -82,6 +83,14 @@ def lib() -> ctypes.CDLL:
             "tq_decompress_kv": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
             "tq_minmax_encode": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]),
             "tq_stream_read": (ctypes.c_int, [_P, ctypes.c_int64, _P, _P]),
+            "tq_octo_record_bytes": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32]),
+            "tq_octo_table_bytes": (ctypes.c_int64, [ctypes.c_int32]),
+            "tq_octo_codebook": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, _P]),
+            "tq_octo_tables": (ctypes.c_int, [ctypes.c_int32, _P, _P]),
+            "tq_octo_encode": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P,
+                                              _P]),
+            "tq_octo_logits": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                              ctypes.c_int32, _P, _P, ctypes.c_float, _P, _P]),
             "tq_minmax_decode": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, ctypes.c_int32, _P, _P]),
             "tq_decode_step": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P, _P, _P, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P,
@@ -280,6 +289,47 @@ def tq_stream_read(src, sink, stream=None):
     """Measurement aid: stream-read the device tensor src (its whole storage)."""
     _check(lib().tq_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)),
            "tq_stream_read")
+
+
+def tq_octo_record_bytes(d: int, bits: int) -> int:
+    n = lib().tq_octo_record_bytes(d, bits)
+    _check(int(n) if n < 0 else 0, "tq_octo_record_bytes")
+    return int(n)
+
+
+def tq_octo_table_bytes(bits: int) -> int:
+    n = lib().tq_octo_table_bytes(bits)
+    _check(int(n) if n < 0 else 0, "tq_octo_table_bytes")
+    return int(n)
+
+
+def tq_octo_codebook(d: int, bits: int):
+    """Host tables: (dirs float32 [4^(bits+1)][4], rho centroids float32 [2^(bits-1)])."""
+    dirs = np.zeros((1 << (2 * (bits + 1)), 4), np.float32)
+    rho = np.zeros(1 << (bits - 1), np.float32)
+    _check(lib().tq_octo_codebook(d, bits, dirs.ctypes.data, rho.ctypes.data), "tq_octo_codebook")
+    return dirs, rho
+
+
+def tq_octo_tables(bits: int, dev_tables, stream=None):
+    """dev_tables: device uint8 tensor of tq_octo_table_bytes(bits) bytes."""
+    _check(lib().tq_octo_tables(bits, _ptr(dev_tables), _stream(stream)), "tq_octo_tables")
+
+
+def tq_octo_encode(X, bits: int, rot, dev_tables, codes, gamma, stream=None):
+    """X: device [n][128] (f32/f16/bf16); codes: uint8 [n][record bytes]; gamma: [n] 16-bit."""
+    _check(lib().tq_octo_encode(_ptr(X), _dtype_code(X), X.shape[0], bits, rot.handle, _ptr(dev_tables),
+                                _ptr(codes), _ptr(gamma), _stream(stream)), "tq_octo_encode")
+
+
+def tq_octo_logits(q, codes, gamma, bits: int, rot, dev_tables, out, scale=None, stream=None):
+    """q: fp32 [heads][group][128]; codes: uint8 [heads][n][record bytes];
+    gamma: [heads][n] 16-bit; out: fp32 [heads][group][n]."""
+    heads, group, _ = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(128)
+    _check(lib().tq_octo_logits(_ptr(q), _ptr(codes), _ptr(gamma), heads, group, codes.shape[1], bits, rot.handle,
+                                _ptr(dev_tables), scale, _ptr(out), _stream(stream)), "tq_octo_logits")
 
 
 def tq_decompress_kv(cache: Cache, slots, K_out, V_out=None, stream=None):

@@ -19,6 +19,10 @@ hipError_t hipGetDeviceCount(int* n) {
 }
 hipError_t hipGetLastError(void) { return hipSuccess; }
 const char* hipGetErrorString(hipError_t) { return "stub"; }
+hipError_t hipMemcpyAsync(void*, const void*, size_t, hipMemcpyKind, hipStream_t) {
+  std::fprintf(stderr, "copy reached without a device\n");
+  std::abort();
+}
 }
 
 namespace tq {
@@ -34,6 +38,8 @@ int launch_reconstruct(const ReconArgs&, void*) { unreachable("reconstruct"); }
 int launch_minmax_encode(const MinmaxArgs&, int, void*) { unreachable("minmax encode"); }
 int launch_minmax_decode(const MinmaxArgs&, int, void*) { unreachable("minmax decode"); }
 int launch_stream_read(const void*, int64_t, uint32_t*, void*) { unreachable("stream read"); }
+int launch_octo_encode(const OctoArgs&, int, void*) { unreachable("triplet encode"); }
+int launch_octo_logits(const OctoArgs&, int, void*) { unreachable("triplet logits"); }
 int decode_slices(int group) { return (group + 7) / 8; }
 }  // namespace tq
 
@@ -128,6 +134,22 @@ int main() {
   CHECK(tq_stream_read(p, int64_t(1) << 30, sink, nullptr) == TQ_ERR_NO_DEVICE);
   CHECK(tq_stream_read(p, -1, sink, nullptr) == TQ_ERR_INVALID_ARG);
   CHECK(tq_stream_read(p, 100, sink, nullptr) == TQ_OK);
+  // triplet codec: tables on the host, every device call stops before the device
+  CHECK(tq_octo_record_bytes(128, 2) == 40 && tq_octo_record_bytes(128, 3) == 56 && tq_octo_record_bytes(128, 4) == 72);
+  CHECK(tq_octo_record_bytes(64, 4) == TQ_ERR_UNSUPPORTED && tq_octo_record_bytes(128, 5) == TQ_ERR_UNSUPPORTED);
+  CHECK(tq_octo_table_bytes(4) == 16384 && tq_octo_table_bytes(1) == TQ_ERR_UNSUPPORTED);
+  for (int b = 2; b <= 4; ++b) {
+    std::vector<float> dirs(size_t(4) << (2 * (b + 1))), rho(size_t(1) << (b - 1));
+    CHECK(tq_octo_codebook(128, b, dirs.data(), rho.data()) == TQ_OK);
+    CHECK(tq_octo_codebook(128, b, nullptr, nullptr) == TQ_OK);
+    CHECK(tq_octo_tables(b, w, nullptr) == TQ_ERR_NO_DEVICE);
+    CHECK(tq_octo_encode(p, TQ_BF16, 7, b, r, p, w, w, nullptr) == TQ_ERR_NO_DEVICE);
+    CHECK(tq_octo_logits(fp, p, p, 8, 8, 100, b, r, p, 0.1f, fp, nullptr) == TQ_ERR_NO_DEVICE);
+  }
+  CHECK(tq_octo_encode(p, TQ_BF16, 7, 4, r, nullptr, w, w, nullptr) == TQ_ERR_INVALID_ARG);
+  CHECK(tq_octo_encode(p, TQ_BF16, -1, 4, r, p, w, w, nullptr) == TQ_ERR_INVALID_ARG);
+  CHECK(tq_octo_logits(fp, p, p, 8, 17, 100, 4, r, p, 0.1f, fp, nullptr) == TQ_ERR_UNSUPPORTED);
+  CHECK(tq_octo_logits(fp, p, p, 0, 8, 100, 4, r, p, 0.1f, fp, nullptr) == TQ_ERR_INVALID_ARG);
   for (tq_cache* cache : caches) tq_cache_destroy(cache);
   tq_rotation_destroy(r);
   std::printf("host sanitize driver: ok\n");

@@ -597,3 +597,134 @@ def test_stream_read_folds_its_loads(device):
             acc ^= int(w[0] ^ w[1] ^ w[2] ^ w[3])
         i += stride
     assert int(sink[0].cpu().numpy().astype(np.uint32)) == acc
+
+
+# ------------------------------------------------------------ triplet codec --
+
+def _octo_tables_dev(bits, device):
+    tb = torch.empty(tq.tq_octo_table_bytes(bits), dtype=torch.uint8, device=device)
+    tq.tq_octo_tables(bits, tb)
+    return tb
+
+
+def _check_octo_codes(rec, g16, x64, bits, seed):
+    """Triplet codes of the GPU against the oracle.  The codes of a triplet
+    are a minimiser over the 3x3 window: equal codes, else codes whose float64
+    error ||t - rho_hat n_hat||^2 is within 2e-6 of the larger of rho^2 and
+    the smallest norm code squared above the oracle's (an fp32 near-tie), or a
+    triplet whose xi or eta lies within 1e-5 of a cell edge (the fp32 map put
+    the window one cell over); fewer than 0.5% of the nonzero triplets off the
+    oracle's pick.  fp16 norms by the usual midpoint rule."""
+    dirs, crho = O.octo_codebooks(128, bits)
+    enc = O.octo_encode(x64, seed, bits, dirs, crho)
+    a, c, k = O.octo_unpack(rec, bits, 128)
+    same = (a == enc["a"]) & (c == enc["c"]) & (k == enc["k"])
+    t = enc["t"]
+    eg = O.octo_triplet_error(t, a, c, k, dirs, crho)
+    rho2 = np.sum(t * t, axis=-1)
+    near_tie = eg <= enc["err"] + 2e-6 * np.maximum(rho2, crho[0] ** 2) + 1e-15
+    rho = np.sqrt(rho2)
+    n = np.where((rho > 0)[..., None], t / np.where(rho > 0, rho, 1.0)[..., None], np.array([0.0, 0.0, 1.0]))
+    xi, eta = O.oct_map(n)
+    nd = 1 << (bits + 1)
+    edge = lambda v: np.abs((v + 1) * nd / 2 - np.round((v + 1) * nd / 2)) < 1e-5 * nd / 2
+    bad = ~same & ~near_tie & ~(edge(xi) | edge(eta))
+    assert not bad.any(), f"{int(bad.sum())} triplet codes are not a minimiser (first at {np.argwhere(bad)[0]})"
+    live = rho > 0          # a zero triplet ties every candidate up to the table's fp32 rounding
+    assert not live.any() or np.mean(~same[live]) < 5e-3, float(np.mean(~same[live]))
+    check_norms(g16, enc["gamma"], what="triplet norms")
+    return int((~same).sum())
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_octo_encode_matches_oracle(device, bits, dt):
+    """1001 keys (62 full groups of 16 and a ragged one) of the outlier-channel
+    key recipe, one of them zero: triplet codes, padding bits and norms."""
+    w = W.DECODE_32K.with_(seq_len=126, num_kv_heads=8)
+    kb, k64 = W.keys(w)
+    n = 1001
+    kb = np.ascontiguousarray(kb.reshape(-1, 128)[:n])
+    x64 = k64.reshape(-1, 128)[:n].copy()
+    kb[5] = 0
+    x64[5] = 0.0
+    if dt == "f32":
+        xf = (x64 * 1.7).astype(np.float32)
+        X, x64 = torch.from_numpy(xf).to(device), xf.astype(np.float64)
+    else:
+        X = to_device(kb, "bf16", device)
+    rot = tq.tq_make_rotation(42, 128)
+    tb = _octo_tables_dev(bits, device)
+    rb = tq.tq_octo_record_bytes(128, bits)
+    codes = torch.full((n, rb), 0xA5, dtype=torch.uint8, device=device)
+    gamma = torch.zeros(n, dtype=torch.int16, device=device)
+    _say("octo encode", bits, dt)
+    tq.tq_octo_encode(X, bits, rot, tb, codes, gamma)
+    torch.cuda.synchronize()
+    rec = codes.cpu().numpy()
+    g16 = gamma.cpu().numpy().view(np.float16)
+    nmis = _check_octo_codes(rec, g16, x64, bits, 42)
+    # bits past the last field are zero (the record is rewritten whole)
+    used = 43 * (3 * bits + 1)
+    allbits = np.unpackbits(rec, axis=1, bitorder="little")
+    assert not allbits[:, used:].any()
+    assert g16[5] == 0
+    _say("  codes off the oracle's pick (near ties):", nmis)
+
+
+@pytest.mark.parametrize("bits,group", [(2, 1), (3, 5), (4, 8), (4, 16)])
+def test_octo_logits_match_oracle(device, bits, group):
+    """Logits straight from the records against the oracle's original-frame
+    q . x_hat, x_hat decoded in float64 from the GPU's own codes and norms:
+    3 heads x 700 keys (two full 256-key tiles and a ragged one)."""
+    heads, n = 3, 700
+    w = W.DECODE_32K.with_(seq_len=700, num_kv_heads=heads, num_q_heads=heads * group)
+    kb, k64 = W.keys(w)                       # [700][heads][128]
+    kb = np.ascontiguousarray(np.swapaxes(kb, 0, 1)).reshape(heads * n, 128)
+    rot = tq.tq_make_rotation(42, 128)
+    tb = _octo_tables_dev(bits, device)
+    rb = tq.tq_octo_record_bytes(128, bits)
+    codes = torch.zeros((heads, n, rb), dtype=torch.uint8, device=device)
+    gamma = torch.zeros((heads, n), dtype=torch.int16, device=device)
+    tq.tq_octo_encode(to_device(kb, "bf16", device), bits, rot, tb, codes.view(heads * n, rb), gamma.view(-1))
+    _, q64 = W.queries(w)                     # [1][heads * group][128]
+    q = torch.from_numpy(q64[0].astype(np.float32).reshape(heads, group, 128)).to(device)
+    out = torch.full((heads, group, n), float("nan"), device=device)
+    scale = 1.0 / math.sqrt(128)
+    _say("octo logits", bits, group)
+    tq.tq_octo_logits(q, codes, gamma, bits, rot, tb, out, scale=scale)
+    torch.cuda.synchronize()
+    dirs, crho = O.octo_codebooks(128, bits)
+    a, c, k = O.octo_unpack(codes.cpu().numpy(), bits, 128)
+    g16 = gamma.cpu().numpy().view(np.float16)
+    xh = O.octo_decode(a, c, k, g16, 42, 128, dirs, crho)      # [heads][n][128]
+    qf = q.cpu().numpy().astype(np.float64)
+    want = scale * np.einsum("hgd,hnd->hgn", qf, xh)
+    csn = scale * np.linalg.norm(qf, axis=-1)[:, :, None] * np.linalg.norm(xh, axis=-1)[:, None, :]
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - want) <= LOGIT_RTOL * csn + 1e-30), float(np.max(np.abs(got - want) / (csn + 1e-30)))
+
+
+def test_octo_small_and_degenerate_sizes(device):
+    """n = 1 and n = 17 (one vector past a group), a zero key whose logits are
+    zero, and a second encode into the same buffers that must overwrite
+    every record bit."""
+    bits = 3
+    rot = tq.tq_make_rotation(7, 128)
+    tb = _octo_tables_dev(bits, device)
+    rb = tq.tq_octo_record_bytes(128, bits)
+    rng = np.random.default_rng(3)
+    for n in (1, 17):
+        x = rng.standard_normal((n, 128)).astype(np.float32)
+        x[0] = 0.0
+        codes = torch.full((n, rb), 0xFF, dtype=torch.uint8, device=device)
+        gamma = torch.full((n,), -1, dtype=torch.int16, device=device)
+        tq.tq_octo_encode(torch.from_numpy(x).to(device), bits, rot, tb, codes, gamma)
+        torch.cuda.synchronize()
+        _check_octo_codes(codes.cpu().numpy(), gamma.cpu().numpy().view(np.float16), x.astype(np.float64), bits, 7)
+        q = torch.from_numpy(rng.standard_normal((1, 2, 128)).astype(np.float32)).to(device)
+        out = torch.full((1, 2, n), float("nan"), device=device)
+        tq.tq_octo_logits(q, codes.view(1, n, rb), gamma.view(1, n), bits, rot, tb, out)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        assert np.all(np.isfinite(o)) and np.all(o[:, :, 0] == 0)

@@ -265,3 +265,49 @@ def test_minmax_argument_checks_happen_before_the_device():
     assert L.tq_minmax_decode(cd, pr + 2, 10, 3, r.handle, tq.TQ_F32, out, None) == tq.TQ_ERR_INVALID_ARG
     assert L.tq_minmax_decode(cd, pr, 10, 1, r.handle, tq.TQ_F32, out, None) == tq.TQ_ERR_UNSUPPORTED
     assert L.tq_minmax_decode(cd, pr, 0, 3, r.handle, tq.TQ_F32, out, None) == tq.TQ_OK
+
+
+# --------------------------------------------------------- triplet codec ----
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_octo_tables_match_oracle(bits):
+    # C++ (double trig and a trig-substitution CDF for rho) against the
+    # oracle (numpy trig, scipy incomplete beta): the fp32 tables agree to
+    # the last bit except where two float64 paths round apart (one ulp)
+    dirs, rho = tq.tq_octo_codebook(128, bits)
+    od, orho = O.octo_codebooks(128, bits)
+    nd = 1 << (bits + 1)
+    assert dirs.shape == (nd * nd, 4) and np.all(dirs[:, 3] == 0)
+    got = dirs[:, :3].reshape(nd, nd, 3)
+    want = od.astype(np.float32)
+    ulp = np.spacing(np.abs(want))
+    assert np.all(np.abs(got - want) <= ulp)
+    assert np.mean(got == want) > 0.99
+    assert np.all(np.abs(rho - orho.astype(np.float32)) <= np.spacing(orho.astype(np.float32)))
+
+
+def test_octo_sizes_and_argument_checks_happen_before_the_device():
+    assert [tq.tq_octo_record_bytes(128, b) for b in (2, 3, 4)] == [40, 56, 72]
+    assert [tq.tq_octo_record_bytes(128, b) for b in (2, 3, 4)] == [O.octo_record_bytes(128, b) for b in (2, 3, 4)]
+    assert [tq.tq_octo_table_bytes(b) for b in (2, 3, 4)] == [1024, 4096, 16384]
+    L = tq.lib()
+    assert L.tq_octo_record_bytes(64, 4) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_octo_table_bytes(5) == tq.TQ_ERR_UNSUPPORTED
+    r = tq.tq_make_rotation(42, 128)
+    r64 = tq.tq_make_rotation(42, 64)
+    X, cd, g, tb, q, out = 0x200000, 0x300000, 0x400000, 0x500000, 0x600000, 0x700000
+    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 4, r64.handle, tb, cd, g, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 1, r.handle, tb, cd, g, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 4, r.handle, None, cd, g, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 4, r.handle, tb + 4, cd, g, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_encode(X, 7, 10, 4, r.handle, tb, cd, g, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_encode(X + 8, tq.TQ_BF16, 10, 4, r.handle, tb, cd, g, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 4, r.handle, tb, cd + 4, g, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_encode(X, tq.TQ_BF16, 0, 4, r.handle, tb, cd, g, None) == tq.TQ_OK
+    assert L.tq_octo_logits(q, cd, g, 8, 17, 100, 4, r.handle, tb, 0.1, out, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_octo_logits(q, cd, g, 0, 8, 100, 4, r.handle, tb, 0.1, out, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_logits(q, cd, g, 8, 8, 100, 4, r.handle, tb, float("nan"), out, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_logits(q + 4, cd, g, 8, 8, 100, 4, r.handle, tb, 0.1, out, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_logits(q, cd, g, 8, 8, 0, 4, r.handle, tb, 0.1, out, None) == tq.TQ_OK
+    assert L.tq_octo_logits(q, cd, g, 8, 8, -1, 4, r.handle, tb, 0.1, out, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_tables(4, None, None) == tq.TQ_ERR_INVALID_ARG
