@@ -295,6 +295,45 @@ def main():
             acc.extend(e[0].elapsed_time(e[1]) for e in ev)
         del mcodes, mparams, mout
 
+    # ---- the octahedral triplet codec: encode every key (head-major, so
+    # that each head's records are contiguous), then the logits of sequence
+    # 0's query group against every key of its KV head straight from the
+    # records.  Outside the timed step, reported beside it.
+    oc_enc_ms, oc_log_ms = [], []
+    if args.only == "both" and not args.no_extras:
+        orot = tq.tq_make_rotation(w.rot_seed, 128)
+        otb = torch.empty(tq.tq_octo_table_bytes(w.bits_k), dtype=torch.uint8, device=dev)
+        tq.tq_octo_tables(w.bits_k, otb, stream)
+        orb = tq.tq_octo_record_bytes(128, w.bits_k)
+        H, G, T = w.num_kv_heads, w.num_q_heads // w.num_kv_heads, w.tokens
+        okh = [s["K"].view(T, H, 128).transpose(0, 1).contiguous() for s in sets]
+        ocodes = [torch.empty((H, T, orb), dtype=torch.uint8, device=dev) for _ in sets]
+        ogam = [torch.empty((H, T), dtype=torch.int16, device=dev) for _ in sets]
+        oq = q[0].float().view(H, G, 128).contiguous()
+        olog = torch.empty((H, G, T), dtype=torch.float32, device=dev)
+        reps = max(5, args.steps // 4)
+
+        def oc_enc(i):
+            j = i % nsets
+            tq.tq_octo_encode(okh[j].view(-1, 128), w.bits_k, orot, otb, ocodes[j].view(-1, orb), ogam[j].view(-1),
+                              stream)
+
+        def oc_log(i):
+            j = i % nsets
+            tq.tq_octo_logits(oq, ocodes[j], ogam[j], w.bits_k, orot, otb, olog, stream=stream)
+
+        for fn, acc in ((oc_enc, oc_enc_ms), (oc_log, oc_log_ms)):
+            for i in range(max(3, nsets)):
+                fn(i)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+            for i in range(reps):
+                ev[i][0].record(stream)
+                fn(i + 3)
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            acc.extend(e[0].elapsed_time(e[1]) for e in ev)
+        del okh, ocodes, ogam, olog
+
     # ---- on-box ceilings: a plain stream read (the library's measurement
     # aid) and a device copy, each over 2 GiB
     onbox = None
@@ -365,6 +404,25 @@ def main():
             "frac": round(db / md_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": db,
             "us_per_launch": round(md_s * 1e6, 2),
             "note": "min/max comparison codec back to bf16, every key and value (two launches)"}
+    if oc_enc_ms:
+        orb = tq.tq_octo_record_bytes(128, w.bits_k)
+        nk = w.tokens * w.num_kv_heads
+        ob = nk * (in_b + orb + 2)                               # bf16 in, record + fp16 norm out
+        oe_s = float(np.mean(oc_enc_ms)) / 1e3
+        kernels["tq_octo_encode"] = {
+            "bound": "hbm", "achieved": round(ob / oe_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(ob / oe_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": ob,
+            "us_per_launch": round(oe_s * 1e6, 2), "vectors_per_s": round(nk / oe_s, 1),
+            "note": "octahedral triplet codec, every key (bits_dir = b+1, bits_norm = b-1); "
+                    "not part of the timed step"}
+        G = w.num_q_heads // w.num_kv_heads
+        lb = nk * (orb + 2) + nk * G * 4 + w.num_q_heads * 128 * 4   # records + norms in, logits out
+        ol_s = float(np.mean(oc_log_ms)) / 1e3
+        kernels["tq_octo_logits"] = {
+            "bound": "hbm", "achieved": round(lb / ol_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(lb / ol_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": lb,
+            "us_per_launch": round(ol_s * 1e6, 2), "keys_per_s": round(nk / ol_s, 1),
+            "note": f"sequence 0's {G} queries per KV head against every key of that head, fp32 logits out"}
     dom = "tq_encode" if enc_s >= dec_s else "tq_decode_attend"
     traffic = None
     tf = os.path.join(ROOT, "profiles", "traffic.json")

@@ -41,9 +41,10 @@ __device__ __forceinline__ int octo_cell(float v, int nd) {
   return min(max(j, 0), nd - 1);
 }
 
-// Equal-area octahedral map of a unit vector: L1 radius sqrt(1 - |z|), the
-// azimuth atan2(|y|, |x|) spread linearly along the diamond edge, the lower
-// hemisphere reflected across the edge.
+// Equal-area octahedral map of the direction of (nx, ny, .) with unit-vector
+// z component nz (nx and ny may carry any common positive scale): L1 radius
+// sqrt(1 - |nz|), the azimuth atan2(|ny|, |nx|) spread linearly along the
+// diamond edge, the lower hemisphere reflected across the edge.
 __device__ __forceinline__ void oct_map(float nx, float ny, float nz, float& xi, float& eta) {
   const float r = sqrtf(fmaxf(1.f - fabsf(nz), 0.f));
   const float phi = atan2f(fabsf(ny), fabsf(nx));
@@ -95,43 +96,38 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
     for (int i = L; i < kOctoTri; i += 16) {
       const float tx = s_y[row][3 * i], ty = s_y[row][3 * i + 1], tz = s_y[row][3 * i + 2];
       const float rho = sqrtf(tx * tx + ty * ty + tz * tz);
-      float nx = 0.f, ny = 0.f, nz = 1.f;
-      if (rho > 0.f) {
-        nx = tx / rho;
-        ny = ty / rho;
-        nz = tz / rho;
-      }
+      // the map needs z / rho only; the azimuth is scale-free
+      const float nz = rho > 0.f ? tz * __builtin_amdgcn_rcpf(rho) : 1.f;
       float xi, eta;
-      oct_map(nx, ny, nz, xi, eta);
+      oct_map(tx, ty, fminf(fmaxf(nz, -1.f), 1.f), xi, eta);
       const int jx = octo_cell(xi, C::kNd), je = octo_cell(eta, C::kNd);
-      float best = INFINITY;
-      uint32_t field = 0;
+      // For a unit direction n_hat the error with the best norm code is
+      // rho^2 + min_k (c_k^2 - 2 c_k p), p = t . n_hat; every c_k > 0, so
+      // that minimum falls as p grows: the 3x3 joint rounding takes the
+      // candidate of largest projection (first on ties), then the norm code
+      // nearest to its p.
+      float best = -INFINITY;
+      int bcell = jx * C::kNd + je;
 #pragma unroll
       for (int da = -1; da <= 1; ++da) {
         const int ca = jx + da;
-        if (ca < 0 || ca >= C::kNd) continue;
 #pragma unroll
         for (int dc = -1; dc <= 1; ++dc) {
           const int cc = je + dc;
-          if (cc < 0 || cc >= C::kNd) continue;
-          const float4 d = s_dir[ca * C::kNd + cc];
+          const bool ok = ca >= 0 && ca < C::kNd && cc >= 0 && cc < C::kNd;
+          const int cell = ok ? ca * C::kNd + cc : 0;
+          const float4 d = s_dir[cell];
           const float p = tx * d.x + ty * d.y + tz * d.z;
-          float cr = a.crho[0];
-          uint32_t k = 0;
-#pragma unroll
-          for (int j = 0; j + 1 < C::kNr; ++j) {
-            const bool up = p > a.trho[j];
-            cr = up ? a.crho[j + 1] : cr;
-            k += up ? 1u : 0u;
-          }
-          const float ex = tx - cr * d.x, ey = ty - cr * d.y, ez = tz - cr * d.z;
-          const float err = ex * ex + ey * ey + ez * ez;
-          if (err < best) {
-            best = err;
-            field = (uint32_t)ca | ((uint32_t)cc << C::kBd) | (k << (2 * C::kBd));
+          if (ok && p > best) {
+            best = p;
+            bcell = cell;
           }
         }
       }
+      uint32_t k = 0;
+#pragma unroll
+      for (int j = 0; j + 1 < C::kNr; ++j) k += best > a.trho[j] ? 1u : 0u;
+      const uint32_t field = (uint32_t)(bcell / C::kNd) | ((uint32_t)(bcell % C::kNd) << C::kBd) | (k << (2 * C::kBd));
       const int bit = i * C::kField, w = bit >> 5, sh = bit & 31;
       atomicOr(&s_rec[row][w], field << sh);
       if (sh + C::kField > 32) atomicOr(&s_rec[row][w + 1], field >> (32 - sh));
@@ -147,22 +143,25 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
 }
 
 // Logits of a head's group of queries against n keys: out = scale * gamma *
-// sum_i rho_hat_i (R q)_i . n_hat_i.  Block (x = tile of 256 keys, y = head).
-// The tile's records are staged in LDS (word stride kWords + 1, odd, so the
-// threads' reads of one field fall in distinct banks); each thread then walks
-// its key's 43 fields in order.
+// sum_i rho_hat_i (R q)_i . n_hat_i.  Block (x = tile of 512 keys, y = head);
+// thread t takes keys t and t + 256 of the tile, so every query read from LDS
+// (a wave-wide broadcast) serves two keys.  The tile's records are staged in
+// LDS (word stride kWords + 1, odd, so the threads' reads of one field fall
+// in distinct banks); each thread walks its keys' 43 fields in order.
+constexpr int kOctoTile = 512;
+
 template <int B, int G>
 __global__ __launch_bounds__(256) void octo_logits_kernel(const OctoArgs a) {
   using C = Octo<B>;
   constexpr int kStride = C::kWords + 1;
   __shared__ float4 s_dir[C::kNd * C::kNd];
   __shared__ float4 s_q[G][kOctoTri + 1];
-  __shared__ uint32_t s_rec[256 * kStride];
+  __shared__ uint32_t s_rec[kOctoTile * kStride];
   __shared__ float s_rho[8];
   const int tid = threadIdx.x;
   const int head = blockIdx.y;
-  const int64_t key0 = (int64_t)blockIdx.x * 256;
-  const int nk = (int)(a.n - key0 < 256 ? a.n - key0 : 256);
+  const int64_t key0 = (int64_t)blockIdx.x * kOctoTile;
+  const int nk = (int)(a.n - key0 < kOctoTile ? a.n - key0 : kOctoTile);
   for (int i = tid; i < C::kNd * C::kNd; i += 256) s_dir[i] = reinterpret_cast<const float4*>(a.dirs)[i];
   if (tid < 8) s_rho[tid] = a.crho[tid];
   {
@@ -171,6 +170,8 @@ __global__ __launch_bounds__(256) void octo_logits_kernel(const OctoArgs a) {
       const int k = i / C::kWords, w = i - k * C::kWords;
       s_rec[k * kStride + w] = src[i];
     }
+    // keys past the end read zero fields (their results are not stored)
+    for (int i = nk * kStride + tid; i < kOctoTile * kStride; i += 256) s_rec[i] = 0u;
   }
   // rotate the group's queries: one per 16-lane row, scaled by the logit scale
   float* qf = reinterpret_cast<float*>(&s_q[0][0]);
@@ -198,30 +199,42 @@ __global__ __launch_bounds__(256) void octo_logits_kernel(const OctoArgs a) {
   }
   __syncthreads();
   if (tid >= nk) return;
-  const int64_t key = key0 + tid;
-  const float gamma = __half2float(__ushort_as_half(a.gamma[(int64_t)head * a.n + key]));
-  const uint32_t* rec = s_rec + tid * kStride;
-  float acc[G];
+  const uint32_t* rec0 = s_rec + tid * kStride;
+  const uint32_t* rec1 = s_rec + (tid + 256) * kStride;
+  float acc0[G], acc1[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) acc[g] = 0.f;
+  for (int g = 0; g < G; ++g) acc0[g] = acc1[g] = 0.f;
 #pragma unroll 2
   for (int i = 0; i < kOctoTri; ++i) {
     const int bit = i * C::kField, wi = bit >> 5, sh = bit & 31;
-    const uint32_t lo = rec[wi], hi = rec[wi + 1];   // word kWords is the pad: read, never used
-    const uint32_t f = (uint32_t)((((uint64_t)hi << 32) | lo) >> sh) & ((1u << C::kField) - 1u);
-    const uint32_t ca = f & (C::kNd - 1), cc = (f >> C::kBd) & (C::kNd - 1), k = f >> (2 * C::kBd);
-    const float4 d = s_dir[ca * C::kNd + cc];
-    const float r = s_rho[k];
-    const float kx = r * d.x, ky = r * d.y, kz = r * d.z;
+    const uint32_t mask = (1u << C::kField) - 1u;
+    // word kWords of a row is the pad: read, never used
+    const uint32_t f0 = (uint32_t)((((uint64_t)rec0[wi + 1] << 32) | rec0[wi]) >> sh) & mask;
+    const uint32_t f1 = (uint32_t)((((uint64_t)rec1[wi + 1] << 32) | rec1[wi]) >> sh) & mask;
+    const float4 d0 = s_dir[(f0 & (C::kNd - 1)) * C::kNd + ((f0 >> C::kBd) & (C::kNd - 1))];
+    const float4 d1 = s_dir[(f1 & (C::kNd - 1)) * C::kNd + ((f1 >> C::kBd) & (C::kNd - 1))];
+    const float r0 = s_rho[f0 >> (2 * C::kBd)], r1 = s_rho[f1 >> (2 * C::kBd)];
+    const float ax = r0 * d0.x, ay = r0 * d0.y, az = r0 * d0.z;
+    const float bx = r1 * d1.x, by = r1 * d1.y, bz = r1 * d1.z;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float4 qv = s_q[g][i];
-      acc[g] = __builtin_fmaf(qv.x, kx, __builtin_fmaf(qv.y, ky, __builtin_fmaf(qv.z, kz, acc[g])));
+      acc0[g] = __builtin_fmaf(qv.x, ax, __builtin_fmaf(qv.y, ay, __builtin_fmaf(qv.z, az, acc0[g])));
+      acc1[g] = __builtin_fmaf(qv.x, bx, __builtin_fmaf(qv.y, by, __builtin_fmaf(qv.z, bz, acc1[g])));
     }
   }
+  const int64_t kA = key0 + tid, kB = kA + 256;
+  const float gA = __half2float(__ushort_as_half(a.gamma[(int64_t)head * a.n + kA]));
+  const bool hasB = tid + 256 < nk;
+  const float gB = hasB ? __half2float(__ushort_as_half(a.gamma[(int64_t)head * a.n + kB])) : 0.f;
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-    if (g < a.group) a.out[((int64_t)head * a.group + g) * a.n + key] = acc[g] * gamma;
+  for (int g = 0; g < G; ++g) {
+    if (g < a.group) {
+      float* o = a.out + ((int64_t)head * a.group + g) * a.n;
+      o[kA] = acc0[g] * gA;
+      if (hasB) o[kB] = acc1[g] * gB;
+    }
+  }
 }
 
 template <int B>
@@ -257,7 +270,7 @@ static void octo_log(const OctoArgs& a, dim3 grid, hipStream_t s) {
 
 int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t tiles = (a.n + 255) / 256;
+  const int64_t tiles = (a.n + kOctoTile - 1) / kOctoTile;
   if (a.n <= 0 || a.heads < 1 || a.heads > 65535 || a.group < 1 || a.group > kOctoMaxGroup ||
       tiles > 0x7FFFFFFF)
     return (int)hipErrorInvalidValue;

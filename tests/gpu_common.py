@@ -126,3 +126,32 @@ def cs_scale(tau, gamma16, qrot_norm, c_norm, rho16=None):
     if rho16 is not None:
         s = s + math.sqrt(math.pi / 2) * np.asarray(rho16, np.float64)
     return tau * np.asarray(gamma16, np.float64) * qrot_norm * s
+
+
+def check_octo_codes(rec, g16, x64, bits, seed):
+    """Triplet codes of the GPU against the oracle.  The codes of a triplet
+    are a minimiser over the 3x3 window: equal codes, else codes whose float64
+    error ||t - rho_hat n_hat||^2 is within 2e-6 of the larger of rho^2 and
+    the smallest norm code squared above the oracle's (an fp32 near-tie), or a
+    triplet whose xi or eta lies within 1e-5 of a cell edge (the fp32 map put
+    the window one cell over); fewer than 0.5% of the nonzero triplets off the
+    oracle's pick.  fp16 norms by the usual midpoint rule."""
+    dirs, crho = O.octo_codebooks(128, bits)
+    enc = O.octo_encode(x64, seed, bits, dirs, crho)
+    a, c, k = O.octo_unpack(rec, bits, 128)
+    same = (a == enc["a"]) & (c == enc["c"]) & (k == enc["k"])
+    t = enc["t"]
+    eg = O.octo_triplet_error(t, a, c, k, dirs, crho)
+    rho2 = np.sum(t * t, axis=-1)
+    near_tie = eg <= enc["err"] + 2e-6 * np.maximum(rho2, crho[0] ** 2) + 1e-15
+    rho = np.sqrt(rho2)
+    n = np.where((rho > 0)[..., None], t / np.where(rho > 0, rho, 1.0)[..., None], np.array([0.0, 0.0, 1.0]))
+    xi, eta = O.oct_map(n)
+    nd = 1 << (bits + 1)
+    edge = lambda v: np.abs((v + 1) * nd / 2 - np.round((v + 1) * nd / 2)) < 1e-5 * nd / 2
+    bad = ~same & ~near_tie & ~(edge(xi) | edge(eta))
+    assert not bad.any(), f"{int(bad.sum())} triplet codes are not a minimiser (first at {np.argwhere(bad)[0]})"
+    live = rho > 0          # a zero triplet ties every candidate up to the table's fp32 rounding
+    assert not live.any() or np.mean(~same[live]) < 5e-3, float(np.mean(~same[live]))
+    check_norms(g16, enc["gamma"], what="triplet norms")
+    return int((~same).sum())

@@ -30,7 +30,7 @@ from kv_cache_vector_encode_amd import tq
 from kv_cache_vector_encode_amd import workloads as W
 from oracle import tq_oracle as O
 
-from gpu_common import (LOGIT_RTOL, OUT_RTOL, check_codes, check_norms, cs_scale, make_cache,
+from gpu_common import (LOGIT_RTOL, OUT_RTOL, check_codes, check_norms, check_octo_codes, cs_scale, make_cache,
                         to_device)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -306,3 +306,38 @@ def test_sweep_logits_1e5_pairs(device, bits):
              f"normalised MSE {mse[qjl] / float(np.mean(s_exact ** 2)):.3e}")
         del cache
     assert mse[True] < 0.85 * mse[False], f"b{bits}: QJL did not lower the logit MSE ({mse})"
+
+
+def test_fullsize_octo_decode_workload(device):
+    w = W.DECODE_32K
+    H, T, G, bits = w.num_kv_heads, w.tokens, w.num_q_heads // w.num_kv_heads, w.bits_k
+    kb, k64 = W.keys(w)                                    # [T][H][128]
+    Kh = to_device(np.ascontiguousarray(np.swapaxes(kb, 0, 1)).reshape(H * T, 128), "bf16", device)
+    rot = tq.tq_make_rotation(w.rot_seed, 128)
+    tb = torch.empty(tq.tq_octo_table_bytes(bits), dtype=torch.uint8, device=device)
+    tq.tq_octo_tables(bits, tb)
+    rb = tq.tq_octo_record_bytes(128, bits)
+    codes = torch.zeros((H, T, rb), dtype=torch.uint8, device=device)
+    gamma = torch.zeros((H, T), dtype=torch.int16, device=device)
+    _say("octo full size: encode", H * T, "keys")
+    tq.tq_octo_encode(Kh, bits, rot, tb, codes.view(-1, rb), gamma.view(-1))
+    _, q64 = W.queries(w)
+    q = torch.from_numpy(q64[0].astype(np.float32).reshape(H, G, 128)).to(device)
+    out = torch.empty((H, G, T), device=device)
+    scale = 1.0 / math.sqrt(128)
+    tq.tq_octo_logits(q, codes, gamma, bits, rot, tb, out, scale=scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2024)
+    hs, ts = rng.integers(0, H, 4096), rng.integers(0, T, 4096)
+    rec = codes.cpu().numpy()[hs, ts]
+    g16 = gamma.cpu().numpy().view(np.float16)[hs, ts]
+    nmis = check_octo_codes(rec, g16, k64[ts, hs], bits, w.rot_seed)
+    dirs, crho = O.octo_codebooks(128, bits)
+    a, c, k = O.octo_unpack(rec, bits, 128)
+    xh = O.octo_decode(a, c, k, g16, w.rot_seed, 128, dirs, crho)           # [4096][128]
+    qf = q.cpu().numpy().astype(np.float64)[hs]                              # [4096][G][128]
+    want = scale * np.einsum("sgd,sd->sg", qf, xh)
+    got = out.cpu().numpy().astype(np.float64)[hs, :, ts]                    # [4096][G]
+    csn = scale * np.linalg.norm(qf, axis=-1) * np.linalg.norm(xh, axis=-1)[:, None]
+    assert np.all(np.abs(got - want) <= LOGIT_RTOL * csn + 1e-30)
+    _say("  sampled codes off the oracle's pick (near ties):", nmis)

@@ -15,7 +15,7 @@ from kv_cache_vector_encode_amd import tq
 from kv_cache_vector_encode_amd import workloads as W
 from oracle import tq_oracle as O
 
-from gpu_common import (LOGIT_RTOL, OUT_RTOL, check_codes, check_norms, cs_scale, encode_gpu,
+from gpu_common import (LOGIT_RTOL, OUT_RTOL, check_codes, check_norms, check_octo_codes, cs_scale, encode_gpu,
                         gpu_codes_at, make_cache, oracle_layout, pool_bytes, to_device)
 
 pytestmark = pytest.mark.gpu
@@ -607,35 +607,6 @@ def _octo_tables_dev(bits, device):
     return tb
 
 
-def _check_octo_codes(rec, g16, x64, bits, seed):
-    """Triplet codes of the GPU against the oracle.  The codes of a triplet
-    are a minimiser over the 3x3 window: equal codes, else codes whose float64
-    error ||t - rho_hat n_hat||^2 is within 2e-6 of the larger of rho^2 and
-    the smallest norm code squared above the oracle's (an fp32 near-tie), or a
-    triplet whose xi or eta lies within 1e-5 of a cell edge (the fp32 map put
-    the window one cell over); fewer than 0.5% of the nonzero triplets off the
-    oracle's pick.  fp16 norms by the usual midpoint rule."""
-    dirs, crho = O.octo_codebooks(128, bits)
-    enc = O.octo_encode(x64, seed, bits, dirs, crho)
-    a, c, k = O.octo_unpack(rec, bits, 128)
-    same = (a == enc["a"]) & (c == enc["c"]) & (k == enc["k"])
-    t = enc["t"]
-    eg = O.octo_triplet_error(t, a, c, k, dirs, crho)
-    rho2 = np.sum(t * t, axis=-1)
-    near_tie = eg <= enc["err"] + 2e-6 * np.maximum(rho2, crho[0] ** 2) + 1e-15
-    rho = np.sqrt(rho2)
-    n = np.where((rho > 0)[..., None], t / np.where(rho > 0, rho, 1.0)[..., None], np.array([0.0, 0.0, 1.0]))
-    xi, eta = O.oct_map(n)
-    nd = 1 << (bits + 1)
-    edge = lambda v: np.abs((v + 1) * nd / 2 - np.round((v + 1) * nd / 2)) < 1e-5 * nd / 2
-    bad = ~same & ~near_tie & ~(edge(xi) | edge(eta))
-    assert not bad.any(), f"{int(bad.sum())} triplet codes are not a minimiser (first at {np.argwhere(bad)[0]})"
-    live = rho > 0          # a zero triplet ties every candidate up to the table's fp32 rounding
-    assert not live.any() or np.mean(~same[live]) < 5e-3, float(np.mean(~same[live]))
-    check_norms(g16, enc["gamma"], what="triplet norms")
-    return int((~same).sum())
-
-
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_octo_encode_matches_oracle(device, bits, dt):
@@ -663,7 +634,7 @@ def test_octo_encode_matches_oracle(device, bits, dt):
     torch.cuda.synchronize()
     rec = codes.cpu().numpy()
     g16 = gamma.cpu().numpy().view(np.float16)
-    nmis = _check_octo_codes(rec, g16, x64, bits, 42)
+    nmis = check_octo_codes(rec, g16, x64, bits, 42)
     # bits past the last field are zero (the record is rewritten whole)
     used = 43 * (3 * bits + 1)
     allbits = np.unpackbits(rec, axis=1, bitorder="little")
@@ -721,7 +692,7 @@ def test_octo_small_and_degenerate_sizes(device):
         gamma = torch.full((n,), -1, dtype=torch.int16, device=device)
         tq.tq_octo_encode(torch.from_numpy(x).to(device), bits, rot, tb, codes, gamma)
         torch.cuda.synchronize()
-        _check_octo_codes(codes.cpu().numpy(), gamma.cpu().numpy().view(np.float16), x.astype(np.float64), bits, 7)
+        check_octo_codes(codes.cpu().numpy(), gamma.cpu().numpy().view(np.float16), x.astype(np.float64), bits, 7)
         q = torch.from_numpy(rng.standard_normal((1, 2, 128)).astype(np.float32)).to(device)
         out = torch.full((1, 2, n), float("nan"), device=device)
         tq.tq_octo_logits(q, codes.view(1, n, rb), gamma.view(1, n), bits, rot, tb, out)
