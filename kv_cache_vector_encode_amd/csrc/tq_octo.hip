@@ -41,13 +41,37 @@ __device__ __forceinline__ int octo_cell(float v, int nd) {
   return min(max(j, 0), nd - 1);
 }
 
+// atan(a) for a in [0, 1] as a * P(a^2), P of degree 7: an odd polynomial
+// fitted here to arctan by iteratively reweighted least squares toward the
+// minimax error (largest error 1.6e-7 rad when evaluated in fp32).
+__device__ __forceinline__ float atan01(float a) {
+  const float s = a * a;
+  float p = -4.054563120e-03f;
+  p = __builtin_fmaf(p, s, 2.186294459e-02f);
+  p = __builtin_fmaf(p, s, -5.591231585e-02f);
+  p = __builtin_fmaf(p, s, 9.642197192e-02f);
+  p = __builtin_fmaf(p, s, -1.390862912e-01f);
+  p = __builtin_fmaf(p, s, 1.994656622e-01f);
+  p = __builtin_fmaf(p, s, -3.332985938e-01f);
+  p = __builtin_fmaf(p, s, 9.999993443e-01f);
+  return a * p;
+}
+
+// atan2(y, x) for y, x >= 0 (0 when both are 0), through atan01 of the
+// smaller over the larger.
+__device__ __forceinline__ float atan2_pos(float y, float x) {
+  const float mx = fmaxf(x, y), mn = fminf(x, y);
+  const float t = atan01(mx > 0.f ? mn * __builtin_amdgcn_rcpf(mx) : 0.f);
+  return y > x ? 1.57079632679489662f - t : t;
+}
+
 // Equal-area octahedral map of the direction of (nx, ny, .) with unit-vector
 // z component nz (nx and ny may carry any common positive scale): L1 radius
 // sqrt(1 - |nz|), the azimuth atan2(|ny|, |nx|) spread linearly along the
 // diamond edge, the lower hemisphere reflected across the edge.
 __device__ __forceinline__ void oct_map(float nx, float ny, float nz, float& xi, float& eta) {
-  const float r = sqrtf(fmaxf(1.f - fabsf(nz), 0.f));
-  const float phi = atan2f(fabsf(ny), fabsf(nx));
+  const float r = __builtin_amdgcn_sqrtf(fmaxf(1.f - fabsf(nz), 0.f));
+  const float phi = atan2_pos(fabsf(ny), fabsf(nx));
   float ae = r * phi * 0.636619772367581343f;   // 2 / pi
   float ax = r - ae;
   if (nz < 0.f) {
@@ -62,12 +86,21 @@ __device__ __forceinline__ void oct_map(float nx, float ny, float nz, float& xi,
 template <int B, int DT>
 __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
   using C = Octo<B>;
-  __shared__ float4 s_dir[C::kNd * C::kNd];
+  // direction table with a one-cell border of NaN entries: the 3x3 window of
+  // any cell is then 9 fixed offsets, and a border candidate's projection is
+  // NaN, which never wins a comparison
+  constexpr int kP = C::kNd + 2;
+  __shared__ float4 s_dir[kP * kP];
   __shared__ float s_y[16][kOctoRowPad];
   __shared__ uint32_t s_rec[16][C::kWords];
   const int tid = threadIdx.x, row = tid >> 4;
   const int L = tid & 15, ell = perm16(L);
-  for (int i = tid; i < C::kNd * C::kNd; i += 256) s_dir[i] = reinterpret_cast<const float4*>(a.dirs)[i];
+  for (int i = tid; i < kP * kP; i += 256) {
+    const int pr = i / kP, pc = i - pr * kP;
+    const bool in = pr >= 1 && pr <= C::kNd && pc >= 1 && pc <= C::kNd;
+    s_dir[i] = in ? reinterpret_cast<const float4*>(a.dirs)[(pr - 1) * C::kNd + (pc - 1)]
+                  : make_float4(NAN, NAN, NAN, NAN);
+  }
   const uint32_t sneg = sign_byte(a.rot, ell);
   uint32_t smask[8];
 #pragma unroll
@@ -77,11 +110,37 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
   }
   const FwhtLane fc = fwht_lane(L);
   const int64_t groups = (a.n + 15) / 16;
+  // the next group's 8 coordinates are loaded while this one is coded
+  constexpr int kRaw = DT == 0 ? 8 : 4;
+  uint32_t raw[kRaw];
+  auto fetch = [&](int64_t grp) {
+    const int64_t vv = grp * 16 + row;
+    const int64_t vc = vv < a.n ? vv : a.n - 1;
+    const uint4* p = DT == 0 ? reinterpret_cast<const uint4*>(static_cast<const float*>(a.src) + vc * kD + 8 * ell)
+                             : reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.src) + vc * kD + 8 * ell);
+    const uint4 r0 = p[0];
+    raw[0] = r0.x; raw[1] = r0.y; raw[2] = r0.z; raw[3] = r0.w;
+    if constexpr (DT == 0) {
+      const uint4 r1 = p[1];
+      raw[4] = r1.x; raw[5] = r1.y; raw[6] = r1.z; raw[7] = r1.w;
+    }
+  };
+  if (blockIdx.x < groups) fetch(blockIdx.x);
   for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
     const int64_t v = grp * 16 + row;
-    const int64_t vc = v < a.n ? v : a.n - 1;
     float x[8];
-    load8_signed<DT>(a.src, vc * kD + 8 * ell, smask, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (DT == 0) {
+        x[i] = __uint_as_float(raw[i] ^ smask[i]);
+      } else {
+        const uint32_t wv = raw[i >> 1] ^ smask[i >> 1];
+        const uint32_t h = (i & 1) ? (wv >> 16) : (wv & 0xFFFFu);
+        if constexpr (DT == 2) x[i] = __uint_as_float(h << 16);
+        else x[i] = __half2float(__ushort_as_half((unsigned short)h));
+      }
+    }
+    if (grp + gridDim.x < groups) fetch(grp + gridDim.x);
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
@@ -95,7 +154,7 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
     __syncthreads();
     for (int i = L; i < kOctoTri; i += 16) {
       const float tx = s_y[row][3 * i], ty = s_y[row][3 * i + 1], tz = s_y[row][3 * i + 2];
-      const float rho = sqrtf(tx * tx + ty * ty + tz * tz);
+      const float rho = __builtin_amdgcn_sqrtf(tx * tx + ty * ty + tz * tz);
       // the map needs z / rho only; the azimuth is scale-free
       const float nz = rho > 0.f ? tz * __builtin_amdgcn_rcpf(rho) : 1.f;
       float xi, eta;
@@ -104,30 +163,25 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
       // For a unit direction n_hat the error with the best norm code is
       // rho^2 + min_k (c_k^2 - 2 c_k p), p = t . n_hat; every c_k > 0, so
       // that minimum falls as p grows: the 3x3 joint rounding takes the
-      // candidate of largest projection (first on ties), then the norm code
-      // nearest to its p.
+      // candidate of largest projection (first on ties, xi-major), then the
+      // norm code nearest to its p.
+      const int base = jx * kP + je;   // padded entry of cell (jx - 1, je - 1)
       float best = -INFINITY;
-      int bcell = jx * C::kNd + je;
+      int bo = 4;
 #pragma unroll
-      for (int da = -1; da <= 1; ++da) {
-        const int ca = jx + da;
-#pragma unroll
-        for (int dc = -1; dc <= 1; ++dc) {
-          const int cc = je + dc;
-          const bool ok = ca >= 0 && ca < C::kNd && cc >= 0 && cc < C::kNd;
-          const int cell = ok ? ca * C::kNd + cc : 0;
-          const float4 d = s_dir[cell];
-          const float p = tx * d.x + ty * d.y + tz * d.z;
-          if (ok && p > best) {
-            best = p;
-            bcell = cell;
-          }
+      for (int o = 0; o < 9; ++o) {
+        const float4 d = s_dir[base + (o / 3) * kP + (o % 3)];
+        const float p = tx * d.x + ty * d.y + tz * d.z;
+        if (p > best) {
+          best = p;
+          bo = o;
         }
       }
+      const int ca = jx - 1 + bo / 3, cc = je - 1 + bo % 3;
       uint32_t k = 0;
 #pragma unroll
       for (int j = 0; j + 1 < C::kNr; ++j) k += best > a.trho[j] ? 1u : 0u;
-      const uint32_t field = (uint32_t)(bcell / C::kNd) | ((uint32_t)(bcell % C::kNd) << C::kBd) | (k << (2 * C::kBd));
+      const uint32_t field = (uint32_t)ca | ((uint32_t)cc << C::kBd) | (k << (2 * C::kBd));
       const int bit = i * C::kField, w = bit >> 5, sh = bit & 31;
       atomicOr(&s_rec[row][w], field << sh);
       if (sh + C::kField > 32) atomicOr(&s_rec[row][w + 1], field >> (32 - sh));
@@ -248,9 +302,10 @@ int launch_octo_encode(const OctoArgs& a, int bits, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t groups = (a.n + 15) / 16;
   if (a.n <= 0) return (int)hipErrorInvalidValue;
-  // the direction table is loaded once per workgroup: at most 8 workgroups
-  // per CU, each looping over groups of 16 vectors
-  const dim3 grid((unsigned)(groups < 2048 ? groups : 2048));
+  // the direction table is loaded once per workgroup: four workgroups per
+  // CU (their LDS fits at every bit width), each looping over groups of 16
+  // vectors, so the whole grid is resident in one round
+  const dim3 grid((unsigned)(groups < 1024 ? groups : 1024));
   switch (bits) {
     case 2: octo_enc<2>(a, grid, s); break;
     case 3: octo_enc<3>(a, grid, s); break;
