@@ -608,7 +608,7 @@ def _octo_tables_dev(bits, device):
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_octo_encode_matches_oracle(device, bits, dt):
     """1001 keys (62 full groups of 16 and a ragged one) of the outlier-channel
     key recipe, one of them zero: triplet codes, padding bits and norms."""
@@ -622,6 +622,9 @@ def test_octo_encode_matches_oracle(device, bits, dt):
     if dt == "f32":
         xf = (x64 * 1.7).astype(np.float32)
         X, x64 = torch.from_numpy(xf).to(device), xf.astype(np.float64)
+    elif dt == "f16":
+        xh = x64.astype(np.float16)
+        X, x64 = torch.from_numpy(xh).to(device), xh.astype(np.float64)
     else:
         X = to_device(kb, "bf16", device)
     rot = tq.tq_make_rotation(42, 128)
