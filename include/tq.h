@@ -317,13 +317,15 @@ int tq_octo_tables(int32_t bits, void* dev_tables, void* hip_stream);
 
 /* Encode n vectors.  X: device [n][128] of dtype (TQ_F32 / TQ_F16 /
  * TQ_BF16), 16-byte aligned; codes: device [n][record bytes], 8-byte aligned;
- * gamma: device [n] fp16; dev_tables: filled by tq_octo_tables(bits).  All
+ * gamma: device [n] fp16; dev_tables / table_bytes: the buffer filled by
+ * tq_octo_tables(bits) and its size, at least tq_octo_table_bytes(bits).  All
  * caller-owned.  Asynchronous on hip_stream.  Errors: TQ_ERR_INVALID_ARG
- * (null pointer, dtype, alignment, n < 0, n >= 2^31), TQ_ERR_UNSUPPORTED
- * (bits, rotation dimension), TQ_ERR_NO_DEVICE, TQ_ERR_HIP. */
+ * (null pointer, dtype, alignment, table too small, n < 0, n >= 2^31),
+ * TQ_ERR_UNSUPPORTED (bits, rotation dimension), TQ_ERR_NO_DEVICE, TQ_ERR_HIP. */
 int tq_octo_encode(const void* X, int32_t dtype, int64_t n, int32_t bits,
-                   const tq_rotation* rot, const void* dev_tables, void* codes,
-                   void* gamma, void* hip_stream);
+                   const tq_rotation* rot, const void* dev_tables,
+                   int64_t table_bytes, void* codes, void* gamma,
+                   void* hip_stream);
 
 /* Logits straight from the records, no reconstructed key written ([P3]
  * Method step 7: the dot product from each triplet's norm and direction):
@@ -335,8 +337,9 @@ int tq_octo_encode(const void* X, int32_t dtype, int64_t n, int32_t bits,
  * TQ_ERR_UNSUPPORTED; a non-finite scale is TQ_ERR_INVALID_ARG). */
 int tq_octo_logits(const float* q, const void* codes, const void* gamma,
                    int32_t heads, int32_t group, int64_t n, int32_t bits,
-                   const tq_rotation* rot, const void* dev_tables, float scale,
-                   float* out, void* hip_stream);
+                   const tq_rotation* rot, const void* dev_tables,
+                   int64_t table_bytes, float scale, float* out,
+                   void* hip_stream);
 
 /* ---------------------------------------------------------------------------
  * Measurement aid (not part of the codec): read `bytes` of device memory at

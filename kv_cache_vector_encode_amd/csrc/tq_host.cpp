@@ -925,11 +925,13 @@ int tq_octo_tables(int32_t bits, void* dev_tables, void* hip_stream) {
 }
 
 namespace {
-int octo_args(int32_t bits, const tq_rotation* rot, const void* dev_tables, tq::OctoArgs& a) {
+int octo_args(int32_t bits, const tq_rotation* rot, const void* dev_tables, int64_t table_bytes, tq::OctoArgs& a) {
   if (!rot || rot->d != tq::kD) return fail(TQ_ERR_UNSUPPORTED, "the triplet codec needs a rotation of dimension 128");
   if (bits < 2 || bits > 4) return fail(TQ_ERR_UNSUPPORTED, "bits must be 2..4");
   if (!dev_tables || reinterpret_cast<uintptr_t>(dev_tables) % 16 != 0)
     return fail(TQ_ERR_INVALID_ARG, "tables must be a 16-byte aligned device buffer filled by tq_octo_tables");
+  if (table_bytes < ((int64_t)16 << (2 * (bits + 1))))
+    return fail(TQ_ERR_INVALID_ARG, "table buffer smaller than tq_octo_table_bytes(bits)");
   std::memset(&a, 0, sizeof(a));
   const OctoTables* t = octo_tables_cached(tq::kD, bits);
   a.dirs = static_cast<const float*>(dev_tables);
@@ -943,11 +945,11 @@ int octo_args(int32_t bits, const tq_rotation* rot, const void* dev_tables, tq::
 }  // namespace
 
 int tq_octo_encode(const void* X, int32_t dtype, int64_t n, int32_t bits, const tq_rotation* rot,
-                   const void* dev_tables, void* codes, void* gamma, void* hip_stream) {
+                   const void* dev_tables, int64_t table_bytes, void* codes, void* gamma, void* hip_stream) {
   if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n < 0");
   if (dtype != TQ_F32 && dtype != TQ_F16 && dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad dtype");
   tq::OctoArgs a;
-  int s = octo_args(bits, rot, dev_tables, a);
+  int s = octo_args(bits, rot, dev_tables, table_bytes, a);
   if (s != TQ_OK) return s;
   if (n == 0) return TQ_OK;
   if (!X || !codes || !gamma) return fail(TQ_ERR_INVALID_ARG, "null pointer");
@@ -968,14 +970,14 @@ int tq_octo_encode(const void* X, int32_t dtype, int64_t n, int32_t bits, const 
 }
 
 int tq_octo_logits(const float* q, const void* codes, const void* gamma, int32_t heads, int32_t group, int64_t n,
-                   int32_t bits, const tq_rotation* rot, const void* dev_tables, float scale, float* out,
-                   void* hip_stream) {
+                   int32_t bits, const tq_rotation* rot, const void* dev_tables, int64_t table_bytes, float scale,
+                   float* out, void* hip_stream) {
   if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n < 0");
   if (heads < 1 || heads > 65535) return fail(TQ_ERR_INVALID_ARG, "heads must be 1..65535");
   if (group < 1 || group > tq::kOctoMaxGroup) return fail(TQ_ERR_UNSUPPORTED, "group must be 1..16");
   if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, "scale must be finite");
   tq::OctoArgs a;
-  int s = octo_args(bits, rot, dev_tables, a);
+  int s = octo_args(bits, rot, dev_tables, table_bytes, a);
   if (s != TQ_OK) return s;
   if (n == 0) return TQ_OK;
   if (!q || !codes || !gamma || !out) return fail(TQ_ERR_INVALID_ARG, "null pointer");

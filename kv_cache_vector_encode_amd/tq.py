@@ -87,10 +87,10 @@ def lib() -> ctypes.CDLL:
             "tq_octo_table_bytes": (ctypes.c_int64, [ctypes.c_int32]),
             "tq_octo_codebook": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, _P]),
             "tq_octo_tables": (ctypes.c_int, [ctypes.c_int32, _P, _P]),
-            "tq_octo_encode": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P,
-                                              _P]),
+            "tq_octo_encode": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P,
+                                              ctypes.c_int64, _P, _P, _P]),
             "tq_octo_logits": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
-                                              ctypes.c_int32, _P, _P, ctypes.c_float, _P, _P]),
+                                              ctypes.c_int32, _P, _P, ctypes.c_int64, ctypes.c_float, _P, _P]),
             "tq_minmax_decode": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, ctypes.c_int32, _P, _P]),
             "tq_decode_step": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P, _P, _P, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P,
@@ -319,7 +319,8 @@ def tq_octo_tables(bits: int, dev_tables, stream=None):
 def tq_octo_encode(X, bits: int, rot, dev_tables, codes, gamma, stream=None):
     """X: device [n][128] (f32/f16/bf16); codes: uint8 [n][record bytes]; gamma: [n] 16-bit."""
     _check(lib().tq_octo_encode(_ptr(X), _dtype_code(X), X.shape[0], bits, rot.handle, _ptr(dev_tables),
-                                _ptr(codes), _ptr(gamma), _stream(stream)), "tq_octo_encode")
+                                dev_tables.numel() * dev_tables.element_size(), _ptr(codes), _ptr(gamma),
+                                _stream(stream)), "tq_octo_encode")
 
 
 def tq_octo_logits(q, codes, gamma, bits: int, rot, dev_tables, out, scale=None, stream=None):
@@ -329,7 +330,8 @@ def tq_octo_logits(q, codes, gamma, bits: int, rot, dev_tables, out, scale=None,
     if scale is None:
         scale = 1.0 / math.sqrt(128)
     _check(lib().tq_octo_logits(_ptr(q), _ptr(codes), _ptr(gamma), heads, group, codes.shape[1], bits, rot.handle,
-                                _ptr(dev_tables), scale, _ptr(out), _stream(stream)), "tq_octo_logits")
+                                _ptr(dev_tables), dev_tables.numel() * dev_tables.element_size(), scale, _ptr(out),
+                                _stream(stream)), "tq_octo_logits")
 
 
 def tq_decompress_kv(cache: Cache, slots, K_out, V_out=None, stream=None):

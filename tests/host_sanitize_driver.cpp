@@ -143,13 +143,14 @@ int main() {
     CHECK(tq_octo_codebook(128, b, dirs.data(), rho.data()) == TQ_OK);
     CHECK(tq_octo_codebook(128, b, nullptr, nullptr) == TQ_OK);
     CHECK(tq_octo_tables(b, w, nullptr) == TQ_ERR_NO_DEVICE);
-    CHECK(tq_octo_encode(p, TQ_BF16, 7, b, r, p, w, w, nullptr) == TQ_ERR_NO_DEVICE);
-    CHECK(tq_octo_logits(fp, p, p, 8, 8, 100, b, r, p, 0.1f, fp, nullptr) == TQ_ERR_NO_DEVICE);
+    CHECK(tq_octo_encode(p, TQ_BF16, 7, b, r, p, 16384, w, w, nullptr) == TQ_ERR_NO_DEVICE);
+    CHECK(tq_octo_logits(fp, p, p, 8, 8, 100, b, r, p, 16384, 0.1f, fp, nullptr) == TQ_ERR_NO_DEVICE);
   }
-  CHECK(tq_octo_encode(p, TQ_BF16, 7, 4, r, nullptr, w, w, nullptr) == TQ_ERR_INVALID_ARG);
-  CHECK(tq_octo_encode(p, TQ_BF16, -1, 4, r, p, w, w, nullptr) == TQ_ERR_INVALID_ARG);
-  CHECK(tq_octo_logits(fp, p, p, 8, 17, 100, 4, r, p, 0.1f, fp, nullptr) == TQ_ERR_UNSUPPORTED);
-  CHECK(tq_octo_logits(fp, p, p, 0, 8, 100, 4, r, p, 0.1f, fp, nullptr) == TQ_ERR_INVALID_ARG);
+  CHECK(tq_octo_encode(p, TQ_BF16, 7, 4, r, nullptr, 16384, w, w, nullptr) == TQ_ERR_INVALID_ARG);
+  CHECK(tq_octo_encode(p, TQ_BF16, -1, 4, r, p, 16384, w, w, nullptr) == TQ_ERR_INVALID_ARG);
+  CHECK(tq_octo_logits(fp, p, p, 8, 17, 100, 4, r, p, 16384, 0.1f, fp, nullptr) == TQ_ERR_UNSUPPORTED);
+  CHECK(tq_octo_logits(fp, p, p, 0, 8, 100, 4, r, p, 16384, 0.1f, fp, nullptr) == TQ_ERR_INVALID_ARG);
+  CHECK(tq_octo_encode(p, TQ_BF16, 7, 4, r, p, 4096, w, w, nullptr) == TQ_ERR_INVALID_ARG);
   for (tq_cache* cache : caches) tq_cache_destroy(cache);
   tq_rotation_destroy(r);
   std::printf("host sanitize driver: ok\n");

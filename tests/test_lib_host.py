@@ -296,18 +296,21 @@ def test_octo_sizes_and_argument_checks_happen_before_the_device():
     r = tq.tq_make_rotation(42, 128)
     r64 = tq.tq_make_rotation(42, 64)
     X, cd, g, tb, q, out = 0x200000, 0x300000, 0x400000, 0x500000, 0x600000, 0x700000
-    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 4, r64.handle, tb, cd, g, None) == tq.TQ_ERR_UNSUPPORTED
-    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 1, r.handle, tb, cd, g, None) == tq.TQ_ERR_UNSUPPORTED
-    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 4, r.handle, None, cd, g, None) == tq.TQ_ERR_INVALID_ARG
-    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 4, r.handle, tb + 4, cd, g, None) == tq.TQ_ERR_INVALID_ARG
-    assert L.tq_octo_encode(X, 7, 10, 4, r.handle, tb, cd, g, None) == tq.TQ_ERR_INVALID_ARG
-    assert L.tq_octo_encode(X + 8, tq.TQ_BF16, 10, 4, r.handle, tb, cd, g, None) == tq.TQ_ERR_INVALID_ARG
-    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 4, r.handle, tb, cd + 4, g, None) == tq.TQ_ERR_INVALID_ARG
-    assert L.tq_octo_encode(X, tq.TQ_BF16, 0, 4, r.handle, tb, cd, g, None) == tq.TQ_OK
-    assert L.tq_octo_logits(q, cd, g, 8, 17, 100, 4, r.handle, tb, 0.1, out, None) == tq.TQ_ERR_UNSUPPORTED
-    assert L.tq_octo_logits(q, cd, g, 0, 8, 100, 4, r.handle, tb, 0.1, out, None) == tq.TQ_ERR_INVALID_ARG
-    assert L.tq_octo_logits(q, cd, g, 8, 8, 100, 4, r.handle, tb, float("nan"), out, None) == tq.TQ_ERR_INVALID_ARG
-    assert L.tq_octo_logits(q + 4, cd, g, 8, 8, 100, 4, r.handle, tb, 0.1, out, None) == tq.TQ_ERR_INVALID_ARG
-    assert L.tq_octo_logits(q, cd, g, 8, 8, 0, 4, r.handle, tb, 0.1, out, None) == tq.TQ_OK
-    assert L.tq_octo_logits(q, cd, g, 8, 8, -1, 4, r.handle, tb, 0.1, out, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 4, r64.handle, tb, 16384, cd, g, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 1, r.handle, tb, 16384, cd, g, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 4, r.handle, None, 16384, cd, g, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 4, r.handle, tb + 4, 16384, cd, g, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_encode(X, 7, 10, 4, r.handle, tb, 16384, cd, g, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_encode(X + 8, tq.TQ_BF16, 10, 4, r.handle, tb, 16384, cd, g, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 4, r.handle, tb, 16384, cd + 4, g, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_encode(X, tq.TQ_BF16, 0, 4, r.handle, tb, 16384, cd, g, None) == tq.TQ_OK
+    assert L.tq_octo_logits(q, cd, g, 8, 17, 100, 4, r.handle, tb, 16384, 0.1, out, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_octo_logits(q, cd, g, 0, 8, 100, 4, r.handle, tb, 16384, 0.1, out, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_logits(q, cd, g, 8, 8, 100, 4, r.handle, tb, 16384, float("nan"), out, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_logits(q + 4, cd, g, 8, 8, 100, 4, r.handle, tb, 16384, 0.1, out, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_logits(q, cd, g, 8, 8, 0, 4, r.handle, tb, 16384, 0.1, out, None) == tq.TQ_OK
+    assert L.tq_octo_logits(q, cd, g, 8, 8, -1, 4, r.handle, tb, 16384, 0.1, out, None) == tq.TQ_ERR_INVALID_ARG
     assert L.tq_octo_tables(4, None, None) == tq.TQ_ERR_INVALID_ARG
+    # a table filled for fewer bits is too small for b = 4
+    assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 4, r.handle, tb, 4096, cd, g, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_logits(q, cd, g, 8, 8, 100, 4, r.handle, tb, 1024, 0.1, out, None) == tq.TQ_ERR_INVALID_ARG
