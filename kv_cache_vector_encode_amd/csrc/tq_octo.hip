@@ -11,10 +11,12 @@
 // Encode: one vector per 16-lane row (the in-register FWHT of the encoder),
 // the rotated coordinates staged in LDS, then each lane takes triplets
 // L, L+16, L+32 of its row; the direction table sits in LDS.
-// Logits: one key per thread; its record is unpacked field by field, each
-// triplet's direction read from the LDS table and scaled by its norm code,
-// and dotted with the group's rotated queries (LDS broadcast).  No K_hat is
-// written anywhere.
+// Logits: for groups of 5..16 queries a matrix-core product of the group's
+// rotated queries with keys decoded in registers (16 keys x 16 queries per
+// tile); for smaller groups a vector kernel that walks each key's fields and
+// dots them with the queries.  Either way each triplet's direction comes
+// from the LDS table scaled by its norm code, and no K_hat is written
+// anywhere.
 
 #include <hip/hip_bf16.h>
 
@@ -22,6 +24,8 @@
 #include "tq_encode_row.h"
 
 namespace tq {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int B>
 struct Octo {
@@ -291,6 +295,97 @@ __global__ __launch_bounds__(256) void octo_logits_kernel(const OctoArgs a) {
   }
 }
 
+// Matrix-core logits for groups of 5..16 queries: per 16-key tile,
+// C[16 keys x 16 queries] += A[16 keys x 4 dims] * B[4 dims x 16 queries]
+// over 33 steps of 4 rotated dims (132: 128 plus the zero pad), fp32 in and
+// out (v_mfma_f32_16x16x4f32).  Lane l holds A[l%16][l/16], B[l/16][l%16]
+// and C[4(l/16)+r][l%16]: the B operands (the rotated, scaled queries) stay
+// in 33 registers for the whole kernel; each A element is one decoded
+// coordinate rho_hat * n_hat[comp] of key l%16, unpacked from the tile's
+// records in LDS.  Each wave takes 16-key tiles in turn.
+constexpr int kOctoMfmaTile = 128;   // keys per workgroup (2 tiles of 16 per wave; 64 / 256 / 512 measured slower)
+
+template <int B>
+__global__ __launch_bounds__(256) void octo_logits_mfma_kernel(const OctoArgs a) {
+  using C = Octo<B>;
+  constexpr int kStride = C::kWords + 1;
+  constexpr int kQd = 132;
+  __shared__ float4 s_dir[C::kNd * C::kNd];
+  __shared__ float s_q[16][kQd];
+  __shared__ uint32_t s_rec[kOctoMfmaTile * kStride];
+  __shared__ float s_rho[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int head = blockIdx.y;
+  const int64_t key0 = (int64_t)blockIdx.x * kOctoMfmaTile;
+  const int nk = (int)(a.n - key0 < kOctoMfmaTile ? a.n - key0 : kOctoMfmaTile);
+  for (int i = tid; i < C::kNd * C::kNd; i += 256) s_dir[i] = reinterpret_cast<const float4*>(a.dirs)[i];
+  if (tid < 8) s_rho[tid] = a.crho[tid];
+  {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.codes + ((int64_t)head * a.n + key0) * C::kRec);
+    for (int i = tid; i < nk * C::kWords; i += 256) {
+      const int k = i / C::kWords, w = i - k * C::kWords;
+      s_rec[k * kStride + w] = src[i];
+    }
+    for (int i = nk * kStride + tid; i < kOctoMfmaTile * kStride; i += 256) s_rec[i] = 0u;
+  }
+  float* qf = &s_q[0][0];
+  for (int i = tid; i < 16 * kQd; i += 256) qf[i] = 0.f;
+  __syncthreads();
+  {
+    const int row = tid >> 4, L = tid & 15, ell = perm16(L);
+    const int rq = row < a.group ? row : 0;
+    const uint32_t sneg = sign_byte(a.rot, ell);
+    uint32_t smask[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) smask[i] = ((sneg >> i) & 1u) << 31;
+    float x[8];
+    load8_signed<0>(a.q, ((int64_t)head * a.group + rq) * kD + 8 * ell, smask, x);
+    const FwhtLane fc = fwht_lane(L);
+    fwht_row(x, fc);
+    const float g = fc.sig * kInvSqrtD * a.scale;
+    if (row < a.group) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_q[row][8 * L + e] = x[e] * g;
+    }
+  }
+  __syncthreads();
+  // The contraction runs over the 44 triplets (the last all-zero in q) in
+  // an order of our choosing: lanes with l/16 = kk take triplets kk, kk+4,
+  // ..., kk+40, one per 3 consecutive steps (components x, y, z), so each
+  // lane decodes a triplet once and feeds it to 3 products.
+  const int col = lane & 15, kk = lane >> 4;
+  float qb[33];
+#pragma unroll
+  for (int m = 0; m < 11; ++m)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      const int dim = 3 * (4 * m + kk) + c;
+      qb[3 * m + c] = dim < kD ? s_q[col][dim] : 0.f;
+    }
+  for (int t = wave; t * 16 < nk; t += 4) {
+    const uint32_t* rec = s_rec + (t * 16 + col) * kStride;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 11; ++m) {
+      const int j = 4 * m + kk;               // triplet 43 reads zero record bits; its q is 0
+      const int bit = j * C::kField, wi = bit >> 5, sh = bit & 31;
+      const uint32_t f = (uint32_t)((((uint64_t)rec[wi + 1] << 32) | rec[wi]) >> sh) & ((1u << C::kField) - 1u);
+      const float4 d = s_dir[(int)(f & (C::kNd - 1)) * C::kNd + (int)((f >> C::kBd) & (C::kNd - 1))];
+      const float r = s_rho[f >> (2 * C::kBd)];
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.x, qb[3 * m], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.y, qb[3 * m + 1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.z, qb[3 * m + 2], acc, 0, 0, 0);
+    }
+    if (col < a.group) {
+      float* o = a.out + ((int64_t)head * a.group + col) * a.n + key0 + t * 16 + 4 * kk;
+      const uint16_t* gp = a.gamma + (int64_t)head * a.n + key0 + t * 16 + 4 * kk;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (t * 16 + 4 * kk + r < nk) o[r] = acc[r] * __half2float(__ushort_as_half(gp[r]));
+    }
+  }
+}
+
 template <int B>
 static void octo_enc(const OctoArgs& a, dim3 grid, hipStream_t s) {
   if (a.dtype == 0) hipLaunchKernelGGL((octo_encode_kernel<B, 0>), grid, dim3(256), 0, s, a);
@@ -318,22 +413,28 @@ int launch_octo_encode(const OctoArgs& a, int bits, void* stream) {
 template <int B>
 static void octo_log(const OctoArgs& a, dim3 grid, hipStream_t s) {
   if (a.group <= 1) hipLaunchKernelGGL((octo_logits_kernel<B, 1>), grid, dim3(256), 0, s, a);
-  else if (a.group <= 4) hipLaunchKernelGGL((octo_logits_kernel<B, 4>), grid, dim3(256), 0, s, a);
-  else if (a.group <= 8) hipLaunchKernelGGL((octo_logits_kernel<B, 8>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((octo_logits_kernel<B, 16>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((octo_logits_kernel<B, 4>), grid, dim3(256), 0, s, a);
+}
+
+template <int B>
+static void octo_log_mfma(const OctoArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((octo_logits_mfma_kernel<B>), grid, dim3(256), 0, s, a);
 }
 
 int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t tiles = (a.n + kOctoTile - 1) / kOctoTile;
-  if (a.n <= 0 || a.heads < 1 || a.heads > 65535 || a.group < 1 || a.group > kOctoMaxGroup ||
-      tiles > 0x7FFFFFFF)
+  if (a.n <= 0 || a.heads < 1 || a.heads > 65535 || a.group < 1 || a.group > kOctoMaxGroup)
     return (int)hipErrorInvalidValue;
+  // groups of up to 4 queries on the vector units; larger groups on the
+  // matrix cores (a 16-query product wastes at most 11 of 16 columns)
+  const bool mfma = a.group > 4;
+  const int64_t tiles = (a.n + (mfma ? kOctoMfmaTile : kOctoTile) - 1) / (mfma ? kOctoMfmaTile : kOctoTile);
+  if (tiles > 0x7FFFFFFF) return (int)hipErrorInvalidValue;
   const dim3 grid((unsigned)tiles, (unsigned)a.heads);
   switch (bits) {
-    case 2: octo_log<2>(a, grid, s); break;
-    case 3: octo_log<3>(a, grid, s); break;
-    case 4: octo_log<4>(a, grid, s); break;
+    case 2: mfma ? octo_log_mfma<2>(a, grid, s) : octo_log<2>(a, grid, s); break;
+    case 3: mfma ? octo_log_mfma<3>(a, grid, s) : octo_log<3>(a, grid, s); break;
+    case 4: mfma ? octo_log_mfma<4>(a, grid, s) : octo_log<4>(a, grid, s); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

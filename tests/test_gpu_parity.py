@@ -646,7 +646,7 @@ def test_octo_encode_matches_oracle(device, bits, dt):
     _say("  codes off the oracle's pick (near ties):", nmis)
 
 
-@pytest.mark.parametrize("bits,group", [(2, 1), (3, 5), (4, 8), (4, 16)])
+@pytest.mark.parametrize("bits,group", [(2, 1), (3, 4), (3, 5), (2, 12), (4, 8), (4, 16)])
 def test_octo_logits_match_oracle(device, bits, group):
     """Logits straight from the records against the oracle's original-frame
     q . x_hat, x_hat decoded in float64 from the GPU's own codes and norms:
