@@ -92,7 +92,8 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
   using C = Octo<B>;
   // direction table with a one-cell border of NaN entries: the 3x3 window of
   // any cell is then 9 fixed offsets, and a border candidate's projection is
-  // NaN, which never wins a comparison
+  // NaN, which never wins a comparison (IEEE compares: the library is built
+  // without fast-math)
   constexpr int kP = C::kNd + 2;
   __shared__ float4 s_dir[kP * kP];
   __shared__ float s_y[16][kOctoRowPad];
