@@ -11,14 +11,14 @@
 // Encode: one vector per 16-lane row (the in-register FWHT of the encoder),
 // the rotated coordinates staged in LDS, then each lane takes triplets
 // L, L+16, L+32 of its row; the direction table sits in LDS.
-// Logits: for groups of 5..16 queries a matrix-core product of the group's
-// rotated queries with keys decoded in registers (16 keys x 16 queries per
-// tile); for smaller groups a vector kernel that walks each key's fields and
-// dots them with the queries.  Either way each triplet's direction comes
-// from the LDS table scaled by its norm code, and no K_hat is written
-// anywhere.
+// Logits: a matrix-core product of the group's rotated queries with keys
+// decoded in registers (16 keys x 16 queries per tile); each triplet's
+// direction comes from the LDS table scaled by its norm code, and no K_hat
+// is written anywhere.
 
 #include <hip/hip_bf16.h>
+
+#include <algorithm>
 
 #include "tq_device.h"
 #include "tq_encode_row.h"
@@ -201,102 +201,8 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
   }
 }
 
-// Logits of a head's group of queries against n keys: out = scale * gamma *
-// sum_i rho_hat_i (R q)_i . n_hat_i.  Block (x = tile of 512 keys, y = head);
-// thread t takes keys t and t + 256 of the tile, so every query read from LDS
-// (a wave-wide broadcast) serves two keys.  The tile's records are staged in
-// LDS (word stride kWords + 1, odd, so the threads' reads of one field fall
-// in distinct banks); each thread walks its keys' 43 fields in order.
-constexpr int kOctoTile = 512;
-
-template <int B, int G>
-__global__ __launch_bounds__(256) void octo_logits_kernel(const OctoArgs a) {
-  using C = Octo<B>;
-  constexpr int kStride = C::kWords + 1;
-  __shared__ float4 s_dir[C::kNd * C::kNd];
-  __shared__ float4 s_q[G][kOctoTri + 1];
-  __shared__ uint32_t s_rec[kOctoTile * kStride];
-  __shared__ float s_rho[8];
-  const int tid = threadIdx.x;
-  const int head = blockIdx.y;
-  const int64_t key0 = (int64_t)blockIdx.x * kOctoTile;
-  const int nk = (int)(a.n - key0 < kOctoTile ? a.n - key0 : kOctoTile);
-  for (int i = tid; i < C::kNd * C::kNd; i += 256) s_dir[i] = reinterpret_cast<const float4*>(a.dirs)[i];
-  if (tid < 8) s_rho[tid] = a.crho[tid];
-  {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.codes + ((int64_t)head * a.n + key0) * C::kRec);
-    for (int i = tid; i < nk * C::kWords; i += 256) {
-      const int k = i / C::kWords, w = i - k * C::kWords;
-      s_rec[k * kStride + w] = src[i];
-    }
-    // keys past the end read zero fields (their results are not stored)
-    for (int i = nk * kStride + tid; i < kOctoTile * kStride; i += 256) s_rec[i] = 0u;
-  }
-  // rotate the group's queries: one per 16-lane row, scaled by the logit scale
-  float* qf = reinterpret_cast<float*>(&s_q[0][0]);
-  for (int i = tid; i < G * (kOctoTri + 1) * 4; i += 256) qf[i] = 0.f;
-  __syncthreads();
-  {
-    const int row = tid >> 4, L = tid & 15, ell = perm16(L);
-    const int rq = row < a.group ? row : 0;
-    const uint32_t sneg = sign_byte(a.rot, ell);
-    uint32_t smask[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) smask[i] = ((sneg >> i) & 1u) << 31;
-    float x[8];
-    load8_signed<0>(a.q, ((int64_t)head * a.group + rq) * kD + 8 * ell, smask, x);
-    const FwhtLane fc = fwht_lane(L);
-    fwht_row(x, fc);
-    const float g = fc.sig * kInvSqrtD * a.scale;
-    if (row < a.group && row < G) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 8 * L + e;
-        qf[(row * (kOctoTri + 1) + j / 3) * 4 + j % 3] = x[e] * g;
-      }
-    }
-  }
-  __syncthreads();
-  if (tid >= nk) return;
-  const uint32_t* rec0 = s_rec + tid * kStride;
-  const uint32_t* rec1 = s_rec + (tid + 256) * kStride;
-  float acc0[G], acc1[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) acc0[g] = acc1[g] = 0.f;
-#pragma unroll 2
-  for (int i = 0; i < kOctoTri; ++i) {
-    const int bit = i * C::kField, wi = bit >> 5, sh = bit & 31;
-    const uint32_t mask = (1u << C::kField) - 1u;
-    // word kWords of a row is the pad: read, never used
-    const uint32_t f0 = (uint32_t)((((uint64_t)rec0[wi + 1] << 32) | rec0[wi]) >> sh) & mask;
-    const uint32_t f1 = (uint32_t)((((uint64_t)rec1[wi + 1] << 32) | rec1[wi]) >> sh) & mask;
-    const float4 d0 = s_dir[(f0 & (C::kNd - 1)) * C::kNd + ((f0 >> C::kBd) & (C::kNd - 1))];
-    const float4 d1 = s_dir[(f1 & (C::kNd - 1)) * C::kNd + ((f1 >> C::kBd) & (C::kNd - 1))];
-    const float r0 = s_rho[f0 >> (2 * C::kBd)], r1 = s_rho[f1 >> (2 * C::kBd)];
-    const float ax = r0 * d0.x, ay = r0 * d0.y, az = r0 * d0.z;
-    const float bx = r1 * d1.x, by = r1 * d1.y, bz = r1 * d1.z;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float4 qv = s_q[g][i];
-      acc0[g] = __builtin_fmaf(qv.x, ax, __builtin_fmaf(qv.y, ay, __builtin_fmaf(qv.z, az, acc0[g])));
-      acc1[g] = __builtin_fmaf(qv.x, bx, __builtin_fmaf(qv.y, by, __builtin_fmaf(qv.z, bz, acc1[g])));
-    }
-  }
-  const int64_t kA = key0 + tid, kB = kA + 256;
-  const float gA = __half2float(__ushort_as_half(a.gamma[(int64_t)head * a.n + kA]));
-  const bool hasB = tid + 256 < nk;
-  const float gB = hasB ? __half2float(__ushort_as_half(a.gamma[(int64_t)head * a.n + kB])) : 0.f;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if (g < a.group) {
-      float* o = a.out + ((int64_t)head * a.group + g) * a.n;
-      o[kA] = acc0[g] * gA;
-      if (hasB) o[kB] = acc1[g] * gB;
-    }
-  }
-}
-
-// Matrix-core logits for groups of 5..16 queries: per 16-key tile,
+// Logits of a head's group of 1..16 queries against n keys: out = scale *
+// gamma * sum_i rho_hat_i (R q)_i . n_hat_i, as a matrix-core product per 16-key tile,
 // C[16 keys x 16 queries] += A[16 keys x 4 dims] * B[4 dims x 16 queries]
 // over 33 steps of 4 rotated dims (132: 128 plus the zero pad), fp32 in and
 // out (v_mfma_f32_16x16x4f32).  Lane l holds A[l%16][l/16], B[l/16][l%16]
@@ -304,7 +210,8 @@ __global__ __launch_bounds__(256) void octo_logits_kernel(const OctoArgs a) {
 // in 33 registers for the whole kernel; each A element is one decoded
 // coordinate rho_hat * n_hat[comp] of key l%16, unpacked from the tile's
 // records in LDS.  Each wave takes 16-key tiles in turn.
-constexpr int kOctoMfmaTile = 128;   // keys per workgroup (2 tiles of 16 per wave; 64 / 256 / 512 measured slower)
+constexpr int kOctoMfmaTile = 128;   // keys per tile step (2 tiles of 16 per wave)
+constexpr int kOctoMfmaWgs = 1024;   // workgroups of a launch (spread over the heads)
 
 template <int B>
 __global__ __launch_bounds__(256) void octo_logits_mfma_kernel(const OctoArgs a) {
@@ -317,18 +224,8 @@ __global__ __launch_bounds__(256) void octo_logits_mfma_kernel(const OctoArgs a)
   __shared__ float s_rho[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y;
-  const int64_t key0 = (int64_t)blockIdx.x * kOctoMfmaTile;
-  const int nk = (int)(a.n - key0 < kOctoMfmaTile ? a.n - key0 : kOctoMfmaTile);
   for (int i = tid; i < C::kNd * C::kNd; i += 256) s_dir[i] = reinterpret_cast<const float4*>(a.dirs)[i];
   if (tid < 8) s_rho[tid] = a.crho[tid];
-  {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.codes + ((int64_t)head * a.n + key0) * C::kRec);
-    for (int i = tid; i < nk * C::kWords; i += 256) {
-      const int k = i / C::kWords, w = i - k * C::kWords;
-      s_rec[k * kStride + w] = src[i];
-    }
-    for (int i = nk * kStride + tid; i < kOctoMfmaTile * kStride; i += 256) s_rec[i] = 0u;
-  }
   float* qf = &s_q[0][0];
   for (int i = tid; i < 16 * kQd; i += 256) qf[i] = 0.f;
   __syncthreads();
@@ -363,6 +260,22 @@ __global__ __launch_bounds__(256) void octo_logits_mfma_kernel(const OctoArgs a)
       const int dim = 3 * (4 * m + kk) + c;
       qb[3 * m + c] = dim < kD ? s_q[col][dim] : 0.f;
     }
+  // the workgroup walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... of
+  // its head, so the table and the queries are set up once per workgroup
+  const int64_t ntiles = (a.n + kOctoMfmaTile - 1) / kOctoMfmaTile;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  const int64_t key0 = tile * kOctoMfmaTile;
+  const int nk = (int)(a.n - key0 < kOctoMfmaTile ? a.n - key0 : kOctoMfmaTile);
+  __syncthreads();   // the previous tile's records are no longer read
+  {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.codes + ((int64_t)head * a.n + key0) * C::kRec);
+    for (int i = tid; i < nk * C::kWords; i += 256) {
+      const int k = i / C::kWords, w = i - k * C::kWords;
+      s_rec[k * kStride + w] = src[i];
+    }
+    for (int i = nk * kStride + tid; i < kOctoMfmaTile * kStride; i += 256) s_rec[i] = 0u;
+  }
+  __syncthreads();
   for (int t = wave; t * 16 < nk; t += 4) {
     const uint32_t* rec = s_rec + (t * 16 + col) * kStride;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -384,6 +297,7 @@ __global__ __launch_bounds__(256) void octo_logits_mfma_kernel(const OctoArgs a)
       for (int r = 0; r < 4; ++r)
         if (t * 16 + 4 * kk + r < nk) o[r] = acc[r] * __half2float(__ushort_as_half(gp[r]));
     }
+  }
   }
 }
 
@@ -412,12 +326,6 @@ int launch_octo_encode(const OctoArgs& a, int bits, void* stream) {
 }
 
 template <int B>
-static void octo_log(const OctoArgs& a, dim3 grid, hipStream_t s) {
-  if (a.group <= 1) hipLaunchKernelGGL((octo_logits_kernel<B, 1>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((octo_logits_kernel<B, 4>), grid, dim3(256), 0, s, a);
-}
-
-template <int B>
 static void octo_log_mfma(const OctoArgs& a, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((octo_logits_mfma_kernel<B>), grid, dim3(256), 0, s, a);
 }
@@ -426,16 +334,15 @@ int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.n <= 0 || a.heads < 1 || a.heads > 65535 || a.group < 1 || a.group > kOctoMaxGroup)
     return (int)hipErrorInvalidValue;
-  // groups of up to 4 queries on the vector units; larger groups on the
-  // matrix cores (a 16-query product wastes at most 11 of 16 columns)
-  const bool mfma = a.group > 4;
-  const int64_t tiles = (a.n + (mfma ? kOctoMfmaTile : kOctoTile) - 1) / (mfma ? kOctoMfmaTile : kOctoTile);
-  if (tiles > 0x7FFFFFFF) return (int)hipErrorInvalidValue;
+  // about kOctoMfmaWgs workgroups in all, each looping over tiles of its
+  // head (the table and the queries are set up once per workgroup)
+  const int64_t tiles = std::min((a.n + kOctoMfmaTile - 1) / kOctoMfmaTile,
+                                 std::max<int64_t>(1, kOctoMfmaWgs / a.heads));
   const dim3 grid((unsigned)tiles, (unsigned)a.heads);
   switch (bits) {
-    case 2: mfma ? octo_log_mfma<2>(a, grid, s) : octo_log<2>(a, grid, s); break;
-    case 3: mfma ? octo_log_mfma<3>(a, grid, s) : octo_log<3>(a, grid, s); break;
-    case 4: mfma ? octo_log_mfma<4>(a, grid, s) : octo_log<4>(a, grid, s); break;
+    case 2: octo_log_mfma<2>(a, grid, s); break;
+    case 3: octo_log_mfma<3>(a, grid, s); break;
+    case 4: octo_log_mfma<4>(a, grid, s); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
