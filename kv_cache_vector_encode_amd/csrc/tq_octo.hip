@@ -261,21 +261,37 @@ __global__ __launch_bounds__(256) void octo_logits_mfma_kernel(const OctoArgs a)
       qb[3 * m + c] = dim < kD ? s_q[col][dim] : 0.f;
     }
   // the workgroup walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... of
-  // its head, so the table and the queries are set up once per workgroup
+  // its head, so the table and the queries are set up once per workgroup;
+  // the next tile's records are loaded into registers while this one is
+  // multiplied
   const int64_t ntiles = (a.n + kOctoMfmaTile - 1) / kOctoMfmaTile;
+  constexpr int kPre = (kOctoMfmaTile * C::kWords + 255) / 256;
+  uint32_t pre[kPre];
+  auto fetch = [&](int64_t tl) {
+    const int64_t k0 = tl * kOctoMfmaTile;
+    const int n_ = (int)(a.n - k0 < kOctoMfmaTile ? a.n - k0 : kOctoMfmaTile);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.codes + ((int64_t)head * a.n + k0) * C::kRec);
+#pragma unroll
+    for (int r = 0; r < kPre; ++r) {
+      const int i = tid + 256 * r;
+      pre[r] = i < n_ * C::kWords ? src[i] : 0u;
+    }
+  };
+  if (blockIdx.x < ntiles) fetch(blockIdx.x);
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
   const int64_t key0 = tile * kOctoMfmaTile;
   const int nk = (int)(a.n - key0 < kOctoMfmaTile ? a.n - key0 : kOctoMfmaTile);
   __syncthreads();   // the previous tile's records are no longer read
-  {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.codes + ((int64_t)head * a.n + key0) * C::kRec);
-    for (int i = tid; i < nk * C::kWords; i += 256) {
+#pragma unroll
+  for (int r = 0; r < kPre; ++r) {
+    const int i = tid + 256 * r;
+    if (i < kOctoMfmaTile * C::kWords) {
       const int k = i / C::kWords, w = i - k * C::kWords;
-      s_rec[k * kStride + w] = src[i];
+      s_rec[k * kStride + w] = pre[r];   // rows past the end hold zeros
     }
-    for (int i = nk * kStride + tid; i < kOctoMfmaTile * kStride; i += 256) s_rec[i] = 0u;
   }
   __syncthreads();
+  if (tile + gridDim.x < ntiles) fetch(tile + gridDim.x);
   for (int t = wave; t * 16 < nk; t += 4) {
     const uint32_t* rec = s_rec + (t * 16 + col) * kStride;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
