@@ -123,8 +123,11 @@ __global__ __launch_bounds__(256) void decompress_kernel(const DecompArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) w[e] = pack16<OUT>(flip(x[2 * e] * gs, sb, 2 * e), flip(x[2 * e + 1] * gs, sb, 2 * e + 1));
     if (v[u] < a.n_vectors) {
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint8_t*>(st.out) + (v[u] * kD + 8 * L) * 2);
-      *dst = make_uint4(w[0], w[1], w[2], w[3]);
+      // the output is written once and not read here: non-temporal stores
+      // (measured 177.9 -> 171.7 us on every key and value of 16 x 8192 tokens)
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint8_t*>(st.out) + (v[u] * kD + 8 * L) * 2);
+      __builtin_nontemporal_store((u32x4){w[0], w[1], w[2], w[3]}, dst);
     }
   }
 }
