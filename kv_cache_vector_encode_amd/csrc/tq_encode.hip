@@ -339,7 +339,10 @@ __device__ __forceinline__ void mx_batch(const EncodeArgs& a, const EncodeStream
     if (g < BITS) {
       const u32x4_t r = *reinterpret_cast<const u32x4_t*>(rec_w + j * kRecStride + 16 * g);
       const Off ro = off + (uint32_t)st.rec_off + __umul24(row, (uint32_t)st.rec_bytes) + 16u * (uint32_t)g;
-      *reinterpret_cast<u32x4_t*>(a.pool + ro) = r;
+      // non-temporal: the cache is read by later launches, not this one
+      // (measured -2% on 2^19 and 2^21 vectors; the same for the 2-byte norm
+      // stores was +3%)
+      __builtin_nontemporal_store(r, reinterpret_cast<u32x4_t*>(a.pool + ro));
     }
     if (g == 0) {
       const Off no = off + (uint32_t)st.norm_off + 2u * row;
