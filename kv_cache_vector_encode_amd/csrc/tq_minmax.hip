@@ -121,7 +121,11 @@ __global__ __launch_bounds__(256) void minmax_decode_kernel(const MinmaxArgs a) 
         w[e] = (uint32_t)__half_as_ushort(__float2half_rn(o[2 * e])) |
                ((uint32_t)__half_as_ushort(__float2half_rn(o[2 * e + 1])) << 16);
     }
-    *reinterpret_cast<uint4*>(static_cast<uint8_t*>(a.out) + (v * kD + 8 * L) * 2) = make_uint4(w[0], w[1], w[2], w[3]);
+    // written once, not read here: non-temporal stores (measured 39.0 -> 34.6 us
+    // on 2^18 vectors, 194 -> 148 us on 2^20)
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store((u32x4){w[0], w[1], w[2], w[3]},
+                                reinterpret_cast<u32x4*>(static_cast<uint8_t*>(a.out) + (v * kD + 8 * L) * 2));
   }
 }
 
