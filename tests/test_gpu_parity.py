@@ -702,3 +702,36 @@ def test_octo_small_and_degenerate_sizes(device):
         torch.cuda.synchronize()
         o = out.cpu().numpy()
         assert np.all(np.isfinite(o)) and np.all(o[:, :, 0] == 0)
+
+
+def test_octo_logits_tile_loop_with_ragged_tail(device):
+    """Many heads leave one workgroup per head, which then walks all of its
+    head's key tiles (128 + 128 + 44 keys here) with the next tile's records
+    prefetched: sampled heads against the oracle."""
+    bits, heads, n, group = 3, 1100, 300, 3
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((heads * n, 128)).astype(np.float32)
+    rot = tq.tq_make_rotation(9, 128)
+    tb = _octo_tables_dev(bits, device)
+    rb = tq.tq_octo_record_bytes(128, bits)
+    codes = torch.zeros((heads, n, rb), dtype=torch.uint8, device=device)
+    gamma = torch.zeros((heads, n), dtype=torch.int16, device=device)
+    tq.tq_octo_encode(torch.from_numpy(x).to(device), bits, rot, tb, codes.view(-1, rb), gamma.view(-1))
+    q = torch.from_numpy(rng.standard_normal((heads, group, 128)).astype(np.float32)).to(device)
+    out = torch.full((heads, group, n), float("nan"), device=device)
+    _say("octo logits tile loop", heads, n)
+    tq.tq_octo_logits(q, codes, gamma, bits, rot, tb, out)
+    torch.cuda.synchronize()
+    got_all = out.cpu().numpy()
+    assert np.all(np.isfinite(got_all))
+    dirs, crho = O.octo_codebooks(128, bits)
+    hs = rng.choice(heads, 24, replace=False)
+    a, c, k = O.octo_unpack(codes.cpu().numpy()[hs], bits, 128)
+    g16 = gamma.cpu().numpy().view(np.float16)[hs]
+    xh = O.octo_decode(a, c, k, g16, 9, 128, dirs, crho)                 # [24][n][128]
+    qf = q.cpu().numpy().astype(np.float64)[hs]
+    scale = 1.0 / math.sqrt(128)
+    want = scale * np.einsum("hgd,hnd->hgn", qf, xh)
+    csn = scale * np.linalg.norm(qf, axis=-1)[:, :, None] * np.linalg.norm(xh, axis=-1)[:, None, :]
+    got = got_all[hs].astype(np.float64)
+    assert np.all(np.abs(got - want) <= LOGIT_RTOL * csn + 1e-30)
