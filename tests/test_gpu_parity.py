@@ -735,3 +735,31 @@ def test_octo_logits_tile_loop_with_ragged_tail(device):
     csn = scale * np.linalg.norm(qf, axis=-1)[:, :, None] * np.linalg.norm(xh, axis=-1)[:, None, :]
     got = got_all[hs].astype(np.float64)
     assert np.all(np.abs(got - want) <= LOGIT_RTOL * csn + 1e-30)
+
+
+def test_octo_encode_scale_edge_cases(device):
+    """The direction codes do not depend on the norm: a vector scaled past the
+    fp16 range (norm stored as 65504) and one scaled far below it (norm
+    rounds to 0 in fp16) take the codes of the unscaled vector, within the
+    near-tie rule; the norms follow the fp16 rule."""
+    bits = 4
+    rng = np.random.default_rng(33)
+    base = rng.standard_normal((32, 128)).astype(np.float32)
+    x = np.concatenate([base, base * np.float32(3e4), base * np.float32(1e-12)])
+    rot = tq.tq_make_rotation(5, 128)
+    tb = _octo_tables_dev(bits, device)
+    rb = tq.tq_octo_record_bytes(128, bits)
+    codes = torch.zeros((96, rb), dtype=torch.uint8, device=device)
+    gamma = torch.zeros(96, dtype=torch.int16, device=device)
+    tq.tq_octo_encode(torch.from_numpy(x).to(device), bits, rot, tb, codes, gamma)
+    torch.cuda.synchronize()
+    rec = codes.cpu().numpy()
+    g16 = gamma.cpu().numpy().view(np.float16)
+    check_octo_codes(rec, g16, x.astype(np.float64), bits, 5)
+    assert np.all(g16[32:64] == np.float16(65504.0))
+    assert np.all(g16[64:] == 0)
+    a0, c0, k0 = O.octo_unpack(rec[:32], bits, 128)
+    for part in (rec[32:64], rec[64:]):
+        a1, c1, k1 = O.octo_unpack(part, bits, 128)
+        same = (a0 == a1) & (c0 == c1) & (k0 == k1)
+        assert same.mean() > 0.99
