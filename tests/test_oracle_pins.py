@@ -293,6 +293,20 @@ def test_fp16_norm_rounding_and_saturation():
     assert np.array_equal(O.fp16_norm(vals).astype(np.float64), want)
 
 
+def test_fp16_sat_rounds_to_nearest_even_and_saturates_both_signs():
+    # fp16 has 11 significant bits: 2049 is a tie between 2048 and 2050 (even
+    # mantissa 2048); 65520 is the tie between 65504 and the overflow, which
+    # round-to-nearest-even would send to infinity: saturation keeps 65504.
+    vals = np.array([0.0, -0.0, 1.5, -2049.0, 2051.0, 65504.0, 65519.0, 65520.0, 1e6, -65520.0, -1e30, 6e-8])
+    want = np.array([0.0, -0.0, 1.5, -2048.0, 2052.0, 65504.0, 65504.0, 65504.0, 65504.0, -65504.0, -65504.0,
+                     5.960464477539063e-08])
+    got = O.fp16_sat(vals)
+    assert got.dtype == np.float16
+    assert np.array_equal(got.astype(np.float64), want)
+    assert np.signbit(got[1]) and not np.signbit(got[0])
+    assert np.all(np.isfinite(got))
+
+
 def test_isotropic_reconstruction_mse_equals_codebook_distortion():
     # R fixed and orthogonal maps Haar-uniform directions to Haar-uniform
     # directions, so E||u - u_hat||^2 = d * D_b exactly in expectation
@@ -412,23 +426,72 @@ def test_qjl_removes_the_inner_product_bias_for_aligned_queries():
         assert abs(bq) < 0.10 * abs(bm), (bits, bm, bq)
 
 
-def test_qjl_mean_error_over_1e5_isotropic_pairs_is_near_zero():
+def test_qjl_mean_error_over_1e5_correlated_pairs_is_near_zero():
+    # q = u + isotropic noise of the same length: <q, u> = 1 on average, so
+    # the MSE-only estimate carries the -d * D_b bias (many standard errors
+    # at 10^5 pairs) and the QJL estimate has to cancel it.  (With q drawn
+    # independently of u both estimates have mean zero, which pins nothing.)
     rng = np.random.default_rng(14)
     c32, _ = O.codebook_fp32(D, 2)
-    errs = []
+    e_mse, e_qjl = [], []
     for trial in range(10):
         g = rng.standard_normal((10000, D))
         u = g / np.linalg.norm(g, axis=1, keepdims=True)
-        q = rng.standard_normal((10000, D))
-        enc = O.encode(u, 77, c32)
-        R = O.rotation_matrix(77, D)
+        q = u + rng.standard_normal((10000, D)) / math.sqrt(D)
+        enc = O.encode(u, 77 + trial, c32)
+        R = O.rotation_matrix(77 + trial, D)
         qr = q @ R.T
         sk = O.qjl_encode(enc["y"], enc["idx"], c32, 300 + trial)
-        est = np.sum(qr * c32[enc["idx"]], axis=1) + O.qjl_dot_estimate(sk["bits"], sk["rho16"], qr, 300 + trial)
-        errs.append(est - np.sum(q * u, axis=1))
-    e = np.concatenate(errs)
-    assert e.size == 100000
-    assert abs(e.mean()) < 4 * e.std() / math.sqrt(e.size)
+        base = np.sum(qr * c32[enc["idx"]], axis=1)
+        corr = O.qjl_dot_estimate(sk["bits"], sk["rho16"], qr, 300 + trial)
+        truth = np.sum(q * u, axis=1)
+        e_mse.append(base - truth)
+        e_qjl.append(base + corr - truth)
+    em, eq = np.concatenate(e_mse), np.concatenate(e_qjl)
+    assert eq.size == 100000
+    se_m, se_q = em.std() / math.sqrt(em.size), eq.std() / math.sqrt(eq.size)
+    bias = -D * O.codebook_distortion(D, 2, c32)
+    assert abs(em.mean() - bias) < 4 * se_m + 0.05 * abs(bias)       # the bias is there ...
+    assert abs(em.mean()) > 20 * se_m
+    assert abs(eq.mean()) < 0.10 * abs(em.mean())                     # ... and QJL removes it
+    assert abs(eq.mean()) < 4 * se_q + 0.02 * abs(bias)
+
+
+def test_qjl_logits_remove_the_score_bias_in_the_original_frame():
+    # logits(q, khat, qjl=...) in the original frame, with the key's own
+    # direction as the query (scaled by a), keys of widely varying norms and
+    # fresh rotation seeds per trial.  Truth: tau * a * gamma.  MSE-only
+    # scores are biased by about -tau * a * gamma * d * D_b; the QJL term
+    # must remove >= 90% of it.  Sketching q instead of R q, dropping gamma16
+    # or tau, or flipping the term's sign all leave (or grow) the bias.
+    rng = np.random.default_rng(19)
+    tau = 1.0 / math.sqrt(D)
+    for bits in (2, 3, 4):
+        c32, _ = O.codebook_fp32(D, bits)
+        rel_mse, rel_qjl = [], []
+        for trial in range(30):
+            n = 120
+            g = rng.standard_normal((n, D))
+            u = g / np.linalg.norm(g, axis=1, keepdims=True)
+            gam = np.exp(rng.uniform(math.log(0.3), math.log(60.0), n))
+            x = u * gam[:, None]
+            seed, seed_q = 2000 + trial, 7000 + trial
+            enc = O.encode(x, seed, c32)
+            sk = O.qjl_encode(enc["y"], enc["idx"], c32, seed_q)
+            khat = O.reconstruct(enc["idx"], enc["gamma16"], seed, c32)
+            qd = dict(bits=sk["bits"], rho16=sk["rho16"], gamma16=enc["gamma16"], seed=seed, seed_qjl=seed_q)
+            for t in range(0, n, 6):            # a query per sampled key, scored against that key
+                a = 2.5
+                q = a * u[t]
+                truth = tau * a * np.float64(enc["gamma16"][t])
+                s0 = O.logits(q, khat[t:t + 1])[0]
+                s1 = O.logits(q, khat[t:t + 1], qjl={k: (v[t:t + 1] if isinstance(v, np.ndarray) else v)
+                                                      for k, v in qd.items()})[0]
+                rel_mse.append((s0 - truth) / truth)
+                rel_qjl.append((s1 - truth) / truth)
+        bm, bq = float(np.mean(rel_mse)), float(np.mean(rel_qjl))
+        assert abs(bm + D * O.codebook_distortion(D, bits, c32)) < 0.1 * abs(bm), (bits, bm)
+        assert abs(bq) < 0.10 * abs(bm), (bits, bm, bq)
 
 
 def test_qjl_sign_bits_and_zero_residual():
