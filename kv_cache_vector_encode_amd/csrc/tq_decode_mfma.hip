@@ -137,7 +137,7 @@ struct Chunk {
   static constexpr int kTailLanes = kRem / 16;
   static constexpr int kSlot = kBytes;
   static constexpr int kDma = kFull + 1;     // copy instructions per chunk
-  static constexpr int kStages = BITS == 2 ? 4 : BITS == 3 ? 3 : 2;
+  static constexpr int kStages = BITS == 2 ? 4 : 2;
   static constexpr int kWaveRing = kStages * 2 * kSlot;
   static_assert(kRem > 0 && kRem % 16 == 0 && kTailLanes <= 64, "tail piece");
   // exec mask of the tail copy
@@ -284,15 +284,21 @@ __device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ush
 // lookup address then fits the instruction's offset field).
 template <int BITS>
 struct DecodeSmem {
-  // Dequantisation tables, one entry per pair of codes (2*BITS bits):
-  //  keys:   (hi | lo << 16, hi | lo << 16) bf16 parts of the two centroids,
-  //  values: f16(c[first]) | f16(c[second]) << 16.
-  // With 4-bit keys the logits take 8-bit integer operands built on the
-  // vector unit (key_planes_b4): no key table, two B-operand steps.
+  // 4-bit codes: the logits take 8-bit integer operands built on the vector
+  // unit (key_planes_b4), no key table; values read a table of code pairs,
+  // f16(c[first]) | f16(c[second]) << 16.
+  // 2- and 3-bit codes: keys and values both read tables of code pairs
+  // (index = the pair's 2b-bit field), entry = the two scaled halves, kept in
+  // 32 copies laid out so that lane L reads copy L % 32 from bank L % 32:
+  // entry e of copy r is word 32 e + r, so any 32 lanes of a read hit 32
+  // different banks whatever codes they look up.
   static constexpr bool kI8 = BITS == 4;
-  static constexpr int kTk = kI8 ? 4 : 2 << (2 * BITS);
-  static constexpr int kTv = 1 << (2 * BITS);
-  static constexpr int kQSteps = kI8 ? 2 : 8;
+  static constexpr bool kTab = BITS <= 3;
+  static constexpr int kRep = 32;
+  static constexpr int kPairs = 1 << (2 * BITS);
+  static constexpr int kTk = kI8 ? 4 : kPairs * kRep;
+  static constexpr int kTv = kI8 ? kPairs : kPairs * kRep;
+  static constexpr int kQSteps = kI8 ? 2 : 4;
   uint32_t tk[kTk];
   uint32_t tv[kTv];
   float qcorr[8], qmult[8];            // 8-bit logits: per-head offset and scale
@@ -302,10 +308,38 @@ struct DecodeSmem {
     alignas(16) uint8_t qs[8 * kD * 4];
     u32x4 qb[kQSteps][64];
   };
-  float cent[2][16];                   // key / value centroids
+  float cent[2][16];                   // key / value centroids (4-bit)
+  uint32_t half[2][16];                // key / value scaled halves (2-, 3-bit)
   float wm[4][8], wl[4][8], ml[2][8];
   alignas(16) uint8_t ring[4 * Chunk<BITS>::kWaveRing];
 };
+
+// Byte address of the table entry for the W-bit field i of a packed
+// little-endian bit string w[] (lane copy r4 = 4 (lane % 32)): the field is
+// moved to bit 7 (entry stride 128 bytes) with one shift or funnel shift and
+// merged with r4 by one and-or.
+template <int W, int N>
+__device__ __forceinline__ uint32_t pair_addr(const uint32_t (&w)[N], int i, uint32_t r4) {
+  const int bit = W * i, wi = bit >> 5, sh = bit & 31;
+  constexpr uint32_t mask = ((1u << W) - 1u) << 7;
+  uint32_t x;
+  if (sh + W <= 32) x = sh >= 7 ? (w[wi] >> (sh - 7)) : (w[wi] << (7 - sh));
+  else x = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], (uint32_t)(sh - 7));
+  return (x & mask) | r4;
+}
+__device__ __forceinline__ uint32_t lds_word(const uint32_t* table, uint32_t byte_addr) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(table) + byte_addr);
+}
+
+// d (lanes of the enabled banks only) = (x of the lane 8 columns away) * m,
+// a 24-bit multiply: with m = 1 or 65536 it places a half in the low or the
+// high half of the word.  Lanes outside BANKS keep d.
+template <int BANKS>
+__device__ __forceinline__ void mul_ror8_banks(uint32_t& d, uint32_t x, uint32_t m) {
+  asm("s_nop 1\n\t"
+      "v_mul_u32_u24_dpp %0, %1, %2 row_ror:8 row_mask:0xf bank_mask:%3"
+      : "+v"(d) : "v"(x), "v"(m), "n"(BANKS));
+}
 
 // Decode step: encode the sequence's new token (keys and values of KV head
 // h) into row `row` of block `blk`, with the vector encoder's row algorithm
@@ -373,7 +407,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
   using C = Chunk<BITS>;
   constexpr int NS = C::kStages;
   __shared__ DecodeSmem<BITS> sm;
-  const uint2* const s_tk2 = reinterpret_cast<const uint2*>(sm.tk);
   const uint32_t* const s_tv2 = sm.tv;
   auto& s_qb = sm.qb;
   auto& s_wm = sm.wm;
@@ -381,8 +414,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
   auto& s_ml = sm.ml;
   uint8_t* const s_ring = sm.ring;
   // per-wave [column][dim] accumulator rows, padded where the ring has room
-  constexpr int kAccRow = 16 * (kD + 4) * 4 <= C::kWaveRing ? kD + 4 : kD;
-  static_assert(16 * kAccRow * 4 <= C::kWaveRing, "wave accumulator must fit in the wave's ring");
+  // (16 columns; 8 on the table path, whose columns of one head are merged
+  // by dim parity)
+  constexpr int kAccRows = DecodeSmem<BITS>::kTab ? 8 : 16;
+  constexpr int kAccRow = kAccRows * (kD + 4) * 4 <= C::kWaveRing ? kD + 4 : kD;
+  static_assert(kAccRows * kAccRow * 4 <= C::kWaveRing, "wave accumulator must fit in the wave's ring");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -479,26 +515,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
   if (!owner) prologue_copies();
 
   constexpr bool kI8 = DecodeSmem<BITS>::kI8;
+  constexpr bool kTab = DecodeSmem<BITS>::kTab;
   constexpr int kLevels = 1 << BITS;
-  // centroids through LDS: one lane writes them from wave-uniform (scalar)
+  // codebooks through LDS: one lane writes them from wave-uniform (scalar)
   // loads of the arguments, so no per-lane argument load is needed
   if (tid == 0) {
 #pragma unroll
     for (int i = 0; i < kLevels; ++i) {
-      sm.cent[0][i] = a.cent_k[i];
-      sm.cent[1][i] = a.cent_v[i];
+      if constexpr (kTab) {
+        sm.half[0][i] = a.f16_k.h[i];
+        sm.half[1][i] = a.f16_v.h[i];
+      } else {
+        sm.cent[0][i] = a.cent_k[i];
+        sm.cent[1][i] = a.cent_v[i];
+      }
     }
   }
   __syncthreads();
-  for (int i = tid; i < (1 << (2 * BITS)); i += 256) {
+  if constexpr (kTab) {
+    // pair tables, 32 copies each (entry e of copy r at word 32 e + r)
     constexpr int mask = kLevels - 1;
-    if constexpr (!kI8) {
-      const float c0 = sm.cent[0][i & mask], c1 = sm.cent[0][i >> BITS];
-      const uint32_t h0 = bf16_bits(c0), h1 = bf16_bits(c1);
-      sm.tk[2 * i] = h0 | (bf16_bits(c0 - bf16_val(h0)) << 16);
-      sm.tk[2 * i + 1] = h1 | (bf16_bits(c1 - bf16_val(h1)) << 16);
+    for (int i = tid; i < DecodeSmem<BITS>::kPairs * DecodeSmem<BITS>::kRep; i += 256) {
+      const int e = i >> 5;
+      sm.tk[i] = sm.half[0][e & mask] | (sm.half[0][e >> BITS] << 16);
+      sm.tv[i] = sm.half[1][e & mask] | (sm.half[1][e >> BITS] << 16);
     }
-    sm.tv[i] = f16_bits(sm.cent[1][i & mask]) | (f16_bits(sm.cent[1][i >> BITS]) << 16);
+  } else {
+    for (int i = tid; i < (1 << (2 * BITS)); i += 256) {
+      constexpr int mask = kLevels - 1;
+      sm.tv[i] = f16_bits(sm.cent[1][i & mask]) | (f16_bits(sm.cent[1][i >> BITS]) << 16);
+    }
   }
   if (wv == 0) wait_pairs_behind<BITS>(owner ? 0 : k_pro);   // the query copy has landed
   __syncthreads();
@@ -562,17 +608,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
           sm.qmult[r] = a.ki8_unit / S;
         }
       } else {
-        // column c -> head c%8, part c/8 (bf16 q_hi, bf16 residual); in the
-        // operand of lane (c, g) at step st, slots (2e, 2e+1) both carry dim
-        // 32g + 4st + e
-        uint32_t* qb = reinterpret_cast<uint32_t*>(s_qb);
+        // column c -> head c%8, part c/8 (f16 q_hi, f16 residual); in the
+        // operand of lane (c, g) at step st, slot s carries dim
+        // 32g + 8st + s, the order of the lane's key codes.  The key table
+        // holds S c, so 1/S is folded in here.
+        uint16_t* qb = reinterpret_cast<uint16_t*>(s_qb);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int d = 8 * p + e, gq = d >> 5, st = (d >> 2) & 7, ee = d & 3;
-          const uint32_t hb = bf16_bits(x[e]);
-          const uint32_t lb = bf16_bits(x[e] - bf16_val(hb));
-          qb[(st * 64 + r + 16 * gq) * 4 + ee] = hb | (hb << 16);
-          qb[(st * 64 + r + 8 + 16 * gq) * 4 + ee] = lb | (lb << 16);
+          const int d = 8 * p + e, gq = d >> 5, st = (d >> 3) & 3, sl = d & 7;
+          const float xv = x[e] * a.f16_k.unscale;
+          const _Float16 hh = (_Float16)xv;
+          const _Float16 hl = (_Float16)(xv - (float)hh);
+          qb[(st * 64 + r + 16 * gq) * 8 + sl] = __builtin_bit_cast(uint16_t, hh);
+          qb[(st * 64 + r + 8 + 16 * gq) * 8 + sl] = __builtin_bit_cast(uint16_t, hl);
         }
       }
     }
@@ -587,9 +635,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
   const bool col_lo = m >= 8;
   const bool col_live = (m & 7) < gcount;
 
-  f32x4 acc[8];
+  // value accumulators: 8-dim tiles t (4-bit), or dim-pair tiles T of the
+  // table path (row R = 4g + r holds dims 8R + 2T and 8R + 2T + 1, by the
+  // column's parity)
+  constexpr int kTiles = kTab ? 4 : 8;
+  f32x4 acc[kTiles];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < kTiles; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const uint32_t r4 = (uint32_t)(lane & 31) << 2;             // this lane's table copy
+  const uint32_t par_shift = col_lo ? 16u : 0u, par_mul = col_lo ? 65536u : 1u;
+  const float v_unscale = a.f16_v.unscale;
   float run_m = -INFINITY, run_l = 0.f;
 
   // logit B operands stay in registers for the whole loop
@@ -639,24 +694,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
 #pragma unroll
         for (int j = 0; j < 4; ++j) fv[X][j] = (float)((c1[X][j] << 8) + c2[X][j]);
     } else {
-      // all table reads first, then the two 8-step product chains interleaved
-      uint32_t kd[2][32];   // (hi | lo) of the lane's 32 codes (dims 32g + i)
-#pragma unroll
-      for (int X = 0; X < 2; ++X)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint2 t = s_tk2[field<2 * BITS>(cur[X].k, i)];
-          kd[X][2 * i] = t.x;
-          kd[X][2 * i + 1] = t.y;
-        }
+      // f16 products over the pair tables: in step st the lane's A operand
+      // holds the scaled halves of its codes 8st .. 8st+7 (dims 32g + 8st +
+      // 0..7 of token row m), one table read per two codes
+      const uint32_t* const tk = sm.tk;
       f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int st = 0; st < 8; ++st)
+      for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int X = 0; X < 2; ++X) {
-          const u32x4 av = {kd[X][4 * st], kd[X][4 * st + 1], kd[X][4 * st + 2], kd[X][4 * st + 3]};
-          c[X] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                         __builtin_bit_cast(bf16x8, qreg[st]), c[X], 0, 0, 0);
+          u32x4 av;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) av[q] = lds_word(tk, pair_addr<2 * BITS>(cur[X].k, 4 * st + q, r4));
+          c[X] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av),
+                                                        __builtin_bit_cast(f16x8, qreg[st]), c[X], 0, 0, 0);
         }
 #pragma unroll
       for (int X = 0; X < 2; ++X)
@@ -675,34 +726,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
       fmac_ror8_4(cs, send, w_par);
     }
     // ---- value operands: table reads issued before the softmax needs them
-    // (tile t = dims 8m+t; the A operand pairs tokens (4g, 4g+1),
-    // (4g+2, 4g+3) of each block)
     u32x4 va[8];
-    {
+    if constexpr (kTab) {
+      // product (block X, tile T) is va[4X + T]: rows = dim pairs (8m + 2T,
+      // 8m + 2T + 1), K slots (2j, 2j + 1) of lane group g = the pair's two
+      // dims of token 4g + j, so one table read gives one operand word
+      const uint32_t* const tv = sm.tv;
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t w1[1] = {cur[X].v[j]};
+            va[4 * X + T][j] = lds_word(tv, pair_addr<2 * BITS>(w1, T, r4));
+          }
+    } else {
+      // tile t = dims 8m+t; the A operand pairs tokens (4g, 4g+1),
+      // (4g+2, 4g+3) of each block
       uint32_t iv[4][8];   // [word pair][t]: code(first) | code(second) << BITS
 #pragma unroll
       for (int X = 0; X < 2; ++X)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const uint32_t wa = cur[X].v[2 * q], wb = cur[X].v[2 * q + 1];
-          if constexpr (BITS == 4) {
-            // whole-word masks: byte k of ze / zo is the pair index of dim
-            // 2k / 2k + 1 (the low nibble from wa, the high one from wb)
-            constexpr uint32_t M = 0x0F0F0F0Fu;
-            uint32_t ze = (wa & M) | ((wb << 4) & ~M);
-            uint32_t zo = ((wa >> 4) & M) | (wb & ~M);
-            // built once: each index below is one byte-select shift of these
-            asm volatile("" : "+v"(ze), "+v"(zo));
+          // whole-word masks: byte k of ze / zo is the pair index of dim
+          // 2k / 2k + 1 (the low nibble from wa, the high one from wb)
+          constexpr uint32_t M = 0x0F0F0F0Fu;
+          uint32_t ze = (wa & M) | ((wb << 4) & ~M);
+          uint32_t zo = ((wa >> 4) & M) | (wb & ~M);
+          // built once: each index below is one byte-select shift of these
+          asm volatile("" : "+v"(ze), "+v"(zo));
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              iv[2 * X + q][2 * k] = (ze >> (8 * k)) & 0xFFu;
-              iv[2 * X + q][2 * k + 1] = (zo >> (8 * k)) & 0xFFu;
-            }
-          } else {
-            constexpr uint32_t mask = (1u << BITS) - 1;
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-              iv[2 * X + q][t] = ((wa >> (BITS * t)) & mask) | (((wb >> (BITS * t)) & mask) << BITS);
+          for (int k = 0; k < 4; ++k) {
+            iv[2 * X + q][2 * k] = (ze >> (8 * k)) & 0xFFu;
+            iv[2 * X + q][2 * k + 1] = (zo >> (8 * k)) & 0xFFu;
           }
         }
 #pragma unroll
@@ -740,38 +798,72 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
       const float alpha = (run_m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(run_m - new_m);
       run_l *= alpha;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+      for (int t = 0; t < kTiles; ++t) acc[t] *= alpha;
     }
     run_m = new_m;
     // all masked: exp2(-inf) = 0; heads past the slice: +inf, so p = 0
     const float mref = !col_live ? INFINITY : (new_m == -INFINITY) ? 0.f : new_m;
-    uint32_t hi[2], lo[2];
+    if constexpr (kTab) {
+      // B of the value product for block X: K slots (2j, 2j + 1) = (token
+      // 4g + j, dim parity 0 / 1); column c takes head c % 8 at parity c / 8,
+      // so its f16(p gamma_v) sits in the low half (c < 8) or the high half
+      // (c >= 8) of slot pair j and the other half is zero.  Lanes hold
+      // their own block's p: the other block's comes from the lane 8 columns
+      // away (block 0 into lanes c >= 8, block 1 into lanes c < 8).
+      uint32_t hv[4];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      float pv[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float p = __builtin_amdgcn_exp2f(s[2 * q + u] - mref);
+      for (int j = 0; j < 4; ++j) {
+        const float p = __builtin_amdgcn_exp2f(s[j] - mref);
         run_l += p;
-        pv[u] = p * (u ? half_hi(gv2[q]) : half_lo(gv2[q]));
+        const float pv = p * ((j & 1) ? half_hi(gv2[j >> 1]) : half_lo(gv2[j >> 1])) * v_unscale;
+        hv[j] = __builtin_bit_cast(uint16_t, (_Float16)pv);
       }
-      // f16(pv) (rounded toward zero) and the f16 of its residual, exact in f32
-      const auto ph = __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]);
-      const auto pl = __builtin_amdgcn_cvt_pkrtz(pv[0] - (float)ph[0], pv[1] - (float)ph[1]);
-      hi[q] = __builtin_bit_cast(uint32_t, ph);
-      lo[q] = __builtin_bit_cast(uint32_t, pl);
-    }
-    // B columns 0..7 take f16(p gamma_v) of both blocks, columns 8..15 its
-    // residual: lanes m < 8 send their block-0 residuals across, lanes m >= 8
-    // their block-1 high parts
-    uint32_t snd[2] = {col_lo ? hi[0] : lo[0], col_lo ? hi[1] : lo[1]}, rcv[2];
-    ror8_2(snd, rcv);
-    const u32x4 pb = col_lo ? (u32x4){rcv[0], rcv[1], lo[0], lo[1]} : (u32x4){hi[0], hi[1], rcv[0], rcv[1]};
-    // ---- values: one product per 8-dim tile
+      u32x4 b0, b1;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, va[t]),
-                                                     __builtin_bit_cast(f16x8, pb), acc[t], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t own = hv[j] << par_shift;
+        uint32_t x0 = own, x1 = own;
+        mul_ror8_banks<0xC>(x0, hv[j], par_mul);
+        mul_ror8_banks<0x3>(x1, hv[j], par_mul);
+        b0[j] = x0;
+        b1[j] = x1;
+      }
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, va[T]),
+                                                       __builtin_bit_cast(f16x8, b0), acc[T], 0, 0, 0);
+        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, va[4 + T]),
+                                                       __builtin_bit_cast(f16x8, b1), acc[T], 0, 0, 0);
+      }
+    } else {
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float pv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float p = __builtin_amdgcn_exp2f(s[2 * q + u] - mref);
+          run_l += p;
+          pv[u] = p * (u ? half_hi(gv2[q]) : half_lo(gv2[q]));
+        }
+        // f16(pv) (rounded toward zero) and the f16 of its residual, exact in f32
+        const auto ph = __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]);
+        const auto pl = __builtin_amdgcn_cvt_pkrtz(pv[0] - (float)ph[0], pv[1] - (float)ph[1]);
+        hi[q] = __builtin_bit_cast(uint32_t, ph);
+        lo[q] = __builtin_bit_cast(uint32_t, pl);
+      }
+      // B columns 0..7 take f16(p gamma_v) of both blocks, columns 8..15 its
+      // residual: lanes m < 8 send their block-0 residuals across, lanes m >= 8
+      // their block-1 high parts
+      uint32_t snd[2] = {col_lo ? hi[0] : lo[0], col_lo ? hi[1] : lo[1]}, rcv[2];
+      ror8_2(snd, rcv);
+      const u32x4 pb = col_lo ? (u32x4){rcv[0], rcv[1], lo[0], lo[1]} : (u32x4){hi[0], hi[1], rcv[0], rcv[1]};
+      // ---- values: one product per 8-dim tile
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, va[t]),
+                                                       __builtin_bit_cast(f16x8, pb), acc[t], 0, 0, 0);
+    }
   };
 
   // ---- main loop: wait for stage k, read it, refill it with pair k + NS
@@ -803,10 +895,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
     s_wl[wave][m] = run_l;
   }
   float* s_acc = reinterpret_cast<float*>(s_ring + wave * C::kWaveRing);   // [column][kAccRow]
+  if constexpr (kTab) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+    for (int T = 0; T < 4; ++T)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s_acc[m * kAccRow + 8 * (4 * g + j) + t] = acc[t][j];
+      for (int j = 0; j < 4; ++j) s_acc[(m & 7) * kAccRow + 8 * (4 * g + j) + 2 * T + (m >> 3)] = acc[T][j];
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_acc[m * kAccRow + 8 * (4 * g + j) + t] = acc[t][j];
+  }
   __syncthreads();
 
   const int64_t nsplit = a.num_splits;
@@ -829,7 +928,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
     for (int w = 0; w < 4; ++w) {
       const float mw = s_wm[w][hd];
       const float* sa = reinterpret_cast<const float*>(s_ring + w * C::kWaveRing);
-      if (mw != -INFINITY) o += __builtin_amdgcn_exp2f(mw - M) * (sa[hd * kAccRow + d] + sa[(hd + 8) * kAccRow + d]);
+      if (mw != -INFINITY)
+        o += __builtin_amdgcn_exp2f(mw - M) * (kTab ? sa[hd * kAccRow + d] : sa[hd * kAccRow + d] + sa[(hd + 8) * kAccRow + d]);
     }
     part_base[((int64_t)split * a.group + g0 + hd) * kPartStride + d] = o;
   }

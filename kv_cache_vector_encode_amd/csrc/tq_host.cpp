@@ -32,6 +32,8 @@ struct tq_cache {
   tq::SignMask rot_qjl;
   tq::CodecTables tab_k;
   tq::CodecTables tab_v;
+  tq::F16Codebook f16_k;      // scaled fp16 forms of the codebooks (decode operands)
+  tq::F16Codebook f16_v;
 };
 
 namespace {
@@ -503,6 +505,60 @@ bool make_key_i8_tables(const float* c, int bits, uint32_t hi[2], uint32_t lo[2]
   return true;
 }
 
+// IEEE half (binary16) bits of a finite double, round to nearest even,
+// with subnormals; |v| past the largest half gives infinity.
+uint16_t half_bits_rne(double v) {
+  const uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  const double a = std::fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  const double m = std::frexp(a, &e);          // a = m 2^e, m in [0.5, 1)
+  int E = e + 14;                               // biased exponent of 1.f 2^(e-1)
+  if (E <= 0) return sign | (uint16_t)std::nearbyint(std::ldexp(a, 24));   // subnormal (1024 = smallest normal)
+  double q = std::nearbyint(std::ldexp(m, 11)); // 11 significant bits, in [1024, 2048]
+  if (q == 2048.0) {
+    q = 1024.0;
+    ++E;
+  }
+  if (E >= 31) return sign | 0x7C00;
+  return sign | (uint16_t)(E << 10) | (uint16_t)((int)q - 1024);
+}
+
+double half_value(uint16_t h) {
+  const int E = (h >> 10) & 31, f = h & 1023;
+  const double v = E == 0 ? std::ldexp((double)f, -24) : std::ldexp(1024.0 + f, E - 25);
+  return (h & 0x8000) ? -v : v;
+}
+
+// fp16 form of a codebook for the matrix-core decode: h_i = half(S c_i),
+// with S = s 2^k, k putting S max|c| in [1, 2) and s in [1, 2) searched
+// over 4096 steps for the least max_i |h_i / S - c_i|.  Half rounding is
+// relative, so a scale at which every centroid lands near a half grid
+// point leaves far less than the plain half-ulp error (d = 128: at most
+// 1.5e-6 for 3-bit and 1.2e-5 for 4-bit codebooks, in the units of the
+// unit-vector coordinates, against 4.3e-5 / 5e-5 at S = 1).
+tq::F16Codebook make_f16_codebook(const float* c, int bits) {
+  tq::F16Codebook f{};
+  const int n = 1 << bits;
+  double cmax = 0.0;
+  for (int i = 0; i < n; ++i) cmax = std::max(cmax, std::fabs((double)c[i]));
+  const double base = cmax > 0.0 ? std::ldexp(1.0, -(int)std::floor(std::log2(cmax))) : 1.0;
+  double best = std::numeric_limits<double>::infinity(), best_s = base;
+  for (int step = 0; step < 4096; ++step) {
+    const double S = base * (1.0 + step / 4096.0);
+    double err = 0.0;
+    for (int i = 0; i < n; ++i) err = std::max(err, std::fabs(half_value(half_bits_rne(S * c[i])) / S - c[i]));
+    if (err < best) {
+      best = err;
+      best_s = S;
+    }
+  }
+  for (int i = 0; i < 16; ++i) f.h[i] = i < n ? half_bits_rne(best_s * c[i]) : 0;
+  f.unscale = (float)(1.0 / best_s);
+  f.max_err = (float)best;
+  return f;
+}
+
 void fill_decode_args(tq::DecodeArgs& a, const void* q, int32_t q_dtype, const tq_cache* c,
                       const int32_t* bt, const int32_t* sl, int32_t num_seqs,
                       int32_t num_q_heads, int32_t max_blocks, float scale) {
@@ -535,6 +591,8 @@ void fill_decode_args(tq::DecodeArgs& a, const void* q, int32_t q_dtype, const t
     a.cent_v[i] = (c->cfg.bits_v > 0 && i < (1 << c->cfg.bits_v)) ? c->tab_v.centroid[i] : 0.f;
   }
   if (!make_key_i8_tables(c->tab_k.centroid, c->cfg.bits_k, a.ki8_hi, a.ki8_lo, &a.ki8_unit)) a.ki8_unit = 0.f;
+  a.f16_k = c->f16_k;
+  a.f16_v = c->f16_v;
 }
 
 }  // namespace
@@ -635,6 +693,8 @@ int tq_cache_create(const tq_cache_config* cfg, void* device_pool, tq_cache** ou
     delete c;
     return s;
   }
+  c->f16_k = make_f16_codebook(c->tab_k.centroid, cfg->bits_k);
+  if (cfg->bits_v > 0) c->f16_v = make_f16_codebook(c->tab_v.centroid, cfg->bits_v);
   *out = c;
   return TQ_OK;
 }

@@ -81,6 +81,15 @@ struct EncodeArgs {
 };
 
 // ---------------------------------------------------------------- decode --
+// A codebook as IEEE half operands of the matrix-core decode: h[i] is the
+// half nearest S c_i for the host-chosen scale S; unscale = 1/S.  max_err =
+// max_i |h_i / S - c_i|.
+struct F16Codebook {
+  uint32_t h[16];
+  float unscale;
+  float max_err;
+};
+
 struct DecodeArgs {
   const void* q;            // [seqs][q_heads][128]
   const uint8_t* pool;
@@ -106,6 +115,8 @@ struct DecodeArgs {
   // mirror's value negated because the codebook is odd-symmetric.
   uint32_t ki8_hi[2], ki8_lo[2];
   float ki8_unit;
+  // 2- and 3-bit keys and values: the codebooks as scaled halves
+  F16Codebook f16_k, f16_v;
 };
 
 // Decode step with append: each sequence's new token (position seq_len - 1,

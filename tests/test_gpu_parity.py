@@ -194,7 +194,10 @@ def _oracle_decode(w, up, bt, lens, q64, group, scale=None, want_out=True):
     return res
 
 
-def _decode_case(device, bits, group, hkv, lens, qjl=False, dtype="bf16", scale=0.0, seed=7):
+def _decode_case(device, bits, group, hkv, lens, qjl=False, dtype="bf16", scale=0.0, seed=7, q_override=None):
+    """dtype: the query dtype handed to the library (bf16 queries of the
+    generator, converted exactly to f16 or f32).  q_override: float64
+    queries [seqs][q_heads][128] passed as f32 instead."""
     nseq = len(lens)
     w = W.DECODE_32K.with_(seed=seed, num_seqs=nseq, seq_len=max(lens), num_kv_heads=hkv,
                            num_q_heads=hkv * group, bits_k=bits, bits_v=bits, qjl=qjl)
@@ -204,6 +207,13 @@ def _decode_case(device, bits, group, hkv, lens, qjl=False, dtype="bf16", scale=
     q = to_device(qb, "bf16", device)
     if dtype == "f32":
         q = q.float()
+    elif dtype == "f16":
+        q = q.float().half()
+        q64 = q.float().cpu().numpy().astype(np.float64)
+    if q_override is not None:
+        q64 = np.asarray(q_override, dtype=np.float64)
+        q = torch.from_numpy(q64.astype(np.float32)).to(device)
+        q64 = q.cpu().numpy().astype(np.float64)
     bt_d = torch.from_numpy(bt).to(device)
     lens_d = torch.tensor(lens, dtype=torch.int32, device=device)
     out = torch.full((nseq, w.num_q_heads, 128), float("nan"), device=device)
@@ -231,12 +241,13 @@ def _decode_case(device, bits, group, hkv, lens, qjl=False, dtype="bf16", scale=
     return out, logits, (q, cache, bt_d, lens_d, ws)
 
 
-def test_decode_attend_longest_split(device, monkeypatch):
+@pytest.mark.parametrize("bits", [3, 4])
+def test_decode_attend_longest_split(device, monkeypatch, bits):
     # 512-block splits (the matrix-core kernel's cap): waves of the first
     # split take 64 block pairs each, so every lane of the per-lane block-
     # table copy is used; 8200 tokens leave a one-block second split.
     monkeypatch.setenv("TQ_BLOCKS_PER_SPLIT", "512")
-    _decode_case(device, 4, 8, 1, [8200, 300])
+    _decode_case(device, bits, 8, 1, [8200, 300])
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
@@ -244,21 +255,49 @@ def test_decode_attend_gqa8(device, bits):
     _decode_case(device, bits, 8, 2, [1, 17, 300, 1029])
 
 
+@pytest.mark.parametrize("bits", [3, 4])
 @pytest.mark.parametrize("group", [1, 2, 5, 16])
-def test_decode_attend_group_sizes(device, group):
-    _decode_case(device, 4, group, 3, [64, 700])
+def test_decode_attend_group_sizes(device, group, bits):
+    _decode_case(device, bits, group, 3, [64, 700])
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("qdt", ["f16", "f32"])
+def test_decode_attend_query_dtypes(device, bits, qdt):
+    # the matrix-core kernel reads fp32 and fp16 queries as well as bf16
+    _decode_case(device, bits, 8, 2, [300, 1029], dtype=qdt)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_decode_attend_concentrated_queries(device, bits):
+    # rotated queries concentrated on one or a few coordinates (q = R^T x
+    # with x a scaled spike plus small noise): the 4-bit logits quantise the
+    # rotated query per head to 16-bit integers, the 2/3-bit ones split it
+    # into f16 high and low parts; both are held to the same 1e-4 bar
+    rng = np.random.default_rng(31 + bits)
+    hkv, group, nseq = 2, 8, 2
+    R = O.rotation_matrix(W.DECODE_32K.rot_seed, 128)
+    x = 1e-3 * rng.standard_normal((nseq, hkv * group, 128))
+    for n in range(nseq):
+        for hq in range(hkv * group):
+            j = rng.integers(0, 128, size=1 + (hq % 3))
+            x[n, hq, j] += rng.choice([-1.0, 1.0], size=j.size) * rng.uniform(4.0, 12.0, size=j.size)
+    q = x @ R                        # R^T x, one row per query head
+    _decode_case(device, bits, group, hkv, [700, 1500], q_override=q)
 
 
 def test_decode_attend_qjl_and_scale(device):
     _decode_case(device, 3, 8, 2, [250, 2100], qjl=True, dtype="f32", scale=0.05)
 
 
-def test_decode_empty_and_long_splits(device):
-    _decode_case(device, 4, 8, 1, [0, 16, 4100, 5])
+@pytest.mark.parametrize("bits", [3, 4])
+def test_decode_empty_and_long_splits(device, bits):
+    _decode_case(device, bits, 8, 1, [0, 16, 4100, 5])
 
 
-def test_decode_is_deterministic(device):
-    out, logits, (q, cache, bt, lens, ws) = _decode_case(device, 4, 8, 2, [900, 1500])
+@pytest.mark.parametrize("bits", [3, 4])
+def test_decode_is_deterministic(device, bits):
+    out, logits, (q, cache, bt, lens, ws) = _decode_case(device, bits, 8, 2, [900, 1500])
     out2 = torch.empty_like(out)
     logits2 = torch.full_like(logits, float("nan"))
     tq.tq_decode_attend(q, cache, bt, lens, out2, ws, logits_out=logits2)
