@@ -95,6 +95,36 @@ __device__ __forceinline__ void ror8_2(const uint32_t (&x)[2], uint32_t (&o)[2])
       : "v"(x[0]), "v"(x[1]));
 }
 
+// Maxima written out: the compiler's fmaxf first canonicalises operands it
+// cannot prove canonical (an extra v_max per operand); the softmax values here
+// are products, exponentials or -inf, never signalling NaNs.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// max of v and v of the lane 8 columns away (the source is a vector-unit
+// result: s_nop 1 gives the DPP read its two wait states)
+__device__ __forceinline__ float vmax_ror8(float v) {
+  float r;
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(v));
+  return r;
+}
+// max over the four 16-lane rows (every lane receives it), with m folded in
+__device__ __forceinline__ float vmax_rows(float v, float m) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float w = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t uw = __float_as_uint(w);
+  const auto b = __builtin_amdgcn_permlane32_swap(uw, uw, false, false);
+  return vmax3(__uint_as_float(b[0]), __uint_as_float(b[1]), m);
+}
+
 // 4-bit key codes -> the two signed-byte planes of their integer centroids,
 // on the vector unit (no table in LDS).  A word holds 8 codes, one nibble
 // each; byte k of the "even" results belongs to the low nibble of byte k of
@@ -146,7 +176,9 @@ struct Chunk {
 };
 
 // Copy one chunk from global memory (wave-uniform src) to LDS byte address
-// lds.  v16 = 16 * lane.  The LDS address of a piece is m0 + instruction
+// lds, with non-temporal loads (the cache is streamed once per call: random
+// 1.6-2.1 KB chunks read 5.6 TB/s plain and 6.2-6.3 TB/s non-temporal in a
+// streaming probe on this chip).  v16 = 16 * lane.  The LDS address of a piece is m0 + instruction
 // offset + lane * 16 (the offset applies to both sides), so every piece
 // lands at its offset inside the slot.  The tail piece runs with the exec
 // mask narrowed to its lanes (inactive lanes neither read nor write); m0 and
@@ -161,10 +193,10 @@ __device__ __forceinline__ void dma_chunk(uint32_t lds, const uint8_t* src, uint
     // offsets vv (see v_slot_src)
     asm volatile(
         "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-        "global_load_lds_dwordx4 %3, %4\n\t"
-        "global_load_lds_dwordx4 %5, %4 offset:1024\n\t"
+        "global_load_lds_dwordx4 %3, %4 nt\n\t"
+        "global_load_lds_dwordx4 %5, %4 offset:1024 nt\n\t"
         "s_mov_b64 %1, exec\n\ts_mov_b32 exec_lo, %6\n\ts_mov_b32 exec_hi, %7\n\ts_nop 1\n\t"
-        "global_load_lds_dwordx4 %3, %4 offset:2048\n\t"
+        "global_load_lds_dwordx4 %3, %4 offset:2048 nt\n\t"
         "s_mov_b64 exec, %1\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(save), "=&s"(esave)
@@ -173,9 +205,9 @@ __device__ __forceinline__ void dma_chunk(uint32_t lds, const uint8_t* src, uint
   } else {
     asm volatile(
         "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-        "global_load_lds_dwordx4 %3, %4\n\t"
+        "global_load_lds_dwordx4 %3, %4 nt\n\t"
         "s_mov_b64 %1, exec\n\ts_mov_b32 exec_lo, %5\n\ts_mov_b32 exec_hi, %6\n\ts_nop 1\n\t"
-        "global_load_lds_dwordx4 %3, %4 offset:1024\n\t"
+        "global_load_lds_dwordx4 %3, %4 offset:1024 nt\n\t"
         "s_mov_b64 exec, %1\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(save), "=&s"(esave)
@@ -720,7 +752,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
       float send[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        cs[j] = fmaf(col_lo ? fv[1][j] : fv[0][j], w_own, kc);
+        cs[j] = kI8 ? fmaf(col_lo ? fv[1][j] : fv[0][j], w_own, kc) : (col_lo ? fv[1][j] : fv[0][j]);
         send[j] = col_lo ? fv[0][j] : fv[1][j];
       }
       fmac_ror8_4(cs, send, w_par);
@@ -788,10 +820,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
       }
     }
     // ---- online softmax over the 32 tokens (per head: both row halves)
-    float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    bm = fmaxf(bm, dpp<kDppRor8>(bm));
-    bm = max_rows(bm);
-    const float new_m = fmaxf(run_m, bm);
+    float bm = vmax(vmax3(s[0], s[1], s[2]), s[3]);
+    bm = vmax_ror8(bm);
+    const float new_m = vmax_rows(bm, run_m);
     // rescale only when some head's running max moved (rare after the first
     // blocks); the accumulators stay in the matrix-core registers otherwise
     if (__builtin_amdgcn_ballot_w64(new_m > run_m) != 0) {
@@ -810,13 +841,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
       // (c >= 8) of slot pair j and the other half is zero.  Lanes hold
       // their own block's p: the other block's comes from the lane 8 columns
       // away (block 0 into lanes c >= 8, block 1 into lanes c < 8).
+      // (the value table holds S_v c: 1/S_v is applied when the waves merge)
       uint32_t hv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float p = __builtin_amdgcn_exp2f(s[j] - mref);
         run_l += p;
-        const float pv = p * ((j & 1) ? half_hi(gv2[j >> 1]) : half_lo(gv2[j >> 1])) * v_unscale;
-        hv[j] = __builtin_bit_cast(uint16_t, (_Float16)pv);
+        const uint32_t gw = gv2[j >> 1];
+        const _Float16 gh = __builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? (gw >> 16) : (gw & 0xFFFFu)));
+        hv[j] = __builtin_bit_cast(uint16_t, (_Float16)(p * (float)gh));
       }
       u32x4 b0, b1;
 #pragma unroll
@@ -868,13 +901,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
 
   // ---- main loop: wait for stage k, read it, refill it with pair k + NS
   // (its block-table entries were fetched one iteration earlier)
+  // The loop is unrolled by the ring depth, so each stage's LDS offset is a
+  // constant of the read instructions.
   const uint8_t* ring = s_ring + wv * C::kWaveRing;
-  for (int k = 0; k < my_n; ++k) {
+  auto step = [&](int k, int u) {   // pair k sits in stage u = k % NS
     wait_pairs_behind<BITS>(min(NS - 1, my_n - 1 - k));
     // the block-table loads are older than the copy just waited for; this
     // keeps their uses below that wait
     asm volatile("" : "+v"(ids0), "+v"(ids1));
-    const uint8_t* st = ring + (k % NS) * 2 * C::kSlot;
+    const uint8_t* st = ring + u * 2 * C::kSlot;
     BlockRegs<BITS> cur[2];
     read_chunk<BITS>(cur[0], st, m, g);
     read_chunk<BITS>(cur[1], st + C::kSlot, m, g);
@@ -884,6 +919,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
       dma_pair(k + NS, (int)__builtin_amdgcn_readlane(ids0, k + NS), (int)__builtin_amdgcn_readlane(ids1, k + NS));
     }
     compute_pair(cur, sb0 + 2 * (wv + 4 * k));
+  };
+  for (int k0 = 0; k0 < my_n; k0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+      if (k0 + u < my_n) step(k0 + u, u);
   }
 
   // ---- merge the 4 waves of the workgroup (each wave's accumulator goes
@@ -899,7 +939,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
 #pragma unroll
     for (int T = 0; T < 4; ++T)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s_acc[(m & 7) * kAccRow + 8 * (4 * g + j) + 2 * T + (m >> 3)] = acc[T][j];
+      for (int j = 0; j < 4; ++j) s_acc[(m & 7) * kAccRow + 8 * (4 * g + j) + 2 * T + (m >> 3)] = acc[T][j] * v_unscale;
   } else {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
