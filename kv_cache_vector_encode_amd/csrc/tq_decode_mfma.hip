@@ -29,8 +29,9 @@
 // lane l's B operand the same way, so only the two must agree on the dims.
 //
 // Work: grid (split, KV-head slice of <= 8 query heads, sequence); 4 waves
-// per workgroup, each takes pairs of 16-token blocks of the split in turn
-// and keeps its own running max / sum / accumulator.
+// per workgroup (4-bit codes) or 8 (2/3-bit codes, whose LDS tables the 8
+// share), each takes pairs of 16-token blocks of the split in turn and keeps
+// its own running max / sum / accumulator.
 //
 // Memory: every wave streams its (block, KV head) chunks into a private ring
 // of LDS stages with global_load_lds (global memory straight to LDS, no
@@ -331,6 +332,9 @@ struct DecodeSmem {
   static constexpr int kTk = kI8 ? 4 : kPairs * kRep;
   static constexpr int kTv = kI8 ? kPairs : kPairs * kRep;
   static constexpr int kQSteps = kI8 ? 2 : 4;
+  // waves per workgroup: the 2/3-bit tables are shared by 8 waves, so two
+  // workgroups (16 waves) fit on a CU
+  static constexpr int kWaves = kTab ? 8 : 4;
   uint32_t tk[kTk];
   uint32_t tv[kTv];
   float qcorr[8], qmult[8];            // 8-bit logits: per-head offset and scale
@@ -342,8 +346,8 @@ struct DecodeSmem {
   };
   float cent[2][16];                   // key / value centroids (4-bit)
   uint32_t half[2][16];                // key / value scaled halves (2-, 3-bit)
-  float wm[4][8], wl[4][8], ml[2][8];
-  alignas(16) uint8_t ring[4 * Chunk<BITS>::kWaveRing];
+  float wm[kWaves][8], wl[kWaves][8], ml[2][8];
+  alignas(16) uint8_t ring[kWaves * Chunk<BITS>::kWaveRing];
 };
 
 // Byte address of the table entry for the W-bit field i of a packed
@@ -434,7 +438,7 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, const AppendAr
 }
 
 template <int BITS, bool LOGITS, bool APPEND>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 3))) void decode_mfma_kernel(
+__global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgpu_waves_per_eu(4))) void decode_mfma_kernel(
     const DecodeArgs a, int ns, int gs, const typename std::conditional<APPEND, AppendArgs, NoAppend>::type ap) {
   using C = Chunk<BITS>;
   constexpr int NS = C::kStages;
@@ -467,10 +471,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
   const int64_t Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const float LOG2E = 1.4426950408889634f;
 
-  // ---- this wave's block pairs: wave, wave + 4, ... of the split
+  // ---- this wave's block pairs: wave, wave + NW, ... of the split
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int npairs = max(0, (sb1 - sb0 + 1) / 2);
-  const int my_n = npairs > wv ? (npairs - wv + 3) / 4 : 0;
+  constexpr int NW = DecodeSmem<BITS>::kWaves;
+  constexpr int NT = 64 * NW;
+  const int my_n = npairs > wv ? (npairs - wv + NW - 1) / NW : 0;
   // the block table is read through the constant address space: it does not
   // change during the launch, so its wave-uniform reads stay scalar loads
   // (the asm around them would otherwise force vector loads and full waits)
@@ -482,7 +488,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
   // block-table entries of this wave's k-th pair (the second block of a
   // split's odd tail re-reads the first; its data is never used)
   auto fetch_pair = [&](int k, int& b0, int& b1) {
-    const int lb = sb0 + 2 * (wv + 4 * k);
+    const int lb = sb0 + 2 * (wv + NW * k);
     b0 = btab[lb];
     b1 = btab[lb + 1 < sb1 ? lb + 1 : lb];
   };
@@ -506,7 +512,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
   uint32_t ids0 = 0, ids1 = 0;
   if (my_n > 0) {
     const int j = min(lane, my_n - 1);
-    const int lb = sb0 + 2 * (wv + 4 * j);
+    const int lb = sb0 + 2 * (wv + NW * j);
     const void* row = a.block_tables + (int64_t)n * a.max_blocks;
     ids0 = load_dword_untracked(row, 4u * (uint32_t)lb);
     ids1 = load_dword_untracked(row, 4u * (uint32_t)(lb + 1 < sb1 ? lb + 1 : lb));
@@ -567,13 +573,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
   if constexpr (kTab) {
     // pair tables, 32 copies each (entry e of copy r at word 32 e + r)
     constexpr int mask = kLevels - 1;
-    for (int i = tid; i < DecodeSmem<BITS>::kPairs * DecodeSmem<BITS>::kRep; i += 256) {
+    for (int i = tid; i < DecodeSmem<BITS>::kPairs * DecodeSmem<BITS>::kRep; i += NT) {
       const int e = i >> 5;
       sm.tk[i] = sm.half[0][e & mask] | (sm.half[0][e >> BITS] << 16);
       sm.tv[i] = sm.half[1][e & mask] | (sm.half[1][e >> BITS] << 16);
     }
   } else {
-    for (int i = tid; i < (1 << (2 * BITS)); i += 256) {
+    for (int i = tid; i < (1 << (2 * BITS)); i += NT) {
       constexpr int mask = kLevels - 1;
       sm.tv[i] = f16_bits(sm.cent[1][i & mask]) | (f16_bits(sm.cent[1][i >> BITS]) << 16);
     }
@@ -918,7 +924,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       dma_pair(k + NS, (int)__builtin_amdgcn_readlane(ids0, k + NS), (int)__builtin_amdgcn_readlane(ids1, k + NS));
     }
-    compute_pair(cur, sb0 + 2 * (wv + 4 * k));
+    compute_pair(cur, sb0 + 2 * (wv + NW * k));
   };
   for (int k0 = 0; k0 < my_n; k0 += NS) {
 #pragma unroll
@@ -926,7 +932,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
       if (k0 + u < my_n) step(k0 + u, u);
   }
 
-  // ---- merge the 4 waves of the workgroup (each wave's accumulator goes
+  // ---- merge the NW waves of the workgroup (each wave's accumulator goes
   // into its own ring, whose copies have all been waited for)
   run_l = sum_rows(run_l);
   run_l += dpp<kDppRor8>(run_l);   // the two row halves hold the pair's two blocks
@@ -952,20 +958,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BITS == 4 ?
   float* part_base = a.partials + (((int64_t)n * Hkv + h) * nsplit) * a.group * kPartStride;
   if (tid < 8) {
     float M = -INFINITY;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_wm[w][tid]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_wm[w][tid]);
     float L = 0.f;
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < NW; ++w)
       if (s_wm[w][tid] != -INFINITY) L += s_wl[w][tid] * __builtin_amdgcn_exp2f(s_wm[w][tid] - M);
     s_ml[0][tid] = M;
     s_ml[1][tid] = L;
   }
   __syncthreads();
-  for (int i = tid; i < gcount * kD; i += 256) {
+  for (int i = tid; i < gcount * kD; i += NT) {
     const int hd = i >> 7, d = i & (kD - 1);
     const float M = s_ml[0][hd];
     float o = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float mw = s_wm[w][hd];
       const float* sa = reinterpret_cast<const float*>(s_ring + w * C::kWaveRing);
       if (mw != -INFINITY)
@@ -992,7 +998,8 @@ static int check_mfma_args(const DecodeArgs& a, int bits) {
   // 4-bit keys need the integer form of the key codebook (odd-symmetric)
   if (bits == 4 && !(a.ki8_unit > 0.f)) return (int)hipErrorInvalidValue;
   // a wave keeps the block-table entries of its pairs one per lane
-  if (a.blocks_per_split < 1 || a.blocks_per_split > 2 * 4 * 64) return (int)hipErrorInvalidValue;
+  const int nw = bits == 4 ? DecodeSmem<4>::kWaves : DecodeSmem<3>::kWaves;
+  if (a.blocks_per_split < 1 || a.blocks_per_split > 2 * nw * 64) return (int)hipErrorInvalidValue;
   return 0;
 }
 
@@ -1002,16 +1009,16 @@ static void launch_mfma(const DecodeArgs& a, const AP& ap, int bits, int ns, int
   const bool lg = a.logits != nullptr;
   switch (bits) {
     case 2:
-      if (lg) hipLaunchKernelGGL((decode_mfma_kernel<2, true, APPEND>), grid, dim3(256), 0, s, a, ns, gs, ap);
-      else hipLaunchKernelGGL((decode_mfma_kernel<2, false, APPEND>), grid, dim3(256), 0, s, a, ns, gs, ap);
+      if (lg) hipLaunchKernelGGL((decode_mfma_kernel<2, true, APPEND>), grid, dim3(64 * DecodeSmem<2>::kWaves), 0, s, a, ns, gs, ap);
+      else hipLaunchKernelGGL((decode_mfma_kernel<2, false, APPEND>), grid, dim3(64 * DecodeSmem<2>::kWaves), 0, s, a, ns, gs, ap);
       break;
     case 3:
-      if (lg) hipLaunchKernelGGL((decode_mfma_kernel<3, true, APPEND>), grid, dim3(256), 0, s, a, ns, gs, ap);
-      else hipLaunchKernelGGL((decode_mfma_kernel<3, false, APPEND>), grid, dim3(256), 0, s, a, ns, gs, ap);
+      if (lg) hipLaunchKernelGGL((decode_mfma_kernel<3, true, APPEND>), grid, dim3(64 * DecodeSmem<3>::kWaves), 0, s, a, ns, gs, ap);
+      else hipLaunchKernelGGL((decode_mfma_kernel<3, false, APPEND>), grid, dim3(64 * DecodeSmem<3>::kWaves), 0, s, a, ns, gs, ap);
       break;
     default:
-      if (lg) hipLaunchKernelGGL((decode_mfma_kernel<4, true, APPEND>), grid, dim3(256), 0, s, a, ns, gs, ap);
-      else hipLaunchKernelGGL((decode_mfma_kernel<4, false, APPEND>), grid, dim3(256), 0, s, a, ns, gs, ap);
+      if (lg) hipLaunchKernelGGL((decode_mfma_kernel<4, true, APPEND>), grid, dim3(64 * DecodeSmem<4>::kWaves), 0, s, a, ns, gs, ap);
+      else hipLaunchKernelGGL((decode_mfma_kernel<4, false, APPEND>), grid, dim3(64 * DecodeSmem<4>::kWaves), 0, s, a, ns, gs, ap);
       break;
   }
 }

@@ -415,21 +415,25 @@ int check_device() {
 int blocks_per_split_for(const tq_cache* c, int32_t num_seqs, int32_t group, int32_t max_blocks, bool mfma,
                          bool attend) {
   const int64_t units = (int64_t)num_seqs * c->cfg.num_kv_heads * tq::decode_slices(group);
-  // matrix-core kernel: at most 64 block pairs per wave (4 waves), the
-  // block-table entries a wave keeps one per lane
-  const int64_t cap = mfma ? 512 : 64;
+  // matrix-core kernel: at most 64 block pairs per wave, the block-table
+  // entries a wave keeps one per lane; 4 waves per workgroup with 4-bit
+  // codes, 8 with 2/3-bit codes
+  const bool b4 = c->cfg.bits_k == 4;
+  const int64_t waves = b4 ? 4 : 8;
+  const int64_t cap = mfma ? 2 * 64 * waves : 64;
   int64_t bps;
   if (mfma) {
-    // four (4-bit codes) or three (2/3-bit) 256-thread workgroups fit on a
-    // CU: aim for one such wave of them.  Short splits (a few pairs per wave)
-    // pay the per-workgroup set-up and merge more than they gain from the
-    // extra workgroups: there aim for two per CU, with a multiple of 8 blocks
-    // so the 4 waves get equal pairs (measured on 1 x 32768 tokens x 8 KV
-    // heads: 22 -> 32 blocks, -9%).
-    const int64_t wgs = 256 * (c->cfg.bits_k == 4 ? 4 : 3);
+    // four 4-wave workgroups (4-bit codes) or two 8-wave workgroups (2/3-bit)
+    // fit on a CU: aim for one such round of them.  Short splits (a few
+    // pairs per wave) pay the per-workgroup set-up and merge more than they
+    // gain from the extra workgroups: there aim for half as many, with a
+    // whole number of pairs per wave (measured on 1 x 32768 tokens x 8 KV
+    // heads, 4-bit codes: 22 -> 32 blocks, -9%).
+    const int64_t wgs = 256 * (b4 ? 4 : 2);
+    const int64_t unit = 2 * waves;
     bps = ((int64_t)max_blocks * units + wgs - 1) / wgs;
-    if (bps <= 32) bps = (((int64_t)max_blocks * units + 511) / 512 + 7) & ~(int64_t)7;
-    if (bps < 8) bps = 8;
+    if (bps <= 32) bps = (((int64_t)max_blocks * units + wgs / 2 - 1) / (wgs / 2) + unit - 1) / unit * unit;
+    if (bps < unit) bps = unit;
   } else {
     bps = ((int64_t)max_blocks * units + 1023) / 1024;
     if (bps < 4) bps = 4;
