@@ -1,19 +1,25 @@
 """Benchmark of the codec's hot path on one MI355X.
 
 One step = the whole path over one batch: tq_encode_kv of every key and value
-of the workload into its compressed paged cache, then one tq_decode_attend of
-every sequence's query over that cache.  Default workload: one sequence of
-32768 tokens, 8 KV heads, 64 query heads (GQA 8), head_dim 128, bf16 K/V with
-outlier-channel keys, 4-bit keys and values, 16-token pages.
+of the workload into a compressed paged cache, and one tq_decode_attend of
+every sequence's query over a full cache.  Default workload: the
+Llama-3.1-70B-shaped layer, 4 sequences x 131072 tokens, 8 KV heads, 64 query
+heads (GQA 8), head_dim 128, bf16 K/V with outlier-channel keys, 3-bit keys
+and values, 16-token pages.
 
-The C sets of inputs, caches and workspaces rotate from step to step (C * set
-bytes >= 1 GiB, four times the 256 MB Infinity Cache), so every step reads
-from HBM.  Inputs are resident on the GPU before timing starts.
+Cold caches: C sets of inputs and caches rotate (C >= 2, and C - 1 sets hold
+at least 1 GiB).  Step i encodes set i mod C and decodes set (i + 1) mod C,
+which was encoded C - 1 steps earlier: at least 1 GiB of other traffic (four
+times the 256 MB Infinity Cache) separates a cache's encode from its decode,
+so the decode reads HBM.  All sets are encoded once before timing.  Inputs
+are resident on the GPU before timing starts.
 
 Printed: one JSON line (rank 0).  `value` is decode-attend GB/s of compressed
-KV read (algorithmic bytes / mean decode-kernel time); encoded vectors/s and
-the encode GB/s are reported beside it, each with its fraction of the 8 TB/s
-HBM peak.  Kernel times are HIP events on the stream the kernels run on.
+KV read (algorithmic bytes / mean decode time: split kernel + merge kernel);
+encoded vectors/s and the encode GB/s are reported beside it, each with its
+fraction of the 8 TB/s HBM peak.  Kernel times are HIP events on the stream
+the kernels run on.  `other_workloads` repeats the step on the 1 x 32768 and
+16 x 8192 decode configurations (4-bit codes).
 """
 
 from __future__ import annotations
@@ -52,26 +58,43 @@ def bytes_per_vector(bits: int, in_bytes: int = 2, qjl: bool = False) -> tuple[i
     return 128 * in_bytes, 128 * bits // 8 + 2 + ((16 + 2) if qjl else 0)
 
 
-def cpu_baseline(w, sample_tokens: int):
-    """The oracle (float64 numpy) on a bounded sample of the same workload."""
-    from threadpoolctl import threadpool_info
+def host_cpu() -> dict:
+    """Model name and core counts of the host (lscpu's model name line)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
 
+
+def _oracle_sample(w, sample_tokens: int):
+    """One timed pass of the oracle over the sample: encode of every key and
+    value, then original-frame decode-attend of every query head.  Returns
+    (encode seconds, decode seconds, vectors)."""
     from kv_cache_vector_encode_amd import workloads as W
     from oracle import tq_oracle as O
 
     c32, _ = O.codebook_fp32(128, w.bits_k)
-    kb, k64 = W.keys(w, 0, sample_tokens)
-    vb, v64 = W.values(w, 0, sample_tokens)
+    _, k64 = W.keys(w, 0, sample_tokens)
+    _, v64 = W.values(w, 0, sample_tokens)
     x = np.concatenate([k64.reshape(-1, 128), v64.reshape(-1, 128)])
     t0 = time.perf_counter()
     encs = [O.encode(x[i:i + 32768], w.rot_seed, c32) for i in range(0, len(x), 32768)]
     t_enc = time.perf_counter() - t0
-    # decode over the sample: reconstruct + original-frame attention for every
-    # query head of the sample's KV heads
-    kidx = np.concatenate([e["idx"] for e in encs])[: len(k64.reshape(-1, 128))].reshape(sample_tokens, w.num_kv_heads, 128)
-    kg = np.concatenate([e["gamma16"] for e in encs])[: sample_tokens * w.num_kv_heads].reshape(sample_tokens, w.num_kv_heads)
-    vidx = np.concatenate([e["idx"] for e in encs])[sample_tokens * w.num_kv_heads:].reshape(sample_tokens, w.num_kv_heads, 128)
-    vg = np.concatenate([e["gamma16"] for e in encs])[sample_tokens * w.num_kv_heads:].reshape(sample_tokens, w.num_kv_heads)
+    nk = sample_tokens * w.num_kv_heads
+    idx = np.concatenate([e["idx"] for e in encs])
+    g16 = np.concatenate([e["gamma16"] for e in encs])
+    kidx, vidx = idx[:nk].reshape(sample_tokens, w.num_kv_heads, 128), idx[nk:].reshape(sample_tokens, w.num_kv_heads, 128)
+    kg, vg = g16[:nk].reshape(sample_tokens, w.num_kv_heads), g16[nk:].reshape(sample_tokens, w.num_kv_heads)
     _, q64 = W.queries(w)
     G = w.num_q_heads // w.num_kv_heads
     t0 = time.perf_counter()
@@ -81,19 +104,123 @@ def cpu_baseline(w, sample_tokens: int):
         for g in range(G):
             O.attention(q64[0, h * G + g], khat, vhat)
     t_dec = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return t_enc, t_dec, len(x)
+
+
+def cpu_baseline(w, sample_tokens: int):
+    """The oracle (float64 numpy), as it stands, on a bounded sample of the
+    same workload: once with the BLAS threads numpy starts with and once on
+    one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     _, comp = bytes_per_vector(w.bits_k)
+    dec_bytes = sample_tokens * w.num_kv_heads * 2 * comp
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    t_enc, t_dec, nvec = _oracle_sample(w, sample_tokens)
+    with threadpool_limits(limits=1):
+        t_enc1, t_dec1, _ = _oracle_sample(w, sample_tokens)
     return {
-        "value": round(sample_tokens * w.num_kv_heads * 2 * comp / t_dec / 1e9, 4),
+        "value": round(dec_bytes / t_dec / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
         "sample": (f"{sample_tokens} tokens x {w.num_kv_heads} KV heads of the workload: float64 numpy oracle "
-                   f"encode of {len(x)} vectors ({len(x) / t_enc:.0f} vectors/s) and original-frame decode-attend "
-                   f"of {w.num_q_heads} query heads over them ({t_dec:.1f} s)"),
-        "encode_vectors_per_s": round(len(x) / t_enc, 1),
+                   f"encode of {nvec} vectors and original-frame decode-attend of {w.num_q_heads} query heads "
+                   f"over them; value = the decode's algorithmic bytes / its time on {threads} BLAS threads"),
+        "encode_vectors_per_s": round(nvec / t_enc, 1),
         "seconds": round(t_enc + t_dec, 2),
+        "one_core": {"value": round(dec_bytes / t_dec1 / 1e9, 4), "unit": "GB/s",
+                     "encode_vectors_per_s": round(nvec / t_enc1, 1), "seconds": round(t_enc1 + t_dec1, 2)},
+        "host": host_cpu(),
     }
+
+
+def measure_step(w, dev, stream, steps: int, warmup: int, only: str = "both", sets_arg: int = 0) -> dict:
+    """Time `steps` steps of workload w (after `warmup`), cold: step i encodes
+    set i mod C and decodes set (i + 1) mod C, encoded C - 1 steps before."""
+    import torch
+
+    from kv_cache_vector_encode_amd import tq
+    from kv_cache_vector_encode_amd import workloads as W
+
+    print(f"# workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+    kb, _ = W.keys(w)
+    vb, _ = W.values(w)
+    qb, _ = W.queries(w)
+    K0 = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(dev)
+    V0 = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(dev)
+    q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).to(dev)
+    slots = torch.from_numpy(W.slot_mapping(w)).to(dev)
+    bt = torch.from_numpy(W.block_tables(w)).to(dev)
+    lens = torch.from_numpy(W.seq_lens(w)).to(dev)
+    del kb, vb
+
+    rot = tq.tq_make_rotation(w.rot_seed, 128)
+    cfg = tq.make_config(w.num_kv_heads, w.num_blocks, w.bits_k, w.bits_v, rot)
+    pool_bytes = tq.tq_cache_bytes(cfg)
+    set_bytes = 2 * K0.numel() * 2 + pool_bytes
+    nsets = sets_arg or max(2, math.ceil((1 << 30) / set_bytes) + 1)
+    sets = []
+    for i in range(nsets):
+        pool = torch.zeros(pool_bytes, dtype=torch.uint8, device=dev)
+        cache = tq.tq_cache_create(cfg, pool)
+        ws = tq.new_workspace(cache, w.num_seqs, w.num_q_heads, bt.shape[1], device=dev)
+        sets.append(dict(K=K0.clone() if i else K0, V=V0.clone() if i else V0, cache=cache, ws=ws,
+                         out=torch.empty((w.num_seqs, w.num_q_heads, 128), device=dev)))
+    # every cache holds the workload's codes before any timed decode
+    for s_ in sets:
+        tq.tq_encode_kv(s_["K"], s_["V"], slots, w.bits_k, s_["cache"], stream)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        if only != "decode":
+            s_ = sets[i % nsets]
+            if ev is not None:
+                ev[0].record(stream)
+            tq.tq_encode_kv(s_["K"], s_["V"], slots, w.bits_k, s_["cache"], stream)
+            if ev is not None:
+                ev[1].record(stream)
+        if only != "encode":
+            s_ = sets[(i + 1) % nsets]
+            if ev is not None:
+                ev[2].record(stream)
+            tq.tq_decode_attend(q, s_["cache"], bt, lens, s_["out"], s_["ws"], stream=stream)
+            if ev is not None:
+                ev[3].record(stream)
+
+    print(f"# {nsets} rotating sets of {set_bytes / 1e6:.1f} MB; warmup {warmup}", file=sys.stderr, flush=True)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    return {
+        "enc_ms": [e[0].elapsed_time(e[1]) for e in evs] if only != "decode" else [float("nan")],
+        "dec_ms": [e[2].elapsed_time(e[3]) for e in evs] if only != "encode" else [float("nan")],
+        "total_ms": start.elapsed_time(stop), "wall_s": t_wall, "nsets": nsets, "set_bytes": set_bytes,
+        "K0": K0, "V0": V0, "q": q, "slots": slots, "bt": bt, "lens": lens, "sets": sets,
+    }
+
+
+def step_summary(w, r) -> dict:
+    """Per-workload line: decode and encode rates of a measure_step result."""
+    nvec = 2 * w.tokens * w.num_kv_heads
+    in_b, comp_b = bytes_per_vector(w.bits_k)
+    enc_s, dec_s = float(np.mean(r["enc_ms"])) / 1e3, float(np.mean(r["dec_ms"])) / 1e3
+    dec_b = w.tokens * w.num_kv_heads * 2 * comp_b
+    return {"decode_gbps": round(dec_b / dec_s / 1e9, 1), "decode_frac_hbm": round(dec_b / dec_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "decode_us": round(dec_s * 1e6, 2), "encode_vectors_per_s": round(nvec / enc_s, 1),
+            "encode_gbps": round(nvec * (in_b + comp_b) / enc_s / 1e9, 1),
+            "encode_frac_hbm": round(nvec * (in_b + comp_b) / enc_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "encode_us": round(enc_s * 1e6, 2), "rotating_sets": r["nsets"], "bits": w.bits_k}
 
 
 def main():
@@ -101,8 +228,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode_1x32768_h8_gqa8_b4")
-    ap.add_argument("--sets", type=int, default=0, help="rotating input/cache sets (0: enough for 1 GiB)")
+    ap.add_argument("--workload", default="llama70b_4x131072_h8_gqa8_b3")
+    ap.add_argument("--sets", type=int, default=0, help="rotating input/cache sets (0: >= 2 and enough that 1 GiB separates a cache's encode from its decode)")
+    ap.add_argument("--no-other-workloads", action="store_true", help="skip the 1 x 32768 and 16 x 8192 workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the decompress and decode-step measurements after the step (profiling aid: their "
@@ -135,80 +263,15 @@ def main():
         return
     w = W.CONFIGS[args.workload]
     tq.lib()
-    print(f"# workload {w.name}: generating inputs", file=sys.stderr, flush=True)
-
-    # ---- inputs (identical copies per set; rotation only defeats the caches)
-    kb, _ = W.keys(w)
-    vb, _ = W.values(w)
-    qb, _ = W.queries(w)
-    K0 = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(dev)
-    V0 = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(dev)
-    q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).to(dev)
-    slots = torch.from_numpy(W.slot_mapping(w)).to(dev)
-    bt = torch.from_numpy(W.block_tables(w)).to(dev)
-    lens = torch.from_numpy(W.seq_lens(w)).to(dev)
-    del kb, vb
-
-    rot = tq.tq_make_rotation(w.rot_seed, 128)
-    cfg = tq.make_config(w.num_kv_heads, w.num_blocks, w.bits_k, w.bits_v, rot)
-    pool_bytes = tq.tq_cache_bytes(cfg)
-    set_bytes = 2 * K0.numel() * 2 + pool_bytes
-    nsets = args.sets or max(1, math.ceil((1 << 30) / set_bytes))
-    sets = []
-    for i in range(nsets):
-        pool = torch.zeros(pool_bytes, dtype=torch.uint8, device=dev)
-        cache = tq.tq_cache_create(cfg, pool)
-        ws = tq.new_workspace(cache, w.num_seqs, w.num_q_heads, bt.shape[1], device=dev)
-        sets.append(dict(K=K0.clone() if i else K0, V=V0.clone() if i else V0, cache=cache, ws=ws,
-                         out=torch.empty((w.num_seqs, w.num_q_heads, 128), device=dev)))
-    torch.cuda.synchronize()
-
+    stream = torch.cuda.current_stream()
+    mres = measure_step(w, dev, stream, args.steps, args.warmup, args.only, args.sets)
+    enc_ms, dec_ms, total_ms, t_wall = mres["enc_ms"], mres["dec_ms"], mres["total_ms"], mres["wall_s"]
+    nsets, set_bytes = mres["nsets"], mres["set_bytes"]
+    K0, V0, q, slots, bt, lens, sets = mres["K0"], mres["V0"], mres["q"], mres["slots"], mres["bt"], mres["lens"], mres["sets"]
     nvec = 2 * w.tokens * w.num_kv_heads
     in_b, comp_b = bytes_per_vector(w.bits_k)
     enc_bytes = nvec * (in_b + comp_b)
     dec_bytes = w.tokens * w.num_kv_heads * 2 * comp_b     # K and V records + norms
-
-    stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
-        s = sets[i % nsets]
-        if args.only != "decode":
-            if ev is not None:
-                ev[0].record(stream)
-            tq.tq_encode_kv(s["K"], s["V"], slots, w.bits_k, s["cache"], stream)
-            if ev is not None:
-                ev[1].record(stream)
-        if args.only != "encode":
-            if ev is not None:
-                ev[2].record(stream)
-            tq.tq_decode_attend(q, s["cache"], bt, lens, s["out"], s["ws"], stream=stream)
-            if ev is not None:
-                ev[3].record(stream)
-
-    if args.only == "decode":
-        # decode-only timing still reads real codes (bank conflicts of the
-        # table lookups depend on them): encode every set once, untimed
-        for s in sets:
-            tq.tq_encode_kv(s["K"], s["V"], slots, w.bits_k, s["cache"], stream)
-        torch.cuda.synchronize()
-    print(f"# {nsets} rotating sets of {set_bytes / 1e6:.1f} MB; warmup {args.warmup}", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(stop)
-    enc_ms = [e[0].elapsed_time(e[1]) for e in evs] if args.only != "decode" else [float("nan")]
-    dec_ms = [e[2].elapsed_time(e[3]) for e in evs] if args.only != "encode" else [float("nan")]
     enc_s = float(np.mean(enc_ms)) / 1e3
     dec_s = float(np.mean(dec_ms)) / 1e3
     dec_gbps = dec_bytes / dec_s / 1e9
@@ -449,7 +512,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16",
+        "dtype_detail": ("decode: matrix-core products with f16 operands and f32 accumulation (2/3-bit keys and all "
+                         "values: codebooks as scaled f16, queries as f16 high + low parts, p*gamma_v as f16; "
+                         "4-bit keys: 16-bit integer centroids and queries as 8-bit planes, exact int32 sums), "
+                         "online softmax and merge in f32; encode: bf16 input, Hadamard product on bf16 matrix "
+                         "cores with f32 accumulation, f32 threshold search, fp16 norms"),
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "seq_len": w.seq_len,
                    "num_kv_heads": w.num_kv_heads, "num_q_heads": w.num_q_heads, "head_dim": 128,
@@ -469,6 +537,21 @@ def main():
         res["onbox_ceiling"] = onbox
     if args.only != "both":
         res["only"] = args.only
+    if not args.no_other_workloads and args.only == "both":
+        # the other decode configurations, the same cold step on each
+        mres.clear()
+        del K0, V0, q, slots, bt, lens, sets
+        torch.cuda.empty_cache()
+        other = {}
+        for name in ("decode_1x32768_h8_gqa8_b4", "prefill_16x8192_h8_gqa8_b4"):
+            if name == w.name:
+                continue
+            wo = W.CONFIGS[name]
+            r = measure_step(wo, dev, stream, min(args.steps, 50), min(args.warmup, 5))
+            other[name] = step_summary(wo, r)
+            r.clear()
+            torch.cuda.empty_cache()
+        res["other_workloads"] = other
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
