@@ -144,6 +144,66 @@ def _dtype_code(t) -> int:
     return m[t.dtype]
 
 
+# ------------------------------------------------------- argument checks --
+# The C ABI takes raw device pointers and trusts the sizes it is given, so
+# every wrapper checks its tensors here first: a wrong index dtype (int64 is
+# torch's default), a non-contiguous view, a wrong shape or a host tensor
+# would otherwise be read out of bounds by the kernels.
+
+_FLOATS = ("float32", "float16", "bfloat16")
+
+
+def _need(t, name: str, dtypes=None, shape=None):
+    """t must be a contiguous torch tensor of one of `dtypes` (torch dtype
+    names) with `shape` (None entries match any size).  Returns t.  Where it
+    lives is checked by _on_gpu once every argument has passed these checks."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if dtypes is not None and str(t.dtype).replace("torch.", "") not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {', '.join(dtypes)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(g) != int(w) for g, w in zip(t.shape, shape)):
+            want = "[" + "][".join("*" if w is None else str(w) for w in shape) + "]"
+            raise ValueError(f"{name}: shape {list(t.shape)}, expected {want}")
+    return t
+
+
+def _need_bytes(t, name: str, nbytes: int):
+    """A contiguous tensor of at least nbytes bytes (any dtype)."""
+    _need(t, name)
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name}: {have} bytes, needs {nbytes}")
+    return t
+
+
+def _int32(t, name: str, shape):
+    return _need(t, name, ("int32",), shape)
+
+
+def _on_gpu(device=None, **tensors):
+    """Every given tensor (None entries are skipped) is on one GPU device:
+    `device` if given (the cache pool's), else the first one's."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: must be on a GPU device, is on {t.device}")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+def _pool_device(cache):
+    import torch
+    pool = getattr(cache, "pool", None)
+    return pool.device if isinstance(pool, torch.Tensor) and pool.device.type == "cuda" else None
+
+
 # ----------------------------------------------------------------- rotation --
 
 class Rotation:
@@ -222,6 +282,12 @@ def tq_cache_create(cfg: CacheConfig, pool) -> Cache:
 
 def tq_encode_kv(K, V, slot_mapping, bits: int, cache: Cache, stream=None):
     """K, V: device tensors [tokens][kv_heads][128] (V None for keys-only)."""
+    dev, H = _pool_device(cache), cache.cfg.num_kv_heads
+    _need(K, "K", _FLOATS, (None, H, 128))
+    if V is not None:
+        _need(V, "V", (str(K.dtype).replace("torch.", ""),), tuple(K.shape))
+    _int32(slot_mapping, "slot_mapping", (K.shape[0],))
+    _on_gpu(dev, K=K, V=V, slot_mapping=slot_mapping)
     _check(lib().tq_encode_kv(_ptr(K), _ptr(V), _dtype_code(K), K.shape[0], _ptr(slot_mapping), bits,
                               cache.handle, _stream(stream)), "tq_encode_kv")
 
@@ -239,21 +305,42 @@ def tq_decode_attend(q, cache: Cache, block_tables, seq_lens, out, workspace, lo
                      scale: float = 0.0, stream=None):
     """q [seqs][q_heads][128]; block_tables int32 [seqs][max_blocks]; out f32
     [seqs][q_heads][128]; workspace: uint8 tensor of tq_decode_workspace_bytes() bytes."""
-    ns, hq, _ = q.shape
+    ns, hq, mb = _check_decode_args(q, cache, block_tables, seq_lens, logits_out)
+    _need(out, "out", ("float32",), (ns, hq, 128))
+    _need_bytes(workspace, "workspace", tq_decode_workspace_bytes(cache, ns, hq, mb))
+    _on_gpu(_pool_device(cache), q=q, block_tables=block_tables, seq_lens=seq_lens, out=out, workspace=workspace,
+            logits_out=logits_out)
     _check(lib().tq_decode_attend(_ptr(q), _dtype_code(q), cache.handle, _ptr(block_tables), _ptr(seq_lens),
                                   ns, hq, block_tables.shape[1], scale, _ptr(out), _ptr(logits_out),
                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _stream(stream)), "tq_decode_attend")
 
 
-def tq_decode_logits(q, cache: Cache, block_tables, seq_lens, logits_out, scale: float = 0.0, stream=None):
+def _check_decode_args(q, cache: Cache, block_tables, seq_lens, logits_out):
+    dev = _pool_device(cache)
+    _need(q, "q", _FLOATS, (None, None, 128))
     ns, hq, _ = q.shape
+    _int32(block_tables, "block_tables", (ns, None))
+    _int32(seq_lens, "seq_lens", (ns,))
+    mb = block_tables.shape[1]
+    if logits_out is not None:
+        _need(logits_out, "logits_out", ("float32",), (ns, hq, mb * BLOCK))
+    return ns, hq, mb
+
+
+def tq_decode_logits(q, cache: Cache, block_tables, seq_lens, logits_out, scale: float = 0.0, stream=None):
+    ns, hq, _ = _check_decode_args(q, cache, block_tables, seq_lens, logits_out)
+    _on_gpu(_pool_device(cache), q=q, block_tables=block_tables, seq_lens=seq_lens, logits_out=logits_out)
     _check(lib().tq_decode_logits(_ptr(q), _dtype_code(q), cache.handle, _ptr(block_tables), _ptr(seq_lens),
                                   ns, hq, block_tables.shape[1], scale, _ptr(logits_out), _stream(stream)),
            "tq_decode_logits")
 
 
 def tq_reconstruct(cache: Cache, slots, which: int, out, stream=None):
+    dev = _pool_device(cache)
+    _int32(slots, "slots", (None,))
+    _need(out, "out", ("float32",), (slots.shape[0], cache.cfg.num_kv_heads, 128))
+    _on_gpu(dev, slots=slots, out=out)
     _check(lib().tq_reconstruct(cache.handle, _ptr(slots), slots.shape[0], which, _ptr(out), _stream(stream)),
            "tq_reconstruct")
 
@@ -263,9 +350,14 @@ def tq_decode_step(q, K_new, V_new, cache: Cache, block_tables, seq_lens, out, w
     """Append every sequence's new token (K_new, V_new [seqs][kv_heads][128],
     at position seq_len - 1) and attend over the whole sequence; arguments
     otherwise as tq_decode_attend."""
-    ns, hq, _ = q.shape
-    if K_new.dtype != V_new.dtype:
-        raise TypeError("K_new and V_new must have one dtype")
+    ns, hq, mb = _check_decode_args(q, cache, block_tables, seq_lens, logits_out)
+    dev, H = _pool_device(cache), cache.cfg.num_kv_heads
+    _need(K_new, "K_new", _FLOATS, (ns, H, 128))
+    _need(V_new, "V_new", (str(K_new.dtype).replace("torch.", ""),), (ns, H, 128))
+    _need(out, "out", ("float32",), (ns, hq, 128))
+    _need_bytes(workspace, "workspace", tq_decode_workspace_bytes(cache, ns, hq, mb))
+    _on_gpu(dev, q=q, K_new=K_new, V_new=V_new, block_tables=block_tables, seq_lens=seq_lens, out=out,
+            workspace=workspace, logits_out=logits_out)
     _check(lib().tq_decode_step(_ptr(q), _dtype_code(q), _ptr(K_new), _ptr(V_new), _dtype_code(K_new), cache.handle,
                                 _ptr(block_tables), _ptr(seq_lens), ns, hq, block_tables.shape[1], scale, _ptr(out),
                                 _ptr(logits_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -275,18 +367,31 @@ def tq_decode_step(q, K_new, V_new, cache: Cache, block_tables, seq_lens, out, w
 def tq_minmax_encode(X, bits: int, rot, codes, params, stream=None):
     """X: device [n][128] (f32/f16/bf16); codes: uint8 [n][16*bits]; params:
     [n][2] 16-bit words (fp16 scale, fp16 zero point)."""
+    _need(X, "X", _FLOATS, (None, 128))
+    n = X.shape[0]
+    _need(codes, "codes", ("uint8",), (n, 16 * bits))
+    _need(params, "params", ("int16", "float16", "bfloat16"), (n, 2))
+    _on_gpu(None, X=X, codes=codes, params=params)
     _check(lib().tq_minmax_encode(_ptr(X), _dtype_code(X), X.shape[0], bits, rot.handle, _ptr(codes),
                                   _ptr(params), _stream(stream)), "tq_minmax_encode")
 
 
 def tq_minmax_decode(codes, params, bits: int, rot, out, stream=None):
     """out: device [n][128] of f32/f16/bf16."""
+    _need(codes, "codes", ("uint8",), (None, 16 * bits))
+    n = codes.shape[0]
+    _need(params, "params", ("int16", "float16", "bfloat16"), (n, 2))
+    _need(out, "out", _FLOATS, (n, 128))
+    _on_gpu(None, codes=codes, params=params, out=out)
     _check(lib().tq_minmax_decode(_ptr(codes), _ptr(params), codes.shape[0], bits, rot.handle,
                                   _dtype_code(out), _ptr(out), _stream(stream)), "tq_minmax_decode")
 
 
 def tq_stream_read(src, sink, stream=None):
     """Measurement aid: stream-read the device tensor src (its whole storage)."""
+    _need(src, "src")
+    _need_bytes(sink, "sink", 4)
+    _on_gpu(None, src=src, sink=sink)
     _check(lib().tq_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)),
            "tq_stream_read")
 
@@ -313,11 +418,19 @@ def tq_octo_codebook(d: int, bits: int):
 
 def tq_octo_tables(bits: int, dev_tables, stream=None):
     """dev_tables: device uint8 tensor of tq_octo_table_bytes(bits) bytes."""
+    _need_bytes(dev_tables, "dev_tables", tq_octo_table_bytes(bits))
+    _on_gpu(None, dev_tables=dev_tables)
     _check(lib().tq_octo_tables(bits, _ptr(dev_tables), _stream(stream)), "tq_octo_tables")
 
 
 def tq_octo_encode(X, bits: int, rot, dev_tables, codes, gamma, stream=None):
     """X: device [n][128] (f32/f16/bf16); codes: uint8 [n][record bytes]; gamma: [n] 16-bit."""
+    _need(X, "X", _FLOATS, (None, 128))
+    n = X.shape[0]
+    _need_bytes(dev_tables, "dev_tables", tq_octo_table_bytes(bits))
+    _need(codes, "codes", ("uint8",), (n, tq_octo_record_bytes(128, bits)))
+    _need(gamma, "gamma", ("int16", "float16"), (n,))
+    _on_gpu(None, X=X, dev_tables=dev_tables, codes=codes, gamma=gamma)
     _check(lib().tq_octo_encode(_ptr(X), _dtype_code(X), X.shape[0], bits, rot.handle, _ptr(dev_tables),
                                 dev_tables.numel() * dev_tables.element_size(), _ptr(codes), _ptr(gamma),
                                 _stream(stream)), "tq_octo_encode")
@@ -326,7 +439,14 @@ def tq_octo_encode(X, bits: int, rot, dev_tables, codes, gamma, stream=None):
 def tq_octo_logits(q, codes, gamma, bits: int, rot, dev_tables, out, scale=None, stream=None):
     """q: fp32 [heads][group][128]; codes: uint8 [heads][n][record bytes];
     gamma: [heads][n] 16-bit; out: fp32 [heads][group][n]."""
+    _need(q, "q", ("float32",), (None, None, 128))
     heads, group, _ = q.shape
+    _need(codes, "codes", ("uint8",), (heads, None, tq_octo_record_bytes(128, bits)))
+    n = codes.shape[1]
+    _need(gamma, "gamma", ("int16", "float16"), (heads, n))
+    _need(out, "out", ("float32",), (heads, group, n))
+    _need_bytes(dev_tables, "dev_tables", tq_octo_table_bytes(bits))
+    _on_gpu(None, q=q, codes=codes, gamma=gamma, out=out, dev_tables=dev_tables)
     if scale is None:
         scale = 1.0 / math.sqrt(128)
     _check(lib().tq_octo_logits(_ptr(q), _ptr(codes), _ptr(gamma), heads, group, codes.shape[1], bits, rot.handle,
@@ -337,7 +457,15 @@ def tq_octo_logits(q, codes, gamma, bits: int, rot, dev_tables, out, scale=None,
 def tq_decompress_kv(cache: Cache, slots, K_out, V_out=None, stream=None):
     """K_out / V_out: device tensors [n][kv_heads][128] of bfloat16 or float16
     (the same dtype); either may be None."""
+    dev, H = _pool_device(cache), cache.cfg.num_kv_heads
+    if K_out is not None and V_out is not None and getattr(K_out, "dtype", None) != getattr(V_out, "dtype", None):
+        raise TypeError("K_out and V_out must have one dtype")
+    _int32(slots, "slots", (None,))
     ref = K_out if K_out is not None else V_out
+    for t, name in ((K_out, "K_out"), (V_out, "V_out")):
+        if t is not None:
+            _need(t, name, ("bfloat16", "float16"), (slots.shape[0], H, 128))
+    _on_gpu(dev, slots=slots, K_out=K_out, V_out=V_out)
     _check(lib().tq_decompress_kv(cache.handle, _ptr(slots), slots.shape[0], _dtype_code(ref) if ref is not None else 2,
                                   _ptr(K_out), _ptr(V_out), _stream(stream)), "tq_decompress_kv")
 

@@ -1,0 +1,135 @@
+"""The Python binding checks every tensor before it hands raw pointers to the
+C ABI: index dtypes (int32, not torch's default int64), contiguity, shapes
+against the cache and the other arguments, dtypes and the device.  These run
+on the host: each bad argument must raise before the library is called."""
+
+import pytest
+import torch
+
+from kv_cache_vector_encode_amd import tq
+
+
+def _cache(bits_k=4, bits_v=4, heads=8):
+    r = tq.tq_make_rotation(42, 128)
+    c = tq.tq_cache_create(tq.make_config(heads, 4, bits_k, bits_v, r), 0x100000)   # never dereferenced
+    c._rots = (r,)
+    return c
+
+
+def _kv(n=10, heads=8, dtype=torch.bfloat16):
+    return torch.zeros((n, heads, 128), dtype=dtype), torch.zeros((n, heads, 128), dtype=dtype)
+
+
+def test_encode_rejects_bad_tensors():
+    c = _cache()
+    K, V = _kv()
+    with pytest.raises(TypeError, match="slot_mapping: dtype torch.int64"):
+        tq.tq_encode_kv(K, V, torch.zeros(10, dtype=torch.int64), 4, c)
+    with pytest.raises(ValueError, match=r"slot_mapping: shape \[9\]"):
+        tq.tq_encode_kv(K, V, torch.zeros(9, dtype=torch.int32), 4, c)
+    with pytest.raises(ValueError, match="K: must be contiguous"):
+        tq.tq_encode_kv(K.transpose(0, 1), V, torch.zeros(10, dtype=torch.int32), 4, c)
+    K6, V6 = _kv(heads=6)
+    with pytest.raises(ValueError, match=r"K: shape \[10, 6, 128\]"):
+        tq.tq_encode_kv(K6, V6, torch.zeros(10, dtype=torch.int32), 4, c)
+    with pytest.raises(TypeError, match="V: dtype torch.float16"):
+        tq.tq_encode_kv(K, V.half(), torch.zeros(10, dtype=torch.int32), 4, c)
+    with pytest.raises(ValueError, match=r"V: shape \[11, 8, 128\]"):
+        tq.tq_encode_kv(K, torch.zeros((11, 8, 128), dtype=torch.bfloat16), torch.zeros(10, dtype=torch.int32), 4, c)
+    with pytest.raises(TypeError, match="K: dtype torch.int8"):
+        tq.tq_encode_kv(K.to(torch.int8), None, torch.zeros(10, dtype=torch.int32), 4, c)
+    with pytest.raises(ValueError, match="must be on a GPU device"):
+        tq.tq_encode_kv(K, V, torch.zeros(10, dtype=torch.int32), 4, c)
+    with pytest.raises(TypeError, match="expected a torch tensor"):
+        tq.tq_encode_kv([1, 2], V, torch.zeros(10, dtype=torch.int32), 4, c)
+
+
+def _decode_args(ns=2, hq=64, mb=5):
+    q = torch.zeros((ns, hq, 128), dtype=torch.bfloat16)
+    bt = torch.zeros((ns, mb), dtype=torch.int32)
+    sl = torch.zeros(ns, dtype=torch.int32)
+    out = torch.zeros((ns, hq, 128), dtype=torch.float32)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    return q, bt, sl, out, ws
+
+
+def test_decode_attend_rejects_bad_tensors():
+    c = _cache()
+    q, bt, sl, out, ws = _decode_args()
+    with pytest.raises(TypeError, match="block_tables: dtype torch.int64"):
+        tq.tq_decode_attend(q, c, bt.long(), sl, out, ws)
+    with pytest.raises(TypeError, match="seq_lens: dtype torch.int64"):
+        tq.tq_decode_attend(q, c, bt, sl.long(), out, ws)
+    with pytest.raises(ValueError, match=r"block_tables: shape \[3, 5\]"):
+        tq.tq_decode_attend(q, c, torch.zeros((3, 5), dtype=torch.int32), sl, out, ws)
+    with pytest.raises(ValueError, match=r"q: shape \[2, 64, 64\]"):
+        tq.tq_decode_attend(torch.zeros((2, 64, 64), dtype=torch.bfloat16), c, bt, sl, out, ws)
+    with pytest.raises(TypeError, match="out: dtype torch.bfloat16"):
+        tq.tq_decode_attend(q, c, bt, sl, out.bfloat16(), ws)
+    with pytest.raises(ValueError, match=r"out: shape \[2, 32, 128\]"):
+        tq.tq_decode_attend(q, c, bt, sl, out[:, :32].contiguous(), ws)
+    with pytest.raises(ValueError, match=r"logits_out: shape \[2, 64, 79\]"):
+        tq.tq_decode_attend(q, c, bt, sl, out, ws, logits_out=torch.zeros((2, 64, 79)))
+    with pytest.raises(ValueError, match="q: must be contiguous"):
+        tq.tq_decode_attend(q.transpose(0, 1), c, bt, sl, out, ws)
+    with pytest.raises(ValueError, match="must be on a GPU device"):
+        tq.tq_decode_attend(q, c, bt, sl, out, ws)
+    with pytest.raises(TypeError, match="block_tables: dtype torch.int64"):
+        tq.tq_decode_logits(q, c, bt.long(), sl, torch.zeros((2, 64, 80)))
+
+
+def test_decode_step_rejects_bad_tensors():
+    c = _cache()
+    q, bt, sl, out, ws = _decode_args()
+    K, V = _kv(n=2)
+    with pytest.raises(ValueError, match=r"K_new: shape \[3, 8, 128\]"):
+        tq.tq_decode_step(q, *_kv(n=3), c, bt, sl, out, ws)
+    with pytest.raises(TypeError, match="V_new: dtype torch.float32"):
+        tq.tq_decode_step(q, K, V.float(), c, bt, sl, out, ws)
+    with pytest.raises(TypeError, match="seq_lens: dtype torch.int64"):
+        tq.tq_decode_step(q, K, V, c, bt, sl.long(), out, ws)
+
+
+def test_reconstruct_and_decompress_reject_bad_tensors():
+    c = _cache()
+    slots = torch.zeros(7, dtype=torch.int32)
+    with pytest.raises(TypeError, match="slots: dtype torch.int64"):
+        tq.tq_reconstruct(c, slots.long(), 0, torch.zeros((7, 8, 128)))
+    with pytest.raises(ValueError, match=r"out: shape \[7, 4, 128\]"):
+        tq.tq_reconstruct(c, slots, 0, torch.zeros((7, 4, 128)))
+    Ko = torch.zeros((7, 8, 128), dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="K_out: dtype torch.float32"):
+        tq.tq_decompress_kv(c, slots, Ko.float(), None)
+    with pytest.raises(TypeError, match="K_out and V_out must have one dtype"):
+        tq.tq_decompress_kv(c, slots, Ko, Ko.half())
+    with pytest.raises(TypeError, match="slots: dtype torch.int64"):
+        tq.tq_decompress_kv(c, slots.long(), Ko, None)
+
+
+def test_minmax_and_octo_reject_bad_tensors():
+    r = tq.tq_make_rotation(42, 128)
+    X = torch.zeros((5, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match=r"codes: shape \[5, 48\]"):
+        tq.tq_minmax_encode(X, 4, r, torch.zeros((5, 48), dtype=torch.uint8), torch.zeros((5, 2), dtype=torch.int16))
+    with pytest.raises(TypeError, match="params: dtype torch.int32"):
+        tq.tq_minmax_encode(X, 4, r, torch.zeros((5, 64), dtype=torch.uint8), torch.zeros((5, 2), dtype=torch.int32))
+    with pytest.raises(ValueError, match=r"out: shape \[5, 64\]"):
+        tq.tq_minmax_decode(torch.zeros((5, 64), dtype=torch.uint8), torch.zeros((5, 2), dtype=torch.int16), 4, r,
+                            torch.zeros((5, 64)))
+    rec = tq.tq_octo_record_bytes(128, 4)
+    tabs = torch.zeros(tq.tq_octo_table_bytes(4), dtype=torch.uint8)
+    # the triplet logits read fp32 queries: a bf16 q would be read as twice its bytes
+    with pytest.raises(TypeError, match="q: dtype torch.bfloat16"):
+        tq.tq_octo_logits(torch.zeros((2, 8, 128), dtype=torch.bfloat16), torch.zeros((2, 9, rec), dtype=torch.uint8),
+                          torch.zeros((2, 9), dtype=torch.int16), 4, r, tabs, torch.zeros((2, 8, 9)))
+    with pytest.raises(ValueError, match=r"out: shape \[2, 8, 10\]"):
+        tq.tq_octo_logits(torch.zeros((2, 8, 128)), torch.zeros((2, 9, rec), dtype=torch.uint8),
+                          torch.zeros((2, 9), dtype=torch.int16), 4, r, tabs, torch.zeros((2, 8, 10)))
+    with pytest.raises(ValueError, match=r"codes: shape \[5, 40\]"):
+        tq.tq_octo_encode(X, 4, r, tabs, torch.zeros((5, 40), dtype=torch.uint8), torch.zeros(5, dtype=torch.int16))
+    with pytest.raises(ValueError, match="dev_tables: 8 bytes, needs"):
+        tq.tq_octo_tables(4, tabs[:8].clone())
+    with pytest.raises(ValueError, match="workspace: 16 bytes, needs"):
+        c = _cache()
+        q, bt, sl, out, _ = _decode_args()
+        tq.tq_decode_attend(q, c, bt, sl, out, torch.zeros(16, dtype=torch.uint8))
