@@ -188,6 +188,25 @@ int tq_decode_attend(const void* q, int32_t q_dtype, const tq_cache* cache,
                      float* logits_out, void* workspace, int64_t workspace_bytes,
                      void* hip_stream);
 
+/* Decode-attend without allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops or harnesses that
+ * forbid hipMalloc).  The same computation, kernels and arguments as
+ * tq_decode_attend, minus the workspace: the per-split partials go to a
+ * fixed buffer inside the library, TQ_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU,
+ * held from the library's first such call on that GPU until the process
+ * ends.  A call whose partials need more (tq_decode_workspace_bytes) returns
+ * TQ_ERR_WORKSPACE before touching the device.  The call itself allocates
+ * nothing.  Every call on one GPU shares that GPU's buffer: calls that
+ * overlap in time on one GPU (other streams, other host threads) race and
+ * must be serialised by the caller.  The buffer needs no initial contents
+ * (each split writes its partials before the merge reads them). */
+#define TQ_NOALLOC_SCRATCH_BYTES (16ll << 20)
+int tq_decode_attend_noalloc(const void* q, int32_t q_dtype, const tq_cache* cache,
+                             const int32_t* block_tables, const int32_t* seq_lens,
+                             int32_t num_seqs, int32_t num_q_heads,
+                             int32_t max_blocks_per_seq, float scale, float* out,
+                             float* logits_out, void* hip_stream);
+
 /* ---------------------------------------------------------------------------
  * One decode step: append each sequence's new token to the compressed cache
  * and attend over the whole sequence, new token included, in one call with

@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
-SOURCES = ["tq_host.cpp", "tq_encode.hip", "tq_decode.hip", "tq_decode_mfma.hip", "tq_merge.hip", "tq_reconstruct.hip", "tq_minmax.hip", "tq_calib.hip", "tq_octo.hip"]
+SOURCES = ["tq_host.cpp", "tq_encode.hip", "tq_decode.hip", "tq_decode_mfma.hip", "tq_merge.hip", "tq_reconstruct.hip", "tq_minmax.hip", "tq_calib.hip", "tq_octo.hip", "tq_scratch.hip"]
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")
 
 

@@ -757,10 +757,13 @@ int64_t tq_decode_workspace_bytes(const tq_cache* cache, int32_t num_seqs, int32
   return nsh * splits * group * tq::kPartStride * 4;
 }
 
-int tq_decode_attend(const void* q, int32_t q_dtype, const tq_cache* cache,
-                     const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
-                     int32_t num_q_heads, int32_t max_blocks_per_seq, float scale, float* out,
-                     float* logits_out, void* workspace, int64_t workspace_bytes, void* hip_stream) {
+// Decode-attend with its partials in `workspace` (caller memory, or the
+// library's fixed scratch when workspace == nullptr and no_alloc is set).
+static int decode_attend_impl(const void* q, int32_t q_dtype, const tq_cache* cache,
+                              const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t max_blocks_per_seq, float scale, float* out,
+                              float* logits_out, void* workspace, int64_t workspace_bytes, bool no_alloc,
+                              void* hip_stream) {
   int s = validate_decode(q, q_dtype, cache, block_tables, seq_lens, num_seqs, num_q_heads,
                           max_blocks_per_seq);
   if (s != TQ_OK) return s;
@@ -768,9 +771,20 @@ int tq_decode_attend(const void* q, int32_t q_dtype, const tq_cache* cache,
   if (num_seqs == 0) return TQ_OK;
   if (!out) return fail(TQ_ERR_INVALID_ARG, "null out");
   const int64_t need = tq_decode_workspace_bytes(cache, num_seqs, num_q_heads, max_blocks_per_seq);
-  if (!workspace || workspace_bytes < need) return fail(TQ_ERR_WORKSPACE, "workspace too small");
-  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(TQ_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  if ((s = check_device()) != TQ_OK) return s;
+  if (need < 0) return (int)need;
+  if (no_alloc) {
+    if (need > tq::kScratchBytes)
+      return fail(TQ_ERR_WORKSPACE, "the call needs " + std::to_string(need) +
+                                        " bytes of split partials; the fixed scratch holds " +
+                                        std::to_string(tq::kScratchBytes) + " (use tq_decode_attend with a workspace)");
+    if ((s = check_device()) != TQ_OK) return s;
+    const int e = tq::scratch_buffer(&workspace, &workspace_bytes);
+    if (e != 0) return hip_fail(e, "scratch address");
+  } else {
+    if (!workspace || workspace_bytes < need) return fail(TQ_ERR_WORKSPACE, "workspace too small");
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(TQ_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if ((s = check_device()) != TQ_OK) return s;
+  }
   tq::DecodeArgs a;
   fill_decode_args(a, q, q_dtype, cache, block_tables, seq_lens, num_seqs, num_q_heads,
                    max_blocks_per_seq, scale);
@@ -785,6 +799,22 @@ int tq_decode_attend(const void* q, int32_t q_dtype, const tq_cache* cache,
                               decode_uses_mfma(cache, true) ? 1 : 0, hip_stream);
   if (err != 0) return hip_fail(err, "decode launch");
   return TQ_OK;
+}
+
+int tq_decode_attend(const void* q, int32_t q_dtype, const tq_cache* cache,
+                     const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t max_blocks_per_seq, float scale, float* out,
+                     float* logits_out, void* workspace, int64_t workspace_bytes, void* hip_stream) {
+  return decode_attend_impl(q, q_dtype, cache, block_tables, seq_lens, num_seqs, num_q_heads, max_blocks_per_seq,
+                            scale, out, logits_out, workspace, workspace_bytes, false, hip_stream);
+}
+
+int tq_decode_attend_noalloc(const void* q, int32_t q_dtype, const tq_cache* cache,
+                             const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t max_blocks_per_seq, float scale, float* out,
+                             float* logits_out, void* hip_stream) {
+  return decode_attend_impl(q, q_dtype, cache, block_tables, seq_lens, num_seqs, num_q_heads, max_blocks_per_seq,
+                            scale, out, logits_out, nullptr, 0, true, hip_stream);
 }
 
 int tq_decode_step(const void* q, int32_t q_dtype, const void* K_new, const void* V_new, int32_t kv_dtype,

@@ -196,6 +196,12 @@ struct OctoArgs {
   float trho[8];            // thresholds, +inf past the last
 };
 
+// The fixed decode scratch of tq_decode_attend_noalloc (tq_scratch.hip):
+// 16 MiB per GPU.  scratch_buffer returns this device's copy (resolved on
+// the first call per device, with it current) and its size; hipError_t value.
+constexpr int64_t kScratchBytes = 16 << 20;
+int scratch_buffer(void** ptr, int64_t* bytes);
+
 // Launchers implemented in the .hip files; return a hipError_t value.
 int launch_encode(const EncodeArgs& a, int num_streams, int in_dtype, void* stream);
 int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int attend, int mfma, void* stream);

@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "tq_decode_workspace_bytes": (ctypes.c_int64, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
             "tq_decode_attend": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.c_float, _P, _P, _P, ctypes.c_int64, _P]),
+            "tq_decode_attend_noalloc": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, _P, ctypes.c_int32,
+                                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P]),
             "tq_decode_logits": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.c_float, _P, _P]),
             "tq_reconstruct": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
@@ -314,6 +316,22 @@ def tq_decode_attend(q, cache: Cache, block_tables, seq_lens, out, workspace, lo
                                   ns, hq, block_tables.shape[1], scale, _ptr(out), _ptr(logits_out),
                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _stream(stream)), "tq_decode_attend")
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def tq_decode_attend_noalloc(q, cache: Cache, block_tables, seq_lens, out, logits_out=None, scale: float = 0.0,
+                             stream=None):
+    """tq_decode_attend with the split partials in the library's fixed
+    per-GPU scratch (NOALLOC_SCRATCH_BYTES) instead of a workspace; the call
+    allocates nothing.  Calls that overlap in time on one GPU race."""
+    ns, hq, mb = _check_decode_args(q, cache, block_tables, seq_lens, logits_out)
+    _need(out, "out", ("float32",), (ns, hq, 128))
+    _on_gpu(_pool_device(cache), q=q, block_tables=block_tables, seq_lens=seq_lens, out=out, logits_out=logits_out)
+    _check(lib().tq_decode_attend_noalloc(_ptr(q), _dtype_code(q), cache.handle, _ptr(block_tables), _ptr(seq_lens),
+                                          ns, hq, mb, scale, _ptr(out), _ptr(logits_out), _stream(stream)),
+           "tq_decode_attend_noalloc")
 
 
 def _check_decode_args(q, cache: Cache, block_tables, seq_lens, logits_out):

@@ -319,3 +319,21 @@ def test_octo_sizes_and_argument_checks_happen_before_the_device():
     # a table filled for fewer bits is too small for b = 4
     assert L.tq_octo_encode(X, tq.TQ_BF16, 10, 4, r.handle, tb, 4096, cd, g, None) == tq.TQ_ERR_INVALID_ARG
     assert L.tq_octo_logits(q, cd, g, 8, 8, 100, 4, r.handle, tb, 1024, 0.1, out, None) == tq.TQ_ERR_INVALID_ARG
+
+
+def test_noalloc_decode_checks_happen_before_the_device():
+    # the allocation-free decode takes tq_decode_attend's arguments minus the
+    # workspace; a call whose split partials would not fit the fixed 16 MiB
+    # scratch is refused before any device call
+    c = _fake_cache()
+    L = tq.lib()
+    q, bt, sl, out = 0x200000, 0x300000, 0x400000, 0x500000
+    need = L.tq_decode_workspace_bytes(c.handle, 64, 64, 8192)
+    assert need > tq.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert L.tq_decode_attend_noalloc(q, 2, c.handle, bt, sl, 64, 64, 8192, 0.0, out, None, None) == tq.TQ_ERR_WORKSPACE
+    assert "fixed scratch" in L.tq_last_error().decode()
+    assert L.tq_decode_attend_noalloc(q, 9, c.handle, bt, sl, 2, 64, 100, 0.0, out, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_decode_attend_noalloc(q, 2, c.handle, bt, sl, 2, 60, 100, 0.0, out, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_decode_attend_noalloc(q, 2, c.handle, bt, sl, 0, 64, 100, 0.0, out, None, None) == tq.TQ_OK
+    ko = _fake_cache(bits_v=0)
+    assert L.tq_decode_attend_noalloc(q, 2, ko.handle, bt, sl, 2, 64, 100, 0.0, out, None, None) == tq.TQ_ERR_INVALID_ARG
