@@ -41,6 +41,7 @@ int launch_stream_read(const void*, int64_t, uint32_t*, void*) { unreachable("st
 int launch_octo_encode(const OctoArgs&, int, void*) { unreachable("triplet encode"); }
 int launch_octo_logits(const OctoArgs&, int, void*) { unreachable("triplet logits"); }
 int decode_slices(int group) { return (group + 7) / 8; }
+int scratch_buffer(void**, int64_t*) { unreachable("scratch address"); }
 }  // namespace tq
 
 #define CHECK(cond)                                                   \
@@ -126,6 +127,10 @@ int main() {
     CHECK(tq_reconstruct(cache, ip, 5, 0, fp, nullptr) == TQ_ERR_NO_DEVICE);
     CHECK(tq_decode_attend(p, 9, cache, ip, ip, 2, 64, 64, 0.f, fp, nullptr, w, ws, nullptr) == TQ_ERR_INVALID_ARG);
     CHECK(tq_decode_attend(p, TQ_BF16, cache, ip, ip, -1, 64, 64, 0.f, fp, nullptr, w, ws, nullptr) == TQ_ERR_INVALID_ARG);
+    const int na = tq_decode_attend_noalloc(p, TQ_BF16, cache, ip, ip, 2, 64, 64, 0.f, fp, nullptr, nullptr);
+    CHECK(na == TQ_ERR_NO_DEVICE || na == TQ_ERR_INVALID_ARG || na == TQ_ERR_UNSUPPORTED);
+    const int big = tq_decode_attend_noalloc(p, TQ_BF16, cache, ip, ip, 64, 64, 8192, 0.f, fp, nullptr, nullptr);
+    CHECK(big == TQ_ERR_WORKSPACE || big == TQ_ERR_INVALID_ARG || big == TQ_ERR_UNSUPPORTED);
   }
   CHECK(tq_minmax_encode(p, TQ_BF16, 7, 3, r, w, w, nullptr) == TQ_ERR_NO_DEVICE);
   CHECK(tq_minmax_decode(p, p, 7, 3, r, TQ_F32, w, nullptr) == TQ_ERR_NO_DEVICE);
