@@ -3,10 +3,10 @@
 //
 // Method: Bit-Axon "TurboQuant: KV Cache Compression", attention under
 // quantisation softmax(Q K_hat^T / sqrt(d_h)) V_hat; deep-dive blog Step 1
-// ("RHT is orthogonal, inner products and attention scores are preserved, so
-// attention can be computed right after the transform without restoring");
-// OCTOPUS summary contributions (the decoder never materialises K_hat; the
-// optional QJL residual adds a correction to q^T k_hat).
+// (the rotation is orthogonal, so inner products and hence attention scores
+// can be taken in the rotated frame without undoing it first); OCTOPUS
+// summary contributions (the decoder never materialises K_hat; the optional
+// QJL residual adds a correction to q^T k_hat).
 //
 // In the rotated frame <q, k_hat_t> = gamma_t <R q, c[codes_t]>, so q is
 // rotated once, every logit is a centroid-lookup dot product, and the value
@@ -20,10 +20,10 @@
 //      products are summed over the row with DPP; scores go to LDS.
 //   B. per head: max and exp-sum over the split (one row per head).
 //   C. values: each row accumulates p_t * gamma_v * c[codes] for its tokens.
-//   D. rows are reduced (shuffles inside a wave, LDS across waves), the
-//      split's (m, l, o_rot) goes to the workspace, and the last workgroup of
-//      the (sequence, slice) to arrive merges all splits, applies R^T and
-//      writes the output (fixed merge order: deterministic results).
+//   D. rows are reduced (shuffles inside a wave, LDS across waves) and the
+//      split's (m, l, o_rot) goes to the workspace; merge_kernel
+//      (tq_merge.hip), a second launch, combines the splits in a fixed order
+//      (deterministic results), applies R^T and writes the output.
 
 #include "tq_device.h"
 

@@ -1,6 +1,6 @@
-// tq_octo: the octahedral triplet codec of the OCTOPUS summary (sections
-// "Octahedral triplet direction quantizer with norm marginals", "MSE-optimal
-// non-uniform bit allocation" and the Method list): the rotated unit
+// tq_octo: the octahedral triplet codec of the OCTOPUS summary (the
+// Contributions list: the triplet direction quantizer with norm marginals
+// and the uneven bit split; and the Method list): the rotated unit
 // direction y = R k / ||k|| is cut into 43 triplets (the last is
 // (y126, y127, 0)); each triplet t = rho n keeps its norm rho and the
 // direction n mapped by the equal-area octahedral map to (xi, eta) in
@@ -45,14 +45,15 @@ __device__ __forceinline__ int octo_cell(float v, int nd) {
   return min(max(j, 0), nd - 1);
 }
 
-// atan(a) for a in [0, 1] as a * P(a^2), P of degree 7: an odd polynomial
-// fitted here to arctan by iteratively reweighted least squares toward the
-// minimax error (largest error 1.6e-7 rad when evaluated in fp32).
+// atan(a) for a in [0, 1] as a * P(a^2), P of degree 7: the odd polynomial
+// of kv_cache_vector_encode_amd/fit_atan.py (Lawson's reweighted least
+// squares toward the minimax fit), coefficients rounded to fp32; largest
+// error 1.34e-7 rad in this fp32 evaluation.
 __device__ __forceinline__ float atan01(float a) {
   const float s = a * a;
-  float p = -4.054563120e-03f;
-  p = __builtin_fmaf(p, s, 2.186294459e-02f);
-  p = __builtin_fmaf(p, s, -5.591231585e-02f);
+  float p = -4.054567311e-03f;
+  p = __builtin_fmaf(p, s, 2.186295763e-02f);
+  p = __builtin_fmaf(p, s, -5.591232702e-02f);
   p = __builtin_fmaf(p, s, 9.642197192e-02f);
   p = __builtin_fmaf(p, s, -1.390862912e-01f);
   p = __builtin_fmaf(p, s, 1.994656622e-01f);

@@ -73,9 +73,10 @@ SQRT_HALF_PI = math.sqrt(math.pi / 2.0)
 
 
 # ---------------------------------------------------------------------------
-# E0: seeded random signs  ([P4] Step 1: "random +/-1 diagonal D from a
-# seed"; [P3] Method step 2 "sign-flipped Walsh-Hadamard rotation"; seed for
-# reproducibility in the [P4] TurboQuantConfig example).
+# E0: seeded random signs  ([P4] Step 1: a diagonal of random signs drawn
+# from a seed; [P3] Method step 2: the Walsh-Hadamard rotation after a sign
+# flip; a fixed seed for reproducibility in the [P4] TurboQuantConfig
+# example).
 # ---------------------------------------------------------------------------
 
 def splitmix64(seed: int, n: int) -> list[int]:
@@ -127,8 +128,8 @@ def rotation_matrix(seed: int, d: int) -> np.ndarray:
 
     [P4] Step 1 applies x*signs, then the Hadamard transform, then divides by
     sqrt(d); [P3] Method step 2 writes R = H diag(s).  The 1/sqrt(d) makes R
-    orthogonal, which [P1] ("rotation preserves length") and [P4] ("RHT is an
-    orthogonal transform, inner products are preserved") require.
+    orthogonal, which [P1] (the rotation keeps vector lengths) and [P4] Step 1
+    (the transform is orthogonal, so inner products survive it) require.
     """
     s = rotation_signs(seed, d).astype(np.float64)
     return hadamard(d) * s[None, :] / math.sqrt(d)
@@ -136,7 +137,7 @@ def rotation_matrix(seed: int, d: int) -> np.ndarray:
 
 # ---------------------------------------------------------------------------
 # E0: Lloyd-Max codebook for the coordinate marginal of a uniform unit vector
-# ([P3] glossary "Lloyd-Max quantization": alternate centroid updates that
+# ([P3] glossary entry for Lloyd-Max quantization: alternate centroid updates that
 # minimise MSE for a given 1-D density, used per coordinate; [P3] key idea:
 # rotation codecs approximate the marginals with per-coordinate Lloyd-Max).
 # ---------------------------------------------------------------------------
@@ -252,7 +253,8 @@ def codebook_distortion(d: int, bits: int, c=None) -> float:
 
 def fp16_norm(gamma) -> np.ndarray:
     """fp16 round-to-nearest-even of the norm, saturating at 65504 ([P4]
-    Step 2 stores magnitude.half(); saturation is this build's reading)."""
+    Step 2 keeps the magnitude as an fp16 value; saturation is this build's
+    reading)."""
     g = np.minimum(np.asarray(gamma, dtype=np.float64), 65504.0)
     return g.astype(np.float16)
 
@@ -290,23 +292,25 @@ def reconstruct(idx, gamma16, seed: int, c32):
 
 
 # ---------------------------------------------------------------------------
-# Comparison codec: per-vector min/max uniform quantiser after the same
-# rotation ([P4] Step 3 compress_value / decompress_value: rotate the whole
-# vector, scale = (max - min) / (2^b - 1), q = round((y - min) / scale),
-# scale and zero point stored as fp16; undone by the inverse rotation).
+# Comparison codec: the per-vector affine (min/max) uniform quantiser after
+# the same rotation ([P4] Step 3's value path): 2^b equally spaced levels
+# spanning [min_j y_j, max_j y_j] of the rotated vector, each coordinate
+# sent to its nearest level; step and lowest level kept as fp16; decoded by
+# the inverse rotation.
 # ---------------------------------------------------------------------------
 
 def fp16_sat(v) -> np.ndarray:
     """fp16 round-to-nearest-even, saturating at +-65504 (this build's reading:
-    the page's .half() would give infinities past the fp16 range)."""
+    a plain fp16 conversion, as the page's listing does, would give
+    infinities past the fp16 range)."""
     return np.clip(np.asarray(v, dtype=np.float64), -65504.0, 65504.0).astype(np.float16)
 
 
 def minmax_encode(x, seed: int, bits: int):
     """Min/max codes of vectors ``x`` (..., d): y = R x (no norm split);
-    lo = min_j y_j, hi = max_j y_j; scale = (hi - lo) / (2^bits - 1);
-    u_j = (y_j - lo) / scale; q_j = round half to even (torch's round) of
-    u_j, clipped to [0, 2^bits - 1].  A vector whose rotated coordinates are
+    the levels are lo + k * scale, k = 0 .. 2^bits - 1, with lo = min_j y_j
+    and scale = (max_j y_j - lo) / (2^bits - 1); q_j is the nearest level's
+    k (ties to the even k).  A vector whose rotated coordinates are
     all equal (scale = 0, e.g. zero) takes every code 0 (the page divides by
     zero there; this build's reading).  scale16 = fp16(scale), zero16 =
     fp16(lo).  Returns dict(codes, scale, zero, scale16, zero16, u, y)."""
@@ -324,8 +328,8 @@ def minmax_encode(x, seed: int, bits: int):
 
 def minmax_decode(codes, scale16, zero16, seed: int):
     """x_hat = R^T (codes * scale16 + zero16), in float64 from the stored
-    fp16 scale and zero point ([P4] Step 3 decompress_value; the inverse is
-    R^T, not a second forward rotation)."""
+    fp16 scale and zero point (each code's level, rotated back; the inverse
+    is R^T, not a second forward rotation)."""
     codes = np.asarray(codes, dtype=np.float64)
     R = rotation_matrix(seed, codes.shape[-1])
     yhat = codes * np.asarray(scale16, dtype=np.float64)[..., None] + np.asarray(zero16, dtype=np.float64)[..., None]
@@ -333,9 +337,10 @@ def minmax_decode(codes, scale16, zero16, seed: int):
 
 
 # ---------------------------------------------------------------------------
-# E6: optional 1-bit QJL residual sketch  ([P3] contribution "Optional 1-bit
-# QJL residual for unbiased dot-product": sketch the signs of the rotated-frame
-# residual through an independent R', store sigma, add a correction to q^T k).
+# E6: optional 1-bit QJL residual sketch  ([P3] Contributions, the optional
+# one-bit QJL residual that makes the inner-product estimate unbiased: sketch
+# the signs of the rotated-frame residual through an independent R', store
+# them, add a correction to q^T k).
 # ---------------------------------------------------------------------------
 
 def qjl_encode(y, idx, c32, seed_qjl: int):
@@ -542,14 +547,14 @@ def unpack_pool(pool, lay: LayoutV1, blocks=None) -> dict:
 
 
 # ---------------------------------------------------------------------------
-# Triplet codec ([P3] "Octahedral triplet direction quantizer with norm
-# marginals" and the Method list, steps 1-7): the rotated unit direction is
+# Triplet codec ([P3] Contributions, the triplet direction quantizer with
+# norm marginals, and the Method list, steps 1-7): the rotated unit direction is
 # cut into ceil(d/3) triplets t_i (the last padded with zeros); each triplet
 # is rho_i = ||t_i|| times a unit direction n_i; n_i goes through an
 # equal-area octahedral map to (xi, eta) in [-1, 1]^2 ([P3] glossary
-# "octahedral map"); xi and eta take b_dir-bit codebooks, rho takes a
-# b_nrm-bit codebook, with (b_dir, b_nrm) = (b + 1, b - 1) ([P3] "MSE-optimal
-# non-uniform bit allocation": B_tri = 2 b_dir + b_nrm); a 3x3 joint rounding
+# entry for the octahedral map); xi and eta take b_dir-bit codebooks, rho takes a
+# b_nrm-bit codebook, with (b_dir, b_nrm) = (b + 1, b - 1) ([P3] Contributions,
+# the MSE-driven uneven split of bits: B_tri = 2 b_dir + b_nrm); a 3x3 joint rounding
 # picks the final codes; the state is (gamma, I_dir, I_nrm).
 # ---------------------------------------------------------------------------
 
