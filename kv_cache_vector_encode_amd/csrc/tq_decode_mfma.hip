@@ -28,10 +28,9 @@
 // 16x16x64 integer product pairs byte s of lane l's A operand with byte s of
 // lane l's B operand the same way, so only the two must agree on the dims.
 //
-// Work: grid (split, KV-head slice of <= 8 query heads, sequence); 4 waves
-// per workgroup (4-bit codes) or 8 (2/3-bit codes, whose LDS tables the 8
-// share), each takes pairs of 16-token blocks of the split in turn and keeps
-// its own running max / sum / accumulator.
+// Work: grid (split, KV-head slice of <= 8 query heads, sequence); 8 waves
+// per workgroup, each takes pairs of 16-token blocks of the split in turn and
+// keeps its own running max / sum / accumulator.
 //
 // Memory: every wave streams its (block, KV head) chunks into a private ring
 // of LDS stages with global_load_lds (global memory straight to LDS, no
@@ -332,9 +331,10 @@ struct DecodeSmem {
   static constexpr int kTk = kI8 ? 4 : kPairs * kRep;
   static constexpr int kTv = kI8 ? kPairs : kPairs * kRep;
   static constexpr int kQSteps = kI8 ? 2 : 4;
-  // waves per workgroup: the 2/3-bit tables are shared by 8 waves, so two
-  // workgroups (16 waves) fit on a CU
-  static constexpr int kWaves = kTab ? 8 : 4;
+  // waves per workgroup: 8, so the per-workgroup set-up (tables, query
+  // rotation) and the split partials are shared by 8 waves; two workgroups
+  // (16 waves) fit on a CU
+  static constexpr int kWaves = 8;
   uint32_t tk[kTk];
   uint32_t tv[kTv];
   float qcorr[8], qmult[8];            // 8-bit logits: per-head offset and scale

@@ -416,20 +416,18 @@ int blocks_per_split_for(const tq_cache* c, int32_t num_seqs, int32_t group, int
                          bool attend) {
   const int64_t units = (int64_t)num_seqs * c->cfg.num_kv_heads * tq::decode_slices(group);
   // matrix-core kernel: at most 64 block pairs per wave, the block-table
-  // entries a wave keeps one per lane; 4 waves per workgroup with 4-bit
-  // codes, 8 with 2/3-bit codes
-  const bool b4 = c->cfg.bits_k == 4;
-  const int64_t waves = b4 ? 4 : 8;
+  // entries a wave keeps one per lane; 8 waves per workgroup
+  const int64_t waves = 8;
   const int64_t cap = mfma ? 2 * 64 * waves : 64;
   int64_t bps;
   if (mfma) {
-    // four 4-wave workgroups (4-bit codes) or two 8-wave workgroups (2/3-bit)
-    // fit on a CU: aim for one such round of them.  Short splits (a few
-    // pairs per wave) pay the per-workgroup set-up and merge more than they
-    // gain from the extra workgroups: there aim for half as many, with a
-    // whole number of pairs per wave (measured on 1 x 32768 tokens x 8 KV
-    // heads, 4-bit codes: 22 -> 32 blocks, -9%).
-    const int64_t wgs = 256 * (b4 ? 4 : 2);
+    // two 8-wave workgroups fit on a CU: aim for one such round of them
+    // (4-bit codes: 3-4% faster than four 4-wave workgroups on 16 x 8192 and
+    // 1 x 32768 tokens x 8 KV heads).  Short splits (a few pairs per wave)
+    // pay the per-workgroup set-up and merge more than they gain from the
+    // extra workgroups: there aim for half as many, with a whole number of
+    // pairs per wave.
+    const int64_t wgs = 256 * 2;
     const int64_t unit = 2 * waves;
     bps = ((int64_t)max_blocks * units + wgs - 1) / wgs;
     if (bps <= 32) bps = (((int64_t)max_blocks * units + wgs / 2 - 1) / (wgs / 2) + unit - 1) / unit * unit;

@@ -243,11 +243,11 @@ def _decode_case(device, bits, group, hkv, lens, qjl=False, dtype="bf16", scale=
 
 @pytest.mark.parametrize("bits", [3, 4])
 def test_decode_attend_longest_split(device, monkeypatch, bits):
-    # splits at the matrix-core kernel's cap (1024 blocks for 8-wave 2/3-bit
-    # workgroups, 512 for 4-wave 4-bit ones): waves of the first split take
-    # 64 block pairs each, so every lane of the per-lane block-table copy is
-    # used; 200 more tokens leave a 13-block second split.
-    cap = 512 if bits == 4 else 1024
+    # splits at the matrix-core kernel's cap (1024 blocks for its 8-wave
+    # workgroups): waves of the first split take 64 block pairs each, so
+    # every lane of the per-lane block-table copy is used; 200 more tokens
+    # leave a 13-block second split.
+    cap = 1024
     monkeypatch.setenv("TQ_BLOCKS_PER_SPLIT", str(cap))
     _decode_case(device, bits, 8, 1, [16 * cap + 200, 300])
 

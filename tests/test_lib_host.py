@@ -185,11 +185,11 @@ def test_qjl_attend_split_sizes_for_long_sequences():
 
 def test_matrix_core_attend_split_sizes():
     # Splits of the matrix-core decode-attend kernel (values, no QJL): aim
-    # at one round of workgroups, four 4-wave ones per CU with 4-bit codes
-    # (1024) and two 8-wave ones otherwise (512); when that leaves splits of
-    # at most 32 blocks, aim at half as many with whole block pairs per wave;
-    # never more than 64 block pairs per wave (a wave keeps its pairs'
-    # block-table entries one per lane): 512 blocks (4-bit), 1024 (2/3-bit).
+    # at one round of workgroups, two 8-wave ones per CU (512); when that
+    # leaves splits of at most 32 blocks, aim at half as many with whole
+    # block pairs per wave (multiples of 16 blocks); never more than 64
+    # block pairs per wave (a wave keeps its pairs' block-table entries one
+    # per lane): 1024 blocks.
     r = tq.tq_make_rotation(42, 128)
     c = tq.tq_cache_create(tq.make_config(8, 4, 4, 4, r), 0x100000)
     c._rots = (r,)
@@ -197,21 +197,21 @@ def test_matrix_core_attend_split_sizes():
     c3._rots = (r,)
     L = tq.lib()
     per = 8 * 132 * 4   # 8 query heads of the group, 132 floats each
-    # 1 x 32768 tokens: 2048 blocks, 8 units -> 16 blocks -> short: 32 blocks -> 64 splits
-    assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 2048) == 1 * 8 * 64 * per
-    # 16 x 8192 tokens: 512 blocks, 128 units -> 64 blocks -> 8 splits
-    assert L.tq_decode_workspace_bytes(c.handle, 16, 64, 512) == 16 * 8 * 8 * per
-    # 4 x 131072 tokens: 8192 blocks, 32 units -> 256 blocks -> 32 splits
-    assert L.tq_decode_workspace_bytes(c.handle, 4, 64, 8192) == 4 * 8 * 32 * per
+    # 1 x 32768 tokens: 2048 blocks, 8 units -> 32 blocks -> short: 64 blocks -> 32 splits
+    assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 2048) == 1 * 8 * 32 * per
+    # 16 x 8192 tokens: 512 blocks, 128 units -> 128 blocks -> 4 splits
+    assert L.tq_decode_workspace_bytes(c.handle, 16, 64, 512) == 16 * 8 * 4 * per
+    # 4 x 131072 tokens: 8192 blocks, 32 units -> 512 blocks -> 16 splits
+    assert L.tq_decode_workspace_bytes(c.handle, 4, 64, 8192) == 4 * 8 * 16 * per
     # 3-bit codes: 512 workgroups -> 512 blocks -> 16 splits
     assert L.tq_decode_workspace_bytes(c3.handle, 4, 64, 8192) == 4 * 8 * 16 * per
     # 3-bit, 1 x 32768 tokens: 2048 blocks, 8 units -> 32 blocks -> short: 64 blocks -> 32 splits
     assert L.tq_decode_workspace_bytes(c3.handle, 1, 64, 2048) == 1 * 8 * 32 * per
     assert L.tq_decode_workspace_bytes(c3.handle, 1, 64, 1024 * 4096) == 1 * 8 * 4096 * per
     assert L.tq_decode_workspace_bytes(c3.handle, 1, 64, 1024 * 4096 + 1) == tq.TQ_ERR_UNSUPPORTED
-    # the 512-block cap and the 4096-split limit
-    assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 512 * 4096) == 1 * 8 * 4096 * per
-    assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 512 * 4096 + 1) == tq.TQ_ERR_UNSUPPORTED
+    # the 1024-block cap and the 4096-split limit
+    assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 1024 * 4096) == 1 * 8 * 4096 * per
+    assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 1024 * 4096 + 1) == tq.TQ_ERR_UNSUPPORTED
 
 
 def test_decompress_argument_checks_happen_before_the_device():
