@@ -268,7 +268,10 @@ template <int BITS>
 struct BlockRegs {
   uint32_t k[BITS];     // 32 codes: dims 32g .. 32g+31 of token row m
   uint32_t v[4];        // 8 codes each: dims 8m .. 8m+7 of tokens 4g .. 4g+3
-  uint32_t gk[2];       // fp16 norms of tokens 4g .. 4g+3
+};
+// fp16 norms of tokens 4g .. 4g+3 of the lane's own block of the pair
+struct PairNorms {
+  uint32_t gk[2];
   uint32_t gv[2];
 };
 
@@ -303,14 +306,27 @@ __device__ __forceinline__ void read_chunk(BlockRegs<BITS>& r, const uint8_t* st
       r.v[i] = __builtin_amdgcn_alignbyte(hi, lo, (uint32_t)(off & 3)) & 0xFFFFFFu;
     }
   }
-  const uint2 a = *reinterpret_cast<const uint2*>(st + C::kOffGK + 8 * g);
-  const uint2 b = *reinterpret_cast<const uint2*>(st + C::kOffGV + 8 * g);
+}
+
+// the norms of the lane's own block: own = st + (lane's block of the pair) * slot
+template <int BITS>
+__device__ __forceinline__ void read_norms(PairNorms& r, const uint8_t* own, int g) {
+  using C = Chunk<BITS>;
+  const uint2 a = *reinterpret_cast<const uint2*>(own + C::kOffGK + 8 * g);
+  const uint2 b = *reinterpret_cast<const uint2*>(own + C::kOffGV + 8 * g);
   r.gk[0] = a.x; r.gk[1] = a.y;
   r.gv[0] = b.x; r.gv[1] = b.y;
 }
 
-__device__ __forceinline__ float half_lo(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w & 0xFFFF))); }
-__device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w >> 16))); }
+// a * (the fp16 value in the low / high half of h), left to the compiler so
+// that it forms a mixed-precision product (v_fma_mix) and pads its hazards
+// (a product right after a transcendental needs a wait state)
+__device__ __forceinline__ float mul_h_lo(float a, uint32_t h) {
+  return a * (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xFFFFu));
+}
+__device__ __forceinline__ float mul_h_hi(float a, uint32_t h) {
+  return a * (float)__builtin_bit_cast(_Float16, (uint16_t)(h >> 16));
+}
 
 // LDS of one workgroup, in one object so the tables sit at address 0 (a
 // lookup address then fits the instruction's offset field).
@@ -704,7 +720,7 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
   const float kc = kI8 ? sm.qcorr[m & 7] * kmult : 0.f;
   const KeyI8Tab kt = {a.ki8_hi[0], a.ki8_hi[1], a.ki8_lo[0], a.ki8_lo[1]};
 
-  auto compute_pair = [&](const BlockRegs<BITS>(&cur)[2], int lb0) {
+  auto compute_pair = [&](const BlockRegs<BITS>(&cur)[2], const PairNorms& nrm, int lb0) {
     // ---- logits of the two blocks (log2 units)
     float fv[2][4];   // this lane's column of each block's product
     if constexpr (kI8) {
@@ -806,11 +822,10 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
     }
 
     // ---- this lane's 4 logits: tokens 4g .. 4g+3 of block xo, head m % 8
-    const uint32_t gk2[2] = {col_lo ? cur[1].gk[0] : cur[0].gk[0], col_lo ? cur[1].gk[1] : cur[0].gk[1]};
-    const uint32_t gv2[2] = {col_lo ? cur[1].gv[0] : cur[0].gv[0], col_lo ? cur[1].gv[1] : cur[0].gv[1]};
+    const uint32_t(&gv2)[2] = nrm.gv;
     float s[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s[j] = cs[j] * ((j & 1) ? half_hi(gk2[j >> 1]) : half_lo(gk2[j >> 1]));
+    for (int j = 0; j < 4; ++j) s[j] = (j & 1) ? mul_h_hi(cs[j], nrm.gk[j >> 1]) : mul_h_lo(cs[j], nrm.gk[j >> 1]);
     const int tok0 = (lb0 + xo) * kBlock + 4 * g;
     if ((lb0 + 2) * kBlock > tok_end) {   // pair reaches past the split's last token
 #pragma unroll
@@ -883,7 +898,7 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
         for (int u = 0; u < 2; ++u) {
           const float p = __builtin_amdgcn_exp2f(s[2 * q + u] - mref);
           run_l += p;
-          pv[u] = p * (u ? half_hi(gv2[q]) : half_lo(gv2[q]));
+          pv[u] = u ? mul_h_hi(p, gv2[q]) : mul_h_lo(p, gv2[q]);
         }
         // f16(pv) (rounded toward zero) and the f16 of its residual, exact in f32
         const auto ph = __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]);
@@ -910,6 +925,7 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
   // The loop is unrolled by the ring depth, so each stage's LDS offset is a
   // constant of the read instructions.
   const uint8_t* ring = s_ring + wv * C::kWaveRing;
+  const int own_slot = col_lo ? C::kSlot : 0;   // the lane's block of the pair
   auto step = [&](int k, int u) {   // pair k sits in stage u = k % NS
     wait_pairs_behind<BITS>(min(NS - 1, my_n - 1 - k));
     // the block-table loads are older than the copy just waited for; this
@@ -917,14 +933,16 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
     asm volatile("" : "+v"(ids0), "+v"(ids1));
     const uint8_t* st = ring + u * 2 * C::kSlot;
     BlockRegs<BITS> cur[2];
+    PairNorms nrm;
     read_chunk<BITS>(cur[0], st, m, g);
     read_chunk<BITS>(cur[1], st + C::kSlot, m, g);
+    read_norms<BITS>(nrm, st + own_slot, g);
     if (k + NS < my_n) {
       // the stage is overwritten only after this wave's reads of it are done
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       dma_pair(k + NS, (int)__builtin_amdgcn_readlane(ids0, k + NS), (int)__builtin_amdgcn_readlane(ids1, k + NS));
     }
-    compute_pair(cur, sb0 + 2 * (wv + NW * k));
+    compute_pair(cur, nrm, sb0 + 2 * (wv + NW * k));
   };
   for (int k0 = 0; k0 < my_n; k0 += NS) {
 #pragma unroll
