@@ -383,14 +383,71 @@ __device__ __forceinline__ uint32_t lds_word(const uint32_t* table, uint32_t byt
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(table) + byte_addr);
 }
 
-// d (lanes of the enabled banks only) = (x of the lane 8 columns away) * m,
-// a 24-bit multiply: with m = 1 or 65536 it places a half in the low or the
-// high half of the word.  Lanes outside BANKS keep d.
-template <int BANKS>
-__device__ __forceinline__ void mul_ror8_banks(uint32_t& d, uint32_t x, uint32_t m) {
+// s[j] = gamma_k * logit of token 4g + j, from the two blocks' logit
+// products f0 / f1 of the table path (column m of a block holds the q_hi
+// part of head m % 8 for m < 8, the q_lo part for m >= 8).  Lanes m < 8 take
+// block 0, lanes m >= 8 block 1: each adds its own column and the one 8
+// columns away, as two adds that write one lane half each (banks 0, 1 /
+// banks 2, 3 of every row); then the product with the fp16 norm (low / high
+// half of gk[j / 2]) as one mixed-precision multiply-add.  f0 and f1 are
+// matrix-core results read here by DPP: the leading s_nops give that read
+// more wait states than the 16x16x32 products need.
+__device__ __forceinline__ void logits_tab(const f32x4& f0, const f32x4& f1, const uint32_t (&gk)[2], float (&s)[4]) {
+  float c0, c1, c2, c3;
+  asm volatile("s_nop 7\n\ts_nop 4\n\t"
+      "v_add_f32_dpp %4, %8, %8 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %4, %12, %12 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %5, %9, %9 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %5, %13, %13 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %6, %10, %10 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %6, %14, %14 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %7, %11, %11 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %7, %15, %15 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_fma_mix_f32 %0, %4, %16, 0 op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mix_f32 %1, %5, %16, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mix_f32 %2, %6, %17, 0 op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mix_f32 %3, %7, %17, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+      : "=&v"(s[0]), "=&v"(s[1]), "=&v"(s[2]), "=&v"(s[3]), "=&v"(c0), "=&v"(c1), "=&v"(c2), "=&v"(c3)
+      : "v"(f0[0]), "v"(f0[1]), "v"(f0[2]), "v"(f0[3]), "v"(f1[0]), "v"(f1[1]), "v"(f1[2]), "v"(f1[3]),
+        "v"(gk[0]), "v"(gk[1]));
+}
+
+// s[j] = c[j] * the fp16 norm in the low / high half of gk[j / 2], as
+// mixed-precision multiply-adds (c are ordinary vector results, not
+// transcendental ones, so no extra wait state is needed)
+__device__ __forceinline__ void scale_by_norms(const float (&c)[4], const uint32_t (&gk)[2], float (&s)[4]) {
+  asm("v_fma_mix_f32 %0, %4, %8, 0 op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mix_f32 %1, %5, %8, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mix_f32 %2, %6, %9, 0 op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mix_f32 %3, %7, %9, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+      : "=&v"(s[0]), "=&v"(s[1]), "=&v"(s[2]), "=&v"(s[3])
+      : "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]), "v"(gk[0]), "v"(gk[1]));
+}
+
+// B operands of the table path's two value products, built from hv[j] (f16
+// bits of p gamma_v of token 4g + j in the low half, high half zero) and
+// hi[j] = hv[j] << 16:
+//   block 0 (becomes hv): lanes c < 8 keep their own hv; lanes c >= 8 take
+//     the hv of lane c - 8 times 65536 (its high half);
+//   block 1 (becomes hi): lanes c >= 8 keep their own hv << 16; lanes c < 8
+//     take the hv of lane c + 8.
+// The block-1 copies run first, while every lane's hv is still its own.
+// m holds 65536 in the lanes c >= 8.  The leading s_nop gives the DPP reads
+// of hv their two wait states; the closing one separates the last DPP write
+// from the matrix-core reads of the operands.
+__device__ __forceinline__ void value_b_tab(uint32_t (&hv)[4], uint32_t (&hi)[4], uint32_t m) {
   asm("s_nop 1\n\t"
-      "v_mul_u32_u24_dpp %0, %1, %2 row_ror:8 row_mask:0xf bank_mask:%3"
-      : "+v"(d) : "v"(x), "v"(m), "n"(BANKS));
+      "v_mov_b32_dpp %4, %0 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_mov_b32_dpp %5, %1 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_mov_b32_dpp %6, %2 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_mov_b32_dpp %7, %3 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_mul_u32_u24_dpp %0, %0, %8 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_mul_u32_u24_dpp %1, %1, %8 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_mul_u32_u24_dpp %2, %2, %8 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_mul_u32_u24_dpp %3, %3, %8 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "s_nop 1"
+      : "+v"(hv[0]), "+v"(hv[1]), "+v"(hv[2]), "+v"(hv[3]), "+v"(hi[0]), "+v"(hi[1]), "+v"(hi[2]), "+v"(hi[3])
+      : "v"(m));
 }
 
 // Decode step: encode the sequence's new token (keys and values of KV head
@@ -697,7 +754,7 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const uint32_t r4 = (uint32_t)(lane & 31) << 2;             // this lane's table copy
-  const uint32_t par_shift = col_lo ? 16u : 0u, par_mul = col_lo ? 65536u : 1u;
+  const uint32_t par_mul = col_lo ? 65536u : 1u;
   const float v_unscale = a.f16_v.unscale;
   float run_m = -INFINITY, run_l = 0.f;
 
@@ -722,7 +779,8 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
 
   auto compute_pair = [&](const BlockRegs<BITS>(&cur)[2], const PairNorms& nrm, int lb0) {
     // ---- logits of the two blocks (log2 units)
-    float fv[2][4];   // this lane's column of each block's product
+    float fv[2][4];   // 8-bit path: this lane's column of each block's product
+    f32x4 ck[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // table path: the products
     if constexpr (kI8) {
       // signed-byte planes of the centroids built on the vector unit, two
       // 64-dim steps per block, one product chain per (block, plane)
@@ -752,7 +810,6 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
       // holds the scaled halves of its codes 8st .. 8st+7 (dims 32g + 8st +
       // 0..7 of token row m), one table read per two codes
       const uint32_t* const tk = sm.tk;
-      f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
@@ -760,24 +817,24 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
           u32x4 av;
 #pragma unroll
           for (int q = 0; q < 4; ++q) av[q] = lds_word(tk, pair_addr<2 * BITS>(cur[X].k, 4 * st + q, r4));
-          c[X] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av),
-                                                        __builtin_bit_cast(f16x8, qreg[st]), c[X], 0, 0, 0);
+          ck[X] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av),
+                                                         __builtin_bit_cast(f16x8, qreg[st]), ck[X], 0, 0, 0);
         }
-#pragma unroll
-      for (int X = 0; X < 2; ++X)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fv[X][j] = c[X][j];
     }
-    // own block's part, plus the other part from the lane 8 columns away
-    float cs[4];
-    {
-      float send[4];
+    // own block's part, plus the other part from the lane 8 columns away,
+    // times the token's key norm: the table path does both in logits_tab
+    float s[4];
+    if constexpr (kTab) {
+      logits_tab(ck[0], ck[1], nrm.gk, s);
+    } else {
+      float cs[4], send[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        cs[j] = kI8 ? fmaf(col_lo ? fv[1][j] : fv[0][j], w_own, kc) : (col_lo ? fv[1][j] : fv[0][j]);
+        cs[j] = fmaf(col_lo ? fv[1][j] : fv[0][j], w_own, kc);
         send[j] = col_lo ? fv[0][j] : fv[1][j];
       }
       fmac_ror8_4(cs, send, w_par);
+      scale_by_norms(cs, nrm.gk, s);
     }
     // ---- value operands: table reads issued before the softmax needs them
     u32x4 va[8];
@@ -823,9 +880,6 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
 
     // ---- this lane's 4 logits: tokens 4g .. 4g+3 of block xo, head m % 8
     const uint32_t(&gv2)[2] = nrm.gv;
-    float s[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s[j] = (j & 1) ? mul_h_hi(cs[j], nrm.gk[j >> 1]) : mul_h_lo(cs[j], nrm.gk[j >> 1]);
     const int tok0 = (lb0 + xo) * kBlock + 4 * g;
     if ((lb0 + 2) * kBlock > tok_end) {   // pair reaches past the split's last token
 #pragma unroll
@@ -863,7 +917,7 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
       // their own block's p: the other block's comes from the lane 8 columns
       // away (block 0 into lanes c >= 8, block 1 into lanes c < 8).
       // (the value table holds S_v c: 1/S_v is applied when the waves merge)
-      uint32_t hv[4];
+      uint32_t hv[4], hi[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float p = __builtin_amdgcn_exp2f(s[j] - mref);
@@ -871,17 +925,10 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
         const uint32_t gw = gv2[j >> 1];
         const _Float16 gh = __builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? (gw >> 16) : (gw & 0xFFFFu)));
         hv[j] = __builtin_bit_cast(uint16_t, (_Float16)(p * (float)gh));
+        hi[j] = hv[j] << 16;
       }
-      u32x4 b0, b1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t own = hv[j] << par_shift;
-        uint32_t x0 = own, x1 = own;
-        mul_ror8_banks<0xC>(x0, hv[j], par_mul);
-        mul_ror8_banks<0x3>(x1, hv[j], par_mul);
-        b0[j] = x0;
-        b1[j] = x1;
-      }
+      value_b_tab(hv, hi, par_mul);
+      const u32x4 b0 = {hv[0], hv[1], hv[2], hv[3]}, b1 = {hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
       for (int T = 0; T < 4; ++T) {
         acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, va[T]),
