@@ -231,22 +231,21 @@ __device__ __forceinline__ void mx_setup(const EncodeArgs& a, MxShared<BITS>& sh
     const uint32_t sb = (wd >> (8 * gg)) & 0xFFu;
     sh.smask[gg][k][q] = (((sb >> (2 * q)) & 1u) << 15) | (((sb >> (2 * q + 1)) & 1u) << 31);
   }
-  const uint32_t one = DT == 2 ? 0x3F80u : 0x3C00u;
-  const int lane = tid & 63, i = lane & 15, gp = lane >> 4;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int e = 2 * w + h;
-      const uint32_t neg = ((i & e) ^ ((i >> 1) & (e >> 1)) ^ ((i >> 2) & gp) ^ ((i >> 3) & (gp >> 1))) & 1u;
-      word |= (one | (neg << 15)) << (16 * h);
-    }
-    B[0][w] = word;
-    B[1][w] = w >= 2 ? word ^ 0x80008000u : word;
-    B[2][w] = B[0][w] ^ 0x80008000u;
-    B[3][w] = B[1][w] ^ 0x80008000u;
-  }
+  // Element e = 2 w + h of B0 at lane (g', i) is negative iff
+  // i0 e0 + i1 e1 + i2 g'0 + i3 g'1 is odd.  Elements e and e + 4 agree, so
+  // B0 = {w0, w1, w0, w1}: w0 (e = 0, 1) carries the lane parity c in both
+  // halves and i0 in the high half, w1 (e = 2, 3) also i1 in both halves.
+  const uint32_t one2 = DT == 2 ? 0x3F803F80u : 0x3C003C00u;
+  const uint32_t lane = (uint32_t)(tid & 63);
+  const uint32_t y = (lane >> 2) & (lane >> 4);            // bit 0: i2 g'0, bit 1: i3 g'1
+  const uint32_t c = (y ^ (y >> 1)) & 1u;
+  const uint32_t w0 = one2 ^ (c ? 0x80008000u : 0u) ^ ((lane & 1u) << 31);
+  const uint32_t w1 = w0 ^ ((lane & 2u) ? 0x80008000u : 0u);
+  const uint32_t n0 = w0 ^ 0x80008000u, n1 = w1 ^ 0x80008000u;
+  B[0] = (u32x4_t){w0, w1, w0, w1};
+  B[1] = (u32x4_t){w0, w1, n0, n1};
+  B[2] = (u32x4_t){n0, n1, n0, n1};
+  B[3] = (u32x4_t){n0, n1, w0, w1};
 }
 
 // One batch: this lane's share of vector j (dims 32 k + 8 g .. +7 in X[k]),
