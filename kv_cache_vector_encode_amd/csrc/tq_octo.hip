@@ -40,14 +40,15 @@ struct Octo {
 
 constexpr int kOctoRowPad = 132;   // LDS floats per row: 128 coordinates, zero pad
 
-// Padded index (column + 1) of the lower of the two grid columns whose
-// centres -1 + (2 j + 1) / nd bracket v: v's cell j = floor((v + 1) nd / 2)
-// and j - 1 when v lies in the lower half of that cell, j and j + 1 in the
-// upper half; i.e. floor((v + 1) nd / 2 + 1/2), clamped to [0, nd] (0 and nd
-// select the NaN border next to the outer columns).
-__device__ __forceinline__ int octo_block_lo1(float v, int nd) {
-  const int h = (int)floorf(__builtin_fmaf(v, 0.5f * (float)nd, 0.5f * (float)nd + 0.5f));
-  return min(max(h, 0), nd);
+// The lower of the two grid columns whose centres -1 + (2 j + 1) / nd
+// bracket v: with v in cell j = floor((v + 1) nd / 2), columns j - 1, j when
+// v lies in the lower half of the cell, j, j + 1 in the upper half; i.e.
+// floor((v + 1) nd / 2 - 1/2).  Clamped to [0, nd - 2], so both columns lie
+// on the grid: next to an outer column the pair is that column and its
+// neighbour, a superset of the pair's part on the grid.
+__device__ __forceinline__ int octo_block_lo(float v, int nd) {
+  const int h = (int)floorf(__builtin_fmaf(v, 0.5f * (float)nd, 0.5f * (float)nd - 0.5f));
+  return min(max(h, 0), nd - 2);
 }
 
 // atan(a) for a in [0, 1] as a * P(a^2), P of degree 7: the odd polynomial
@@ -96,22 +97,14 @@ __device__ __forceinline__ void oct_map(float nx, float ny, float nz, float& xi,
 template <int B, int DT>
 __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
   using C = Octo<B>;
-  // direction table with a one-cell border of NaN entries: the 3x3 window of
-  // any cell is then 9 fixed offsets, and a border candidate's projection is
-  // NaN, which never wins a comparison (IEEE compares: the library is built
-  // without fast-math)
-  constexpr int kP = C::kNd + 2;
-  __shared__ float4 s_dir[kP * kP];
+  // direction table [xi code][eta code], (x, y, z, 0) per entry
+  constexpr int kNd = C::kNd;
+  __shared__ float4 s_dir[kNd * kNd];
   __shared__ float s_y[16][kOctoRowPad];
   __shared__ uint32_t s_rec[16][C::kWords];
   const int tid = threadIdx.x, row = tid >> 4;
   const int L = tid & 15, ell = perm16(L);
-  for (int i = tid; i < kP * kP; i += 256) {
-    const int pr = i / kP, pc = i - pr * kP;
-    const bool in = pr >= 1 && pr <= C::kNd && pc >= 1 && pc <= C::kNd;
-    s_dir[i] = in ? reinterpret_cast<const float4*>(a.dirs)[(pr - 1) * C::kNd + (pc - 1)]
-                  : make_float4(NAN, NAN, NAN, NAN);
-  }
+  for (int i = tid; i < kNd * kNd; i += 256) s_dir[i] = reinterpret_cast<const float4*>(a.dirs)[i];
   const uint32_t sneg = sign_byte(a.rot, ell);
   uint32_t smask[8];
 #pragma unroll
@@ -170,30 +163,30 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
       const float nz = rho > 0.f ? tz * __builtin_amdgcn_rcpf(rho) : 1.f;
       float xi, eta;
       oct_map(tx, ty, fminf(fmaxf(nz, -1.f), 1.f), xi, eta);
-      const int a1 = octo_block_lo1(xi, C::kNd), c1 = octo_block_lo1(eta, C::kNd);
+      const int a0 = octo_block_lo(xi, kNd), c0 = octo_block_lo(eta, kNd);
       // For a unit direction n_hat the error with the best norm code is
       // rho^2 + min_k (c_k^2 - 2 c_k p), p = t . n_hat; every c_k > 0, so
       // that minimum falls as p grows: the 3x3 joint rounding takes the
       // candidate of largest projection (first on ties, xi-major), then the
       // norm code nearest to its p.  That candidate always lies in the 2x2
       // block of the window on the side of the point's quadrant of its cell
-      // (columns a1 - 1, a1 and rows c1 - 1, c1): a dense float64 scan of the
+      // (columns a0, a0 + 1 and rows c0, c0 + 1): a dense float64 scan of the
       // (xi, eta) square at every bit width finds the best projection of the
       // other five cells never above the block's, equal only on the folds of
       // the map, where mirror cells tie.  So only the block is scanned.
-      const int base = a1 * kP + c1;   // padded entry of cell (a1 - 1, c1 - 1)
+      const int base = a0 * kNd + c0;
       float best = -INFINITY;
       int bo = 0;
 #pragma unroll
       for (int o = 0; o < 4; ++o) {
-        const float4 d = s_dir[base + (o >> 1) * kP + (o & 1)];
+        const float4 d = s_dir[base + (o >> 1) * kNd + (o & 1)];
         const float p = tx * d.x + ty * d.y + tz * d.z;
         if (p > best) {
           best = p;
           bo = o;
         }
       }
-      const int ca = a1 - 1 + (bo >> 1), cc = c1 - 1 + (bo & 1);
+      const int ca = a0 + (bo >> 1), cc = c0 + (bo & 1);
       // norm code: the number of ascending thresholds below p (seven
       // independent compares at b = 4; a binary search's dependent chain of
       // compares and selects measured 10% slower)
@@ -344,11 +337,11 @@ int launch_octo_encode(const OctoArgs& a, int bits, void* stream) {
   if (a.n <= 0) return (int)hipErrorInvalidValue;
   // The direction table is loaded once per workgroup, and each workgroup
   // loops over groups of 16 vectors.  As many workgroups as fit on the 256
-  // CUs at once, so the whole grid is resident in one round: 5 per CU at
-  // b = 4 (28 KB of LDS each), 8 (the wave limit) at b = 2, 3.  Measured
-  // against 4 per CU: 64.4 against 69.8 us (b = 4, 262k vectors), 746
-  // against 850 us (b = 3, 4.2M vectors).
-  const int64_t cap = 256 * (bits == 4 ? 5 : 8);
+  // CUs at once, so the whole grid is resident in one round: 6 per CU at
+  // b = 4 (25.6 KB of LDS each), 8 (the wave limit) at b = 2, 3.  Measured
+  // against 4 per CU: 746 against 850 us (b = 3, 4.2M vectors); b = 4 with
+  // a bordered 28 KB table, 5 per CU: 64.4 against 69.8 us (262k vectors).
+  const int64_t cap = 256 * (bits == 4 ? 6 : 8);
   const dim3 grid((unsigned)(groups < cap ? groups : cap));
   switch (bits) {
     case 2: octo_enc<2>(a, grid, s); break;

@@ -9,8 +9,9 @@ over the other five cells never exceeds the block's.  This test checks that
 property in float64 on the stored (fp32) direction tables at every bit width:
 random points over the whole square, thin strips along the outer edges (where
 the map folds the square's border onto itself and mirror cells tie) and along
-the interior folds (xi = 0, eta = 0, |xi| + |eta| = 1).  It also checks that
-the kernel's half-cell index gives the oracle's cell.
+the interior folds (xi = 0, eta = 0, |xi| + |eta| = 1).  The block is formed
+as in the kernel: the two grid columns (rows) whose centres bracket xi (eta),
+and next to an outer column that column and its neighbour.
 """
 
 import numpy as np
@@ -19,22 +20,22 @@ import pytest
 from oracle import tq_oracle as O
 
 
+def _block_lo(v, nd):
+    """Lower column of the block, as the kernel forms it: the lower of the two
+    column centres around v, floor((v + 1) nd / 2 - 1/2), clamped to
+    [0, nd - 2] (next to an outer column: that column and its neighbour)."""
+    return np.clip(np.floor((v + 1.0) * (nd / 2) - 0.5).astype(np.int64), 0, nd - 2)
+
+
 def _block_margin(xi, eta, dirs, nd):
     """(best projection in the quadrant block) - (best over the other cells
     of the 3x3 window), for the unit directions at (xi, eta)."""
     n = O.oct_unmap(xi, eta)
     jx = np.clip(np.floor((xi + 1.0) * (nd / 2)).astype(np.int64), 0, nd - 1)
     je = np.clip(np.floor((eta + 1.0) * (nd / 2)).astype(np.int64), 0, nd - 1)
-    hx = np.clip(np.floor((xi + 1.0) * nd).astype(np.int64), 0, 2 * nd - 1)
-    he = np.clip(np.floor((eta + 1.0) * nd).astype(np.int64), 0, 2 * nd - 1)
-    # the kernel's half-cell index reproduces the oracle's cell
-    assert np.array_equal(hx >> 1, jx) and np.array_equal(he >> 1, je)
-    a0 = (hx >> 1) - 1 + (hx & 1)
-    c0 = (he >> 1) - 1 + (he & 1)
-    # the kernel's form: the lower of the two column centres around v, plus 1
-    a1 = np.clip(np.floor((xi + 1.0) * (nd / 2) + 0.5).astype(np.int64), 0, nd)
-    c1 = np.clip(np.floor((eta + 1.0) * (nd / 2) + 0.5).astype(np.int64), 0, nd)
-    assert np.array_equal(a1 - 1, a0) and np.array_equal(c1 - 1, c0)
+    a0, c0 = _block_lo(xi, nd), _block_lo(eta, nd)
+    # the block lies inside the window of the point's cell
+    assert np.all((a0 >= jx - 1) & (a0 + 1 <= jx + 1) & (c0 >= je - 1) & (c0 + 1 <= je + 1))
     best_in = np.full(xi.shape, -np.inf)
     best_out = np.full(xi.shape, -np.inf)
     for da in (-1, 0, 1):
@@ -79,17 +80,14 @@ def test_block_scan_matches_the_full_window_on_the_oracles_codes():
         ref = O.octo_encode_triplets(t, b, dirs, crho)
         rho = np.sqrt(np.sum(t * t, axis=-1))
         xi, eta = O.oct_map(t / rho[:, None])
-        hx = np.clip(np.floor((xi + 1.0) * nd).astype(np.int64), 0, 2 * nd - 1)
-        he = np.clip(np.floor((eta + 1.0) * nd).astype(np.int64), 0, 2 * nd - 1)
-        a0, c0 = (hx >> 1) - 1 + (hx & 1), (he >> 1) - 1 + (he & 1)
+        a0, c0 = _block_lo(xi, nd), _block_lo(eta, nd)
         best = np.full(rho.shape, -np.inf)
         A = np.zeros(rho.shape, np.int64)
         C = np.zeros(rho.shape, np.int64)
         for da in (0, 1):
             for dc in (0, 1):
                 a, c = a0 + da, c0 + dc
-                ok = (a >= 0) & (a < nd) & (c >= 0) & (c < nd)
-                p = np.where(ok, np.sum(t * dirs[np.clip(a, 0, nd - 1), np.clip(c, 0, nd - 1)], axis=-1), -np.inf)
+                p = np.sum(t * dirs[a, c], axis=-1)
                 take = p > best
                 best, A, C = np.where(take, p, best), np.where(take, a, A), np.where(take, c, C)
         assert np.array_equal(A, ref["a"]) and np.array_equal(C, ref["c"]), b
