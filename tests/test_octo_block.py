@@ -91,3 +91,34 @@ def test_block_scan_matches_the_full_window_on_the_oracles_codes():
                 take = p > best
                 best, A, C = np.where(take, p, best), np.where(take, a, A), np.where(take, c, C)
         assert np.array_equal(A, ref["a"]) and np.array_equal(C, ref["c"]), b
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_map_error_leaves_the_block_choice(b):
+    """The GPU map is approximate (a polynomial arctangent within 1.6e-7 rad,
+    fp32 arithmetic), so its xi and eta differ slightly from the oracle's.
+    Shifted by 2e-5 in any direction (about 100 times that), the block still
+    holds the window's best cell."""
+    dirs, _ = O.octo_codebooks(128, b)
+    nd = 1 << O.octo_bits(b)[0]
+    rng = np.random.default_rng(31 + b)
+    xi, eta = rng.uniform(-1, 1, 400_000), rng.uniform(-1, 1, 400_000)
+    n = O.oct_unmap(xi, eta)
+    jx = np.clip(np.floor((xi + 1.0) * (nd / 2)).astype(np.int64), 0, nd - 1)
+    je = np.clip(np.floor((eta + 1.0) * (nd / 2)).astype(np.int64), 0, nd - 1)
+    best = np.full(xi.shape, -np.inf)
+    A = np.zeros(xi.shape, np.int64)
+    C = np.zeros(xi.shape, np.int64)
+    for da in (-1, 0, 1):
+        for dc in (-1, 0, 1):
+            a, c = jx + da, je + dc
+            ok = (a >= 0) & (a < nd) & (c >= 0) & (c < nd)
+            p = np.where(ok, np.sum(n * dirs[np.clip(a, 0, nd - 1), np.clip(c, 0, nd - 1)], axis=-1), -np.inf)
+            take = p > best
+            best, A, C = np.where(take, p, best), np.where(take, a, A), np.where(take, c, C)
+    for sx in (-1.0, 1.0):
+        for sy in (-1.0, 1.0):
+            a0 = _block_lo(np.clip(xi + sx * 2e-5, -1, 1), nd)
+            c0 = _block_lo(np.clip(eta + sy * 2e-5, -1, 1), nd)
+            inside = ((A == a0) | (A == a0 + 1)) & ((C == c0) | (C == c0 + 1))
+            assert np.all(inside), int(np.sum(~inside))
