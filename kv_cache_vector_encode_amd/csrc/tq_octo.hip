@@ -218,16 +218,25 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
 // coordinate rho_hat * n_hat[comp] of key l%16, unpacked from the tile's
 // records in LDS.  Each wave takes 16-key tiles in turn.
 constexpr int kOctoMfmaTile = 128;   // keys per tile step (2 tiles of 16 per wave)
-constexpr int kOctoMfmaWgs = 1024;   // workgroups of a launch (spread over the heads)
 
+// 5 waves per SIMD at b = 2, 3 (the kernel held to 96 VGPRs: 248 against
+// 263 us on the 4.2M keys of llama70b at b = 3); at b = 4 that limit spills
+// and measured slower, so it keeps 4
 template <int B>
-__global__ __launch_bounds__(256) void octo_logits_mfma_kernel(const OctoArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B == 4 ? 4 : 5))) void octo_logits_mfma_kernel(
+    const OctoArgs a) {
   using C = Octo<B>;
   constexpr int kStride = C::kWords + 1;
   constexpr int kQd = 132;
   __shared__ float4 s_dir[C::kNd * C::kNd];
-  __shared__ float s_q[16][kQd];
-  __shared__ uint32_t s_rec[kOctoMfmaTile * kStride];
+  // the rotated queries are read into registers once, before the first
+  // tile's records are staged: the two share their LDS
+  __shared__ union {
+    float q[16][kQd];
+    uint32_t rec[kOctoMfmaTile * kStride];
+  } s_u;
+  auto& s_q = s_u.q;
+  uint32_t* const s_rec = s_u.rec;
   __shared__ float s_rho[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y;
@@ -270,7 +279,8 @@ __global__ __launch_bounds__(256) void octo_logits_mfma_kernel(const OctoArgs a)
   // the workgroup walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... of
   // its head, so the table and the queries are set up once per workgroup;
   // the next tile's records are loaded into registers while this one is
-  // multiplied
+  // multiplied (the barrier at the top of the tile loop also orders the
+  // reads of s_q above before the first records overwrite it)
   const int64_t ntiles = (a.n + kOctoMfmaTile - 1) / kOctoMfmaTile;
   constexpr int kPre = (kOctoMfmaTile * C::kWords + 255) / 256;
   uint32_t pre[kPre];
@@ -361,10 +371,12 @@ int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.n <= 0 || a.heads < 1 || a.heads > 65535 || a.group < 1 || a.group > kOctoMaxGroup)
     return (int)hipErrorInvalidValue;
-  // about kOctoMfmaWgs workgroups in all, each looping over tiles of its
-  // head (the table and the queries are set up once per workgroup)
-  const int64_t tiles = std::min((a.n + kOctoMfmaTile - 1) / kOctoMfmaTile,
-                                 std::max<int64_t>(1, kOctoMfmaWgs / a.heads));
+  // about as many workgroups as are resident at once (waves per SIMD: 4 at
+  // b = 4, 5 at b = 2, 3, one workgroup's wave on each SIMD), spread over
+  // the heads, each looping over tiles of its head (the table and the
+  // queries are set up once per workgroup)
+  const int64_t wgs = 256 * (bits == 4 ? 4 : 5);
+  const int64_t tiles = std::min((a.n + kOctoMfmaTile - 1) / kOctoMfmaTile, std::max<int64_t>(1, wgs / a.heads));
   const dim3 grid((unsigned)tiles, (unsigned)a.heads);
   switch (bits) {
     case 2: octo_log_mfma<2>(a, grid, s); break;
