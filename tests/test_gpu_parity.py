@@ -687,6 +687,30 @@ def test_octo_encode_matches_oracle(device, bits, dt):
     _say("  codes off the oracle's pick (near ties):", nmis)
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_octo_encode_workgroups_loop_over_groups(device, bits):
+    """More groups of 16 vectors than the encoder launches workgroups (1536
+    at 4 bits, 2048 at 2 and 3): half the workgroups code a second group
+    with the prefetched input, and the last group is ragged.  Every code and
+    norm against the oracle."""
+    wgs = 1536 if bits == 4 else 2048
+    n = wgs * 16 * 3 // 2 + 7
+    w = W.DECODE_32K.with_(seq_len=n // 8 + 1, num_kv_heads=8)
+    kb, k64 = W.keys(w)
+    kb = np.ascontiguousarray(kb.reshape(-1, 128)[:n])
+    x64 = k64.reshape(-1, 128)[:n].copy()
+    rot = tq.tq_make_rotation(42, 128)
+    tb = _octo_tables_dev(bits, device)
+    rb = tq.tq_octo_record_bytes(128, bits)
+    codes = torch.full((n, rb), 0xA5, dtype=torch.uint8, device=device)
+    gamma = torch.zeros(n, dtype=torch.int16, device=device)
+    _say("octo encode loop", bits, n)
+    tq.tq_octo_encode(to_device(kb, "bf16", device), bits, rot, tb, codes, gamma)
+    torch.cuda.synchronize()
+    nmis = check_octo_codes(codes.cpu().numpy(), gamma.cpu().numpy().view(np.float16), x64, bits, 42)
+    _say("  codes off the oracle's pick (near ties):", nmis)
+
+
 @pytest.mark.parametrize("bits,group", [(2, 1), (3, 4), (3, 5), (2, 12), (4, 8), (4, 16)])
 def test_octo_logits_match_oracle(device, bits, group):
     """Logits straight from the records against the oracle's original-frame
