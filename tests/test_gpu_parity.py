@@ -252,6 +252,65 @@ def test_decode_attend_longest_split(device, monkeypatch, bits):
     _decode_case(device, bits, 8, 1, [16 * cap + 200, 300])
 
 
+def test_pool_beyond_4gib(device):
+    """A 5.4 GB pool (3-bit keys and values, 8 KV heads, 420,000 blocks): the
+    encoder's 64-bit offset path (the pool is past 4 GiB), and the decode's
+    and the decompression's block addressing past 4 GiB.  Two sequences'
+    blocks sit across the 4 GiB boundary and at the top of the pool.  Their
+    blocks, copied into a compact cache, equal a direct encode of the same
+    tokens into it; decode-attend and decompression give bit-equal results on
+    both pools; the compact cache's outputs and logits match the oracle."""
+    nb_big = 420_000
+    w = W.DECODE_32K.with_(num_seqs=2, seq_len=300, num_kv_heads=8, num_q_heads=64, bits_k=3, bits_v=3)
+    per_block = tq.tq_cache_bytes(tq.make_config(8, 1, 3, 3, tq.tq_make_rotation(w.rot_seed, 128)))
+    boundary = (1 << 32) // per_block                    # the first block that starts past 4 GiB
+    ids = np.concatenate([np.arange(boundary - 10, boundary + 10), np.arange(nb_big - 20, nb_big)])
+    assert ids.size >= w.num_blocks and nb_big * per_block > (1 << 32) + per_block
+    remap = ids[:w.num_blocks].astype(np.int32)
+    bt = W.block_tables(w)
+    slots = W.slot_mapping(w)
+    bt_big = remap[bt]
+    slots_big = remap[slots // 16] * 16 + slots % 16
+    big = make_cache(w, device, num_blocks=nb_big)
+    _say("pool past 4 GiB:", nb_big * per_block, "bytes")
+    encode_gpu(w, device, slots=slots_big, cache=big)
+    small, _, _, _ = encode_gpu(w, device)
+    torch.cuda.synchronize()
+    used = torch.from_numpy(remap.astype(np.int64)).to(device)
+    copied = big.pool.view(nb_big, per_block).index_select(0, used)
+    assert torch.equal(copied, small.pool.view(w.num_blocks, per_block)), "codes written past 4 GiB differ"
+    qb, q64 = W.queries(w)
+    q = to_device(qb, "bf16", device)
+    lens = torch.tensor([300, 300], dtype=torch.int32, device=device)
+    outs, logs = [], []
+    for cache, table in ((big, bt_big), (small, bt)):
+        out = torch.empty((2, 64, 128), device=device)
+        lg = torch.empty((2, 64, bt.shape[1] * 16), device=device)
+        ws = tq.new_workspace(cache, 2, 64, bt.shape[1], device=device)
+        tq.tq_decode_attend(q, cache, torch.from_numpy(np.ascontiguousarray(table)).to(device), lens, out, ws,
+                            logits_out=lg)
+        outs.append(out)
+        logs.append(lg)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(logs[0][:, :, :300], logs[1][:, :, :300])
+    up = O.unpack_pool(pool_bytes(small), oracle_layout(w))
+    ref = _oracle_decode(w, up, bt, [300, 300], q64, 8)
+    go, gl = outs[1].cpu().numpy().astype(np.float64), logs[1].cpu().numpy().astype(np.float64)
+    for (n, hq), (sv, scl, o) in ref.items():
+        assert np.all(np.abs(gl[n, hq, :300] - sv) <= LOGIT_RTOL * scl), (n, hq)
+        assert np.linalg.norm(go[n, hq] - o) <= OUT_RTOL * np.linalg.norm(o), (n, hq)
+    dec = []
+    for cache, sl in ((big, slots_big), (small, slots)):
+        Ko = torch.empty((slots.size, 8, 128), dtype=torch.bfloat16, device=device)
+        Vo = torch.empty_like(Ko)
+        tq.tq_decompress_kv(cache, torch.from_numpy(np.ascontiguousarray(sl, dtype=np.int32)).to(device), Ko, Vo)
+        dec.append((Ko, Vo))
+    torch.cuda.synchronize()
+    assert torch.equal(dec[0][0], dec[1][0]) and torch.equal(dec[0][1], dec[1][1])
+    del big, copied
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_decode_attend_gqa8(device, bits):
     _decode_case(device, bits, 8, 2, [1, 17, 300, 1029])
