@@ -341,3 +341,81 @@ def test_fullsize_octo_decode_workload(device):
     csn = scale * np.linalg.norm(qf, axis=-1) * np.linalg.norm(xh, axis=-1)[:, None]
     assert np.all(np.abs(got - want) <= LOGIT_RTOL * csn + 1e-30)
     _say("  sampled codes off the oracle's pick (near ties):", nmis)
+
+
+def test_longest_sequence_at_the_split_limit(device):
+    """The longest sequence decode-attend takes: 4096 splits of 1024 blocks,
+    4,194,304 blocks (67,108,859 tokens, a ragged last block) of one KV head
+    with 3-bit codes (a 6.7 GB pool), 8 query heads; the merge folds its 4096
+    partials per head in 32 rounds.  Every key but five points against the
+    queries (logits near -20), the five hot ones along them (near +20), so the
+    other 67 million tokens carry a total softmax weight below 1e-8 and the
+    output is the oracle's attention over the hot tokens.  Checked: the hot
+    tokens' logits and the output against the oracle, and every other logit
+    at least 30 below the hot ones."""
+    bits, nblk = 3, 4096 * 1024
+    T = nblk * 16 - 5
+    rng = np.random.default_rng(4096)
+    e = rng.standard_normal(128)
+    e /= np.linalg.norm(e)
+    q64 = 15.0 * (e[None, :] + 0.05 * rng.standard_normal((8, 128)))
+    q64 = (torch.from_numpy(q64.astype(np.float32)).double().numpy())[None]        # [1][8][128], f32 values
+    hot = np.array([0, 5_000_003, 16384 * 2048, 41_000_017, T - 1], dtype=np.int64)   # one at a split's first token
+    cold_k = torch.from_numpy((-15.0 * e).astype(np.float32)).to(device).to(torch.bfloat16)
+    hot_k = torch.from_numpy((15.0 * e).astype(np.float32)).to(device).to(torch.bfloat16)
+    vbank = torch.from_numpy(rng.standard_normal((1024, 128)).astype(np.float32)).to(device).to(torch.bfloat16)
+    rot = tq.tq_make_rotation(42, 128)
+    cfg = tq.make_config(1, nblk, bits, bits, rot)
+    cache = tq.tq_cache_create(cfg, torch.zeros(tq.tq_cache_bytes(cfg), dtype=torch.uint8, device=device))
+    cache._rots = (rot,)
+    _say("longest sequence:", T, "tokens,", tq.tq_cache_bytes(cfg), "pool bytes")
+    step = 1 << 23
+    for t0 in range(0, T, step):
+        cnt = min(step, T - t0)
+        idx = torch.arange(t0, t0 + cnt, device=device)
+        K = cold_k.expand(cnt, 1, 128).contiguous()
+        sel = hot[(hot >= t0) & (hot < t0 + cnt)] - t0
+        if sel.size:
+            K[torch.from_numpy(sel).to(device), 0] = hot_k
+        V = vbank.index_select(0, idx % 1024).view(cnt, 1, 128)
+        tq.tq_encode_kv(K, V, idx.to(torch.int32), bits, cache)
+        torch.cuda.synchronize()
+        del K, V, idx
+    bt = torch.arange(nblk, dtype=torch.int32, device=device).view(1, nblk)
+    lens = torch.tensor([T], dtype=torch.int32, device=device)
+    q = torch.from_numpy(q64.astype(np.float32)).to(device)
+    out = torch.full((1, 8, 128), float("nan"), device=device)
+    logits = torch.empty((1, 8, nblk * 16), device=device)
+    ws = tq.new_workspace(cache, 1, 8, nblk, device=device)
+    tq.tq_decode_attend(q, cache, bt, lens, out, ws, logits_out=logits)
+    torch.cuda.synchronize()
+    # the hot tokens' codes from their blocks, and the oracle over them
+    lay_full = O.LayoutV1(128, 1, bits, bits, False, nblk)
+    view = cache.pool.view(nblk, 1, lay_full.block_bytes)
+    arr = view.index_select(0, torch.from_numpy(hot // 16).to(device)).cpu().numpy()
+    up = O.unpack_pool(arr, O.LayoutV1(128, 1, bits, bits, False, hot.size))
+    r = hot % 16
+    c32, _ = O.codebook_fp32(128, bits)
+    khat = O.reconstruct(up["k_idx"][np.arange(hot.size), 0, r], up["k_g16"][np.arange(hot.size), 0, r], 42, c32)
+    vhat = O.reconstruct(up["v_idx"][np.arange(hot.size), 0, r], up["v_g16"][np.arange(hot.size), 0, r], 42, c32)
+    R = O.rotation_matrix(42, 128)
+    tau = 1 / math.sqrt(128)
+    hot_d = torch.from_numpy(hot).to(device)
+    mask = torch.ones(nblk * 16, dtype=torch.bool, device=device)
+    mask[hot_d] = False
+    mask[T:] = False
+    go = out.cpu().numpy().astype(np.float64)
+    for hq in range(8):
+        o, s = O.attention(q64[0, hq], khat, vhat)
+        kg = up["k_g16"][np.arange(hot.size), 0, r]
+        kidx = up["k_idx"][np.arange(hot.size), 0, r]
+        scl = cs_scale(tau, kg, np.linalg.norm(R @ q64[0, hq]), np.linalg.norm(c32[kidx], axis=1))
+        gl_hot = logits[0, hq].index_select(0, hot_d).cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(gl_hot - s) <= LOGIT_RTOL * scl), hq
+        cold_max = float(logits[0, hq][mask].max())
+        assert cold_max <= float(s.min()) - 30.0, (hq, cold_max, float(s.min()))
+        e_o = np.linalg.norm(go[0, hq] - o) / np.linalg.norm(o)
+        assert e_o <= OUT_RTOL, (hq, e_o)
+    _say("  hot logits", np.round(s, 2), "cold max", round(cold_max, 2))
+    del cache, logits, ws, mask
+    torch.cuda.empty_cache()
