@@ -343,31 +343,36 @@ def test_fullsize_octo_decode_workload(device):
     _say("  sampled codes off the oracle's pick (near ties):", nmis)
 
 
-def test_longest_sequence_at_the_split_limit(device):
-    """The longest sequence decode-attend takes: 4096 splits of 1024 blocks,
-    4,194,304 blocks (67,108,859 tokens, a ragged last block) of one KV head
-    with 3-bit codes (a 6.7 GB pool), 8 query heads; the merge folds its 4096
-    partials per head in 32 rounds.  Every key but five points against the
-    queries (logits near -20), the five hot ones along them (near +20), so the
-    other 67 million tokens carry a total softmax weight below 1e-8 and the
-    output is the oracle's attention over the hot tokens.  Checked: the hot
-    tokens' logits and the output against the oracle, and every other logit
-    at least 30 below the hot ones."""
-    bits, nblk = 3, 4096 * 1024
+@pytest.mark.parametrize("qjl", [False, True])
+def test_longest_sequence_at_the_split_limit(device, qjl):
+    """The longest sequence decode-attend takes: 4096 splits of the largest
+    split size, i.e. 4,194,304 blocks (67,108,859 tokens, a ragged last block;
+    a 6.7 GB pool) for the matrix-core kernel, and 262,144 blocks (4,194,299
+    tokens) for the vector kernel that QJL caches take; one KV head with
+    3-bit codes, 8 query heads; the merge folds 4096 partials per head in 32
+    rounds.  Every key but five points against the queries (logits near
+    -20), the five hot ones along them (near +20), so the other tokens carry
+    a total softmax weight below 1e-8 and the output is the oracle's
+    attention over the hot tokens.  Checked: the hot tokens' logits and the
+    output against the oracle, and every other logit at least 30 below the
+    hot ones."""
+    bits, nblk = 3, 4096 * (64 if qjl else 1024)
     T = nblk * 16 - 5
     rng = np.random.default_rng(4096)
     e = rng.standard_normal(128)
     e /= np.linalg.norm(e)
     q64 = 15.0 * (e[None, :] + 0.05 * rng.standard_normal((8, 128)))
     q64 = (torch.from_numpy(q64.astype(np.float32)).double().numpy())[None]        # [1][8][128], f32 values
-    hot = np.array([0, 5_000_003, 16384 * 2048, 41_000_017, T - 1], dtype=np.int64)   # one at a split's first token
+    split_tokens = 16 * nblk // 4096
+    hot = np.array([0, T // 13 + 3, split_tokens * 2048, T // 5 * 3 + 17, T - 1], dtype=np.int64)   # one at a split's first token
     cold_k = torch.from_numpy((-15.0 * e).astype(np.float32)).to(device).to(torch.bfloat16)
     hot_k = torch.from_numpy((15.0 * e).astype(np.float32)).to(device).to(torch.bfloat16)
     vbank = torch.from_numpy(rng.standard_normal((1024, 128)).astype(np.float32)).to(device).to(torch.bfloat16)
     rot = tq.tq_make_rotation(42, 128)
-    cfg = tq.make_config(1, nblk, bits, bits, rot)
+    rot2 = tq.tq_make_rotation(43, 128) if qjl else None
+    cfg = tq.make_config(1, nblk, bits, bits, rot, qjl, rot2)
     cache = tq.tq_cache_create(cfg, torch.zeros(tq.tq_cache_bytes(cfg), dtype=torch.uint8, device=device))
-    cache._rots = (rot,)
+    cache._rots = (rot, rot2)
     _say("longest sequence:", T, "tokens,", tq.tq_cache_bytes(cfg), "pool bytes")
     step = 1 << 23
     for t0 in range(0, T, step):
@@ -390,10 +395,10 @@ def test_longest_sequence_at_the_split_limit(device):
     tq.tq_decode_attend(q, cache, bt, lens, out, ws, logits_out=logits)
     torch.cuda.synchronize()
     # the hot tokens' codes from their blocks, and the oracle over them
-    lay_full = O.LayoutV1(128, 1, bits, bits, False, nblk)
+    lay_full = O.LayoutV1(128, 1, bits, bits, qjl, nblk)
     view = cache.pool.view(nblk, 1, lay_full.block_bytes)
     arr = view.index_select(0, torch.from_numpy(hot // 16).to(device)).cpu().numpy()
-    up = O.unpack_pool(arr, O.LayoutV1(128, 1, bits, bits, False, hot.size))
+    up = O.unpack_pool(arr, O.LayoutV1(128, 1, bits, bits, qjl, hot.size))
     r = hot % 16
     c32, _ = O.codebook_fp32(128, bits)
     khat = O.reconstruct(up["k_idx"][np.arange(hot.size), 0, r], up["k_g16"][np.arange(hot.size), 0, r], 42, c32)
@@ -405,11 +410,18 @@ def test_longest_sequence_at_the_split_limit(device):
     mask[hot_d] = False
     mask[T:] = False
     go = out.cpu().numpy().astype(np.float64)
+    kg = up["k_g16"][np.arange(hot.size), 0, r]
+    kidx = up["k_idx"][np.arange(hot.size), 0, r]
+    qj = None
+    if qjl:
+        qj = dict(bits=up["qjl_bits"][np.arange(hot.size), 0, r], rho16=up["rho16"][np.arange(hot.size), 0, r],
+                  gamma16=kg, seed=42, seed_qjl=43)
     for hq in range(8):
-        o, s = O.attention(q64[0, hq], khat, vhat)
-        kg = up["k_g16"][np.arange(hot.size), 0, r]
-        kidx = up["k_idx"][np.arange(hot.size), 0, r]
-        scl = cs_scale(tau, kg, np.linalg.norm(R @ q64[0, hq]), np.linalg.norm(c32[kidx], axis=1))
+        s = O.logits(q64[0, hq], khat, qjl=qj)
+        p = np.exp(s - s.max())
+        o = (p / p.sum()) @ vhat
+        scl = cs_scale(tau, kg, np.linalg.norm(R @ q64[0, hq]), np.linalg.norm(c32[kidx], axis=1),
+                       qj["rho16"] if qj else None)
         gl_hot = logits[0, hq].index_select(0, hot_d).cpu().numpy().astype(np.float64)
         assert np.all(np.abs(gl_hot - s) <= LOGIT_RTOL * scl), hq
         cold_max = float(logits[0, hq][mask].max())
