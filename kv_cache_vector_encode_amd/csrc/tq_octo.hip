@@ -69,17 +69,19 @@ __device__ __forceinline__ float atan01(float a) {
 }
 
 // atan2(y, x) for y, x >= 0 (0 when both are 0), through atan01 of the
-// smaller over the larger.
+// smaller over the larger (the larger floored at 1e-30, so 0 / 0 gives 0)
 __device__ __forceinline__ float atan2_pos(float y, float x) {
   const float mx = fmaxf(x, y), mn = fminf(x, y);
-  const float t = atan01(mx > 0.f ? mn * __builtin_amdgcn_rcpf(mx) : 0.f);
+  const float t = atan01(mn * __builtin_amdgcn_rcpf(fmaxf(mx, 1e-30f)));
   return y > x ? 1.57079632679489662f - t : t;
 }
 
 // Equal-area octahedral map of the direction of (nx, ny, .) with unit-vector
-// z component nz (nx and ny may carry any common positive scale): L1 radius
-// sqrt(1 - |nz|), the azimuth atan2(|ny|, |nx|) spread linearly along the
-// diamond edge, the lower hemisphere reflected across the edge.
+// z component nz (nx and ny may carry any common positive scale; |nz| may
+// exceed 1 by a rounding error): L1 radius sqrt(1 - |nz|), the azimuth
+// atan2(|ny|, |nx|) spread linearly along the diamond edge, the lower
+// hemisphere reflected across the edge, the signs of nx and ny copied (a
+// coordinate of -0 takes the negative side: the map's two sides agree there).
 __device__ __forceinline__ void oct_map(float nx, float ny, float nz, float& xi, float& eta) {
   const float r = __builtin_amdgcn_sqrtf(fmaxf(1.f - fabsf(nz), 0.f));
   const float phi = atan2_pos(fabsf(ny), fabsf(nx));
@@ -90,8 +92,8 @@ __device__ __forceinline__ void oct_map(float nx, float ny, float nz, float& xi,
     ax = 1.f - ae;
     ae = 1.f - t;
   }
-  xi = nx < 0.f ? -ax : ax;
-  eta = ny < 0.f ? -ae : ae;
+  xi = __builtin_copysignf(ax, nx);
+  eta = __builtin_copysignf(ae, ny);
 }
 
 template <int B, int DT>
@@ -158,11 +160,11 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
     __syncthreads();
     for (int i = L; i < kOctoTri; i += 16) {
       const float tx = s_y[row][3 * i], ty = s_y[row][3 * i + 1], tz = s_y[row][3 * i + 2];
-      const float rho = __builtin_amdgcn_sqrtf(tx * tx + ty * ty + tz * tz);
+      const float rr = tx * tx + ty * ty + tz * tz;
       // the map needs z / rho only; the azimuth is scale-free
-      const float nz = rho > 0.f ? tz * __builtin_amdgcn_rcpf(rho) : 1.f;
+      const float nz = rr > 0.f ? tz * __builtin_amdgcn_rsqf(rr) : 1.f;
       float xi, eta;
-      oct_map(tx, ty, fminf(fmaxf(nz, -1.f), 1.f), xi, eta);
+      oct_map(tx, ty, nz, xi, eta);
       const int a0 = octo_block_lo(xi, kNd), c0 = octo_block_lo(eta, kNd);
       // For a unit direction n_hat the error with the best norm code is
       // rho^2 + min_k (c_k^2 - 2 c_k p), p = t . n_hat; every c_k > 0, so
@@ -189,7 +191,8 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
       const int ca = a0 + (bo >> 1), cc = c0 + (bo & 1);
       // norm code: the number of ascending thresholds below p (seven
       // independent compares at b = 4; a binary search's dependent chain of
-      // compares and selects measured 10% slower)
+      // compares and selects measured 10% slower, a bucketed table search 0.5%
+      // faster)
       uint32_t k = 0;
 #pragma unroll
       for (int j = 0; j + 1 < C::kNr; ++j) k += best > a.trho[j] ? 1u : 0u;
