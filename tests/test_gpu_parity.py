@@ -316,9 +316,11 @@ def test_decode_attend_gqa8(device, bits):
     _decode_case(device, bits, 8, 2, [1, 17, 300, 1029])
 
 
-@pytest.mark.parametrize("bits", [3, 4])
-@pytest.mark.parametrize("group", [1, 2, 5, 16])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("group", [1, 2, 5, 9, 12, 16])
 def test_decode_attend_group_sizes(device, group, bits):
+    # 9 and 12 query heads per KV head run as two slices of 5 + 4 and 6 + 6
+    # heads: columns of heads past a slice stay empty
     _decode_case(device, bits, group, 3, [64, 700])
 
 
@@ -455,9 +457,9 @@ def test_decode_step_appends_and_attends(device, bits):
     _step_case(device, bits, 8, 2, [17, 700, 1024, 1, 0])
 
 
-@pytest.mark.parametrize("group", [1, 16])
+@pytest.mark.parametrize("group", [1, 12, 16])
 def test_decode_step_group_sizes(device, group):
-    # 16 query heads per KV head: two slices of 8 both append the token
+    # 12 or 16 query heads per KV head: two slices both append the token
     _step_case(device, 4, group, 2, [300, 2100], kv_dtype="f32")
 
 
