@@ -298,12 +298,17 @@ __device__ __forceinline__ void read_chunk(BlockRegs<BITS>& r, const uint8_t* st
     } else if constexpr (BITS == 2) {
       r.v[i] = *reinterpret_cast<const uint16_t*>(st + off);
     } else {
-      // 24 bits at byte off: two aligned dwords (the second may reach into
-      // the gamma_k region of the slot) and a byte funnel shift
-      const int al = off & ~3;
-      const uint32_t lo = *reinterpret_cast<const uint32_t*>(st + al);
-      const uint32_t hi = *reinterpret_cast<const uint32_t*>(st + al + 4);
-      r.v[i] = __builtin_amdgcn_alignbyte(hi, lo, (uint32_t)(off & 3)) & 0xFFFFFFu;
+      // 24 bits at byte off (4 pair fields), funnel-shifted so that pair
+      // field T lands at bit 7 + 6T: field 0 is then already where the table
+      // address wants it (v_field_addr).  The two aligned dwords start 1-4
+      // bytes below off, so the shift 8 (off - base) - 7 is never negative;
+      // the lower one may hold K codes, the upper one may reach into the
+      // gamma_k region of the slot (bits outside the fields are masked off).
+      const int dm = off & 3;
+      const int base = off - (dm ? dm : 4);
+      const uint32_t lo = *reinterpret_cast<const uint32_t*>(st + base);
+      const uint32_t hi = *reinterpret_cast<const uint32_t*>(st + base + 4);
+      r.v[i] = __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(8 * (off - base) - 7));
     }
   }
 }
@@ -378,6 +383,19 @@ __device__ __forceinline__ uint32_t pair_addr(const uint32_t (&w)[N], int i, uin
   if (sh + W <= 32) x = sh >= 7 ? (w[wi] >> (sh - 7)) : (w[wi] << (7 - sh));
   else x = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], (uint32_t)(sh - 7));
   return (x & mask) | r4;
+}
+// The same for the value codes of 2- and 3-bit caches as read_chunk leaves
+// them: 2-bit, field T at bit 4T (pair_addr); 3-bit, at bit 7 + 6T, so field
+// 0 needs no shift.
+template <int BITS>
+__device__ __forceinline__ uint32_t v_field_addr(uint32_t w, int T, uint32_t r4) {
+  if constexpr (BITS == 3) {
+    constexpr uint32_t mask = 0x3Fu << 7;
+    return ((T ? w >> (6 * T) : w) & mask) | r4;
+  } else {
+    const uint32_t w1[1] = {w};
+    return pair_addr<2 * BITS>(w1, T, r4);
+  }
 }
 __device__ __forceinline__ uint32_t lds_word(const uint32_t* table, uint32_t byte_addr) {
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(table) + byte_addr);
@@ -848,10 +866,7 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
 #pragma unroll
         for (int T = 0; T < 4; ++T)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t w1[1] = {cur[X].v[j]};
-            va[4 * X + T][j] = lds_word(tv, pair_addr<2 * BITS>(w1, T, r4));
-          }
+          for (int j = 0; j < 4; ++j) va[4 * X + T][j] = lds_word(tv, v_field_addr<BITS>(cur[X].v[j], T, r4));
     } else {
       // tile t = dims 8m+t; the A operand pairs tokens (4g, 4g+1),
       // (4g+2, 4g+3) of each block
