@@ -406,7 +406,7 @@ int check_device() {
 }
 
 // Blocks per split of a decode launch.  The matrix-core kernel keeps no
-// per-split score buffer, so its splits are sized for one round of three
+// per-split score buffer, so its splits are sized for one round of two
 // workgroups per CU (256 CUs); the vector kernel stages its split's scores in
 // LDS and caps a split at 64 blocks.  A decode-attend launch has at most
 // kMaxSplits splits per (sequence, KV head), which bounds the workspace.
