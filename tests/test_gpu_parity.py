@@ -252,6 +252,22 @@ def test_decode_attend_longest_split(device, monkeypatch, bits):
     _decode_case(device, bits, 8, 1, [16 * cap + 200, 300])
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bps", [32, 64])
+def test_decode_attend_short_splits(device, monkeypatch, bits, bps):
+    # splits of 32 or 64 blocks (two or four block pairs per wave, the sizes
+    # small decodes get): three full splits and a ragged fourth, a sequence
+    # one token short of a split, one of a single block, an empty one
+    monkeypatch.setenv("TQ_BLOCKS_PER_SPLIT", str(bps))
+    _decode_case(device, bits, 8, 2, [16 * bps * 3 + 200, 16 * bps - 1, 9, 0])
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_decode_step_short_splits(device, monkeypatch, bits):
+    monkeypatch.setenv("TQ_BLOCKS_PER_SPLIT", "64")
+    _step_case(device, bits, 8, 2, [16 * 64 * 2 + 17, 1024, 1, 0])
+
+
 def test_pool_beyond_4gib(device):
     """A 5.4 GB pool (3-bit keys and values, 8 KV heads, 420,000 blocks): the
     encoder's 64-bit offset path (the pool is past 4 GiB), and the decode's
