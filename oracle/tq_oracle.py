@@ -63,7 +63,7 @@ __all__ = [
     "oct_map", "oct_unmap", "octo_dir_codebook", "rho_cdf",
     "rho_partial_mean", "rho_lloyd_max", "octo_codebooks", "octo_encode",
     "octo_encode_triplets", "octo_triplet_error", "octo_decode",
-    "octo_record_bytes", "octo_pack", "octo_unpack",
+    "octo_record_bytes", "octo_pack", "octo_unpack", "octo_qjl_encode",
 ]
 
 _MASK64 = (1 << 64) - 1
@@ -743,6 +743,31 @@ def octo_decode(a, c, k, gamma16, seed: int, d: int, dirs, crho):
     yh = np.asarray(crho)[k][..., None] * dirs[a, c]
     yh = yh.reshape(yh.shape[:-2] + (-1,))[..., :d]
     return np.asarray(gamma16, dtype=np.float64)[..., None] * (yh @ rotation_matrix(seed, d))
+
+
+def octo_qjl_encode(x, seed: int, seed_qjl: int, b: int, dirs, crho):
+    """OCTOPUS-QJL ([P3] Method step 8, the optional residual sketch that
+    makes the dot-product estimate unbiased): the triplet codes of
+    octo_encode, plus the one-bit sketch of what they leave out, taken as in
+    qjl_encode.  y = R u is the rotated unit direction (the first d entries
+    of the triplets), y_hat its reconstruction from the codes (octo_decode
+    before the inverse rotation); r = y - y_hat, rho16 = fp16(||r||),
+    z = R' r with R' the independent rotation of seed_qjl, bit_j = [z_j < 0].
+    The logits then add scale * gamma16 * qjl_dot_estimate(bits, rho16, R q)
+    to scale * q . x_hat (logits(..., qjl=...)).
+    Returns octo_encode's dict plus qjl_bits (uint8 0/1, (..., d)), qjl_rho,
+    qjl_rho16, qjl_z."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    e = octo_encode(x, seed, b, dirs, crho)
+    y = e["t"].reshape(e["t"].shape[:-2] + (-1,))[..., :d]
+    yh = np.asarray(crho)[e["k"]][..., None] * dirs[e["a"], e["c"]]
+    yh = yh.reshape(yh.shape[:-2] + (-1,))[..., :d]
+    r = y - yh
+    rho = np.sqrt(np.sum(r * r, axis=-1))
+    z = r @ rotation_matrix(seed_qjl, d).T
+    e.update(qjl_bits=(z < 0).astype(np.uint8), qjl_rho=rho, qjl_rho16=fp16_norm(rho), qjl_z=z)
+    return e
 
 
 def octo_record_bytes(d: int, b: int) -> int:

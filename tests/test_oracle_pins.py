@@ -784,6 +784,79 @@ def test_triplet_codec_matches_the_pages_synthetic_results():
         assert mse < lm[b]                               # below the per-coordinate codec
 
 
+def test_triplet_codec_inner_product_error_matches_the_pages():
+    """The pages' "IP" figures, read as mean |<q, k> - <q, k_hat>| over
+    Gaussian q, k in d = 128 (golden file header): OCTOPUS at 2 / 3 / 4 bits
+    and OCTOPUS-QJL (the residual sketch of octo_qjl_encode, estimate as in
+    logits(..., qjl=...)) at 2 bits, each within 7%.  A sketch of the wrong
+    residual, of q instead of R q, or one that drops gamma or rho would not
+    bring the 2-bit error down by the page's quarter."""
+    rows = [r.split() for r in _golden_lines("octopus_synthetic_ip.txt")]
+    page = {(r[0], int(r[1])): float(r[2]) for r in rows}
+    rng = np.random.default_rng(21)
+    n = 4000
+    x = rng.standard_normal((n, D))
+    q = rng.standard_normal((n, D))
+    exact = np.sum(q * x, 1)
+    for b in (2, 3, 4):
+        dirs, crho = O.octo_codebooks(D, b)
+        e = O.octo_qjl_encode(x, 7, 99, b, dirs, crho)
+        xh = O.octo_decode(e["a"], e["c"], e["k"], e["gamma16"], 7, D, dirs, crho)
+        ip = np.mean(np.abs(exact - np.sum(q * xh, 1)))
+        assert abs(ip - page[("octopus", b)]) < 0.07 * page[("octopus", b)], (b, ip)
+        if b == 2:
+            tau = 1.0 / math.sqrt(D)
+            s = np.array([O.logits(q[i], xh[i:i + 1], qjl={"bits": e["qjl_bits"][i:i + 1], "rho16": e["qjl_rho16"][i:i + 1],
+                                                            "gamma16": e["gamma16"][i:i + 1], "seed": 7, "seed_qjl": 99})[0]
+                          for i in range(n)]) / tau
+            ipq = np.mean(np.abs(exact - s))
+            assert abs(ipq - page[("octopus_qjl", 2)]) < 0.07 * page[("octopus_qjl", 2)], ipq
+            assert ipq < 0.8 * ip
+
+
+def test_triplet_qjl_sketch_removes_the_inner_product_bias():
+    """With the query along the key (q = x), <q, k_hat> falls short of
+    <q, k> = |x|^2 by about |x|^2 * MSE (the reconstruction is shorter than
+    the key); the residual sketch's estimate is unbiased, so OCTOPUS-QJL
+    removes at least 90% of that bias at every width."""
+    rng = np.random.default_rng(22)
+    n = 3000
+    x = rng.standard_normal((n, D))
+    for b in (2, 3, 4):
+        dirs, crho = O.octo_codebooks(D, b)
+        e = O.octo_qjl_encode(x, 5, 77, b, dirs, crho)
+        xh = O.octo_decode(e["a"], e["c"], e["k"], e["gamma16"], 5, D, dirs, crho)
+        exact = np.sum(x * x, 1)
+        plain = np.sum(x * xh, 1)
+        R = O.rotation_matrix(5, D)
+        est = O.qjl_dot_estimate(e["qjl_bits"], e["qjl_rho16"], x @ R.T, 77)
+        corrected = plain + e["gamma16"].astype(np.float64) * est
+        bias, bias_q = np.mean((plain - exact) / exact), np.mean((corrected - exact) / exact)
+        assert bias < -0.004, (b, bias)     # about -MSE: -0.09, -0.026, -0.007
+        assert abs(bias_q) < 0.1 * abs(bias), (b, bias, bias_q)
+
+
+def test_triplet_qjl_residual_is_what_the_codes_leave_out():
+    """r = y - y_hat exactly: y_hat + r rebuilds the rotated unit direction,
+    |r|^2 is the triplet codec's squared error, and the sketch bits are the
+    signs of R' r (brute force on a few vectors)."""
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((6, D)) * rng.uniform(0.1, 10, (6, 1))
+    b = 3
+    dirs, crho = O.octo_codebooks(D, b)
+    e = O.octo_qjl_encode(x, 3, 4, b, dirs, crho)
+    R, Rq = O.rotation_matrix(3, D), O.rotation_matrix(4, D)
+    u = x / np.linalg.norm(x, axis=1, keepdims=True)
+    y = u @ R.T
+    for i in range(6):
+        yh = np.concatenate([crho[e["k"][i, j]] * dirs[e["a"][i, j], e["c"][i, j]] for j in range(O.octo_triplets(D))])[:D]
+        r = y[i] - yh
+        np.testing.assert_allclose(e["qjl_rho"][i], np.linalg.norm(r), rtol=1e-12)
+        np.testing.assert_array_equal(e["qjl_bits"][i], (Rq @ r < 0).astype(np.uint8))
+        xh = O.octo_decode(e["a"][i], e["c"][i], e["k"][i], 1.0, 3, D, dirs, crho)
+        np.testing.assert_allclose(np.sum((u[i] - xh) ** 2), e["qjl_rho"][i] ** 2, rtol=1e-9)
+
+
 def test_triplet_records_place_fields_lsb_first():
     b = 2                       # fields of 3 + 3 + 1 = 7 bits
     nt = O.octo_triplets(D)
