@@ -360,6 +360,35 @@ int tq_octo_logits(const float* q, const void* codes, const void* gamma,
                    int64_t table_bytes, float scale, float* out,
                    void* hip_stream);
 
+/* OCTOPUS-QJL ([P3] Method step 8, the optional residual sketch that makes
+ * the dot-product estimate unbiased).  tq_octo_encode_qjl writes what
+ * tq_octo_encode writes, plus a one-bit sketch of what the codes leave out:
+ * with y = R k / ||k|| (coordinates 0..127) and y_hat its reconstruction
+ * from the codes, r = y - y_hat, z = R' r through the independent rotation
+ * rot_qjl, and per vector
+ *   signs: 16 bytes, bit j (byte j / 8, bit j % 8) = [z_j < 0];
+ *   rho:   fp16 ||r|| (round to nearest even, saturating at 65504).
+ * signs: device [n][16], 16-byte aligned; rho: device [n] fp16, 2-byte
+ * aligned; both caller-owned.  tq_octo_logits_qjl adds the sketch's
+ * estimate of the residual's share to every logit:
+ *   out[h][g][j] = scale * gamma_hj * (sum_i rho_hat_hji (R q_hg)_i . n_hat_hji
+ *                  + sqrt(pi/2) / sqrt(128) * rho_hj * sum_j' sgn_j' (R' R q_hg)_j')
+ * with sgn = +1 for a clear bit, -1 for a set one; signs [heads][n][16] and
+ * rho [heads][n] as the encoder wrote them.  Arguments and errors otherwise
+ * as tq_octo_encode / tq_octo_logits; a missing or non-128 rot_qjl is
+ * TQ_ERR_UNSUPPORTED, a null or misaligned signs / rho TQ_ERR_INVALID_ARG. */
+int tq_octo_encode_qjl(const void* X, int32_t dtype, int64_t n, int32_t bits,
+                       const tq_rotation* rot, const tq_rotation* rot_qjl,
+                       const void* dev_tables, int64_t table_bytes,
+                       void* codes, void* gamma, void* signs, void* rho,
+                       void* hip_stream);
+int tq_octo_logits_qjl(const float* q, const void* codes, const void* gamma,
+                       const void* signs, const void* rho, int32_t heads,
+                       int32_t group, int64_t n, int32_t bits,
+                       const tq_rotation* rot, const tq_rotation* rot_qjl,
+                       const void* dev_tables, int64_t table_bytes,
+                       float scale, float* out, void* hip_stream);
+
 /* ---------------------------------------------------------------------------
  * Measurement aid (not part of the codec): read `bytes` of device memory at
  * `src` as a plain stream (grid-stride 16-byte non-temporal loads) and write

@@ -1036,18 +1036,37 @@ int octo_args(int32_t bits, const tq_rotation* rot, const void* dev_tables, int6
 }
 }  // namespace
 
-int tq_octo_encode(const void* X, int32_t dtype, int64_t n, int32_t bits, const tq_rotation* rot,
-                   const void* dev_tables, int64_t table_bytes, void* codes, void* gamma, void* hip_stream) {
+namespace {
+// The sketch buffers of OCTOPUS-QJL (all null for the plain codec): the
+// second rotation, 16-byte aligned sign records, 2-byte aligned norms.
+int octo_qjl_args(const tq_rotation* rot_qjl, const void* signs, const void* rho, bool want, tq::OctoArgs& a) {
+  if (!want) return TQ_OK;
+  if (!rot_qjl || rot_qjl->d != tq::kD) return fail(TQ_ERR_UNSUPPORTED, "the residual sketch needs a rotation of dimension 128");
+  if (!signs || !rho) return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  if (reinterpret_cast<uintptr_t>(signs) % 16 != 0 || reinterpret_cast<uintptr_t>(rho) % 2 != 0)
+    return fail(TQ_ERR_INVALID_ARG, "signs must be 16-byte aligned, rho 2-byte");
+  a.qjl_signs = const_cast<uint8_t*>(static_cast<const uint8_t*>(signs));
+  a.qjl_rho = const_cast<uint16_t*>(static_cast<const uint16_t*>(rho));
+  to_mask(rot_qjl->signs, a.rot_qjl);
+  return TQ_OK;
+}
+
+int octo_encode_impl(const void* X, int32_t dtype, int64_t n, int32_t bits, const tq_rotation* rot,
+                     const tq_rotation* rot_qjl, const void* dev_tables, int64_t table_bytes, void* codes, void* gamma,
+                     void* signs, void* rho, bool qjl, void* hip_stream) {
   if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n < 0");
   if (dtype != TQ_F32 && dtype != TQ_F16 && dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad dtype");
   tq::OctoArgs a;
   int s = octo_args(bits, rot, dev_tables, table_bytes, a);
   if (s != TQ_OK) return s;
+  if (qjl && (!rot_qjl || rot_qjl->d != tq::kD))
+    return fail(TQ_ERR_UNSUPPORTED, "the residual sketch needs a rotation of dimension 128");
   if (n == 0) return TQ_OK;
   if (!X || !codes || !gamma) return fail(TQ_ERR_INVALID_ARG, "null pointer");
   if (reinterpret_cast<uintptr_t>(X) % 16 != 0 || reinterpret_cast<uintptr_t>(codes) % 8 != 0 ||
       reinterpret_cast<uintptr_t>(gamma) % 2 != 0)
     return fail(TQ_ERR_INVALID_ARG, "X must be 16-byte aligned, codes 8-byte, gamma 2-byte");
+  if ((s = octo_qjl_args(rot_qjl, signs, rho, qjl, a)) != TQ_OK) return s;
   if (n >= ((int64_t)1 << 31)) return fail(TQ_ERR_INVALID_ARG, "too many vectors");
   if ((s = check_device()) != TQ_OK) return s;
   a.src = X;
@@ -1061,9 +1080,10 @@ int tq_octo_encode(const void* X, int32_t dtype, int64_t n, int32_t bits, const 
   return TQ_OK;
 }
 
-int tq_octo_logits(const float* q, const void* codes, const void* gamma, int32_t heads, int32_t group, int64_t n,
-                   int32_t bits, const tq_rotation* rot, const void* dev_tables, int64_t table_bytes, float scale,
-                   float* out, void* hip_stream) {
+int octo_logits_impl(const float* q, const void* codes, const void* gamma, const void* signs, const void* rho,
+                     int32_t heads, int32_t group, int64_t n, int32_t bits, const tq_rotation* rot,
+                     const tq_rotation* rot_qjl, const void* dev_tables, int64_t table_bytes, float scale, float* out,
+                     bool qjl, void* hip_stream) {
   if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n < 0");
   if (heads < 1 || heads > 65535) return fail(TQ_ERR_INVALID_ARG, "heads must be 1..65535");
   if (group < 1 || group > tq::kOctoMaxGroup) return fail(TQ_ERR_UNSUPPORTED, "group must be 1..16");
@@ -1071,11 +1091,14 @@ int tq_octo_logits(const float* q, const void* codes, const void* gamma, int32_t
   tq::OctoArgs a;
   int s = octo_args(bits, rot, dev_tables, table_bytes, a);
   if (s != TQ_OK) return s;
+  if (qjl && (!rot_qjl || rot_qjl->d != tq::kD))
+    return fail(TQ_ERR_UNSUPPORTED, "the residual sketch needs a rotation of dimension 128");
   if (n == 0) return TQ_OK;
   if (!q || !codes || !gamma || !out) return fail(TQ_ERR_INVALID_ARG, "null pointer");
   if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(codes) % 8 != 0 ||
       reinterpret_cast<uintptr_t>(gamma) % 2 != 0 || reinterpret_cast<uintptr_t>(out) % 4 != 0)
     return fail(TQ_ERR_INVALID_ARG, "q must be 16-byte aligned, codes 8-byte, gamma 2-byte, out 4-byte");
+  if ((s = octo_qjl_args(rot_qjl, signs, rho, qjl, a)) != TQ_OK) return s;
   if (n * heads >= ((int64_t)1 << 31)) return fail(TQ_ERR_INVALID_ARG, "too many keys");
   if ((s = check_device()) != TQ_OK) return s;
   a.q = q;
@@ -1089,6 +1112,35 @@ int tq_octo_logits(const float* q, const void* codes, const void* gamma, int32_t
   int err = tq::launch_octo_logits(a, bits, hip_stream);
   if (err != 0) return hip_fail(err, "triplet logits launch");
   return TQ_OK;
+}
+}  // namespace
+
+int tq_octo_encode(const void* X, int32_t dtype, int64_t n, int32_t bits, const tq_rotation* rot,
+                   const void* dev_tables, int64_t table_bytes, void* codes, void* gamma, void* hip_stream) {
+  return octo_encode_impl(X, dtype, n, bits, rot, nullptr, dev_tables, table_bytes, codes, gamma, nullptr, nullptr,
+                          false, hip_stream);
+}
+
+int tq_octo_encode_qjl(const void* X, int32_t dtype, int64_t n, int32_t bits, const tq_rotation* rot,
+                       const tq_rotation* rot_qjl, const void* dev_tables, int64_t table_bytes, void* codes,
+                       void* gamma, void* signs, void* rho, void* hip_stream) {
+  return octo_encode_impl(X, dtype, n, bits, rot, rot_qjl, dev_tables, table_bytes, codes, gamma, signs, rho, true,
+                          hip_stream);
+}
+
+int tq_octo_logits(const float* q, const void* codes, const void* gamma, int32_t heads, int32_t group, int64_t n,
+                   int32_t bits, const tq_rotation* rot, const void* dev_tables, int64_t table_bytes, float scale,
+                   float* out, void* hip_stream) {
+  return octo_logits_impl(q, codes, gamma, nullptr, nullptr, heads, group, n, bits, rot, nullptr, dev_tables,
+                          table_bytes, scale, out, false, hip_stream);
+}
+
+int tq_octo_logits_qjl(const float* q, const void* codes, const void* gamma, const void* signs, const void* rho,
+                       int32_t heads, int32_t group, int64_t n, int32_t bits, const tq_rotation* rot,
+                       const tq_rotation* rot_qjl, const void* dev_tables, int64_t table_bytes, float scale,
+                       float* out, void* hip_stream) {
+  return octo_logits_impl(q, codes, gamma, signs, rho, heads, group, n, bits, rot, rot_qjl, dev_tables, table_bytes,
+                          scale, out, true, hip_stream);
 }
 
 int tq_reconstruct(const tq_cache* cache, const int32_t* slots, int64_t n, int32_t which,

@@ -194,6 +194,12 @@ struct OctoArgs {
   SignMask rot;
   float crho[8];            // norm centroids (2^(b-1) used)
   float trho[8];            // thresholds, +inf past the last
+  // OCTOPUS-QJL (null: the plain codec): per vector 16 bytes of residual
+  // sketch signs and the residual norm (fp16); written by the encoder, read
+  // by the logits
+  uint8_t* qjl_signs;       // [heads][n][16]
+  uint16_t* qjl_rho;        // [heads][n] fp16
+  SignMask rot_qjl;
 };
 
 // The fixed decode scratch of tq_decode_attend_noalloc (tq_scratch.hip):

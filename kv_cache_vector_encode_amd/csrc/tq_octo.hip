@@ -96,7 +96,7 @@ __device__ __forceinline__ void oct_map(float nx, float ny, float nz, float& xi,
   eta = __builtin_copysignf(ae, ny);
 }
 
-template <int B, int DT>
+template <int B, int DT, bool QJL>
 __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
   using C = Octo<B>;
   // direction table [xi code][eta code], (x, y, z, 0) per entry
@@ -104,9 +104,11 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
   __shared__ float4 s_dir[kNd * kNd];
   __shared__ float s_y[16][kOctoRowPad];
   __shared__ uint32_t s_rec[16][C::kWords];
+  __shared__ float s_crho[8];
   const int tid = threadIdx.x, row = tid >> 4;
   const int L = tid & 15, ell = perm16(L);
   for (int i = tid; i < kNd * kNd; i += 256) s_dir[i] = reinterpret_cast<const float4*>(a.dirs)[i];
+  if (QJL && tid < 8) s_crho[tid] = a.crho[tid];
   const uint32_t sneg = sign_byte(a.rot, ell);
   uint32_t smask[8];
 #pragma unroll
@@ -197,11 +199,46 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
 #pragma unroll
       for (int j = 0; j + 1 < C::kNr; ++j) k += best > a.trho[j] ? 1u : 0u;
       const uint32_t field = (uint32_t)ca | ((uint32_t)cc << C::kBd) | (k << (2 * C::kBd));
+      if constexpr (QJL) {
+        // what the codes leave out of the triplet, in place of it (the lane
+        // owns these three coordinates)
+        const float4 d = s_dir[ca * kNd + cc];
+        const float rk = s_crho[k];
+        s_y[row][3 * i] = __builtin_fmaf(-rk, d.x, tx);
+        s_y[row][3 * i + 1] = __builtin_fmaf(-rk, d.y, ty);
+        s_y[row][3 * i + 2] = __builtin_fmaf(-rk, d.z, tz);
+      }
       const int bit = i * C::kField, w = bit >> 5, sh = bit & 31;
       atomicOr(&s_rec[row][w], field << sh);
       if (sh + C::kField > 32) atomicOr(&s_rec[row][w + 1], field >> (32 - sh));
     }
     __syncthreads();
+    if constexpr (QJL) {
+      // one-bit sketch of the residual r (coordinates 0..127 of the row):
+      // lane L takes coordinates 8L..8L+7, flips them by the second
+      // rotation's signs and runs the row FWHT, after which it holds output
+      // coordinates 8 perm16(L) + e of R' r (times fc.sig); bit e of byte
+      // perm16(L) of the sign record is [(R' r)_j < 0], rho = ||r||
+      float r[8];
+      float rr = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        r[e] = s_y[row][8 * L + e];
+        rr = __builtin_fmaf(r[e], r[e], rr);
+      }
+      const float rho = __builtin_amdgcn_sqrtf(row_sum(rr));
+      const uint32_t qneg = sign_byte(a.rot_qjl, L);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = flip(r[e], qneg, e);
+      fwht_row(r, fc);
+      uint32_t sbits = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sbits |= ((fc.sig * r[e]) < 0.f ? 1u : 0u) << e;
+      if (v < a.n) {
+        a.qjl_signs[v * 16 + perm16(L)] = (uint8_t)sbits;
+        if (L == 0) a.qjl_rho[v] = __half_as_ushort(__float2half_rn(fminf(rho, 65504.f)));
+      }
+    }
     if (v < a.n) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + v * C::kRec);
       for (int w = L; w < C::kWords; w += 16) dst[w] = s_rec[row][w];
@@ -224,9 +261,10 @@ constexpr int kOctoMfmaTile = 128;   // keys per tile step (2 tiles of 16 per wa
 
 // 5 waves per SIMD at b = 2, 3 (the kernel held to 96 VGPRs: 248 against
 // 263 us on the 4.2M keys of llama70b at b = 3); at b = 4 that limit spills
-// and measured slower, so it keeps 4
-template <int B>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B == 4 ? 4 : 5))) void octo_logits_mfma_kernel(
+// and measured slower, so it keeps 4; the QJL variant's 32 more query
+// registers leave room for 3
+template <int B, bool QJL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B == 4 ? 4 : 5))) void octo_logits_mfma_kernel(
     const OctoArgs a) {
   using C = Octo<B>;
   constexpr int kStride = C::kWords + 1;
@@ -235,18 +273,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B == 4 ? 4 
   // the rotated queries are read into registers once, before the first
   // tile's records are staged: the two share their LDS
   __shared__ union {
-    float q[16][kQd];
+    struct {
+      float q[16][kQd];
+      float w[QJL ? 16 : 1][kD];   // OCTOPUS-QJL: R' R q (scaled), natural order
+    } qw;
     uint32_t rec[kOctoMfmaTile * kStride];
   } s_u;
-  auto& s_q = s_u.q;
+  auto& s_q = s_u.qw.q;
+  auto& s_w = s_u.qw.w;
+  static_assert(sizeof(s_u.qw) == sizeof(float) * (16 * kQd + (QJL ? 16 : 1) * kD), "q and w are contiguous");
   uint32_t* const s_rec = s_u.rec;
   __shared__ float s_rho[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y;
   for (int i = tid; i < C::kNd * C::kNd; i += 256) s_dir[i] = reinterpret_cast<const float4*>(a.dirs)[i];
   if (tid < 8) s_rho[tid] = a.crho[tid];
+  // queries past the group (and, with the sketch, their R' R q) stay zero
   float* qf = &s_q[0][0];
-  for (int i = tid; i < 16 * kQd; i += 256) qf[i] = 0.f;
+  for (int i = tid; i < 16 * kQd + (QJL ? 16 * kD : 0); i += 256) qf[i] = 0.f;
   __syncthreads();
   {
     const int row = tid >> 4, L = tid & 15, ell = perm16(L);
@@ -264,6 +308,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B == 4 ? 4 
 #pragma unroll
       for (int e = 0; e < 8; ++e) s_q[row][8 * L + e] = x[e] * g;
     }
+    if constexpr (QJL) {
+      // the residual sketch is read against R' (R q): the second rotation
+      // of the lane's natural coordinates 8L..8L+7, after which the lane
+      // holds coordinates 8 perm16(L) + e (times fc.sig), as in the encoder
+      const uint32_t qneg = sign_byte(a.rot_qjl, L);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = flip(x[e] * g, qneg, e);
+      fwht_row(x, fc);
+      if (row < a.group) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_w[row][8 * perm16(L) + e] = x[e] * fc.sig * kInvSqrtD;
+      }
+    }
   }
   __syncthreads();
   // The contraction runs over the 44 triplets (the last all-zero in q) in
@@ -279,6 +336,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B == 4 ? 4 
       const int dim = 3 * (4 * m + kk) + c;
       qb[3 * m + c] = dim < kD ? s_q[col][dim] : 0.f;
     }
+  // OCTOPUS-QJL: 32 more steps of 4 sketch coordinates, lane kk taking
+  // coordinate 4 s + kk of step s
+  float qw[QJL ? 32 : 1];
+  if constexpr (QJL) {
+#pragma unroll
+    for (int st = 0; st < 32; ++st) qw[st] = s_w[col][4 * st + kk];
+  }
   // the workgroup walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... of
   // its head, so the table and the queries are set up once per workgroup;
   // the next tile's records are loaded into registers while this one is
@@ -326,6 +390,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B == 4 ? 4 
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.y, qb[3 * m + 1], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.z, qb[3 * m + 2], acc, 0, 0, 0);
     }
+    if constexpr (QJL) {
+      // A[key][j] = +-sqrt(pi/2)/sqrt(d) rho16 by the key's sign bit j
+      // (set: negative), so the products add the residual estimate
+      // sqrt(pi/2)/sqrt(d) rho16 sum_j sgn_j (R' R q)_j to the logit
+      const int key = t * 16 + col;
+      const int64_t kg = (int64_t)head * a.n + key0 + (key < nk ? key : 0);
+      const uint4 sg = *reinterpret_cast<const uint4*>(a.qjl_signs + kg * 16);
+      const float sk = key < nk ? 0.1107783657f * __half2float(__ushort_as_half(a.qjl_rho[kg])) : 0.f;
+      const uint32_t sgs[4] = {sg.x >> kk, sg.y >> kk, sg.z >> kk, sg.w >> kk};
+      const uint32_t skb = __float_as_uint(sk);
+#pragma unroll
+      for (int st = 0; st < 32; ++st) {
+        const uint32_t neg = ((sgs[st >> 3] >> (4 * (st & 7))) & 1u) << 31;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(skb ^ neg), qw[st], acc, 0, 0, 0);
+      }
+    }
     if (col < a.group) {
       float* o = a.out + ((int64_t)head * a.group + col) * a.n + key0 + t * 16 + 4 * kk;
       const uint16_t* gp = a.gamma + (int64_t)head * a.n + key0 + t * 16 + 4 * kk;
@@ -337,11 +417,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B == 4 ? 4 
   }
 }
 
+template <int B, bool QJL>
+static void octo_enc_q(const OctoArgs& a, dim3 grid, hipStream_t s) {
+  if (a.dtype == 0) hipLaunchKernelGGL((octo_encode_kernel<B, 0, QJL>), grid, dim3(256), 0, s, a);
+  else if (a.dtype == 1) hipLaunchKernelGGL((octo_encode_kernel<B, 1, QJL>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((octo_encode_kernel<B, 2, QJL>), grid, dim3(256), 0, s, a);
+}
 template <int B>
 static void octo_enc(const OctoArgs& a, dim3 grid, hipStream_t s) {
-  if (a.dtype == 0) hipLaunchKernelGGL((octo_encode_kernel<B, 0>), grid, dim3(256), 0, s, a);
-  else if (a.dtype == 1) hipLaunchKernelGGL((octo_encode_kernel<B, 1>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((octo_encode_kernel<B, 2>), grid, dim3(256), 0, s, a);
+  if (a.qjl_signs) octo_enc_q<B, true>(a, grid, s);
+  else octo_enc_q<B, false>(a, grid, s);
 }
 
 int launch_octo_encode(const OctoArgs& a, int bits, void* stream) {
@@ -367,7 +452,8 @@ int launch_octo_encode(const OctoArgs& a, int bits, void* stream) {
 
 template <int B>
 static void octo_log_mfma(const OctoArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((octo_logits_mfma_kernel<B>), grid, dim3(256), 0, s, a);
+  if (a.qjl_signs) hipLaunchKernelGGL((octo_logits_mfma_kernel<B, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((octo_logits_mfma_kernel<B, false>), grid, dim3(256), 0, s, a);
 }
 
 int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
@@ -378,7 +464,7 @@ int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
   // b = 4, 5 at b = 2, 3, one workgroup's wave on each SIMD), spread over
   // the heads, each looping over tiles of its head (the table and the
   // queries are set up once per workgroup)
-  const int64_t wgs = 256 * (bits == 4 ? 4 : 5);
+  const int64_t wgs = 256 * (a.qjl_signs ? 3 : bits == 4 ? 4 : 5);
   const int64_t tiles = std::min((a.n + kOctoMfmaTile - 1) / kOctoMfmaTile, std::max<int64_t>(1, wgs / a.heads));
   const dim3 grid((unsigned)tiles, (unsigned)a.heads);
   switch (bits) {

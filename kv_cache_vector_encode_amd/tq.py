@@ -93,6 +93,11 @@ def lib() -> ctypes.CDLL:
                                               ctypes.c_int64, _P, _P, _P]),
             "tq_octo_logits": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                               ctypes.c_int32, _P, _P, ctypes.c_int64, ctypes.c_float, _P, _P]),
+            "tq_octo_encode_qjl": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P,
+                                                  ctypes.c_int64, _P, _P, _P, _P, _P]),
+            "tq_octo_logits_qjl": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                                  ctypes.c_int32, _P, _P, _P, ctypes.c_int64, ctypes.c_float, _P,
+                                                  _P]),
             "tq_minmax_decode": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, ctypes.c_int32, _P, _P]),
             "tq_decode_step": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P, _P, _P, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P,
@@ -470,6 +475,44 @@ def tq_octo_logits(q, codes, gamma, bits: int, rot, dev_tables, out, scale=None,
     _check(lib().tq_octo_logits(_ptr(q), _ptr(codes), _ptr(gamma), heads, group, codes.shape[1], bits, rot.handle,
                                 _ptr(dev_tables), dev_tables.numel() * dev_tables.element_size(), scale, _ptr(out),
                                 _stream(stream)), "tq_octo_logits")
+
+
+def tq_octo_encode_qjl(X, bits: int, rot, rot_qjl, dev_tables, codes, gamma, signs, rho, stream=None):
+    """tq_octo_encode plus the residual sketch: signs uint8 [n][16] (16-byte
+    aligned), rho [n] 16-bit."""
+    _need(X, "X", _FLOATS, (None, 128))
+    n = X.shape[0]
+    _need_bytes(dev_tables, "dev_tables", tq_octo_table_bytes(bits))
+    _need(codes, "codes", ("uint8",), (n, tq_octo_record_bytes(128, bits)))
+    _need(gamma, "gamma", ("int16", "float16"), (n,))
+    _need(signs, "signs", ("uint8",), (n, 16))
+    _need(rho, "rho", ("int16", "float16"), (n,))
+    _on_gpu(None, X=X, dev_tables=dev_tables, codes=codes, gamma=gamma, signs=signs, rho=rho)
+    _check(lib().tq_octo_encode_qjl(_ptr(X), _dtype_code(X), n, bits, rot.handle, rot_qjl.handle, _ptr(dev_tables),
+                                    dev_tables.numel() * dev_tables.element_size(), _ptr(codes), _ptr(gamma),
+                                    _ptr(signs), _ptr(rho), _stream(stream)), "tq_octo_encode_qjl")
+
+
+def tq_octo_logits_qjl(q, codes, gamma, signs, rho, bits: int, rot, rot_qjl, dev_tables, out, scale=None,
+                       stream=None):
+    """tq_octo_logits plus the residual sketch's estimate: signs uint8
+    [heads][n][16], rho [heads][n] 16-bit, as tq_octo_encode_qjl wrote them."""
+    _need(q, "q", ("float32",), (None, None, 128))
+    heads, group, _ = q.shape
+    _need(codes, "codes", ("uint8",), (heads, None, tq_octo_record_bytes(128, bits)))
+    n = codes.shape[1]
+    _need(gamma, "gamma", ("int16", "float16"), (heads, n))
+    _need(signs, "signs", ("uint8",), (heads, n, 16))
+    _need(rho, "rho", ("int16", "float16"), (heads, n))
+    _need(out, "out", ("float32",), (heads, group, n))
+    _need_bytes(dev_tables, "dev_tables", tq_octo_table_bytes(bits))
+    _on_gpu(None, q=q, codes=codes, gamma=gamma, signs=signs, rho=rho, out=out, dev_tables=dev_tables)
+    if scale is None:
+        scale = 1.0 / math.sqrt(128)
+    _check(lib().tq_octo_logits_qjl(_ptr(q), _ptr(codes), _ptr(gamma), _ptr(signs), _ptr(rho), heads, group, n, bits,
+                                    rot.handle, rot_qjl.handle, _ptr(dev_tables),
+                                    dev_tables.numel() * dev_tables.element_size(), scale, _ptr(out),
+                                    _stream(stream)), "tq_octo_logits_qjl")
 
 
 def tq_decompress_kv(cache: Cache, slots, K_out, V_out=None, stream=None):

@@ -129,6 +129,18 @@ def test_minmax_and_octo_reject_bad_tensors():
         tq.tq_octo_encode(X, 4, r, tabs, torch.zeros((5, 40), dtype=torch.uint8), torch.zeros(5, dtype=torch.int16))
     with pytest.raises(ValueError, match="dev_tables: 8 bytes, needs"):
         tq.tq_octo_tables(4, tabs[:8].clone())
+    r2 = tq.tq_make_rotation(43, 128)
+    codes, gam = torch.zeros((5, 72), dtype=torch.uint8), torch.zeros(5, dtype=torch.int16)
+    with pytest.raises(ValueError, match=r"signs: shape \[5, 8\]"):
+        tq.tq_octo_encode_qjl(X, 4, r, r2, tabs, codes, gam, torch.zeros((5, 8), dtype=torch.uint8), gam.clone())
+    with pytest.raises(TypeError, match="rho: dtype torch.float32"):
+        tq.tq_octo_encode_qjl(X, 4, r, r2, tabs, codes, gam, torch.zeros((5, 16), dtype=torch.uint8), torch.zeros(5))
+    with pytest.raises(ValueError, match=r"signs: shape \[2, 9, 8\]"):
+        tq.tq_octo_logits_qjl(torch.zeros((2, 8, 128)), torch.zeros((2, 9, rec), dtype=torch.uint8),
+                              torch.zeros((2, 9), dtype=torch.int16), torch.zeros((2, 9, 8), dtype=torch.uint8),
+                              torch.zeros((2, 9), dtype=torch.int16), 4, r, r2, tabs, torch.zeros((2, 8, 9)))
+    with pytest.raises(ValueError, match="must be on a GPU device"):
+        tq.tq_octo_encode_qjl(X, 4, r, r2, tabs, codes, gam, torch.zeros((5, 16), dtype=torch.uint8), gam.clone())
     with pytest.raises(ValueError, match="workspace: 16 bytes, needs"):
         c = _cache()
         q, bt, sl, out, _ = _decode_args()

@@ -6,6 +6,7 @@ Full-size configurations are in test_gpu_fullsize.py.
 """
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -905,3 +906,143 @@ def test_octo_encode_scale_edge_cases(device):
         a1, c1, k1 = O.octo_unpack(part, bits, 128)
         same = (a0 == a1) & (c0 == c1) & (k0 == k1)
         assert same.mean() > 0.99
+
+
+# ------------------------------------------------------ triplet codec + QJL --
+
+def _octo_qjl_encode_gpu(X, bits, rot, rot2, tb, device):
+    n = X.shape[0]
+    rb = tq.tq_octo_record_bytes(128, bits)
+    codes = torch.full((n, rb), 0xA5, dtype=torch.uint8, device=device)
+    gamma = torch.zeros(n, dtype=torch.int16, device=device)
+    signs = torch.full((n, 16), 0x5A, dtype=torch.uint8, device=device)
+    rho = torch.zeros(n, dtype=torch.int16, device=device)
+    tq.tq_octo_encode_qjl(X, bits, rot, rot2, tb, codes, gamma, signs, rho)
+    return codes, gamma, signs, rho
+
+
+def _oracle_residual(x64, codes, bits, seed, seed_qjl):
+    """The rotated-frame residual of the GPU's own codes, in float64, and its
+    sketch coordinates z = R' r."""
+    n = x64.shape[0]
+    dirs, crho = O.octo_codebooks(128, bits)
+    a, c, k = O.octo_unpack(codes, bits, 128)
+    gam = np.linalg.norm(x64, axis=1)
+    u = np.where((gam > 0)[:, None], x64 / np.where(gam > 0, gam, 1.0)[:, None], 0.0)
+    y = u @ O.rotation_matrix(seed, 128).T
+    yh = (crho[k][..., None] * dirs[a, c]).reshape(n, -1)[:, :128]
+    r = y - yh
+    return r, np.linalg.norm(r, axis=1), r @ O.rotation_matrix(seed_qjl, 128).T
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_octo_qjl_encode_matches_oracle(device, bits):
+    """OCTOPUS-QJL encode of 1001 keys (62 full groups of 16 and a ragged one,
+    a zero key among them): the codes and norms equal tq_octo_encode's; the
+    residual norm and the sketch signs match the oracle's residual of those
+    codes.  A sign may differ only where |z_j| is within 1e-5 |r| of zero
+    (fp32 against float64); the norm within fp16 rounding."""
+    w = W.DECODE_32K.with_(seq_len=126, num_kv_heads=8)
+    kb, k64 = W.keys(w)
+    n = 1001
+    kb = np.ascontiguousarray(kb.reshape(-1, 128)[:n])
+    x64 = k64.reshape(-1, 128)[:n].copy()
+    kb[5] = 0
+    x64[5] = 0.0
+    X = to_device(kb, "bf16", device)
+    rot, rot2 = tq.tq_make_rotation(42, 128), tq.tq_make_rotation(4242, 128)
+    tb = _octo_tables_dev(bits, device)
+    rb = tq.tq_octo_record_bytes(128, bits)
+    codes = torch.zeros((n, rb), dtype=torch.uint8, device=device)
+    gamma = torch.zeros(n, dtype=torch.int16, device=device)
+    _say("octo qjl encode", bits)
+    tq.tq_octo_encode(X, bits, rot, tb, codes, gamma)
+    cq, gq, signs, rho = _octo_qjl_encode_gpu(X, bits, rot, rot2, tb, device)
+    torch.cuda.synchronize()
+    assert torch.equal(codes, cq) and torch.equal(gamma, gq)
+    _, rn, z = _oracle_residual(x64, cq.cpu().numpy(), bits, 42, 4242)
+    r16 = rho.cpu().numpy().view(np.float16).astype(np.float64)
+    assert np.all(np.abs(r16 - rn) <= 2.0 ** -11 * rn + 1e-6), float(np.max(np.abs(r16 - rn) / rn))
+    got = np.unpackbits(signs.cpu().numpy(), axis=1, bitorder="little").astype(bool)
+    off = got != (z < 0)
+    band = np.abs(z) <= 1e-5 * rn[:, None]
+    assert not np.any(off & ~band), int(np.sum(off & ~band))
+    _say("  sketch signs in the band:", int(np.sum(off)))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("group", [1, 8, 16])
+def test_octo_qjl_logits_match_oracle(device, bits, group):
+    """Logits with the residual estimate against the oracle's logits(...,
+    qjl=...) over x_hat and the sketch the GPU stored: 3 heads x 700 keys (two
+    full 256-key tiles and a ragged one), held to 1e-4 of |q| times the
+    bound |x_hat| + sqrt(pi/2) rho gamma of the two terms."""
+    heads, n = 3, 700
+    w = W.DECODE_32K.with_(seq_len=700, num_kv_heads=heads, num_q_heads=heads * group)
+    kb, _ = W.keys(w)
+    kb = np.ascontiguousarray(np.swapaxes(kb, 0, 1)).reshape(heads * n, 128)
+    rot, rot2 = tq.tq_make_rotation(42, 128), tq.tq_make_rotation(4242, 128)
+    tb = _octo_tables_dev(bits, device)
+    codes, gamma, signs, rho = _octo_qjl_encode_gpu(to_device(kb, "bf16", device), bits, rot, rot2, tb, device)
+    rb = tq.tq_octo_record_bytes(128, bits)
+    _, q64 = W.queries(w)
+    q = torch.from_numpy(q64[0].astype(np.float32).reshape(heads, group, 128)).to(device)
+    out = torch.full((heads, group, n), float("nan"), device=device)
+    scale = 1.0 / math.sqrt(128)
+    _say("octo qjl logits", bits, group)
+    tq.tq_octo_logits_qjl(q, codes.view(heads, n, rb), gamma.view(heads, n), signs.view(heads, n, 16),
+                          rho.view(heads, n), bits, rot, rot2, tb, out, scale=scale)
+    torch.cuda.synchronize()
+    dirs, crho = O.octo_codebooks(128, bits)
+    a, c, k = O.octo_unpack(codes.cpu().numpy().reshape(heads, n, rb), bits, 128)
+    g16 = gamma.cpu().numpy().view(np.float16).reshape(heads, n)
+    r16 = rho.cpu().numpy().view(np.float16).reshape(heads, n)
+    sb = np.unpackbits(signs.cpu().numpy(), axis=1, bitorder="little").reshape(heads, n, 128)
+    xh = O.octo_decode(a, c, k, g16, 42, 128, dirs, crho)
+    qf = q.cpu().numpy().astype(np.float64)
+    got = out.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for h in range(heads):
+        bound = np.linalg.norm(xh[h], axis=1) + math.sqrt(math.pi / 2) * r16[h].astype(np.float64) * g16[h].astype(np.float64)
+        for g in range(group):
+            want = O.logits(qf[h, g], xh[h], scale=scale,
+                            qjl={"bits": sb[h], "rho16": r16[h], "gamma16": g16[h], "seed": 42, "seed_qjl": 4242})
+            tol = LOGIT_RTOL * scale * np.linalg.norm(qf[h, g]) * bound
+            err = np.abs(got[h, g] - want)
+            assert np.all(err <= tol), (h, g, float(np.max(err / tol)))
+            worst = max(worst, float(np.max(err / tol)))
+    _say(f"  worst error / bar {worst:.3f}")
+
+
+def test_octo_qjl_inner_product_error_matches_the_pages(device):
+    """Through the GPU path (encode and logits with scale 1 give the estimate
+    of q . k), on Gaussian keys and queries in d = 128: the mean |q . k -
+    estimate| of the plain triplet logits and of the OCTOPUS-QJL logits at 2
+    bits come within 7% of the pages' inner-product errors (2.682 and 2.015),
+    and the sketch brings the error down by more than a fifth."""
+    rows = [r.split() for r in open(os.path.join(os.path.dirname(__file__), "golden", "octopus_synthetic_ip.txt"))
+            if r.strip() and not r.startswith("#")]
+    page = {(r[0], int(r[1])): float(r[2]) for r in rows}
+    bits, n, group = 2, 8192, 16
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((n, 128)).astype(np.float32)
+    qn = rng.standard_normal((1, group, 128)).astype(np.float32)
+    rot, rot2 = tq.tq_make_rotation(8, 128), tq.tq_make_rotation(9, 128)
+    tb = _octo_tables_dev(bits, device)
+    codes, gamma, signs, rho = _octo_qjl_encode_gpu(torch.from_numpy(x).to(device), bits, rot, rot2, tb, device)
+    rb = tq.tq_octo_record_bytes(128, bits)
+    q = torch.from_numpy(qn).to(device)
+    plain = torch.empty((1, group, n), device=device)
+    withq = torch.empty((1, group, n), device=device)
+    tq.tq_octo_logits(q, codes.view(1, n, rb), gamma.view(1, n), bits, rot, tb, plain, scale=1.0)
+    tq.tq_octo_logits_qjl(q, codes.view(1, n, rb), gamma.view(1, n), signs.view(1, n, 16), rho.view(1, n), bits,
+                          rot, rot2, tb, withq, scale=1.0)
+    torch.cuda.synchronize()
+    exact = qn[0].astype(np.float64) @ x.astype(np.float64).T
+    ip = float(np.mean(np.abs(exact - plain[0].cpu().numpy())))
+    ipq = float(np.mean(np.abs(exact - withq[0].cpu().numpy())))
+    _say(f"GPU inner-product error at 2 bits: {ip:.3f} (page {page[('octopus', 2)]}), "
+         f"with the sketch {ipq:.3f} (page {page[('octopus_qjl', 2)]})")
+    assert abs(ip - page[("octopus", 2)]) < 0.07 * page[("octopus", 2)]
+    assert abs(ipq - page[("octopus_qjl", 2)]) < 0.07 * page[("octopus_qjl", 2)]
+    assert ipq < 0.8 * ip

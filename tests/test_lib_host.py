@@ -321,6 +321,28 @@ def test_octo_sizes_and_argument_checks_happen_before_the_device():
     assert L.tq_octo_logits(q, cd, g, 8, 8, 100, 4, r.handle, tb, 1024, 0.1, out, None) == tq.TQ_ERR_INVALID_ARG
 
 
+def test_octo_qjl_argument_checks_happen_before_the_device():
+    L = tq.lib()
+    r = tq.tq_make_rotation(42, 128)
+    r2 = tq.tq_make_rotation(43, 128)
+    r64 = tq.tq_make_rotation(42, 64)
+    X, cd, g, tb, q, out, sg, rh = 0x200000, 0x300000, 0x400000, 0x500000, 0x600000, 0x700000, 0x800000, 0x900000
+    enc = L.tq_octo_encode_qjl
+    assert enc(X, tq.TQ_BF16, 10, 4, r.handle, None, tb, 16384, cd, g, sg, rh, None) == tq.TQ_ERR_UNSUPPORTED
+    assert enc(X, tq.TQ_BF16, 10, 4, r.handle, r64.handle, tb, 16384, cd, g, sg, rh, None) == tq.TQ_ERR_UNSUPPORTED
+    assert enc(X, tq.TQ_BF16, 10, 4, r.handle, r2.handle, tb, 16384, cd, g, None, rh, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(X, tq.TQ_BF16, 10, 4, r.handle, r2.handle, tb, 16384, cd, g, sg, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(X, tq.TQ_BF16, 10, 4, r.handle, r2.handle, tb, 16384, cd, g, sg + 8, rh, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(X, tq.TQ_BF16, 10, 4, r.handle, r2.handle, tb, 16384, cd, g, sg, rh + 1, None) == tq.TQ_ERR_INVALID_ARG
+    assert enc(X, tq.TQ_BF16, 0, 4, r.handle, r2.handle, tb, 16384, cd, g, sg, rh, None) == tq.TQ_OK
+    lg = L.tq_octo_logits_qjl
+    assert lg(q, cd, g, sg, rh, 8, 8, 100, 4, r.handle, None, tb, 16384, 0.1, out, None) == tq.TQ_ERR_UNSUPPORTED
+    assert lg(q, cd, g, None, rh, 8, 8, 100, 4, r.handle, r2.handle, tb, 16384, 0.1, out, None) == tq.TQ_ERR_INVALID_ARG
+    assert lg(q, cd, g, sg + 4, rh, 8, 8, 100, 4, r.handle, r2.handle, tb, 16384, 0.1, out, None) == tq.TQ_ERR_INVALID_ARG
+    assert lg(q, cd, g, sg, rh, 8, 17, 100, 4, r.handle, r2.handle, tb, 16384, 0.1, out, None) == tq.TQ_ERR_UNSUPPORTED
+    assert lg(q, cd, g, sg, rh, 8, 8, 0, 4, r.handle, r2.handle, tb, 16384, 0.1, out, None) == tq.TQ_OK
+
+
 def test_noalloc_decode_checks_happen_before_the_device():
     # the allocation-free decode takes tq_decode_attend's arguments minus the
     # workspace; a call whose split partials would not fit the fixed 16 MiB
