@@ -362,7 +362,7 @@ def main():
     # that each head's records are contiguous), then the logits of sequence
     # 0's query group against every key of its KV head straight from the
     # records.  Outside the timed step, reported beside it.
-    oc_enc_ms, oc_log_ms = [], []
+    oc_enc_ms, oc_log_ms, oq_enc_ms, oq_log_ms = [], [], [], []
     if args.only == "both" and not args.no_extras:
         orot = tq.tq_make_rotation(w.rot_seed, 128)
         otb = torch.empty(tq.tq_octo_table_bytes(w.bits_k), dtype=torch.uint8, device=dev)
@@ -374,6 +374,11 @@ def main():
         ogam = [torch.empty((H, T), dtype=torch.int16, device=dev) for _ in sets]
         oq = q[0].float().view(H, G, 128).contiguous()
         olog = torch.empty((H, G, T), dtype=torch.float32, device=dev)
+        # OCTOPUS-QJL: the same codes plus the residual sketch (16 sign bytes
+        # and an fp16 norm per key)
+        orot2 = tq.tq_make_rotation(w.rot_seed + 1, 128)
+        osig = [torch.empty((H, T, 16), dtype=torch.uint8, device=dev) for _ in sets]
+        orho = [torch.empty((H, T), dtype=torch.int16, device=dev) for _ in sets]
         reps = max(5, args.steps // 4)
 
         def oc_enc(i):
@@ -385,7 +390,17 @@ def main():
             j = i % nsets
             tq.tq_octo_logits(oq, ocodes[j], ogam[j], w.bits_k, orot, otb, olog, stream=stream)
 
-        for fn, acc in ((oc_enc, oc_enc_ms), (oc_log, oc_log_ms)):
+        def oq_enc(i):
+            j = i % nsets
+            tq.tq_octo_encode_qjl(okh[j].view(-1, 128), w.bits_k, orot, orot2, otb, ocodes[j].view(-1, orb),
+                                  ogam[j].view(-1), osig[j].view(-1, 16), orho[j].view(-1), stream)
+
+        def oq_log(i):
+            j = i % nsets
+            tq.tq_octo_logits_qjl(oq, ocodes[j], ogam[j], osig[j], orho[j], w.bits_k, orot, orot2, otb, olog,
+                                  stream=stream)
+
+        for fn, acc in ((oc_enc, oc_enc_ms), (oc_log, oc_log_ms), (oq_enc, oq_enc_ms), (oq_log, oq_log_ms)):
             for i in range(max(3, nsets)):
                 fn(i)
             ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
@@ -395,7 +410,7 @@ def main():
                 ev[i][1].record(stream)
             torch.cuda.synchronize()
             acc.extend(e[0].elapsed_time(e[1]) for e in ev)
-        del okh, ocodes, ogam, olog
+        del okh, ocodes, ogam, olog, osig, orho
 
     # ---- on-box ceilings: a plain stream read (the library's measurement
     # aid) and a device copy, each over 2 GiB
@@ -486,6 +501,21 @@ def main():
             "frac": round(lb / ol_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": lb,
             "us_per_launch": round(ol_s * 1e6, 2), "keys_per_s": round(nk / ol_s, 1),
             "note": f"sequence 0's {G} queries per KV head against every key of that head, fp32 logits out"}
+    if oq_enc_ms:
+        qb = nk * (in_b + orb + 2 + 16 + 2)                      # plus 16 sign bytes and an fp16 norm out
+        qe_s = float(np.mean(oq_enc_ms)) / 1e3
+        kernels["tq_octo_encode_qjl"] = {
+            "bound": "hbm", "achieved": round(qb / qe_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(qb / qe_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": qb,
+            "us_per_launch": round(qe_s * 1e6, 2), "vectors_per_s": round(nk / qe_s, 1),
+            "note": "OCTOPUS-QJL: the triplet codes of every key plus the one-bit sketch of their residual"}
+        qlb = nk * (orb + 2 + 16 + 2) + nk * G * 4 + w.num_q_heads * 128 * 4
+        ql_s = float(np.mean(oq_log_ms)) / 1e3
+        kernels["tq_octo_logits_qjl"] = {
+            "bound": "hbm", "achieved": round(qlb / ql_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(qlb / ql_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": qlb,
+            "us_per_launch": round(ql_s * 1e6, 2), "keys_per_s": round(nk / ql_s, 1),
+            "note": f"OCTOPUS-QJL logits: {G} queries per KV head against every key, with the residual estimate"}
     dom = "tq_encode" if enc_s >= dec_s else "tq_decode_attend"
     traffic = None
     tf = os.path.join(ROOT, "profiles", "traffic.json")

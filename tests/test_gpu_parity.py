@@ -1023,24 +1023,25 @@ def test_octo_qjl_inner_product_error_matches_the_pages(device):
     rows = [r.split() for r in open(os.path.join(os.path.dirname(__file__), "golden", "octopus_synthetic_ip.txt"))
             if r.strip() and not r.startswith("#")]
     page = {(r[0], int(r[1])): float(r[2]) for r in rows}
-    bits, n, group = 2, 8192, 16
+    bits, heads, n, group = 2, 8, 1024, 16      # 128 queries, 8192 keys
     rng = np.random.default_rng(61)
-    x = rng.standard_normal((n, 128)).astype(np.float32)
-    qn = rng.standard_normal((1, group, 128)).astype(np.float32)
+    x = rng.standard_normal((heads, n, 128)).astype(np.float32)
+    qn = rng.standard_normal((heads, group, 128)).astype(np.float32)
     rot, rot2 = tq.tq_make_rotation(8, 128), tq.tq_make_rotation(9, 128)
     tb = _octo_tables_dev(bits, device)
-    codes, gamma, signs, rho = _octo_qjl_encode_gpu(torch.from_numpy(x).to(device), bits, rot, rot2, tb, device)
+    codes, gamma, signs, rho = _octo_qjl_encode_gpu(torch.from_numpy(x.reshape(-1, 128)).to(device), bits, rot, rot2,
+                                                    tb, device)
     rb = tq.tq_octo_record_bytes(128, bits)
     q = torch.from_numpy(qn).to(device)
-    plain = torch.empty((1, group, n), device=device)
-    withq = torch.empty((1, group, n), device=device)
-    tq.tq_octo_logits(q, codes.view(1, n, rb), gamma.view(1, n), bits, rot, tb, plain, scale=1.0)
-    tq.tq_octo_logits_qjl(q, codes.view(1, n, rb), gamma.view(1, n), signs.view(1, n, 16), rho.view(1, n), bits,
-                          rot, rot2, tb, withq, scale=1.0)
+    plain = torch.empty((heads, group, n), device=device)
+    withq = torch.empty((heads, group, n), device=device)
+    tq.tq_octo_logits(q, codes.view(heads, n, rb), gamma.view(heads, n), bits, rot, tb, plain, scale=1.0)
+    tq.tq_octo_logits_qjl(q, codes.view(heads, n, rb), gamma.view(heads, n), signs.view(heads, n, 16),
+                          rho.view(heads, n), bits, rot, rot2, tb, withq, scale=1.0)
     torch.cuda.synchronize()
-    exact = qn[0].astype(np.float64) @ x.astype(np.float64).T
-    ip = float(np.mean(np.abs(exact - plain[0].cpu().numpy())))
-    ipq = float(np.mean(np.abs(exact - withq[0].cpu().numpy())))
+    exact = np.einsum("hgd,hnd->hgn", qn.astype(np.float64), x.astype(np.float64))
+    ip = float(np.mean(np.abs(exact - plain.cpu().numpy())))
+    ipq = float(np.mean(np.abs(exact - withq.cpu().numpy())))
     _say(f"GPU inner-product error at 2 bits: {ip:.3f} (page {page[('octopus', 2)]}), "
          f"with the sketch {ipq:.3f} (page {page[('octopus_qjl', 2)]})")
     assert abs(ip - page[("octopus", 2)]) < 0.07 * page[("octopus", 2)]
