@@ -389,6 +389,28 @@ int tq_octo_logits_qjl(const float* q, const void* codes, const void* gamma,
                        const void* dev_tables, int64_t table_bytes,
                        float scale, float* out, void* hip_stream);
 
+/* Decode-attend over triplet-coded keys and values ([P3] Method step 7:
+ * scores and values straight from each triplet's norm and direction codes,
+ * no reconstructed key or value written; [P2] attention
+ * softmax(q K_hat^T scale) V_hat), on the flat per-head buffers of
+ * tq_octo_encode (keys and values coded with the same rotation and bits):
+ *   out[h][g] = sum_j softmax_j(scale * q_hg . k_hat_hj) v_hat_hj
+ * q: device fp32 [heads][group][128], 16-byte aligned; k_codes / v_codes:
+ * [heads][n][record bytes], 8-byte aligned; k_gamma / v_gamma: [heads][n]
+ * fp16; out: fp32 [heads][group][128], 16-byte aligned (n = 0 gives zeros);
+ * workspace: device, 16-byte aligned, at least
+ * tq_octo_attend_workspace_bytes(heads, group, n) bytes, for the split
+ * partials.  All caller-owned; asynchronous on hip_stream (a split kernel and
+ * a merge).  group in 1..16, heads in 1..65535, heads * n < 2^31.  Errors as
+ * tq_octo_logits, plus TQ_ERR_WORKSPACE for a short workspace. */
+int64_t tq_octo_attend_workspace_bytes(int32_t heads, int32_t group, int64_t n);
+int tq_octo_attend(const float* q, const void* k_codes, const void* k_gamma,
+                   const void* v_codes, const void* v_gamma, int32_t heads,
+                   int32_t group, int64_t n, int32_t bits,
+                   const tq_rotation* rot, const void* dev_tables,
+                   int64_t table_bytes, float scale, float* out,
+                   void* workspace, int64_t workspace_bytes, void* hip_stream);
+
 /* ---------------------------------------------------------------------------
  * Measurement aid (not part of the codec): read `bytes` of device memory at
  * `src` as a plain stream (grid-stride 16-byte non-temporal loads) and write

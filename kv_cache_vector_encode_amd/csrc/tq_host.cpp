@@ -1143,6 +1143,79 @@ int tq_octo_logits_qjl(const float* q, const void* codes, const void* gamma, con
                           scale, out, true, hip_stream);
 }
 
+namespace {
+// Splits of a triplet decode-attend: about three workgroups per CU in all
+// (the kernel's registers allow three waves per SIMD), each split a
+// multiple of the 128 keys a workgroup stages at a time; at most 1024.
+void octo_attend_split(int32_t heads, int64_t n, int64_t& split_len, int32_t& nsplit) {
+  const int64_t ch = tq::kOctoAttChunk;
+  const int64_t want = std::max<int64_t>(1, (n * heads + 767) / 768);
+  split_len = std::max<int64_t>(ch, (want + ch - 1) / ch * ch);
+  if ((n + split_len - 1) / split_len > 1024) split_len = ((n + 1023) / 1024 + ch - 1) / ch * ch;
+  nsplit = (int32_t)std::max<int64_t>(1, (n + split_len - 1) / split_len);
+}
+}  // namespace
+
+int64_t tq_octo_attend_workspace_bytes(int32_t heads, int32_t group, int64_t n) {
+  if (heads < 1 || heads > 65535 || group < 1 || group > tq::kOctoMaxGroup || n < 0)
+    return fail(TQ_ERR_INVALID_ARG, "heads 1..65535, group 1..16, n >= 0");
+  int64_t split_len;
+  int32_t nsplit;
+  octo_attend_split(heads, n, split_len, nsplit);
+  return (int64_t)heads * 4 * nsplit * group * tq::kPartStride * (int64_t)sizeof(float);
+}
+
+int tq_octo_attend(const float* q, const void* k_codes, const void* k_gamma, const void* v_codes,
+                   const void* v_gamma, int32_t heads, int32_t group, int64_t n, int32_t bits,
+                   const tq_rotation* rot, const void* dev_tables, int64_t table_bytes, float scale, float* out,
+                   void* workspace, int64_t workspace_bytes, void* hip_stream) {
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n < 0");
+  if (heads < 1 || heads > 65535) return fail(TQ_ERR_INVALID_ARG, "heads must be 1..65535");
+  if (group < 1 || group > tq::kOctoMaxGroup) return fail(TQ_ERR_UNSUPPORTED, "group must be 1..16");
+  if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, "scale must be finite");
+  tq::OctoArgs a;
+  int s = octo_args(bits, rot, dev_tables, table_bytes, a);
+  if (s != TQ_OK) return s;
+  if (!q || !out || !workspace || (n > 0 && (!k_codes || !k_gamma || !v_codes || !v_gamma)))
+    return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(k_codes) % 8 != 0 ||
+      reinterpret_cast<uintptr_t>(v_codes) % 8 != 0 || reinterpret_cast<uintptr_t>(k_gamma) % 2 != 0 ||
+      reinterpret_cast<uintptr_t>(v_gamma) % 2 != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(TQ_ERR_INVALID_ARG, "q, out and workspace must be 16-byte aligned, codes 8-byte, norms 2-byte");
+  if (n * heads >= ((int64_t)1 << 31)) return fail(TQ_ERR_INVALID_ARG, "too many keys");
+  const int64_t need = tq_octo_attend_workspace_bytes(heads, group, n);
+  if (workspace_bytes < need) return fail(TQ_ERR_WORKSPACE, "workspace smaller than tq_octo_attend_workspace_bytes");
+  if ((s = check_device()) != TQ_OK) return s;
+  a.q = q;
+  a.codes = const_cast<uint8_t*>(static_cast<const uint8_t*>(k_codes));
+  a.gamma = const_cast<uint16_t*>(static_cast<const uint16_t*>(k_gamma));
+  a.vcodes = static_cast<const uint8_t*>(v_codes);
+  a.vgamma = static_cast<const uint16_t*>(v_gamma);
+  a.partials = static_cast<float*>(workspace);
+  a.n = n;
+  a.heads = heads;
+  a.group = group;
+  a.scale = scale;
+  octo_attend_split(heads, n, a.split_len, a.num_splits);
+  int err = tq::launch_octo_attend(a, bits, hip_stream);
+  if (err != 0) return hip_fail(err, "triplet attend launch");
+  // the main decode's merge: num_kv_heads = heads, 4 partials per split
+  tq::DecodeArgs m;
+  std::memset(&m, 0, sizeof(m));
+  m.out = out;
+  m.partials = a.partials;
+  m.num_seqs = 1;
+  m.num_kv_heads = heads;
+  m.num_q_heads = heads * group;
+  m.group = group;
+  m.num_splits = 4 * a.num_splits;
+  m.rot = a.rot;
+  err = tq::launch_merge(m, hip_stream);
+  if (err != 0) return hip_fail(err, "merge launch");
+  return TQ_OK;
+}
+
 int tq_reconstruct(const tq_cache* cache, const int32_t* slots, int64_t n, int32_t which,
                    float* out, void* hip_stream) {
   if (!cache) return fail(TQ_ERR_INVALID_ARG, "null cache");

@@ -200,7 +200,14 @@ struct OctoArgs {
   uint8_t* qjl_signs;       // [heads][n][16]
   uint16_t* qjl_rho;        // [heads][n] fp16
   SignMask rot_qjl;
+  // decode-attend over triplet-coded keys (codes, gamma) and values
+  const uint8_t* vcodes;    // [heads][n][rec_bytes]
+  const uint16_t* vgamma;   // [heads][n] fp16
+  float* partials;          // [heads][4 * splits][group][kPartStride]
+  int64_t split_len;        // keys per split, a multiple of kOctoAttChunk
+  int32_t num_splits;
 };
+constexpr int kOctoAttChunk = 128;   // keys a decode-attend workgroup stages at a time
 
 // The fixed decode scratch of tq_decode_attend_noalloc (tq_scratch.hip):
 // 16 MiB per GPU.  scratch_buffer returns this device's copy (resolved on
@@ -222,5 +229,6 @@ int launch_minmax_decode(const MinmaxArgs& a, int bits, void* stream);
 int launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 int launch_octo_encode(const OctoArgs& a, int bits, void* stream);
 int launch_octo_logits(const OctoArgs& a, int bits, void* stream);
+int launch_octo_attend(const OctoArgs& a, int bits, void* stream);   // then launch_merge
 
 }  // namespace tq

@@ -476,4 +476,201 @@ int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
   return (int)hipGetLastError();
 }
 
+
+// Decode-attend over triplet-coded keys and values of one head per
+// workgroup row ([P3] Method step 7: every score and every value from its
+// triplets' norms and directions, no K_hat or V_hat written; [P2] attention
+// softmax(q K^T scale) V): a split of split_len keys per workgroup, staged
+// 128 keys at a time (records and norms of keys and values), each wave
+// taking 16-key sub-tiles in turn and keeping its own online softmax, in
+// log2 units (scale * log2(e) folded into the queries), and accumulators.
+//  - Scores: the logits kernel's product, C[16 keys x 16 queries] over 33
+//    steps of 4 rotated dims, times gamma_k.
+//  - Values: C[16 dims x 16 queries] += A[16 dims x 4 keys] * B[4 keys x 16
+//    queries] over 4 key steps, B = p * gamma_v through LDS.  The 144 rows of
+//    the 9 dim tiles are (triplet, component) pairs: row m of tile 3u + c is
+//    component c of triplet 16u + m, so a lane decodes three triplets of a
+//    key per step (field, direction, norm) and feeds nine products.  Rows
+//    past dim 127 (triplet 42's pad, triplets 43..47) hold zero.
+//  - Each wave writes its own partial (o_rot, m in natural-log units, l);
+//    merge_kernel combines the 4 * splits partials of a head, normalises and
+//    rotates back.
+template <int B>
+__global__ __launch_bounds__(256) void octo_attend_kernel(const OctoArgs a) {
+  using C = Octo<B>;
+  constexpr int kStride = C::kWords + 1;
+  constexpr int kQd = 132;
+  constexpr int kCh = kOctoAttChunk;
+  __shared__ float4 s_dir[C::kNd * C::kNd];
+  __shared__ union {
+    float q[16][kQd];
+    struct {
+      uint32_t rec[2][kCh * kStride];   // key, value records of the chunk
+      float g[2][kCh];                  // their norms (0 past the chunk's end)
+    } ch;
+  } s_u;
+  __shared__ float s_rho[8];
+  __shared__ float s_p[4][16][17];      // per wave: p * gamma_v, [key][query]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int head = blockIdx.y, split = blockIdx.x;
+  const int64_t kb0 = (int64_t)split * a.split_len;
+  const int64_t kb1 = a.n < kb0 + a.split_len ? a.n : kb0 + a.split_len;
+  const float LOG2E = 1.4426950408889634f;
+  for (int i = tid; i < C::kNd * C::kNd; i += 256) s_dir[i] = reinterpret_cast<const float4*>(a.dirs)[i];
+  if (tid < 8) s_rho[tid] = a.crho[tid];
+  float* qf = &s_u.q[0][0];
+  for (int i = tid; i < 16 * kQd; i += 256) qf[i] = 0.f;   // queries past the group stay zero
+  __syncthreads();
+  {
+    const int row = tid >> 4, L = tid & 15, ell = perm16(L);
+    const int rq = row < a.group ? row : 0;
+    const uint32_t sneg = sign_byte(a.rot, ell);
+    uint32_t smask[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) smask[i] = ((sneg >> i) & 1u) << 31;
+    float x[8];
+    load8_signed<0>(a.q, ((int64_t)head * a.group + rq) * kD + 8 * ell, smask, x);
+    const FwhtLane fc = fwht_lane(L);
+    fwht_row(x, fc);
+    const float g = fc.sig * kInvSqrtD * a.scale * LOG2E;
+    if (row < a.group) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_u.q[row][8 * L + e] = x[e] * g;
+    }
+  }
+  __syncthreads();
+  const int col = lane & 15, kk = lane >> 4;
+  float qb[33];
+#pragma unroll
+  for (int m = 0; m < 11; ++m)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      const int dim = 3 * (4 * m + kk) + c;
+      qb[3 * m + c] = dim < kD ? s_u.q[col][dim] : 0.f;
+    }
+  float run_m = -INFINITY, run_l = 0.f;
+  f32x4 acc[9];
+#pragma unroll
+  for (int T = 0; T < 9; ++T) acc[T] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  auto field_of = [&](const uint32_t* rec, int j) -> uint32_t {
+    const int bit = j * C::kField, wi = bit >> 5, sh = bit & 31;
+    return (uint32_t)((((uint64_t)rec[wi + 1] << 32) | rec[wi]) >> sh) & ((1u << C::kField) - 1u);
+  };
+  const uint8_t* kcod = a.codes + (int64_t)head * a.n * C::kRec;
+  const uint8_t* vcod = a.vcodes + (int64_t)head * a.n * C::kRec;
+  const uint16_t* kg = a.gamma + (int64_t)head * a.n;
+  const uint16_t* vg = a.vgamma + (int64_t)head * a.n;
+  for (int64_t c0 = kb0; c0 < kb1; c0 += kCh) {   // the same trip count in every wave
+    const int nk = (int)(kb1 - c0 < kCh ? kb1 - c0 : kCh);
+    __syncthreads();   // the previous chunk (or the queries) is no longer read
+    for (int i = tid; i < kCh * C::kWords; i += 256) {
+      const int k = i / C::kWords, w = i - k * C::kWords;
+      const bool in = k < nk;
+      s_u.ch.rec[0][k * kStride + w] = in ? reinterpret_cast<const uint32_t*>(kcod + (c0 + k) * C::kRec)[w] : 0u;
+      s_u.ch.rec[1][k * kStride + w] = in ? reinterpret_cast<const uint32_t*>(vcod + (c0 + k) * C::kRec)[w] : 0u;
+    }
+    if (tid < kCh) {
+      const bool in = tid < nk;
+      s_u.ch.g[0][tid] = in ? __half2float(__ushort_as_half(kg[c0 + tid])) : 0.f;
+      s_u.ch.g[1][tid] = in ? __half2float(__ushort_as_half(vg[c0 + tid])) : 0.f;
+    }
+    __syncthreads();
+    for (int t = wave; t * 16 < nk; t += 4) {
+      // ---- scores of keys 16t .. 16t+15 (rows 4kk + r) for query col
+      const uint32_t* rk = s_u.ch.rec[0] + (t * 16 + col) * kStride;
+      f32x4 sl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 11; ++m) {
+        const uint32_t f = field_of(rk, 4 * m + kk);   // triplet 43 reads zero bits; its q is 0
+        const float4 d = s_dir[(int)(f & (C::kNd - 1)) * C::kNd + (int)((f >> C::kBd) & (C::kNd - 1))];
+        const float r = s_rho[f >> (2 * C::kBd)];
+        sl = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.x, qb[3 * m], sl, 0, 0, 0);
+        sl = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.y, qb[3 * m + 1], sl, 0, 0, 0);
+        sl = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.z, qb[3 * m + 2], sl, 0, 0, 0);
+      }
+      float sc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = t * 16 + 4 * kk + r;
+        sc[r] = key < nk ? sl[r] * s_u.ch.g[0][key] : -INFINITY;
+      }
+      // ---- online softmax for query col over the 16 keys
+      const float bm = max_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+      const float new_m = fmaxf(run_m, bm);
+      if (__builtin_amdgcn_ballot_w64(new_m > run_m) != 0) {
+        const float alpha = run_m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(run_m - new_m);
+        run_l *= alpha;
+#pragma unroll
+        for (int T = 0; T < 9; ++T) acc[T] *= alpha;
+      }
+      run_m = new_m;
+      const float mref = new_m == -INFINITY ? 0.f : new_m;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(sc[r] - mref);   // exp2(-inf) = 0
+        run_l += p;
+        s_p[wave][4 * kk + r][col] = p * s_u.ch.g[1][t * 16 + 4 * kk + r];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // ---- values: step s takes keys 16t + 4s .. +3 (key 4s + kk in this lane)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const float b = s_p[wave][4 * st + kk][col];
+        const uint32_t* rv = s_u.ch.rec[1] + (t * 16 + 4 * st + kk) * kStride;
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+          const int j = 16 * u + col;                 // triplet of rows col of tiles 3u .. 3u+2
+          const uint32_t f = field_of(rv, j < kOctoTri ? j : kOctoTri - 1);
+          const float4 d = s_dir[(int)(f & (C::kNd - 1)) * C::kNd + (int)((f >> C::kBd) & (C::kNd - 1))];
+          const float r = j < kOctoTri ? s_rho[f >> (2 * C::kBd)] : 0.f;
+          acc[3 * u] = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.x, b, acc[3 * u], 0, 0, 0);
+          acc[3 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.y, b, acc[3 * u + 1], 0, 0, 0);
+          // component z of triplet 42 is the pad coordinate (dim 128)
+          acc[3 * u + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(j < kOctoTri - 1 ? r * d.z : 0.f, b, acc[3 * u + 2],
+                                                               0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();   // s_p is rewritten by the next sub-tile
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+  // ---- this wave's partial: rows 4kk + r of tile 3u + c are component c of
+  // triplet 16u + 4kk + r, i.e. dim 3 (16u + 4kk + r) + c
+  run_l = sum_rows(run_l);
+  if (col < a.group) {
+    float* pp = a.partials + (((int64_t)head * (4 * a.num_splits) + 4 * split + wave) * a.group + col) * kPartStride;
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+      for (int c = 0; c < 3; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int dim = 3 * (16 * u + 4 * kk + r) + c;
+          if (dim < kD) pp[dim] = acc[3 * u + c][r];
+        }
+    if (kk == 0) {
+      pp[128] = run_m * (1.f / LOG2E);   // natural-log units for the merge
+      pp[129] = run_l;
+    }
+  }
+}
+
+int launch_octo_attend(const OctoArgs& a, int bits, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.n < 0 || a.heads < 1 || a.heads > 65535 || a.group < 1 || a.group > kOctoMaxGroup || a.num_splits < 1 ||
+      a.split_len < kOctoAttChunk || a.split_len % kOctoAttChunk != 0 || (int64_t)a.num_splits * a.split_len < a.n)
+    return (int)hipErrorInvalidValue;
+  const dim3 grid((unsigned)a.num_splits, (unsigned)a.heads);
+  switch (bits) {
+    case 2: hipLaunchKernelGGL((octo_attend_kernel<2>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((octo_attend_kernel<3>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((octo_attend_kernel<4>), grid, dim3(256), 0, s, a); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
 }  // namespace tq

@@ -93,6 +93,10 @@ def lib() -> ctypes.CDLL:
                                               ctypes.c_int64, _P, _P, _P]),
             "tq_octo_logits": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                               ctypes.c_int32, _P, _P, ctypes.c_int64, ctypes.c_float, _P, _P]),
+            "tq_octo_attend_workspace_bytes": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]),
+            "tq_octo_attend": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                              ctypes.c_int32, _P, _P, ctypes.c_int64, ctypes.c_float, _P, _P,
+                                              ctypes.c_int64, _P]),
             "tq_octo_encode_qjl": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P,
                                                   ctypes.c_int64, _P, _P, _P, _P, _P]),
             "tq_octo_logits_qjl": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
@@ -513,6 +517,38 @@ def tq_octo_logits_qjl(q, codes, gamma, signs, rho, bits: int, rot, rot_qjl, dev
                                     rot.handle, rot_qjl.handle, _ptr(dev_tables),
                                     dev_tables.numel() * dev_tables.element_size(), scale, _ptr(out),
                                     _stream(stream)), "tq_octo_logits_qjl")
+
+
+def tq_octo_attend_workspace_bytes(heads: int, group: int, n: int) -> int:
+    v = lib().tq_octo_attend_workspace_bytes(heads, group, n)
+    _check(int(v) if v < 0 else 0, "tq_octo_attend_workspace_bytes")
+    return int(v)
+
+
+def tq_octo_attend(q, k_codes, k_gamma, v_codes, v_gamma, bits: int, rot, dev_tables, out, workspace, scale=None,
+                   stream=None):
+    """q: fp32 [heads][group][128]; k_codes / v_codes: uint8 [heads][n][record
+    bytes]; k_gamma / v_gamma: [heads][n] 16-bit; out: fp32 [heads][group][128];
+    workspace: device uint8 of tq_octo_attend_workspace_bytes(heads, group, n)."""
+    _need(q, "q", ("float32",), (None, None, 128))
+    heads, group, _ = q.shape
+    rb = tq_octo_record_bytes(128, bits)
+    _need(k_codes, "k_codes", ("uint8",), (heads, None, rb))
+    n = k_codes.shape[1]
+    _need(v_codes, "v_codes", ("uint8",), (heads, n, rb))
+    _need(k_gamma, "k_gamma", ("int16", "float16"), (heads, n))
+    _need(v_gamma, "v_gamma", ("int16", "float16"), (heads, n))
+    _need(out, "out", ("float32",), (heads, group, 128))
+    _need_bytes(dev_tables, "dev_tables", tq_octo_table_bytes(bits))
+    _need_bytes(workspace, "workspace", tq_octo_attend_workspace_bytes(heads, group, n))
+    _on_gpu(None, q=q, k_codes=k_codes, k_gamma=k_gamma, v_codes=v_codes, v_gamma=v_gamma, out=out,
+            dev_tables=dev_tables, workspace=workspace)
+    if scale is None:
+        scale = 1.0 / math.sqrt(128)
+    _check(lib().tq_octo_attend(_ptr(q), _ptr(k_codes), _ptr(k_gamma), _ptr(v_codes), _ptr(v_gamma), heads, group, n,
+                                bits, rot.handle, _ptr(dev_tables), dev_tables.numel() * dev_tables.element_size(),
+                                scale, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream)), "tq_octo_attend")
 
 
 def tq_decompress_kv(cache: Cache, slots, K_out, V_out=None, stream=None):

@@ -40,6 +40,8 @@ int launch_minmax_decode(const MinmaxArgs&, int, void*) { unreachable("minmax de
 int launch_stream_read(const void*, int64_t, uint32_t*, void*) { unreachable("stream read"); }
 int launch_octo_encode(const OctoArgs&, int, void*) { unreachable("triplet encode"); }
 int launch_octo_logits(const OctoArgs&, int, void*) { unreachable("triplet logits"); }
+int launch_octo_attend(const OctoArgs&, int, void*) { unreachable("triplet attend"); }
+int launch_merge(const DecodeArgs&, void*) { unreachable("merge"); }
 int decode_slices(int group) { return (group + 7) / 8; }
 int scratch_buffer(void**, int64_t*) { unreachable("scratch address"); }
 }  // namespace tq
@@ -150,7 +152,16 @@ int main() {
     CHECK(tq_octo_tables(b, w, nullptr) == TQ_ERR_NO_DEVICE);
     CHECK(tq_octo_encode(p, TQ_BF16, 7, b, r, p, 16384, w, w, nullptr) == TQ_ERR_NO_DEVICE);
     CHECK(tq_octo_logits(fp, p, p, 8, 8, 100, b, r, p, 16384, 0.1f, fp, nullptr) == TQ_ERR_NO_DEVICE);
+    CHECK(tq_octo_encode_qjl(p, TQ_BF16, 7, b, r, r, p, 16384, w, w, w, w, nullptr) == TQ_ERR_NO_DEVICE);
+    CHECK(tq_octo_logits_qjl(fp, p, p, p, p, 8, 8, 100, b, r, r, p, 16384, 0.1f, fp, nullptr) == TQ_ERR_NO_DEVICE);
+    CHECK(tq_octo_attend(fp, p, p, p, p, 8, 8, 100, b, r, p, 16384, 0.1f, fp, w, int64_t(1) << 30, nullptr) ==
+          TQ_ERR_NO_DEVICE);
   }
+  CHECK(tq_octo_attend_workspace_bytes(8, 8, 100) > 0 && tq_octo_attend_workspace_bytes(0, 8, 100) == TQ_ERR_INVALID_ARG);
+  CHECK(tq_octo_attend(fp, p, p, p, p, 8, 8, 100, 4, r, p, 16384, 0.1f, fp, w, 16, nullptr) == TQ_ERR_WORKSPACE);
+  CHECK(tq_octo_attend(fp, p, p, p, p, 8, 17, 100, 4, r, p, 16384, 0.1f, fp, w, 16, nullptr) == TQ_ERR_UNSUPPORTED);
+  CHECK(tq_octo_logits_qjl(fp, p, p, p, p, 8, 8, 100, 4, r, nullptr, p, 16384, 0.1f, fp, nullptr) == TQ_ERR_UNSUPPORTED);
+  CHECK(tq_octo_encode_qjl(p, TQ_BF16, 7, 4, r, r, p, 16384, w, w, nullptr, w, nullptr) == TQ_ERR_INVALID_ARG);
   CHECK(tq_octo_encode(p, TQ_BF16, 7, 4, r, nullptr, 16384, w, w, nullptr) == TQ_ERR_INVALID_ARG);
   CHECK(tq_octo_encode(p, TQ_BF16, -1, 4, r, p, 16384, w, w, nullptr) == TQ_ERR_INVALID_ARG);
   CHECK(tq_octo_logits(fp, p, p, 8, 17, 100, 4, r, p, 16384, 0.1f, fp, nullptr) == TQ_ERR_UNSUPPORTED);

@@ -1047,3 +1047,73 @@ def test_octo_qjl_inner_product_error_matches_the_pages(device):
     assert abs(ip - page[("octopus", 2)]) < 0.07 * page[("octopus", 2)]
     assert abs(ipq - page[("octopus_qjl", 2)]) < 0.07 * page[("octopus_qjl", 2)]
     assert ipq < 0.8 * ip
+
+
+# ------------------------------------------- decode-attend over triplet codes --
+
+def _octo_attend_case(device, bits, heads, group, n, seed=3):
+    """Keys and values of the outlier-channel recipe coded by tq_octo_encode,
+    attended by tq_octo_attend; checked against the oracle's attention over
+    k_hat and v_hat decoded in float64 from the GPU's own records (2e-3 of
+    the output norm)."""
+    w = W.DECODE_32K.with_(seed=seed, seq_len=max(n, 1), num_kv_heads=heads, num_q_heads=heads * group)
+    kb, _ = W.keys(w)
+    vb, _ = W.values(w)
+    kb = np.ascontiguousarray(np.swapaxes(kb, 0, 1)[:, :n]).reshape(heads * n, 128)
+    vb = np.ascontiguousarray(np.swapaxes(vb, 0, 1)[:, :n]).reshape(heads * n, 128)
+    rot = tq.tq_make_rotation(42, 128)
+    tb = _octo_tables_dev(bits, device)
+    rb = tq.tq_octo_record_bytes(128, bits)
+    kc = torch.zeros((heads, n, rb), dtype=torch.uint8, device=device)
+    vc = torch.zeros((heads, n, rb), dtype=torch.uint8, device=device)
+    kg = torch.zeros((heads, n), dtype=torch.int16, device=device)
+    vg = torch.zeros((heads, n), dtype=torch.int16, device=device)
+    if n:
+        tq.tq_octo_encode(to_device(kb, "bf16", device), bits, rot, tb, kc.view(-1, rb), kg.view(-1))
+        tq.tq_octo_encode(to_device(vb, "bf16", device), bits, rot, tb, vc.view(-1, rb), vg.view(-1))
+    _, q64 = W.queries(w)
+    q = torch.from_numpy(q64[0].astype(np.float32).reshape(heads, group, 128)).to(device)
+    out = torch.full((heads, group, 128), float("nan"), device=device)
+    ws = torch.empty(tq.tq_octo_attend_workspace_bytes(heads, group, n), dtype=torch.uint8, device=device)
+    scale = 1.0 / math.sqrt(128)
+    _say("octo attend", bits, heads, group, n)
+    tq.tq_octo_attend(q, kc, kg, vc, vg, bits, rot, tb, out, ws, scale=scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    if n == 0:
+        assert np.all(got == 0)
+        return 0.0
+    dirs, crho = O.octo_codebooks(128, bits)
+    ka, kcc, kk_ = O.octo_unpack(kc.cpu().numpy(), bits, 128)
+    va, vcc, vk_ = O.octo_unpack(vc.cpu().numpy(), bits, 128)
+    kh = O.octo_decode(ka, kcc, kk_, kg.cpu().numpy().view(np.float16), 42, 128, dirs, crho)
+    vh = O.octo_decode(va, vcc, vk_, vg.cpu().numpy().view(np.float16), 42, 128, dirs, crho)
+    qf = q.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for h in range(heads):
+        for g in range(group):
+            ref, _ = O.attention(qf[h, g], kh[h], vh[h], scale)
+            e = np.linalg.norm(got[h, g] - ref) / np.linalg.norm(ref)
+            assert e <= OUT_RTOL, (h, g, e)
+            worst = max(worst, e)
+    _say(f"  worst relative error {worst:.2e}")
+    return worst
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("group", [1, 8, 16])
+def test_octo_attend_matches_oracle(device, bits, group):
+    # 3 heads x 1000 keys: eight 128-key splits per head, a ragged last one
+    _octo_attend_case(device, bits, 3, group, 1000)
+
+
+def test_octo_attend_small_and_empty(device):
+    # one key, a sub-tile tail, one chunk plus one key, and no keys (zeros)
+    for n in (1, 5, 129, 0):
+        _octo_attend_case(device, 3, 2, 8, n)
+
+
+def test_octo_attend_multi_chunk_splits(device):
+    # 150,000 keys of one head: 256-key splits of two staged chunks each
+    assert tq.tq_octo_attend_workspace_bytes(1, 8, 150000) == 4 * 586 * 8 * 132 * 4
+    _octo_attend_case(device, 4, 1, 8, 150000)

@@ -343,6 +343,29 @@ def test_octo_qjl_argument_checks_happen_before_the_device():
     assert lg(q, cd, g, sg, rh, 8, 8, 0, 4, r.handle, r2.handle, tb, 16384, 0.1, out, None) == tq.TQ_OK
 
 
+def test_octo_attend_argument_checks_happen_before_the_device():
+    L = tq.lib()
+    r = tq.tq_make_rotation(42, 128)
+    q, kc, kg, vc, vg, tb, out, ws = (0x200000 + 0x100000 * i for i in range(8))
+    need = L.tq_octo_attend_workspace_bytes(8, 8, 100)
+    # 100 keys of 8 heads: one 128-key split per head, 4 wave partials of 8 queries
+    assert need == 8 * 4 * 1 * 8 * 132 * 4
+    assert L.tq_octo_attend_workspace_bytes(0, 8, 100) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_octo_attend_workspace_bytes(8, 17, 100) == tq.TQ_ERR_INVALID_ARG
+    at = L.tq_octo_attend
+    assert at(q, kc, kg, vc, vg, 8, 8, 100, 4, r.handle, tb, 16384, 0.1, out, ws, need - 1, None) == tq.TQ_ERR_WORKSPACE
+    assert at(q, kc, kg, vc, vg, 8, 17, 100, 4, r.handle, tb, 16384, 0.1, out, ws, need, None) == tq.TQ_ERR_UNSUPPORTED
+    assert at(q, kc, kg, vc, vg, 8, 8, 100, 5, r.handle, tb, 16384, 0.1, out, ws, need, None) == tq.TQ_ERR_UNSUPPORTED
+    assert at(q, kc, kg, None, vg, 8, 8, 100, 4, r.handle, tb, 16384, 0.1, out, ws, need, None) == tq.TQ_ERR_INVALID_ARG
+    assert at(q, kc, kg, vc, vg, 8, 8, 100, 4, r.handle, tb, 16384, 0.1, out + 4, ws, need, None) == tq.TQ_ERR_INVALID_ARG
+    assert at(q, kc, kg, vc, vg, 8, 8, 100, 4, r.handle, tb, 16384, float("inf"), out, ws, need, None) == tq.TQ_ERR_INVALID_ARG
+    # splits stay whole 128-key chunks and at most 1024 per head
+    for heads, n in ((1, 1), (8, 32768), (1, 1 << 24), (64, 131072)):
+        b = L.tq_octo_attend_workspace_bytes(heads, 1, n)
+        nsplit = b // (heads * 4 * 132 * 4)
+        assert 1 <= nsplit <= 1024 and nsplit * heads * 4 * 132 * 4 == b
+
+
 def test_noalloc_decode_checks_happen_before_the_device():
     # the allocation-free decode takes tq_decode_attend's arguments minus the
     # workspace; a call whose split partials would not fit the fixed 16 MiB
