@@ -362,7 +362,7 @@ def main():
     # that each head's records are contiguous), then the logits of sequence
     # 0's query group against every key of its KV head straight from the
     # records.  Outside the timed step, reported beside it.
-    oc_enc_ms, oc_log_ms, oq_enc_ms, oq_log_ms = [], [], [], []
+    oc_enc_ms, oc_log_ms, oq_enc_ms, oq_log_ms, oa_ms = [], [], [], [], []
     if args.only == "both" and not args.no_extras:
         orot = tq.tq_make_rotation(w.rot_seed, 128)
         otb = torch.empty(tq.tq_octo_table_bytes(w.bits_k), dtype=torch.uint8, device=dev)
@@ -379,6 +379,20 @@ def main():
         orot2 = tq.tq_make_rotation(w.rot_seed + 1, 128)
         osig = [torch.empty((H, T, 16), dtype=torch.uint8, device=dev) for _ in sets]
         orho = [torch.empty((H, T), dtype=torch.int16, device=dev) for _ in sets]
+        # decode-attend over triplet-coded keys and values: every sequence's
+        # query group against its own keys; a "head" of the call is one
+        # (KV head, sequence), whose keys are contiguous in the [H][T] layout
+        NS, S = w.num_seqs, w.seq_len
+        ovh = [s["V"].view(T, H, 128).transpose(0, 1).contiguous() for s in sets]
+        ovcodes = [torch.empty((H, T, orb), dtype=torch.uint8, device=dev) for _ in sets]
+        ovgam = [torch.empty((H, T), dtype=torch.int16, device=dev) for _ in sets]
+        for j in range(nsets):
+            tq.tq_octo_encode(ovh[j].view(-1, 128), w.bits_k, orot, otb, ovcodes[j].view(-1, orb), ovgam[j].view(-1),
+                              stream)
+        del ovh
+        oqa = q.float().view(NS, H, G, 128).transpose(0, 1).reshape(H * NS, G, 128).contiguous()
+        oout = torch.empty((H * NS, G, 128), dtype=torch.float32, device=dev)
+        ows = torch.empty(tq.tq_octo_attend_workspace_bytes(H * NS, G, S), dtype=torch.uint8, device=dev)
         reps = max(5, args.steps // 4)
 
         def oc_enc(i):
@@ -400,7 +414,14 @@ def main():
             tq.tq_octo_logits_qjl(oq, ocodes[j], ogam[j], osig[j], orho[j], w.bits_k, orot, orot2, otb, olog,
                                   stream=stream)
 
-        for fn, acc in ((oc_enc, oc_enc_ms), (oc_log, oc_log_ms), (oq_enc, oq_enc_ms), (oq_log, oq_log_ms)):
+        def oa_att(i):
+            j = i % nsets
+            tq.tq_octo_attend(oqa, ocodes[j].view(H * NS, S, orb), ogam[j].view(H * NS, S),
+                              ovcodes[j].view(H * NS, S, orb), ovgam[j].view(H * NS, S), w.bits_k, orot, otb, oout,
+                              ows, stream=stream)
+
+        for fn, acc in ((oc_enc, oc_enc_ms), (oc_log, oc_log_ms), (oq_enc, oq_enc_ms), (oq_log, oq_log_ms),
+                        (oa_att, oa_ms)):
             for i in range(max(3, nsets)):
                 fn(i)
             ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
@@ -410,7 +431,7 @@ def main():
                 ev[i][1].record(stream)
             torch.cuda.synchronize()
             acc.extend(e[0].elapsed_time(e[1]) for e in ev)
-        del okh, ocodes, ogam, olog, osig, orho
+        del okh, ocodes, ogam, olog, osig, orho, ovcodes, ovgam, oout, ows
 
     # ---- on-box ceilings: a plain stream read (the library's measurement
     # aid) and a device copy, each over 2 GiB
@@ -516,6 +537,15 @@ def main():
             "frac": round(qlb / ql_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": qlb,
             "us_per_launch": round(ql_s * 1e6, 2), "keys_per_s": round(nk / ql_s, 1),
             "note": f"OCTOPUS-QJL logits: {G} queries per KV head against every key, with the residual estimate"}
+    if oa_ms:
+        ab = 2 * nk * (orb + 2) + 2 * w.num_seqs * w.num_q_heads * 128 * 4   # key and value records + norms in
+        oa_s = float(np.mean(oa_ms)) / 1e3
+        kernels["tq_octo_attend"] = {
+            "bound": "hbm", "achieved": round(ab / oa_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(ab / oa_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": ab,
+            "us_per_launch": round(oa_s * 1e6, 2),
+            "note": "decode-attend over triplet-coded keys and values, every sequence's query group "
+                    "(split kernel + merge); not part of the timed step"}
     dom = "tq_encode" if enc_s >= dec_s else "tq_decode_attend"
     traffic = None
     tf = os.path.join(ROOT, "profiles", "traffic.json")
