@@ -26,6 +26,7 @@
 namespace tq {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 template <int B>
 struct Octo {
@@ -482,21 +483,25 @@ int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
 // triplets' norms and directions, no K_hat or V_hat written; [P2] attention
 // softmax(q K^T scale) V): a split of split_len keys per workgroup, staged
 // 128 keys at a time (records and norms of keys and values), each wave
-// taking 16-key sub-tiles in turn and keeping its own online softmax, in
-// log2 units (scale * log2(e) folded into the queries), and accumulators.
-//  - Scores: the logits kernel's product, C[16 keys x 16 queries] over 33
-//    steps of 4 rotated dims, times gamma_k.
-//  - Values: C[16 dims x 16 queries] += A[16 dims x 4 keys] * B[4 keys x 16
-//    queries] over 4 key steps, B = p * gamma_v through LDS.  The 144 rows of
-//    the 9 dim tiles are (triplet, component) pairs: row m of tile 3u + c is
-//    component c of triplet 16u + m, so a lane decodes three triplets of a
-//    key per step (field, direction, norm) and feeds nine products.  Rows
-//    past dim 127 (triplet 42's pad, triplets 43..47) hold zero.
+// taking a 32-key sub-tile of the chunk and keeping its own online softmax,
+// in log2 units (scale * log2(e) folded into the queries), and accumulators.
+//  - Scores: the logits kernel's fp32 product, C[16 keys x 16 queries] over
+//    33 steps of 4 rotated dims, twice, times gamma_k.
+//  - Values: C[16 rows x 16 queries] += A[16 rows x 32 keys] * B[32 keys x 16
+//    queries] on 16-bit operands with fp32 accumulation, B = f16(p gamma_v)
+//    through LDS.  The 144 rows of the 9 row tiles are (triplet, component)
+//    pairs: row m of tile 3u + c is component c of triplet 16u + m, so a
+//    lane decodes triplet 16u + col of its 8 keys (field, direction, norm)
+//    once for three products.  Rows past dim 127 (triplet 42's pad
+//    component, triplets 43..47) hold zero.  The operands' rounding (2^-11
+//    relative) is far inside the output bar; the scores stay fp32.
 //  - Each wave writes its own partial (o_rot, m in natural-log units, l);
 //    merge_kernel combines the 4 * splits partials of a head, normalises and
 //    rotates back.
+// Held to 3 waves per SIMD (168 VGPRs, one spilled): left to itself the
+// compiler takes 204 and 2 waves, 1014 against 576 us on llama70b's keys
 template <int B>
-__global__ __launch_bounds__(256) void octo_attend_kernel(const OctoArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void octo_attend_kernel(const OctoArgs a) {
   using C = Octo<B>;
   constexpr int kStride = C::kWords + 1;
   constexpr int kQd = 132;
@@ -510,7 +515,7 @@ __global__ __launch_bounds__(256) void octo_attend_kernel(const OctoArgs a) {
     } ch;
   } s_u;
   __shared__ float s_rho[8];
-  __shared__ float s_p[4][16][17];      // per wave: p * gamma_v, [key][query]
+  __shared__ float s_p[4][16][36];      // per wave: p * gamma_v, [query][key of the 32-key sub-tile]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y, split = blockIdx.x;
   const int64_t kb0 = (int64_t)split * a.split_len;
@@ -575,27 +580,37 @@ __global__ __launch_bounds__(256) void octo_attend_kernel(const OctoArgs a) {
       s_u.ch.g[1][tid] = in ? __half2float(__ushort_as_half(vg[c0 + tid])) : 0.f;
     }
     __syncthreads();
-    for (int t = wave; t * 16 < nk; t += 4) {
-      // ---- scores of keys 16t .. 16t+15 (rows 4kk + r) for query col
-      const uint32_t* rk = s_u.ch.rec[0] + (t * 16 + col) * kStride;
-      f32x4 sl = {0.f, 0.f, 0.f, 0.f};
+    for (int t = wave; t * 32 < nk; t += 4) {
+      // ---- scores of keys 32t .. 32t+31, two 16-key products: row 4kk + r
+      // of half X is key 32t + 16X + 4kk + r, for query col
+      f32x4 sl[2];
 #pragma unroll
-      for (int m = 0; m < 11; ++m) {
-        const uint32_t f = field_of(rk, 4 * m + kk);   // triplet 43 reads zero bits; its q is 0
-        const float4 d = s_dir[(int)(f & (C::kNd - 1)) * C::kNd + (int)((f >> C::kBd) & (C::kNd - 1))];
-        const float r = s_rho[f >> (2 * C::kBd)];
-        sl = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.x, qb[3 * m], sl, 0, 0, 0);
-        sl = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.y, qb[3 * m + 1], sl, 0, 0, 0);
-        sl = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.z, qb[3 * m + 2], sl, 0, 0, 0);
-      }
-      float sc[4];
+      for (int X = 0; X < 2; ++X) {
+        const uint32_t* rk = s_u.ch.rec[0] + (t * 32 + 16 * X + col) * kStride;
+        sl[X] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = t * 16 + 4 * kk + r;
-        sc[r] = key < nk ? sl[r] * s_u.ch.g[0][key] : -INFINITY;
+        for (int m = 0; m < 11; ++m) {
+          const uint32_t f = field_of(rk, 4 * m + kk);   // triplet 43 reads zero bits; its q is 0
+          const float4 d = s_dir[(int)(f & (C::kNd - 1)) * C::kNd + (int)((f >> C::kBd) & (C::kNd - 1))];
+          const float r = s_rho[f >> (2 * C::kBd)];
+          sl[X] = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.x, qb[3 * m], sl[X], 0, 0, 0);
+          sl[X] = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.y, qb[3 * m + 1], sl[X], 0, 0, 0);
+          sl[X] = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.z, qb[3 * m + 2], sl[X], 0, 0, 0);
+        }
       }
-      // ---- online softmax for query col over the 16 keys
-      const float bm = max_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+      float sc[8];
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = t * 32 + 16 * X + 4 * kk + r;
+          sc[4 * X + r] = key < nk ? sl[X][r] * s_u.ch.g[0][key] : -INFINITY;
+        }
+      // ---- online softmax for query col over the 32 keys
+      float bm = sc[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) bm = fmaxf(bm, sc[i]);
+      bm = max_rows(bm);
       const float new_m = fmaxf(run_m, bm);
       if (__builtin_amdgcn_ballot_w64(new_m > run_m) != 0) {
         const float alpha = run_m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(run_m - new_m);
@@ -606,31 +621,43 @@ __global__ __launch_bounds__(256) void octo_attend_kernel(const OctoArgs a) {
       run_m = new_m;
       const float mref = new_m == -INFINITY ? 0.f : new_m;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sc[r] - mref);   // exp2(-inf) = 0
-        run_l += p;
-        s_p[wave][4 * kk + r][col] = p * s_u.ch.g[1][t * 16 + 4 * kk + r];
-      }
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 16 * X + 4 * kk + r;
+          const float p = __builtin_amdgcn_exp2f(sc[4 * X + r] - mref);   // exp2(-inf) = 0
+          run_l += p;
+          s_p[wave][col][key] = p * s_u.ch.g[1][t * 32 + key];
+        }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // ---- values: step s takes keys 16t + 4s .. +3 (key 4s + kk in this lane)
+      // ---- values: one 32-key product per row tile on 16-bit operands
+      // (fp32 accumulation).  Lane (kk, col) holds K slots 8kk .. 8kk+7,
+      // keys 32t + 8kk + i: B = f16(p gamma_v) of query col, A = f16 of the
+      // components of triplet 16u + col of those keys (row col of tiles 3u,
+      // 3u+1, 3u+2)
+      f16x8 bv;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const float b = s_p[wave][4 * st + kk][col];
-        const uint32_t* rv = s_u.ch.rec[1] + (t * 16 + 4 * st + kk) * kStride;
+      for (int i = 0; i < 8; ++i) bv[i] = (_Float16)s_p[wave][col][8 * kk + i];
 #pragma unroll
-        for (int u = 0; u < 3; ++u) {
-          const int j = 16 * u + col;                 // triplet of rows col of tiles 3u .. 3u+2
-          const uint32_t f = field_of(rv, j < kOctoTri ? j : kOctoTri - 1);
+      for (int u = 0; u < 3; ++u) {
+        const int j = 16 * u + col;
+        const int jc = j < kOctoTri ? j : kOctoTri - 1;
+        f16x8 ax, ay, az;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t* rv = s_u.ch.rec[1] + (t * 32 + 8 * kk + i) * kStride;
+          const uint32_t f = field_of(rv, jc);
           const float4 d = s_dir[(int)(f & (C::kNd - 1)) * C::kNd + (int)((f >> C::kBd) & (C::kNd - 1))];
           const float r = j < kOctoTri ? s_rho[f >> (2 * C::kBd)] : 0.f;
-          acc[3 * u] = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.x, b, acc[3 * u], 0, 0, 0);
-          acc[3 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.y, b, acc[3 * u + 1], 0, 0, 0);
-          // component z of triplet 42 is the pad coordinate (dim 128)
-          acc[3 * u + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(j < kOctoTri - 1 ? r * d.z : 0.f, b, acc[3 * u + 2],
-                                                               0, 0, 0);
+          ax[i] = (_Float16)(r * d.x);
+          ay[i] = (_Float16)(r * d.y);
+          az[i] = (_Float16)(j < kOctoTri - 1 ? r * d.z : 0.f);   // triplet 42's z is the pad
         }
+        acc[3 * u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bv, acc[3 * u], 0, 0, 0);
+        acc[3 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ay, bv, acc[3 * u + 1], 0, 0, 0);
+        acc[3 * u + 2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bv, acc[3 * u + 2], 0, 0, 0);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();   // s_p is rewritten by the next sub-tile
