@@ -52,6 +52,29 @@ __device__ __forceinline__ int octo_block_lo(float v, int nd) {
   return min(max(h, 0), nd - 2);
 }
 
+// A buffer resource over the n bytes at p (raw, stride 0, 32-bit data
+// format): a load whose offset lies at or past n returns zero and touches
+// no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
+}
+
+// Copy the direction table (N entries of (x, y, z, 0)) to LDS with every
+// load issued before the first store (a loop that stores as it loads waits
+// one memory round trip per iteration); indices past N re-read the last
+// entry and store nothing.
+template <int N>
+__device__ __forceinline__ void load_dirs(float4* s_dir, const float* dirs, int tid) {
+  constexpr int kIt = (N + 255) / 256;
+  const float4* src = reinterpret_cast<const float4*>(dirs);
+  float4 t[kIt];
+#pragma unroll
+  for (int r = 0; r < kIt; ++r) t[r] = src[min(tid + 256 * r, N - 1)];
+#pragma unroll
+  for (int r = 0; r < kIt; ++r)
+    if (tid + 256 * r < N) s_dir[tid + 256 * r] = t[r];
+}
+
 // atan(a) for a in [0, 1] as a * P(a^2), P of degree 7: the odd polynomial
 // of kv_cache_vector_encode_amd/fit_atan.py (Lawson's reweighted least
 // squares toward the minimax fit), coefficients rounded to fp32; largest
@@ -108,7 +131,7 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
   __shared__ float s_crho[8];
   const int tid = threadIdx.x, row = tid >> 4;
   const int L = tid & 15, ell = perm16(L);
-  for (int i = tid; i < kNd * kNd; i += 256) s_dir[i] = reinterpret_cast<const float4*>(a.dirs)[i];
+  load_dirs<kNd * kNd>(s_dir, a.dirs, tid);
   if (QJL && tid < 8) s_crho[tid] = a.crho[tid];
   const uint32_t sneg = sign_byte(a.rot, ell);
   uint32_t smask[8];
@@ -260,12 +283,12 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
 // records in LDS.  Each wave takes 16-key tiles in turn.
 constexpr int kOctoMfmaTile = 128;   // keys per tile step (2 tiles of 16 per wave)
 
-// 5 waves per SIMD at b = 2, 3 (the kernel held to 96 VGPRs: 248 against
-// 263 us on the 4.2M keys of llama70b at b = 3); at b = 4 that limit spills
-// and measured slower, so it keeps 4; the QJL variant's 32 more query
-// registers leave room for 3
+// 5 waves per SIMD at b = 2 (the kernel held to 96 VGPRs); at b = 3, 4
+// that limit spills (b = 3: 235 against 226 us at 4 waves on the 4.2M keys
+// of llama70b), so they keep 4; the QJL variant's 32 more query registers
+// leave room for 3
 template <int B, bool QJL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B == 4 ? 4 : 5))) void octo_logits_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B == 2 ? 5 : 4))) void octo_logits_mfma_kernel(
     const OctoArgs a) {
   using C = Octo<B>;
   constexpr int kStride = C::kWords + 1;
@@ -278,16 +301,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B
       float q[16][kQd];
       float w[QJL ? 16 : 1][kD];   // OCTOPUS-QJL: R' R q (scaled), natural order
     } qw;
-    uint32_t rec[kOctoMfmaTile * kStride];
+    struct {                       // one tile of keys, zeros past the last
+      uint32_t rec[kOctoMfmaTile * kStride];
+      float g[kOctoMfmaTile];                  // norms
+      uint4 sg[QJL ? kOctoMfmaTile : 1];       // OCTOPUS-QJL: sign sketches
+      float sk[QJL ? kOctoMfmaTile : 1];       // and sqrt(pi/2)/sqrt(d) times their norms
+    } t;
   } s_u;
   auto& s_q = s_u.qw.q;
   auto& s_w = s_u.qw.w;
   static_assert(sizeof(s_u.qw) == sizeof(float) * (16 * kQd + (QJL ? 16 : 1) * kD), "q and w are contiguous");
-  uint32_t* const s_rec = s_u.rec;
+  uint32_t* const s_rec = s_u.t.rec;
   __shared__ float s_rho[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y;
-  for (int i = tid; i < C::kNd * C::kNd; i += 256) s_dir[i] = reinterpret_cast<const float4*>(a.dirs)[i];
+  load_dirs<C::kNd * C::kNd>(s_dir, a.dirs, tid);
   if (tid < 8) s_rho[tid] = a.crho[tid];
   // queries past the group (and, with the sketch, their R' R q) stay zero
   float* qf = &s_q[0][0];
@@ -346,23 +374,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B
   }
   // the workgroup walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... of
   // its head, so the table and the queries are set up once per workgroup;
-  // the next tile's records are loaded into registers while this one is
-  // multiplied (the barrier at the top of the tile loop also orders the
-  // reads of s_q above before the first records overwrite it)
+  // the next tile's records (and sketches) are loaded into registers while
+  // this one is multiplied, its norms once the products are done (a
+  // register fewer held through them), so the products read LDS only (the
+  // barrier at the top of the tile loop also orders the reads of s_q above
+  // before the first records overwrite it)
   const int64_t ntiles = (a.n + kOctoMfmaTile - 1) / kOctoMfmaTile;
   constexpr int kPre = (kOctoMfmaTile * C::kWords + 255) / 256;
   uint32_t pre[kPre];
+  uint16_t pg, pr;              // norm and sketch norm of key tid % 128
+  uint32_t ps[QJL ? 2 : 1];     // sketch words tid and tid + 256 of the tile
   auto fetch = [&](int64_t tl) {
     const int64_t k0 = tl * kOctoMfmaTile;
     const int n_ = (int)(a.n - k0 < kOctoMfmaTile ? a.n - k0 : kOctoMfmaTile);
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.codes + ((int64_t)head * a.n + k0) * C::kRec);
+    const int64_t kb = (int64_t)head * a.n + k0;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.codes + kb * C::kRec);
 #pragma unroll
     for (int r = 0; r < kPre; ++r) {
       const int i = tid + 256 * r;
       pre[r] = i < n_ * C::kWords ? src[i] : 0u;
     }
+    // indices past the tile's last key re-read it (stored as zeros, or
+    // multiplied by a zero norm)
+    if constexpr (QJL) {
+      const uint32_t* sp = reinterpret_cast<const uint32_t*>(a.qjl_signs + kb * 16);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int i = tid + 256 * r;
+        ps[r] = sp[4 * min(i >> 2, n_ - 1) + (i & 3)];
+      }
+    }
   };
-  if (blockIdx.x < ntiles) fetch(blockIdx.x);
+  auto fetch_norms = [&](int64_t tl) {
+    const int64_t k0 = tl * kOctoMfmaTile;
+    const int n_ = (int)(a.n - k0 < kOctoMfmaTile ? a.n - k0 : kOctoMfmaTile);
+    const int64_t kg = (int64_t)head * a.n + k0 + min(tid & (kOctoMfmaTile - 1), n_ - 1);
+    pg = a.gamma[kg];
+    if constexpr (QJL) pr = a.qjl_rho[kg];
+  };
+  if (blockIdx.x < ntiles) {
+    fetch(blockIdx.x);
+    fetch_norms(blockIdx.x);
+  }
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
   const int64_t key0 = tile * kOctoMfmaTile;
   const int nk = (int)(a.n - key0 < kOctoMfmaTile ? a.n - key0 : kOctoMfmaTile);
@@ -374,6 +427,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B
       const int k = i / C::kWords, w = i - k * C::kWords;
       s_rec[k * kStride + w] = pre[r];   // rows past the end hold zeros
     }
+  }
+  if (tid < kOctoMfmaTile) {
+    s_u.t.g[tid] = tid < nk ? __half2float(__ushort_as_half(pg)) : 0.f;
+    if constexpr (QJL) s_u.t.sk[tid] = tid < nk ? 0.1107783657f * __half2float(__ushort_as_half(pr)) : 0.f;
+  }
+  if constexpr (QJL) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) reinterpret_cast<uint32_t*>(s_u.t.sg)[tid + 256 * r] = ps[r];
   }
   __syncthreads();
   if (tile + gridDim.x < ntiles) fetch(tile + gridDim.x);
@@ -395,10 +456,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B
       // A[key][j] = +-sqrt(pi/2)/sqrt(d) rho16 by the key's sign bit j
       // (set: negative), so the products add the residual estimate
       // sqrt(pi/2)/sqrt(d) rho16 sum_j sgn_j (R' R q)_j to the logit
-      const int key = t * 16 + col;
-      const int64_t kg = (int64_t)head * a.n + key0 + (key < nk ? key : 0);
-      const uint4 sg = *reinterpret_cast<const uint4*>(a.qjl_signs + kg * 16);
-      const float sk = key < nk ? 0.1107783657f * __half2float(__ushort_as_half(a.qjl_rho[kg])) : 0.f;
+      const uint4 sg = s_u.t.sg[t * 16 + col];
+      const float sk = s_u.t.sk[t * 16 + col];   // zero past the last key
       const uint32_t sgs[4] = {sg.x >> kk, sg.y >> kk, sg.z >> kk, sg.w >> kk};
       const uint32_t skb = __float_as_uint(sk);
 #pragma unroll
@@ -409,12 +468,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B
     }
     if (col < a.group) {
       float* o = a.out + ((int64_t)head * a.group + col) * a.n + key0 + t * 16 + 4 * kk;
-      const uint16_t* gp = a.gamma + (int64_t)head * a.n + key0 + t * 16 + 4 * kk;
+      const float4 g = *reinterpret_cast<const float4*>(&s_u.t.g[t * 16 + 4 * kk]);
+      const float gr[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (t * 16 + 4 * kk + r < nk) o[r] = acc[r] * __half2float(__ushort_as_half(gp[r]));
+        if (t * 16 + 4 * kk + r < nk) o[r] = acc[r] * gr[r];
     }
   }
+  if (tile + gridDim.x < ntiles) fetch_norms(tile + gridDim.x);
   }
 }
 
@@ -461,11 +522,12 @@ int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.n <= 0 || a.heads < 1 || a.heads > 65535 || a.group < 1 || a.group > kOctoMaxGroup)
     return (int)hipErrorInvalidValue;
-  // about as many workgroups as are resident at once (waves per SIMD: 4 at
-  // b = 4, 5 at b = 2, 3, one workgroup's wave on each SIMD), spread over
+  // about as many workgroups as are resident at once (waves per SIMD: 5 at
+  // b = 2, 4 at b = 3, 4, 3 with the sketch; one workgroup's wave on each
+  // SIMD), spread over
   // the heads, each looping over tiles of its head (the table and the
   // queries are set up once per workgroup)
-  const int64_t wgs = 256 * (a.qjl_signs ? 3 : bits == 4 ? 4 : 5);
+  const int64_t wgs = 256 * (a.qjl_signs ? 3 : bits == 2 ? 5 : 4);
   const int64_t tiles = std::min((a.n + kOctoMfmaTile - 1) / kOctoMfmaTile, std::max<int64_t>(1, wgs / a.heads));
   const dim3 grid((unsigned)tiles, (unsigned)a.heads);
   switch (bits) {
@@ -521,7 +583,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void o
   const int64_t kb0 = (int64_t)split * a.split_len;
   const int64_t kb1 = a.n < kb0 + a.split_len ? a.n : kb0 + a.split_len;
   const float LOG2E = 1.4426950408889634f;
-  for (int i = tid; i < C::kNd * C::kNd; i += 256) s_dir[i] = reinterpret_cast<const float4*>(a.dirs)[i];
+  load_dirs<C::kNd * C::kNd>(s_dir, a.dirs, tid);
   if (tid < 8) s_rho[tid] = a.crho[tid];
   float* qf = &s_u.q[0][0];
   for (int i = tid; i < 16 * kQd; i += 256) qf[i] = 0.f;   // queries past the group stay zero
@@ -567,17 +629,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void o
   const uint16_t* vg = a.vgamma + (int64_t)head * a.n;
   for (int64_t c0 = kb0; c0 < kb1; c0 += kCh) {   // the same trip count in every wave
     const int nk = (int)(kb1 - c0 < kCh ? kb1 - c0 : kCh);
+    // the chunk's records and norms, every load issued before the first
+    // store: the nk records are nk * kWords consecutive words, read through
+    // a range of that many words (slots past them load as zeros)
+    constexpr int kIt = (kCh * C::kWords + 255) / 256;
+    const int nb = 4 * nk * C::kWords;   // bytes of the chunk's records
+    const uint8_t* kc = kcod + c0 * C::kRec;
+    const uint8_t* vc = vcod + c0 * C::kRec;
+    uint32_t kr[kIt], vr[kIt];
+#pragma unroll
+    for (int r = 0; r < kIt; ++r) {   // pass r reads bytes [1024 r, 1024 r + 1024)
+      // the same for every lane: read it from the first so the range stays scalar
+      const int left = __builtin_amdgcn_readfirstlane(max(nb - 1024 * r, 0));
+      kr[r] = __builtin_amdgcn_raw_buffer_load_b32(byte_range(kc + 1024 * r, left), 4 * tid, 0, 0);
+      vr[r] = __builtin_amdgcn_raw_buffer_load_b32(byte_range(vc + 1024 * r, left), 4 * tid, 0, 0);
+    }
+    const int tc = min(tid & (kCh - 1), nk - 1);
+    const uint16_t gk16 = kg[c0 + tc], gv16 = vg[c0 + tc];
     __syncthreads();   // the previous chunk (or the queries) is no longer read
-    for (int i = tid; i < kCh * C::kWords; i += 256) {
-      const int k = i / C::kWords, w = i - k * C::kWords;
-      const bool in = k < nk;
-      s_u.ch.rec[0][k * kStride + w] = in ? reinterpret_cast<const uint32_t*>(kcod + (c0 + k) * C::kRec)[w] : 0u;
-      s_u.ch.rec[1][k * kStride + w] = in ? reinterpret_cast<const uint32_t*>(vcod + (c0 + k) * C::kRec)[w] : 0u;
+#pragma unroll
+    for (int r = 0; r < kIt; ++r) {
+      const int i = tid + 256 * r;
+      if (i < kCh * C::kWords) {
+        const int k = i / C::kWords, w = i - k * C::kWords;
+        s_u.ch.rec[0][k * kStride + w] = kr[r];
+        s_u.ch.rec[1][k * kStride + w] = vr[r];
+      }
     }
     if (tid < kCh) {
       const bool in = tid < nk;
-      s_u.ch.g[0][tid] = in ? __half2float(__ushort_as_half(kg[c0 + tid])) : 0.f;
-      s_u.ch.g[1][tid] = in ? __half2float(__ushort_as_half(vg[c0 + tid])) : 0.f;
+      s_u.ch.g[0][tid] = in ? __half2float(__ushort_as_half(gk16)) : 0.f;
+      s_u.ch.g[1][tid] = in ? __half2float(__ushort_as_half(gv16)) : 0.f;
     }
     __syncthreads();
     for (int t = wave; t * 32 < nk; t += 4) {
