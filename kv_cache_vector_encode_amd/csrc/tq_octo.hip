@@ -184,8 +184,14 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
     if (L < kOctoRowPad - kD) s_y[row][kD + L] = 0.f;
     for (int w = L; w < C::kWords; w += 16) s_rec[row][w] = 0u;
     __syncthreads();
-    for (int i = L; i < kOctoTri; i += 16) {
-      const float tx = s_y[row][3 * i], ty = s_y[row][3 * i + 1], tz = s_y[row][3 * i + 2];
+    // the group's 16 x 43 triplets in one flat list over the 256 threads:
+    // 2.69 passes, so the last wave has no third pass (with 43 per 16-lane
+    // row every wave ran three)
+    // (unrolled, so each pass's row and triplet index are computed once)
+#pragma unroll
+    for (int f = tid; f < 16 * kOctoTri; f += 256) {
+      const int rw = f / kOctoTri, i = f - rw * kOctoTri;
+      const float tx = s_y[rw][3 * i], ty = s_y[rw][3 * i + 1], tz = s_y[rw][3 * i + 2];
       const float rr = tx * tx + ty * ty + tz * tz;
       // the map needs z / rho only; the azimuth is scale-free
       const float nz = rr > 0.f ? tz * __builtin_amdgcn_rsqf(rr) : 1.f;
@@ -228,13 +234,13 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
         // owns these three coordinates)
         const float4 d = s_dir[ca * kNd + cc];
         const float rk = s_crho[k];
-        s_y[row][3 * i] = __builtin_fmaf(-rk, d.x, tx);
-        s_y[row][3 * i + 1] = __builtin_fmaf(-rk, d.y, ty);
-        s_y[row][3 * i + 2] = __builtin_fmaf(-rk, d.z, tz);
+        s_y[rw][3 * i] = __builtin_fmaf(-rk, d.x, tx);
+        s_y[rw][3 * i + 1] = __builtin_fmaf(-rk, d.y, ty);
+        s_y[rw][3 * i + 2] = __builtin_fmaf(-rk, d.z, tz);
       }
       const int bit = i * C::kField, w = bit >> 5, sh = bit & 31;
-      atomicOr(&s_rec[row][w], field << sh);
-      if (sh + C::kField > 32) atomicOr(&s_rec[row][w + 1], field >> (32 - sh));
+      atomicOr(&s_rec[rw][w], field << sh);
+      if (sh + C::kField > 32) atomicOr(&s_rec[rw][w + 1], field >> (32 - sh));
     }
     __syncthreads();
     if constexpr (QJL) {
