@@ -9,8 +9,8 @@
 // and its neighbours picks the codes with the least ||t - rho_hat n_hat||^2.
 //
 // Encode: one vector per 16-lane row (the in-register FWHT of the encoder),
-// the rotated coordinates staged in LDS, then each lane takes triplets
-// L, L+16, L+32 of its row; the direction table sits in LDS.
+// the rotated coordinates staged in LDS, then the workgroup's threads take
+// the 16 vectors' triplets as one flat list; the direction table sits in LDS.
 // Logits: a matrix-core product of the group's rotated queries with keys
 // decoded in registers (16 keys x 16 queries per tile); each triplet's
 // direction comes from the LDS table scaled by its norm code, and no K_hat
@@ -27,6 +27,7 @@ namespace tq {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int B>
 struct Octo {
@@ -559,10 +560,12 @@ int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
 //    queries] on 16-bit operands with fp32 accumulation, B = f16(p gamma_v)
 //    through LDS.  The 144 rows of the 9 row tiles are (triplet, component)
 //    pairs: row m of tile 3u + c is component c of triplet 16u + m, so a
-//    lane decodes triplet 16u + col of its 8 keys (field, direction, norm)
-//    once for three products.  Rows past dim 127 (triplet 42's pad
-//    component, triplets 43..47) hold zero.  The operands' rounding (2^-11
-//    relative) is far inside the output bar; the scores stay fp32.
+//    lane decodes triplet 16u + col of its 8 keys once for three products:
+//    at b <= 3 from an LDS table of the three f16 products rho_k n for every
+//    field value (one read per triplet), at b = 4 (a 64 KB table) from the
+//    field's direction and norm.  Rows past dim 127 (triplet 42's pad
+//    component, triplets 43..47) are never stored.  The operands' rounding
+//    (2^-11 relative) is far inside the output bar; the scores stay fp32.
 //  - Each wave writes its own partial (o_rot, m in natural-log units, l);
 //    merge_kernel combines the 4 * splits partials of a head, normalises and
 //    rotates back.
@@ -584,6 +587,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void o
   } s_u;
   __shared__ float s_rho[8];
   __shared__ float s_p[4][16][36];      // per wave: p * gamma_v, [query][key of the 32-key sub-tile]
+  // b <= 3: by field value (the field's bits as the index), the f16 values
+  // rho n_x, rho n_y (low, high half of .x), rho n_z (low half of .y)
+  constexpr int kVtN = C::kNr * C::kNd * C::kNd;
+  constexpr bool kVT = kVtN <= 1024;
+  __shared__ uint2 s_vt[kVT ? kVtN : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y, split = blockIdx.x;
   const int64_t kb0 = (int64_t)split * a.split_len;
@@ -594,6 +602,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void o
   float* qf = &s_u.q[0][0];
   for (int i = tid; i < 16 * kQd; i += 256) qf[i] = 0.f;   // queries past the group stay zero
   __syncthreads();
+  if constexpr (kVT) {
+    for (int e = tid; e < kVtN; e += 256) {
+      const float4 d = s_dir[(e & (C::kNd - 1)) * C::kNd + ((e >> C::kBd) & (C::kNd - 1))];
+      const float r = s_rho[e >> (2 * C::kBd)];
+      const _Float16 hx = (_Float16)(r * d.x), hy = (_Float16)(r * d.y), hz = (_Float16)(r * d.z);
+      s_vt[e] = make_uint2((uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16),
+                           (uint32_t)__builtin_bit_cast(uint16_t, hz));
+    }
+  }
   {
     const int row = tid >> 4, L = tid & 15, ell = perm16(L);
     const int rq = row < a.group ? row : 0;
@@ -728,6 +745,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void o
       f16x8 bv;
 #pragma unroll
       for (int i = 0; i < 8; ++i) bv[i] = (_Float16)s_p[wave][col][8 * kk + i];
+      if constexpr (kVT) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+          // rows of triplets past 42 and triplet 42's z land in dims >= 128,
+          // which the partial store skips: their table reads need only stay
+          // inside the record
+          const int jc = min(16 * u + col, kOctoTri - 1);
+          uint32_t xy[8], zz[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint2 e = s_vt[field_of(s_u.ch.rec[1] + (t * 32 + 8 * kk + i) * kStride, jc)];
+            xy[i] = e.x;
+            zz[i] = e.y;
+          }
+          u32x4 px, py, pz;   // f16 pairs (key 2w, key 2w + 1)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            px[w] = __builtin_amdgcn_perm(xy[2 * w + 1], xy[2 * w], 0x05040100u);
+            py[w] = __builtin_amdgcn_perm(xy[2 * w + 1], xy[2 * w], 0x07060302u);
+            pz[w] = __builtin_amdgcn_perm(zz[2 * w + 1], zz[2 * w], 0x05040100u);
+          }
+          acc[3 * u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, px), bv, acc[3 * u], 0, 0, 0);
+          acc[3 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, py), bv, acc[3 * u + 1], 0, 0, 0);
+          acc[3 * u + 2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, pz), bv, acc[3 * u + 2], 0, 0, 0);
+        }
+      } else {
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
         const int j = 16 * u + col;
@@ -746,6 +789,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void o
         acc[3 * u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bv, acc[3 * u], 0, 0, 0);
         acc[3 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ay, bv, acc[3 * u + 1], 0, 0, 0);
         acc[3 * u + 2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bv, acc[3 * u + 2], 0, 0, 0);
+      }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();   // s_p is rewritten by the next sub-tile
