@@ -28,6 +28,7 @@ namespace tq {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 template <int B>
 struct Octo {
@@ -60,20 +61,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void* p, int 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
 }
 
-// Copy the direction table (N entries of (x, y, z, 0)) to LDS with every
-// load issued before the first store (a loop that stores as it loads waits
-// one memory round trip per iteration); indices past N re-read the last
-// entry and store nothing.
-template <int N>
+// Copy the direction table ([xi code][eta code] of (x, y, z, 0), nd x nd
+// entries) to LDS with every load issued before the first store (a loop
+// that stores as it loads waits one memory round trip per iteration);
+// indices past the table re-read its last entry and store nothing.  With
+// kT the copy is transposed to [eta code][xi code], so that the low 2 kBd
+// bits of a triplet field (xi code, then eta code) index it directly.
+template <int ND, bool kT>
 __device__ __forceinline__ void load_dirs(float4* s_dir, const float* dirs, int tid) {
-  constexpr int kIt = (N + 255) / 256;
+  constexpr int N = ND * ND, kIt = (N + 255) / 256;
   const float4* src = reinterpret_cast<const float4*>(dirs);
   float4 t[kIt];
 #pragma unroll
   for (int r = 0; r < kIt; ++r) t[r] = src[min(tid + 256 * r, N - 1)];
 #pragma unroll
-  for (int r = 0; r < kIt; ++r)
-    if (tid + 256 * r < N) s_dir[tid + 256 * r] = t[r];
+  for (int r = 0; r < kIt; ++r) {
+    const int i = tid + 256 * r;   // = a ND + c
+    if (i < N) s_dir[kT ? (i % ND) * ND + i / ND : i] = t[r];
+  }
 }
 
 // atan(a) for a in [0, 1] as a * P(a^2), P of degree 7: the odd polynomial
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
   __shared__ float s_crho[8];
   const int tid = threadIdx.x, row = tid >> 4;
   const int L = tid & 15, ell = perm16(L);
-  load_dirs<kNd * kNd>(s_dir, a.dirs, tid);
+  load_dirs<kNd, false>(s_dir, a.dirs, tid);
   if (QJL && tid < 8) s_crho[tid] = a.crho[tid];
   const uint32_t sneg = sign_byte(a.rot, ell);
   uint32_t smask[8];
@@ -320,14 +325,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B
   static_assert(sizeof(s_u.qw) == sizeof(float) * (16 * kQd + (QJL ? 16 : 1) * kD), "q and w are contiguous");
   uint32_t* const s_rec = s_u.t.rec;
   __shared__ float s_rho[8];
+  // b <= 3: by field value (the field's bits as the index), the products
+  // (rho n_x, rho n_y, rho n_z, 0) of its norm code and direction (the
+  // same table in the decode-attend kernel measured 8% slower there)
+  constexpr int kPtN = C::kNr * C::kNd * C::kNd;
+  constexpr bool kPT = kPtN <= 1024;
+  __shared__ float4 s_pt[kPT ? kPtN : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y;
-  load_dirs<C::kNd * C::kNd>(s_dir, a.dirs, tid);
+  load_dirs<C::kNd, true>(s_dir, a.dirs, tid);
   if (tid < 8) s_rho[tid] = a.crho[tid];
   // queries past the group (and, with the sketch, their R' R q) stay zero
   float* qf = &s_q[0][0];
   for (int i = tid; i < 16 * kQd + (QJL ? 16 * kD : 0); i += 256) qf[i] = 0.f;
   __syncthreads();
+  if constexpr (kPT) {   // read after the tile barriers below
+    for (int e = tid; e < kPtN; e += 256) {
+      const float4 d = s_dir[e & (C::kNd * C::kNd - 1)];
+      const float r = s_rho[e >> (2 * C::kBd)];
+      s_pt[e] = make_float4(r * d.x, r * d.y, r * d.z, 0.f);
+    }
+  }
   {
     const int row = tid >> 4, L = tid & 15, ell = perm16(L);
     const int rq = row < a.group ? row : 0;
@@ -453,11 +471,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B
       const int j = 4 * m + kk;               // triplet 43 reads zero record bits; its q is 0
       const int bit = j * C::kField, wi = bit >> 5, sh = bit & 31;
       const uint32_t f = (uint32_t)((((uint64_t)rec[wi + 1] << 32) | rec[wi]) >> sh) & ((1u << C::kField) - 1u);
-      const float4 d = s_dir[(int)(f & (C::kNd - 1)) * C::kNd + (int)((f >> C::kBd) & (C::kNd - 1))];
-      const float r = s_rho[f >> (2 * C::kBd)];
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.x, qb[3 * m], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.y, qb[3 * m + 1], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.z, qb[3 * m + 2], acc, 0, 0, 0);
+      float4 k3;   // rho n of the key's triplet
+      if constexpr (kPT) {
+        k3 = s_pt[f];
+      } else {
+        const float4 d = s_dir[f & (C::kNd * C::kNd - 1)];
+        const float r = s_rho[f >> (2 * C::kBd)];
+        k3 = make_float4(r * d.x, r * d.y, r * d.z, 0.f);
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k3.x, qb[3 * m], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k3.y, qb[3 * m + 1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k3.z, qb[3 * m + 2], acc, 0, 0, 0);
     }
     if constexpr (QJL) {
       // A[key][j] = +-sqrt(pi/2)/sqrt(d) rho16 by the key's sign bit j
@@ -562,10 +586,12 @@ int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
 //    pairs: row m of tile 3u + c is component c of triplet 16u + m, so a
 //    lane decodes triplet 16u + col of its 8 keys once for three products:
 //    at b <= 3 from an LDS table of the three f16 products rho_k n for every
-//    field value (one read per triplet), at b = 4 (a 64 KB table) from the
-//    field's direction and norm.  Rows past dim 127 (triplet 42's pad
-//    component, triplets 43..47) are never stored.  The operands' rounding
-//    (2^-11 relative) is far inside the output bar; the scores stay fp32.
+//    field value (one read per triplet); at b = 4, where that table would
+//    take 64 KB, from the field's direction and norm (f16 direction and
+//    norm tables multiplied in f16 measured 3% slower).  Rows past dim 127
+//    (triplet 42's pad component, triplets 43..47) are never stored.  The
+//    operands' rounding (2^-11 relative) is far inside the output bar; the
+//    scores stay fp32.
 //  - Each wave writes its own partial (o_rot, m in natural-log units, l);
 //    merge_kernel combines the 4 * splits partials of a head, normalises and
 //    rotates back.
@@ -597,14 +623,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void o
   const int64_t kb0 = (int64_t)split * a.split_len;
   const int64_t kb1 = a.n < kb0 + a.split_len ? a.n : kb0 + a.split_len;
   const float LOG2E = 1.4426950408889634f;
-  load_dirs<C::kNd * C::kNd>(s_dir, a.dirs, tid);
+  load_dirs<C::kNd, true>(s_dir, a.dirs, tid);
   if (tid < 8) s_rho[tid] = a.crho[tid];
   float* qf = &s_u.q[0][0];
   for (int i = tid; i < 16 * kQd; i += 256) qf[i] = 0.f;   // queries past the group stay zero
   __syncthreads();
   if constexpr (kVT) {
     for (int e = tid; e < kVtN; e += 256) {
-      const float4 d = s_dir[(e & (C::kNd - 1)) * C::kNd + ((e >> C::kBd) & (C::kNd - 1))];
+      const float4 d = s_dir[e & (C::kNd * C::kNd - 1)];
       const float r = s_rho[e >> (2 * C::kBd)];
       const _Float16 hx = (_Float16)(r * d.x), hy = (_Float16)(r * d.y), hz = (_Float16)(r * d.z);
       s_vt[e] = make_uint2((uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16),
@@ -696,7 +722,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void o
 #pragma unroll
         for (int m = 0; m < 11; ++m) {
           const uint32_t f = field_of(rk, 4 * m + kk);   // triplet 43 reads zero bits; its q is 0
-          const float4 d = s_dir[(int)(f & (C::kNd - 1)) * C::kNd + (int)((f >> C::kBd) & (C::kNd - 1))];
+          const float4 d = s_dir[f & (C::kNd * C::kNd - 1)];
           const float r = s_rho[f >> (2 * C::kBd)];
           sl[X] = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.x, qb[3 * m], sl[X], 0, 0, 0);
           sl[X] = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.y, qb[3 * m + 1], sl[X], 0, 0, 0);
@@ -772,24 +798,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void o
         }
       } else {
 #pragma unroll
-      for (int u = 0; u < 3; ++u) {
-        const int j = 16 * u + col;
-        const int jc = j < kOctoTri ? j : kOctoTri - 1;
-        f16x8 ax, ay, az;
+        for (int u = 0; u < 3; ++u) {
+          const int jc = min(16 * u + col, kOctoTri - 1);   // as above
+          uint32_t xy[8], zz[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t* rv = s_u.ch.rec[1] + (t * 32 + 8 * kk + i) * kStride;
-          const uint32_t f = field_of(rv, jc);
-          const float4 d = s_dir[(int)(f & (C::kNd - 1)) * C::kNd + (int)((f >> C::kBd) & (C::kNd - 1))];
-          const float r = j < kOctoTri ? s_rho[f >> (2 * C::kBd)] : 0.f;
-          ax[i] = (_Float16)(r * d.x);
-          ay[i] = (_Float16)(r * d.y);
-          az[i] = (_Float16)(j < kOctoTri - 1 ? r * d.z : 0.f);   // triplet 42's z is the pad
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t f = field_of(s_u.ch.rec[1] + (t * 32 + 8 * kk + i) * kStride, jc);
+            const float4 d = s_dir[f & (C::kNd * C::kNd - 1)];
+            const float r = s_rho[f >> (2 * C::kBd)];
+            const f16x2 hxy = {(_Float16)(r * d.x), (_Float16)(r * d.y)};
+            xy[i] = __builtin_bit_cast(uint32_t, hxy);
+            zz[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(r * d.z));
+          }
+          u32x4 px, py, pz;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            px[w] = __builtin_amdgcn_perm(xy[2 * w + 1], xy[2 * w], 0x05040100u);
+            py[w] = __builtin_amdgcn_perm(xy[2 * w + 1], xy[2 * w], 0x07060302u);
+            pz[w] = __builtin_amdgcn_perm(zz[2 * w + 1], zz[2 * w], 0x05040100u);
+          }
+          acc[3 * u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, px), bv, acc[3 * u], 0, 0, 0);
+          acc[3 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, py), bv, acc[3 * u + 1], 0, 0, 0);
+          acc[3 * u + 2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, pz), bv, acc[3 * u + 2], 0, 0, 0);
         }
-        acc[3 * u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bv, acc[3 * u], 0, 0, 0);
-        acc[3 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ay, bv, acc[3 * u + 1], 0, 0, 0);
-        acc[3 * u + 2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bv, acc[3 * u + 2], 0, 0, 0);
-      }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();   // s_p is rewritten by the next sub-tile
