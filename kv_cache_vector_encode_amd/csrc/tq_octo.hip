@@ -29,6 +29,19 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// bf16 bits of x rounded to nearest even (x finite)
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+// x = hi + lo + e, hi and lo bf16 (hi = bf16(x), lo = bf16(x - hi)), |e| <=
+// 2^-17 |x|: the two halves of a split operand
+__device__ __forceinline__ void bf16_split(float x, uint32_t& hi, uint32_t& lo) {
+  hi = bf16_bits(x);
+  lo = bf16_bits(x - __uint_as_float(hi << 16));
+}
 
 template <int B>
 struct Octo {
@@ -285,22 +298,26 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
 }
 
 // Logits of a head's group of 1..16 queries against n keys: out = scale *
-// gamma * sum_i rho_hat_i (R q)_i . n_hat_i, as a matrix-core product per 16-key tile,
-// C[16 keys x 16 queries] += A[16 keys x 4 dims] * B[4 dims x 16 queries]
-// over 33 steps of 4 rotated dims (132: 128 plus the zero pad), fp32 in and
-// out (v_mfma_f32_16x16x4f32).  Lane l holds A[l%16][l/16], B[l/16][l%16]
-// and C[4(l/16)+r][l%16]: the B operands (the rotated, scaled queries) stay
-// in 33 registers for the whole kernel; each A element is one decoded
-// coordinate rho_hat * n_hat[comp] of key l%16, unpacked from the tile's
-// records in LDS.  Each wave takes 16-key tiles in turn.
+// gamma * sum_i rho_hat_i (R q)_i . n_hat_i, as a matrix-core product per
+// 16-key tile, C[16 keys x 16 queries] += A[16 keys x K] * B[K x 16 queries]
+// over the 132 rotated dims (128 plus the zero pad) in an order of the
+// kernel's choosing.  Each A element is one decoded coordinate rho_hat *
+// n_hat[comp] of key l%16, unpacked from the tile's records in LDS; the B
+// operands (the rotated, scaled queries) stay in registers for the whole
+// kernel; C[4(l/16)+r][l%16] sits in lane l.  Each wave takes 16-key tiles
+// in turn.
+//  - b = 4: 33 steps of 4 dims on v_mfma_f32_16x16x4f32, fp32 in and out.
+//  - b <= 3: 5 steps of 32 dims on v_mfma_f32_16x16x32_bf16, each operand
+//    split into bf16 high and low halves (three products per step), the
+//    key's halves read from a table of every field value's products: 15
+//    instructions of 16 cycles per tile instead of 33 of 32.
 constexpr int kOctoMfmaTile = 128;   // keys per tile step (2 tiles of 16 per wave)
 
-// 5 waves per SIMD at b = 2 (the kernel held to 96 VGPRs); at b = 3, 4
-// that limit spills (b = 3: 235 against 226 us at 4 waves on the 4.2M keys
-// of llama70b), so they keep 4; the QJL variant's 32 more query registers
-// leave room for 3
+// Waves per SIMD: 4 at b = 2 and 4; 3 at b = 3 (the bf16 operands take 134
+// VGPRs: 154 against 166 us at 4 waves with 3 spills, on the 4.2M keys of
+// llama70b) and with the sketch (its 32 more query registers)
 template <int B, bool QJL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B == 2 ? 5 : 4))) void octo_logits_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL || B == 3 ? 3 : 4))) void octo_logits_mfma_kernel(
     const OctoArgs a) {
   using C = Octo<B>;
   constexpr int kStride = C::kWords + 1;
@@ -326,11 +343,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B
   uint32_t* const s_rec = s_u.t.rec;
   __shared__ float s_rho[8];
   // b <= 3: by field value (the field's bits as the index), the products
-  // (rho n_x, rho n_y, rho n_z, 0) of its norm code and direction (the
-  // same table in the decode-attend kernel measured 8% slower there)
+  // (x, y, z) = rho n of its norm code and direction, split into bf16
+  // halves: (x, y), (y, z) of the high parts, then of the low parts
   constexpr int kPtN = C::kNr * C::kNd * C::kNd;
   constexpr bool kPT = kPtN <= 1024;
-  __shared__ float4 s_pt[kPT ? kPtN : 1];
+  __shared__ uint4 s_pt[kPT ? kPtN : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y;
   load_dirs<C::kNd, true>(s_dir, a.dirs, tid);
@@ -343,7 +360,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B
     for (int e = tid; e < kPtN; e += 256) {
       const float4 d = s_dir[e & (C::kNd * C::kNd - 1)];
       const float r = s_rho[e >> (2 * C::kBd)];
-      s_pt[e] = make_float4(r * d.x, r * d.y, r * d.z, 0.f);
+      uint32_t xh, xl, yh, yl, zh, zl;
+      bf16_split(r * d.x, xh, xl);
+      bf16_split(r * d.y, yh, yl);
+      bf16_split(r * d.z, zh, zl);
+      s_pt[e] = make_uint4(xh | (yh << 16), yh | (zh << 16), xl | (yl << 16), yl | (zl << 16));
     }
   }
   {
@@ -382,14 +403,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B
   // ..., kk+40, one per 3 consecutive steps (components x, y, z), so each
   // lane decodes a triplet once and feeds it to 3 products.
   const int col = lane & 15, kk = lane >> 4;
-  float qb[33];
+  // fp32 operands (b = 4): step 3m + c takes component c of triplet 4m + kk
+  float qb[kPT ? 1 : 33];
+  // bf16 operands (b <= 3): K slot 8s + e of step s (e < 8) is component
+  // c % 3 of triplet 4 (c / 3) + kk, c = 8s + e < 33 (zero past 32); the
+  // queries split into bf16 high and low halves, the products
+  // hi.hi + hi.lo + lo.hi lose |q_lo k_lo| and the halves' rounding, about
+  // 2^-15 |q_i k_i| a term
+  u32x4 qh[kPT ? 5 : 1], ql[kPT ? 5 : 1];
+  if constexpr (kPT) {
 #pragma unroll
-  for (int m = 0; m < 11; ++m)
+    for (int st = 0; st < 5; ++st)
 #pragma unroll
-    for (int c = 0; c < 3; ++c) {
-      const int dim = 3 * (4 * m + kk) + c;
-      qb[3 * m + c] = dim < kD ? s_q[col][dim] : 0.f;
-    }
+      for (int w = 0; w < 4; ++w) {
+        uint32_t h[2], l[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int c = 8 * st + 2 * w + hf, dim = 3 * (4 * (c / 3) + kk) + c % 3;
+          bf16_split(c < 33 && dim < kD ? s_q[col][dim] : 0.f, h[hf], l[hf]);
+        }
+        qh[st][w] = h[0] | (h[1] << 16);
+        ql[st][w] = l[0] | (l[1] << 16);
+      }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 11; ++m)
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        const int dim = 3 * (4 * m + kk) + c;
+        qb[3 * m + c] = dim < kD ? s_q[col][dim] : 0.f;
+      }
+  }
   // OCTOPUS-QJL: 32 more steps of 4 sketch coordinates, lane kk taking
   // coordinate 4 s + kk of step s
   float qw[QJL ? 32 : 1];
@@ -466,22 +510,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 3 : B
   for (int t = wave; t * 16 < nk; t += 4) {
     const uint32_t* rec = s_rec + (t * 16 + col) * kStride;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < 11; ++m) {
+    auto field = [&](int m) -> uint32_t {
       const int j = 4 * m + kk;               // triplet 43 reads zero record bits; its q is 0
       const int bit = j * C::kField, wi = bit >> 5, sh = bit & 31;
-      const uint32_t f = (uint32_t)((((uint64_t)rec[wi + 1] << 32) | rec[wi]) >> sh) & ((1u << C::kField) - 1u);
-      float4 k3;   // rho n of the key's triplet
-      if constexpr (kPT) {
-        k3 = s_pt[f];
-      } else {
+      return (uint32_t)((((uint64_t)rec[wi + 1] << 32) | rec[wi]) >> sh) & ((1u << C::kField) - 1u);
+    };
+    if constexpr (kPT) {
+      // A in the slot order of qh/ql: per pair of triplets m, m+1 the words
+      // (x_m, y_m), (z_m, x_m+1), (y_m+1, z_m+1), from the table's (x, y)
+      // and (y, z) words and one byte permute; triplet 10 ends the list
+      uint4 e[11];
+      uint32_t ah[20], al[20];
+      auto word = [&](int w) {   // the words of slots 2w, 2w + 1, high and low parts
+        const int p = w / 3, r = w % 3;
+        if (w >= 17) {
+          ah[w] = al[w] = 0u;
+        } else if (w >= 15) {    // triplet 10: (x, y), (z, 0)
+          ah[w] = w == 15 ? e[10].x : e[10].y >> 16;
+          al[w] = w == 15 ? e[10].z : e[10].w >> 16;
+        } else if (r == 0) {
+          ah[w] = e[2 * p].x;
+          al[w] = e[2 * p].z;
+        } else if (r == 1) {
+          ah[w] = __builtin_amdgcn_perm(e[2 * p + 1].x, e[2 * p].y, 0x05040302u);
+          al[w] = __builtin_amdgcn_perm(e[2 * p + 1].z, e[2 * p].w, 0x05040302u);
+        } else {
+          ah[w] = e[2 * p + 1].y;
+          al[w] = e[2 * p + 1].w;
+        }
+      };
+      // step st reads triplets up to (8 st + 7) / 3 (and 10 at st = 3), so
+      // the table reads are issued one step ahead and few are live at once
+      constexpr int kLast[5] = {2, 5, 7, 10, 10};
+#pragma unroll
+      for (int m = 0; m <= kLast[0]; ++m) e[m] = s_pt[field(m)];
+#pragma unroll
+      for (int st = 0; st < 5; ++st) {
+        if (st + 1 < 5) {
+#pragma unroll
+          for (int m = kLast[st] + 1; m <= kLast[st + 1]; ++m) e[m] = s_pt[field(m)];
+        }
+#pragma unroll
+        for (int w = 4 * st; w < 4 * st + 4; ++w) word(w);
+        const u32x4 h = {ah[4 * st], ah[4 * st + 1], ah[4 * st + 2], ah[4 * st + 3]};
+        const u32x4 l = {al[4 * st], al[4 * st + 1], al[4 * st + 2], al[4 * st + 3]};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h), __builtin_bit_cast(bf16x8, qh[st]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h), __builtin_bit_cast(bf16x8, ql[st]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l), __builtin_bit_cast(bf16x8, qh[st]), acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 11; ++m) {
+        const uint32_t f = field(m);
         const float4 d = s_dir[f & (C::kNd * C::kNd - 1)];
         const float r = s_rho[f >> (2 * C::kBd)];
-        k3 = make_float4(r * d.x, r * d.y, r * d.z, 0.f);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.x, qb[3 * m], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.y, qb[3 * m + 1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.z, qb[3 * m + 2], acc, 0, 0, 0);
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k3.x, qb[3 * m], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k3.y, qb[3 * m + 1], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k3.z, qb[3 * m + 2], acc, 0, 0, 0);
     }
     if constexpr (QJL) {
       // A[key][j] = +-sqrt(pi/2)/sqrt(d) rho16 by the key's sign bit j
@@ -553,12 +640,12 @@ int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.n <= 0 || a.heads < 1 || a.heads > 65535 || a.group < 1 || a.group > kOctoMaxGroup)
     return (int)hipErrorInvalidValue;
-  // about as many workgroups as are resident at once (waves per SIMD: 5 at
-  // b = 2, 4 at b = 3, 4, 3 with the sketch; one workgroup's wave on each
+  // about as many workgroups as are resident at once (waves per SIMD: 4 at
+  // b = 2, 4, 3 at b = 3 and with the sketch; one workgroup's wave on each
   // SIMD), spread over
   // the heads, each looping over tiles of its head (the table and the
   // queries are set up once per workgroup)
-  const int64_t wgs = 256 * (a.qjl_signs ? 3 : bits == 2 ? 5 : 4);
+  const int64_t wgs = 256 * (a.qjl_signs || bits == 3 ? 3 : 4);
   const int64_t tiles = std::min((a.n + kOctoMfmaTile - 1) / kOctoMfmaTile, std::max<int64_t>(1, wgs / a.heads));
   const dim3 grid((unsigned)tiles, (unsigned)a.heads);
   switch (bits) {

@@ -819,7 +819,9 @@ def test_octo_logits_match_oracle(device, bits, group):
     want = scale * np.einsum("hgd,hnd->hgn", qf, xh)
     csn = scale * np.linalg.norm(qf, axis=-1)[:, :, None] * np.linalg.norm(xh, axis=-1)[:, None, :]
     got = out.cpu().numpy().astype(np.float64)
-    assert np.all(np.abs(got - want) <= LOGIT_RTOL * csn + 1e-30), float(np.max(np.abs(got - want) / (csn + 1e-30)))
+    worst = float(np.max(np.abs(got - want) / (csn + 1e-30)))
+    print(f"  worst logit error {worst:.2e} of |q| |k_hat| scale (bar {LOGIT_RTOL:.0e})")
+    assert np.all(np.abs(got - want) <= LOGIT_RTOL * csn + 1e-30), worst
 
 
 def test_octo_small_and_degenerate_sizes(device):
