@@ -1162,7 +1162,7 @@ int64_t tq_octo_attend_workspace_bytes(int32_t heads, int32_t group, int64_t n) 
   int64_t split_len;
   int32_t nsplit;
   octo_attend_split(heads, n, split_len, nsplit);
-  return (int64_t)heads * 4 * nsplit * group * tq::kPartStride * (int64_t)sizeof(float);
+  return (int64_t)heads * nsplit * group * tq::kPartStride * (int64_t)sizeof(float);
 }
 
 int tq_octo_attend(const float* q, const void* k_codes, const void* k_gamma, const void* v_codes,
@@ -1200,7 +1200,7 @@ int tq_octo_attend(const float* q, const void* k_codes, const void* k_gamma, con
   octo_attend_split(heads, n, a.split_len, a.num_splits);
   int err = tq::launch_octo_attend(a, bits, hip_stream);
   if (err != 0) return hip_fail(err, "triplet attend launch");
-  // the main decode's merge: num_kv_heads = heads, 4 partials per split
+  // the main decode's merge: num_kv_heads = heads, one partial per split
   tq::DecodeArgs m;
   std::memset(&m, 0, sizeof(m));
   m.out = out;
@@ -1209,7 +1209,7 @@ int tq_octo_attend(const float* q, const void* k_codes, const void* k_gamma, con
   m.num_kv_heads = heads;
   m.num_q_heads = heads * group;
   m.group = group;
-  m.num_splits = 4 * a.num_splits;
+  m.num_splits = a.num_splits;
   m.rot = a.rot;
   err = tq::launch_merge(m, hip_stream);
   if (err != 0) return hip_fail(err, "merge launch");

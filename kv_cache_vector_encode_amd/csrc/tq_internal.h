@@ -203,7 +203,7 @@ struct OctoArgs {
   // decode-attend over triplet-coded keys (codes, gamma) and values
   const uint8_t* vcodes;    // [heads][n][rec_bytes]
   const uint16_t* vgamma;   // [heads][n] fp16
-  float* partials;          // [heads][4 * splits][group][kPartStride]
+  float* partials;          // [heads][splits][group][kPartStride]
   int64_t split_len;        // keys per split, a multiple of kOctoAttChunk
   int32_t num_splits;
 };

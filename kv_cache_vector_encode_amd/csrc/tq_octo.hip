@@ -679,9 +679,9 @@ int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
 //    (triplet 42's pad component, triplets 43..47) are never stored.  The
 //    operands' rounding (2^-11 relative) is far inside the output bar; the
 //    scores stay fp32.
-//  - Each wave writes its own partial (o_rot, m in natural-log units, l);
-//    merge_kernel combines the 4 * splits partials of a head, normalises and
-//    rotates back.
+//  - The 4 waves' (o_rot, m, l) are merged in LDS in a fixed order, and the
+//    split writes one partial (m in natural-log units); merge_kernel
+//    combines a head's splits, normalises and rotates back.
 // Held to 3 waves per SIMD (168 VGPRs, one spilled): left to itself the
 // compiler takes 204 and 2 waves, 1014 against 576 us on llama70b's keys
 template <int B>
@@ -700,6 +700,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void o
   } s_u;
   __shared__ float s_rho[8];
   __shared__ float s_p[4][16][36];      // per wave: p * gamma_v, [query][key of the 32-key sub-tile]
+  __shared__ float s_wml[4][2][16];     // per wave: m (log2 units), l of each query, for the final merge
   // b <= 3: by field value (the field's bits as the index), the f16 values
   // rho n_x, rho n_y (low, high half of .x), rho n_z (low half of .y)
   constexpr int kVtN = C::kNr * C::kNd * C::kNd;
@@ -914,23 +915,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void o
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
-  // ---- this wave's partial: rows 4kk + r of tile 3u + c are component c of
-  // triplet 16u + 4kk + r, i.e. dim 3 (16u + 4kk + r) + c
+  // ---- the split's partial: the 4 waves' (m, l, o_rot) merged in LDS in a
+  // fixed order (w0 + w1 + w2 + w3, deterministic), written by wave 3.
+  // Rows 4kk + r of tile 3u + c are component c of triplet 16u + 4kk + r,
+  // i.e. dim 3 (16u + 4kk + r) + c.
   run_l = sum_rows(run_l);
-  if (col < a.group) {
-    float* pp = a.partials + (((int64_t)head * (4 * a.num_splits) + 4 * split + wave) * a.group + col) * kPartStride;
+  __syncthreads();   // every wave is done with the chunk buffers
+  if (kk == 0) {
+    s_wml[wave][0][col] = run_m;
+    s_wml[wave][1][col] = run_l;
+  }
+  __syncthreads();
+  float M = s_wml[0][0][col], L = 0.f;
+#pragma unroll
+  for (int w = 1; w < 4; ++w) M = fmaxf(M, s_wml[w][0][col]);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = s_wml[w][0][col];
+    L += (mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M)) * s_wml[w][1][col];
+  }
+  const float alpha = run_m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(run_m - M);   // M >= run_m
+  float* const buf = reinterpret_cast<float*>(&s_u);   // [query][145]: rows T * 16 + 4kk + r
+  static_assert(sizeof(s_u) >= 16 * 145 * sizeof(float), "merge buffer");
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int T = 0; T < 9; ++T)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float& b = buf[col * 145 + T * 16 + 4 * kk + r];
+          b = (w == 0 ? 0.f : b) + alpha * acc[T][r];
+        }
+    }
+    __syncthreads();
+  }
+  if (wave == 3 && col < a.group) {
+    float* pp = a.partials + (((int64_t)head * a.num_splits + split) * a.group + col) * kPartStride;
 #pragma unroll
     for (int u = 0; u < 3; ++u)
 #pragma unroll
       for (int c = 0; c < 3; ++c)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int dim = 3 * (16 * u + 4 * kk + r) + c;
-          if (dim < kD) pp[dim] = acc[3 * u + c][r];
+          const int T = 3 * u + c, dim = 3 * (16 * u + 4 * kk + r) + c;
+          if (dim < kD) pp[dim] = buf[col * 145 + T * 16 + 4 * kk + r] + alpha * acc[T][r];
         }
     if (kk == 0) {
-      pp[128] = run_m * (1.f / LOG2E);   // natural-log units for the merge
-      pp[129] = run_l;
+      pp[128] = M * (1.f / LOG2E);   // natural-log units for the merge
+      pp[129] = L;
     }
   }
 }

@@ -1117,5 +1117,5 @@ def test_octo_attend_small_and_empty(device):
 
 def test_octo_attend_multi_chunk_splits(device):
     # 150,000 keys of one head: 256-key splits of two staged chunks each
-    assert tq.tq_octo_attend_workspace_bytes(1, 8, 150000) == 4 * 586 * 8 * 132 * 4
+    assert tq.tq_octo_attend_workspace_bytes(1, 8, 150000) == 586 * 8 * 132 * 4
     _octo_attend_case(device, 4, 1, 8, 150000)

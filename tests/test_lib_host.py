@@ -348,8 +348,8 @@ def test_octo_attend_argument_checks_happen_before_the_device():
     r = tq.tq_make_rotation(42, 128)
     q, kc, kg, vc, vg, tb, out, ws = (0x200000 + 0x100000 * i for i in range(8))
     need = L.tq_octo_attend_workspace_bytes(8, 8, 100)
-    # 100 keys of 8 heads: one 128-key split per head, 4 wave partials of 8 queries
-    assert need == 8 * 4 * 1 * 8 * 132 * 4
+    # 100 keys of 8 heads: one 128-key split per head, one partial of 8 queries
+    assert need == 8 * 1 * 8 * 132 * 4
     assert L.tq_octo_attend_workspace_bytes(0, 8, 100) == tq.TQ_ERR_INVALID_ARG
     assert L.tq_octo_attend_workspace_bytes(8, 17, 100) == tq.TQ_ERR_INVALID_ARG
     at = L.tq_octo_attend
@@ -362,8 +362,8 @@ def test_octo_attend_argument_checks_happen_before_the_device():
     # splits stay whole 128-key chunks and at most 1024 per head
     for heads, n in ((1, 1), (8, 32768), (1, 1 << 24), (64, 131072)):
         b = L.tq_octo_attend_workspace_bytes(heads, 1, n)
-        nsplit = b // (heads * 4 * 132 * 4)
-        assert 1 <= nsplit <= 1024 and nsplit * heads * 4 * 132 * 4 == b
+        nsplit = b // (heads * 132 * 4)
+        assert 1 <= nsplit <= 1024 and nsplit * heads * 132 * 4 == b
 
 
 def test_noalloc_decode_checks_happen_before_the_device():
