@@ -306,18 +306,21 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
 // operands (the rotated, scaled queries) stay in registers for the whole
 // kernel; C[4(l/16)+r][l%16] sits in lane l.  Each wave takes 16-key tiles
 // in turn.
-//  - b = 4: 33 steps of 4 dims on v_mfma_f32_16x16x4f32, fp32 in and out.
-//  - b <= 3: 5 steps of 32 dims on v_mfma_f32_16x16x32_bf16, each operand
-//    split into bf16 high and low halves (three products per step), the
-//    key's halves read from a table of every field value's products: 15
-//    instructions of 16 cycles per tile instead of 33 of 32.
+//  - 5 steps of 32 dims on v_mfma_f32_16x16x32_bf16, each operand split
+//    into bf16 high and low halves (three products per step): 15
+//    instructions of 16 cycles per tile instead of 33 fp32 ones of 32.  At
+//    b <= 3 the key's halves are read from a table of every field value's
+//    products; at b = 4 (a 128 KB table) they are formed in registers.
+//  - With the sketch at b = 4: 33 steps of 4 dims on
+//    v_mfma_f32_16x16x4f32, fp32 in and out.
 constexpr int kOctoMfmaTile = 128;   // keys per tile step (2 tiles of 16 per wave)
 
-// Waves per SIMD: 4 at b = 2 and 4; 3 at b = 3 (the bf16 operands take 134
+// Waves per SIMD: 4 at b = 2; 3 at b = 3 (the bf16 operands take 134
 // VGPRs: 154 against 166 us at 4 waves with 3 spills, on the 4.2M keys of
-// llama70b) and with the sketch (its 32 more query registers)
+// llama70b), at b = 4 (the split in registers takes 168) and with the
+// sketch (its 32 more query registers)
 template <int B, bool QJL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL || B == 3 ? 3 : 4))) void octo_logits_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL || B >= 3 ? 3 : 4))) void octo_logits_mfma_kernel(
     const OctoArgs a) {
   using C = Octo<B>;
   constexpr int kStride = C::kWords + 1;
@@ -403,15 +406,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL || B ==
   // ..., kk+40, one per 3 consecutive steps (components x, y, z), so each
   // lane decodes a triplet once and feeds it to 3 products.
   const int col = lane & 15, kk = lane >> 4;
-  // fp32 operands (b = 4): step 3m + c takes component c of triplet 4m + kk
-  float qb[kPT ? 1 : 33];
-  // bf16 operands (b <= 3): K slot 8s + e of step s (e < 8) is component
+  // bf16-split operands everywhere but with the sketch at b = 4 (the
+  // sketch's 32 query registers beside them spilled there: 45 against 42 us
+  // on decode_1x32768); that case keeps fp32 operands, step 3m + c taking
+  // component c of triplet 4m + kk
+  constexpr bool kSplit = kPT || !QJL;
+  float qb[kSplit ? 1 : 33];
+  // bf16 operands: K slot 8s + e of step s (e < 8) is component
   // c % 3 of triplet 4 (c / 3) + kk, c = 8s + e < 33 (zero past 32); the
   // queries split into bf16 high and low halves, the products
   // hi.hi + hi.lo + lo.hi lose |q_lo k_lo| and the halves' rounding, about
   // 2^-15 |q_i k_i| a term
-  u32x4 qh[kPT ? 5 : 1], ql[kPT ? 5 : 1];
-  if constexpr (kPT) {
+  u32x4 qh[kSplit ? 5 : 1], ql[kSplit ? 5 : 1];
+  if constexpr (kSplit) {
 #pragma unroll
     for (int st = 0; st < 5; ++st)
 #pragma unroll
@@ -559,6 +566,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL || B ==
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l), __builtin_bit_cast(bf16x8, qh[st]), acc, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+    } else if constexpr (kSplit) {
+      // b = 4: the key's products formed in registers and split there (hi
+      // the value truncated to bf16, lo = bf16(x - hi), |lo| <= 2^-8 |x|),
+      // slot c = component c % 3 of triplet c / 3, zero past 32
+      float v[40];
+#pragma unroll
+      for (int c = 33; c < 40; ++c) v[c] = 0.f;
+      auto trip = [&](int m) {
+        const uint32_t f = field(m);
+        const float4 d = s_dir[f & (C::kNd * C::kNd - 1)];
+        const float r = s_rho[f >> (2 * C::kBd)];
+        v[3 * m] = r * d.x;
+        v[3 * m + 1] = r * d.y;
+        v[3 * m + 2] = r * d.z;
+      };
+      constexpr int kLast[5] = {2, 5, 7, 10, 10};
+#pragma unroll
+      for (int m = 0; m <= kLast[0]; ++m) trip(m);
+#pragma unroll
+      for (int st = 0; st < 5; ++st) {
+        if (st + 1 < 5) {
+#pragma unroll
+          for (int m = kLast[st] + 1; m <= kLast[st + 1]; ++m) trip(m);
+        }
+        u32x4 h, l;
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          const float x0 = v[8 * st + 2 * w4], x1 = v[8 * st + 2 * w4 + 1];
+          const uint32_t b0 = __float_as_uint(x0), b1 = __float_as_uint(x1);
+          h[w4] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          const bf16x2 lo = {(__bf16)(x0 - __uint_as_float(b0 & 0xFFFF0000u)), (__bf16)(x1 - __uint_as_float(b1 & 0xFFFF0000u))};
+          l[w4] = __builtin_bit_cast(uint32_t, lo);
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h), __builtin_bit_cast(bf16x8, qh[st]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h), __builtin_bit_cast(bf16x8, ql[st]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l), __builtin_bit_cast(bf16x8, qh[st]), acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     } else {
 #pragma unroll
       for (int m = 0; m < 11; ++m) {
@@ -641,11 +687,11 @@ int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
   if (a.n <= 0 || a.heads < 1 || a.heads > 65535 || a.group < 1 || a.group > kOctoMaxGroup)
     return (int)hipErrorInvalidValue;
   // about as many workgroups as are resident at once (waves per SIMD: 4 at
-  // b = 2, 4, 3 at b = 3 and with the sketch; one workgroup's wave on each
+  // b = 2, 3 at b = 3, 4 and with the sketch; one workgroup's wave on each
   // SIMD), spread over
   // the heads, each looping over tiles of its head (the table and the
   // queries are set up once per workgroup)
-  const int64_t wgs = 256 * (a.qjl_signs || bits == 3 ? 3 : 4);
+  const int64_t wgs = 256 * (a.qjl_signs || bits >= 3 ? 3 : 4);
   const int64_t tiles = std::min((a.n + kOctoMfmaTile - 1) / kOctoMfmaTile, std::max<int64_t>(1, wgs / a.heads));
   const dim3 grid((unsigned)tiles, (unsigned)a.heads);
   switch (bits) {
