@@ -1144,12 +1144,13 @@ int tq_octo_logits_qjl(const float* q, const void* codes, const void* gamma, con
 }
 
 namespace {
-// Splits of a triplet decode-attend: about three workgroups per CU in all
-// (the kernel's registers allow three waves per SIMD), each split a
-// multiple of the 128 keys a workgroup stages at a time; at most 1024.
+// Splits of a triplet decode-attend: about two workgroups per CU in all
+// (the kernel's registers allow two waves per SIMD; 768 splits, one and a
+// half rounds, measured 20-30% slower), each split a multiple of the 128
+// keys a workgroup stages at a time; at most 1024.
 void octo_attend_split(int32_t heads, int64_t n, int64_t& split_len, int32_t& nsplit) {
   const int64_t ch = tq::kOctoAttChunk;
-  const int64_t want = std::max<int64_t>(1, (n * heads + 767) / 768);
+  const int64_t want = std::max<int64_t>(1, (n * heads + 511) / 512);
   split_len = std::max<int64_t>(ch, (want + ch - 1) / ch * ch);
   if ((n + split_len - 1) / split_len > 1024) split_len = ((n + 1023) / 1024 + ch - 1) / ch * ch;
   nsplit = (int32_t)std::max<int64_t>(1, (n + split_len - 1) / split_len);

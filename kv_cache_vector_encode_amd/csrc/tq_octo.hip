@@ -711,8 +711,9 @@ int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
 // 128 keys at a time (records and norms of keys and values), each wave
 // taking a 32-key sub-tile of the chunk and keeping its own online softmax,
 // in log2 units (scale * log2(e) folded into the queries), and accumulators.
-//  - Scores: the logits kernel's fp32 product, C[16 keys x 16 queries] over
-//    33 steps of 4 rotated dims, twice, times gamma_k.
+//  - Scores: the logits kernel's product at b = 4, C[16 keys x 16 queries]
+//    over 5 steps of 32 rotated dims on bf16-split operands (three bf16
+//    products per step, about 2^-15 relative a term), twice, times gamma_k.
 //  - Values: C[16 rows x 16 queries] += A[16 rows x 32 keys] * B[32 keys x 16
 //    queries] on 16-bit operands with fp32 accumulation, B = f16(p gamma_v)
 //    through LDS.  The 144 rows of the 9 row tiles are (triplet, component)
@@ -723,15 +724,16 @@ int launch_octo_logits(const OctoArgs& a, int bits, void* stream) {
 //    take 64 KB, from the field's direction and norm (f16 direction and
 //    norm tables multiplied in f16 measured 3% slower).  Rows past dim 127
 //    (triplet 42's pad component, triplets 43..47) are never stored.  The
-//    operands' rounding (2^-11 relative) is far inside the output bar; the
-//    scores stay fp32.
+//    operands' rounding (2^-11 relative) is far inside the output bar.
 //  - The 4 waves' (o_rot, m, l) are merged in LDS in a fixed order, and the
 //    split writes one partial (m in natural-log units); merge_kernel
 //    combines a head's splits, normalises and rotates back.
-// Held to 3 waves per SIMD (168 VGPRs, one spilled): left to itself the
-// compiler takes 204 and 2 waves, 1014 against 576 us on llama70b's keys
+// 2 waves per SIMD (190-206 VGPRs) and about two workgroups per CU in all:
+// at 3 waves the split scores spilled 80 registers; against the fp32 scores
+// at 3 waves, 40 against 44 us on decode_1x32768, 307 against 311 us on
+// llama70b
 template <int B>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void octo_attend_kernel(const OctoArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void octo_attend_kernel(const OctoArgs a) {
   using C = Octo<B>;
   constexpr int kStride = C::kWords + 1;
   constexpr int kQd = 132;
@@ -790,13 +792,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void o
   }
   __syncthreads();
   const int col = lane & 15, kk = lane >> 4;
-  float qb[33];
+  // bf16-split query operands: K slot 8s + e of step s is component c % 3
+  // of triplet 4 (c / 3) + kk, c = 8s + e < 33 (zero past 32)
+  u32x4 qh[5], ql[5];
 #pragma unroll
-  for (int m = 0; m < 11; ++m)
+  for (int st = 0; st < 5; ++st)
 #pragma unroll
-    for (int c = 0; c < 3; ++c) {
-      const int dim = 3 * (4 * m + kk) + c;
-      qb[3 * m + c] = dim < kD ? s_u.q[col][dim] : 0.f;
+    for (int w = 0; w < 4; ++w) {
+      uint32_t h[2], l[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int c = 8 * st + 2 * w + hf, dim = 3 * (4 * (c / 3) + kk) + c % 3;
+        bf16_split(c < 33 && dim < kD ? s_u.q[col][dim] : 0.f, h[hf], l[hf]);
+      }
+      qh[st][w] = h[0] | (h[1] << 16);
+      ql[st][w] = l[0] | (l[1] << 16);
     }
   float run_m = -INFINITY, run_l = 0.f;
   f32x4 acc[9];
@@ -853,14 +863,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void o
       for (int X = 0; X < 2; ++X) {
         const uint32_t* rk = s_u.ch.rec[0] + (t * 32 + 16 * X + col) * kStride;
         sl[X] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        float v[40];   // slot c: component c % 3 of triplet c / 3, zero past 32
 #pragma unroll
-        for (int m = 0; m < 11; ++m) {
+        for (int c = 33; c < 40; ++c) v[c] = 0.f;
+        auto trip = [&](int m) {
           const uint32_t f = field_of(rk, 4 * m + kk);   // triplet 43 reads zero bits; its q is 0
           const float4 d = s_dir[f & (C::kNd * C::kNd - 1)];
           const float r = s_rho[f >> (2 * C::kBd)];
-          sl[X] = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.x, qb[3 * m], sl[X], 0, 0, 0);
-          sl[X] = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.y, qb[3 * m + 1], sl[X], 0, 0, 0);
-          sl[X] = __builtin_amdgcn_mfma_f32_16x16x4f32(r * d.z, qb[3 * m + 2], sl[X], 0, 0, 0);
+          v[3 * m] = r * d.x;
+          v[3 * m + 1] = r * d.y;
+          v[3 * m + 2] = r * d.z;
+        };
+        constexpr int kLast[5] = {2, 5, 7, 10, 10};
+#pragma unroll
+        for (int m = 0; m <= kLast[0]; ++m) trip(m);
+#pragma unroll
+        for (int st = 0; st < 5; ++st) {
+          if (st + 1 < 5) {
+#pragma unroll
+            for (int m = kLast[st] + 1; m <= kLast[st + 1]; ++m) trip(m);
+          }
+          u32x4 h, l;
+#pragma unroll
+          for (int w4 = 0; w4 < 4; ++w4) {
+            const float x0 = v[8 * st + 2 * w4], x1 = v[8 * st + 2 * w4 + 1];
+            const uint32_t b0 = __float_as_uint(x0), b1 = __float_as_uint(x1);
+            h[w4] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 lo = {(__bf16)(x0 - __uint_as_float(b0 & 0xFFFF0000u)), (__bf16)(x1 - __uint_as_float(b1 & 0xFFFF0000u))};
+            l[w4] = __builtin_bit_cast(uint32_t, lo);
+          }
+          sl[X] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h), __builtin_bit_cast(bf16x8, qh[st]), sl[X], 0, 0, 0);
+          sl[X] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h), __builtin_bit_cast(bf16x8, ql[st]), sl[X], 0, 0, 0);
+          sl[X] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l), __builtin_bit_cast(bf16x8, qh[st]), sl[X], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       float sc[8];

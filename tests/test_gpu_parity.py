@@ -1116,6 +1116,7 @@ def test_octo_attend_small_and_empty(device):
 
 
 def test_octo_attend_multi_chunk_splits(device):
-    # 150,000 keys of one head: 256-key splits of two staged chunks each
-    assert tq.tq_octo_attend_workspace_bytes(1, 8, 150000) == 586 * 8 * 132 * 4
+    # 150,000 keys of one head: 391 splits of 384 keys, three staged chunks
+    # each (the last split 240 keys: a whole chunk and a short one)
+    assert tq.tq_octo_attend_workspace_bytes(1, 8, 150000) == 391 * 8 * 132 * 4
     _octo_attend_case(device, 4, 1, 8, 150000)
