@@ -313,6 +313,8 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
 //    products; at b = 4 (a 128 KB table) they are formed in registers.
 //  - With the sketch at b = 4: 33 steps of 4 dims on
 //    v_mfma_f32_16x16x4f32, fp32 in and out.
+//  - The sketch (OCTOPUS-QJL) adds 4 steps of 32 coordinates on bf16-split
+//    operands to the same accumulator.
 constexpr int kOctoMfmaTile = 128;   // keys per tile step (2 tiles of 16 per wave)
 
 // Waves per SIMD: 4 at b = 2; 3 at b = 3 (the bf16 operands take 134
@@ -441,12 +443,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL || B >=
         qb[3 * m + c] = dim < kD ? s_q[col][dim] : 0.f;
       }
   }
-  // OCTOPUS-QJL: 32 more steps of 4 sketch coordinates, lane kk taking
-  // coordinate 4 s + kk of step s
-  float qw[QJL ? 32 : 1];
+  // OCTOPUS-QJL: 4 more steps of 32 sketch coordinates on bf16-split
+  // operands; word w of lane kk in step s holds coordinates j = 32 s + 4 kk
+  // + w and j + 16, whose sign bits sit at bits 4 kk + w and 4 kk + w + 16
+  // of word s of the key's sign record
+  u32x4 wh[QJL ? 4 : 1], wl[QJL ? 4 : 1];
   if constexpr (QJL) {
 #pragma unroll
-    for (int st = 0; st < 32; ++st) qw[st] = s_w[col][4 * st + kk];
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t h0, l0, h1, l1;
+        bf16_split(s_w[col][32 * st + 4 * kk + w], h0, l0);
+        bf16_split(s_w[col][32 * st + 4 * kk + w + 16], h1, l1);
+        wh[st][w] = h0 | (h1 << 16);
+        wl[st][w] = l0 | (l1 << 16);
+      }
   }
   // the workgroup walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... of
   // its head, so the table and the queries are set up once per workgroup;
@@ -622,12 +634,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL || B >=
       // sqrt(pi/2)/sqrt(d) rho16 sum_j sgn_j (R' R q)_j to the logit
       const uint4 sg = s_u.t.sg[t * 16 + col];
       const float sk = s_u.t.sk[t * 16 + col];   // zero past the last key
-      const uint32_t sgs[4] = {sg.x >> kk, sg.y >> kk, sg.z >> kk, sg.w >> kk};
-      const uint32_t skb = __float_as_uint(sk);
+      uint32_t skh, skl;
+      bf16_split(sk, skh, skl);
+      const uint32_t bh = skh * 0x10001u, bl = skl * 0x10001u;   // both halves
+      const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
 #pragma unroll
-      for (int st = 0; st < 32; ++st) {
-        const uint32_t neg = ((sgs[st >> 3] >> (4 * (st & 7))) & 1u) << 31;
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(skb ^ neg), qw[st], acc, 0, 0, 0);
+      for (int st = 0; st < 4; ++st) {
+        u32x4 h, l;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // sign bits 4kk + w and 4kk + w + 16 moved to 15 and 31 (negating
+          // both halves of a split value negates it exactly)
+          const uint32_t neg = (sw[st] << (15 - 4 * kk - w)) & 0x80008000u;
+          h[w] = bh ^ neg;
+          l[w] = bl ^ neg;
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h), __builtin_bit_cast(bf16x8, wh[st]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h), __builtin_bit_cast(bf16x8, wl[st]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l), __builtin_bit_cast(bf16x8, wh[st]), acc, 0, 0, 0);
       }
     }
     if (col < a.group) {
