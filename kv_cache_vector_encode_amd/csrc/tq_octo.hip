@@ -61,9 +61,11 @@ constexpr int kOctoRowPad = 132;   // LDS floats per row: 128 coordinates, zero 
 // v lies in the lower half of the cell, j, j + 1 in the upper half; i.e.
 // floor((v + 1) nd / 2 - 1/2).  Clamped to [0, nd - 2], so both columns lie
 // on the grid: next to an outer column the pair is that column and its
-// neighbour, a superset of the pair's part on the grid.
+// neighbour, a superset of the pair's part on the grid.  |v| <= 1 keeps the
+// argument at or above -1/2, where truncation toward zero and the floor
+// differ only on (-1, 0), which the clamp takes to 0 either way.
 __device__ __forceinline__ int octo_block_lo(float v, int nd) {
-  const int h = (int)floorf(__builtin_fmaf(v, 0.5f * (float)nd, 0.5f * (float)nd - 0.5f));
+  const int h = (int)__builtin_fmaf(v, 0.5f * (float)nd, 0.5f * (float)nd - 0.5f);
   return min(max(h, 0), nd - 2);
 }
 
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
   __shared__ float s_crho[8];
   const int tid = threadIdx.x, row = tid >> 4;
   const int L = tid & 15, ell = perm16(L);
-  load_dirs<kNd, false>(s_dir, a.dirs, tid);
+  load_dirs<kNd, true>(s_dir, a.dirs, tid);   // [eta code][xi code]
   if (QJL && tid < 8) s_crho[tid] = a.crho[tid];
   const uint32_t sneg = sign_byte(a.rot, ell);
   uint32_t smask[8];
@@ -227,19 +229,24 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
       // (xi, eta) square at every bit width finds the best projection of the
       // other five cells never above the block's, equal only on the folds of
       // the map, where mirror cells tie.  So only the block is scanned.
-      const int base = a0 * kNd + c0;
-      float best = -INFINITY;
+      // In the transposed table the entry of (xi code a, eta code c) sits at
+      // a + c nd, which is also the field's direction bits a | c << kBd; so
+      // the candidates are base + {0, nd, 1, nd + 1} (xi-major: (a0, c0),
+      // (a0, c0 + 1), (a0 + 1, c0), (a0 + 1, c0 + 1)), and the winner's
+      // offset is its field's offset as well
+      const int base = a0 + (c0 << C::kBd);
+      float best = 0.f;
       int bo = 0;
 #pragma unroll
       for (int o = 0; o < 4; ++o) {
-        const float4 d = s_dir[base + (o >> 1) * kNd + (o & 1)];
+        const int off = (o >> 1) + (o & 1) * kNd;
+        const float4 d = s_dir[base + off];
         const float p = tx * d.x + ty * d.y + tz * d.z;
-        if (p > best) {
+        if (o == 0 || p > best) {
           best = p;
-          bo = o;
+          bo = off;
         }
       }
-      const int ca = a0 + (bo >> 1), cc = c0 + (bo & 1);
       // norm code: the number of ascending thresholds below p (seven
       // independent compares at b = 4; a binary search's dependent chain of
       // compares and selects measured 10% slower, a bucketed table search 0.5%
@@ -247,11 +254,11 @@ __global__ __launch_bounds__(256) void octo_encode_kernel(const OctoArgs a) {
       uint32_t k = 0;
 #pragma unroll
       for (int j = 0; j + 1 < C::kNr; ++j) k += best > a.trho[j] ? 1u : 0u;
-      const uint32_t field = (uint32_t)ca | ((uint32_t)cc << C::kBd) | (k << (2 * C::kBd));
+      const uint32_t field = (uint32_t)(base + bo) + (k << (2 * C::kBd));
       if constexpr (QJL) {
         // what the codes leave out of the triplet, in place of it (the lane
         // owns these three coordinates)
-        const float4 d = s_dir[ca * kNd + cc];
+        const float4 d = s_dir[base + bo];
         const float rk = s_crho[k];
         s_y[rw][3 * i] = __builtin_fmaf(-rk, d.x, tx);
         s_y[rw][3 * i + 1] = __builtin_fmaf(-rk, d.y, ty);
