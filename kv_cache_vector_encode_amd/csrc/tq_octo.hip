@@ -113,12 +113,19 @@ __device__ __forceinline__ float atan01(float a) {
   return a * p;
 }
 
-// atan2(y, x) for y, x >= 0 (0 when both are 0), through atan01 of the
-// smaller over the larger (the larger floored at 1e-30, so 0 / 0 gives 0)
-__device__ __forceinline__ float atan2_pos(float y, float x) {
-  const float mx = fmaxf(x, y), mn = fminf(x, y);
-  const float t = atan01(mn * __builtin_amdgcn_rcpf(fmaxf(mx, 1e-30f)));
-  return y > x ? 1.57079632679489662f - t : t;
+// atan2(|y|, |x|) (0 when both are 0), through atan01 of the smaller
+// magnitude over the larger (the larger floored at 1e-30, so 0 / 0 gives 0).
+// The larger and smaller are one max3 and one min with absolute-value
+// operands, written out: fmaxf / fminf first canonicalise operands the
+// compiler cannot prove canonical (one more instruction each); x and y are
+// finite here.
+__device__ __forceinline__ float atan2_abs(float y, float x) {
+  float mx, mn;
+  asm("v_max3_f32 %0, |%2|, |%3|, %4\n\tv_min_f32_e64 %1, |%2|, |%3|"
+      : "=&v"(mx), "=&v"(mn)
+      : "v"(x), "v"(y), "v"(1e-30f));
+  const float t = atan01(mn * __builtin_amdgcn_rcpf(mx));
+  return fabsf(y) > fabsf(x) ? 1.57079632679489662f - t : t;
 }
 
 // Equal-area octahedral map of the direction of (nx, ny, .) with unit-vector
@@ -129,7 +136,7 @@ __device__ __forceinline__ float atan2_pos(float y, float x) {
 // coordinate of -0 takes the negative side: the map's two sides agree there).
 __device__ __forceinline__ void oct_map(float nx, float ny, float nz, float& xi, float& eta) {
   const float r = __builtin_amdgcn_sqrtf(fmaxf(1.f - fabsf(nz), 0.f));
-  const float phi = atan2_pos(fabsf(ny), fabsf(nx));
+  const float phi = atan2_abs(ny, nx);
   float ae = r * phi * 0.636619772367581343f;   // 2 / pi
   float ax = r - ae;
   if (nz < 0.f) {
