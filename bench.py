@@ -327,6 +327,42 @@ def main():
             torch.cuda.synchronize()
             acc.extend(e[0].elapsed_time(e[1]) for e in ev)
 
+    # ---- caches with the QJL residual sketch on the keys (E6): encode every
+    # key and value into them, and decode-attend over them (the vector-unit
+    # kernels); two caches used in turn
+    qe_ms, qd_ms = [], []
+    if args.only == "both" and not args.no_extras:
+        qrot = tq.tq_make_rotation(w.rot_seed, 128)
+        qrot2 = tq.tq_make_rotation(w.rot_seed + 1, 128)
+        qcfg = tq.make_config(w.num_kv_heads, w.num_blocks, w.bits_k, w.bits_v, qrot, True, qrot2)
+        qsets = []
+        for i in range(2):
+            qpool = torch.zeros(tq.tq_cache_bytes(qcfg), dtype=torch.uint8, device=dev)
+            qc = tq.tq_cache_create(qcfg, qpool)
+            qsets.append(dict(cache=qc, ws=tq.new_workspace(qc, w.num_seqs, w.num_q_heads, bt.shape[1], device=dev),
+                              out=torch.empty((w.num_seqs, w.num_q_heads, 128), device=dev)))
+        reps = max(5, args.steps // 4)
+
+        def q_enc(i):
+            s, c = sets[i % nsets], qsets[i % 2]
+            tq.tq_encode_kv(s["K"], s["V"], slots, w.bits_k, c["cache"], stream)
+
+        def q_dec(i):
+            c = qsets[(i + 1) % 2]
+            tq.tq_decode_attend(q, c["cache"], bt, lens, c["out"], c["ws"], stream=stream)
+
+        for fn, acc in ((q_enc, qe_ms), (q_dec, qd_ms)):
+            for i in range(3):
+                fn(i)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+            for i in range(reps):
+                ev[i][0].record(stream)
+                fn(i + 3)
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            acc.extend(e[0].elapsed_time(e[1]) for e in ev)
+        del qsets
+
     # ---- the min/max comparison codec on the same keys and values
     mm_enc_ms, mm_dec_ms = [], []
     if args.only == "both" and not args.no_extras:
@@ -488,6 +524,27 @@ def main():
             "unfused_us": round(un_s * 1e6, 2),
             "note": "append each sequence's new token + decode-attend in one call; unfused_us = tq_encode_kv of "
                     "the new tokens + tq_decode_attend; not part of the timed step"}
+    if qe_ms:
+        # keys carry 16 sign bytes and an fp16 residual norm more
+        qkb = 128 * w.bits_k // 8 + 2 + 16 + 2
+        qvb = 128 * w.bits_v // 8 + 2
+        th = w.tokens * w.num_kv_heads
+        qeb = th * (2 * in_b + qkb + qvb)
+        qe_s = float(np.mean(qe_ms)) / 1e3
+        kernels["tq_encode_kv_qjl"] = {
+            "bound": "hbm", "achieved": round(qeb / qe_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(qeb / qe_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": qeb,
+            "us_per_launch": round(qe_s * 1e6, 2), "vectors_per_s": round(2 * th / qe_s, 1),
+            "note": "encode into a cache with the QJL residual sketch on the keys (vector-unit kernel); "
+                    "not part of the timed step"}
+        qdb = th * (qkb + qvb)
+        qd_s = float(np.mean(qd_ms)) / 1e3
+        kernels["tq_decode_attend_qjl"] = {
+            "bound": "hbm", "achieved": round(qdb / qd_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(qdb / qd_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": qdb,
+            "us_per_launch": round(qd_s * 1e6, 2),
+            "note": "decode-attend over a cache with the QJL residual sketch (vector-unit kernel, split + merge); "
+                    "not part of the timed step"}
     if mm_enc_ms:
         mb = nvec * (in_b + 128 * w.bits_k // 8 + 4)            # bf16 in, codes + fp16 scale and zero out
         me_s = float(np.mean(mm_enc_ms)) / 1e3

@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a, int ns,
   __shared__ float s_p[ATTEND ? kMaxSplitTokens * GMAX : 1];
   __shared__ float s_ml[2][GMAX];
   __shared__ float s_red[ATTEND ? 4 : 1][GMAX][kD];
+  __shared__ int s_bt[kMaxSplitTokens / kBlock];   // the split's blocks, clamped into the pool
 
   const int tid = threadIdx.x;
   const int r = tid >> 4, p = tid & 15;
@@ -61,6 +62,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a, int ns,
   if (tid < 16) {
     s_ck[tid] = a.cent_k[tid];
     s_cv[tid] = a.cent_v[tid];
+  }
+  const int32_t* btab = a.block_tables + (int64_t)n * a.max_blocks;
+  const int nb = t1 > t0 ? (t1 - t0 + kBlock - 1) / kBlock : 0;   // t0 is a block multiple
+  for (int i = tid; i < nb; i += 256) {
+    const int b = btab[t0 / kBlock + i];
+    s_bt[i] = (b >= 0 && b < a.num_blocks) ? b : 0;
   }
 
   // ---- D0: rotate this slice's queries, q_rot = H D q / sqrt(d) (and R' q_rot)
@@ -104,25 +111,45 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a, int ns,
       if constexpr (QJL) wreg[g][e] = g < gcount ? s_w[g][8 * p + e] : 0.f;
     }
 
-  const int32_t* btab = a.block_tables + (int64_t)n * a.max_blocks;
   const int64_t Hkv = a.num_kv_heads;
+  // Rows take token row r of the split's blocks in turn, kU blocks at a
+  // time with every load of the batch issued before the first use (a loop
+  // that loads and uses one token at a time waits out a memory round trip
+  // per token); blocks past the split's end re-read its last block and are
+  // not used
+  constexpr int kU = 4;
+  auto blk_base = [&](int i) {
+    return a.pool + ((int64_t)s_bt[min(i, nb - 1)] * Hkv + h) * a.lay.block_bytes;
+  };
 
   // ---- A: logits
-  for (int tok = t0 + r; tok < t1; tok += 16) {
-    int blk = btab[tok >> 4];
-    blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
-    const int row = tok & 15;
-    const uint8_t* base = a.pool + ((int64_t)blk * Hkv + h) * a.lay.block_bytes;
-    const uint32_t cw = load_codes8<BK>(base + a.lay.off_k + (int64_t)row * a.lay.k_rec, p);
+  for (int i0 = 0; i0 < nb; i0 += kU) {
+    uint32_t cwb[kU], sbb[kU];
+    unsigned short gkb[kU], rhb[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const uint8_t* base = blk_base(i0 + u);
+      cwb[u] = load_codes8<BK>(base + a.lay.off_k + (int64_t)r * a.lay.k_rec, p);
+      gkb[u] = *reinterpret_cast<const unsigned short*>(base + a.lay.off_gk + 2 * r);
+      if constexpr (QJL) {
+        sbb[u] = base[a.lay.off_sign + r * 16 + p];
+        rhb[u] = *reinterpret_cast<const unsigned short*>(base + a.lay.off_rho + 2 * r);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+    const int tok = t0 + (i0 + u) * kBlock + r;
+    if (i0 + u >= nb || tok >= t1) break;   // uniform across rows but for the last block
+    const uint32_t cw = cwb[u];
     float c[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) c[e] = s_ck[(cw >> (BK * e)) & ((1u << BK) - 1)];
-    const float gk = load_half(base + a.lay.off_gk + 2 * row);
+    const float gk = __half2float(__ushort_as_half(gkb[u]));
     float qj_rho = 0.f;
     uint32_t sbits = 0;
     if constexpr (QJL) {
-      sbits = base[a.lay.off_sign + row * 16 + p];
-      qj_rho = load_half(base + a.lay.off_rho + 2 * row) * (kSqrtHalfPi * kInvSqrtD);
+      sbits = sbb[u];
+      qj_rho = __half2float(__ushort_as_half(rhb[u])) * (kSqrtHalfPi * kInvSqrtD);
     }
     float mine = 0.f;
 #pragma unroll
@@ -145,6 +172,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a, int ns,
       if (a.logits)
         a.logits[((int64_t)n * Hq + (int64_t)h * a.group + g0 + p) * a.logits_stride + tok] = mine;
       if constexpr (ATTEND) s_p[(tok - t0) * GMAX + p] = mine;
+    }
     }
   }
   if constexpr (!ATTEND) return;
@@ -176,13 +204,21 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a, int ns,
   for (int g = 0; g < GMAX; ++g)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-  for (int tok = t0 + r; tok < t1; tok += 16) {
-    int blk = btab[tok >> 4];
-    blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
-    const int row = tok & 15;
-    const uint8_t* base = a.pool + ((int64_t)blk * Hkv + h) * a.lay.block_bytes;
-    const uint32_t cw = load_codes8<BV>(base + a.lay.off_v + (int64_t)row * a.lay.v_rec, p);
-    const float gv = load_half(base + a.lay.off_gv + 2 * row);
+  for (int i0 = 0; i0 < nb; i0 += kU) {
+    uint32_t cwb[kU];
+    unsigned short gvb[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const uint8_t* base = blk_base(i0 + u);
+      cwb[u] = load_codes8<BV>(base + a.lay.off_v + (int64_t)r * a.lay.v_rec, p);
+      gvb[u] = *reinterpret_cast<const unsigned short*>(base + a.lay.off_gv + 2 * r);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+    const int tok = t0 + (i0 + u) * kBlock + r;
+    if (i0 + u >= nb || tok >= t1) break;
+    const uint32_t cw = cwb[u];
+    const float gv = __half2float(__ushort_as_half(gvb[u]));
     float c[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) c[e] = s_cv[(cw >> (BV * e)) & ((1u << BV) - 1)];
@@ -191,6 +227,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a, int ns,
       const float pw = s_p[(tok - t0) * GMAX + g] * gv;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[g][e] = __builtin_fmaf(pw, c[e], acc[g][e]);
+    }
     }
   }
 
