@@ -151,21 +151,25 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a, int ns,
       sbits = sbb[u];
       qj_rho = __half2float(__ushort_as_half(rhb[u])) * (kSqrtHalfPi * kInvSqrtD);
     }
+    // the residual estimate's weights +-tau rho of this token's 8 sign bits,
+    // shared by every head: it joins the lane's part of the logit before the
+    // row sum (one 16-lane sum per head instead of two)
+    [[maybe_unused]] float cs[8];
+    if constexpr (QJL) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cs[e] = flip(qj_rho, sbits, e);
+    }
     float mine = 0.f;
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(c[e], qreg[g][e], dot);
-      dot = row_sum(dot);
-      float sg = a.scale * gk * dot;
       if constexpr (QJL) {
-        float qd = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qd += flip(wreg[g][e], sbits, e);
-        qd = row_sum(qd);
-        sg = __builtin_fmaf(a.scale * gk * qj_rho, qd, sg);
+        for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(cs[e], wreg[g][e], dot);
       }
+      const float sg = a.scale * gk * row_sum(dot);
       if (p == g) mine = sg;
     }
     if (p < gcount) {
