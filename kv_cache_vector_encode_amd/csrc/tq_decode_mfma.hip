@@ -152,22 +152,24 @@ __device__ __forceinline__ void key_planes_b4(uint32_t w, const KeyI8Tab& t, uin
   lo = __builtin_amdgcn_perm(t.l1, t.l0, so) ^ mo;
 }
 
-// Geometry of one (block, KV head) chunk of a cache with values and no QJL
-// sidecar (K codes [16][16b] | V codes [16][16b] | gamma_k [16] | gamma_v
-// [16], fp16 norms), and of its LDS stage slot.  The chunk is copied by kFull
-// 1 KiB pieces (64 lanes x 16 B) and one tail piece of kRem bytes by the
-// first kRem / 16 lanes, so a slot holds exactly one chunk.  kStages block
-// pairs per wave.
-template <int BITS>
+// Geometry of one (block, KV head) chunk of a cache with values (K codes
+// [16][16b] | V codes [16][16b] | gamma_k [16] | gamma_v [16], fp16 norms;
+// with the QJL sidecar also rho [16], fp16 residual norms, and signs
+// [16][16 B]), and of its LDS stage slot.  The chunk is copied by kFull 1 KiB
+// pieces (64 lanes x 16 B) and one tail piece of kRem bytes by the first
+// kRem / 16 lanes, so a slot holds exactly one chunk.  kStages block pairs
+// per wave.
+template <int BITS, bool QJL = false>
 struct Chunk {
-  static constexpr int kBytes = 512 * BITS + 64;
+  static constexpr int kBytes = 512 * BITS + 64 + (QJL ? 32 + 256 : 0);
   static constexpr int kOffV = 256 * BITS, kOffGK = 512 * BITS, kOffGV = 512 * BITS + 32;
+  static constexpr int kOffRho = 512 * BITS + 64, kOffSign = kOffRho + 32;
   static constexpr int kFull = kBytes / 1024;
   static constexpr int kRem = kBytes - 1024 * kFull;
   static constexpr int kTailLanes = kRem / 16;
   static constexpr int kSlot = kBytes;
   static constexpr int kDma = kFull + 1;     // copy instructions per chunk
-  static constexpr int kStages = BITS == 2 ? 4 : 2;
+  static constexpr int kStages = BITS == 2 && !QJL ? 4 : 2;
   static constexpr int kWaveRing = kStages * 2 * kSlot;
   static_assert(kRem > 0 && kRem % 16 == 0 && kTailLanes <= 64, "tail piece");
   // exec mask of the tail copy
@@ -183,9 +185,9 @@ struct Chunk {
 // lands at its offset inside the slot.  The tail piece runs with the exec
 // mask narrowed to its lanes (inactive lanes neither read nor write); m0 and
 // exec are saved and restored inside the asm.
-template <int BITS>
+template <int BITS, bool QJL>
 __device__ __forceinline__ void dma_chunk(uint32_t lds, const uint8_t* src, uint32_t v16, uint32_t vv) {
-  using C = Chunk<BITS>;
+  using C = Chunk<BITS, QJL>;
   uint32_t save;
   uint64_t esave;
   if constexpr (BITS == 4) {
@@ -244,9 +246,9 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 // wait for the oldest staged pair while `behind` younger pairs stay in flight
-template <int BITS>
+template <int BITS, bool QJL>
 __device__ __forceinline__ void wait_pairs_behind(int behind) {
-  constexpr int P = 2 * Chunk<BITS>::kDma;
+  constexpr int P = 2 * Chunk<BITS, QJL>::kDma;
   if (behind <= 0) wait_vm<0>();
   else if (behind == 1) wait_vm<P>();
   else if (behind == 2) wait_vm<2 * P>();
@@ -273,6 +275,12 @@ struct BlockRegs {
 struct PairNorms {
   uint32_t gk[2];
   uint32_t gv[2];
+};
+// QJL sidecar of both blocks of a pair: word g of token m's sign record, and
+// the fp16 residual norms of tokens 4g .. 4g+3
+struct PairQjl {
+  uint32_t sw[2];
+  uint32_t rh[2][2];
 };
 
 // this lane's codes and norms of one chunk staged in LDS at st
@@ -335,7 +343,7 @@ __device__ __forceinline__ float mul_h_hi(float a, uint32_t h) {
 
 // LDS of one workgroup, in one object so the tables sit at address 0 (a
 // lookup address then fits the instruction's offset field).
-template <int BITS>
+template <int BITS, bool QJL = false>
 struct DecodeSmem {
   // 4-bit codes: the logits take 8-bit integer operands built on the vector
   // unit (key_planes_b4), no key table; values read a table of code pairs,
@@ -368,7 +376,7 @@ struct DecodeSmem {
   float cent[2][16];                   // key / value centroids (4-bit)
   uint32_t half[2][16];                // key / value scaled halves (2-, 3-bit)
   float wm[kWaves][8], wl[kWaves][8], ml[2][8];
-  alignas(16) uint8_t ring[kWaves * Chunk<BITS>::kWaveRing];
+  alignas(16) uint8_t ring[kWaves * Chunk<BITS, QJL>::kWaveRing];
 };
 
 // Byte address of the table entry for the W-bit field i of a packed
@@ -528,12 +536,13 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, const AppendAr
   __syncthreads();
 }
 
-template <int BITS, bool LOGITS, bool APPEND>
+template <int BITS, bool LOGITS, bool APPEND, bool QJL = false>
 __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgpu_waves_per_eu(4))) void decode_mfma_kernel(
     const DecodeArgs a, int ns, int gs, const typename std::conditional<APPEND, AppendArgs, NoAppend>::type ap) {
-  using C = Chunk<BITS>;
+  static_assert(!QJL || (BITS <= 3 && !APPEND), "the QJL term runs on the table path, without the append");
+  using C = Chunk<BITS, QJL>;
   constexpr int NS = C::kStages;
-  __shared__ DecodeSmem<BITS> sm;
+  __shared__ DecodeSmem<BITS, QJL> sm;
   const uint32_t* const s_tv2 = sm.tv;
   auto& s_qb = sm.qb;
   auto& s_wm = sm.wm;
@@ -591,8 +600,8 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
   const uint32_t vv = v_slot_src(lane);
   auto dma_pair = [&](int k, int b0, int b1) {   // k-th pair of this wave into stage k % NS
     const uint32_t st = ring_lds + (uint32_t)((k % NS) * 2 * C::kSlot);
-    dma_chunk<BITS>(st, chunk_src(b0), v16, vv);
-    dma_chunk<BITS>(st + C::kSlot, chunk_src(b1), v16, vv);
+    dma_chunk<BITS, QJL>(st, chunk_src(b0), v16, vv);
+    dma_chunk<BITS, QJL>(st + C::kSlot, chunk_src(b1), v16, vv);
   };
   // Block-table entries of this wave's pairs for the loop: lane j holds
   // those of pair j (at most 64 pairs per wave, by the split size), read
@@ -675,13 +684,20 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
       sm.tv[i] = f16_bits(sm.cent[1][i & mask]) | (f16_bits(sm.cent[1][i >> BITS]) << 16);
     }
   }
-  if (wv == 0) wait_pairs_behind<BITS>(owner ? 0 : k_pro);   // the query copy has landed
+  if (wv == 0) wait_pairs_behind<BITS, QJL>(owner ? 0 : k_pro);   // the query copy has landed
   __syncthreads();
 
   // ---- rotate this slice's queries (rows of 16 lanes, one head each; the
   // logit scale and log2(e) are folded in, so logits come out in log2 units)
   // and scatter them into the B operands of the logit product.  Columns of
   // heads past the slice are zero.
+  // QJL: w = R' (R q) of the rotation rows' heads, lane p holding
+  // coordinates 8 perm16(p) + e (zero for heads past the slice)
+  [[maybe_unused]] float wq[QJL ? 8 : 1];
+  if constexpr (QJL) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wq[e] = 0.f;
+  }
   {
     const int r = tid >> 4, p = tid & 15;
     float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -702,6 +718,18 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
       const float sc = fc.sig * kInvSqrtD * a.scale * LOG2E;
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] *= sc;
+      if constexpr (QJL) {
+        // the residual sketch is read against R' applied to the scaled
+        // R q: flip dims 8p..8p+7 by byte p of R' and run the row FWHT again
+        const int ws = p >> 2;
+        const uint32_t wd2 = ws == 0 ? a.rot_qjl.neg[0] : ws == 1 ? a.rot_qjl.neg[1] : ws == 2 ? a.rot_qjl.neg[2] : a.rot_qjl.neg[3];
+        const uint32_t sq = (wd2 >> (8 * (p & 3))) & 0xFFu;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wq[e] = flip(x[e], sq, e);
+        fwht_row(wq, fc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wq[e] *= fc.sig * kInvSqrtD;
+      }
     }
     // every read of the staged queries is done before the B operands,
     // which share their storage, are written
@@ -781,6 +809,33 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
   u32x4 qreg[QS];
 #pragma unroll
   for (int st = 0; st < QS; ++st) qreg[st] = s_qb[st][lane];
+  // QJL: B operands of the sketch product, built in the same storage once
+  // every wave holds its query operands.  Column c -> head c % 8, part c / 8
+  // (f16 w_hi, f16 residual); in the operand of lane (c, g) at step st, slot
+  // 2k carries coordinate j = 32g + 4st + k and slot 2k + 1 coordinate j + 16,
+  // whose sign bits sit at bits 4st + k and 4st + k + 16 of word g of the
+  // token's sign record.
+  [[maybe_unused]] u32x4 wreg[QJL ? 4 : 1];
+  if constexpr (QJL) {
+    __syncthreads();
+    const int r = tid >> 4, p = tid & 15;
+    if (r < 8) {
+      uint16_t* wb = reinterpret_cast<uint16_t*>(s_qb);
+      const int lo = perm16(p);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 8 * lo + e, gq = d >> 5, j = d & 31;
+        const int st = (j & 15) >> 2, sl = 2 * (j & 3) + (j >> 4);
+        const _Float16 hh = (_Float16)wq[e];
+        const _Float16 hl = (_Float16)(wq[e] - (float)hh);
+        wb[(st * 64 + r + 16 * gq) * 8 + sl] = __builtin_bit_cast(uint16_t, hh);
+        wb[(st * 64 + r + 8 + 16 * gq) * 8 + sl] = __builtin_bit_cast(uint16_t, hl);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 4; ++st) wreg[st] = s_qb[st][lane];
+  }
   // After the logit products, the two 8-lane halves of every row hold the
   // two parts of the same head's sums (column m: q_hi / Qh for m < 8, q_lo /
   // Ql for m >= 8).  Each half keeps one block of the pair: lanes m < 8 take
@@ -795,7 +850,7 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
   const float kc = kI8 ? sm.qcorr[m & 7] * kmult : 0.f;
   const KeyI8Tab kt = {a.ki8_hi[0], a.ki8_hi[1], a.ki8_lo[0], a.ki8_lo[1]};
 
-  auto compute_pair = [&](const BlockRegs<BITS>(&cur)[2], const PairNorms& nrm, int lb0) {
+  auto compute_pair = [&](const BlockRegs<BITS>(&cur)[2], const PairNorms& nrm, [[maybe_unused]] const PairQjl& qj, int lb0) {
     // ---- logits of the two blocks (log2 units)
     float fv[2][4];   // 8-bit path: this lane's column of each block's product
     f32x4 ck[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // table path: the products
@@ -838,6 +893,36 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
           ck[X] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av),
                                                          __builtin_bit_cast(f16x8, qreg[st]), ck[X], 0, 0, 0);
         }
+      if constexpr (QJL) {
+        // residual estimate: C[16 tokens x 16] = S[16 x 128] W[128 x 16],
+        // S = the tokens' sign bits as f16 +-1 (exact), W = R' R q split
+        // into f16 halves like the query; each word's two sign bits move to
+        // the two f16 sign positions with one shift and one and-or.  Then
+        // each logit gains sqrt(pi/2)/sqrt(d) rho_t times its sum, before
+        // the two halves are added and the key norm applied.
+        f32x4 cq[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int X = 0; X < 2; ++X) {
+            u32x4 sa;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int sh = 15 - 4 * st - q;
+              sa[q] = ((sh ? qj.sw[X] << sh : qj.sw[X]) & 0x80008000u) | 0x3C003C00u;
+            }
+            cq[X] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, sa),
+                                                           __builtin_bit_cast(f16x8, wreg[st]), cq[X], 0, 0, 0);
+          }
+        constexpr float kTau = 0.1107783657f;   // sqrt(pi/2) / sqrt(128)
+#pragma unroll
+        for (int X = 0; X < 2; ++X)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float tr = (j & 1) ? mul_h_hi(kTau, qj.rh[X][j >> 1]) : mul_h_lo(kTau, qj.rh[X][j >> 1]);
+            ck[X][j] = __builtin_fmaf(tr, cq[X][j], ck[X][j]);
+          }
+      }
     }
     // own block's part, plus the other part from the lane 8 columns away,
     // times the token's key norm: the table path does both in logits_tab
@@ -989,7 +1074,7 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
   const uint8_t* ring = s_ring + wv * C::kWaveRing;
   const int own_slot = col_lo ? C::kSlot : 0;   // the lane's block of the pair
   auto step = [&](int k, int u) {   // pair k sits in stage u = k % NS
-    wait_pairs_behind<BITS>(min(NS - 1, my_n - 1 - k));
+    wait_pairs_behind<BITS, QJL>(min(NS - 1, my_n - 1 - k));
     // the block-table loads are older than the copy just waited for; this
     // keeps their uses below that wait
     asm volatile("" : "+v"(ids0), "+v"(ids1));
@@ -999,12 +1084,23 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
     read_chunk<BITS>(cur[0], st, m, g);
     read_chunk<BITS>(cur[1], st + C::kSlot, m, g);
     read_norms<BITS>(nrm, st + own_slot, g);
+    PairQjl qj;
+    if constexpr (QJL) {
+#pragma unroll
+      for (int X = 0; X < 2; ++X) {
+        const uint8_t* sx = st + X * C::kSlot;
+        qj.sw[X] = *reinterpret_cast<const uint32_t*>(sx + C::kOffSign + 16 * m + 4 * g);
+        const uint2 rr = *reinterpret_cast<const uint2*>(sx + C::kOffRho + 8 * g);
+        qj.rh[X][0] = rr.x;
+        qj.rh[X][1] = rr.y;
+      }
+    }
     if (k + NS < my_n) {
       // the stage is overwritten only after this wave's reads of it are done
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       dma_pair(k + NS, (int)__builtin_amdgcn_readlane(ids0, k + NS), (int)__builtin_amdgcn_readlane(ids1, k + NS));
     }
-    compute_pair(cur, nrm, sb0 + 2 * (wv + NW * k));
+    compute_pair(cur, nrm, qj, sb0 + 2 * (wv + NW * k));
   };
   for (int k0 = 0; k0 < my_n; k0 += NS) {
 #pragma unroll
@@ -1067,14 +1163,16 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
   }
 }
 
-static int check_mfma_args(const DecodeArgs& a, int bits) {
-  // the kernel's chunk geometry is fixed at compile time: values, no sidecar
-  const int64_t expect = 512 * bits + 64;
+static int check_mfma_args(const DecodeArgs& a, int bits, bool qjl) {
+  // the kernel's chunk geometry is fixed at compile time: values, and the
+  // QJL sidecar (2- and 3-bit caches) right after the norms
+  const int64_t expect = 512 * bits + 64 + (qjl ? 32 + 256 : 0);
   if (a.lay.block_bytes != expect || a.lay.off_k != 0 || a.lay.off_v != 256 * bits ||
       a.lay.off_gk != 512 * bits || a.lay.off_gv != 512 * bits + 32 ||
+      (qjl && (a.lay.off_rho != 512 * bits + 64 || a.lay.off_sign != 512 * bits + 96)) ||
       (reinterpret_cast<uintptr_t>(a.pool) & 15) != 0)
     return (int)hipErrorInvalidValue;
-  if (bits < 2 || bits > 4) return (int)hipErrorInvalidValue;
+  if (bits < 2 || bits > 4 || (qjl && bits > 3)) return (int)hipErrorInvalidValue;
   // 4-bit keys need the integer form of the key codebook (odd-symmetric)
   if (bits == 4 && !(a.ki8_unit > 0.f)) return (int)hipErrorInvalidValue;
   // a wave keeps the block-table entries of its pairs one per lane
@@ -1084,9 +1182,21 @@ static int check_mfma_args(const DecodeArgs& a, int bits) {
 }
 
 template <bool APPEND, typename AP>
-static void launch_mfma(const DecodeArgs& a, const AP& ap, int bits, int ns, int gs, hipStream_t s) {
+static void launch_mfma(const DecodeArgs& a, const AP& ap, int bits, bool qjl, int ns, int gs, hipStream_t s) {
   const dim3 grid((unsigned)a.num_splits, (unsigned)(a.num_kv_heads * ns), (unsigned)a.num_seqs);
   const bool lg = a.logits != nullptr;
+  if constexpr (!APPEND) {
+    if (qjl) {
+      if (bits == 2) {
+        if (lg) hipLaunchKernelGGL((decode_mfma_kernel<2, true, false, true>), grid, dim3(64 * DecodeSmem<2>::kWaves), 0, s, a, ns, gs, ap);
+        else hipLaunchKernelGGL((decode_mfma_kernel<2, false, false, true>), grid, dim3(64 * DecodeSmem<2>::kWaves), 0, s, a, ns, gs, ap);
+      } else {
+        if (lg) hipLaunchKernelGGL((decode_mfma_kernel<3, true, false, true>), grid, dim3(64 * DecodeSmem<3>::kWaves), 0, s, a, ns, gs, ap);
+        else hipLaunchKernelGGL((decode_mfma_kernel<3, false, false, true>), grid, dim3(64 * DecodeSmem<3>::kWaves), 0, s, a, ns, gs, ap);
+      }
+      return;
+    }
+  }
   switch (bits) {
     case 2:
       if (lg) hipLaunchKernelGGL((decode_mfma_kernel<2, true, APPEND>), grid, dim3(64 * DecodeSmem<2>::kWaves), 0, s, a, ns, gs, ap);
@@ -1103,20 +1213,20 @@ static void launch_mfma(const DecodeArgs& a, const AP& ap, int bits, int ns, int
   }
 }
 
-int launch_decode_mfma(const DecodeArgs& a, int bits, int ns, int gs, void* stream) {
-  const int e = check_mfma_args(a, bits);
+int launch_decode_mfma(const DecodeArgs& a, int bits, bool qjl, int ns, int gs, void* stream) {
+  const int e = check_mfma_args(a, bits, qjl);
   if (e) return e;
-  launch_mfma<false>(a, NoAppend{}, bits, ns, gs, static_cast<hipStream_t>(stream));
+  launch_mfma<false>(a, NoAppend{}, bits, qjl, ns, gs, static_cast<hipStream_t>(stream));
   return (int)hipGetLastError();
 }
 
 // Decode step: append each sequence's new token, attend, merge.
 int launch_decode_step(const DecodeArgs& a, const AppendArgs& ap, int bits, void* stream) {
-  const int e = check_mfma_args(a, bits);
+  const int e = check_mfma_args(a, bits, false);
   if (e) return e;
   const int ns = decode_slices(a.group);
   const int gs = (a.group + ns - 1) / ns;
-  launch_mfma<true>(a, ap, bits, ns, gs, static_cast<hipStream_t>(stream));
+  launch_mfma<true>(a, ap, bits, false, ns, gs, static_cast<hipStream_t>(stream));
   const hipError_t le = hipGetLastError();
   if (le != hipSuccess) return (int)le;
   return launch_merge(a, stream);

@@ -450,12 +450,13 @@ int blocks_per_split_for(const tq_cache* c, int32_t num_seqs, int32_t group, int
   return (int)bps;
 }
 
-// Decode-attend without a QJL sidecar runs on the matrix cores.
+// Decode-attend runs on the matrix cores, with a QJL sidecar too for 2- and
+// 3-bit caches (4-bit QJL caches stay on the vector units).
 // TQ_DECODE_VALU=1 selects the vector-unit kernel instead (comparison only).
 bool decode_uses_mfma(const tq_cache* c, bool attend) {
   if (const char* env = std::getenv("TQ_DECODE_VALU"))
     if (std::atoi(env) == 1) return false;
-  return attend && !c->cfg.qjl;
+  return attend && (!c->cfg.qjl || c->cfg.bits_k <= 3);
 }
 
 int validate_decode(const void* q, int32_t q_dtype, const tq_cache* cache,
@@ -824,7 +825,7 @@ int tq_decode_step(const void* q, int32_t q_dtype, const void* K_new, const void
   const tq_cache_config& cfg = cache->cfg;
   if (cfg.bits_v == 0) return fail(TQ_ERR_INVALID_ARG, "decode_step needs a cache with values");
   if (cfg.bits_v != cfg.bits_k) return fail(TQ_ERR_BITS_MISMATCH, "decode_step needs keys and values of one bit width");
-  if (!decode_uses_mfma(cache, true))
+  if (!decode_uses_mfma(cache, true) || cache->cfg.qjl)
     return fail(TQ_ERR_UNSUPPORTED, "decode_step runs on the matrix-core decode (no QJL sidecar)");
   if (kv_dtype != TQ_F32 && kv_dtype != TQ_F16 && kv_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad kv_dtype");
   if (num_seqs == 0) return TQ_OK;

@@ -219,7 +219,7 @@ int scratch_buffer(void** ptr, int64_t* bytes);
 int launch_encode(const EncodeArgs& a, int num_streams, int in_dtype, void* stream);
 int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int attend, int mfma, void* stream);
 int decode_slices(int group);
-int launch_decode_mfma(const DecodeArgs& a, int bits, int ns, int gs, void* stream);
+int launch_decode_mfma(const DecodeArgs& a, int bits, bool qjl, int ns, int gs, void* stream);
 int launch_merge(const DecodeArgs& a, void* stream);
 int launch_decode_step(const DecodeArgs& a, const AppendArgs& ap, int bits, void* stream);
 int launch_reconstruct(const ReconArgs& a, void* stream);

@@ -347,8 +347,9 @@ def test_fullsize_octo_decode_workload(device):
 def test_longest_sequence_at_the_split_limit(device, qjl):
     """The longest sequence decode-attend takes: 4096 splits of the largest
     split size, i.e. 4,194,304 blocks (67,108,859 tokens, a ragged last block;
-    a 6.7 GB pool) for the matrix-core kernel, and 262,144 blocks (4,194,299
-    tokens) for the vector kernel that QJL caches take; one KV head with
+    a 6.7 GB pool) without the QJL sidecar, and 262,144 blocks (4,194,299
+    tokens, the vector kernel's limit, which 4-bit QJL caches take; this
+    3-bit one runs on the matrix-core kernel) with it; one KV head with
     3-bit codes, 8 query heads; the merge folds 4096 partials per head in 32
     rounds.  Every key but five points against the queries (logits near
     -20), the five hot ones along them (near +20), so the other tokens carry

@@ -370,6 +370,16 @@ def test_decode_attend_qjl_and_scale(device):
     _decode_case(device, 3, 8, 2, [250, 2100], qjl=True, dtype="f32", scale=0.05)
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("group", [1, 5, 8, 12])
+def test_decode_attend_qjl(device, bits, group):
+    # 2- and 3-bit caches with the QJL sidecar run on the matrix-core decode
+    # (the residual estimate as a sign-matrix product), 4-bit ones on the
+    # vector kernel; logits against the oracle's QJL-corrected scores, an
+    # empty sequence, a single token, ragged tails and whole block pairs
+    _decode_case(device, bits, group, 2, [0, 1, 300, 1029], qjl=True)
+
+
 @pytest.mark.parametrize("bits", [3, 4])
 def test_decode_empty_and_long_splits(device, bits):
     _decode_case(device, bits, 8, 1, [0, 16, 4100, 5])
