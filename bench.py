@@ -543,8 +543,8 @@ def main():
             "bound": "hbm", "achieved": round(qdb / qd_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(qdb / qd_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": qdb,
             "us_per_launch": round(qd_s * 1e6, 2),
-            "note": "decode-attend over a cache with the QJL residual sketch (split + merge: the matrix-core kernel "
-                    "at 2 and 3 bits, the vector-unit kernel at 4); not part of the timed step"}
+            "note": "decode-attend over a cache with the QJL residual sketch (matrix-core split kernel + merge); "
+                    "not part of the timed step"}
     if mm_enc_ms:
         mb = nvec * (in_b + 128 * w.bits_k // 8 + 4)            # bf16 in, codes + fp16 scale and zero out
         me_s = float(np.mean(mm_enc_ms)) / 1e3

@@ -286,7 +286,7 @@ int launch_decode(const DecodeArgs& a, int bits_k, int bits_v, int qjl, int atte
   const int ns = (a.group + 7) / 8;
   const int gs = (a.group + ns - 1) / ns;
   if (attend && bits_v != bits_k) return (int)hipErrorInvalidValue;
-  if (attend && mfma && (!qjl || bits_k <= 3)) {
+  if (attend && mfma) {
     const int e = launch_decode_mfma(a, bits_k, qjl != 0, ns, gs, stream);
     return e ? e : launch_merge(a, stream);
   }

@@ -536,10 +536,13 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, const AppendAr
   __syncthreads();
 }
 
+// 4 waves per SIMD (two 8-wave workgroups per CU); a 4-bit QJL chunk ring
+// leaves room for one workgroup per CU, so that variant may take the
+// registers of 2
 template <int BITS, bool LOGITS, bool APPEND, bool QJL = false>
-__global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgpu_waves_per_eu(4))) void decode_mfma_kernel(
+__global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgpu_waves_per_eu(QJL && BITS == 4 ? 2 : 4))) void decode_mfma_kernel(
     const DecodeArgs a, int ns, int gs, const typename std::conditional<APPEND, AppendArgs, NoAppend>::type ap) {
-  static_assert(!QJL || (BITS <= 3 && !APPEND), "the QJL term runs on the table path, without the append");
+  static_assert(!QJL || !APPEND, "the decode step takes caches without the QJL sidecar");
   using C = Chunk<BITS, QJL>;
   constexpr int NS = C::kStages;
   __shared__ DecodeSmem<BITS, QJL> sm;
@@ -820,7 +823,7 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
     __syncthreads();
     const int r = tid >> 4, p = tid & 15;
     if (r < 8) {
-      uint16_t* wb = reinterpret_cast<uint16_t*>(s_qb);
+      uint16_t* wb = reinterpret_cast<uint16_t*>(sm.qs);   // 4 KB: 4 steps x 64 lanes x 16 B
       const int lo = perm16(p);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -834,7 +837,7 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
     }
     __syncthreads();
 #pragma unroll
-    for (int st = 0; st < 4; ++st) wreg[st] = s_qb[st][lane];
+    for (int st = 0; st < 4; ++st) wreg[st] = reinterpret_cast<const u32x4*>(sm.qs)[st * 64 + lane];
   }
   // After the logit products, the two 8-lane halves of every row hold the
   // two parts of the same head's sums (column m: q_hi / Qh for m < 8, q_lo /
@@ -850,6 +853,28 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
   const float kc = kI8 ? sm.qcorr[m & 7] * kmult : 0.f;
   const KeyI8Tab kt = {a.ki8_hi[0], a.ki8_hi[1], a.ki8_lo[0], a.ki8_lo[1]};
 
+  // QJL: the residual estimate of both blocks of a pair, C[16 tokens x 16]
+  // = S[16 x 128] W[128 x 16], S = the tokens' sign bits as f16 +-1 (exact),
+  // W = R' R q split into f16 halves like the query; each word's two sign
+  // bits move to the two f16 sign positions with one shift and one and-or
+  [[maybe_unused]] auto sketch_pair = [&](const PairQjl& qj, f32x4(&cq)[2]) {
+#pragma unroll
+    for (int X = 0; X < 2; ++X) cq[X] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int X = 0; X < 2; ++X) {
+        u32x4 sa;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int sh = 15 - 4 * st - q;
+          sa[q] = ((sh ? qj.sw[X] << sh : qj.sw[X]) & 0x80008000u) | 0x3C003C00u;
+        }
+        cq[X] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, sa),
+                                                       __builtin_bit_cast(f16x8, wreg[st]), cq[X], 0, 0, 0);
+      }
+  };
+  constexpr float kTau = 0.1107783657f;   // sqrt(pi/2) / sqrt(128)
   auto compute_pair = [&](const BlockRegs<BITS>(&cur)[2], const PairNorms& nrm, [[maybe_unused]] const PairQjl& qj, int lb0) {
     // ---- logits of the two blocks (log2 units)
     float fv[2][4];   // 8-bit path: this lane's column of each block's product
@@ -894,27 +919,10 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
                                                          __builtin_bit_cast(f16x8, qreg[st]), ck[X], 0, 0, 0);
         }
       if constexpr (QJL) {
-        // residual estimate: C[16 tokens x 16] = S[16 x 128] W[128 x 16],
-        // S = the tokens' sign bits as f16 +-1 (exact), W = R' R q split
-        // into f16 halves like the query; each word's two sign bits move to
-        // the two f16 sign positions with one shift and one and-or.  Then
-        // each logit gains sqrt(pi/2)/sqrt(d) rho_t times its sum, before
-        // the two halves are added and the key norm applied.
-        f32x4 cq[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-#pragma unroll
-          for (int X = 0; X < 2; ++X) {
-            u32x4 sa;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int sh = 15 - 4 * st - q;
-              sa[q] = ((sh ? qj.sw[X] << sh : qj.sw[X]) & 0x80008000u) | 0x3C003C00u;
-            }
-            cq[X] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, sa),
-                                                           __builtin_bit_cast(f16x8, wreg[st]), cq[X], 0, 0, 0);
-          }
-        constexpr float kTau = 0.1107783657f;   // sqrt(pi/2) / sqrt(128)
+        // each logit gains sqrt(pi/2)/sqrt(d) rho_t times its sketch sum,
+        // before the two halves are added and the key norm applied
+        f32x4 cq[2];
+        sketch_pair(qj, cq);
 #pragma unroll
         for (int X = 0; X < 2; ++X)
 #pragma unroll
@@ -937,6 +945,25 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
         send[j] = col_lo ? fv[0][j] : fv[1][j];
       }
       fmac_ror8_4(cs, send, w_par);
+      if constexpr (QJL) {
+        // the own block's sketch sum: own column plus the partner's column
+        // (the lane 8 away keeps the other block), times tau rho_t
+        f32x4 cq[2];
+        sketch_pair(qj, cq);
+        float qo[4], qs[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          qo[j] = col_lo ? cq[1][j] : cq[0][j];
+          qs[j] = col_lo ? cq[0][j] : cq[1][j];
+        }
+        fmac_ror8_4(qo, qs, 1.f);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t rh = col_lo ? qj.rh[1][j >> 1] : qj.rh[0][j >> 1];
+          const float tr = (j & 1) ? mul_h_hi(kTau, rh) : mul_h_lo(kTau, rh);
+          cs[j] = __builtin_fmaf(tr, qo[j], cs[j]);
+        }
+      }
       scale_by_norms(cs, nrm.gk, s);
     }
     // ---- value operands: table reads issued before the softmax needs them
@@ -1165,14 +1192,14 @@ __global__ __launch_bounds__(64 * DecodeSmem<BITS>::kWaves) __attribute__((amdgp
 
 static int check_mfma_args(const DecodeArgs& a, int bits, bool qjl) {
   // the kernel's chunk geometry is fixed at compile time: values, and the
-  // QJL sidecar (2- and 3-bit caches) right after the norms
+  // QJL sidecar right after the norms
   const int64_t expect = 512 * bits + 64 + (qjl ? 32 + 256 : 0);
   if (a.lay.block_bytes != expect || a.lay.off_k != 0 || a.lay.off_v != 256 * bits ||
       a.lay.off_gk != 512 * bits || a.lay.off_gv != 512 * bits + 32 ||
       (qjl && (a.lay.off_rho != 512 * bits + 64 || a.lay.off_sign != 512 * bits + 96)) ||
       (reinterpret_cast<uintptr_t>(a.pool) & 15) != 0)
     return (int)hipErrorInvalidValue;
-  if (bits < 2 || bits > 4 || (qjl && bits > 3)) return (int)hipErrorInvalidValue;
+  if (bits < 2 || bits > 4) return (int)hipErrorInvalidValue;
   // 4-bit keys need the integer form of the key codebook (odd-symmetric)
   if (bits == 4 && !(a.ki8_unit > 0.f)) return (int)hipErrorInvalidValue;
   // a wave keeps the block-table entries of its pairs one per lane
@@ -1190,6 +1217,9 @@ static void launch_mfma(const DecodeArgs& a, const AP& ap, int bits, bool qjl, i
       if (bits == 2) {
         if (lg) hipLaunchKernelGGL((decode_mfma_kernel<2, true, false, true>), grid, dim3(64 * DecodeSmem<2>::kWaves), 0, s, a, ns, gs, ap);
         else hipLaunchKernelGGL((decode_mfma_kernel<2, false, false, true>), grid, dim3(64 * DecodeSmem<2>::kWaves), 0, s, a, ns, gs, ap);
+      } else if (bits == 4) {
+        if (lg) hipLaunchKernelGGL((decode_mfma_kernel<4, true, false, true>), grid, dim3(64 * DecodeSmem<4>::kWaves), 0, s, a, ns, gs, ap);
+        else hipLaunchKernelGGL((decode_mfma_kernel<4, false, false, true>), grid, dim3(64 * DecodeSmem<4>::kWaves), 0, s, a, ns, gs, ap);
       } else {
         if (lg) hipLaunchKernelGGL((decode_mfma_kernel<3, true, false, true>), grid, dim3(64 * DecodeSmem<3>::kWaves), 0, s, a, ns, gs, ap);
         else hipLaunchKernelGGL((decode_mfma_kernel<3, false, false, true>), grid, dim3(64 * DecodeSmem<3>::kWaves), 0, s, a, ns, gs, ap);

@@ -450,13 +450,12 @@ int blocks_per_split_for(const tq_cache* c, int32_t num_seqs, int32_t group, int
   return (int)bps;
 }
 
-// Decode-attend runs on the matrix cores, with a QJL sidecar too for 2- and
-// 3-bit caches (4-bit QJL caches stay on the vector units).
+// Decode-attend runs on the matrix cores, with or without the QJL sidecar.
 // TQ_DECODE_VALU=1 selects the vector-unit kernel instead (comparison only).
-bool decode_uses_mfma(const tq_cache* c, bool attend) {
+bool decode_uses_mfma(const tq_cache*, bool attend) {
   if (const char* env = std::getenv("TQ_DECODE_VALU"))
     if (std::atoi(env) == 1) return false;
-  return attend && (!c->cfg.qjl || c->cfg.bits_k <= 3);
+  return attend;
 }
 
 int validate_decode(const void* q, int32_t q_dtype, const tq_cache* cache,

@@ -348,8 +348,8 @@ def test_longest_sequence_at_the_split_limit(device, qjl):
     """The longest sequence decode-attend takes: 4096 splits of the largest
     split size, i.e. 4,194,304 blocks (67,108,859 tokens, a ragged last block;
     a 6.7 GB pool) without the QJL sidecar, and 262,144 blocks (4,194,299
-    tokens, the vector kernel's limit, which 4-bit QJL caches take; this
-    3-bit one runs on the matrix-core kernel) with it; one KV head with
+    tokens) with it (the same matrix-core kernel, a shorter sequence: the
+    vector kernel's old limit); one KV head with
     3-bit codes, 8 query heads; the merge folds 4096 partials per head in 32
     rounds.  Every key but five points against the queries (logits near
     -20), the five hot ones along them (near +20), so the other tokens carry

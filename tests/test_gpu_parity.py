@@ -373,10 +373,11 @@ def test_decode_attend_qjl_and_scale(device):
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("group", [1, 5, 8, 12])
 def test_decode_attend_qjl(device, bits, group):
-    # 2- and 3-bit caches with the QJL sidecar run on the matrix-core decode
-    # (the residual estimate as a sign-matrix product), 4-bit ones on the
-    # vector kernel; logits against the oracle's QJL-corrected scores, an
-    # empty sequence, a single token, ragged tails and whole block pairs
+    # caches with the QJL sidecar run on the matrix-core decode (the
+    # residual estimate as a sign-matrix product, added to the f16 table
+    # path's columns at 2 and 3 bits, to the integer path's combined logit
+    # at 4); logits against the oracle's QJL-corrected scores, an empty
+    # sequence, a single token, ragged tails and whole block pairs
     _decode_case(device, bits, group, 2, [0, 1, 300, 1029], qjl=True)
 
 

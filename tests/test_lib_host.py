@@ -169,18 +169,19 @@ def test_no_device_is_reported_without_touching_memory():
 
 
 def test_qjl_attend_split_sizes_for_long_sequences():
-    # The QJL decode-attend kernel caps a split at 64 blocks; long sequences
-    # take more splits (up to 4096 per sequence and KV head), not an error.
+    # Caches with the QJL sidecar take the matrix-core decode-attend kernel
+    # at every width, so their splits are those of the caches without it
+    # (at most 1024 blocks, up to 4096 splits per sequence and KV head)
     r, rq = tq.tq_make_rotation(42, 128), tq.tq_make_rotation(43, 128)
-    cfg = tq.make_config(8, 4, 4, 4, r, qjl=True, rot_qjl=rq)
-    c = tq.tq_cache_create(cfg, 0x100000)
-    c._rots = (r, rq)
     L = tq.lib()
-    # 4 sequences of 131072 tokens: 8192 blocks -> 128 splits of 64 blocks
-    n = L.tq_decode_workspace_bytes(c.handle, 4, 64, 8192)
-    assert n == 4 * 8 * 128 * 8 * 132 * 4
-    assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 64 * 4096) > 0
-    assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 64 * 4096 + 1) == tq.TQ_ERR_UNSUPPORTED
+    for bits in (2, 3, 4):
+        c = tq.tq_cache_create(tq.make_config(8, 4, bits, bits, r, qjl=True, rot_qjl=rq), 0x100000)
+        p = tq.tq_cache_create(tq.make_config(8, 4, bits, bits, r), 0x100000)
+        c._rots = p._rots = (r, rq)
+        for ns, mb in ((4, 8192), (1, 2048), (16, 512), (1, 1024 * 4096)):
+            n = L.tq_decode_workspace_bytes(c.handle, ns, 64, mb)
+            assert n > 0 and n == L.tq_decode_workspace_bytes(p.handle, ns, 64, mb), (bits, ns, mb)
+        assert L.tq_decode_workspace_bytes(c.handle, 1, 64, 1024 * 4096 + 1) == tq.TQ_ERR_UNSUPPORTED
 
 
 def test_matrix_core_attend_split_sizes():
