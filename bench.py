@@ -535,7 +535,7 @@ def main():
             "bound": "hbm", "achieved": round(qeb / qe_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(qeb / qe_s / 1e9 / HBM_PEAK_GBPS, 4), "bytes_per_launch": qeb,
             "us_per_launch": round(qe_s * 1e6, 2), "vectors_per_s": round(2 * th / qe_s, 1),
-            "note": "encode into a cache with the QJL residual sketch on the keys (vector-unit kernel); "
+            "note": "encode into a cache with the QJL residual sketch on the keys (matrix-core encoder, sketch product in split f16); "
                     "not part of the timed step"}
         qdb = th * (qkb + qvb)
         qd_s = float(np.mean(qd_ms)) / 1e3

@@ -10,11 +10,12 @@
 // direction indices).
 //
 // Two kernels:
-//  * encode_mx_kernel (bf16 / f16 input, no QJL sidecar): the Hadamard
-//    product on the matrix cores, 16 vectors per wave; the norm, the bucketed
-//    threshold search and the packing stay on the vector ALUs (described at
-//    the kernel).
-//  * encode_kernel (fp32 input, or the QJL sidecar): one vector (d = 128)
+//  * encode_mx_kernel (bf16 / f16 input, with or without the QJL sidecar):
+//    the Hadamard product on the matrix cores, 16 vectors per wave; the norm,
+//    the bucketed threshold search and the packing stay on the vector ALUs
+//    (described at the kernel).  The sidecar's second Hadamard product runs on
+//    the matrix cores too.
+//  * encode_kernel (fp32 input): one vector (d = 128)
 //    per 16-lane row, 8 coordinates per lane, the FWHT as in-lane butterflies
 //    plus DPP lane stages, so a wave64 encodes 4 vectors at once and a
 //    256-thread workgroup 16.  A workgroup handles kIters such groups; all
@@ -164,7 +165,7 @@ __device__ __forceinline__ float dot2_acc(uint32_t w, uint32_t b, float c) {
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core encode for 16-bit inputs (no QJL sidecar).
+// Matrix-core encode for 16-bit inputs.
 //
 // The Hadamard part of the rotation is the dense product Y = H X' for a batch
 // of 16 vectors: X' is the 128 x 16 input with the sign flips applied as an
@@ -184,6 +185,17 @@ __device__ __forceinline__ float dot2_acc(uint32_t w, uint32_t b, float c) {
 //                   + n0 s2                             odd tiles: elements 4..7
 //                   + n1 k0 + n2 k1                     same for the whole tile and step
 // so each operand is one of +-B0, +-B1, B1 being B0 with elements 4..7 negated.
+//
+// QJL sidecar (keys of a QJL cache): the residual r = y / (|x| sqrt(128)) -
+// centroid(code) of the lane's coordinates 32 m + 8 g .. +7 sits exactly
+// where step m of a second product with H reads its input, so H D' r is the
+// same 8 tiles x 4 steps with D' (the sketch's signs) applied as sign-bit
+// xors.  r is not exact in 16 bits: it is scaled by 2^10 and split into f16
+// high and low parts (high truncated, low = the rest, both in f16), and the
+// two products accumulate in fp32.  What the split drops is below 2^-22 of
+// each |r_i|, so each output is off by at most 2^-22 sqrt(128) |r| < 3e-6 |r|
+// from the fp32 product, and only such near-zero outputs can take the other
+// sign bit.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -213,11 +225,31 @@ struct MxShared {
   __align__(16) uint8_t rec[4][16 * kRecStride];      // per wave: 16 packed records
 };
 
+// QJL sidecar: the sketch's sign-bit masks (as smask) and 2^10 x the centroids.
+struct MxQjlShared {
+  u32x4_t qmask[4][4];
+  float cent[16];
+};
+
 // Bucket table, sign masks (shared) and the H operands B0, B1, -B0, -B1 of
 // this lane (lane = (g', i) of the A layout).
-template <int BITS, int DT>
-__device__ __forceinline__ void mx_setup(const EncodeArgs& a, MxShared<BITS>& sh, u32x4_t (&B)[4], int tid) {
+template <int BITS, int DT, bool QJL>
+__device__ __forceinline__ void mx_setup(const EncodeArgs& a, MxShared<BITS>& sh, MxQjlShared& shq, u32x4_t (&B)[4],
+                                         int tid) {
   fill_lut(sh.lut, a.tab, a.tab.lut_scale, a.tab.lut_offset - 0.5f, tid);
+  if constexpr (QJL) {
+    if (tid >= 64 && tid < 128) {
+      const int gg = (tid >> 4) & 3, k = (tid >> 2) & 3, q = tid & 3;
+      const uint32_t n0 = __builtin_amdgcn_readfirstlane(a.rot_qjl.neg[0]);
+      const uint32_t n1 = __builtin_amdgcn_readfirstlane(a.rot_qjl.neg[1]);
+      const uint32_t n2 = __builtin_amdgcn_readfirstlane(a.rot_qjl.neg[2]);
+      const uint32_t n3 = __builtin_amdgcn_readfirstlane(a.rot_qjl.neg[3]);
+      const uint32_t wd = k == 0 ? n0 : k == 1 ? n1 : k == 2 ? n2 : n3;
+      const uint32_t sb = (wd >> (8 * gg)) & 0xFFu;
+      shq.qmask[gg][k][q] = (((sb >> (2 * q)) & 1u) << 15) | (((sb >> (2 * q + 1)) & 1u) << 31);
+    }
+    if (tid >= 128 && tid < 144) shq.cent[tid - 128] = 1024.f * a.tab.centroid[tid - 128];   // 2^10 c, exact
+  }
   if (tid < 64) {
     const int gg = tid >> 4, k = (tid >> 2) & 3, q = tid & 3;
     // sign byte 4 k + gg, picked among wave-uniform (scalar) loads of the
@@ -271,9 +303,10 @@ __device__ __forceinline__ void mx_load(const EncodeArgs& a, const void* src, ui
   o.slot = v < nvec ? a.slot_mapping[t] : -1;
 }
 
-template <int BITS, int DT, bool OFF32>
+template <int BITS, int DT, bool OFF32, bool QJL>
 __device__ __forceinline__ void mx_batch(const EncodeArgs& a, const EncodeStream& st, const MxBatch& in,
-                                         const u32x4_t (&B)[4], MxShared<BITS>& sh, int wave, int g, int j) {
+                                         const u32x4_t (&B)[4], MxShared<BITS>& sh, const MxQjlShared& shq, int wave,
+                                         int g, int j) {
   constexpr int kRecStride = MxShared<BITS>::kRecStride;
   const float lut_scale = a.tab.lut_scale, lut_off = a.tab.lut_offset - 0.5f;
   uint8_t* rec_w = sh.rec[wave];
@@ -291,6 +324,12 @@ __device__ __forceinline__ void mx_batch(const EncodeArgs& a, const EncodeStream
   u32x4_t xs[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) xs[k] = in.X[k] ^ sh.smask[g][k];
+  // QJL: 2^10 r as f16 high and low parts with the sketch's signs applied,
+  // and the lane's share of |2^10 r|^2
+  const bool qjl = QJL && st.qjl != 0;
+  const float zu = ss > 0.f ? kInvSqrtD * __builtin_amdgcn_rsqf(ss) : 0.f;
+  u32x4_t rh[4], rl[4];
+  float rr = 0.f;
 
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -304,6 +343,21 @@ __device__ __forceinline__ void mx_batch(const EncodeArgs& a, const EncodeStream
     const float y[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
     uint32_t code[8];
     row_codes<BITS>(y, zs, lut_off, sh.lut, code);
+    if constexpr (QJL) {
+      if (qjl) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // 1024 (y zu - c) as one fma: scaling by a power of two is exact
+          const float r0 = __builtin_fmaf(y[2 * w], 1024.f * zu, -shq.cent[code[2 * w]]);
+          const float r1 = __builtin_fmaf(y[2 * w + 1], 1024.f * zu, -shq.cent[code[2 * w + 1]]);
+          rr = __builtin_fmaf(r0, r0, __builtin_fmaf(r1, r1, rr));
+          const auto h = __builtin_amdgcn_cvt_pkrtz(r0, r1);
+          const auto l = __builtin_amdgcn_cvt_pkrtz(r0 - (float)h[0], r1 - (float)h[1]);
+          rh[m][w] = __builtin_bit_cast(uint32_t, h) ^ shq.qmask[g][m][w];
+          rl[m][w] = __builtin_bit_cast(uint32_t, l) ^ shq.qmask[g][m][w];
+        }
+      }
+    }
     uint32_t word = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) word |= code[e] << (BITS * e);
@@ -318,6 +372,33 @@ __device__ __forceinline__ void mx_batch(const EncodeArgs& a, const EncodeStream
       const bool odd = (g & 1) != 0;
       *reinterpret_cast<uint16_t*>(dst + (odd ? 1 : 0)) = (uint16_t)(odd ? word >> 8 : word);
       dst[odd ? 0 : 2] = (uint8_t)(odd ? word : word >> 16);
+    }
+  }
+  float rho = 0.f;
+  if constexpr (QJL) {
+    if (qjl) {
+      rho = __builtin_amdgcn_sqrtf(sum_rows(rr)) * (1.f / 1024.f);
+      // the H operands in f16 (+-1 has the same sign bit in both formats)
+      u32x4_t Bh[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Bh[i] = DT == 2 ? B[i] ^ (0x3F803F80u ^ 0x3C003C00u) : B[i];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int neg = ((m & k) ^ ((m >> 1) & (k >> 1))) & 1;
+          c0 = mfma_h<1>(Bh[2 * neg], rh[k], c0);
+          c1 = mfma_h<1>(Bh[1 + 2 * neg], rh[k], c1);
+          c0 = mfma_h<1>(Bh[2 * neg], rl[k], c0);
+          c1 = mfma_h<1>(Bh[1 + 2 * neg], rl[k], c1);
+        }
+        uint32_t bits = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bits |= (c0[e] < 0.f ? 1u : 0u) << e | (c1[e] < 0.f ? 1u : 0u) << (e + 4);
+        // sign byte of coordinates 32 m + 8 g .. +7 in the record's padding
+        rec_w[j * kRecStride + 16 * BITS + 4 * m + g] = (uint8_t)bits;
+      }
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -347,6 +428,17 @@ __device__ __forceinline__ void mx_batch(const EncodeArgs& a, const EncodeStream
       const Off no = off + (uint32_t)st.norm_off + 2u * row;
       *reinterpret_cast<__half*>(a.pool + no) = __float2half_rn(fminf(gamma, 65504.f));
     }
+    if constexpr (QJL) {
+      if (qjl && g == 3) {
+        const u32x4_t sg = *reinterpret_cast<const u32x4_t*>(rec_w + j * kRecStride + 16 * BITS);
+        const Off so = off + (uint32_t)a.sign_off + 16u * row;
+        __builtin_nontemporal_store(sg, reinterpret_cast<u32x4_t*>(a.pool + so));
+      }
+      if (qjl && g == 1) {
+        const Off ro = off + (uint32_t)a.rho_off + 2u * row;
+        *reinterpret_cast<__half*>(a.pool + ro) = __float2half_rn(fminf(rho, 65504.f));
+      }
+    }
   }
   // the next batch rewrites this wave's staging records
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -355,9 +447,10 @@ __device__ __forceinline__ void mx_batch(const EncodeArgs& a, const EncodeStream
 }
 
 // kMxBatches batches per wave, all loads issued up front.
-template <int BITS, int DT, bool OFF32>
+template <int BITS, int DT, bool OFF32, bool QJL>
 __global__ __launch_bounds__(256) void encode_mx_kernel(const EncodeArgs a) {
   __shared__ MxShared<BITS> sh;
+  __shared__ MxQjlShared shq;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
   // the input loads go first: the set-up's per-lane reads of the argument
@@ -368,10 +461,10 @@ __global__ __launch_bounds__(256) void encode_mx_kernel(const EncodeArgs a) {
 #pragma unroll
   for (int u = 0; u < kMxBatches; ++u) mx_load(a, st.src, b0 + u, g, j, in[u]);
   u32x4_t B[4];
-  mx_setup<BITS, DT>(a, sh, B, tid);
+  mx_setup<BITS, DT, QJL>(a, sh, shq, B, tid);
   __syncthreads();   // bucket table and sign masks
 #pragma unroll
-  for (int u = 0; u < kMxBatches; ++u) mx_batch<BITS, DT, OFF32>(a, st, in[u], B, sh, wave, g, j);
+  for (int u = 0; u < kMxBatches; ++u) mx_batch<BITS, DT, OFF32, QJL>(a, st, in[u], B, sh, shq, wave, g, j);
 }
 
 // TQ_ENCODE_GENERIC=1 keeps 16-bit inputs on encode_kernel (comparison only).
@@ -387,9 +480,9 @@ template <int BITS, int DT>
 static int launch_bits_dt(const EncodeArgs& a, int streams, bool qjl, hipStream_t s) {
   // 16-byte record stores need 16-byte aligned chunks and record regions
   // (the layout's sizes are multiples of 16; the pool base is checked)
-  const bool mx = DT != 0 && !qjl && !encode_generic_only() && a.num_vectors < ((int64_t)1 << 31) &&
+  const bool mx = DT != 0 && !encode_generic_only() && a.num_vectors < ((int64_t)1 << 31) &&
                   a.block_bytes % 16 == 0 && a.stream[0].rec_off % 16 == 0 && a.stream[1].rec_off % 16 == 0 &&
-                  (reinterpret_cast<uintptr_t>(a.pool) & 15) == 0;
+                  (!qjl || a.sign_off % 16 == 0) && (reinterpret_cast<uintptr_t>(a.pool) & 15) == 0;
   if (mx) {
     constexpr int DT16 = DT == 0 ? 1 : DT;
     // 32-bit cache offsets: the whole pool below 4 GiB, block index and
@@ -398,10 +491,14 @@ static int launch_bits_dt(const EncodeArgs& a, int streams, bool qjl, hipStream_
     const bool off32 = blocks < ((int64_t)1 << 24) && per_block < ((int64_t)1 << 24) &&
                        blocks * per_block <= ((int64_t)1 << 32) - per_block;
     dim3 gmx((unsigned)((a.num_vectors + 64 * kMxBatches - 1) / (64 * kMxBatches)), (unsigned)streams);
-    if (off32)
-      hipLaunchKernelGGL((encode_mx_kernel<BITS, DT16, true>), gmx, dim3(256), 0, s, a);
+    if (qjl && off32)
+      hipLaunchKernelGGL((encode_mx_kernel<BITS, DT16, true, true>), gmx, dim3(256), 0, s, a);
+    else if (qjl)
+      hipLaunchKernelGGL((encode_mx_kernel<BITS, DT16, false, true>), gmx, dim3(256), 0, s, a);
+    else if (off32)
+      hipLaunchKernelGGL((encode_mx_kernel<BITS, DT16, true, false>), gmx, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((encode_mx_kernel<BITS, DT16, false>), gmx, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((encode_mx_kernel<BITS, DT16, false, false>), gmx, dim3(256), 0, s, a);
     return (int)hipGetLastError();
   }
   const int64_t groups = (a.num_vectors + 16 * kIters - 1) / (16 * kIters);   // 64 vectors each

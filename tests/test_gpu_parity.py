@@ -76,11 +76,25 @@ def test_encode_matches_oracle(device, bits, dtype):
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_encode_qjl_keys_only(device, bits):
-    w = W.SWEEP_64K.with_(seq_len=777, num_kv_heads=4, bits_k=bits, qjl=True)
-    cache, k64, _, slots = encode_gpu(w, device)
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_encode_qjl_keys_only(device, bits, dtype):
+    # 16-bit keys take the matrix-core encoder (the sketch's Hadamard product
+    # in split f16 operands), fp32 keys the vector encoder
+    w = W.SWEEP_64K.with_(seq_len=777, num_kv_heads=4, bits_k=bits, qjl=True,
+                          in_dtype="bf16" if dtype == "bf16" else "f32")
+    _say("qjl encode", bits, dtype)
+    kb, k64 = W.keys(w)
+    if dtype == "f16":
+        kb = kb.astype(np.float16)
+        k64 = kb.astype(np.float64)
+        K = torch.from_numpy(kb).to(device)
+    else:
+        K = to_device(kb, w.in_dtype, device)
+    slots = W.slot_mapping(w)
+    cache = make_cache(w, device)
+    tq.tq_encode_kv(K, None, torch.from_numpy(slots).to(device), bits, cache)
     res = _check_encode(w, cache, k64, None, slots, oracle_layout(w))
-    _say("qjl", bits, res)
+    _say("  ", res)
 
 
 def test_encode_tiny_fp32_config(device):
